@@ -1,0 +1,337 @@
+/*
+ * fp64 CPU oracle for the selective state-space scan -- plain loops, libm exp.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the product path. It shares no code
+ * with the HIP library.
+ *
+ * What is computed, and where it comes from:
+ *  - The selective SSM recurrence of Gu & Dao, "Mamba: Linear-Time Sequence
+ *    Modeling with Selective State Spaces" (2023; listed in the references of
+ *    the ssm-bench README): per (batch, channel) a state of N values evolves
+ *    with input-dependent step Delta_t and input-dependent B_t, C_t
+ *    ("Efficient Sequence Modeling: From S4 to Mamba-3", section 03 System,
+ *    mamba_minimal.py: "selectivity", explicit time-loop scan).
+ *  - Discretisation by exponential-Euler: Abar = exp(Delta*A), Bbar = Delta*B
+ *    (same page, section 04 Approach and section 09 Validation: Mamba-3
+ *    reduces to exponential-Euler when lambda = 1, theta = 0).
+ *  - Output y = C.h + D*x, then gated by silu(z) = z*sigmoid(z) (the gated
+ *    block of Gu & Dao 2023; gate applied after the skip term).
+ *  - SSD (Mamba-2): A is one scalar per head and the state per head is an
+ *    (N, P) matrix; the chunked form splits L into chunks, computes the
+ *    intra-chunk part as decayed-attention matrix products and carries the
+ *    (N, P) state from chunk to chunk (same page, section 03, mamba2_minimal.py;
+ *    section 04 "Chunked SSD with a sequential reference"; Dao & Gu 2024,
+ *    "Transformers are SSMs", listed in the ssm-bench references).
+ *  - step(): the same recurrence advanced by one token (section 03,
+ *    mamba_minimal.py "incremental step()"; section 09 "step() equals a full
+ *    forward").
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n <= 0) n = omp_get_num_procs();
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^{-z}) */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* y = (C.h + D x) * silu(z), with the optional parts left out when absent. */
+static double finish_output(double ch, const double* Dskip, long dix, double xv,
+                            const double* z, long zix) {
+    double v = ch;
+    if (Dskip) v += Dskip[dix] * xv;
+    if (z) v *= silu(z[zix]);
+    return v;
+}
+
+static int bad_dims(int a, int b, int c, int d) { return a < 0 || b < 0 || c < 0 || d < 0; }
+
+/* ---------------------------------------------------------------- O1 ---- */
+int oracle_scan(int B, int L, int D, int N,
+                const double* x, const double* delta, const double* A,
+                const double* Bm, const double* Cm, const double* Dskip,
+                const double* z, const double* h0, double* y, double* h_final) {
+    if (bad_dims(B, L, D, N)) return -1;
+    if ((long)B * L * D > 0 && (!x || !delta || !y)) return -1;
+    if ((long)D * N > 0 && !A) return -1;
+    if ((long)B * L * N > 0 && (!Bm || !Cm)) return -1;
+    long units = (long)B * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u) {
+        long b = u / D, d = u % D;
+        double* h = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));
+        for (int n = 0; n < N; ++n) h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+        for (long t = 0; t < L; ++t) {
+            long i = (b * L + t) * D + d;        /* [B,L,D] */
+            const double* Bt = Bm + (b * L + t) * N; /* [B,L,N] */
+            const double* Ct = Cm + (b * L + t) * N;
+            double dt = delta[i], xv = x[i];
+            double ch = 0.0;
+            for (int n = 0; n < N; ++n) {
+                double abar = exp(dt * A[d * N + n]); /* exponential-Euler */
+                h[n] = abar * h[n] + dt * Bt[n] * xv;
+                ch += Ct[n] * h[n];
+            }
+            y[i] = finish_output(ch, Dskip, d, xv, z, i);
+        }
+        if (h_final)
+            for (int n = 0; n < N; ++n) h_final[(b * D + d) * N + n] = h[n];
+        free(h);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O2 ---- */
+int oracle_ssd_seq(int B, int L, int H, int P, int N,
+                   const double* x, const double* delta, const double* A,
+                   const double* Bm, const double* Cm, const double* Dskip,
+                   const double* z, const double* h0, double* y, double* h_final) {
+    if (bad_dims(B, L, H, P) || N < 0) return -1;
+    long units = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u) {
+        long b = u / H, hh = u % H;
+        long NP = (long)N * P;
+        double* S = (double*)malloc(sizeof(double) * (NP > 0 ? NP : 1)); /* S[n][p] */
+        for (long k = 0; k < NP; ++k) S[k] = h0 ? h0[(b * H + hh) * NP + k] : 0.0;
+        for (long t = 0; t < L; ++t) {
+            double dt = delta[(b * L + t) * H + hh];
+            double abar = exp(dt * A[hh]);
+            const double* Bt = Bm + (b * L + t) * N;
+            const double* Ct = Cm + (b * L + t) * N;
+            const double* xt = x + ((b * L + t) * H + hh) * P;
+            for (int n = 0; n < N; ++n)
+                for (int p = 0; p < P; ++p)
+                    S[n * P + p] = abar * S[n * P + p] + dt * Bt[n] * xt[p];
+            for (int p = 0; p < P; ++p) {
+                double ch = 0.0;
+                for (int n = 0; n < N; ++n) ch += Ct[n] * S[n * P + p];
+                long i = ((b * L + t) * H + hh) * P + p;
+                y[i] = finish_output(ch, Dskip, hh, xt[p], z, i);
+            }
+        }
+        if (h_final)
+            for (long k = 0; k < NP; ++k) h_final[(b * H + hh) * NP + k] = S[k];
+        free(S);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O3 ----
+ * Chunk c covers t in [cQ, min((c+1)Q, L)). With lambda_k = Delta_k*A_h and
+ * s_i the inclusive in-chunk prefix sum of lambda:
+ *   Y_diag[i] = sum_{j<=i} (C_i . B_j) exp(s_i - s_j) Delta_j x_j
+ *   Y_off[i]  = exp(s_i) C_i . S_in
+ *   S_out     = exp(s_last) S_in + sum_j exp(s_last - s_j) Delta_j B_j (x) x_j
+ * The decay from j to i excludes step j's own factor (it is applied when
+ * Delta_j B_j x_j enters the state).
+ */
+int oracle_ssd_chunked(int B, int L, int H, int P, int N, int Q,
+                       const double* x, const double* delta, const double* A,
+                       const double* Bm, const double* Cm, const double* Dskip,
+                       const double* z, const double* h0, double* y, double* h_final) {
+    if (bad_dims(B, L, H, P) || N < 0 || Q < 1) return -1;
+    long units = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u) {
+        long b = u / H, hh = u % H;
+        long NP = (long)N * P;
+        double* S = (double*)malloc(sizeof(double) * (NP > 0 ? NP : 1));
+        double* Snew = (double*)malloc(sizeof(double) * (NP > 0 ? NP : 1));
+        double* s = (double*)malloc(sizeof(double) * Q);
+        double* G = (double*)malloc(sizeof(double) * (size_t)Q * Q); /* C_i . B_j */
+        for (long k = 0; k < NP; ++k) S[k] = h0 ? h0[(b * H + hh) * NP + k] : 0.0;
+        for (long c0 = 0; c0 < L; c0 += Q) {
+            int len = (int)((L - c0) < Q ? (L - c0) : Q);
+            double acc = 0.0;
+            for (int i = 0; i < len; ++i) {
+                acc += delta[(b * L + c0 + i) * H + hh] * A[hh];
+                s[i] = acc;
+            }
+            for (int i = 0; i < len; ++i)
+                for (int j = 0; j <= i; ++j) {
+                    double g = 0.0;
+                    for (int n = 0; n < N; ++n)
+                        g += Cm[(b * L + c0 + i) * N + n] * Bm[(b * L + c0 + j) * N + n];
+                    G[i * Q + j] = g;
+                }
+            for (int i = 0; i < len; ++i) {
+                long ti = b * L + c0 + i;
+                for (int p = 0; p < P; ++p) {
+                    double yd = 0.0;
+                    for (int j = 0; j <= i; ++j) {
+                        long tj = b * L + c0 + j;
+                        yd += G[i * Q + j] * exp(s[i] - s[j]) * delta[tj * H + hh] *
+                              x[(tj * H + hh) * P + p];
+                    }
+                    double yo = 0.0;
+                    for (int n = 0; n < N; ++n) yo += Cm[ti * N + n] * S[n * P + p];
+                    yo *= exp(s[i]);
+                    long ix = (ti * H + hh) * P + p;
+                    y[ix] = finish_output(yd + yo, Dskip, hh, x[ix], z, ix);
+                }
+            }
+            double slast = s[len - 1];
+            for (int n = 0; n < N; ++n)
+                for (int p = 0; p < P; ++p) {
+                    double v = exp(slast) * S[n * P + p];
+                    for (int j = 0; j < len; ++j) {
+                        long tj = b * L + c0 + j;
+                        v += exp(slast - s[j]) * delta[tj * H + hh] * Bm[tj * N + n] *
+                             x[(tj * H + hh) * P + p];
+                    }
+                    Snew[n * P + p] = v;
+                }
+            memcpy(S, Snew, sizeof(double) * NP);
+        }
+        if (h_final)
+            for (long k = 0; k < NP; ++k) h_final[(b * H + hh) * NP + k] = S[k];
+        free(S); free(Snew); free(s); free(G);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O4 ---- */
+int oracle_step(int B, int D, int N, double* state,
+                const double* x, const double* delta, const double* A,
+                const double* Bm, const double* Cm, const double* Dskip,
+                const double* z, double* y) {
+    if (bad_dims(B, D, N, 0)) return -1;
+    long units = (long)B * D;
+#pragma omp parallel for schedule(static)
+    for (long u = 0; u < units; ++u) {
+        long b = u / D, d = u % D;
+        double dt = delta[u], xv = x[u];
+        double* h = state + u * N;
+        double ch = 0.0;
+        for (int n = 0; n < N; ++n) {
+            h[n] = exp(dt * A[d * N + n]) * h[n] + dt * Bm[b * N + n] * xv;
+            ch += Cm[b * N + n] * h[n];
+        }
+        y[u] = finish_output(ch, Dskip, d, xv, z, u);
+    }
+    return 0;
+}
+
+int oracle_ssd_step(int B, int H, int P, int N, double* state,
+                    const double* x, const double* delta, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip,
+                    const double* z, double* y) {
+    if (bad_dims(B, H, P, N)) return -1;
+    long units = (long)B * H;
+#pragma omp parallel for schedule(static)
+    for (long u = 0; u < units; ++u) {
+        long b = u / H, hh = u % H;
+        double dt = delta[u];
+        double abar = exp(dt * A[hh]);
+        double* S = state + u * (long)N * P;
+        const double* xt = x + u * P;
+        for (int n = 0; n < N; ++n)
+            for (int p = 0; p < P; ++p)
+                S[n * P + p] = abar * S[n * P + p] + dt * Bm[b * N + n] * xt[p];
+        for (int p = 0; p < P; ++p) {
+            double ch = 0.0;
+            for (int n = 0; n < N; ++n) ch += Cm[b * N + n] * S[n * P + p];
+            y[u * P + p] = finish_output(ch, Dskip, hh, xt[p], z, u * P + p);
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- O5 ----
+ * Unrolled state, every product written out:
+ *   h_T = (prod_{k=0..T} a_k) h0 + sum_{s<=T} (prod_{k=s+1..T} a_k) Delta_s B_s x_s
+ * with a_k = exp(Delta_k A). O(L^2) per state element: tiny shapes only.
+ */
+int oracle_scan_unroll(int B, int L, int D, int N,
+                       const double* x, const double* delta, const double* A,
+                       const double* Bm, const double* Cm, const double* Dskip,
+                       const double* z, const double* h0, double* y, double* h_final) {
+    if (bad_dims(B, L, D, N)) return -1;
+    for (long b = 0; b < B; ++b)
+        for (long d = 0; d < D; ++d)
+            for (long T = 0; T < L; ++T) {
+                long iT = (b * L + T) * D + d;
+                double ch = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    double hT = 0.0;
+                    if (h0) {
+                        double pr = 1.0;
+                        for (long k = 0; k <= T; ++k)
+                            pr *= exp(delta[(b * L + k) * D + d] * A[d * N + n]);
+                        hT += pr * h0[(b * D + d) * N + n];
+                    }
+                    for (long s2 = 0; s2 <= T; ++s2) {
+                        double pr = 1.0;
+                        for (long k = s2 + 1; k <= T; ++k)
+                            pr *= exp(delta[(b * L + k) * D + d] * A[d * N + n]);
+                        long is = (b * L + s2) * D + d;
+                        hT += pr * delta[is] * Bm[(b * L + s2) * N + n] * x[is];
+                    }
+                    ch += Cm[(b * L + T) * N + n] * hT;
+                    if (h_final && T == L - 1) h_final[(b * D + d) * N + n] = hT;
+                }
+                y[iT] = finish_output(ch, Dskip, d, x[iT], z, iT);
+            }
+    if (L == 0 && h_final)
+        for (long k = 0; k < (long)B * D * N; ++k) h_final[k] = h0 ? h0[k] : 0.0;
+    return 0;
+}
+
+int oracle_ssd_unroll(int B, int L, int H, int P, int N,
+                      const double* x, const double* delta, const double* A,
+                      const double* Bm, const double* Cm, const double* Dskip,
+                      const double* z, const double* h0, double* y, double* h_final) {
+    if (bad_dims(B, L, H, P) || N < 0) return -1;
+    long NP = (long)N * P;
+    for (long b = 0; b < B; ++b)
+        for (long hh = 0; hh < H; ++hh)
+            for (long T = 0; T < L; ++T)
+                for (int p = 0; p < P; ++p) {
+                    long iT = ((b * L + T) * H + hh) * P + p;
+                    double ch = 0.0;
+                    for (int n = 0; n < N; ++n) {
+                        double hT = 0.0;
+                        if (h0) {
+                            double pr = 1.0;
+                            for (long k = 0; k <= T; ++k)
+                                pr *= exp(delta[(b * L + k) * H + hh] * A[hh]);
+                            hT += pr * h0[(b * H + hh) * NP + n * P + p];
+                        }
+                        for (long s2 = 0; s2 <= T; ++s2) {
+                            double pr = 1.0;
+                            for (long k = s2 + 1; k <= T; ++k)
+                                pr *= exp(delta[(b * L + k) * H + hh] * A[hh]);
+                            hT += pr * delta[(b * L + s2) * H + hh] * Bm[(b * L + s2) * N + n] *
+                                  x[((b * L + s2) * H + hh) * P + p];
+                        }
+                        ch += Cm[(b * L + T) * N + n] * hT;
+                        if (h_final && T == L - 1) h_final[(b * H + hh) * NP + n * P + p] = hT;
+                    }
+                    y[iT] = finish_output(ch, Dskip, hh, x[iT], z, iT);
+                }
+    if (L == 0 && h_final)
+        for (long k = 0; k < (long)B * H * NP; ++k) h_final[k] = h0 ? h0[k] : 0.0;
+    return 0;
+}

@@ -1,0 +1,78 @@
+/*
+ * fp64 CPU oracle for the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this: only the test suite, the smoke check and the benchmark's CPU
+ * baseline leg use it. It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * Every function takes fp64 arrays (the exact upcast of whatever the caller
+ * stored), contiguous and row-major with the last index fastest, and returns
+ * 0 on success or -1 on a bad argument. Optional inputs are NULL when absent:
+ *   Dskip NULL -> no skip term;  z NULL -> no gate;  h0 NULL -> zero state;
+ *   h_final NULL -> not written.
+ *
+ * Layouts (Mamba-1):  x, delta, z, y [B,L,D]; Bm, Cm [B,L,N]; A [D,N];
+ *                     Dskip [D]; h0, h_final [B,D,N].
+ * Layouts (SSD):      x, z, y [B,L,H,P]; delta [B,L,H]; A [H]; Bm, Cm [B,L,N];
+ *                     Dskip [H]; h0, h_final [B,H,N,P].
+ * Layouts (step):     state [B,D,N] (updated in place); x, delta, z, y [B,D];
+ *                     Bm, Cm [B,N]; A [D,N]; Dskip [D].
+ */
+#ifndef SSM_ORACLE_H
+#define SSM_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of OpenMP threads the oracle uses (n <= 0 restores the default). */
+void oracle_set_threads(int n);
+int oracle_get_threads(void);
+
+/* O1: Mamba-1 selective scan, one time step after another. */
+int oracle_scan(int B, int L, int D, int N,
+                const double* x, const double* delta, const double* A,
+                const double* Bm, const double* Cm, const double* Dskip,
+                const double* z, const double* h0, double* y, double* h_final);
+
+/* O2: Mamba-2 (SSD) recurrence with a scalar decay per head, sequential. */
+int oracle_ssd_seq(int B, int L, int H, int P, int N,
+                   const double* x, const double* delta, const double* A,
+                   const double* Bm, const double* Cm, const double* Dskip,
+                   const double* z, const double* h0, double* y, double* h_final);
+
+/* O3: SSD in chunked (decayed-attention) form with chunk length Q >= 1. */
+int oracle_ssd_chunked(int B, int L, int H, int P, int N, int Q,
+                       const double* x, const double* delta, const double* A,
+                       const double* Bm, const double* Cm, const double* Dskip,
+                       const double* z, const double* h0, double* y, double* h_final);
+
+/* O4: one recurrent decode step; state is read and written in place. */
+int oracle_step(int B, int D, int N, double* state,
+                const double* x, const double* delta, const double* A,
+                const double* Bm, const double* Cm, const double* Dskip,
+                const double* z, double* y);
+
+/* O4': one SSD decode step (scalar decay per head); state [B,H,N,P] in place;
+ * x, z, y [B,H,P]; delta [B,H]; Bm, Cm [B,N]; A, Dskip [H]. */
+int oracle_ssd_step(int B, int H, int P, int N, double* state,
+                    const double* x, const double* delta, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip,
+                    const double* z, double* y);
+
+/* O5: brute-force unrolled state (O(L^2) explicit products), tiny shapes. */
+int oracle_scan_unroll(int B, int L, int D, int N,
+                       const double* x, const double* delta, const double* A,
+                       const double* Bm, const double* Cm, const double* Dskip,
+                       const double* z, const double* h0, double* y, double* h_final);
+
+int oracle_ssd_unroll(int B, int L, int H, int P, int N,
+                      const double* x, const double* delta, const double* A,
+                      const double* Bm, const double* Cm, const double* Dskip,
+                      const double* z, const double* h0, double* y, double* h_final);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

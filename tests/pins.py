@@ -1,0 +1,352 @@
+"""Pins of the fp64 oracle: checks that tie it to something other than itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with what the mathematics fixes: closed forms, brute-force
+unrolling, textbook special cases, exact invariances and the chunked-vs-
+sequential equivalence that the "From S4 to Mamba-3" case study tests
+(section 04 "Chunked SSD with a sequential reference", section 09 Validation:
+aligned (32) and misaligned (64) chunks; step() equals a full forward).
+
+The same functions run against planted-mistake builds of the oracle in
+``test_oracle_mutants.py``: every planted mistake must fail at least one pin.
+"""
+import math
+
+import numpy as np
+
+TIGHT = 1e-10  # fp64 vs fp64: differences are rounding-order only
+
+
+def relerr(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b.ravel())
+    d = np.linalg.norm((a - b).ravel())
+    return d / nb if nb > 0 else d
+
+
+def close(a, b, tol=TIGHT, what=""):
+    e = relerr(a, b)
+    assert e <= tol, f"{what}: normwise relative error {e:.3e} > {tol:.1e}"
+
+
+# ----------------------------------------------------------- random problems
+def mamba1_problem(B, L, D, N, seed, h0=True, Dskip=True, z=True):
+    """fp64 Mamba-1 problem with distinct A per (d, n) and positive Delta."""
+    r = np.random.default_rng(seed)
+    return dict(
+        x=r.standard_normal((B, L, D)),
+        delta=np.logaddexp(0.0, r.normal(-2.0, 1.0, (B, L, D))),
+        A=-np.exp(r.uniform(-1.0, 1.5, (D, N))),
+        Bm=r.standard_normal((B, L, N)) / math.sqrt(N),
+        Cm=r.standard_normal((B, L, N)) / math.sqrt(N),
+        D=r.standard_normal(D) if Dskip else None,
+        z=r.standard_normal((B, L, D)) if z else None,
+        h0=0.5 * r.standard_normal((B, D, N)) if h0 else None,
+    )
+
+
+def ssd_problem(B, L, H, P, N, seed, h0=True, Dskip=True, z=True):
+    r = np.random.default_rng(seed)
+    return dict(
+        x=r.standard_normal((B, L, H, P)),
+        delta=np.logaddexp(0.0, r.normal(-2.0, 1.0, (B, L, H))),
+        A=-np.exp(r.uniform(0.0, math.log(16.0), H)),
+        Bm=r.standard_normal((B, L, N)) / math.sqrt(N),
+        Cm=r.standard_normal((B, L, N)) / math.sqrt(N),
+        D=r.standard_normal(H) if Dskip else None,
+        z=r.standard_normal((B, L, H, P)) if z else None,
+        h0=0.5 * r.standard_normal((B, H, N, P)) if h0 else None,
+    )
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def ssd_as_mamba1(p):
+    """SSD problem -> the Mamba-1 problem with D' = H*P channels that it equals:
+    channel h*P+p gets x[..,h,p], Delta[..,h], A[h] for every state index n,
+    skip D[h], and the (N, P) state transposed to (P, N)."""
+    x = p["x"]
+    B, L, H, P = x.shape
+    N = p["Bm"].shape[2]
+    m = dict(
+        x=x.reshape(B, L, H * P),
+        delta=np.repeat(p["delta"], P, axis=2),
+        A=np.repeat(p["A"], P)[:, None] * np.ones((1, N)),
+        Bm=p["Bm"], Cm=p["Cm"],
+        D=None if p["D"] is None else np.repeat(p["D"], P),
+        z=None if p["z"] is None else p["z"].reshape(B, L, H * P),
+        h0=None if p["h0"] is None else p["h0"].transpose(0, 1, 3, 2).reshape(B, H * P, N),
+    )
+    return m
+
+
+# ----------------------------------------------------------------- P1
+def pin_chunked_equals_sequential(orc):
+    """SSD chunked form == sequential recurrence for aligned, misaligned, ragged,
+    single-step and longer-than-L chunks."""
+    for L, Q in [(96, 32), (96, 64), (100, 7), (64, 1), (100, 256), (50, 50), (33, 32)]:
+        p = ssd_problem(2, L, 3, 4, 5, seed=L * 1000 + Q)
+        ys, hs = orc.ssd_seq(**p)
+        yc, hc = orc.ssd_chunked(**p, chunk=Q)
+        close(yc, ys, what=f"chunked y L={L} Q={Q}")
+        close(hc, hs, what=f"chunked h_final L={L} Q={Q}")
+
+
+# ----------------------------------------------------------------- P2
+def _mamba1_constant_closed_form(x0, d0, A, b0, c0, Dv, z0, h0, L):
+    """Constant inputs: h_t = a^{t+1} h0 + beta (1 - a^{t+1})/(1 - a),
+    a = exp(delta A), beta = delta B x; the ratio is expm1((t+1) delta A) / expm1(delta A)."""
+    Dd, N = A.shape
+    t1 = np.arange(1, L + 1)[:, None, None]                  # [L,1,1]
+    lam = d0 * A[None]                                        # [1,D,N]
+    geo = np.expm1(t1 * lam) / np.expm1(lam)                  # [L,D,N]
+    h = np.exp(t1 * lam) * h0[None] + (d0 * b0[None, None, :] * x0) * geo
+    v = (c0[None, None, :] * h).sum(-1) + Dv[None] * x0
+    return v * silu(z0), h[-1]
+
+
+def pin_constant_input_closed_form(orc):
+    """Geometric-series closed form for constant inputs (all four recurrences)."""
+    B, L, D, N = 1, 37, 3, 4
+    r = np.random.default_rng(7)
+    x0, d0, z0 = 0.7, 0.05, -0.4
+    A = -np.exp(r.uniform(-1, 1.5, (D, N)))
+    b0 = r.standard_normal(N)
+    c0 = r.standard_normal(N)
+    Dv = r.standard_normal(D)
+    h0 = r.standard_normal((B, D, N))
+    yref, href = _mamba1_constant_closed_form(x0, d0, A, b0, c0, Dv, z0, h0[0], L)
+    args = dict(x=np.full((B, L, D), x0), delta=np.full((B, L, D), d0), A=A,
+                Bm=np.broadcast_to(b0, (B, L, N)), Cm=np.broadcast_to(c0, (B, L, N)),
+                D=Dv, z=np.full((B, L, D), z0), h0=h0)
+    y, hf = orc.scan(**args)
+    close(y[0], yref, what="scan closed form y")
+    close(hf[0], href, what="scan closed form h")
+    # the decode step iterated L times
+    st = h0.copy()
+    ys = []
+    for t in range(L):
+        yt, st = orc.step(st, np.full((B, D), x0), np.full((B, D), d0), A, b0[None], c0[None],
+                          D=Dv, z=np.full((B, D), z0))
+        ys.append(yt[0])
+    close(np.stack(ys), yref, what="step closed form y")
+    close(st[0], href, what="step closed form h")
+    # SSD: scalar A per head; state (N, P); every p sees the same constants
+    H, P = 2, 3
+    Ah = -np.exp(r.uniform(0, math.log(16), H))
+    Dh = r.standard_normal(H)
+    hs0 = r.standard_normal((B, H, N, P))
+    sargs = dict(x=np.full((B, L, H, P), x0), delta=np.full((B, L, H), d0), A=Ah,
+                 Bm=np.broadcast_to(b0, (B, L, N)), Cm=np.broadcast_to(c0, (B, L, N)),
+                 D=Dh, z=np.full((B, L, H, P), z0), h0=hs0)
+    for name, fn in [("ssd_seq", orc.ssd_seq), ("ssd_chunked", lambda **k: orc.ssd_chunked(**k, chunk=8))]:
+        y, hf = fn(**sargs)
+        for h in range(H):
+            for p_ in range(P):
+                yr, hr = _mamba1_constant_closed_form(
+                    x0, d0, np.full((1, N), Ah[h]), b0, c0, np.array([Dh[h]]), z0,
+                    hs0[0, h, :, p_][None], L)
+                close(y[0, :, h, p_], yr[:, 0], what=f"{name} closed form y")
+                close(hf[0, h, :, p_], hr[0], what=f"{name} closed form h")
+    # SSD decode step iterated
+    st = hs0.copy()
+    ys = []
+    for t in range(L):
+        yt, st = orc.ssd_step(st, np.full((B, H, P), x0), np.full((B, H), d0), Ah, b0[None],
+                              c0[None], D=Dh, z=np.full((B, H, P), z0))
+        ys.append(yt[0])
+    ys = np.stack(ys)
+    for h in range(H):
+        yr, hr = _mamba1_constant_closed_form(x0, d0, np.full((1, N), Ah[h]), b0, c0,
+                                              np.array([Dh[h]]), z0, hs0[0, h, :, 0][None], L)
+        close(ys[:, h, 0], yr[:, 0], what="ssd_step closed form y")
+
+
+# ----------------------------------------------------------------- P3, P4
+def pin_prefill_one_equals_step(orc):
+    """L = 1 prefill == one decode step from the same state (y and state)."""
+    p = mamba1_problem(2, 1, 5, 6, seed=3)
+    y, hf = orc.scan(**p)
+    ys, st = orc.step(p["h0"], p["x"][:, 0], p["delta"][:, 0], p["A"], p["Bm"][:, 0],
+                      p["Cm"][:, 0], D=p["D"], z=p["z"][:, 0])
+    close(ys, y[:, 0], what="step vs L=1 y")
+    close(st, hf, what="step vs L=1 state")
+    q = ssd_problem(2, 1, 3, 4, 5, seed=4)
+    y, hf = orc.ssd_seq(**q)
+    ys, st = orc.ssd_step(q["h0"], q["x"][:, 0], q["delta"][:, 0], q["A"], q["Bm"][:, 0],
+                          q["Cm"][:, 0], D=q["D"], z=q["z"][:, 0])
+    close(ys, y[:, 0], what="ssd_step vs L=1 y")
+    close(st, hf, what="ssd_step vs L=1 state")
+
+
+def pin_prefill_then_step(orc):
+    """prefill(L) then step(token L+1) == prefill(L+1): last y and final state."""
+    L = 23
+    p = mamba1_problem(2, L + 1, 4, 5, seed=5)
+    yfull, hfull = orc.scan(**p)
+    cut = {k: (v[:, :L] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in p.items()}
+    _, h = orc.scan(**cut)
+    ys, st = orc.step(h, p["x"][:, L], p["delta"][:, L], p["A"], p["Bm"][:, L], p["Cm"][:, L],
+                      D=p["D"], z=p["z"][:, L])
+    close(ys, yfull[:, L], what="prefill+step y")
+    close(st, hfull, what="prefill+step state")
+    q = ssd_problem(2, L + 1, 2, 3, 4, seed=6)
+    yfull, hfull = orc.ssd_seq(**q)
+    cut = {k: (v[:, :L] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in q.items()}
+    _, h = orc.ssd_chunked(**cut, chunk=8)
+    ys, st = orc.ssd_step(h, q["x"][:, L], q["delta"][:, L], q["A"], q["Bm"][:, L],
+                          q["Cm"][:, L], D=q["D"], z=q["z"][:, L])
+    close(ys, yfull[:, L], what="ssd prefill+step y")
+    close(st, hfull, what="ssd prefill+step state")
+
+
+# ----------------------------------------------------------------- P5
+def pin_brute_force_unroll(orc):
+    """Sequential recurrences == the state written out as explicit products."""
+    for (B, L, D, N, s) in [(1, 12, 3, 4, 11), (2, 7, 2, 3, 12), (1, 1, 1, 1, 13)]:
+        p = mamba1_problem(B, L, D, N, seed=s)
+        y, hf = orc.scan(**p)
+        yu, hu = orc.scan_unroll(**p)
+        close(y, yu, what="scan vs unroll y")
+        close(hf, hu, what="scan vs unroll h")
+    for (B, L, H, P, N, s) in [(1, 12, 2, 3, 4, 21), (2, 6, 1, 2, 3, 22)]:
+        q = ssd_problem(B, L, H, P, N, seed=s)
+        y, hf = orc.ssd_seq(**q)
+        yu, hu = orc.ssd_unroll(**q)
+        close(y, yu, what="ssd vs unroll y")
+        close(hf, hu, what="ssd vs unroll h")
+
+
+# ----------------------------------------------------------------- P6
+def pin_special_cases(orc):
+    """A = 0: the state is h0 plus a cumulative sum; Delta = 0: the state never
+    moves; C = 0 and D = 0: the output is zero; C = 0 alone: y = D x silu(z)."""
+    p = mamba1_problem(2, 19, 3, 4, seed=31)
+    p0 = dict(p, A=np.zeros_like(p["A"]))
+    y, hf = orc.scan(**p0)
+    inc = p["delta"][..., None] * p["Bm"][:, :, None, :] * p["x"][..., None]   # [B,L,D,N]
+    h = p["h0"][:, None] + np.cumsum(inc, axis=1)
+    v = np.einsum("bln,bldn->bld", p["Cm"], h) + p["D"] * p["x"]
+    close(y, v * silu(p["z"]), what="A=0 cumsum y")
+    close(hf, h[:, -1], what="A=0 cumsum h")
+    pd = dict(p, delta=np.zeros_like(p["delta"]))
+    y, hf = orc.scan(**pd)
+    v = np.einsum("bln,bdn->bld", p["Cm"], p["h0"]) + p["D"] * p["x"]
+    close(y, v * silu(p["z"]), what="Delta=0 y")
+    close(hf, p["h0"], what="Delta=0 h")
+    pc = dict(p, Cm=np.zeros_like(p["Cm"]), D=np.zeros_like(p["D"]))
+    y, _ = orc.scan(**pc)
+    assert np.all(y == 0.0), "C=0, D=0 must give y=0"
+    pc = dict(p, Cm=np.zeros_like(p["Cm"]))
+    y, _ = orc.scan(**pc)
+    close(y, p["D"] * p["x"] * silu(p["z"]), what="C=0 y")
+    # no gate, no skip: y = C . h only
+    pn = dict(p, z=None, D=None)
+    y, _ = orc.scan(**pn)
+    yd, _ = orc.scan(**dict(pn, D=np.zeros_like(p["D"])))
+    close(y, yd, what="D=None vs D=0")
+    # SSD with A = 0 reduces to a cumulative sum of outer products
+    q = ssd_problem(1, 11, 2, 3, 4, seed=32)
+    q0 = dict(q, A=np.zeros_like(q["A"]))
+    inc = (q["delta"][..., None, None] * q["Bm"][:, :, None, :, None]
+           * q["x"][:, :, :, None, :])                                           # [B,L,H,N,P]
+    S = q["h0"][:, None] + np.cumsum(inc, axis=1)
+    v = np.einsum("bln,blhnp->blhp", q["Cm"], S) + q["D"][None, None, :, None] * q["x"]
+    for name, fn in [("seq", orc.ssd_seq), ("chunk", lambda **k: orc.ssd_chunked(**k, chunk=4))]:
+        y, hf = fn(**q0)
+        close(y, v * silu(q["z"]), what=f"ssd {name} A=0 y")
+        close(hf, S[:, -1], what=f"ssd {name} A=0 h")
+
+
+# ----------------------------------------------------------------- P7
+def pin_ssd_equals_mamba1_mapping(orc):
+    """SSD == Mamba-1 with D = H*P channels sharing Delta and A per head."""
+    q = ssd_problem(2, 17, 3, 4, 5, seed=41)
+    m = ssd_as_mamba1(q)
+    ym, hm = orc.scan(**m)
+    B, L, H, P = q["x"].shape
+    N = q["Bm"].shape[2]
+    for name, fn in [("seq", orc.ssd_seq), ("chunk", lambda **k: orc.ssd_chunked(**k, chunk=6))]:
+        y, hf = fn(**q)
+        close(y.reshape(B, L, H * P), ym, what=f"ssd {name} vs mamba1 y")
+        close(hf.transpose(0, 1, 3, 2).reshape(B, H * P, N), hm, what=f"ssd {name} vs mamba1 h")
+
+
+# ----------------------------------------------------------------- P8
+def pin_split_carry(orc):
+    """scan(x[:m]) -> h; scan(x[m:], h0 = h) == scan(x), at several cut points."""
+    p = mamba1_problem(2, 40, 3, 4, seed=51)
+    y, hf = orc.scan(**p)
+    for m in (1, 13, 39):
+        a = {k: (v[:, :m] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in p.items()}
+        y1, h1 = orc.scan(**a)
+        b = {k: (v[:, m:] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in p.items()}
+        b["h0"] = h1
+        y2, h2 = orc.scan(**b)
+        close(np.concatenate([y1, y2], axis=1), y, what=f"split y m={m}")
+        close(h2, hf, what=f"split h m={m}")
+    q = ssd_problem(1, 40, 2, 3, 4, seed=52)
+    y, hf = orc.ssd_seq(**q)
+    for m in (9, 30):
+        a = {k: (v[:, :m] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in q.items()}
+        y1, h1 = orc.ssd_chunked(**a, chunk=8)
+        b = {k: (v[:, m:] if k in ("x", "delta", "Bm", "Cm", "z") else v) for k, v in q.items()}
+        b["h0"] = h1
+        y2, h2 = orc.ssd_chunked(**b, chunk=8)
+        close(np.concatenate([y1, y2], axis=1), y, what=f"ssd split y m={m}")
+        close(h2, hf, what=f"ssd split h m={m}")
+
+
+# ----------------------------------------------------------------- P9
+def pin_causality(orc):
+    """Changing inputs at t' > t leaves y[:t+1] bit-identical."""
+    p = mamba1_problem(1, 30, 3, 4, seed=61)
+    y, _ = orc.scan(**p)
+    t = 17
+    pp = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+    for k in ("x", "delta", "Bm", "Cm", "z"):
+        pp[k][:, t + 1:] = pp[k][:, t + 1:] * 1.5 + 0.25
+    y2, _ = orc.scan(**pp)
+    assert np.array_equal(y[:, :t + 1], y2[:, :t + 1]), "scan is not causal"
+    assert not np.array_equal(y[:, t + 1:], y2[:, t + 1:])
+    q = ssd_problem(1, 30, 2, 3, 4, seed=62)
+    for fn in (orc.ssd_seq, lambda **k: orc.ssd_chunked(**k, chunk=8)):
+        y, _ = fn(**q)
+        qq = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in q.items()}
+        for k in ("x", "delta", "Bm", "Cm", "z"):
+            qq[k][:, t + 1:] = qq[k][:, t + 1:] * 1.5 + 0.25
+        y2, _ = fn(**qq)
+        assert np.array_equal(y[:, :t + 1], y2[:, :t + 1]), "ssd is not causal"
+
+
+# ----------------------------------------------------------------- P10
+def pin_linearity(orc):
+    """y(alpha x, alpha h0) = alpha y(x, h0) for fixed Delta, B, C, z (exact for alpha = 2)."""
+    p = mamba1_problem(2, 21, 3, 4, seed=71)
+    y, hf = orc.scan(**p)
+    y2, h2 = orc.scan(**dict(p, x=2 * p["x"], h0=2 * p["h0"]))
+    assert np.array_equal(y2, 2 * y) and np.array_equal(h2, 2 * hf)
+    y3, h3 = orc.scan(**dict(p, x=-3 * p["x"], h0=-3 * p["h0"]))
+    close(y3, -3 * y, what="linearity y")
+    close(h3, -3 * hf, what="linearity h")
+    q = ssd_problem(1, 21, 2, 3, 4, seed=72)
+    y, hf = orc.ssd_chunked(**q, chunk=5)
+    y2, h2 = orc.ssd_chunked(**dict(q, x=2 * q["x"], h0=2 * q["h0"]), chunk=5)
+    assert np.array_equal(y2, 2 * y) and np.array_equal(h2, 2 * hf)
+
+
+ALL_PINS = [
+    pin_chunked_equals_sequential,
+    pin_constant_input_closed_form,
+    pin_prefill_one_equals_step,
+    pin_prefill_then_step,
+    pin_brute_force_unroll,
+    pin_special_cases,
+    pin_ssd_equals_mamba1_mapping,
+    pin_split_carry,
+    pin_causality,
+    pin_linearity,
+]

@@ -1,0 +1,62 @@
+"""Planted mistakes in the oracle must be caught by the pins (CPU only).
+
+Each mutant is a one-spot text edit of ``oracle/oracle.c`` (a dropped term, a
+wrong sign or index, a transposed operand, an off-by-one decay), compiled into a
+throw-away library. The test passes when at least one pin fails on it.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "scan_decay_sign": ("abar = exp(dt * A[d * N + n]); /*", "abar = exp(-dt * A[d * N + n]); /*"),
+    "scan_drop_delta_in_input": ("h[n] = abar * h[n] + dt * Bt[n] * xv;", "h[n] = abar * h[n] + Bt[n] * xv;"),
+    "scan_C_swapped_for_B": ("ch += Ct[n] * h[n];", "ch += Bt[n] * h[n];"),
+    "scan_output_before_update": ("abar = exp(dt * A[d * N + n]); /* exponential-Euler */\n                h[n] = abar * h[n] + dt * Bt[n] * xv;\n                ch += Ct[n] * h[n];",
+                                  "abar = exp(dt * A[d * N + n]); /* exponential-Euler */\n                ch += Ct[n] * h[n];\n                h[n] = abar * h[n] + dt * Bt[n] * xv;"),
+    "scan_A_index_transposed": ("abar = exp(dt * A[d * N + n]); /* exponential-Euler */", "abar = exp(dt * A[n * D + d]); /* exponential-Euler */"),
+    "skip_term_dropped": ("if (Dskip) v += Dskip[dix] * xv;", ""),
+    "gate_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "ssd_seq_wrong_head_decay": ("double abar = exp(dt * A[hh]);\n            const double* Bt", "double abar = exp(dt * A[0]);\n            const double* Bt"),
+    "ssd_seq_state_transposed": ("ch += Ct[n] * S[n * P + p];\n                long i", "ch += Ct[n] * S[p * N + n];\n                long i"),
+    "ssd_chunk_exclusive_prefix": ("acc += delta[(b * L + c0 + i) * H + hh] * A[hh];\n                s[i] = acc;",
+                                   "s[i] = acc;\n                acc += delta[(b * L + c0 + i) * H + hh] * A[hh];"),
+    "ssd_chunk_no_offdiag_decay": ("yo *= exp(s[i]);", ""),
+    "ssd_chunk_no_state_decay": ("double v = exp(slast) * S[n * P + p];", "double v = S[n * P + p];"),
+    "ssd_chunk_strict_causal": ("for (int j = 0; j <= i; ++j) {\n                        long tj", "for (int j = 0; j < i; ++j) {\n                        long tj"),
+    "ssd_chunk_G_transposed": ("g += Cm[(b * L + c0 + i) * N + n] * Bm[(b * L + c0 + j) * N + n];",
+                               "g += Cm[(b * L + c0 + j) * N + n] * Bm[(b * L + c0 + i) * N + n];"),
+    "step_no_decay": ("h[n] = exp(dt * A[d * N + n]) * h[n] + dt * Bm[b * N + n] * xv;", "h[n] = h[n] + dt * Bm[b * N + n] * xv;"),
+    "ssd_step_no_delta": ("S[n * P + p] = abar * S[n * P + p] + dt * Bm[b * N + n] * xt[p];", "S[n * P + p] = abar * S[n * P + p] + Bm[b * N + n] * xt[p];"),
+    "hfinal_not_written": ("h_final[(b * D + d) * N + n] = h[n];", "h_final[(b * D + d) * N + n] = 0.0;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "oracle.c"
+    src.write_text(source.replace(old, new))
+    (tmp_path / "oracle.h").write_text(open(os.path.join(os.path.dirname(SRC), "oracle.h")).read())
+    lib = obuild.build(src=str(src), out=str(tmp_path / f"lib_{name}.so"), quiet=True)
+    mut = oracle.Oracle(lib)
+    failures = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mut)
+        except (AssertionError, ValueError, FloatingPointError) as e:
+            failures.append(pin.__name__)
+    assert failures, f"no pin caught the planted mistake {name}"
