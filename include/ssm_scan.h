@@ -1,0 +1,141 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
+ *
+ * Three entry points, each a hand-written HIP kernel pipeline for CDNA4:
+ *   ssm_scan_fwd   Mamba-1 selective scan over a whole sequence (prefill)
+ *   ssm_ssd_fwd    Mamba-2 SSD: scalar decay per head, chunked decayed-attention form
+ *   ssm_step       one-token recurrent decode step, state updated in place
+ *
+ * The operation (selective SSM of Gu & Dao, "Mamba: Linear-Time Sequence
+ * Modeling with Selective State Spaces", 2023, and the SSD form of Dao & Gu,
+ * "Transformers are SSMs", 2024 -- both in the ssm-bench README's references;
+ * the variants as described by "Efficient Sequence Modeling: From S4 to
+ * Mamba-3", section 03 System: mamba_minimal.py has input-dependent Delta, B, C
+ * and an incremental step(); mamba2_minimal.py has a scalar A per head, chunked
+ * decayed-attention matmuls and a carried (N, P) state):
+ *
+ *   per (batch b, channel d), state h in R^N, for t = 0 .. L-1:
+ *     h_t = exp(Delta_t * A) (.) h_{t-1} + Delta_t * B_t * x_t      (exponential-Euler:
+ *     y_t = (C_t . h_t + D * x_t) * silu(z_t),  silu(z) = z / (1 + e^-z)   section 04/09)
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are contiguous, row-major, last index fastest.
+ *  - Every pointer is a DEVICE pointer owned by the caller. The library never
+ *    allocates, frees or synchronises inside these calls and keeps no pointer
+ *    after return, except for work in flight on `stream`.
+ *  - `stream` is a hipStream_t (NULL = the default stream). All work is queued
+ *    asynchronously on it; results are ready when the stream reaches that point.
+ *  - `io` (ssm_dtype_t) is the storage type of x, delta, B, C, z and y.
+ *    A, D, h0, h_final and the decode state are always fp32.
+ *    Arithmetic is fp32 throughout (fp32 state and accumulation).
+ *  - delta is used as given (already positive: no softplus inside).
+ *  - A holds the actual (negative) decay rates, not log(-A).
+ *  - B and C are one group shared by all channels (Mamba-1) or all heads (SSD).
+ *  - Optional pointers may be NULL: Dskip (no skip term), z (no gate),
+ *    h0 (zero initial state), h_final (not written).
+ *  - Aliasing: y must not alias any input; h_final must not alias h0.
+ *  - Errors: arguments are validated BEFORE any HIP call. A rejected call has
+ *    queued nothing. Status codes are below; ssm_last_error() returns a
+ *    human-readable detail of the calling thread's last failure.
+ *    No C++ exception crosses this boundary.
+ *  - Results are deterministic run to run (no floating-point atomics).
+ *  - Thread-safe and reentrant: no mutable global state beyond a per-thread
+ *    error message and cached device properties.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_INVALID_ARG = 1, /* null required pointer, bad dimension, misaligned pointer */
+    SSM_ERR_UNSUPPORTED = 2, /* shape outside the compiled range (e.g. unsupported N or P) */
+    SSM_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than *_workspace_size() */
+    SSM_ERR_HIP = 4          /* a HIP launch error (hipGetLastError after the launch) */
+} ssm_status_t;
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+/* Static string naming a status code. */
+const char* ssm_status_string(int status);
+
+/* Detail of the calling thread's last non-OK status ("" if none). */
+const char* ssm_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * ssm_scan_fwd -- Mamba-1 selective scan (prefill).
+ *
+ *   x, delta, z, y : [B, L, D]  io dtype     (z may be NULL)
+ *   A              : [D, N]     fp32, A < 0 as used in exp(delta * A)
+ *   Bm, Cm         : [B, L, N]  io dtype, shared by all D channels
+ *   Dskip          : [D]        fp32 or NULL
+ *   h0             : [B, D, N]  fp32 or NULL (zeros)
+ *   h_final        : [B, D, N]  fp32 out, or NULL
+ *   workspace      : device scratch of at least ssm_scan_workspace_size(B, L, D, N)
+ *                    bytes (NULL allowed when that size is 0); contents on entry
+ *                    are ignored and on return are undefined.
+ * Supported: N in {4, 8, 16, 32, 64}; B, D >= 1; L >= 0 (L = 0 writes h_final = h0).
+ * Every pointer must be 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t ssm_scan_workspace_size(int B, int L, int D, int N);
+
+int ssm_scan_fwd(int B, int L, int D, int N, int io,
+                 const void* x, const void* delta, const float* A,
+                 const void* Bm, const void* Cm, const float* Dskip,
+                 const void* z, const float* h0,
+                 void* y, float* h_final,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_ssd_fwd -- Mamba-2 SSD chunked scan (prefill), scalar decay per head.
+ *
+ *   x, z, y : [B, L, H, P]  io dtype     (z may be NULL)
+ *   delta   : [B, L, H]     io dtype
+ *   A       : [H]           fp32, A_h < 0
+ *   Bm, Cm  : [B, L, N]     io dtype, one group shared by all H heads
+ *   Dskip   : [H]           fp32 or NULL
+ *   h0      : [B, H, N, P]  fp32 or NULL (zeros)
+ *   h_final : [B, H, N, P]  fp32 out, or NULL
+ *   chunk   : chunk length Q >= 1 (0 = default 256). The last chunk is ragged
+ *             when Q does not divide L. The result does not depend on Q beyond
+ *             rounding.
+ * Supported: io = SSM_BF16; N in {64, 128}; P in {64}; chunk <= 256.
+ * ------------------------------------------------------------------------- */
+size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk);
+
+int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
+                const void* x, const void* delta, const float* A,
+                const void* Bm, const void* Cm, const float* Dskip,
+                const void* z, const float* h0,
+                void* y, float* h_final,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_step -- one-token recurrent decode step, state read and written in place.
+ *
+ *   state  : [B, D, N]  fp32, updated in place
+ *   x, delta, z, y : [B, D]  io dtype   (z may be NULL)
+ *   A      : [D, N]  fp32
+ *   Bm, Cm : [B, N]  io dtype
+ *   Dskip  : [D]     fp32 or NULL
+ * Supported: N in {4, 8, 16, 32, 64}.
+ * ------------------------------------------------------------------------- */
+int ssm_step(int B, int D, int N, int io,
+             float* state, const void* x, const void* delta, const float* A,
+             const void* Bm, const void* Cm, const float* Dskip, const void* z,
+             void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

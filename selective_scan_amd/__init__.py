@@ -1,0 +1,19 @@
+"""MI355X (gfx950) selective state-space scan.
+
+Python binding of the C ABI in ``include/ssm_scan.h`` (library ``libssm_scan.so``,
+built in-tree by ``python -m selective_scan_amd.build``). The functions keep the
+C names, take torch tensors that already live on the GPU, allocate outputs and
+workspace with ``torch.empty`` and pass raw device pointers and the current HIP
+stream. Every step of the computation runs in the library's HIP kernels; there
+is no fallback of any kind: without the built library importing the low-level
+module raises.
+"""
+from .ops import (  # noqa: F401
+    SsmError,
+    lib,
+    ssm_scan_fwd,
+    ssm_scan_workspace_size,
+    ssm_ssd_fwd,
+    ssm_ssd_workspace_size,
+    ssm_step,
+)

@@ -1,0 +1,160 @@
+// C ABI of the selective-scan library: argument validation (before any HIP call),
+// status codes and dispatch to the gfx950 launchers. Declared in include/ssm_scan.h.
+#include "ssm_scan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <limits>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fn, const char* what) {
+    g_last_error = std::string(fn) + ": " + what;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return SSM_OK;
+}
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// n1*n2*... fits in int64 without overflow
+bool product_ok(std::initializer_list<long long> dims, long long limit = std::numeric_limits<long long>::max()) {
+    long long p = 1;
+    for (long long d : dims) {
+        if (d < 0) return false;
+        if (d != 0 && p > limit / d) return false;
+        p *= d;
+    }
+    return true;
+}
+
+int hip_status(hipError_t e, const char* fn) {
+    if (e == hipSuccess) return ok();
+    char buf[256];
+    std::snprintf(buf, sizeof buf, "HIP error %d (%s)", (int)e, hipGetErrorString(e));
+    return fail(SSM_ERR_HIP, fn, buf);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(int s) {
+    switch (s) {
+        case SSM_OK: return "SSM_OK";
+        case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG";
+        case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
+        case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE";
+        case SSM_ERR_HIP: return "SSM_ERR_HIP";
+        default: return "SSM_ERR_UNKNOWN";
+    }
+}
+
+const char* ssm_last_error(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------------ scan
+size_t ssm_scan_workspace_size(int B, int L, int D, int N) {
+    if (B < 1 || L < 0 || D < 1 || !ssm::scan_supported_n(N)) return 0;
+    if (!product_ok({B, L, D, N})) return 0;
+    return ssm::scan_workspace_bytes(B, L, D, N);
+}
+
+int ssm_scan_fwd(int B, int L, int D, int N, int io,
+                 const void* x, const void* delta, const float* A,
+                 const void* Bm, const void* Cm, const float* Dskip,
+                 const void* z, const float* h0,
+                 void* y, float* h_final,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssm_scan_fwd";
+    if (B < 1 || D < 1 || L < 0 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1 and L >= 0");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (!ssm::scan_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64");
+    if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
+    if (!product_ok({B, L, D, N}) || !product_ok({B, L, D}, 1LL << 40))
+        return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if (!A) return fail(SSM_ERR_INVALID_ARG, fn, "A is NULL");
+    if (L > 0 && (!x || !delta || !Bm || !Cm || !y))
+        return fail(SSM_ERR_INVALID_ARG, fn, "x, delta, Bm, Cm and y are required");
+    const void* ptrs[] = {x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    const int es = io == SSM_BF16 ? 2 : 4;
+    const ssm::ScanPlan plan = ssm::scan_plan(B, L, D, N);
+    if ((long long)plan.Ls * D * es >= (1LL << 31))
+        return fail(SSM_ERR_UNSUPPORTED, fn, "one segment of [L, D] exceeds 2 GiB");
+    const size_t need = ssm::scan_workspace_bytes(B, L, D, N);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, fn, "workspace missing or smaller than ssm_scan_workspace_size()");
+    ssm::ScanArgs a{B, L, D, N, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace};
+    return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ------------------------------------------------------------------ SSD
+size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk) {
+    const int Q = chunk == 0 ? 256 : chunk;
+    if (B < 1 || L < 0 || H < 1 || P < 1 || N < 1 || Q < 1) return 0;
+    if (!product_ok({B, L, H, P}) || !product_ok({B, H, N, P})) return 0;
+    return ssm::ssd_workspace_bytes(B, L, H, P, N, Q);
+}
+
+int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
+                const void* x, const void* delta, const float* A,
+                const void* Bm, const void* Cm, const float* Dskip,
+                const void* z, const float* h0,
+                void* y, float* h_final,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssm_ssd_fwd";
+    if (B < 1 || H < 1 || P < 1 || N < 1 || L < 0 || chunk < 0)
+        return fail(SSM_ERR_INVALID_ARG, fn, "B, H, P, N must be >= 1, L >= 0, chunk >= 0");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    const int Q = chunk == 0 ? 256 : chunk;
+    const char* why = ssm::ssd_unsupported_reason(L, H, P, N, Q, io == SSM_BF16);
+    if (why[0] != '\0') return fail(SSM_ERR_UNSUPPORTED, fn, why);
+    if (!product_ok({B, L, H, P}, 1LL << 40) || !product_ok({B, H, N, P}, 1LL << 40))
+        return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if (!A) return fail(SSM_ERR_INVALID_ARG, fn, "A is NULL");
+    if (L > 0 && (!x || !delta || !Bm || !Cm || !y))
+        return fail(SSM_ERR_INVALID_ARG, fn, "x, delta, Bm, Cm and y are required");
+    const void* ptrs[] = {x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    const size_t need = ssm::ssd_workspace_bytes(B, L, H, P, N, Q);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, fn, "workspace missing or smaller than ssm_ssd_workspace_size()");
+    ssm::SsdArgs a{B, L, H, P, N, Q, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace};
+    return hip_status(ssm::launch_ssd_fwd(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ------------------------------------------------------------------ step
+int ssm_step(int B, int D, int N, int io,
+             float* state, const void* x, const void* delta, const float* A,
+             const void* Bm, const void* Cm, const float* Dskip, const void* z,
+             void* y, void* stream) {
+    const char* fn = "ssm_step";
+    if (B < 1 || D < 1 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (!ssm::step_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64");
+    if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
+    if (!product_ok({B, D, N}, 1LL << 40)) return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if (!state || !x || !delta || !A || !Bm || !Cm || !y)
+        return fail(SSM_ERR_INVALID_ARG, fn, "state, x, delta, A, Bm, Cm and y are required");
+    const void* ptrs[] = {state, x, delta, A, Bm, Cm, Dskip, z, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    ssm::StepArgs a{B, D, N, io == SSM_BF16, state, x, delta, A, Bm, Cm, Dskip, z, y};
+    return hip_status(ssm::launch_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the C ABI
+// in api.cpp validates arguments and then calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ssm {
+
+// ------------------------------------------------------------ Mamba-1 scan
+struct ScanArgs {
+    int B, L, D, N;
+    bool bf16;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    const float* h0;
+    void* y;
+    float* h_final;
+    void* ws;
+};
+
+// How the sequence is cut for the L-parallel scan: S segments of Ls steps
+// (the last one may be shorter). Depends only on the shape.
+struct ScanPlan {
+    int S;
+    int Ls;
+};
+
+bool scan_supported_n(int N);
+ScanPlan scan_plan(int B, int L, int D, int N);
+size_t scan_workspace_bytes(int B, int L, int D, int N);
+hipError_t launch_scan_fwd(const ScanArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------ decode step
+struct StepArgs {
+    int B, D, N;
+    bool bf16;
+    float* state;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    void* y;
+};
+
+bool step_supported_n(int N);
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------ SSD
+struct SsdArgs {
+    int B, L, H, P, N, Q;
+    bool bf16;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    const float* h0;
+    void* y;
+    float* h_final;
+    void* ws;
+};
+
+// Returns an empty string when the shape is supported, else the reason.
+const char* ssd_unsupported_reason(int L, int H, int P, int N, int Q, bool bf16);
+size_t ssd_workspace_bytes(int B, int L, int H, int P, int N, int Q);
+hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t stream);
+
+}  // namespace ssm

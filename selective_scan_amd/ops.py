@@ -1,0 +1,191 @@
+"""ctypes marshalling for the C ABI of ``libssm_scan.so`` (see include/ssm_scan.h).
+
+Argument checks here only concern the Python side (tensor device, dtype,
+contiguity, shapes); the library validates again before any HIP call and every
+non-OK status becomes an ``SsmError``.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm_scan.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+SSM_OK = 0
+
+_lib = None
+
+
+class SsmError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+
+
+def lib():
+    """The loaded ``libssm_scan.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m selective_scan_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, sz, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    L.ssm_abi_version.argtypes, L.ssm_abi_version.restype = [], i
+    L.ssm_status_string.argtypes, L.ssm_status_string.restype = [i], ctypes.c_char_p
+    L.ssm_last_error.argtypes, L.ssm_last_error.restype = [], ctypes.c_char_p
+    L.ssm_scan_workspace_size.argtypes, L.ssm_scan_workspace_size.restype = [i, i, i, i], sz
+    L.ssm_scan_fwd.argtypes = [i, i, i, i, i] + [vp] * 10 + [vp, sz, vp]
+    L.ssm_scan_fwd.restype = i
+    L.ssm_ssd_workspace_size.argtypes, L.ssm_ssd_workspace_size.restype = [i] * 6, sz
+    L.ssm_ssd_fwd.argtypes = [i] * 7 + [vp] * 10 + [vp, sz, vp]
+    L.ssm_ssd_fwd.restype = i
+    L.ssm_step.argtypes = [i, i, i, i] + [fp] + [vp] * 8 + [vp]
+    L.ssm_step.restype = i
+    _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ helpers
+def _io_code(t):
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    if t.dtype == torch.float32:
+        return SSM_F32
+    raise TypeError(f"io tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device, required=True):
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _raise(fn, status):
+    L = lib()
+    raise SsmError(fn, status, L.ssm_last_error().decode())
+
+
+# ------------------------------------------------------------------ Mamba-1
+def ssm_scan_workspace_size(B, L, D, N):
+    return int(lib().ssm_scan_workspace_size(B, L, D, N))
+
+
+def ssm_scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, y=None, h_final=None,
+                 workspace=None, stream=None, want_final_state=True):
+    """Mamba-1 selective scan. x, delta, z: [B, L, D]; Bm, Cm: [B, L, N] (bf16 or fp32);
+    A: [D, N], D: [D], h0: [B, D, N] fp32. Returns (y, h_final) (h_final None if not wanted)."""
+    Bb, L, Dd = x.shape
+    N = A.shape[1]
+    dev, io = x.device, x.dtype
+    _check(delta, "delta", (Bb, L, Dd), io, dev)
+    _check(A, "A", (Dd, N), torch.float32, dev)
+    _check(Bm, "Bm", (Bb, L, N), io, dev)
+    _check(Cm, "Cm", (Bb, L, N), io, dev)
+    _check(D, "D", (Dd,), torch.float32, dev, required=False)
+    _check(z, "z", (Bb, L, Dd), io, dev, required=False)
+    _check(h0, "h0", (Bb, Dd, N), torch.float32, dev, required=False)
+    _check(x, "x", (Bb, L, Dd), io, dev)
+    if y is None:
+        y = torch.empty((Bb, L, Dd), dtype=io, device=dev)
+    _check(y, "y", (Bb, L, Dd), io, dev)
+    if want_final_state and h_final is None:
+        h_final = torch.empty((Bb, Dd, N), dtype=torch.float32, device=dev)
+    _check(h_final, "h_final", (Bb, Dd, N), torch.float32, dev, required=False)
+    need = ssm_scan_workspace_size(Bb, L, Dd, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_scan_fwd(Bb, L, Dd, N, _io_code(x), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+                            _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final),
+                            _ptr(workspace), wbytes, _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_scan_fwd", st)
+    return y, h_final
+
+
+# ------------------------------------------------------------------ SSD
+def ssm_ssd_workspace_size(B, L, H, P, N, chunk=0):
+    return int(lib().ssm_ssd_workspace_size(B, L, H, P, N, chunk))
+
+
+def ssm_ssd_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, chunk=0, y=None,
+                h_final=None, workspace=None, stream=None, want_final_state=True):
+    """Mamba-2 SSD chunked scan. x, z: [B, L, H, P]; delta: [B, L, H]; Bm, Cm: [B, L, N];
+    A, D: [H] fp32; h0: [B, H, N, P] fp32. Returns (y, h_final)."""
+    Bb, L, H, P = x.shape
+    N = Bm.shape[2]
+    dev, io = x.device, x.dtype
+    _check(x, "x", (Bb, L, H, P), io, dev)
+    _check(delta, "delta", (Bb, L, H), io, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(Bm, "Bm", (Bb, L, N), io, dev)
+    _check(Cm, "Cm", (Bb, L, N), io, dev)
+    _check(D, "D", (H,), torch.float32, dev, required=False)
+    _check(z, "z", (Bb, L, H, P), io, dev, required=False)
+    _check(h0, "h0", (Bb, H, N, P), torch.float32, dev, required=False)
+    if y is None:
+        y = torch.empty((Bb, L, H, P), dtype=io, device=dev)
+    _check(y, "y", (Bb, L, H, P), io, dev)
+    if want_final_state and h_final is None:
+        h_final = torch.empty((Bb, H, N, P), dtype=torch.float32, device=dev)
+    _check(h_final, "h_final", (Bb, H, N, P), torch.float32, dev, required=False)
+    need = ssm_ssd_workspace_size(Bb, L, H, P, N, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_ssd_fwd(Bb, L, H, P, N, int(chunk), _io_code(x), _ptr(x), _ptr(delta), _ptr(A),
+                           _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final),
+                           _ptr(workspace), wbytes, _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_ssd_fwd", st)
+    return y, h_final
+
+
+# ------------------------------------------------------------------ decode
+def ssm_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=None):
+    """One decode step. state: [B, D, N] fp32 (updated in place); x, delta, z: [B, D];
+    Bm, Cm: [B, N]; A: [D, N]; D: [D]. Returns y [B, D]."""
+    Bb, Dd, N = state.shape
+    dev, io = x.device, x.dtype
+    _check(state, "state", (Bb, Dd, N), torch.float32, dev)
+    _check(x, "x", (Bb, Dd), io, dev)
+    _check(delta, "delta", (Bb, Dd), io, dev)
+    _check(A, "A", (Dd, N), torch.float32, dev)
+    _check(Bm, "Bm", (Bb, N), io, dev)
+    _check(Cm, "Cm", (Bb, N), io, dev)
+    _check(D, "D", (Dd,), torch.float32, dev, required=False)
+    _check(z, "z", (Bb, Dd), io, dev, required=False)
+    if y is None:
+        y = torch.empty((Bb, Dd), dtype=io, device=dev)
+    _check(y, "y", (Bb, Dd), io, dev)
+    st = lib().ssm_step(Bb, Dd, N, _io_code(x), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                        _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_step", st)
+    return y

@@ -76,7 +76,7 @@ def to_torch(a, device="cpu"):
     import torch
     if a is None:
         return None
-    a = np.ascontiguousarray(a)
+    a = np.require(a, requirements=["C", "W"])
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(a).to(device)
@@ -114,7 +114,7 @@ def scan_inputs(B, L, D, N, dtype=BF16, seed=0, with_D=True, with_z=True, with_h
     s = 1.0 / math.sqrt(N)
     out["Bm"] = store(_normal(seed, TID_B, (B, L, N)) * s, dtype)
     out["Cm"] = store(_normal(seed, TID_C, (B, L, N)) * s, dtype)
-    out["A"] = np.broadcast_to(-(np.arange(N, dtype=np.float64) + 1.0), (D, N)).astype(np.float32)
+    out["A"] = np.ascontiguousarray(np.broadcast_to(-(np.arange(N, dtype=np.float32) + 1.0), (D, N)))
     out["D"] = _normal(seed, TID_D, (D,)).astype(np.float32) if with_D else None
     out["h0"] = (0.1 * _normal(seed, TID_STATE0, (B, D, N))).astype(np.float32) if with_h0 else None
     out["dtype"] = dtype
@@ -149,7 +149,7 @@ def step_inputs(B, D, N, steps, dtype=BF16, seed=0, with_D=True, with_z=True):
     s = 1.0 / math.sqrt(N)
     out["Bm"] = store(_normal(seed, TID_B, (steps, B, N)) * s, dtype)
     out["Cm"] = store(_normal(seed, TID_C, (steps, B, N)) * s, dtype)
-    out["A"] = np.broadcast_to(-(np.arange(N, dtype=np.float64) + 1.0), (D, N)).astype(np.float32)
+    out["A"] = np.ascontiguousarray(np.broadcast_to(-(np.arange(N, dtype=np.float32) + 1.0), (D, N)))
     out["D"] = _normal(seed, TID_D, (D,)).astype(np.float32) if with_D else None
     out["dtype"] = dtype
     return out

@@ -1,0 +1,100 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects
+bad arguments before any HIP call (these run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_scan_amd as ssa
+from selective_scan_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+# fake, 16-byte aligned device addresses: validation failures never dereference them
+P = ctypes.c_void_p(0x10000)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("ssm_scan_fwd", "ssm_ssd_fwd", "ssm_step"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} is declared in include/ssm_scan.h but not exported"
+
+
+def test_version_and_status_strings():
+    L = ops.lib()
+    assert L.ssm_abi_version() == 1
+    assert L.ssm_status_string(0) == b"SSM_OK"
+    assert L.ssm_status_string(3) == b"SSM_ERR_WORKSPACE"
+    assert L.ssm_status_string(99) == b"SSM_ERR_UNKNOWN"
+
+
+def _scan(B=1, L=8, D=64, N=16, io=1, x=P, delta=P, A=P, Bm=P, Cm=P, Dk=None, z=None, h0=None,
+          y=P, hf=None, ws=None, wsb=0):
+    return ops.lib().ssm_scan_fwd(B, L, D, N, io, x, delta, A, Bm, Cm, Dk, z, h0, y, hf, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(D=0), 1), (dict(L=-1), 1), (dict(N=0), 1), (dict(io=7), 1),
+    (dict(N=12), 2), (dict(N=128), 2), (dict(B=70000), 2),
+    (dict(x=None), 1), (dict(A=None), 1), (dict(y=None), 1), (dict(Cm=None), 1),
+    (dict(x=ctypes.c_void_p(0x10004)), 1),
+])
+def test_scan_rejects_bad_arguments(kw, status):
+    assert _scan(**kw) == status
+    assert ops.lib().ssm_last_error().startswith(b"ssm_scan_fwd: ")
+
+
+def test_scan_workspace_checks():
+    need = ssa.ssm_scan_workspace_size(1, 4096, 1536, 16)
+    assert need > 0
+    assert _scan(L=4096, D=1536, ws=None, wsb=0) == 3
+    assert _scan(L=4096, D=1536, ws=P, wsb=need - 1) == 3
+    assert ssa.ssm_scan_workspace_size(1, 4096, 1536, 12) == 0
+    assert ssa.ssm_scan_workspace_size(1, 32, 64, 16) == 0  # a single segment needs none
+
+
+def test_step_rejects_bad_arguments():
+    L = ops.lib()
+    ok = dict(B=2, D=64, N=16, io=1)
+    def call(**kw):
+        a = dict(ok, state=P, x=P, delta=P, A=P, Bm=P, Cm=P, Dk=None, z=None, y=P)
+        a.update(kw)
+        return L.ssm_step(a["B"], a["D"], a["N"], a["io"], a["state"], a["x"], a["delta"], a["A"],
+                          a["Bm"], a["Cm"], a["Dk"], a["z"], a["y"], None)
+    assert call(B=0) == 1
+    assert call(N=5) == 2
+    assert call(state=None) == 1
+    assert call(y=ctypes.c_void_p(0x10008)) == 1
+    assert call(io=3) == 1
+
+
+def test_ssd_rejects_bad_arguments():
+    L = ops.lib()
+    def call(B=1, Lq=64, H=2, Pp=64, N=128, chunk=0, io=1, x=P):
+        return L.ssm_ssd_fwd(B, Lq, H, Pp, N, chunk, io, x, P, P, P, P, None, None, None, P, None,
+                             None, 0, None)
+    assert call(B=0) == 1
+    assert call(chunk=-1) == 1
+    assert call(io=9) == 1
+
+
+def test_python_binding_checks_tensors_before_calling():
+    import torch
+    x = torch.zeros(1, 4, 8)  # CPU tensors: the binding checks shapes/dtypes first
+    with pytest.raises(TypeError):
+        ssa.ssm_scan_fwd(x.to(torch.float64), x, torch.zeros(8, 16), torch.zeros(1, 4, 16),
+                         torch.zeros(1, 4, 16))

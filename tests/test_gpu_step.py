@@ -1,0 +1,75 @@
+"""GPU parity of ssm_step (recurrent decode) against the fp64 oracle, and the
+step == prefill relations on the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_scan_amd as ssa
+import ssm_inputs as si
+from gpu_util import DEV, gpu_scan, out_f64, storage
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_steps(w, steps):
+    """Chain `steps` GPU decode steps and the same oracle steps; compare every y and the state."""
+    st_g = torch.from_numpy(w["state0"]).to(DEV)
+    st_o = w["state0"].astype(np.float64)
+    A = torch.from_numpy(w["A"]).to(DEV)
+    Dk = None if w["D"] is None else torch.from_numpy(w["D"]).to(DEV)
+    Af, Df = w["A"].astype(np.float64), None if w["D"] is None else w["D"].astype(np.float64)
+    for s in range(steps):
+        tok = {k: (None if w[k] is None else w[k][s]) for k in ("x", "delta", "z", "Bm", "Cm")}
+        td = {k: (None if v is None else si.to_torch(np.ascontiguousarray(v), DEV)) for k, v in tok.items()}
+        y = ssa.ssm_step(st_g, td["x"], td["delta"], A, td["Bm"], td["Cm"], D=Dk, z=td["z"])
+        yo, st_o = oracle.step(st_o, si.to_f64(tok["x"]), si.to_f64(tok["delta"]), Af,
+                               si.to_f64(tok["Bm"]), si.to_f64(tok["Cm"]), D=Df, z=si.to_f64(tok["z"]))
+        torch.cuda.synchronize()
+        compare(out_f64(y), yo, storage(w), what=f"step {s} y")
+    compare(st_g.cpu().numpy(), st_o, "f32", what="state after steps")
+
+
+@pytest.mark.parametrize("case", [
+    (1, 64, 16, si.BF16, True, True), (3, 100, 4, si.F32, False, False),
+    (2, 1000, 8, si.BF16, True, False), (4, 300, 32, si.F32, False, True),
+    (2, 130, 64, si.BF16, True, True), (1, 1, 16, si.F32, True, True),
+], ids=lambda c: "B{}_D{}_N{}_{}_D{}z{}".format(*c))
+def test_step_small(case):
+    B, D, N, dt, wd, wz = case
+    print(f"[step small] {case}", flush=True)
+    w = si.step_inputs(B, D, N, steps=12, dtype=dt, seed=3, with_D=wd, with_z=wz)
+    _run_steps(w, 12)
+
+
+def test_step_config_bf16_B64_D3072_N16():
+    print("[step] bf16 B64 D3072 N16, 25 chained steps", flush=True)
+    w = si.step_inputs(64, 3072, 16, steps=25, dtype=si.BF16, seed=0)
+    _run_steps(w, 25)
+
+
+def test_step_equals_prefill_of_one_on_gpu():
+    w = si.scan_inputs(2, 1, 320, 16, dtype=si.BF16, seed=8, with_h0=True)
+    y, hf = gpu_scan(w)
+    st = torch.from_numpy(w["h0"]).to(DEV)
+    t = {k: si.to_torch(np.ascontiguousarray(w[k][:, 0]), DEV) for k in ("x", "delta", "z", "Bm", "Cm")}
+    ys = ssa.ssm_step(st, t["x"], t["delta"], torch.from_numpy(w["A"]).to(DEV), t["Bm"], t["Cm"],
+                      D=torch.from_numpy(w["D"]).to(DEV), z=t["z"])
+    torch.cuda.synchronize()
+    compare(out_f64(ys), out_f64(y)[:, 0], "bf16", what="step vs L=1 y")
+    compare(st.cpu().numpy(), out_f64(hf), "f32", what="step vs L=1 state")
+
+
+def test_prefill_then_step_equals_longer_prefill_on_gpu():
+    L = 777
+    w = si.scan_inputs(2, L + 1, 256, 16, dtype=si.BF16, seed=9, with_h0=True)
+    yfull, hfull = gpu_scan(w)
+    cut = {k: np.ascontiguousarray(w[k][:, :L]) for k in ("x", "delta", "z", "Bm", "Cm")}
+    _, h = gpu_scan(dict(w, **cut))
+    t = {k: si.to_torch(np.ascontiguousarray(w[k][:, L]), DEV) for k in ("x", "delta", "z", "Bm", "Cm")}
+    ys = ssa.ssm_step(h, t["x"], t["delta"], torch.from_numpy(w["A"]).to(DEV), t["Bm"], t["Cm"],
+                      D=torch.from_numpy(w["D"]).to(DEV), z=t["z"])
+    torch.cuda.synchronize()
+    compare(out_f64(ys), out_f64(yfull)[:, L], "bf16", what="prefill+step y")
+    compare(h.cpu().numpy(), out_f64(hfull), "f32", what="prefill+step state")
