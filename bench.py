@@ -1,0 +1,337 @@
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu] [--no-other]
+
+A step is one ssm_scan_fwd call over one batch of synthetic input already
+resident in HBM (bf16 I/O, B=1, L=4096, D=1536, N=16 by default). Inputs rotate
+over several independent batches whose total size exceeds the 256 MB
+last-level (MALL) cache, so every step streams its batch from HBM.
+
+Prints ONE JSON line: throughput in state updates/s (B*L*D*N per step), the
+roofline of the dominant kernel (timed live with HIP events recorded around
+each kernel launch on the launch stream), and the fp64 oracle timed on the
+host cores on a bounded sample of the same workload. ``other_paths`` holds the
+same measurements for the long-sequence scan, the SSD and the decode step.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks and unit counts
+HBM_PEAK_GBS = 8000.0
+CUS, LANES, CLOCK_GHZ = 256, 64, 2.4
+LANE_SLOTS_PER_S = CUS * LANES * CLOCK_GHZ * 1e9      # one fp32 VALU op per lane per clock
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+# per state update the minimal instruction mix: v_mul (Delta*A), v_exp_f32 (half
+# rate: 2 lane-slots), v_mul (u*B), v_fma (state), v_fma (C.h) -> 6 lane-slots
+SLOTS_PER_UPDATE = 6.0
+
+
+def hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+class KernelTimer:
+    """HIP events recorded by the library around every kernel launch it makes."""
+
+    def __init__(self, n):
+        self.h = hip()
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev[i] = e
+        self.n = n
+
+    def start(self, lib):
+        lib.ssm_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        lib.ssm_profile_events(ctypes.cast(self.ev, ctypes.c_void_p), self.n)
+
+    def stop(self, lib):
+        return lib.ssm_profile_events(None, 0)
+
+    def elapsed_ms(self, i, j):
+        self.h.hipEventSynchronize(self.ev[j])
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j]) == 0
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.h.hipEventDestroy(self.ev[i])
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ scan
+def scan_setup(wl, dev, max_sets=16):
+    import torch
+    import ssm_inputs as si
+    import selective_scan_amd as ssa
+    B, L, D, N = wl["B"], wl["L"], wl["D"], wl["N"]
+    es = 2 if wl["dtype"] == si.BF16 else 4
+    set_bytes = 4 * B * L * D * es + 2 * B * L * N * es
+    R = max(1, min(max_sets, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for r in range(R):
+        w = si.scan_inputs(B, L, D, N, dtype=wl["dtype"], seed=r)
+        t = {k: si.to_torch(w[k], dev) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D")}
+        t["y"] = torch.empty_like(t["x"])
+        t["hf"] = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+        sets.append(t)
+        if r == 0:
+            w0 = w
+    ws_bytes = ssa.ssm_scan_workspace_size(B, L, D, N)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    return sets, ws, w0, set_bytes
+
+
+def scan_call(t, ws):
+    import selective_scan_amd as ssa
+    ssa.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], D=t["D"], z=t["z"],
+                     y=t["y"], h_final=t["hf"], workspace=ws)
+
+
+def scan_alg_bytes(wl):
+    """Algorithmic HBM bytes per call: read x, Delta, z, B, C, A, D; write y, h_final."""
+    B, L, D, N = wl["B"], wl["L"], wl["D"], wl["N"]
+    es = 2 if wl["dtype"] == "bf16" else 4
+    return 4 * B * L * D * es + 2 * B * L * N * es + (D * N + D) * 4 + B * D * N * 4
+
+
+def count_kernels(call):
+    """Kernels one call launches: the library records one event per launch plus one."""
+    import selective_scan_amd as ssa
+    lib = ssa.ops.lib()
+    kt = KernelTimer(64)
+    kt.start(lib)
+    call()
+    used = kt.stop(lib)
+    sync()
+    kt.close()
+    return used - 1
+
+
+def time_calls(call, sets, steps, warmup, n_kernels):
+    """Time `steps` calls (rotating over `sets`) with outer events, and every
+    kernel of every call with the library's profiling events."""
+    import torch
+    import selective_scan_amd as ssa
+    lib = ssa.ops.lib()
+    for i in range(warmup):
+        call(sets[i % len(sets)])
+    sync()
+    kt = KernelTimer(steps * (n_kernels + 1))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    sync()
+    kt.start(lib)
+    t0.record()
+    for i in range(steps):
+        call(sets[(warmup + i) % len(sets)])
+    t1.record()
+    used = kt.stop(lib)
+    sync()
+    total_ms = t0.elapsed_time(t1)
+    per_k = n_kernels + 1
+    assert used == steps * per_k, f"recorded {used} events, expected {steps * per_k}"
+    ker = np.array([[kt.elapsed_ms(s * per_k + k, s * per_k + k + 1) for k in range(n_kernels)]
+                    for s in range(steps)])
+    kt.close()
+    return total_ms, ker
+
+
+def scan_bench(name, wl, steps, warmup, dev):
+    sets, ws, w0, set_bytes = scan_setup(wl, dev)
+    nk = count_kernels(lambda: scan_call(sets[0], ws))
+    total_ms, ker = time_calls(lambda t: scan_call(t, ws), sets, steps, warmup, nk)
+    upd = wl["B"] * wl["L"] * wl["D"] * wl["N"]
+    ms = total_ms / steps
+    kmean = ker.mean(axis=0)
+    dom = int(np.argmax(kmean))
+    alg = scan_alg_bytes(wl)
+    res = dict(
+        workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3),
+        tokens_per_s=wl["B"] * wl["L"] / (ms * 1e-3),
+        hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        kernel_ms=[float(v) for v in kmean], dominant_kernel=dom, sets=len(sets),
+        set_mb=set_bytes / 1e6,
+    )
+    tdom = kmean[dom] * 1e-3
+    achieved = SLOTS_PER_UPDATE * upd / tdom / 1e12
+    peak = LANE_SLOTS_PER_S / 1e12
+    res["roofline"] = dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s",
+                           frac=achieved / peak, traffic=None,
+                           kernel="segment_kernel (final pass)" if nk > 1 else "segment_kernel")
+    res["hbm_roofline_dominant"] = dict(achieved=alg / tdom / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                                        frac=alg / tdom / 1e9 / HBM_PEAK_GBS)
+    return res, w0
+
+
+def scan_cpu_baseline(wl, w0, budget_s=15.0):
+    """The fp64 oracle (as it stands) on the host cores: whole sequences of as many
+    channels as fit in about `budget_s` seconds (all of them when they fit)."""
+    import oracle
+    import ssm_inputs as si
+    o = oracle.get()
+    o.set_threads(len(os.sched_getaffinity(0)))
+    T = o.get_threads()
+    f = {k: si.to_f64(w0[k]) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D")}
+    B, L, D, N = wl["B"], wl["L"], wl["D"], wl["N"]
+
+    def run(dsel):
+        sl = slice(0, dsel)
+        c = lambda a: np.ascontiguousarray(a[:, :, sl])
+        t0 = time.perf_counter()
+        o.scan(c(f["x"]), c(f["delta"]), np.ascontiguousarray(f["A"][sl]), f["Bm"], f["Cm"],
+               D=np.ascontiguousarray(f["D"][sl]), z=c(f["z"]))
+        return time.perf_counter() - t0
+
+    probe = run(min(D, T))                       # one channel per thread
+    dsel = int(min(D, max(T, budget_s / max(probe, 1e-6) * T * 0.7)))
+    reps, els = 0, []
+    while reps < 5 and (reps == 0 or sum(els) < 2.0):
+        els.append(run(dsel))
+        reps += 1
+    el = float(np.median(els))
+    upd = B * L * dsel * N
+    return dict(value=upd / el, unit="state updates/s", cores=T, kind="oracle",
+                sample=f"fp64 oracle (sequential recurrence) on B={B}, L={L}, {dsel} of {D} channels, "
+                       f"N={N}: {upd / 1e6:.1f} M updates, median of {reps} run(s), {el:.3f} s each")
+
+
+# ------------------------------------------------------------------ decode
+def step_bench(wl, dev, reps=3):
+    import torch
+    import selective_scan_amd as ssa
+    import ssm_inputs as si
+    B, D, N, steps = wl["B"], wl["D"], wl["N"], wl["steps"]
+    w = si.step_inputs(B, D, N, steps=steps, dtype=wl["dtype"], seed=0)
+    tok = {k: si.to_torch(w[k], dev) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A = torch.from_numpy(w["A"]).to(dev)
+    Dk = torch.from_numpy(w["D"]).to(dev)
+    st0 = torch.from_numpy(w["state0"]).to(dev)
+    st = st0.clone()
+    y = torch.empty((steps, B, D), dtype=tok["x"].dtype, device=dev)
+
+    def run():
+        for s in range(steps):
+            ssa.ssm_step(st, tok["x"][s], tok["delta"][s], A, tok["Bm"][s], tok["Cm"][s], D=Dk,
+                         z=tok["z"][s], y=y[s])
+
+    run()
+    sync()
+    times = []
+    for _ in range(reps):
+        st.copy_(st0)
+        sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        sync()
+        times.append(e0.elapsed_time(e1))
+    # HIP-graph replay of the same 1000 launches
+    g = torch.cuda.CUDAGraph()
+    st.copy_(st0)
+    sync()
+    s_ = torch.cuda.Stream()
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            run()
+    sync()
+    gtimes = []
+    for _ in range(reps):
+        st.copy_(st0)
+        sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        sync()
+        gtimes.append(e0.elapsed_time(e1))
+    es = 2 if wl["dtype"] == "bf16" else 4
+    alg = 2 * B * D * N * 4 + 4 * B * D * es + 2 * B * N * es + (D * N + D) * 4
+    med = float(np.median(times)) / steps
+    gmed = float(np.median(gtimes)) / steps
+    return dict(workload="step_bf16_B64_D3072_N16_x1000", ms_per_step_stream=med,
+                ms_per_step_graph=gmed, updates_per_s_graph=B * D * N / (gmed * 1e-3),
+                tokens_per_s_graph=B / (gmed * 1e-3),
+                hbm_gbs_graph=alg / (gmed * 1e-3) / 1e9,
+                note="state (12.6 MB) stays resident in the 256 MB MALL across in-place steps")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="scan_bf16_B1_L4096_D1536_N16")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-other", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the selective scan here has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import ssm_inputs as si
+    dev = torch.device("cuda:0")
+    wl = si.WORKLOADS[args.workload]
+    assert wl["kind"] == "scan", "the headline bench line is a scan workload"
+    res, w0 = scan_bench(args.workload, wl, args.steps, args.warmup, dev)
+    out = {
+        "metric": "selective-scan state updates/s (B*L*D*N) + % of MI355X HBM roofline",
+        "value": res["updates_per_s"],
+        "unit": "state updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl["dtype"] == "f32" else "f32 (bf16 I/O)",
+        "data": "synthetic (seeded; distributions of the pages' workloads)",
+        "config": {"workload": args.workload, "B": wl["B"], "L": wl["L"], "D": wl["D"],
+                   "N": wl["N"], "io": wl["dtype"], "rotating_input_sets": res["sets"]},
+        "tokens_per_s": res["tokens_per_s"],
+        "hbm_gbs": res["hbm_gbs"],
+        "hbm_frac": res["hbm_frac"],
+        "kernel_ms": res["kernel_ms"],
+        "roofline": res["roofline"],
+        "hbm_roofline_dominant": res["hbm_roofline_dominant"],
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = scan_cpu_baseline(wl, w0)
+    if not args.no_other:
+        other = {}
+        r2, _ = scan_bench("scan_bf16_B8_L32768_D512_N16", si.WORKLOADS["scan_bf16_B8_L32768_D512_N16"],
+                           steps=5, warmup=2, dev=dev)
+        other["scan_long"] = {k: r2[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
+                                                   "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
+        other["decode"] = step_bench(si.WORKLOADS["step_bf16_B64_D3072_N16_x1000"], dev)
+        out["other_paths"] = other
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

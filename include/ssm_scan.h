@@ -72,6 +72,16 @@ const char* ssm_status_string(int status);
 /* Detail of the calling thread's last non-OK status ("" if none). */
 const char* ssm_last_error(void);
 
+/* Kernel-level timing without a profiler (diagnostic; for benchmarks).
+ * After ssm_profile_events(events, n) with n > 0, every entry point called from
+ * this thread records, on its stream, one event right before each kernel it
+ * launches and one after its last launch, taking events[0], events[1], ... in
+ * order (each a hipEvent_t created by the caller); recording stops when the n
+ * events are used up. ssm_profile_events(NULL, 0) switches recording off.
+ * Returns the number of events recorded since the previous call. Per thread;
+ * the library never creates, synchronises or destroys the events. */
+int ssm_profile_events(void* const* events, int n);
+
 /* ---------------------------------------------------------------------------
  * ssm_scan_fwd -- Mamba-1 selective scan (prefill).
  *

@@ -15,6 +15,13 @@ namespace {
 
 thread_local std::string g_last_error;
 
+struct ProfileEvents {
+    void* const* ev = nullptr;
+    int n = 0;
+    int used = 0;
+};
+thread_local ProfileEvents g_prof;
+
 int fail(int status, const char* fn, const char* what) {
     g_last_error = std::string(fn) + ": " + what;
     return status;
@@ -47,7 +54,23 @@ int hip_status(hipError_t e, const char* fn) {
 
 }  // namespace
 
+namespace ssm {
+void profile_mark(hipStream_t stream) {
+    if (g_prof.ev == nullptr || g_prof.used >= g_prof.n) return;
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.ev[g_prof.used]), stream);
+    ++g_prof.used;
+}
+}  // namespace ssm
+
 extern "C" {
+
+int ssm_profile_events(void* const* events, int n) {
+    const int used = g_prof.used;
+    g_prof.ev = (events != nullptr && n > 0) ? events : nullptr;
+    g_prof.n = g_prof.ev ? n : 0;
+    g_prof.used = 0;
+    return used;
+}
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 

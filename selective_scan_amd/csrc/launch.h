@@ -7,6 +7,10 @@
 
 namespace ssm {
 
+// Records the next caller-provided timing event on `stream` if the calling
+// thread enabled ssm_profile_events(); otherwise does nothing.
+void profile_mark(hipStream_t stream);
+
 // ------------------------------------------------------------ Mamba-1 scan
 struct ScanArgs {
     int B, L, D, N;

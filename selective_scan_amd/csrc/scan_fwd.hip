@@ -11,14 +11,20 @@
 // Per state update the hot loop issues v_mul (Delta*A), v_exp_f32, v_mul (u*B),
 // v_fma (state) and v_fma (C.h).
 //
-// L-parallelism. B*D channels alone cannot fill 256 CUs, so the sequence is cut
-// into S segments and scanned in three launches:
-//   1. segment_aggregate: every segment but the last runs the recurrence from a
-//      zero state and stores its end state H_s and sum(Delta) of the segment;
-//   2. carry_combine: per (b, n, d), h_in(s+1) = exp(A sum(Delta_s)) h_in(s) + H_s
-//      sequentially over segments (tiny), written over H_s;
-//   3. segment_final: every segment runs the recurrence again from its true
-//      carried-in state and writes y (and h_final for the last segment).
+// L-parallelism. B*D channels alone cannot fill 256 CUs, so each chain of 64
+// channels is cut into S segments of Ls steps; W consecutive segments form a
+// group, handled by one workgroup of W waves (one wave per segment). Two launches:
+//   1. segment_aggregate: every wave runs its segment from a zero state (end
+//      state H_s, decay P_s = exp(A sum Delta)); the group's waves then form, in
+//      LDS, each segment's exclusive in-group prefix E_s (and the in-group prefix
+//      of sum Delta), and the last wave the group's own aggregate (GP_g, GH_g).
+//   2. segment_final: each workgroup folds the aggregates of all earlier groups
+//      (waves fold disjoint ranges in parallel, then combine in LDS) into the
+//      state entering its group, forms each segment's carried-in state
+//      h_in = exp(A * prefix sum Delta) h_group + E_s, and runs the recurrence
+//      again from it, writing y (and h_final at the end of the sequence).
+// (P1, H1) then (P2, H2) compose to (P2 P1, P2 H1 + H2): the recurrence is an
+// affine map of the state, so segments compose like affine maps.
 #include "common.h"
 #include "launch.h"
 
@@ -27,165 +33,333 @@
 namespace ssm {
 namespace {
 
-constexpr int kPrefetch = 4;
+constexpr int kPrefetch = 8;
+constexpr int kTargetWaves = 4096;
+constexpr int kMinSegment = 32;
 
 struct Geom {
-    int S, Ls;
-    int threads;  // lanes per workgroup (multiple of 64, <= 256)
+    int Ls;  // steps per segment
+    int S;   // segments per chain
+    int W;   // segments (waves) per workgroup
+    int G;   // groups per chain
 };
 
-__host__ __device__ inline size_t ws_h_elems(int B, int S, int N, int D) {
-    return (size_t)B * (S - 1) * N * D;
+inline int max_group(int N) { return std::max(1, std::min(8, 128 / N)); }
+
+Geom geom(int B, int L, int D, int N) {
+    Geom g{1, 0, 1, 0};
+    if (L <= 0) return g;
+    const long chains = (long)B * ((D + 63) / 64);
+    const long s_target = (kTargetWaves + chains - 1) / chains;
+    long Ls = std::max<long>(kMinSegment, (L + s_target - 1) / s_target);
+    Ls = std::min<long>(Ls, L);
+    g.Ls = (int)Ls;
+    g.S = (int)((L + Ls - 1) / Ls);
+    g.W = std::min(max_group(N), g.S);
+    g.G = (g.S + g.W - 1) / g.W;
+    return g;
 }
 
-template <int N, bool BF16, bool FINAL, bool HAS_Z, bool HAS_D>
-__global__ void __launch_bounds__(256)
-segment_kernel(ScanArgs a, int S, int Ls) {
-    constexpr uint32_t es = BF16 ? 2 : 4;
-    const int seg = blockIdx.x;
-    const int b = blockIdx.z;
-    const int d = blockIdx.y * blockDim.x + threadIdx.x;
-    const int D = a.D, L = a.L;
-    const int dc = d < D ? d : D - 1;   // lanes past D mirror the last channel, never store
-    const int t0 = seg * Ls;
-    const int len = min(Ls, L - t0);
-    const size_t row0 = (size_t)b * L + t0;  // first (b, t) row of this segment
-    const uint32_t seg_bytes = (uint32_t)len * (uint32_t)D * es;
+// workspace layout (floats), all with the channel index fastest:
+//   E  [B][S][N][D]   exclusive in-group prefix state of each segment
+//   CS [B][S][D]      in-group prefix of sum(Delta) before each segment
+//   GH [B][G-1][N][D] aggregate end state of each group (from zero)
+//   GP [B][G-1][N][D] aggregate decay of each group
+struct WsLayout {
+    size_t E, CS, GH, GP, total;
+};
 
-    const char* xb = static_cast<const char*>(a.x) + row0 * D * es;
-    const char* db = static_cast<const char*>(a.delta) + row0 * D * es;
-    const auto rx = make_rsrc(xb, seg_bytes);
-    const auto rd = make_rsrc(db, seg_bytes);
-    // z and y descriptors (unused when not FINAL / no gate: they then point at x)
-    const auto rz = make_rsrc((FINAL && HAS_Z) ? static_cast<const char*>(a.z) + row0 * D * es : xb,
-                              seg_bytes);
-    const auto ry = make_rsrc(FINAL ? static_cast<const char*>(a.y) + row0 * D * es : xb, seg_bytes);
-    const uint32_t voff = (uint32_t)dc * es;
-    const uint32_t rstride = (uint32_t)D * es;
+__host__ __device__ inline WsLayout ws_layout(int B, int D, int N, int S, int G) {
+    WsLayout w;
+    const size_t g1 = G > 1 ? (size_t)(G - 1) : 0;
+    w.E = 0;
+    w.CS = w.E + (size_t)B * S * N * D;
+    w.GH = w.CS + (size_t)B * S * D;
+    w.GP = w.GH + (size_t)B * g1 * N * D;
+    w.total = w.GP + (size_t)B * g1 * N * D;
+    return w;
+}
+
+// Uniform rows of B or C for one time step, kept packed until use.
+template <int N, bool BF16>
+struct Row {
+    static constexpr int K = BF16 ? N / 2 : N;
+    uint32_t v[K];
+    __device__ __forceinline__ void load(const void* base, long row) {
+        cu32* p = (cu32*)(base) + row * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = p[k];
+    }
+    __device__ __forceinline__ float at(int n) const {
+        if constexpr (BF16) return (n & 1) ? bf16_hi(v[n >> 1]) : bf16_lo(v[n >> 1]);
+        else return __uint_as_float(v[n]);
+    }
+};
+
+// Raw element of an io tensor (bf16 bits or fp32 bits); widened only at use, so a
+// prefetched load is not waited for until the step that consumes it.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float widen(uint32_t v) {
+    if constexpr (BF16) return __uint_as_float(v << 16);
+    else return __uint_as_float(v);
+}
+
+// One wave's segment of the recurrence. Construction issues the first loads
+// (kPrefetch steps of x, Delta[, z] and the first B[, C] rows), so a caller can
+// start them before other prologue work; run() then walks the segment.
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL>
+struct Segment {
+    static constexpr uint32_t es = BF16 ? 2 : 4;
+    static constexpr bool kZ = FINAL && HAS_Z;
+    __amdgpu_buffer_rsrc_t rx, rd, rz, ry;
+    uint32_t voff, rstride;
+    const void* Bbase;
+    const void* Cbase;
+    int len;
+    uint32_t dq[kPrefetch], xq[kPrefetch], zq[kPrefetch];
+    Row<N, BF16> Bn, Cn;
+
+    __device__ __forceinline__ Segment(const ScanArgs& a, int b, int dc, int t0, int len_) : len(len_) {
+        const size_t row0 = (size_t)b * a.L + t0;
+        const uint32_t bytes = (uint32_t)len * (uint32_t)a.D * es;
+        const char* xb = static_cast<const char*>(a.x) + row0 * a.D * es;
+        rx = make_rsrc(xb, bytes);
+        rd = make_rsrc(static_cast<const char*>(a.delta) + row0 * a.D * es, bytes);
+        rz = make_rsrc(kZ ? static_cast<const char*>(a.z) + row0 * a.D * es : xb, bytes);
+        ry = make_rsrc(FINAL ? static_cast<const char*>(a.y) + row0 * a.D * es : xb, bytes);
+        voff = (uint32_t)dc * es;
+        rstride = (uint32_t)a.D * es;
+        Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
+        Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) {
+            const uint32_t so = (uint32_t)min(k, len - 1) * rstride;
+            dq[k] = load_raw<BF16>(rd, voff, so);
+            xq[k] = load_raw<BF16>(rx, voff, so);
+            zq[k] = kZ ? load_raw<BF16>(rz, voff, so) : 0u;
+        }
+        Bn.load(Bbase, 0);
+        if constexpr (FINAL) Cn.load(Cbase, 0);
+    }
+
+    // one time step t from ring slot k; RELOAD: refill the slot with step t + kPrefetch
+    template <bool RELOAD>
+    __device__ __forceinline__ void step(int t, int k, const float (&A2)[N], float (&h)[N], float Dv,
+                                         bool store, float& sumd) {
+        const float dv = widen<BF16>(dq[k]), xv = widen<BF16>(xq[k]);
+        const float zv = kZ ? widen<BF16>(zq[k]) : 0.0f;
+        if constexpr (RELOAD) {
+            const uint32_t so = (uint32_t)min(t + kPrefetch, len - 1) * rstride;
+            dq[k] = load_raw<BF16>(rd, voff, so);
+            xq[k] = load_raw<BF16>(rx, voff, so);
+            if constexpr (kZ) zq[k] = load_raw<BF16>(rz, voff, so);
+        }
+        const Row<N, BF16> Bt = Bn;
+        Row<N, BF16> Ct;
+        if constexpr (FINAL) Ct = Cn;
+        const int tn = min(t + 1, len - 1);
+        Bn.load(Bbase, tn);
+        if constexpr (FINAL) Cn.load(Cbase, tn);
+        const float u = dv * xv;
+        if constexpr (FINAL) {
+            float y0 = 0.0f, y1 = 0.0f;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float ab = exp2_fast(dv * A2[n]);
+                h[n] = __builtin_fmaf(ab, h[n], u * Bt.at(n));
+                if (n & 1) y1 = __builtin_fmaf(Ct.at(n), h[n], y1);
+                else y0 = __builtin_fmaf(Ct.at(n), h[n], y0);
+            }
+            float v = y0 + y1;
+            if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
+            if constexpr (HAS_Z) v *= silu(zv);
+            if (store) store_io<BF16>(ry, voff, (uint32_t)t * rstride, v);
+        } else {
+            sumd += dv;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float ab = exp2_fast(dv * A2[n]);
+                h[n] = __builtin_fmaf(ab, h[n], u * Bt.at(n));
+            }
+        }
+    }
+
+    // the whole segment from state h: full blocks of kPrefetch steps with a
+    // static ring slot per step, then the tail straight from the ring.
+    __device__ __forceinline__ void run(const float (&A2)[N], float (&h)[N], float Dv, bool store,
+                                        float& sumd) {
+        int t = 0;
+        for (; t + kPrefetch <= len; t += kPrefetch) {
+#pragma unroll
+            for (int k = 0; k < kPrefetch; ++k) step<true>(t + k, k, A2, h, Dv, store, sumd);
+        }
+#pragma unroll
+        for (int k = 0; k < kPrefetch - 1; ++k)
+            if (t + k < len) step<false>(t + k, k, A2, h, Dv, store, sumd);
+    }
+};
+
+template <int N, bool BF16>
+__global__ void __launch_bounds__(512)
+segment_aggregate(ScanArgs a, Geom g) {
+    extern __shared__ float lds[];
+    const int W = g.W;
+    // the wave index is uniform across the wave: say so, so that everything derived
+    // from it (segment, descriptors, offsets) lives in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.x, b = blockIdx.z;
+    const int D = a.D;
+    const int d = blockIdx.y * 64 + lane;
+    const int dc = d < D ? d : D - 1;
+    const int s = grp * W + wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
 
     float A2[N], h[N];
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
-
-    float* wsH = static_cast<float*>(a.ws);
-    float* wsSd = wsH + ws_h_elems(a.B, S, N, D);
-    if (FINAL && seg > 0) {
-        const float* hin = wsH + (((size_t)b * (S - 1) + (seg - 1)) * N) * D + dc;
-#pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = hin[(size_t)n * D];
-    } else if (FINAL && a.h0 != nullptr) {
-        const float* hp = a.h0 + ((size_t)b * D + dc) * N;
-#pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = hp[n];
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = 0.0f;
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+        h[n] = 0.0f;
     }
-    float Dv = 0.0f;
-    if constexpr (FINAL && HAS_D) Dv = a.Dskip[dc];
-
-    const void* Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
-    const void* Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
-
-    // prefetch ring of kPrefetch steps (steps past the end re-read the last row)
-    float dq[kPrefetch], xq[kPrefetch], zq[kPrefetch];
-#pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-        const uint32_t so = (uint32_t)min(k, len - 1) * rstride;
-        dq[k] = load_io<BF16>(rd, voff, so);
-        xq[k] = load_io<BF16>(rx, voff, so);
-        if constexpr (FINAL && HAS_Z) zq[k] = load_io<BF16>(rz, voff, so);
-        else zq[k] = 0.0f;
-    }
-
     float sumd = 0.0f;
-    for (int tb = 0; tb < len; tb += kPrefetch) {
-#pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) {
-            const int t = tb + k;
-            if (t >= len) break;
-            const float dv = dq[k], xv = xq[k], zv = zq[k];
-            {
-                const uint32_t so = (uint32_t)min(t + kPrefetch, len - 1) * rstride;
-                dq[k] = load_io<BF16>(rd, voff, so);
-                xq[k] = load_io<BF16>(rx, voff, so);
-                if constexpr (FINAL && HAS_Z) zq[k] = load_io<BF16>(rz, voff, so);
-            }
-            float Bt[N];
-            load_uniform_row<N, BF16>(Bbase, t, Bt);
-            const float u = dv * xv;
-            if constexpr (FINAL) {
-                float Ct[N];
-                load_uniform_row<N, BF16>(Cbase, t, Ct);
-                float y0 = 0.0f, y1 = 0.0f;
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float ab = exp2_fast(dv * A2[n]);
-                    h[n] = __builtin_fmaf(ab, h[n], u * Bt[n]);
-                    if (n & 1) y1 = __builtin_fmaf(Ct[n], h[n], y1);
-                    else y0 = __builtin_fmaf(Ct[n], h[n], y0);
-                }
-                float v = y0 + y1;
-                if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
-                if constexpr (HAS_Z) v *= silu(zv);
-                if (d < D) store_io<BF16>(ry, voff, (uint32_t)t * rstride, v);
-            } else {
-                sumd += dv;
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float ab = exp2_fast(dv * A2[n]);
-                    h[n] = __builtin_fmaf(ab, h[n], u * Bt[n]);
-                }
-            }
-        }
+    if (len > 0) {
+        Segment<N, BF16, false, false, false> seg(a, b, dc, t0, len);
+        seg.run(A2, h, 0.0f, false, sumd);
     }
+    // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]; a segment past L is the identity (1, 0).
+    float* sP = lds;
+    float* sH = sP + W * N * 64;
+    float* sS = sH + W * N * 64;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        sP[(wave * N + n) * 64 + lane] = exp2_fast(A2[n] * sumd);
+        sH[(wave * N + n) * 64 + lane] = h[n];
+    }
+    sS[wave * 64 + lane] = sumd;
+    __syncthreads();
 
-    if (d >= D) return;
-    if constexpr (FINAL) {
-        if (seg == S - 1 && a.h_final != nullptr) {
-            float* hp = a.h_final + ((size_t)b * D + d) * N;
+    float E[N];
 #pragma unroll
-            for (int n = 0; n < N; ++n) hp[n] = h[n];
+    for (int n = 0; n < N; ++n) E[n] = 0.0f;
+    float cs = 0.0f;
+    for (int j = 0; j < wave; ++j) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            E[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], E[n], sH[(j * N + n) * 64 + lane]);
+        cs += sS[j * 64 + lane];
+    }
+    if (d >= D || s >= g.S) return;
+    const WsLayout wl = ws_layout(a.B, D, N, g.S, g.G);
+    float* ws = static_cast<float*>(a.ws);
+    float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + d;
+#pragma unroll
+    for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
+    ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+    // the group's own aggregate, needed by later groups
+    const bool last_in_group = (wave == W - 1) || (s == g.S - 1);
+    if (last_in_group && grp < g.G - 1) {
+        float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + grp) * N * D + d;
+        float* GP = ws + wl.GP + ((size_t)b * (g.G - 1) + grp) * N * D + d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            GH[(size_t)n * D] = __builtin_fmaf(sP[(wave * N + n) * 64 + lane], E[n], h[n]);
+            GP[(size_t)n * D] = exp2_fast(A2[n] * (cs + sumd));
         }
-    } else {
-        float* hout = wsH + (((size_t)b * (S - 1) + seg) * N) * D + d;
-#pragma unroll
-        for (int n = 0; n < N; ++n) hout[(size_t)n * D] = h[n];
-        wsSd[((size_t)b * (S - 1) + seg) * D + d] = sumd;
     }
 }
 
-// h_in(s+1) = exp(A sum(Delta_s)) h_in(s) + H_s, s = 0 .. S-2, per (b, n, d).
-template <int N>
-__global__ void __launch_bounds__(256)
-carry_combine(const float* __restrict__ A, const float* __restrict__ h0, float* ws,
-              int B, int D, int S) {
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)B * N * D;
-    if (idx >= total) return;
-    const int d = (int)(idx % D);
-    const int n = (int)((idx / D) % N);
-    const int b = (int)(idx / ((size_t)D * N));
-    float* wsH = ws;
-    const float* wsSd = ws + ws_h_elems(B, S, N, D);
-    const float a2 = A[(size_t)d * N + n] * kLog2e;
-    float h = h0 ? h0[((size_t)b * D + d) * N + n] : 0.0f;
-    constexpr int U = 8;
-    for (int s0 = 0; s0 < S - 1; s0 += U) {
-        float Hs[U], Sd[U];
+template <int N, bool BF16, bool HAS_Z, bool HAS_D>
+__global__ void __launch_bounds__(512)
+segment_final(ScanArgs a, Geom g) {
+    extern __shared__ float lds[];
+    const int W = g.W;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.x, b = blockIdx.z;
+    const int D = a.D;
+    const int d = blockIdx.y * 64 + lane;
+    const int dc = d < D ? d : D - 1;
+    const int s = grp * W + wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
+    const int lenc = len > 0 ? len : 1;   // a wave past L still takes part in the barrier
+    const WsLayout wl = ws_layout(a.B, D, N, g.S, g.G);
+    const float* ws = static_cast<const float*>(a.ws);
+
+    // independent loads first: the segment's first inputs, A, h0 and this
+    // segment's in-group prefix; the carry from earlier groups comes after.
+    Segment<N, BF16, HAS_Z, HAS_D, true> seg(a, b, dc, min(t0, a.L - 1), lenc);
+    float A2[N], hg[N], E[N];
+    float cs = 0.0f;
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int s = min(s0 + k, S - 2);
-            Hs[k] = wsH[(((size_t)b * (S - 1) + s) * N + n) * D + d];
-            Sd[k] = wsSd[((size_t)b * (S - 1) + s) * D + d];
-        }
+    for (int n = 0; n < N; ++n) A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+    if (g.S > 1) {
+        const int sc = s < g.S ? s : g.S - 1;
+        cs = ws[wl.CS + ((size_t)b * g.S + sc) * D + dc];
+        const float* Ep = ws + wl.E + ((size_t)b * g.S + sc) * N * D + dc;
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int s = s0 + k;
-            if (s >= S - 1) break;
-            h = __builtin_fmaf(exp2_fast(a2 * Sd[k]), h, Hs[k]);
-            wsH[(((size_t)b * (S - 1) + s) * N + n) * D + d] = h;
+        for (int n = 0; n < N; ++n) E[n] = Ep[(size_t)n * D];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) E[n] = 0.0f;
+    }
+    if (a.h0 != nullptr) {
+        const float* hp = a.h0 + ((size_t)b * D + dc) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = hp[n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = 0.0f;
+    }
+    if (grp > 0) {
+        // State entering this group: compose the aggregates of groups 0 .. grp-1.
+        // Wave w composes one contiguous range of them; the ranges are then applied in order.
+        const int per = (grp + W - 1) / W;
+        const int k0 = min(grp, wave * per), k1 = min(grp, k0 + per);
+        float Pc[N], Hc[N];
+#pragma unroll
+        for (int n = 0; n < N; ++n) { Pc[n] = 1.0f; Hc[n] = 0.0f; }
+        for (int k = k0; k < k1; ++k) {
+            const float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + k) * N * D + dc;
+            const float* GP = ws + wl.GP + ((size_t)b * (g.G - 1) + k) * N * D + dc;
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const float p = GP[(size_t)n * D];
+                Hc[n] = __builtin_fmaf(p, Hc[n], GH[(size_t)n * D]);
+                Pc[n] *= p;
+            }
         }
+        float* sP = lds;
+        float* sH = sP + W * N * 64;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            sP[(wave * N + n) * 64 + lane] = Pc[n];
+            sH[(wave * N + n) * 64 + lane] = Hc[n];
+        }
+        __syncthreads();
+        for (int j = 0; j < W; ++j) {
+#pragma unroll
+            for (int n = 0; n < N; ++n)
+                hg[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], hg[n], sH[(j * N + n) * 64 + lane]);
+        }
+    }
+    if (len <= 0) return;
+
+    float h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hg[n], E[n]);
+    const float Dv = HAS_D ? a.Dskip[dc] : 0.0f;
+    float unused = 0.0f;
+    seg.run(A2, h, Dv, d < D, unused);
+    if (d < D && s == g.S - 1 && a.h_final != nullptr) {
+        float* hp = a.h_final + ((size_t)b * D + d) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hp[n] = h[n];
     }
 }
 
@@ -195,54 +369,38 @@ __global__ void copy_state(const float* __restrict__ h0, float* __restrict__ out
     if (i < n) out[i] = h0 ? h0[i] : 0.0f;
 }
 
-Geom geom(int B, int L, int D, int N) {
-    (void)N;
-    Geom g;
-    const int cw = (D + 63) / 64;                  // channel waves per batch row
-    g.threads = 64 * std::min(4, cw);
-    const long waves = (long)B * cw;
-    const int target = 4096;                       // waves for the final pass
-    long S = (target + waves - 1) / waves;
-    const int min_len = 32;
-    S = std::min<long>(S, std::max<long>(1, (L + min_len - 1) / min_len));
-    S = std::max<long>(S, 1);
-    int Ls = (int)((L + S - 1) / S);
-    if (Ls < 1) Ls = 1;
-    g.Ls = Ls;
-    g.S = L > 0 ? (L + Ls - 1) / Ls : 0;
-    return g;
-}
-
 template <int N, bool BF16>
 hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     const Geom g = geom(a.B, a.L, a.D, a.N);
     if (a.L == 0) {
         if (a.h_final) {
             const size_t n = (size_t)a.B * a.D * a.N;
+            profile_mark(st);
             hipLaunchKernelGGL(copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                                a.h0, a.h_final, n);
+            profile_mark(st);
         }
         return hipGetLastError();
     }
-    const dim3 block(g.threads);
-    const unsigned gy = (unsigned)((a.D + g.threads - 1) / g.threads);
+    const dim3 grid(g.G, (a.D + 63) / 64, a.B);
+    const dim3 block(64 * g.W);
+    const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
+    const size_t lds_fin = g.G > 1 ? (size_t)g.W * 2 * N * 64 * sizeof(float) : 0;
     if (g.S > 1) {
-        hipLaunchKernelGGL((segment_kernel<N, BF16, false, false, false>),
-                           dim3(g.S - 1, gy, a.B), block, 0, st, a, g.S, g.Ls);
-        const size_t tot = (size_t)a.B * N * a.D;
-        hipLaunchKernelGGL(carry_combine<N>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
-                           a.A, a.h0, static_cast<float*>(a.ws), a.B, a.D, g.S);
+        profile_mark(st);
+        hipLaunchKernelGGL((segment_aggregate<N, BF16>), grid, block, lds_agg, st, a, g);
     }
-    const dim3 grid(g.S, gy, a.B);
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
+    profile_mark(st);
     if (hz && hd)
-        hipLaunchKernelGGL((segment_kernel<N, BF16, true, true, true>), grid, block, 0, st, a, g.S, g.Ls);
+        hipLaunchKernelGGL((segment_final<N, BF16, true, true>), grid, block, lds_fin, st, a, g);
     else if (hz)
-        hipLaunchKernelGGL((segment_kernel<N, BF16, true, true, false>), grid, block, 0, st, a, g.S, g.Ls);
+        hipLaunchKernelGGL((segment_final<N, BF16, true, false>), grid, block, lds_fin, st, a, g);
     else if (hd)
-        hipLaunchKernelGGL((segment_kernel<N, BF16, true, false, true>), grid, block, 0, st, a, g.S, g.Ls);
+        hipLaunchKernelGGL((segment_final<N, BF16, false, true>), grid, block, lds_fin, st, a, g);
     else
-        hipLaunchKernelGGL((segment_kernel<N, BF16, true, false, false>), grid, block, 0, st, a, g.S, g.Ls);
+        hipLaunchKernelGGL((segment_final<N, BF16, false, false>), grid, block, lds_fin, st, a, g);
+    profile_mark(st);
     return hipGetLastError();
 }
 
@@ -270,7 +428,7 @@ ScanPlan scan_plan(int B, int L, int D, int N) {
 size_t scan_workspace_bytes(int B, int L, int D, int N) {
     const Geom g = geom(B, L, D, N);
     if (g.S <= 1) return 0;
-    return (ws_h_elems(B, g.S, N, D) + (size_t)B * (g.S - 1) * D) * sizeof(float);
+    return ws_layout(B, D, N, g.S, g.G).total * sizeof(float);
 }
 
 hipError_t launch_scan_fwd(const ScanArgs& a, hipStream_t st) {

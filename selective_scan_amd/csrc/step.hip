@@ -67,10 +67,12 @@ hipError_t launch_n(const StepArgs& a, hipStream_t st) {
     const int threads = a.D >= 256 ? 256 : ((a.D + 63) / 64) * 64;
     const dim3 grid((unsigned)((a.D + threads - 1) / threads), (unsigned)a.B);
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
+    profile_mark(st);
     if (hz && hd) hipLaunchKernelGGL((step_kernel<N, BF16, true, true>), grid, dim3(threads), 0, st, a);
     else if (hz) hipLaunchKernelGGL((step_kernel<N, BF16, true, false>), grid, dim3(threads), 0, st, a);
     else if (hd) hipLaunchKernelGGL((step_kernel<N, BF16, false, true>), grid, dim3(threads), 0, st, a);
     else hipLaunchKernelGGL((step_kernel<N, BF16, false, false>), grid, dim3(threads), 0, st, a);
+    profile_mark(st);
     return hipGetLastError();
 }
 
