@@ -119,7 +119,8 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
  *   chunk   : chunk length Q >= 1 (0 = default 256). The last chunk is ragged
  *             when Q does not divide L. The result does not depend on Q beyond
  *             rounding.
- * Supported: io = SSM_BF16; N in {64, 128}; P in {64}; chunk <= 256.
+ * Supported: io = SSM_BF16; N in {64, 128}; P = 64; chunk a multiple of 32 in
+ * [32, 256]; B, H <= 65535.
  * ------------------------------------------------------------------------- */
 size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk);
 

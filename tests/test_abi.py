@@ -90,6 +90,12 @@ def test_ssd_rejects_bad_arguments():
     assert call(B=0) == 1
     assert call(chunk=-1) == 1
     assert call(io=9) == 1
+    assert call(io=0) == 2          # fp32 I/O not built for SSD
+    assert call(Pp=32) == 2
+    assert call(N=96) == 2
+    assert call(chunk=48) == 2
+    assert call(chunk=512) == 2
+    assert call(B=70000) == 2
 
 
 def test_python_binding_checks_tensors_before_calling():
