@@ -218,6 +218,58 @@ def scan_cpu_baseline(wl, w0, budget_s=15.0):
                        f"N={N}: {upd / 1e6:.1f} M updates, median of {reps} run(s), {el:.3f} s each")
 
 
+# ------------------------------------------------------------------ SSD
+def ssd_alg(wl):
+    """Algorithmic HBM bytes and dense matrix flops per call.
+    bytes: read x, Delta, B, C, A; write y, h_final.
+    flops: G = C B^T once per (batch, chunk) (shared by the heads), and per
+    (batch, head, chunk) M X, the chunk state and C H: 2QQN + H(2QQP + 4QNP)."""
+    B, L, H, P, N, Q = wl["B"], wl["L"], wl["H"], wl["P"], wl["N"], wl["chunk"]
+    byt = 2 * (2 * B * L * H * P) + 2 * B * L * H + 2 * 2 * B * L * N + 4 * H + 4 * B * H * N * P
+    fl = 0.0
+    for c0 in range(0, L, Q):
+        q = min(Q, L - c0)
+        fl += B * (2.0 * q * q * N + H * (2.0 * q * q * P + 4.0 * q * N * P))
+    return byt, fl
+
+
+def ssd_bench(name, wl, steps, warmup, dev, max_sets=3):
+    import torch
+    import selective_scan_amd as ssa
+    import ssm_inputs as si
+    B, L, H, P, N, Q = wl["B"], wl["L"], wl["H"], wl["P"], wl["N"], wl["chunk"]
+    sets = []
+    for r in range(max_sets):
+        w = si.ssd_inputs(B, L, H, P, N, seed=r)
+        t = {k: si.to_torch(w[k], dev) for k in ("x", "delta", "Bm", "Cm", "A")}
+        t["y"] = torch.empty_like(t["x"])
+        t["hf"] = torch.empty((B, H, N, P), dtype=torch.float32, device=dev)
+        sets.append(t)
+    need = ssa.ssm_ssd_workspace_size(B, L, H, P, N, Q)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def call(t):
+        ssa.ssm_ssd_fwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], chunk=Q, y=t["y"],
+                        h_final=t["hf"], workspace=ws)
+
+    nk = count_kernels(lambda: call(sets[0]))
+    total_ms, ker = time_calls(call, sets, steps, warmup, nk)
+    ms = total_ms / steps
+    kmean = ker.mean(axis=0)
+    byt, fl = ssd_alg(wl)
+    upd = B * L * H * P * N
+    tdom = kmean[int(np.argmax(kmean))] * 1e-3
+    return dict(workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3),
+                tokens_per_s=B * L / (ms * 1e-3), kernel_ms=[float(v) for v in kmean],
+                hbm_gbs=byt / (ms * 1e-3) / 1e9, hbm_frac=byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                mfma_tflops=fl / (ms * 1e-3) / 1e12,
+                mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                roofline=dict(bound="hbm", achieved=byt / (ms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, traffic=None,
+                              kernel="whole call (two kernels)"),
+                dominant_kernel_ms=tdom * 1e3, alg_bytes=byt, alg_flops=fl)
+
+
 # ------------------------------------------------------------------ decode
 def step_bench(wl, dev, reps=3):
     import torch
@@ -328,6 +380,9 @@ def main():
                            steps=5, warmup=2, dev=dev)
         other["scan_long"] = {k: r2[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
                                                    "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
+        for nm in ("ssd_bf16_B4_L8192_H24_P64_N128_Q256", "ssd_bf16_B4_L8192_H24_P64_N128_Q64",
+                   "ssd_bf16_B4_L8000_H24_P64_N128_Q256"):
+            other[nm] = ssd_bench(nm, si.WORKLOADS[nm], steps=10, warmup=3, dev=dev)
         other["decode"] = step_bench(si.WORKLOADS["step_bf16_B64_D3072_N16_x1000"], dev)
         out["other_paths"] = other
     print(json.dumps(out))

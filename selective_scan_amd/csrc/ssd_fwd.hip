@@ -9,7 +9,7 @@
 //   y_i = exp(s_i) C_i . H_in  +  sum_{j<=i} (C_i . B_j) exp(s_i - s_j) Delta_j x_j
 // and the state after it is H_out = exp(s_last) H_in + sum_j exp(s_last - s_j) Delta_j B_j (x) x_j.
 //
-// Kernels (one workgroup of 4 waves per (batch, head, super-chunk); a
+// Kernels (one workgroup of 8 waves per (batch, head, super-chunk); a
 // super-chunk is a run of consecutive chunks walked in order with the state in LDS):
 //   ssd_super_state  every super-chunk but the last: its aggregate state from a
 //                    zero start, and its total log2 decay;
@@ -18,10 +18,14 @@
 //                    G^T = B C^T, M = G o decay o Delta (causal), Y_diag = M X,
 //                    y = (Y_off + Y_diag + D x) silu(z), then the chunk state
 //                    S = (w o X)^T B and H <- e^{s_last} H + S.
-// Matrix cores: v_mfma_f32_16x16x32_bf16 throughout. Operands that are stored in
-// bf16 (B, C, x) enter exactly; operands formed in fp32 (H, M, w o x) are split
-// into a bf16 high part and a bf16 remainder, i.e. two MFMAs, which keeps about
-// 16 significant bits (a single bf16 rounding would cost ~1e-3 relative error).
+// Matrix cores: v_mfma_f32_16x16x32_bf16 throughout. Operands stored in bf16
+// (B, C, x) enter exactly; operands formed in fp32 (H, M, w o x) are split into a
+// bf16 high part and a bf16 remainder, i.e. two MFMAs, which keeps about 16
+// significant bits (a single bf16 rounding would cost ~1e-3 relative error).
+// x and B of a chunk are staged in LDS row-major with plain 16-byte copies;
+// where a product contracts over time, its operand is read with the LDS
+// transpose read (ds_read_b64_tr_b16), which hands each lane four consecutive
+// time steps of one column.
 #include "common.h"
 #include "launch.h"
 
@@ -32,12 +36,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kThreads = 256;      // 4 waves
-constexpr int kTargetBlocks = 768; // workgroups of the scan kernel
-constexpr int kP = 64;             // head dim handled: one 16-wide p-block per wave
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTargetBlocks = 768;  // workgroups of the scan kernel
+constexpr int kP = 64;              // head dim handled
+constexpr int kXS = kP + 16;        // LDS row stride (elements) of x rows
+constexpr int kPad = 16;            // LDS row padding (elements) of B rows
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -54,12 +63,25 @@ __device__ __forceinline__ void split8(const float (&v)[8], bf16x8& hi, bf16x8& 
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Transposed operand read from a row-major [k][m] bf16 array in LDS (row stride
+// `rs` elements): lane i of each 16-lane group receives rows k0 .. k0+3 of column
+// m0 + i. Each lane of the group points at row k0 + i/4, columns m0 + 4(i%4) ...+3.
+__device__ __forceinline__ bf16x4 ld_tr4(const u16* base, int rs, int k0, int m0) {
+    const int i = threadIdx.x & 15;
+    const u16* p = base + (k0 + (i >> 2)) * rs + m0 + 4 * (i & 3);
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 struct SsdGeom {
     int Q;    // chunk length
     int C;    // chunks per sequence
     int cps;  // chunks per super-chunk
     int K;    // super-chunks per sequence
-    int QS;   // LDS row stride (elements) of the transposed bf16 tiles
 };
 
 SsdGeom ssd_geom(int B, int L, int H, int Q) {
@@ -71,25 +93,24 @@ SsdGeom ssd_geom(int B, int L, int H, int Q) {
     K = std::max<long>(1, std::min<long>(K, g.C));
     g.cps = g.C > 0 ? (int)((g.C + K - 1) / K) : 1;
     g.K = g.C > 0 ? (g.C + g.cps - 1) / g.cps : 0;
-    g.QS = Q + 8;
     return g;
 }
 
 // LDS layout (bytes), per workgroup
 struct Smem {
-    int xt, bt, ht, s2, dt, w, red, total;
+    int xs, bs, ht, s2, dt, w, red, total;
 };
 
 template <int N>
-__host__ __device__ inline Smem smem_layout(int Q, int QS) {
+__host__ __device__ inline Smem smem_layout(int Q) {
     Smem s;
-    s.xt = 0;                                       // bf16 [P][QS]   x^T of the chunk
-    s.bt = s.xt + kP * QS * 2;                      // bf16 [N][QS]   B^T of the chunk
-    s.ht = s.bt + N * QS * 2;                       // f32  [P][N+4]  state H^T
-    s.s2 = s.ht + kP * (N + 4) * 4;                 // f32  [Q]       inclusive log2-decay prefix
-    s.dt = s.s2 + Q * 4;                            // f32  [Q]       Delta
-    s.w = s.dt + Q * 4;                             // f32  [Q]       exp2(s_last - s_t) Delta_t
-    s.red = s.w + Q * 4;                            // f32  [4]       broadcast slot (s_last)
+    s.xs = 0;                              // bf16 [Q][kXS]     x rows of the chunk
+    s.bs = s.xs + Q * kXS * 2;             // bf16 [Q][N+kPad]  B rows of the chunk
+    s.ht = s.bs + Q * (N + kPad) * 2;      // f32  [P][N+4]     state H^T
+    s.s2 = s.ht + kP * (N + 4) * 4;        // f32  [Q]          inclusive log2-decay prefix
+    s.dt = s.s2 + Q * 4;                   // f32  [Q]          Delta
+    s.w = s.dt + Q * 4;                    // f32  [Q]          exp2(s_last - s_t) Delta_t
+    s.red = s.w + Q * 4;                   // f32  [4]          broadcast slot (s_last)
     s.total = s.red + 16;
     return s;
 }
@@ -97,17 +118,17 @@ __host__ __device__ inline Smem smem_layout(int Q, int QS) {
 // workspace (floats): Hagg [B][H][K-1][P][N], Lam [B][H][K-1]
 __host__ __device__ inline size_t ws_hagg(int B, int H, int K, int N) { return (size_t)B * H * (K - 1) * kP * N; }
 
-// Stage one chunk: Delta, log2-decay prefix, weights (wave 0) and the transposed
-// x and B tiles (all waves). Rows past `len` are zero.
+// Stage one chunk: Delta, log2-decay prefix and weights (wave 0), x and B rows
+// (all threads). Rows past `len` are zero.
 template <int N>
-__device__ void stage_chunk(const SsdArgs& a, char* lds, const Smem& sm, int QS, int b, int h,
-                            int t0, int len, float A2) {
+__device__ void stage_chunk(const SsdArgs& a, char* lds, const Smem& sm, int b, int h, int t0, int len,
+                            float A2) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Q = a.Q;
-    float* s2 = reinterpret_cast<float*>(lds + sm.s2);
-    float* dt = reinterpret_cast<float*>(lds + sm.dt);
-    float* w = reinterpret_cast<float*>(lds + sm.w);
     if (wave == 0) {
+        float* s2 = reinterpret_cast<float*>(lds + sm.s2);
+        float* dt = reinterpret_cast<float*>(lds + sm.dt);
+        float* w = reinterpret_cast<float*>(lds + sm.w);
         // 4 consecutive steps per lane (Q <= 256), fp64 prefix, then a wave-wide scan
         const u16* dp = static_cast<const u16*>(a.delta);
         float dv[4];
@@ -126,13 +147,11 @@ __device__ void stage_chunk(const SsdArgs& a, char* lds, const Smem& sm, int QS,
             if (lane >= off) incl += v;
         }
         const double excl = incl - run;
-        // s_last = prefix at len-1, held by lane (len-1)/4
-        float sl = 0.0f;
+        float sl;
         {
             const int ll = (len - 1) >> 2, kk = (len - 1) & 3;
             const double lk = kk == 0 ? loc[0] : kk == 1 ? loc[1] : kk == 2 ? loc[2] : loc[3];
-            const double mine = excl + lk;
-            sl = (float)__shfl(mine, ll, 64);
+            sl = (float)__shfl(excl + lk, ll, 64);
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -146,48 +165,50 @@ __device__ void stage_chunk(const SsdArgs& a, char* lds, const Smem& sm, int QS,
         }
         if (lane == 0) reinterpret_cast<float*>(lds + sm.red)[0] = sl;
     }
-    // x rows -> x^T: 8 lanes per row of P=64 (16 B each)
-    u16* xt = reinterpret_cast<u16*>(lds + sm.xt);
-    for (int r = tid >> 3; r < Q; r += kThreads / 8) {
-        const int p0 = (tid & 7) * 8;
+    // x rows: 8 x 16 B per row
+    u16* xs = reinterpret_cast<u16*>(lds + sm.xs);
+    for (int q = tid; q < Q * (kP / 8); q += kThreads) {
+        const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (r < len)
             v = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.x) +
-                                                (((size_t)b * a.L + t0 + r) * a.H + h) * kP + p0);
-        const u16* e = reinterpret_cast<const u16*>(&v);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) xt[(p0 + k) * QS + r] = e[k];
+                                                (((size_t)b * a.L + t0 + r) * a.H + h) * kP + c8);
+        *reinterpret_cast<uint4*>(xs + r * kXS + c8) = v;
     }
-    // B rows -> B^T: N/8 lanes per row
-    u16* bt = reinterpret_cast<u16*>(lds + sm.bt);
-    constexpr int LPR = N / 8;
-    for (int r = tid / LPR; r < Q; r += kThreads / LPR) {
-        const int n0 = (tid % LPR) * 8;
+    // B rows: N/8 x 16 B per row
+    u16* bs = reinterpret_cast<u16*>(lds + sm.bs);
+    for (int q = tid; q < Q * (N / 8); q += kThreads) {
+        const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (r < len)
-            v = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.Bm) + ((size_t)b * a.L + t0 + r) * N + n0);
-        const u16* e = reinterpret_cast<const u16*>(&v);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bt[(n0 + k) * QS + r] = e[k];
+            v = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.Bm) + ((size_t)b * a.L + t0 + r) * N + c8);
+        *reinterpret_cast<uint4*>(bs + r * (N + kPad) + c8) = v;
     }
 }
 
-// Chunk state S^T = (w o X)^T B for this wave's p-block, accumulated in sacc
-// (lane holds S^T[p = wave*16 + 4g + r][n = nb*16 + l%16]).
+// Chunk state S^T = (w o X)^T B on this wave's tiles: p-block pb = wave % 4 and
+// n-blocks nb0 .. nb0 + NBW - 1. Lane holds S^T[p = pb*16 + 4g + r][n = nb*16 + l%16].
 template <int N>
-__device__ __forceinline__ void chunk_state(const char* lds, const Smem& sm, int QS, int len,
-                                            f32x4 (&sacc)[N / 16]) {
+struct StateTiles {
+    static constexpr int NBW = N / 32;  // n-blocks per wave (8 waves = 4 p-blocks x 2 halves)
+    f32x4 acc[NBW];
+};
+
+template <int N>
+__device__ __forceinline__ void chunk_state(const char* lds, const Smem& sm, int len, StateTiles<N>& st) {
+    constexpr int NBW = StateTiles<N>::NBW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c = lane & 15;
-    const u16* xt = reinterpret_cast<const u16*>(lds + sm.xt);
-    const u16* bt = reinterpret_cast<const u16*>(lds + sm.bt);
+    const int g = lane >> 4;
+    const int pb = wave & 3, nb0 = (wave >> 2) * NBW;
+    const u16* xs = reinterpret_cast<const u16*>(lds + sm.xs);
+    const u16* bs = reinterpret_cast<const u16*>(lds + sm.bs);
     const float* w = reinterpret_cast<const float*>(lds + sm.w);
 #pragma unroll
-    for (int nb = 0; nb < N / 16; ++nb) sacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NBW; ++k) st.acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kbn = (len + 31) >> 5;
     for (int kb = 0; kb < kbn; ++kb) {
         const int t = kb * 32 + 8 * g;
-        const bf16x8 xv = ld_bf16x8(xt + (wave * 16 + c) * QS + t);
+        const bf16x8 xv = cat(ld_tr4(xs, kXS, t, pb * 16), ld_tr4(xs, kXS, t + 4, pb * 16));
         const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + t);
         const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + t + 4);
         float v[8];
@@ -199,27 +220,30 @@ __device__ __forceinline__ void chunk_state(const char* lds, const Smem& sm, int
         bf16x8 ahi, alo;
         split8(v, ahi, alo);
 #pragma unroll
-        for (int nb = 0; nb < N / 16; ++nb) {
-            const bf16x8 bop = ld_bf16x8(bt + (nb * 16 + c) * QS + t);
-            sacc[nb] = mfma(ahi, bop, sacc[nb]);
-            sacc[nb] = mfma(alo, bop, sacc[nb]);
+        for (int k = 0; k < NBW; ++k) {
+            const int n0 = (nb0 + k) * 16;
+            const bf16x8 bop = cat(ld_tr4(bs, N + kPad, t, n0), ld_tr4(bs, N + kPad, t + 4, n0));
+            st.acc[k] = mfma(ahi, bop, st.acc[k]);
+            st.acc[k] = mfma(alo, bop, st.acc[k]);
         }
     }
 }
 
-// H^T <- exp2(s_last) H^T + S^T on this wave's rows
+// H^T <- exp2(s_last) H^T + S^T on this wave's tiles
 template <int N>
-__device__ __forceinline__ void state_update(char* lds, const Smem& sm, const f32x4 (&sacc)[N / 16]) {
+__device__ __forceinline__ void state_update(char* lds, const Smem& sm, const StateTiles<N>& st) {
+    constexpr int NBW = StateTiles<N>::NBW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
+    const int pb = wave & 3, nb0 = (wave >> 2) * NBW;
     float* ht = reinterpret_cast<float*>(lds + sm.ht);
     const float decay = exp2_fast(reinterpret_cast<const float*>(lds + sm.red)[0]);
 #pragma unroll
-    for (int nb = 0; nb < N / 16; ++nb)
+    for (int k = 0; k < NBW; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float* p = ht + (wave * 16 + 4 * g + r) * (N + 4) + nb * 16 + c;
-            *p = __builtin_fmaf(decay, *p, sacc[nb][r]);
+            float* p = ht + (pb * 16 + 4 * g + r) * (N + 4) + (nb0 + k) * 16 + c;
+            *p = __builtin_fmaf(decay, *p, st.acc[k][r]);
         }
 }
 
@@ -227,7 +251,7 @@ template <int N>
 __global__ void __launch_bounds__(kThreads)
 ssd_super_state(SsdArgs a, SsdGeom geo) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const Smem sm = smem_layout<N>(geo.Q, geo.QS);
+    const Smem sm = smem_layout<N>(geo.Q);
     const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const float A2 = a.A[h] * kLog2e;
@@ -239,13 +263,12 @@ ssd_super_state(SsdArgs a, SsdGeom geo) {
         const int t0 = cc * geo.Q;
         const int len = min(geo.Q, a.L - t0);
         __syncthreads();  // previous chunk fully consumed
-        stage_chunk<N>(a, lds, sm, geo.QS, b, h, t0, len, A2);
+        stage_chunk<N>(a, lds, sm, b, h, t0, len, A2);
         __syncthreads();
-        f32x4 sacc[N / 16];
-        chunk_state<N>(lds, sm, geo.QS, len, sacc);
+        StateTiles<N> st;
+        chunk_state<N>(lds, sm, len, st);
         lam += (double)reinterpret_cast<const float*>(lds + sm.red)[0];
-        __syncthreads();
-        state_update<N>(lds, sm, sacc);
+        state_update<N>(lds, sm, st);
     }
     __syncthreads();
     float* out = static_cast<float*>(a.ws) + (((size_t)b * a.H + h) * (geo.K - 1) + k) * kP * N;
@@ -256,22 +279,100 @@ ssd_super_state(SsdArgs a, SsdGeom geo) {
     }
 }
 
+// Outputs of one 16-row block I of a chunk.
+template <int N, bool HAS_Z, bool HAS_D>
+__device__ __forceinline__ void chunk_rows(const SsdArgs& a, const char* lds, const Smem& sm, int b, int h,
+                                           int t0, int len, int I, const bf16x8 (&cop)[N / 32], float Dh) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    const u16* xs = reinterpret_cast<const u16*>(lds + sm.xs);
+    const u16* bs = reinterpret_cast<const u16*>(lds + sm.bs);
+    const float* ht = reinterpret_cast<const float*>(lds + sm.ht);
+    const float* s2 = reinterpret_cast<const float*>(lds + sm.s2);
+    const float* dt = reinterpret_cast<const float*>(lds + sm.dt);
+    const int ia = I * 16 + c;  // this lane's A-operand row
+    f32x4 acc[kP / 16];
+#pragma unroll
+    for (int pb = 0; pb < kP / 16; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Y_off = C H (H^T rows are the B operand), then rows scaled by exp2(s_i)
+#pragma unroll
+    for (int kb = 0; kb < N / 32; ++kb)
+#pragma unroll
+        for (int pb = 0; pb < kP / 16; ++pb) {
+            const float* hp = ht + (pb * 16 + c) * (N + 4) + kb * 32 + 8 * g;
+            const f32x4 h0v = *reinterpret_cast<const f32x4*>(hp);
+            const f32x4 h1v = *reinterpret_cast<const f32x4*>(hp + 4);
+            const float v[8] = {h0v[0], h0v[1], h0v[2], h0v[3], h1v[0], h1v[1], h1v[2], h1v[3]};
+            bf16x8 hhi, hlo;
+            split8(v, hhi, hlo);
+            acc[pb] = mfma(cop[kb], hhi, acc[pb]);
+            acc[pb] = mfma(cop[kb], hlo, acc[pb]);
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float sc = exp2_fast(s2[I * 16 + 4 * g + r]);
+#pragma unroll
+        for (int pb = 0; pb < kP / 16; ++pb) acc[pb][r] *= sc;
+    }
+    // Y_diag = M X over 32-wide column blocks J up to the block's last row
+    const float s2i = s2[ia];
+    for (int J = 0; J * 32 <= I * 16 + 15; ++J) {
+        f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < N / 32; ++kb) {
+            const bf16x8 b0 = ld_bf16x8(bs + (J * 32 + c) * (N + kPad) + kb * 32 + 8 * g);
+            const bf16x8 b1 = ld_bf16x8(bs + (J * 32 + 16 + c) * (N + kPad) + kb * 32 + 8 * g);
+            g0 = mfma(b0, cop[kb], g0);  // G^T[j][i]: lane holds G[ia][J*32 + 4g + r]
+            g1 = mfma(b1, cop[kb], g1);  //            and G[ia][J*32 + 16 + 4g + r]
+        }
+        float m[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = J * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+            const float gv = e < 4 ? g0[e] : g1[e - 4];
+            const bool ok = (j <= ia) && (j < len) && (ia < len);
+            m[e] = ok ? gv * exp2_fast(s2i - s2[j]) * dt[j] : 0.0f;
+        }
+        bf16x8 mhi, mlo;
+        split8(m, mhi, mlo);
+#pragma unroll
+        for (int pb = 0; pb < kP / 16; ++pb) {
+            // x at the same (g, e) -> j mapping: two runs of 4 steps
+            const bf16x8 xop = cat(ld_tr4(xs, kXS, J * 32 + 4 * g, pb * 16),
+                                   ld_tr4(xs, kXS, J * 32 + 16 + 4 * g, pb * 16));
+            acc[pb] = mfma(mhi, xop, acc[pb]);
+            acc[pb] = mfma(mlo, xop, acc[pb]);
+        }
+    }
+    // epilogue: rows i = I*16 + 4g + r, columns p = pb*16 + c
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = I * 16 + 4 * g + r;
+        if (i >= len) continue;
+        const size_t rowoff = (((size_t)b * a.L + t0 + i) * a.H + h) * kP;
+#pragma unroll
+        for (int pb = 0; pb < kP / 16; ++pb) {
+            const int p = pb * 16 + c;
+            float v = acc[pb][r];
+            if constexpr (HAS_D) v = __builtin_fmaf(Dh, bf16_to_f32(xs[i * kXS + p]), v);
+            if constexpr (HAS_Z) v *= silu(bf16_to_f32(static_cast<const u16*>(a.z)[rowoff + p]));
+            static_cast<u16*>(a.y)[rowoff + p] = f32_to_bf16(v);
+        }
+    }
+}
+
 template <int N, bool HAS_Z, bool HAS_D>
 __global__ void __launch_bounds__(kThreads)
 ssd_chunk_scan(SsdArgs a, SsdGeom geo) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    const Smem sm = smem_layout<N>(geo.Q, geo.QS);
+    const Smem sm = smem_layout<N>(geo.Q);
     const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int QS = geo.QS;
     const float A2 = a.A[h] * kLog2e;
     const float Dh = HAS_D ? a.Dskip[h] : 0.0f;
     float* ht = reinterpret_cast<float*>(lds + sm.ht);
-    const u16* xt = reinterpret_cast<const u16*>(lds + sm.xt);
-    const float* s2 = reinterpret_cast<const float*>(lds + sm.s2);
-    const float* dt = reinterpret_cast<const float*>(lds + sm.dt);
 
     // state entering this super-chunk: h0 folded with the earlier aggregates
     {
@@ -290,107 +391,35 @@ ssd_chunk_scan(SsdArgs a, SsdGeom geo) {
     const bool last_super = (k == geo.K - 1);
     const int c0 = k * geo.cps, c1 = min(geo.C, c0 + geo.cps);
     const u16* Cg = static_cast<const u16*>(a.Cm);
-    const u16* Bg = static_cast<const u16*>(a.Bm);
+    // row blocks of this wave: 16-row blocks pair up (I, R-1-I) to balance the causal work
+    const int R = geo.Q / 16;
+    const int I0 = wave, I1 = (R == 16) ? 15 - wave : -1;
     for (int cc = c0; cc < c1; ++cc) {
         const int t0 = cc * geo.Q;
         const int len = min(geo.Q, a.L - t0);
-        __syncthreads();
-        stage_chunk<N>(a, lds, sm, QS, b, h, t0, len, A2);
-        __syncthreads();
-
-        // ---- outputs: row blocks I = wave, wave+4, ... of 16 rows
-        for (int I = wave; I * 16 < len; I += 4) {
-            const int ia = I * 16 + c;  // this lane's A-operand row
-            bf16x8 cop[N / 32];
+        // C rows of this wave's blocks straight from global (prefetched before the barrier)
+        bf16x8 cop0[N / 32], cop1[N / 32];
 #pragma unroll
-            for (int kb = 0; kb < N / 32; ++kb) {
-                if (ia < len) cop[kb] = ld_bf16x8(Cg + ((size_t)b * a.L + t0 + ia) * N + kb * 32 + 8 * g);
-                else cop[kb] = bf16x8{};
-            }
-            f32x4 acc[kP / 16];
-#pragma unroll
-            for (int pb = 0; pb < kP / 16; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // Y_off = C H (H^T rows are the B operand), then rows scaled by exp2(s_i)
-#pragma unroll
-            for (int kb = 0; kb < N / 32; ++kb)
-#pragma unroll
-                for (int pb = 0; pb < kP / 16; ++pb) {
-                    const float* hp = ht + (pb * 16 + c) * (N + 4) + kb * 32 + 8 * g;
-                    const f32x4 h0v = *reinterpret_cast<const f32x4*>(hp);
-                    const f32x4 h1v = *reinterpret_cast<const f32x4*>(hp + 4);
-                    const float v[8] = {h0v[0], h0v[1], h0v[2], h0v[3], h1v[0], h1v[1], h1v[2], h1v[3]};
-                    bf16x8 hhi, hlo;
-                    split8(v, hhi, hlo);
-                    acc[pb] = mfma(cop[kb], hhi, acc[pb]);
-                    acc[pb] = mfma(cop[kb], hlo, acc[pb]);
-                }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = I * 16 + 4 * g + r;
-                const float sc = exp2_fast(s2[i < geo.Q ? i : geo.Q - 1]);
-#pragma unroll
-                for (int pb = 0; pb < kP / 16; ++pb) acc[pb][r] *= sc;
-            }
-            // Y_diag = M X over 32-wide column blocks J with J*32 <= last row of the block
-            const float s2i = s2[ia < geo.Q ? ia : geo.Q - 1];
-            for (int J = 0; J * 32 <= I * 16 + 15; ++J) {
-                f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int j0 = J * 32 + c, j1 = J * 32 + 16 + c;
-#pragma unroll
-                for (int kb = 0; kb < N / 32; ++kb) {
-                    const bf16x8 b0 = j0 < len ? ld_bf16x8(Bg + ((size_t)b * a.L + t0 + j0) * N + kb * 32 + 8 * g)
-                                               : bf16x8{};
-                    const bf16x8 b1 = j1 < len ? ld_bf16x8(Bg + ((size_t)b * a.L + t0 + j1) * N + kb * 32 + 8 * g)
-                                               : bf16x8{};
-                    g0 = mfma(b0, cop[kb], g0);   // G^T[j][i]: lane holds G[ia][J*32 + 4g + r]
-                    g1 = mfma(b1, cop[kb], g1);   //            and G[ia][J*32 + 16 + 4g + r]
-                }
-                float m[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = J * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-                    const float gv = e < 4 ? g0[e] : g1[e - 4];
-                    const bool ok = (j <= ia) && (j < len) && (ia < len);
-                    const float dec = exp2_fast(s2i - s2[j < geo.Q ? j : geo.Q - 1]);
-                    m[e] = ok ? gv * dec * dt[j < geo.Q ? j : geo.Q - 1] : 0.0f;
-                }
-                bf16x8 mhi, mlo;
-                split8(m, mhi, mlo);
-#pragma unroll
-                for (int pb = 0; pb < kP / 16; ++pb) {
-                    // x at the same (g, e) -> j mapping: two runs of 4 steps
-                    const u16* xr = xt + (pb * 16 + c) * QS + J * 32;
-                    const bf16x4 xa = *reinterpret_cast<const bf16x4*>(xr + 4 * g);
-                    const bf16x4 xb = *reinterpret_cast<const bf16x4*>(xr + 16 + 4 * g);
-                    const bf16x8 xop = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
-                    acc[pb] = mfma(mhi, xop, acc[pb]);
-                    acc[pb] = mfma(mlo, xop, acc[pb]);
-                }
-            }
-            // epilogue: rows i = I*16 + 4g + r, columns p = pb*16 + c
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = I * 16 + 4 * g + r;
-                if (i >= len) continue;
-                const size_t rowoff = (((size_t)b * a.L + t0 + i) * a.H + h) * kP;
-#pragma unroll
-                for (int pb = 0; pb < kP / 16; ++pb) {
-                    const int p = pb * 16 + c;
-                    float v = acc[pb][r];
-                    if constexpr (HAS_D) v = __builtin_fmaf(Dh, bf16_to_f32(static_cast<const u16*>(a.x)[rowoff + p]), v);
-                    if constexpr (HAS_Z) v *= silu(bf16_to_f32(static_cast<const u16*>(a.z)[rowoff + p]));
-                    static_cast<u16*>(a.y)[rowoff + p] = f32_to_bf16(v);
-                }
-            }
+        for (int kb = 0; kb < N / 32; ++kb) {
+            const int i0 = I0 * 16 + c, i1 = I1 * 16 + c;
+            cop0[kb] = (I0 < R && i0 < len) ? ld_bf16x8(Cg + ((size_t)b * a.L + t0 + i0) * N + kb * 32 + 8 * g)
+                                            : bf16x8{};
+            cop1[kb] = (I1 >= 0 && i1 < len) ? ld_bf16x8(Cg + ((size_t)b * a.L + t0 + i1) * N + kb * 32 + 8 * g)
+                                             : bf16x8{};
         }
-        // ---- state after the chunk (not needed after the last chunk of a
-        // super-chunk, except at the very end of the sequence for h_final)
+        __syncthreads();
+        stage_chunk<N>(a, lds, sm, b, h, t0, len, A2);
+        __syncthreads();
+        if (I0 < R && I0 * 16 < len) chunk_rows<N, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, cop0, Dh);
+        if (I1 >= 0 && I1 * 16 < len) chunk_rows<N, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I1, cop1, Dh);
+        // state after the chunk (not needed after the last chunk of a super-chunk,
+        // except at the very end of the sequence for h_final)
         const bool need_state = (cc < c1 - 1) || (last_super && a.h_final != nullptr);
         if (need_state) {
-            f32x4 sacc[N / 16];
-            chunk_state<N>(lds, sm, QS, len, sacc);
+            StateTiles<N> st;
+            chunk_state<N>(lds, sm, len, st);
             __syncthreads();  // every wave has finished reading H^T for Y_off
-            state_update<N>(lds, sm, sacc);
+            state_update<N>(lds, sm, st);
         }
     }
     if (last_super && a.h_final != nullptr) {
@@ -420,7 +449,7 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
         return hipGetLastError();
     }
     const SsdGeom geo = ssd_geom(a.B, a.L, a.H, a.Q);
-    const Smem sm = smem_layout<N>(geo.Q, geo.QS);
+    const Smem sm = smem_layout<N>(geo.Q);
     if (geo.K > 1) {
         profile_mark(st);
         hipLaunchKernelGGL((ssd_super_state<N>), dim3(geo.K - 1, a.H, a.B), dim3(kThreads), sm.total, st, a, geo);
@@ -439,7 +468,6 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
 }  // namespace
 
 const char* ssd_unsupported_reason(int L, int H, int P, int N, int Q, bool bf16) {
-    (void)L;
     if (!bf16) return "SSD supports bf16 I/O only";
     if (P != kP) return "SSD supports head dim P = 64 only";
     if (N != 64 && N != 128) return "SSD supports N = 64 or 128";
