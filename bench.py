@@ -131,26 +131,30 @@ def count_kernels(call):
 
 
 def time_calls(call, sets, steps, warmup, n_kernels):
-    """Time `steps` calls (rotating over `sets`) with outer events, and every
-    kernel of every call with the library's profiling events."""
+    """Time `steps` calls (rotating over `sets`) between two events on the launch
+    stream; then time every kernel of another `steps` calls with the library's
+    profiling events (kept out of the throughput run: an event record between two
+    launches adds a dispatch gap)."""
     import torch
     import selective_scan_amd as ssa
     lib = ssa.ops.lib()
     for i in range(warmup):
         call(sets[i % len(sets)])
     sync()
-    kt = KernelTimer(steps * (n_kernels + 1))
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    sync()
-    kt.start(lib)
     t0.record()
     for i in range(steps):
         call(sets[(warmup + i) % len(sets)])
     t1.record()
-    used = kt.stop(lib)
     sync()
     total_ms = t0.elapsed_time(t1)
+    kt = KernelTimer(steps * (n_kernels + 1))
+    kt.start(lib)
+    for i in range(steps):
+        call(sets[(warmup + steps + i) % len(sets)])
+    used = kt.stop(lib)
+    sync()
     per_k = n_kernels + 1
     assert used == steps * per_k, f"recorded {used} events, expected {steps * per_k}"
     ker = np.array([[kt.elapsed_ms(s * per_k + k, s * per_k + k + 1) for k in range(n_kernels)]
@@ -339,6 +343,8 @@ def main():
     ap.add_argument("--workload", default="scan_bf16_B1_L4096_D1536_N16")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-other", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the selective scan here has no multi-GPU path "
@@ -347,6 +353,15 @@ def main():
     import torch
     import ssm_inputs as si
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        sync()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "calibrate_copy_bytes_written": dst.numel() * 4,
+                          "launches": 5}))
+        return
     wl = si.WORKLOADS[args.workload]
     assert wl["kind"] == "scan", "the headline bench line is a scan workload"
     res, w0 = scan_bench(args.workload, wl, args.steps, args.warmup, dev)

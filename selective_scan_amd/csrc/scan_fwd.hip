@@ -13,15 +13,15 @@
 //
 // L-parallelism. B*D channels alone cannot fill 256 CUs, so each chain of 64
 // channels is cut into S segments of Ls steps; W consecutive segments form a
-// group, handled by one workgroup of W waves (one wave per segment). Two launches:
+// group, handled by one workgroup of W waves (one wave per segment). Three launches:
 //   1. segment_aggregate: every wave runs its segment from a zero state (end
 //      state H_s, decay P_s = exp(A sum Delta)); the group's waves then form, in
 //      LDS, each segment's exclusive in-group prefix E_s (and the in-group prefix
 //      of sum Delta), and the last wave the group's own aggregate (GP_g, GH_g).
-//   2. segment_final: each workgroup folds the aggregates of all earlier groups
-//      (waves fold disjoint ranges in parallel, then combine in LDS) into the
-//      state entering its group, forms each segment's carried-in state
-//      h_in = exp(A * prefix sum Delta) h_group + E_s, and runs the recurrence
+//   2. group_carry: per (batch, channel, state index) a short sequential pass
+//      over the groups gives the state entering each group (linear in groups).
+//   3. segment_final: each wave forms its segment's carried-in state
+//      h_in = exp(A * prefix sum Delta) h_group + E_s and runs the recurrence
 //      again from it, writing y (and h_final at the end of the sequence).
 // (P1, H1) then (P2, H2) compose to (P2 P1, P2 H1 + H2): the recurrence is an
 // affine map of the state, so segments compose like affine maps.
@@ -33,9 +33,22 @@
 namespace ssm {
 namespace {
 
-constexpr int kPrefetch = 8;
-constexpr int kTargetWaves = 4096;
-constexpr int kMinSegment = 32;
+// Geometry defaults; each can be overridden at build time (-DSSM_SCAN_...).
+#ifndef SSM_SCAN_PREFETCH
+#define SSM_SCAN_PREFETCH 8
+#endif
+#ifndef SSM_SCAN_TARGET_WAVES
+#define SSM_SCAN_TARGET_WAVES 4096
+#endif
+#ifndef SSM_SCAN_MIN_SEGMENT
+#define SSM_SCAN_MIN_SEGMENT 32
+#endif
+#ifndef SSM_SCAN_MAX_GROUP
+#define SSM_SCAN_MAX_GROUP 4
+#endif
+constexpr int kPrefetch = SSM_SCAN_PREFETCH;       // steps of x/Delta/z in flight per lane
+constexpr int kTargetWaves = SSM_SCAN_TARGET_WAVES;  // waves the final pass aims for
+constexpr int kMinSegment = SSM_SCAN_MIN_SEGMENT;    // shortest segment (steps)
 
 struct Geom {
     int Ls;  // steps per segment
@@ -44,7 +57,7 @@ struct Geom {
     int G;   // groups per chain
 };
 
-inline int max_group(int N) { return std::max(1, std::min(8, 128 / N)); }
+inline int max_group(int N) { return std::max(1, std::min(SSM_SCAN_MAX_GROUP, 128 / N)); }
 
 Geom geom(int B, int L, int D, int N) {
     Geom g{1, 0, 1, 0};
@@ -63,7 +76,8 @@ Geom geom(int B, int L, int D, int N) {
 // workspace layout (floats), all with the channel index fastest:
 //   E  [B][S][N][D]   exclusive in-group prefix state of each segment
 //   CS [B][S][D]      in-group prefix of sum(Delta) before each segment
-//   GH [B][G-1][N][D] aggregate end state of each group (from zero)
+//   GH [B][G-1][N][D] aggregate end state of each group (from zero); group_carry
+//                     overwrites slot g with the state entering group g+1
 //   GP [B][G-1][N][D] aggregate decay of each group
 struct WsLayout {
     size_t E, CS, GH, GP, total;
@@ -206,7 +220,7 @@ struct Segment {
 };
 
 template <int N, bool BF16>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(64 * SSM_SCAN_MAX_GROUP)
 segment_aggregate(ScanArgs a, Geom g) {
     extern __shared__ float lds[];
     const int W = g.W;
@@ -257,10 +271,12 @@ segment_aggregate(ScanArgs a, Geom g) {
     if (d >= D || s >= g.S) return;
     const WsLayout wl = ws_layout(a.B, D, N, g.S, g.G);
     float* ws = static_cast<float*>(a.ws);
-    float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + d;
+    if (wave > 0) {  // the first segment of a group starts from the group's own entering state
+        float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + d;
 #pragma unroll
-    for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
-    ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+        for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
+        ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+    }
     // the group's own aggregate, needed by later groups
     const bool last_in_group = (wave == W - 1) || (s == g.S - 1);
     if (last_in_group && grp < g.G - 1) {
@@ -274,10 +290,42 @@ segment_aggregate(ScanArgs a, Geom g) {
     }
 }
 
+// state entering each group: carry(0) = h0, carry(g+1) = GP_g carry(g) + GH_g,
+// written over GH_g; one thread per (batch, state index, channel)
+template <int N>
+__global__ void __launch_bounds__(256)
+group_carry(const float* __restrict__ h0, float* ws, int B, int D, Geom g) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)B * N * D) return;
+    const int d = (int)(idx % D);
+    const int n = (int)((idx / D) % N);
+    const int b = (int)(idx / ((size_t)D * N));
+    const WsLayout wl = ws_layout(B, D, N, g.S, g.G);
+    float* GH = ws + wl.GH + (size_t)b * (g.G - 1) * N * D + (size_t)n * D + d;
+    const float* GP = ws + wl.GP + (size_t)b * (g.G - 1) * N * D + (size_t)n * D + d;
+    const size_t st = (size_t)N * D;
+    float h = h0 ? h0[((size_t)b * D + d) * N + n] : 0.0f;
+    constexpr int U = 16;
+    for (int k0 = 0; k0 < g.G - 1; k0 += U) {
+        float p[U], q[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int kk = min(k0 + k, g.G - 2);
+            p[k] = GP[kk * st];
+            q[k] = GH[kk * st];
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (k0 + k >= g.G - 1) break;
+            h = __builtin_fmaf(p[k], h, q[k]);
+            GH[(k0 + k) * st] = h;
+        }
+    }
+}
+
 template <int N, bool BF16, bool HAS_Z, bool HAS_D>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(64 * SSM_SCAN_MAX_GROUP)
 segment_final(ScanArgs a, Geom g) {
-    extern __shared__ float lds[];
     const int W = g.W;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = blockIdx.x, b = blockIdx.z;
@@ -286,29 +334,23 @@ segment_final(ScanArgs a, Geom g) {
     const int dc = d < D ? d : D - 1;
     const int s = grp * W + wave;
     const int t0 = s * g.Ls;
-    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
-    const int lenc = len > 0 ? len : 1;   // a wave past L still takes part in the barrier
+    if (s >= g.S) return;
+    const int len = min(g.Ls, a.L - t0);
     const WsLayout wl = ws_layout(a.B, D, N, g.S, g.G);
     const float* ws = static_cast<const float*>(a.ws);
 
-    // independent loads first: the segment's first inputs, A, h0 and this
-    // segment's in-group prefix; the carry from earlier groups comes after.
-    Segment<N, BF16, HAS_Z, HAS_D, true> seg(a, b, dc, min(t0, a.L - 1), lenc);
+    // every load that does not depend on the recurrence first: the segment's
+    // first inputs, A, the state entering the group and the in-group prefix
+    Segment<N, BF16, HAS_Z, HAS_D, true> seg(a, b, dc, t0, len);
     float A2[N], hg[N], E[N];
     float cs = 0.0f;
 #pragma unroll
     for (int n = 0; n < N; ++n) A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
-    if (g.S > 1) {
-        const int sc = s < g.S ? s : g.S - 1;
-        cs = ws[wl.CS + ((size_t)b * g.S + sc) * D + dc];
-        const float* Ep = ws + wl.E + ((size_t)b * g.S + sc) * N * D + dc;
+    if (grp > 0) {
+        const float* cp = ws + wl.GH + ((size_t)b * (g.G - 1) + grp - 1) * N * D + dc;
 #pragma unroll
-        for (int n = 0; n < N; ++n) E[n] = Ep[(size_t)n * D];
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) E[n] = 0.0f;
-    }
-    if (a.h0 != nullptr) {
+        for (int n = 0; n < N; ++n) hg[n] = cp[(size_t)n * D];
+    } else if (a.h0 != nullptr) {
         const float* hp = a.h0 + ((size_t)b * D + dc) * N;
 #pragma unroll
         for (int n = 0; n < N; ++n) hg[n] = hp[n];
@@ -316,40 +358,15 @@ segment_final(ScanArgs a, Geom g) {
 #pragma unroll
         for (int n = 0; n < N; ++n) hg[n] = 0.0f;
     }
-    if (grp > 0) {
-        // State entering this group: compose the aggregates of groups 0 .. grp-1.
-        // Wave w composes one contiguous range of them; the ranges are then applied in order.
-        const int per = (grp + W - 1) / W;
-        const int k0 = min(grp, wave * per), k1 = min(grp, k0 + per);
-        float Pc[N], Hc[N];
+    if (wave > 0) {
+        cs = ws[wl.CS + ((size_t)b * g.S + s) * D + dc];
+        const float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + dc;
 #pragma unroll
-        for (int n = 0; n < N; ++n) { Pc[n] = 1.0f; Hc[n] = 0.0f; }
-        for (int k = k0; k < k1; ++k) {
-            const float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + k) * N * D + dc;
-            const float* GP = ws + wl.GP + ((size_t)b * (g.G - 1) + k) * N * D + dc;
+        for (int n = 0; n < N; ++n) E[n] = Ep[(size_t)n * D];
+    } else {
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                const float p = GP[(size_t)n * D];
-                Hc[n] = __builtin_fmaf(p, Hc[n], GH[(size_t)n * D]);
-                Pc[n] *= p;
-            }
-        }
-        float* sP = lds;
-        float* sH = sP + W * N * 64;
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            sP[(wave * N + n) * 64 + lane] = Pc[n];
-            sH[(wave * N + n) * 64 + lane] = Hc[n];
-        }
-        __syncthreads();
-        for (int j = 0; j < W; ++j) {
-#pragma unroll
-            for (int n = 0; n < N; ++n)
-                hg[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], hg[n], sH[(j * N + n) * 64 + lane]);
-        }
+        for (int n = 0; n < N; ++n) E[n] = 0.0f;
     }
-    if (len <= 0) return;
-
     float h[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hg[n], E[n]);
@@ -385,10 +402,16 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     const dim3 grid(g.G, (a.D + 63) / 64, a.B);
     const dim3 block(64 * g.W);
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
-    const size_t lds_fin = g.G > 1 ? (size_t)g.W * 2 * N * 64 * sizeof(float) : 0;
+    const size_t lds_fin = 0;
     if (g.S > 1) {
         profile_mark(st);
         hipLaunchKernelGGL((segment_aggregate<N, BF16>), grid, block, lds_agg, st, a, g);
+    }
+    if (g.G > 1) {
+        const size_t tot = (size_t)a.B * N * a.D;
+        profile_mark(st);
+        hipLaunchKernelGGL((group_carry<N>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
+                           a.h0, static_cast<float*>(a.ws), a.B, a.D, g);
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     profile_mark(st);
