@@ -10,7 +10,7 @@
 // and the state after it is H_out = exp(s_last) H_in + sum_j exp(s_last - s_j) Delta_j B_j (x) x_j.
 //
 // Kernels (one workgroup of 8 waves per (batch, head, super-chunk); a
-// super-chunk is a run of consecutive chunks walked in order with the state in LDS):
+// super-chunk is a run of consecutive chunks walked in order):
 //   ssd_super_state  every super-chunk but the last: its aggregate state from a
 //                    zero start, and its total log2 decay;
 //   ssd_chunk_scan   folds the aggregates of earlier super-chunks into the state
@@ -18,14 +18,20 @@
 //                    G^T = B C^T, M = G o decay o Delta (causal), Y_diag = M X,
 //                    y = (Y_off + Y_diag + D x) silu(z), then the chunk state
 //                    S = (w o X)^T B and H <- e^{s_last} H + S.
+// The fp32 state H^T (P x N) lives in registers, each wave owning the 16x16 tiles
+// it accumulates S into; after every update its bf16 high part and bf16
+// remainder are written to LDS, where they are the operands of Y_off.
 // Matrix cores: v_mfma_f32_16x16x32_bf16 throughout. Operands stored in bf16
-// (B, C, x) enter exactly; operands formed in fp32 (H, M, w o x) are split into a
-// bf16 high part and a bf16 remainder, i.e. two MFMAs, which keeps about 16
-// significant bits (a single bf16 rounding would cost ~1e-3 relative error).
-// x and B of a chunk are staged in LDS row-major with plain 16-byte copies;
-// where a product contracts over time, its operand is read with the LDS
-// transpose read (ds_read_b64_tr_b16), which hands each lane four consecutive
-// time steps of one column.
+// (B, C, x) enter exactly; operands formed in fp32 (H, M, w o x) enter as a bf16
+// high part plus a bf16 remainder, i.e. two MFMAs, which keeps about 16
+// significant bits (one bf16 rounding would cost ~1e-3 relative error).
+// x and B rows of a chunk are staged in LDS with 16-byte copies (loaded one chunk
+// ahead into registers); where a product contracts over time, its operand is read
+// with the LDS transpose read (ds_read_b64_tr_b16), which hands each lane four
+// consecutive time steps of one column.
+// Below the diagonal, exp2(s_i - s_j) = exp2(s_i - s_r) exp2(s_r - s_j) with r the
+// last step of j's 32-step block: one exp per row and a per-column factor staged
+// once per chunk (both factors <= 1, so neither can overflow).
 #include "common.h"
 #include "launch.h"
 
@@ -47,17 +53,19 @@ constexpr int kTargetBlocks = 768;  // workgroups of the scan kernel
 constexpr int kP = 64;              // head dim handled
 constexpr int kXS = kP + 16;        // LDS row stride (elements) of x rows
 constexpr int kPad = 16;            // LDS row padding (elements) of B rows
+constexpr int kHPad = 8;            // LDS row padding (elements) of the bf16 state rows
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v = hi + lo with hi the truncation of v to bf16 (exact) and lo = bf16(v - hi)
 __device__ __forceinline__ void split8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)v[e];
-        hi[e] = h;
-        lo[e] = (__bf16)(v[e] - (float)h);
+        const uint32_t u = __float_as_uint(v[e]) & 0xffff0000u;
+        hi[e] = __builtin_bit_cast(__bf16, (u16)(u >> 16));
+        lo[e] = (__bf16)(v[e] - __uint_as_float(u));
     }
 }
 
@@ -98,19 +106,21 @@ SsdGeom ssd_geom(int B, int L, int H, int Q) {
 
 // LDS layout (bytes), per workgroup
 struct Smem {
-    int xs, bs, ht, s2, dt, w, red, total;
+    int xs, bs, hh, hl, s2, dt, w, cf, red, total;
 };
 
 template <int N>
 __host__ __device__ inline Smem smem_layout(int Q) {
     Smem s;
-    s.xs = 0;                              // bf16 [Q][kXS]     x rows of the chunk
-    s.bs = s.xs + Q * kXS * 2;             // bf16 [Q][N+kPad]  B rows of the chunk
-    s.ht = s.bs + Q * (N + kPad) * 2;      // f32  [P][N+4]     state H^T
-    s.s2 = s.ht + kP * (N + 4) * 4;        // f32  [Q]          inclusive log2-decay prefix
-    s.dt = s.s2 + Q * 4;                   // f32  [Q]          Delta
-    s.w = s.dt + Q * 4;                    // f32  [Q]          exp2(s_last - s_t) Delta_t
-    s.red = s.w + Q * 4;                   // f32  [4]          broadcast slot (s_last)
+    s.xs = 0;                              // bf16 [Q][kXS]       x rows of the chunk
+    s.bs = s.xs + Q * kXS * 2;             // bf16 [Q][N+kPad]    B rows of the chunk
+    s.hh = s.bs + Q * (N + kPad) * 2;      // bf16 [P][N+kHPad]   state H^T, high part
+    s.hl = s.hh + kP * (N + kHPad) * 2;    // bf16 [P][N+kHPad]   state H^T, remainder
+    s.s2 = s.hl + kP * (N + kHPad) * 2;    // f32  [Q]   inclusive log2-decay prefix
+    s.dt = s.s2 + Q * 4;                   // f32  [Q]   Delta
+    s.w = s.dt + Q * 4;                    // f32  [Q]   exp2(s_last - s_t) Delta_t
+    s.cf = s.w + Q * 4;                    // f32  [Q]   exp2(s_r - s_t) Delta_t, r = t | 31
+    s.red = s.cf + Q * 4;                  // f32  [4]   broadcast slot (s_last)
     s.total = s.red + 16;
     return s;
 }
@@ -118,26 +128,80 @@ __host__ __device__ inline Smem smem_layout(int Q) {
 // workspace (floats): Hagg [B][H][K-1][P][N], Lam [B][H][K-1]
 __host__ __device__ inline size_t ws_hagg(int B, int H, int K, int N) { return (size_t)B * H * (K - 1) * kP * N; }
 
-// Stage one chunk: Delta, log2-decay prefix and weights (wave 0), x and B rows
-// (all threads). Rows past `len` are zero.
+// Rows of x and B of one chunk held in registers between the global load and the
+// LDS store (so the next chunk's loads overlap the current chunk's work).
 template <int N>
-__device__ void stage_chunk(const SsdArgs& a, char* lds, const Smem& sm, int b, int h, int t0, int len,
-                            float A2) {
+struct ChunkRows {
+    static constexpr int XQ = 256 * (kP / 8) / kThreads;   // 16-byte pieces per thread, Q = 256
+    static constexpr int BQ = 256 * (N / 8) / kThreads;
+    uint4 xv[XQ];
+    uint4 bv[BQ];
+    float dv[4];
+};
+
+template <int N>
+__device__ __forceinline__ void load_x_rows(const SsdArgs& a, int b, int h, int t0, int len, ChunkRows<N>& cr) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int Q = a.Q;
+#pragma unroll
+    for (int k = 0; k < ChunkRows<N>::XQ; ++k) {
+        const int q = tid + k * kThreads;
+        const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
+        cr.xv[k] = make_uint4(0, 0, 0, 0);
+        if (r < len)
+            cr.xv[k] = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.x) +
+                                                       (((size_t)b * a.L + t0 + r) * a.H + h) * kP + c8);
+    }
+    if (wave == 0) {
+        const u16* dp = static_cast<const u16*>(a.delta);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = lane * 4 + k;
+            cr.dv[k] = (t < len) ? bf16_to_f32(dp[((size_t)b * a.L + t0 + t) * a.H + h]) : 0.0f;
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void load_b_rows(const SsdArgs& a, int b, int t0, int len, ChunkRows<N>& cr) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < ChunkRows<N>::BQ; ++k) {
+        const int q = tid + k * kThreads;
+        const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
+        cr.bv[k] = make_uint4(0, 0, 0, 0);
+        if (r < len)
+            cr.bv[k] = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.Bm) + ((size_t)b * a.L + t0 + r) * N + c8);
+    }
+}
+
+// Write a chunk's rows into LDS and (wave 0) its decay prefix, weights and column factors.
+template <int N>
+__device__ __forceinline__ void store_rows(char* lds, const Smem& sm, int Q, int len, float A2, const ChunkRows<N>& cr) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    u16* xs = reinterpret_cast<u16*>(lds + sm.xs);
+    u16* bs = reinterpret_cast<u16*>(lds + sm.bs);
+#pragma unroll
+    for (int k = 0; k < ChunkRows<N>::XQ; ++k) {
+        const int q = tid + k * kThreads;
+        const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
+        if (r < Q) *reinterpret_cast<uint4*>(xs + r * kXS + c8) = cr.xv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < ChunkRows<N>::BQ; ++k) {
+        const int q = tid + k * kThreads;
+        const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
+        if (r < Q) *reinterpret_cast<uint4*>(bs + r * (N + kPad) + c8) = cr.bv[k];
+    }
     if (wave == 0) {
         float* s2 = reinterpret_cast<float*>(lds + sm.s2);
         float* dt = reinterpret_cast<float*>(lds + sm.dt);
         float* w = reinterpret_cast<float*>(lds + sm.w);
+        float* cf = reinterpret_cast<float*>(lds + sm.cf);
         // 4 consecutive steps per lane (Q <= 256), fp64 prefix, then a wave-wide scan
-        const u16* dp = static_cast<const u16*>(a.delta);
-        float dv[4];
         double loc[4], run = 0.0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int t = lane * 4 + k;
-            dv[k] = (t < len) ? bf16_to_f32(dp[((size_t)b * a.L + t0 + t) * a.H + h]) : 0.0f;
-            run += (double)(dv[k] * A2);
+            run += (double)(cr.dv[k] * A2);
             loc[k] = run;
         }
         double incl = run;
@@ -147,42 +211,34 @@ __device__ void stage_chunk(const SsdArgs& a, char* lds, const Smem& sm, int b, 
             if (lane >= off) incl += v;
         }
         const double excl = incl - run;
+        float sv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = lane * 4 + k;
+            sv[k] = (float)(excl + loc[k]);
+            if (t >= len) sv[k] = 0.0f;
+        }
         float sl;
         {
             const int ll = (len - 1) >> 2, kk = (len - 1) & 3;
-            const double lk = kk == 0 ? loc[0] : kk == 1 ? loc[1] : kk == 2 ? loc[2] : loc[3];
-            sl = (float)__shfl(excl + lk, ll, 64);
+            const float lk = kk == 0 ? sv[0] : kk == 1 ? sv[1] : kk == 2 ? sv[2] : sv[3];
+            sl = __shfl(lk, ll, 64);
         }
+        // end of each 32-step block (lanes 8m .. 8m+7 cover block m): held by lane 8m+7, element 3
+        const float send = __shfl(sv[3], (lane & ~7) | 7, 64);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int t = lane * 4 + k;
             if (t < Q) {
-                const float sv = t < len ? (float)(excl + loc[k]) : sl;
-                s2[t] = sv;
-                dt[t] = dv[k];
-                w[t] = t < len ? exp2_fast(sl - sv) * dv[k] : 0.0f;
+                const float s = t < len ? sv[k] : sl;
+                const float r = min(t | 31, len - 1) == t ? s : (((t | 31) < len) ? send : sl);
+                s2[t] = s;
+                dt[t] = cr.dv[k];
+                w[t] = t < len ? exp2_fast(sl - s) * cr.dv[k] : 0.0f;
+                cf[t] = t < len ? exp2_fast(r - s) * cr.dv[k] : 0.0f;
             }
         }
         if (lane == 0) reinterpret_cast<float*>(lds + sm.red)[0] = sl;
-    }
-    // x rows: 8 x 16 B per row
-    u16* xs = reinterpret_cast<u16*>(lds + sm.xs);
-    for (int q = tid; q < Q * (kP / 8); q += kThreads) {
-        const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < len)
-            v = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.x) +
-                                                (((size_t)b * a.L + t0 + r) * a.H + h) * kP + c8);
-        *reinterpret_cast<uint4*>(xs + r * kXS + c8) = v;
-    }
-    // B rows: N/8 x 16 B per row
-    u16* bs = reinterpret_cast<u16*>(lds + sm.bs);
-    for (int q = tid; q < Q * (N / 8); q += kThreads) {
-        const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < len)
-            v = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.Bm) + ((size_t)b * a.L + t0 + r) * N + c8);
-        *reinterpret_cast<uint4*>(bs + r * (N + kPad) + c8) = v;
     }
 }
 
@@ -229,22 +285,50 @@ __device__ __forceinline__ void chunk_state(const char* lds, const Smem& sm, int
     }
 }
 
-// H^T <- exp2(s_last) H^T + S^T on this wave's tiles
+// The fp32 state on this wave's tiles (same layout as StateTiles).
 template <int N>
-__device__ __forceinline__ void state_update(char* lds, const Smem& sm, const StateTiles<N>& st) {
+struct State {
+    f32x4 h[StateTiles<N>::NBW];
+};
+
+// H <- exp2(s_last) H + S (registers)
+template <int N>
+__device__ __forceinline__ void state_update(const char* lds, const Smem& sm, State<N>& hs, const StateTiles<N>& st) {
+    const float decay = exp2_fast(reinterpret_cast<const float*>(lds + sm.red)[0]);
+#pragma unroll
+    for (int k = 0; k < StateTiles<N>::NBW; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs.h[k][r] = __builtin_fmaf(decay, hs.h[k][r], st.acc[k][r]);
+}
+
+// bf16 high part and remainder of this wave's state tiles into LDS
+template <int N>
+__device__ __forceinline__ void state_to_lds(char* lds, const Smem& sm, const State<N>& hs) {
     constexpr int NBW = StateTiles<N>::NBW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int pb = wave & 3, nb0 = (wave >> 2) * NBW;
-    float* ht = reinterpret_cast<float*>(lds + sm.ht);
-    const float decay = exp2_fast(reinterpret_cast<const float*>(lds + sm.red)[0]);
+    u16* hh = reinterpret_cast<u16*>(lds + sm.hh);
+    u16* hl = reinterpret_cast<u16*>(lds + sm.hl);
 #pragma unroll
     for (int k = 0; k < NBW; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float* p = ht + (pb * 16 + 4 * g + r) * (N + 4) + (nb0 + k) * 16 + c;
-            *p = __builtin_fmaf(decay, *p, st.acc[k][r]);
+            const float v = hs.h[k][r];
+            const uint32_t u = __float_as_uint(v) & 0xffff0000u;
+            const int off = (pb * 16 + 4 * g + r) * (N + kHPad) + (nb0 + k) * 16 + c;
+            hh[off] = (u16)(u >> 16);
+            hl[off] = f32_to_bf16(v - __uint_as_float(u));
         }
+}
+
+// Element (p, n) of this lane's state tiles, for k = n-block offset, r = row offset
+template <int N>
+__device__ __forceinline__ void tile_pn(int k, int r, int& p, int& n) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    p = (wave & 3) * 16 + 4 * g + r;
+    n = ((wave >> 2) * StateTiles<N>::NBW + k) * 16 + c;
 }
 
 template <int N>
@@ -253,66 +337,77 @@ ssd_super_state(SsdArgs a, SsdGeom geo) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const Smem sm = smem_layout<N>(geo.Q);
     const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x;
     const float A2 = a.A[h] * kLog2e;
-    float* ht = reinterpret_cast<float*>(lds + sm.ht);
-    for (int i = tid; i < kP * (N + 4); i += kThreads) ht[i] = 0.0f;
+    State<N> hs;
+#pragma unroll
+    for (int kk = 0; kk < StateTiles<N>::NBW; ++kk) hs.h[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
     double lam = 0.0;
     const int c0 = k * geo.cps, c1 = min(geo.C, c0 + geo.cps);
+    ChunkRows<N> cr;
+    load_x_rows<N>(a, b, h, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
+    load_b_rows<N>(a, b, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
     for (int cc = c0; cc < c1; ++cc) {
         const int t0 = cc * geo.Q;
         const int len = min(geo.Q, a.L - t0);
         __syncthreads();  // previous chunk fully consumed
-        stage_chunk<N>(a, lds, sm, b, h, t0, len, A2);
+        store_rows<N>(lds, sm, geo.Q, len, A2, cr);
         __syncthreads();
+        if (cc + 1 < c1) {
+            const int ln = min(geo.Q, a.L - t0 - geo.Q);
+            load_x_rows<N>(a, b, h, t0 + geo.Q, ln, cr);
+            load_b_rows<N>(a, b, t0 + geo.Q, ln, cr);
+        }
         StateTiles<N> st;
         chunk_state<N>(lds, sm, len, st);
         lam += (double)reinterpret_cast<const float*>(lds + sm.red)[0];
-        state_update<N>(lds, sm, st);
+        state_update<N>(lds, sm, hs, st);
     }
-    __syncthreads();
     float* out = static_cast<float*>(a.ws) + (((size_t)b * a.H + h) * (geo.K - 1) + k) * kP * N;
-    for (int i = tid; i < kP * N; i += kThreads) out[i] = ht[(i / N) * (N + 4) + (i % N)];
-    if (tid == 0) {
+#pragma unroll
+    for (int kk = 0; kk < StateTiles<N>::NBW; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int p, n;
+            tile_pn<N>(kk, r, p, n);
+            out[p * N + n] = hs.h[kk][r];
+        }
+    if (threadIdx.x == 0) {
         float* lamp = static_cast<float*>(a.ws) + ws_hagg(a.B, a.H, geo.K, N);
         lamp[((size_t)b * a.H + h) * (geo.K - 1) + k] = (float)lam;
     }
 }
 
-// Outputs of one 16-row block I of a chunk.
-template <int N, bool HAS_Z, bool HAS_D>
+// Outputs of one 16-row block I of a chunk, for NPB p-blocks starting at pb0.
+template <int N, int NPB, bool HAS_Z, bool HAS_D>
 __device__ __forceinline__ void chunk_rows(const SsdArgs& a, const char* lds, const Smem& sm, int b, int h,
-                                           int t0, int len, int I, const bf16x8 (&cop)[N / 32], float Dh) {
+                                           int t0, int len, int I, int pb0, const bf16x8 (&cop)[N / 32], float Dh) {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
     const u16* xs = reinterpret_cast<const u16*>(lds + sm.xs);
     const u16* bs = reinterpret_cast<const u16*>(lds + sm.bs);
-    const float* ht = reinterpret_cast<const float*>(lds + sm.ht);
+    const u16* hh = reinterpret_cast<const u16*>(lds + sm.hh);
+    const u16* hl = reinterpret_cast<const u16*>(lds + sm.hl);
     const float* s2 = reinterpret_cast<const float*>(lds + sm.s2);
     const float* dt = reinterpret_cast<const float*>(lds + sm.dt);
+    const float* cf = reinterpret_cast<const float*>(lds + sm.cf);
     const int ia = I * 16 + c;  // this lane's A-operand row
-    f32x4 acc[kP / 16];
+    f32x4 acc[NPB];
 #pragma unroll
-    for (int pb = 0; pb < kP / 16; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Y_off = C H (H^T rows are the B operand), then rows scaled by exp2(s_i)
+    for (int q = 0; q < NPB; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Y_off = C H: the state's bf16 high part and remainder (rows of H^T) are B operands
 #pragma unroll
     for (int kb = 0; kb < N / 32; ++kb)
 #pragma unroll
-        for (int pb = 0; pb < kP / 16; ++pb) {
-            const float* hp = ht + (pb * 16 + c) * (N + 4) + kb * 32 + 8 * g;
-            const f32x4 h0v = *reinterpret_cast<const f32x4*>(hp);
-            const f32x4 h1v = *reinterpret_cast<const f32x4*>(hp + 4);
-            const float v[8] = {h0v[0], h0v[1], h0v[2], h0v[3], h1v[0], h1v[1], h1v[2], h1v[3]};
-            bf16x8 hhi, hlo;
-            split8(v, hhi, hlo);
-            acc[pb] = mfma(cop[kb], hhi, acc[pb]);
-            acc[pb] = mfma(cop[kb], hlo, acc[pb]);
+        for (int q = 0; q < NPB; ++q) {
+            const int off = ((pb0 + q) * 16 + c) * (N + kHPad) + kb * 32 + 8 * g;
+            acc[q] = mfma(cop[kb], ld_bf16x8(hh + off), acc[q]);
+            acc[q] = mfma(cop[kb], ld_bf16x8(hl + off), acc[q]);
         }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float sc = exp2_fast(s2[I * 16 + 4 * g + r]);
 #pragma unroll
-        for (int pb = 0; pb < kP / 16; ++pb) acc[pb][r] *= sc;
+        for (int q = 0; q < NPB; ++q) acc[q][r] *= sc;
     }
     // Y_diag = M X over 32-wide column blocks J up to the block's last row
     const float s2i = s2[ia];
@@ -326,34 +421,46 @@ __device__ __forceinline__ void chunk_rows(const SsdArgs& a, const char* lds, co
             g1 = mfma(b1, cop[kb], g1);  //            and G[ia][J*32 + 16 + 4g + r]
         }
         float m[8];
+        if (J * 32 + 31 < I * 16) {
+            // whole column block below this row block: row factor x column factor
+            const float rowf = exp2_fast(s2i - s2[J * 32 + 31]);
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(cf + J * 32 + 4 * g);
+            const f32x4 c1 = *reinterpret_cast<const f32x4*>(cf + J * 32 + 16 + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = J * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-            const float gv = e < 4 ? g0[e] : g1[e - 4];
-            const bool ok = (j <= ia) && (j < len) && (ia < len);
-            m[e] = ok ? gv * exp2_fast(s2i - s2[j]) * dt[j] : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                m[e] = g0[e] * rowf * c0[e];
+                m[e + 4] = g1[e] * rowf * c1[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = J * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+                const float gv = e < 4 ? g0[e] : g1[e - 4];
+                const bool ok = (j <= ia) && (j < len);
+                m[e] = ok ? gv * exp2_fast(s2i - s2[j]) * dt[j] : 0.0f;
+            }
         }
         bf16x8 mhi, mlo;
         split8(m, mhi, mlo);
 #pragma unroll
-        for (int pb = 0; pb < kP / 16; ++pb) {
+        for (int q = 0; q < NPB; ++q) {
             // x at the same (g, e) -> j mapping: two runs of 4 steps
-            const bf16x8 xop = cat(ld_tr4(xs, kXS, J * 32 + 4 * g, pb * 16),
-                                   ld_tr4(xs, kXS, J * 32 + 16 + 4 * g, pb * 16));
-            acc[pb] = mfma(mhi, xop, acc[pb]);
-            acc[pb] = mfma(mlo, xop, acc[pb]);
+            const bf16x8 xop = cat(ld_tr4(xs, kXS, J * 32 + 4 * g, (pb0 + q) * 16),
+                                   ld_tr4(xs, kXS, J * 32 + 16 + 4 * g, (pb0 + q) * 16));
+            acc[q] = mfma(mhi, xop, acc[q]);
+            acc[q] = mfma(mlo, xop, acc[q]);
         }
     }
-    // epilogue: rows i = I*16 + 4g + r, columns p = pb*16 + c
+    // epilogue: rows i = I*16 + 4g + r, columns p = (pb0 + q)*16 + c
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = I * 16 + 4 * g + r;
         if (i >= len) continue;
         const size_t rowoff = (((size_t)b * a.L + t0 + i) * a.H + h) * kP;
 #pragma unroll
-        for (int pb = 0; pb < kP / 16; ++pb) {
-            const int p = pb * 16 + c;
-            float v = acc[pb][r];
+        for (int q = 0; q < NPB; ++q) {
+            const int p = (pb0 + q) * 16 + c;
+            float v = acc[q][r];
             if constexpr (HAS_D) v = __builtin_fmaf(Dh, bf16_to_f32(xs[i * kXS + p]), v);
             if constexpr (HAS_Z) v *= silu(bf16_to_f32(static_cast<const u16*>(a.z)[rowoff + p]));
             static_cast<u16*>(a.y)[rowoff + p] = f32_to_bf16(v);
@@ -372,62 +479,103 @@ ssd_chunk_scan(SsdArgs a, SsdGeom geo) {
     const int g = lane >> 4, c = lane & 15;
     const float A2 = a.A[h] * kLog2e;
     const float Dh = HAS_D ? a.Dskip[h] : 0.0f;
-    float* ht = reinterpret_cast<float*>(lds + sm.ht);
+    const int c0 = k * geo.cps, c1 = min(geo.C, c0 + geo.cps);
+
+    ChunkRows<N> cr;
+    load_x_rows<N>(a, b, h, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
+    load_b_rows<N>(a, b, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
 
     // state entering this super-chunk: h0 folded with the earlier aggregates
+    State<N> hs;
     {
         const float* hagg = static_cast<const float*>(a.ws);
         const float* lamp = hagg + ws_hagg(a.B, a.H, geo.K, N);
-        for (int i = tid; i < kP * N; i += kThreads) {
-            const int p = i / N, n = i % N;
-            float v = a.h0 ? a.h0[(((size_t)b * a.H + h) * N + n) * kP + p] : 0.0f;
-            for (int kk = 0; kk < k; ++kk) {
-                const size_t base = ((size_t)b * a.H + h) * (geo.K - 1) + kk;
-                v = __builtin_fmaf(exp2_fast(lamp[base]), v, hagg[base * kP * N + i]);
+#pragma unroll
+        for (int kk = 0; kk < StateTiles<N>::NBW; ++kk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                int p, n;
+                tile_pn<N>(kk, r, p, n);
+                hs.h[kk][r] = a.h0 ? a.h0[(((size_t)b * a.H + h) * N + n) * kP + p] : 0.0f;
             }
-            ht[p * (N + 4) + n] = v;
+        for (int j = 0; j < k; ++j) {
+            const size_t base = ((size_t)b * a.H + h) * (geo.K - 1) + j;
+            const float dec = exp2_fast(lamp[base]);
+#pragma unroll
+            for (int kk = 0; kk < StateTiles<N>::NBW; ++kk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    int p, n;
+                    tile_pn<N>(kk, r, p, n);
+                    hs.h[kk][r] = __builtin_fmaf(dec, hs.h[kk][r], hagg[base * kP * N + p * N + n]);
+                }
         }
+        state_to_lds<N>(lds, sm, hs);
     }
     const bool last_super = (k == geo.K - 1);
-    const int c0 = k * geo.cps, c1 = min(geo.C, c0 + geo.cps);
     const u16* Cg = static_cast<const u16*>(a.Cm);
-    // row blocks of this wave: 16-row blocks pair up (I, R-1-I) to balance the causal work
+    // Work split of the output phase over the 8 waves, by the number R of 16-row blocks:
+    //   R >= 8: wave w takes block w and, when R - 1 - w >= 8, block R - 1 - w too
+    //           (pairs balance the causal work), all 4 p-blocks;
+    //   R = 4:  wave w takes block w % 4 and 2 of the p-blocks;
+    //   R = 2:  wave w takes block w % 2 and 1 p-block;
+    //   R = 6:  waves 0..5 take one block each, all p-blocks.
     const int R = geo.Q / 16;
-    const int I0 = wave, I1 = (R == 16) ? 15 - wave : -1;
+    int I0 = wave, I1 = -1, npb = 4, pb0 = 0;
+    if (R >= 8) {
+        if (R - 1 - wave >= 8) I1 = R - 1 - wave;
+    } else if (R == 4) {
+        I0 = wave & 3; npb = 2; pb0 = (wave >> 2) * 2;
+    } else if (R == 2) {
+        I0 = wave & 1; npb = 1; pb0 = wave >> 1;
+    } else if (wave >= R) {
+        I0 = -1;
+    }
     for (int cc = c0; cc < c1; ++cc) {
         const int t0 = cc * geo.Q;
         const int len = min(geo.Q, a.L - t0);
-        // C rows of this wave's blocks straight from global (prefetched before the barrier)
+        // C rows of this wave's blocks straight from global
         bf16x8 cop0[N / 32], cop1[N / 32];
 #pragma unroll
         for (int kb = 0; kb < N / 32; ++kb) {
             const int i0 = I0 * 16 + c, i1 = I1 * 16 + c;
-            cop0[kb] = (I0 < R && i0 < len) ? ld_bf16x8(Cg + ((size_t)b * a.L + t0 + i0) * N + kb * 32 + 8 * g)
-                                            : bf16x8{};
+            cop0[kb] = (I0 >= 0 && i0 < len) ? ld_bf16x8(Cg + ((size_t)b * a.L + t0 + i0) * N + kb * 32 + 8 * g) : bf16x8{};
             cop1[kb] = (I1 >= 0 && i1 < len) ? ld_bf16x8(Cg + ((size_t)b * a.L + t0 + i1) * N + kb * 32 + 8 * g)
                                              : bf16x8{};
         }
+        __syncthreads();  // previous chunk's LDS reads done, state copy written
+        store_rows<N>(lds, sm, geo.Q, len, A2, cr);
         __syncthreads();
-        stage_chunk<N>(a, lds, sm, b, h, t0, len, A2);
-        __syncthreads();
-        if (I0 < R && I0 * 16 < len) chunk_rows<N, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, cop0, Dh);
-        if (I1 >= 0 && I1 * 16 < len) chunk_rows<N, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I1, cop1, Dh);
+        // next chunk's x rows and Delta load during the output phase, its B rows after it
+        const int ln = cc + 1 < c1 ? min(geo.Q, a.L - t0 - geo.Q) : 0;
+        if (ln > 0) load_x_rows<N>(a, b, h, t0 + geo.Q, ln, cr);
+        if (I0 >= 0 && I0 * 16 < len) {
+            if (npb == 4) chunk_rows<N, 4, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, pb0, cop0, Dh);
+            else if (npb == 2) chunk_rows<N, 2, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, pb0, cop0, Dh);
+            else chunk_rows<N, 1, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, pb0, cop0, Dh);
+        }
+        if (I1 >= 0 && I1 * 16 < len) chunk_rows<N, 4, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I1, 0, cop1, Dh);
+        if (ln > 0) load_b_rows<N>(a, b, t0 + geo.Q, ln, cr);
         // state after the chunk (not needed after the last chunk of a super-chunk,
         // except at the very end of the sequence for h_final)
         const bool need_state = (cc < c1 - 1) || (last_super && a.h_final != nullptr);
         if (need_state) {
             StateTiles<N> st;
             chunk_state<N>(lds, sm, len, st);
-            __syncthreads();  // every wave has finished reading H^T for Y_off
-            state_update<N>(lds, sm, st);
+            state_update<N>(lds, sm, hs, st);
+            __syncthreads();  // every wave has finished reading the state copy for Y_off
+            if (cc < c1 - 1) state_to_lds<N>(lds, sm, hs);
         }
     }
     if (last_super && a.h_final != nullptr) {
-        __syncthreads();
-        for (int i = tid; i < kP * N; i += kThreads) {
-            const int n = i / kP, p = i % kP;
-            a.h_final[(((size_t)b * a.H + h) * N + n) * kP + p] = ht[p * (N + 4) + n];
-        }
+#pragma unroll
+        for (int kk = 0; kk < StateTiles<N>::NBW; ++kk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                int p, n;
+                tile_pn<N>(kk, r, p, n);
+                a.h_final[(((size_t)b * a.H + h) * N + n) * kP + p] = hs.h[kk][r];
+            }
     }
 }
 

@@ -56,6 +56,9 @@ SMALL = [
     (3, 96, 2, 64, 64, True, True, True),
     (1, 1, 2, 128, 256, True, True, True),
     (1, 2100, 2, 64, 96, True, True, True),
+    (1, 800, 2, 128, 192, True, True, True),
+    (2, 700, 1, 64, 224, False, True, True),
+    (1, 650, 2, 128, 160, True, False, True),
 ]
 
 
