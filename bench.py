@@ -163,6 +163,25 @@ def time_calls(call, sets, steps, warmup, n_kernels):
     return total_ms, ker
 
 
+def committed_traffic(kernel_source, workload):
+    """HBM bytes per launch of the dominant kernel, from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary for this workload -- only while the kernel's
+    source is byte-identical to the one the counters were taken on."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    src = os.path.join(ROOT, "selective_scan_amd", "csrc", kernel_source)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    if not (m_b and m_h):
+        return None
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return int(m_b.group(1)) if cur == m_h.group(1) else None
+
+
 def scan_bench(name, wl, steps, warmup, dev):
     sets, ws, w0, set_bytes = scan_setup(wl, dev)
     nk = count_kernels(lambda: scan_call(sets[0], ws))
@@ -183,7 +202,7 @@ def scan_bench(name, wl, steps, warmup, dev):
     achieved = SLOTS_PER_UPDATE * upd / tdom / 1e12
     peak = LANE_SLOTS_PER_S / 1e12
     res["roofline"] = dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s",
-                           frac=achieved / peak, traffic=None,
+                           frac=achieved / peak, traffic=committed_traffic("scan_fwd.hip", name),
                            kernel="segment_kernel (final pass)" if nk > 1 else "segment_kernel")
     res["hbm_roofline_dominant"] = dict(achieved=alg / tdom / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
                                         frac=alg / tdom / 1e9 / HBM_PEAK_GBS)
