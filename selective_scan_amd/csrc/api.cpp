@@ -172,6 +172,7 @@ int ssm_step(int B, int D, int N, int io,
     if (!ssm::step_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64");
     if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
     if (!product_ok({B, D, N}, 1LL << 40)) return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if ((long long)D * N > (1LL << 32)) return fail(SSM_ERR_UNSUPPORTED, fn, "D * N must be <= 2^32");
     if (!state || !x || !delta || !A || !Bm || !Cm || !y)
         return fail(SSM_ERR_INVALID_ARG, fn, "state, x, delta, A, Bm, Cm and y are required");
     const void* ptrs[] = {state, x, delta, A, Bm, Cm, Dskip, z, y};

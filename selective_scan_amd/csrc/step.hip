@@ -3,75 +3,111 @@
 // ("Efficient Sequence Modeling: From S4 to Mamba-3", section 03: mamba_minimal.py
 // has an incremental step() for decoding; section 09: step() equals a full forward).
 //
-// Bandwidth-bound: one lane per (batch, channel) reads its N-float state row and
-// its A row with 16-byte vector loads, B and C of its batch row are wave-uniform
-// (scalar loads), and the state is written back once. Workgroups never straddle
-// two batch rows, so the uniform loads are valid for every lane.
+// Bandwidth-bound: the state row of a (batch, channel) pair is N contiguous floats,
+// and A is [D][N], so both are walked as flat float4 arrays. QPC = N/4 consecutive
+// lanes share a channel, each owning one float4 quarter of its state, so every
+// load/store instruction of a wave covers 1 KiB of contiguous state. Each lane
+// handles kReps quarters spaced one workgroup apart; the quarter index within the
+// channel is the same for all of them (the workgroup size is a multiple of QPC),
+// so a lane reads its 4 B and 4 C values once. C . h is summed over the QPC lanes
+// with cross-lane shuffles and the channel's first lane writes y.
 #include "common.h"
 #include "launch.h"
+
+#ifndef SSM_STEP_REPS
+#define SSM_STEP_REPS 2
+#endif
 
 namespace ssm {
 namespace {
 
-template <int N, bool BF16, bool HAS_Z, bool HAS_D>
-__global__ void __launch_bounds__(256) step_kernel(StepArgs a) {
-    const int b = blockIdx.y;
-    const int d = blockIdx.x * blockDim.x + threadIdx.x;
-    const int D = a.D;
-    if (d >= D) return;
-    const size_t i = (size_t)b * D + d;
-    float dv, xv, zv = 0.0f;
-    if constexpr (BF16) {
-        dv = bf16_to_f32(static_cast<const uint16_t*>(a.delta)[i]);
-        xv = bf16_to_f32(static_cast<const uint16_t*>(a.x)[i]);
-        if constexpr (HAS_Z) zv = bf16_to_f32(static_cast<const uint16_t*>(a.z)[i]);
-    } else {
-        dv = static_cast<const float*>(a.delta)[i];
-        xv = static_cast<const float*>(a.x)[i];
-        if constexpr (HAS_Z) zv = static_cast<const float*>(a.z)[i];
-    }
-    float Bt[N], Ct[N];
-    load_uniform_row<N, BF16>(a.Bm, b, Bt);
-    load_uniform_row<N, BF16>(a.Cm, b, Ct);
+constexpr int kStepThreads = 256;
+constexpr int kReps = SSM_STEP_REPS;
 
-    float4* st = reinterpret_cast<float4*>(a.state + i * N);
-    const float4* Ar = reinterpret_cast<const float4*>(a.A + (size_t)d * N);
-    float h[N], A2[N];
-#pragma unroll
-    for (int k = 0; k < N / 4; ++k) {
-        const float4 s4 = st[k];
-        const float4 a4 = Ar[k];
-        h[4 * k] = s4.x; h[4 * k + 1] = s4.y; h[4 * k + 2] = s4.z; h[4 * k + 3] = s4.w;
-        A2[4 * k] = a4.x * kLog2e; A2[4 * k + 1] = a4.y * kLog2e;
-        A2[4 * k + 2] = a4.z * kLog2e; A2[4 * k + 3] = a4.w * kLog2e;
+template <bool BF16>
+__device__ __forceinline__ float load_io_at(const void* p, size_t i) {
+    if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    else return static_cast<const float*>(p)[i];
+}
+
+// The 4 values of row `row` of an [.][N] io-dtype matrix starting at column 4q.
+template <int N, bool BF16>
+__device__ __forceinline__ float4 load_quarter(const void* p, int row, int q) {
+    if constexpr (BF16) {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + (size_t)row * N + 4 * q);
+        return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+    } else {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + (size_t)row * N + 4 * q);
     }
-    const float u = dv * xv;
-    float y0 = 0.0f, y1 = 0.0f;
+}
+
+template <int N, bool BF16, bool HAS_Z, bool HAS_D>
+__global__ void __launch_bounds__(kStepThreads) step_kernel(StepArgs a) {
+    constexpr int QPC = N / 4;
+    static_assert(kStepThreads % QPC == 0, "a channel's lanes must not straddle two reps");
+    const int b = blockIdx.y;
+    const int t = threadIdx.x;
+    const int q = t & (QPC - 1);
+    const int D = a.D;
+    const int F = D * QPC;  // float4 quarters in one batch row
+    const int f0 = blockIdx.x * (kStepThreads * kReps) + t;
+
+    const float4 Bq = load_quarter<N, BF16>(a.Bm, b, q);
+    const float4 Cq = load_quarter<N, BF16>(a.Cm, b, q);
+    float4* st = reinterpret_cast<float4*>(a.state + (size_t)b * D * N);
+    const float4* Af = reinterpret_cast<const float4*>(a.A);
+
+    float4 h[kReps], A4[kReps];
+    float dv[kReps], xv[kReps], zv[kReps];
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        h[n] = __builtin_fmaf(exp2_fast(dv * A2[n]), h[n], u * Bt[n]);
-        if (n & 1) y1 = __builtin_fmaf(Ct[n], h[n], y1);
-        else y0 = __builtin_fmaf(Ct[n], h[n], y0);
+    for (int r = 0; r < kReps; ++r) {
+        const int f = f0 + r * kStepThreads;
+        const int d = f / QPC;
+        if (f < F) {
+            h[r] = st[f];
+            A4[r] = Af[f];
+            dv[r] = load_io_at<BF16>(a.delta, (size_t)b * D + d);
+            xv[r] = load_io_at<BF16>(a.x, (size_t)b * D + d);
+            zv[r] = HAS_Z ? load_io_at<BF16>(a.z, (size_t)b * D + d) : 0.0f;
+        } else {
+            h[r] = A4[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            dv[r] = xv[r] = zv[r] = 0.0f;
+        }
     }
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) st[k] = make_float4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
-    float v = y0 + y1;
-    if constexpr (HAS_D) v = __builtin_fmaf(a.Dskip[d], xv, v);
-    if constexpr (HAS_Z) v *= silu(zv);
-    if constexpr (BF16) static_cast<uint16_t*>(a.y)[i] = f32_to_bf16(v);
-    else static_cast<float*>(a.y)[i] = v;
+    for (int r = 0; r < kReps; ++r) {
+        const int f = f0 + r * kStepThreads;
+        const float dt = dv[r], u = dv[r] * xv[r];
+        float4 hn;
+        hn.x = __builtin_fmaf(exp2_fast(dt * kLog2e * A4[r].x), h[r].x, u * Bq.x);
+        hn.y = __builtin_fmaf(exp2_fast(dt * kLog2e * A4[r].y), h[r].y, u * Bq.y);
+        hn.z = __builtin_fmaf(exp2_fast(dt * kLog2e * A4[r].z), h[r].z, u * Bq.z);
+        hn.w = __builtin_fmaf(exp2_fast(dt * kLog2e * A4[r].w), h[r].w, u * Bq.w);
+        if (f < F) st[f] = hn;
+        float p = __builtin_fmaf(Cq.x, hn.x, Cq.y * hn.y) + __builtin_fmaf(Cq.z, hn.z, Cq.w * hn.w);
+#pragma unroll
+        for (int o = QPC / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o);
+        if (q == 0 && f < F) {
+            const int d = f / QPC;
+            float v = p;
+            if constexpr (HAS_D) v = __builtin_fmaf(a.Dskip[d], xv[r], v);
+            if constexpr (HAS_Z) v *= silu(zv[r]);
+            if constexpr (BF16) static_cast<uint16_t*>(a.y)[(size_t)b * D + d] = f32_to_bf16(v);
+            else static_cast<float*>(a.y)[(size_t)b * D + d] = v;
+        }
+    }
 }
 
 template <int N, bool BF16>
 hipError_t launch_n(const StepArgs& a, hipStream_t st) {
-    const int threads = a.D >= 256 ? 256 : ((a.D + 63) / 64) * 64;
-    const dim3 grid((unsigned)((a.D + threads - 1) / threads), (unsigned)a.B);
+    const long F = (long)a.D * (N / 4);
+    const dim3 grid((unsigned)((F + kStepThreads * kReps - 1) / (kStepThreads * kReps)), (unsigned)a.B);
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     profile_mark(st);
-    if (hz && hd) hipLaunchKernelGGL((step_kernel<N, BF16, true, true>), grid, dim3(threads), 0, st, a);
-    else if (hz) hipLaunchKernelGGL((step_kernel<N, BF16, true, false>), grid, dim3(threads), 0, st, a);
-    else if (hd) hipLaunchKernelGGL((step_kernel<N, BF16, false, true>), grid, dim3(threads), 0, st, a);
-    else hipLaunchKernelGGL((step_kernel<N, BF16, false, false>), grid, dim3(threads), 0, st, a);
+    if (hz && hd) hipLaunchKernelGGL((step_kernel<N, BF16, true, true>), grid, dim3(kStepThreads), 0, st, a);
+    else if (hz) hipLaunchKernelGGL((step_kernel<N, BF16, true, false>), grid, dim3(kStepThreads), 0, st, a);
+    else if (hd) hipLaunchKernelGGL((step_kernel<N, BF16, false, true>), grid, dim3(kStepThreads), 0, st, a);
+    else hipLaunchKernelGGL((step_kernel<N, BF16, false, false>), grid, dim3(kStepThreads), 0, st, a);
     profile_mark(st);
     return hipGetLastError();
 }
