@@ -120,7 +120,7 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
  *             when Q does not divide L. The result does not depend on Q beyond
  *             rounding.
  * Supported: io = SSM_BF16; N in {64, 128}; P = 64; chunk a multiple of 32 in
- * [32, 256]; B, H <= 65535.
+ * [32, 256]; B, H <= 65535; B * H <= 2^24; L * H * P * 2 < 2^31.
  * ------------------------------------------------------------------------- */
 size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk);
 

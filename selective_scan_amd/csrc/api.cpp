@@ -146,6 +146,7 @@ int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
     const char* why = ssm::ssd_unsupported_reason(L, H, P, N, Q, io == SSM_BF16);
     if (why[0] != '\0') return fail(SSM_ERR_UNSUPPORTED, fn, why);
     if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
+    if ((long long)B * H > (1LL << 24)) return fail(SSM_ERR_UNSUPPORTED, fn, "B * H must be <= 2^24");
     if (!product_ok({B, L, H, P}, 1LL << 40) || !product_ok({B, H, N, P}, 1LL << 40))
         return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
     if (!A) return fail(SSM_ERR_INVALID_ARG, fn, "A is NULL");

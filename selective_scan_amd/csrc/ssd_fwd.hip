@@ -12,26 +12,35 @@
 // Kernels (one workgroup of 8 waves per (batch, head, super-chunk); a
 // super-chunk is a run of consecutive chunks walked in order):
 //   ssd_super_state  every super-chunk but the last: its aggregate state from a
-//                    zero start, and its total log2 decay;
-//   ssd_chunk_scan   folds the aggregates of earlier super-chunks into the state
-//                    entering its own, then for every chunk: Y_off = diag(e^s) C H,
-//                    G^T = B C^T, M = G o decay o Delta (causal), Y_diag = M X,
-//                    y = (Y_off + Y_diag + D x) silu(z), then the chunk state
-//                    S = (w o X)^T B and H <- e^{s_last} H + S.
+//                    zero start and its total log2 decay;
+//   ssd_carry        per (batch, head, state element), a linear walk over the
+//                    super-chunks that turns the aggregates into the state
+//                    entering each super-chunk (h0 folded in), in place;
+//   ssd_chunk_scan   starting from its entering state, for every chunk:
+//                    Y_off = diag(e^s) C H, G^T = B C^T, M = G o decay o Delta
+//                    (causal), Y_diag = M X, y = (Y_off + Y_diag + D x) silu(z),
+//                    then the chunk state S = (w o X)^T B and H <- e^{s_last} H + S.
 // The fp32 state H^T (P x N) lives in registers, each wave owning the 16x16 tiles
 // it accumulates S into; after every update its bf16 high part and bf16
 // remainder are written to LDS, where they are the operands of Y_off.
-// Matrix cores: v_mfma_f32_16x16x32_bf16 throughout. Operands stored in bf16
-// (B, C, x) enter exactly; operands formed in fp32 (H, M, w o x) enter as a bf16
-// high part plus a bf16 remainder, i.e. two MFMAs, which keeps about 16
-// significant bits (one bf16 rounding would cost ~1e-3 relative error).
-// x and B rows of a chunk are staged in LDS with 16-byte copies (loaded one chunk
-// ahead into registers); where a product contracts over time, its operand is read
-// with the LDS transpose read (ds_read_b64_tr_b16), which hands each lane four
+// Matrix cores: the output phase works on 32-row blocks with
+// v_mfma_f32_32x32x16_bf16 (each B / x / state operand fetched from LDS feeds
+// twice the flops of a 16x16 tile); the chunk state uses v_mfma_f32_16x16x32_bf16.
+// Operands stored in bf16 (B, C, x) enter exactly; operands formed in fp32
+// (H, M, w o x) enter as a bf16 high part plus a bf16 remainder, i.e. two MFMAs,
+// which keeps about 16 significant bits (one bf16 rounding would cost ~1e-3
+// relative error). Where a product contracts over time, its operand is read with
+// the LDS transpose read (ds_read_b64_tr_b16), which hands each lane four
 // consecutive time steps of one column.
 // Below the diagonal, exp2(s_i - s_j) = exp2(s_i - s_r) exp2(s_r - s_j) with r the
 // last step of j's 32-step block: one exp per row and a per-column factor staged
 // once per chunk (both factors <= 1, so neither can overflow).
+// Pipeline per chunk: the next chunk's x rows and Delta load into registers
+// during the output phase, its B rows during the state phase (super_state: both
+// two chunks ahead); one wave (in the scan kernel the one with the least output
+// work) writes its decay prefix into the second of two prefix buffers, and the C
+// rows of a wave's first output block load across the barrier; two barriers per
+// chunk.
 #include "common.h"
 #include "launch.h"
 
@@ -44,23 +53,37 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// LDS-typed pointers keep the address arithmetic in 32 bits
+typedef __attribute__((address_space(3))) char lds_t;
+typedef __attribute__((address_space(3))) u16 lds_u16;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTargetBlocks = 768;  // workgroups of the scan kernel
 constexpr int kP = 64;              // head dim handled
+constexpr int kMaxQ = 256;          // longest chunk
 constexpr int kXS = kP + 16;        // LDS row stride (elements) of x rows
 constexpr int kPad = 16;            // LDS row padding (elements) of B rows
 constexpr int kHPad = 8;            // LDS row padding (elements) of the bf16 state rows
+constexpr int kArrays = 5;          // per-step arrays of a prefix buffer: s2, dt, w, cf, es
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // v = hi + lo with hi the truncation of v to bf16 (exact) and lo = bf16(v - hi)
-__device__ __forceinline__ void split8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint32_t u = __float_as_uint(v[e]) & 0xffff0000u;
@@ -69,14 +92,15 @@ __device__ __forceinline__ void split8(const float (&v)[8], bf16x8& hi, bf16x8& 
     }
 }
 
-__device__ __forceinline__ bf16x8 ld_bf16x8(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 ld_bf16x8(const lds_u16* p) { return *reinterpret_cast<const lds_bf16x8*>(p); }
+__device__ __forceinline__ f32x4 ld_f32x4(const lds_f32* p) { return *reinterpret_cast<const lds_f32x4*>(p); }
 
 // Transposed operand read from a row-major [k][m] bf16 array in LDS (row stride
 // `rs` elements): lane i of each 16-lane group receives rows k0 .. k0+3 of column
 // m0 + i. Each lane of the group points at row k0 + i/4, columns m0 + 4(i%4) ...+3.
-__device__ __forceinline__ bf16x4 ld_tr4(const u16* base, int rs, int k0, int m0) {
+__device__ __forceinline__ bf16x4 ld_tr4(const lds_u16* base, int rs, int k0, int m0) {
     const int i = threadIdx.x & 15;
-    const u16* p = base + (k0 + (i >> 2)) * rs + m0 + 4 * (i & 3);
+    const lds_u16* p = base + (k0 + (i >> 2)) * rs + m0 + 4 * (i & 3);
     const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
@@ -104,9 +128,57 @@ SsdGeom ssd_geom(int B, int L, int H, int Q) {
     return g;
 }
 
+// Output work of one chunk: up to two items per wave, an item being a 32-row
+// block I and npb 32-column blocks of p starting at pb0 (npb = 0: none).
+struct OutPlan {
+    int8_t I[kWaves][2];
+    int8_t pb0[kWaves][2];
+    int8_t npb[kWaves][2];
+    int8_t pw;  // the least loaded wave: it loads Delta and computes the decay prefix
+};
+
+// Longest-processing-time assignment of the items of R row blocks to the 4 SIMDs
+// (waves w and w + 4 share SIMD w % 4) and to their waves. Whole row blocks are
+// split into single p-blocks, heaviest first, until there are 8 items; an
+// item's cost counts its MFMAs (G and Y_diag per column block, Y_off).
+OutPlan out_plan(int R, int N) {
+    struct Item { int I, pb0, npb; };
+    Item items[2 * kMaxQ / 32];
+    int n = 0;
+    for (int I = 0; I < R; ++I) items[n++] = {I, 0, 2};
+    for (int I = R - 1; I >= 0 && n < kWaves; --I) {
+        items[I] = {I, 0, 1};
+        items[n++] = {I, 1, 1};
+    }
+    auto cost = [N](const Item& it) { return (it.I + 1) * (N / 16 + 4 * it.npb) + 2 * (N / 16) * it.npb; };
+    std::sort(items, items + n, [&](const Item& x, const Item& y) { return cost(x) > cost(y); });
+    OutPlan p{};
+    int load_w[kWaves] = {}, used[kWaves] = {}, load_s[4] = {};
+    for (int k = 0; k < n; ++k) {
+        int best = -1;
+        for (int w = 0; w < kWaves; ++w) {
+            if (used[w] == 2) continue;
+            if (best < 0 || load_s[w % 4] < load_s[best % 4] ||
+                (load_s[w % 4] == load_s[best % 4] && load_w[w] < load_w[best]))
+                best = w;
+        }
+        const int c = cost(items[k]);
+        p.I[best][used[best]] = (int8_t)items[k].I;
+        p.pb0[best][used[best]] = (int8_t)items[k].pb0;
+        p.npb[best][used[best]] = (int8_t)items[k].npb;
+        ++used[best];
+        load_w[best] += c;
+        load_s[best % 4] += c;
+    }
+    p.pw = 0;
+    for (int w = 1; w < kWaves; ++w)
+        if (load_w[w] < load_w[p.pw]) p.pw = (int8_t)w;
+    return p;
+}
+
 // LDS layout (bytes), per workgroup
 struct Smem {
-    int xs, bs, hh, hl, s2, dt, w, cf, red, total;
+    int xs, bs, hh, hl, sv, red, total;
 };
 
 template <int N>
@@ -116,130 +188,175 @@ __host__ __device__ inline Smem smem_layout(int Q) {
     s.bs = s.xs + Q * kXS * 2;             // bf16 [Q][N+kPad]    B rows of the chunk
     s.hh = s.bs + Q * (N + kPad) * 2;      // bf16 [P][N+kHPad]   state H^T, high part
     s.hl = s.hh + kP * (N + kHPad) * 2;    // bf16 [P][N+kHPad]   state H^T, remainder
-    s.s2 = s.hl + kP * (N + kHPad) * 2;    // f32  [Q]   inclusive log2-decay prefix
-    s.dt = s.s2 + Q * 4;                   // f32  [Q]   Delta
-    s.w = s.dt + Q * 4;                    // f32  [Q]   exp2(s_last - s_t) Delta_t
-    s.cf = s.w + Q * 4;                    // f32  [Q]   exp2(s_r - s_t) Delta_t, r = t | 31
-    s.red = s.cf + Q * 4;                  // f32  [4]   broadcast slot (s_last)
+    s.sv = s.hl + kP * (N + kHPad) * 2;    // f32  [2][kArrays][Q] two prefix buffers
+    s.red = s.sv + 2 * kArrays * Q * 4;    // f32  [2]  s_last of each prefix buffer
     s.total = s.red + 16;
     return s;
+}
+
+// Per-step arrays of prefix buffer sb: 0 s2 (inclusive log2-decay prefix),
+// 1 dt (Delta), 2 w = exp2(s_last - s_t) Delta_t, 3 cf = exp2(s_r - s_t) Delta_t with
+// r = t | 31, 4 es = exp2(s_t).
+__device__ __forceinline__ lds_f32* sv_arr(lds_t* lds, const Smem& sm, int Q, int sb, int which) {
+    return reinterpret_cast<lds_f32*>(lds + sm.sv) + (sb * kArrays + which) * Q;
+}
+__device__ __forceinline__ const lds_f32* sv_arr(const lds_t* lds, const Smem& sm, int Q, int sb, int which) {
+    return reinterpret_cast<const lds_f32*>(lds + sm.sv) + (sb * kArrays + which) * Q;
+}
+__device__ __forceinline__ float s_last(const lds_t* lds, const Smem& sm, int sb) {
+    return reinterpret_cast<const lds_f32*>(lds + sm.red)[sb];
 }
 
 // workspace (floats): Hagg [B][H][K-1][P][N], Lam [B][H][K-1]
 __host__ __device__ inline size_t ws_hagg(int B, int H, int K, int N) { return (size_t)B * H * (K - 1) * kP * N; }
 
-// Rows of x and B of one chunk held in registers between the global load and the
-// LDS store (so the next chunk's loads overlap the current chunk's work).
-template <int N>
-struct ChunkRows {
-    static constexpr int XQ = 256 * (kP / 8) / kThreads;   // 16-byte pieces per thread, Q = 256
-    static constexpr int BQ = 256 * (N / 8) / kThreads;
-    uint4 xv[XQ];
-    uint4 bv[BQ];
-    float dv[4];
+// Buffer views of one batch row's slabs: x, z, y [L][H][P], Delta [L][H], B, C
+// [L][N], each sized to its slab, so a time step t >= L reads zeros and a store
+// there is dropped (the ragged tail of the last chunk needs no masking).
+// Offsets are bytes within the slab.
+struct Views {
+    __amdgpu_buffer_rsrc_t x, dl, bm, cm, z, y;
+    uint32_t xrow;  // bytes per time step of x, z, y: H P 2
+    uint32_t xh;    // offset of head h inside a step: h P 2
+    uint32_t drow;  // bytes per time step of Delta: H 2
 };
 
 template <int N>
-__device__ __forceinline__ void load_x_rows(const SsdArgs& a, int b, int h, int t0, int len, ChunkRows<N>& cr) {
+__device__ __forceinline__ Views make_views(const SsdArgs& a, int b, int h) {
+    Views v;
+    const size_t lhp = (size_t)a.L * a.H * kP;
+    const u16* x = static_cast<const u16*>(a.x) + (size_t)b * lhp;
+    v.x = make_rsrc(x, (uint32_t)(lhp * 2));
+    v.z = make_rsrc(a.z ? static_cast<const u16*>(a.z) + (size_t)b * lhp : x, (uint32_t)(lhp * 2));
+    v.y = make_rsrc(static_cast<u16*>(a.y) + (size_t)b * lhp, (uint32_t)(lhp * 2));
+    v.dl = make_rsrc(static_cast<const u16*>(a.delta) + (size_t)b * a.L * a.H, (uint32_t)((size_t)a.L * a.H * 2));
+    v.bm = make_rsrc(static_cast<const u16*>(a.Bm) + (size_t)b * a.L * N, (uint32_t)((size_t)a.L * N * 2));
+    v.cm = make_rsrc(static_cast<const u16*>(a.Cm) + (size_t)b * a.L * N, (uint32_t)((size_t)a.L * N * 2));
+    v.xrow = (uint32_t)(a.H * kP * 2);
+    v.xh = (uint32_t)(h * kP * 2);
+    v.drow = (uint32_t)(a.H * 2);
+    return v;
+}
+
+__device__ __forceinline__ u32x4 ld_buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Rows of x and B of one chunk (and, in the prefix wave, its Delta) held in registers
+// between the global load and the LDS store.
+template <int N>
+struct ChunkRows {
+    static constexpr int XQ = kMaxQ * (kP / 8) / kThreads;  // 16-byte pieces per thread
+    static constexpr int BQ = kMaxQ * (N / 8) / kThreads;
+    u32x4 xv[XQ];
+    u32x4 bv[BQ];
+    float dv[4];
+};
+
+// x rows (and, in wave pw, Delta) of the chunk starting at step t0; rows of
+// pieces that start at or past Q are not loaded.
+template <int N>
+__device__ __forceinline__ void load_x_rows(const Views& v, int Q, int t0, ChunkRows<N>& cr, int pw) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
     for (int k = 0; k < ChunkRows<N>::XQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
-        cr.xv[k] = make_uint4(0, 0, 0, 0);
-        if (r < len)
-            cr.xv[k] = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.x) +
-                                                       (((size_t)b * a.L + t0 + r) * a.H + h) * kP + c8);
+        if (k * kThreads / (kP / 8) < Q) cr.xv[k] = ld_buf16(v.x, (uint32_t)(t0 + r) * v.xrow + v.xh + 2 * c8);
     }
-    if (wave == 0) {
-        const u16* dp = static_cast<const u16*>(a.delta);
+    if (wave == pw) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int t = lane * 4 + k;
-            cr.dv[k] = (t < len) ? bf16_to_f32(dp[((size_t)b * a.L + t0 + t) * a.H + h]) : 0.0f;
+            cr.dv[k] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+                v.dl, (int)((uint32_t)(t0 + t) * v.drow + v.xh / kP), 0, 0));
         }
     }
 }
 
 template <int N>
-__device__ __forceinline__ void load_b_rows(const SsdArgs& a, int b, int t0, int len, ChunkRows<N>& cr) {
+__device__ __forceinline__ void load_b_rows(const Views& v, int Q, int t0, ChunkRows<N>& cr) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < ChunkRows<N>::BQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
-        cr.bv[k] = make_uint4(0, 0, 0, 0);
-        if (r < len)
-            cr.bv[k] = *reinterpret_cast<const uint4*>(static_cast<const u16*>(a.Bm) + ((size_t)b * a.L + t0 + r) * N + c8);
+        if (k * kThreads / (N / 8) < Q) cr.bv[k] = ld_buf16(v.bm, (uint32_t)((t0 + r) * N + c8) * 2);
     }
 }
 
-// Write a chunk's rows into LDS and (wave 0) its decay prefix, weights and column factors.
+// x and B rows of a chunk from registers into LDS (rows >= len hold zeros)
 template <int N>
-__device__ __forceinline__ void store_rows(char* lds, const Smem& sm, int Q, int len, float A2, const ChunkRows<N>& cr) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    u16* xs = reinterpret_cast<u16*>(lds + sm.xs);
-    u16* bs = reinterpret_cast<u16*>(lds + sm.bs);
+__device__ __forceinline__ void store_xb(lds_t* lds, const Smem& sm, int Q, const ChunkRows<N>& cr) {
+    const int tid = threadIdx.x;
+    lds_u16* xs = reinterpret_cast<lds_u16*>(lds + sm.xs);
+    lds_u16* bs = reinterpret_cast<lds_u16*>(lds + sm.bs);
 #pragma unroll
     for (int k = 0; k < ChunkRows<N>::XQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
-        if (r < Q) *reinterpret_cast<uint4*>(xs + r * kXS + c8) = cr.xv[k];
+        if (k * kThreads / (kP / 8) < Q && r < Q) *reinterpret_cast<lds_u32x4*>(xs + r * kXS + c8) = cr.xv[k];
     }
 #pragma unroll
     for (int k = 0; k < ChunkRows<N>::BQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
-        if (r < Q) *reinterpret_cast<uint4*>(bs + r * (N + kPad) + c8) = cr.bv[k];
+        if (k * kThreads / (N / 8) < Q && r < Q) *reinterpret_cast<lds_u32x4*>(bs + r * (N + kPad) + c8) = cr.bv[k];
     }
-    if (wave == 0) {
-        float* s2 = reinterpret_cast<float*>(lds + sm.s2);
-        float* dt = reinterpret_cast<float*>(lds + sm.dt);
-        float* w = reinterpret_cast<float*>(lds + sm.w);
-        float* cf = reinterpret_cast<float*>(lds + sm.cf);
-        // 4 consecutive steps per lane (Q <= 256), fp64 prefix, then a wave-wide scan
-        double loc[4], run = 0.0;
+}
+
+// One wave: the chunk's decay prefix and per-step factors into prefix buffer sb.
+// Lane l owns steps 4l .. 4l+3 (Q <= 256); fp64 running sums, then a wave scan.
+__device__ __forceinline__ void chunk_prefix(lds_t* lds, const Smem& sm, int Q, int sb, int len, float A2,
+                                             const float (&dv)[4]) {
+    const int lane = threadIdx.x & 63;
+    lds_f32* s2 = sv_arr(lds, sm, Q, sb, 0);
+    lds_f32* dt = sv_arr(lds, sm, Q, sb, 1);
+    lds_f32* w = sv_arr(lds, sm, Q, sb, 2);
+    lds_f32* cf = sv_arr(lds, sm, Q, sb, 3);
+    lds_f32* es = sv_arr(lds, sm, Q, sb, 4);
+    double loc[4], run = 0.0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            run += (double)(cr.dv[k] * A2);
-            loc[k] = run;
-        }
-        double incl = run;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
-        }
-        const double excl = incl - run;
-        float sv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t = lane * 4 + k;
-            sv[k] = (float)(excl + loc[k]);
-            if (t >= len) sv[k] = 0.0f;
-        }
-        float sl;
-        {
-            const int ll = (len - 1) >> 2, kk = (len - 1) & 3;
-            const float lk = kk == 0 ? sv[0] : kk == 1 ? sv[1] : kk == 2 ? sv[2] : sv[3];
-            sl = __shfl(lk, ll, 64);
-        }
-        // end of each 32-step block (lanes 8m .. 8m+7 cover block m): held by lane 8m+7, element 3
-        const float send = __shfl(sv[3], (lane & ~7) | 7, 64);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t = lane * 4 + k;
-            if (t < Q) {
-                const float s = t < len ? sv[k] : sl;
-                const float r = min(t | 31, len - 1) == t ? s : (((t | 31) < len) ? send : sl);
-                s2[t] = s;
-                dt[t] = cr.dv[k];
-                w[t] = t < len ? exp2_fast(sl - s) * cr.dv[k] : 0.0f;
-                cf[t] = t < len ? exp2_fast(r - s) * cr.dv[k] : 0.0f;
-            }
-        }
-        if (lane == 0) reinterpret_cast<float*>(lds + sm.red)[0] = sl;
+    for (int k = 0; k < 4; ++k) {
+        run += (double)(dv[k] * A2);
+        loc[k] = run;
     }
+    double incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    const double excl = incl - run;
+    float sv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int t = lane * 4 + k;
+        sv[k] = (float)(excl + loc[k]);
+        if (t >= len) sv[k] = 0.0f;
+    }
+    float sl;
+    {
+        const int ll = (len - 1) >> 2, kk = (len - 1) & 3;
+        const float lk = kk == 0 ? sv[0] : kk == 1 ? sv[1] : kk == 2 ? sv[2] : sv[3];
+        sl = __shfl(lk, ll, 64);
+    }
+    // end of each 32-step block (lanes 8m .. 8m+7 cover block m): held by lane 8m+7, element 3
+    const float send = __shfl(sv[3], (lane & ~7) | 7, 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int t = lane * 4 + k;
+        if (t < Q) {
+            const float s = t < len ? sv[k] : sl;
+            const float r = min(t | 31, len - 1) == t ? s : (((t | 31) < len) ? send : sl);
+            s2[t] = s;
+            dt[t] = dv[k];
+            w[t] = t < len ? exp2_fast(sl - s) * dv[k] : 0.0f;
+            cf[t] = t < len ? exp2_fast(r - s) * dv[k] : 0.0f;
+            es[t] = exp2_fast(s);
+        }
+    }
+    if (lane == 0) reinterpret_cast<lds_f32*>(lds + sm.red)[sb] = sl;
 }
 
 // Chunk state S^T = (w o X)^T B on this wave's tiles: p-block pb = wave % 4 and
@@ -251,36 +368,60 @@ struct StateTiles {
 };
 
 template <int N>
-__device__ __forceinline__ void chunk_state(const char* lds, const Smem& sm, int len, StateTiles<N>& st) {
+__device__ __forceinline__ void chunk_state(const lds_t* lds, const Smem& sm, int Q, int sb, int len,
+                                            StateTiles<N>& st) {
     constexpr int NBW = StateTiles<N>::NBW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4;
     const int pb = wave & 3, nb0 = (wave >> 2) * NBW;
-    const u16* xs = reinterpret_cast<const u16*>(lds + sm.xs);
-    const u16* bs = reinterpret_cast<const u16*>(lds + sm.bs);
-    const float* w = reinterpret_cast<const float*>(lds + sm.w);
+    const lds_u16* xs = reinterpret_cast<const lds_u16*>(lds + sm.xs);
+    const lds_u16* bs = reinterpret_cast<const lds_u16*>(lds + sm.bs);
+    const lds_f32* w = sv_arr(lds, sm, Q, sb, 2);
 #pragma unroll
     for (int k = 0; k < NBW; ++k) st.acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int kbn = (len + 31) >> 5;
-    for (int kb = 0; kb < kbn; ++kb) {
+    // operands of one 32-step block: x (4 + 4 steps of column p), the weights,
+    // and the B operands of this wave's n-blocks
+    struct Ops {
+        bf16x8 x;
+        f32x4 w0, w1;
+        bf16x8 b[NBW];
+    };
+    auto fetch = [&](int kb, Ops& o) {
         const int t = kb * 32 + 8 * g;
-        const bf16x8 xv = cat(ld_tr4(xs, kXS, t, pb * 16), ld_tr4(xs, kXS, t + 4, pb * 16));
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + t);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + t + 4);
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[e] = (float)xv[e] * w0[e];
-            v[e + 4] = (float)xv[e + 4] * w1[e];
-        }
-        bf16x8 ahi, alo;
-        split8(v, ahi, alo);
+        o.x = cat(ld_tr4(xs, kXS, t, pb * 16), ld_tr4(xs, kXS, t + 4, pb * 16));
+        o.w0 = ld_f32x4(w + t);
+        o.w1 = ld_f32x4(w + t + 4);
 #pragma unroll
         for (int k = 0; k < NBW; ++k) {
             const int n0 = (nb0 + k) * 16;
-            const bf16x8 bop = cat(ld_tr4(bs, N + kPad, t, n0), ld_tr4(bs, N + kPad, t + 4, n0));
-            st.acc[k] = mfma(ahi, bop, st.acc[k]);
-            st.acc[k] = mfma(alo, bop, st.acc[k]);
+            o.b[k] = cat(ld_tr4(bs, N + kPad, t, n0), ld_tr4(bs, N + kPad, t + 4, n0));
+        }
+    };
+    auto use = [&](const Ops& o) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = (float)o.x[e] * o.w0[e];
+            v[e + 4] = (float)o.x[e + 4] * o.w1[e];
+        }
+        bf16x8 ahi, alo;
+        split8(v, ahi, alo);
+        // high parts first, then remainders: no two back-to-back MFMAs share an accumulator
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) st.acc[k] = mfma16(ahi, o.b[k], st.acc[k]);
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) st.acc[k] = mfma16(alo, o.b[k], st.acc[k]);
+    };
+    // two operand sets in flight: block kb + 1 is read while block kb is used
+    const int kbn = (len + 31) >> 5;
+    Ops o0, o1;
+    fetch(0, o0);
+    for (int kb = 0; kb < kbn; kb += 2) {
+        if (kb + 1 < kbn) fetch(kb + 1, o1);
+        use(o0);
+        if (kb + 1 < kbn) {
+            if (kb + 2 < kbn) fetch(kb + 2, o0);
+            use(o1);
         }
     }
 }
@@ -293,8 +434,9 @@ struct State {
 
 // H <- exp2(s_last) H + S (registers)
 template <int N>
-__device__ __forceinline__ void state_update(const char* lds, const Smem& sm, State<N>& hs, const StateTiles<N>& st) {
-    const float decay = exp2_fast(reinterpret_cast<const float*>(lds + sm.red)[0]);
+__device__ __forceinline__ void state_update(const lds_t* lds, const Smem& sm, int sb, State<N>& hs,
+                                             const StateTiles<N>& st) {
+    const float decay = exp2_fast(s_last(lds, sm, sb));
 #pragma unroll
     for (int k = 0; k < StateTiles<N>::NBW; ++k)
 #pragma unroll
@@ -303,13 +445,13 @@ __device__ __forceinline__ void state_update(const char* lds, const Smem& sm, St
 
 // bf16 high part and remainder of this wave's state tiles into LDS
 template <int N>
-__device__ __forceinline__ void state_to_lds(char* lds, const Smem& sm, const State<N>& hs) {
+__device__ __forceinline__ void state_to_lds(lds_t* lds, const Smem& sm, const State<N>& hs) {
     constexpr int NBW = StateTiles<N>::NBW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const int pb = wave & 3, nb0 = (wave >> 2) * NBW;
-    u16* hh = reinterpret_cast<u16*>(lds + sm.hh);
-    u16* hl = reinterpret_cast<u16*>(lds + sm.hl);
+    lds_u16* hh = reinterpret_cast<lds_u16*>(lds + sm.hh);
+    lds_u16* hl = reinterpret_cast<lds_u16*>(lds + sm.hl);
 #pragma unroll
     for (int k = 0; k < NBW; ++k)
 #pragma unroll
@@ -331,36 +473,72 @@ __device__ __forceinline__ void tile_pn(int k, int r, int& p, int& n) {
     n = ((wave >> 2) * StateTiles<N>::NBW + k) * 16 + c;
 }
 
+// Block coordinates of a 1-D grid of B * K' * H workgroups, heads fastest.
+// Workgroups go round-robin to the 8 XCDs (each with its own L2); when the
+// count allows, consecutive coordinates are given to one XCD so that all heads
+// of a (batch, super-chunk), which read the same B and C rows, share its L2.
+__device__ __forceinline__ void block_coords(int H, int Kp, int& h, int& k, int& b) {
+    const int total = (int)gridDim.x, id = (int)blockIdx.x;
+    const int idp = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+    h = idp % H;
+    const int r = idp / H;
+    k = r % Kp;
+    b = r / Kp;
+}
+
 template <int N>
 __global__ void __launch_bounds__(kThreads)
 ssd_super_state(SsdArgs a, SsdGeom geo) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    lds_t* lds = (lds_t*)lds_raw;
     const Smem sm = smem_layout<N>(geo.Q);
-    const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int h, k, b;
+    block_coords(a.H, geo.K - 1, h, k, b);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float A2 = a.A[h] * kLog2e;
     State<N> hs;
 #pragma unroll
     for (int kk = 0; kk < StateTiles<N>::NBW; ++kk) hs.h[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
     double lam = 0.0;
     const int c0 = k * geo.cps, c1 = min(geo.C, c0 + geo.cps);
-    ChunkRows<N> cr;
-    load_x_rows<N>(a, b, h, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
-    load_b_rows<N>(a, b, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
-    for (int cc = c0; cc < c1; ++cc) {
+    const Views v = make_views<N>(a, b, h);
+    // Rows arrive two chunks ahead of their use: while chunk cc is contracted,
+    // `nxt` holds the loads of chunk cc + 1 in flight and `nxt2` receives those
+    // of chunk cc + 2. The two register sets swap roles every chunk (the loop
+    // body is written out twice so that no in-flight register is copied).
+    ChunkRows<N> ra, rb;
+    {
+        const int len0 = min(geo.Q, a.L - c0 * geo.Q);
+        load_x_rows<N>(v, geo.Q, c0 * geo.Q, rb, 0);
+        load_b_rows<N>(v, geo.Q, c0 * geo.Q, rb);
+        if (c0 + 1 < c1) {
+            load_x_rows<N>(v, geo.Q, (c0 + 1) * geo.Q, ra, 0);
+            load_b_rows<N>(v, geo.Q, (c0 + 1) * geo.Q, ra);
+        }
+        if (wave == 0) chunk_prefix(lds, sm, geo.Q, 0, len0, A2, rb.dv);
+        store_xb<N>(lds, sm, geo.Q, rb);
+    }
+    auto step = [&](int cc, ChunkRows<N>& nxt, ChunkRows<N>& nxt2) {
+        const int sb = (cc - c0) & 1;
         const int t0 = cc * geo.Q;
         const int len = min(geo.Q, a.L - t0);
-        __syncthreads();  // previous chunk fully consumed
-        store_rows<N>(lds, sm, geo.Q, len, A2, cr);
-        __syncthreads();
-        if (cc + 1 < c1) {
-            const int ln = min(geo.Q, a.L - t0 - geo.Q);
-            load_x_rows<N>(a, b, h, t0 + geo.Q, ln, cr);
-            load_b_rows<N>(a, b, t0 + geo.Q, ln, cr);
+        const int ln = cc + 1 < c1 ? min(geo.Q, a.L - t0 - geo.Q) : 0;
+        __syncthreads();  // rows and prefix of this chunk visible
+        if (cc + 2 < c1) {
+            load_x_rows<N>(v, geo.Q, t0 + 2 * geo.Q, nxt2, 0);
+            load_b_rows<N>(v, geo.Q, t0 + 2 * geo.Q, nxt2);
         }
         StateTiles<N> st;
-        chunk_state<N>(lds, sm, len, st);
-        lam += (double)reinterpret_cast<const float*>(lds + sm.red)[0];
-        state_update<N>(lds, sm, hs, st);
+        chunk_state<N>(lds, sm, geo.Q, sb, len, st);
+        state_update<N>(lds, sm, sb, hs, st);
+        lam += (double)s_last(lds, sm, sb);
+        if (ln > 0 && wave == 0) chunk_prefix(lds, sm, geo.Q, sb ^ 1, ln, A2, nxt.dv);
+        __syncthreads();  // every read of this chunk's rows done
+        if (ln > 0) store_xb<N>(lds, sm, geo.Q, nxt);
+    };
+    for (int cc = c0; cc < c1; cc += 2) {
+        step(cc, ra, rb);
+        if (cc + 1 < c1) step(cc + 1, rb, ra);
     }
     float* out = static_cast<float*>(a.ws) + (((size_t)b * a.H + h) * (geo.K - 1) + k) * kP * N;
 #pragma unroll
@@ -377,194 +555,225 @@ ssd_super_state(SsdArgs a, SsdGeom geo) {
     }
 }
 
-// Outputs of one 16-row block I of a chunk, for NPB p-blocks starting at pb0.
-template <int N, int NPB, bool HAS_Z, bool HAS_D>
-__device__ __forceinline__ void chunk_rows(const SsdArgs& a, const char* lds, const Smem& sm, int b, int h,
-                                           int t0, int len, int I, int pb0, const bf16x8 (&cop)[N / 32], float Dh) {
+// Aggregates -> entering states: slot k (k = 0 .. K-2) of (b, h) becomes the
+// state entering super-chunk k + 1, H_in(k+1) = exp2(Lam_k) H_in(k) + Hagg_k,
+// with H_in(0) = h0 (or zero). One thread per state element (p, n).
+template <int N>
+__global__ void __launch_bounds__(256)
+ssd_carry(const float* __restrict__ h0, float* __restrict__ ws, int B, int H, int K) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    if (e >= kP * N) return;
+    const int p = e / N, n = e % N;
+    const size_t bh = (size_t)b * H + h;
+    float v = h0 ? h0[(bh * N + n) * kP + p] : 0.0f;
+    const float* lam = ws + ws_hagg(B, H, K, N) + bh * (K - 1);
+    float* slot = ws + bh * (K - 1) * kP * N + e;
+    for (int k = 0; k < K - 1; ++k) {
+        v = __builtin_fmaf(exp2_fast(lam[k]), v, slot[(size_t)k * kP * N]);
+        slot[(size_t)k * kP * N] = v;
+    }
+}
+
+// C rows of a 32-row block as MFMA operands: lane holds row 32 I + l % 32,
+// columns 16 ks + 8 (l / 32) .. +7 for ks = 0 .. N/16 - 1 (zeros past len).
+template <int N>
+__device__ __forceinline__ void load_c(const Views& v, int t0, int I, bf16x8 (&cop)[N / 16]) {
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, c = lane & 15;
-    const u16* xs = reinterpret_cast<const u16*>(lds + sm.xs);
-    const u16* bs = reinterpret_cast<const u16*>(lds + sm.bs);
-    const u16* hh = reinterpret_cast<const u16*>(lds + sm.hh);
-    const u16* hl = reinterpret_cast<const u16*>(lds + sm.hl);
-    const float* s2 = reinterpret_cast<const float*>(lds + sm.s2);
-    const float* dt = reinterpret_cast<const float*>(lds + sm.dt);
-    const float* cf = reinterpret_cast<const float*>(lds + sm.cf);
-    const int ia = I * 16 + c;  // this lane's A-operand row
-    f32x4 acc[NPB];
+    const uint32_t off = (uint32_t)((t0 + 32 * I + (lane & 31)) * N + 8 * (lane >> 5)) * 2;
 #pragma unroll
-    for (int q = 0; q < NPB; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Y_off = C H: the state's bf16 high part and remainder (rows of H^T) are B operands
+    for (int ks = 0; ks < N / 16; ++ks) cop[ks] = __builtin_bit_cast(bf16x8, ld_buf16(v.cm, off + 32 * ks));
+}
+
+// Outputs of one 32-row block I of a chunk for NPB 32-column blocks of p from pb0.
+// Lane l: hf = l / 32, c = l % 32. MFMA 32x32x16 layouts: A operand A[c][8 hf + e],
+// B operand B[8 hf + e][c], accumulator element r at row 8(r/4) + 4 hf + r%4, column c.
+template <int N, int NPB, bool HAS_Z, bool HAS_D>
+__device__ __forceinline__ void out_item(const Views& v, const lds_t* lds, const Smem& sm, int Q, int sb,
+                                         int t0, int len, int I, int pb0, const bf16x8 (&cop)[N / 16], float Dh) {
+    const int lane = threadIdx.x & 63;
+    const int hf = lane >> 5, c = lane & 31, gh = (lane >> 4) & 1;
+    const lds_u16* xs = reinterpret_cast<const lds_u16*>(lds + sm.xs);
+    const lds_u16* bs = reinterpret_cast<const lds_u16*>(lds + sm.bs);
+    const lds_u16* hh = reinterpret_cast<const lds_u16*>(lds + sm.hh);
+    const lds_u16* hl = reinterpret_cast<const lds_u16*>(lds + sm.hl);
+    const lds_f32* s2 = sv_arr(lds, sm, Q, sb, 0);
+    const lds_f32* dt = sv_arr(lds, sm, Q, sb, 1);
+    const lds_f32* cf = sv_arr(lds, sm, Q, sb, 3);
+    const lds_f32* es = sv_arr(lds, sm, Q, sb, 4);
+    f32x16 acc[NPB];
 #pragma unroll
-    for (int kb = 0; kb < N / 32; ++kb)
+    for (int q = 0; q < NPB; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+    // Y_off = C H: rows of H^T (high part and remainder) are the B operands
+#pragma unroll
+    for (int ks = 0; ks < N / 16; ++ks)
 #pragma unroll
         for (int q = 0; q < NPB; ++q) {
-            const int off = ((pb0 + q) * 16 + c) * (N + kHPad) + kb * 32 + 8 * g;
-            acc[q] = mfma(cop[kb], ld_bf16x8(hh + off), acc[q]);
-            acc[q] = mfma(cop[kb], ld_bf16x8(hl + off), acc[q]);
+            const int off = (32 * (pb0 + q) + c) * (N + kHPad) + 16 * ks + 8 * hf;
+            acc[q] = mfma32(cop[ks], ld_bf16x8(hh + off), acc[q]);
+            acc[q] = mfma32(cop[ks], ld_bf16x8(hl + off), acc[q]);
         }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float sc = exp2_fast(s2[I * 16 + 4 * g + r]);
+    for (int rq = 0; rq < 4; ++rq) {
+        const f32x4 e4 = ld_f32x4(es + 32 * I + 8 * rq + 4 * hf);
 #pragma unroll
-        for (int q = 0; q < NPB; ++q) acc[q][r] *= sc;
+        for (int q = 0; q < NPB; ++q)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[q][4 * rq + rr] *= e4[rr];
     }
-    // Y_diag = M X over 32-wide column blocks J up to the block's last row
-    const float s2i = s2[ia];
-    for (int J = 0; J * 32 <= I * 16 + 15; ++J) {
-        f32x4 g0 = f32x4{0.f, 0.f, 0.f, 0.f}, g1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Y_diag = M X over 32-wide column blocks J <= I
+    const int i = 32 * I + c;  // this lane's row of G and M
+    const float s2i = s2[i];
+    for (int J = 0; J <= I && 32 * J < len; ++J) {
+        f32x16 g;
 #pragma unroll
-        for (int kb = 0; kb < N / 32; ++kb) {
-            const bf16x8 b0 = ld_bf16x8(bs + (J * 32 + c) * (N + kPad) + kb * 32 + 8 * g);
-            const bf16x8 b1 = ld_bf16x8(bs + (J * 32 + 16 + c) * (N + kPad) + kb * 32 + 8 * g);
-            g0 = mfma(b0, cop[kb], g0);  // G^T[j][i]: lane holds G[ia][J*32 + 4g + r]
-            g1 = mfma(b1, cop[kb], g1);  //            and G[ia][J*32 + 16 + 4g + r]
-        }
-        float m[8];
-        if (J * 32 + 31 < I * 16) {
-            // whole column block below this row block: row factor x column factor
-            const float rowf = exp2_fast(s2i - s2[J * 32 + 31]);
-            const f32x4 c0 = *reinterpret_cast<const f32x4*>(cf + J * 32 + 4 * g);
-            const f32x4 c1 = *reinterpret_cast<const f32x4*>(cf + J * 32 + 16 + 4 * g);
+        for (int r = 0; r < 16; ++r) g[r] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                m[e] = g0[e] * rowf * c0[e];
-                m[e + 4] = g1[e] * rowf * c1[e];
+        for (int ks = 0; ks < N / 16; ++ks)
+            g = mfma32(ld_bf16x8(bs + (32 * J + c) * (N + kPad) + 16 * ks + 8 * hf), cop[ks], g);
+        // lane holds G[i][j] for j = 32 J + 8 (r/4) + 4 hf + r % 4
+        float m[16];
+        if (J < I) {
+            const float rowf = exp2_fast(s2i - s2[32 * J + 31]);
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const f32x4 c4 = ld_f32x4(cf + 32 * J + 8 * rq + 4 * hf);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) m[4 * rq + rr] = g[4 * rq + rr] * rowf * c4[rr];
             }
         } else {
+            // causal mask j <= i, i.e. 8 (r/4) + r % 4 <= c - 4 hf; columns j >= len
+            // only meet rows i >= len, which are never stored (their x rows are zero)
+            const int cl = c - 4 * hf;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = J * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-                const float gv = e < 4 ? g0[e] : g1[e - 4];
-                const bool ok = (j <= ia) && (j < len);
-                m[e] = ok ? gv * exp2_fast(s2i - s2[j]) * dt[j] : 0.0f;
+            for (int rq = 0; rq < 4; ++rq) {
+                const int j0 = 32 * J + 8 * rq + 4 * hf;
+                const f32x4 sj = ld_f32x4(s2 + j0);
+                const f32x4 dj = ld_f32x4(dt + j0);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    m[4 * rq + rr] = (8 * rq + rr <= cl) ? g[4 * rq + rr] * exp2_fast(s2i - sj[rr]) * dj[rr] : 0.0f;
             }
         }
-        bf16x8 mhi, mlo;
-        split8(m, mhi, mlo);
+        // two 16-step halves of the block; rows of x in the same (hf, e) -> j order
 #pragma unroll
-        for (int q = 0; q < NPB; ++q) {
-            // x at the same (g, e) -> j mapping: two runs of 4 steps
-            const bf16x8 xop = cat(ld_tr4(xs, kXS, J * 32 + 4 * g, (pb0 + q) * 16),
-                                   ld_tr4(xs, kXS, J * 32 + 16 + 4 * g, (pb0 + q) * 16));
-            acc[q] = mfma(mhi, xop, acc[q]);
-            acc[q] = mfma(mlo, xop, acc[q]);
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+            bf16x8 mhi, mlo;
+            split8(m + 8 * ks2, mhi, mlo);
+            const int k0 = 32 * J + 16 * ks2 + 4 * hf;
+#pragma unroll
+            for (int q = 0; q < NPB; ++q) {
+                const int m0 = 32 * (pb0 + q) + 16 * gh;
+                const bf16x8 xop = cat(ld_tr4(xs, kXS, k0, m0), ld_tr4(xs, kXS, k0 + 8, m0));
+                acc[q] = mfma32(mhi, xop, acc[q]);
+                acc[q] = mfma32(mlo, xop, acc[q]);
+            }
         }
     }
-    // epilogue: rows i = I*16 + 4g + r, columns p = (pb0 + q)*16 + c
+    // epilogue: rows 32 I + 8 (r/4) + 4 hf + r % 4, columns p = 32 (pb0 + q) + c;
+    // rows past the sequence end fall outside the y view and are dropped
+    const uint32_t off0 = (uint32_t)(t0 + 32 * I + 4 * hf) * v.xrow + v.xh + 2 * (32 * pb0 + c);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = I * 16 + 4 * g + r;
-        if (i >= len) continue;
-        const size_t rowoff = (((size_t)b * a.L + t0 + i) * a.H + h) * kP;
+    for (int r = 0; r < 16; ++r) {
+        const int row = 32 * I + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const uint32_t off = off0 + (uint32_t)(8 * (r >> 2) + (r & 3)) * v.xrow;
 #pragma unroll
         for (int q = 0; q < NPB; ++q) {
-            const int p = (pb0 + q) * 16 + c;
-            float v = acc[q][r];
-            if constexpr (HAS_D) v = __builtin_fmaf(Dh, bf16_to_f32(xs[i * kXS + p]), v);
-            if constexpr (HAS_Z) v *= silu(bf16_to_f32(static_cast<const u16*>(a.z)[rowoff + p]));
-            static_cast<u16*>(a.y)[rowoff + p] = f32_to_bf16(v);
+            float val = acc[q][r];
+            if constexpr (HAS_D) val = __builtin_fmaf(Dh, bf16_to_f32(xs[row * kXS + 32 * (pb0 + q) + c]), val);
+            if constexpr (HAS_Z)
+                val *= silu(bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(v.z, (int)(off + 64 * q), 0, 0)));
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), v.y, (int)(off + 64 * q), 0, 0);
         }
     }
+    (void)len;
+}
+
+template <int N, bool HAS_Z, bool HAS_D>
+__device__ __forceinline__ void run_item(const Views& v, const lds_t* lds, const Smem& sm, int Q, int sb, int t0,
+                                         int len, int I, int pb0, int npb, const bf16x8 (&cop)[N / 16], float Dh) {
+    if (npb == 2) out_item<N, 2, HAS_Z, HAS_D>(v, lds, sm, Q, sb, t0, len, I, pb0, cop, Dh);
+    else out_item<N, 1, HAS_Z, HAS_D>(v, lds, sm, Q, sb, t0, len, I, pb0, cop, Dh);
 }
 
 template <int N, bool HAS_Z, bool HAS_D>
 __global__ void __launch_bounds__(kThreads)
-ssd_chunk_scan(SsdArgs a, SsdGeom geo) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
+    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+    lds_t* lds = (lds_t*)lds_raw;
     const Smem sm = smem_layout<N>(geo.Q);
-    const int k = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, c = lane & 15;
+    int h, k, b;
+    block_coords(a.H, geo.K, h, k, b);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float A2 = a.A[h] * kLog2e;
     const float Dh = HAS_D ? a.Dskip[h] : 0.0f;
     const int c0 = k * geo.cps, c1 = min(geo.C, c0 + geo.cps);
+    const int I0 = plan.I[wave][0], P0 = plan.pb0[wave][0], N0 = plan.npb[wave][0];
+    const int I1 = plan.I[wave][1], P1 = plan.pb0[wave][1], N1 = plan.npb[wave][1];
+    const int PW = plan.pw;
 
-    ChunkRows<N> cr;
-    load_x_rows<N>(a, b, h, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
-    load_b_rows<N>(a, b, c0 * geo.Q, min(geo.Q, a.L - c0 * geo.Q), cr);
-
-    // state entering this super-chunk: h0 folded with the earlier aggregates
+    // state entering this super-chunk: h0 (or zero) for the first, else the
+    // slot the carry kernel filled
     State<N> hs;
     {
-        const float* hagg = static_cast<const float*>(a.ws);
-        const float* lamp = hagg + ws_hagg(a.B, a.H, geo.K, N);
+        const size_t bh = (size_t)b * a.H + h;
+        const float* slot = static_cast<const float*>(a.ws) + (bh * (geo.K - 1) + (k - 1)) * kP * N;
 #pragma unroll
         for (int kk = 0; kk < StateTiles<N>::NBW; ++kk)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 int p, n;
                 tile_pn<N>(kk, r, p, n);
-                hs.h[kk][r] = a.h0 ? a.h0[(((size_t)b * a.H + h) * N + n) * kP + p] : 0.0f;
+                float v = 0.0f;
+                if (k > 0) v = slot[p * N + n];
+                else if (a.h0) v = a.h0[(bh * N + n) * kP + p];
+                hs.h[kk][r] = v;
             }
-        for (int j = 0; j < k; ++j) {
-            const size_t base = ((size_t)b * a.H + h) * (geo.K - 1) + j;
-            const float dec = exp2_fast(lamp[base]);
-#pragma unroll
-            for (int kk = 0; kk < StateTiles<N>::NBW; ++kk)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    int p, n;
-                    tile_pn<N>(kk, r, p, n);
-                    hs.h[kk][r] = __builtin_fmaf(dec, hs.h[kk][r], hagg[base * kP * N + p * N + n]);
-                }
-        }
+    }
+    const Views v = make_views<N>(a, b, h);
+    ChunkRows<N> cr;
+    bf16x8 cop[N / 16];
+    {
+        const int len0 = min(geo.Q, a.L - c0 * geo.Q);
+        load_x_rows<N>(v, geo.Q, c0 * geo.Q, cr, PW);
+        load_b_rows<N>(v, geo.Q, c0 * geo.Q, cr);
+        if (N0 > 0) load_c<N>(v, c0 * geo.Q, I0, cop);
         state_to_lds<N>(lds, sm, hs);
+        if (wave == PW) chunk_prefix(lds, sm, geo.Q, 0, len0, A2, cr.dv);
+        store_xb<N>(lds, sm, geo.Q, cr);
     }
     const bool last_super = (k == geo.K - 1);
-    const u16* Cg = static_cast<const u16*>(a.Cm);
-    // Work split of the output phase over the 8 waves, by the number R of 16-row blocks:
-    //   R >= 8: wave w takes block w and, when R - 1 - w >= 8, block R - 1 - w too
-    //           (pairs balance the causal work), all 4 p-blocks;
-    //   R = 4:  wave w takes block w % 4 and 2 of the p-blocks;
-    //   R = 2:  wave w takes block w % 2 and 1 p-block;
-    //   R = 6:  waves 0..5 take one block each, all p-blocks.
-    const int R = geo.Q / 16;
-    int I0 = wave, I1 = -1, npb = 4, pb0 = 0;
-    if (R >= 8) {
-        if (R - 1 - wave >= 8) I1 = R - 1 - wave;
-    } else if (R == 4) {
-        I0 = wave & 3; npb = 2; pb0 = (wave >> 2) * 2;
-    } else if (R == 2) {
-        I0 = wave & 1; npb = 1; pb0 = wave >> 1;
-    } else if (wave >= R) {
-        I0 = -1;
-    }
     for (int cc = c0; cc < c1; ++cc) {
+        const int sb = (cc - c0) & 1;
         const int t0 = cc * geo.Q;
         const int len = min(geo.Q, a.L - t0);
-        // C rows of this wave's blocks straight from global
-        bf16x8 cop0[N / 32], cop1[N / 32];
-#pragma unroll
-        for (int kb = 0; kb < N / 32; ++kb) {
-            const int i0 = I0 * 16 + c, i1 = I1 * 16 + c;
-            cop0[kb] = (I0 >= 0 && i0 < len) ? ld_bf16x8(Cg + ((size_t)b * a.L + t0 + i0) * N + kb * 32 + 8 * g) : bf16x8{};
-            cop1[kb] = (I1 >= 0 && i1 < len) ? ld_bf16x8(Cg + ((size_t)b * a.L + t0 + i1) * N + kb * 32 + 8 * g)
-                                             : bf16x8{};
-        }
-        __syncthreads();  // previous chunk's LDS reads done, state copy written
-        store_rows<N>(lds, sm, geo.Q, len, A2, cr);
-        __syncthreads();
-        // next chunk's x rows and Delta load during the output phase, its B rows after it
         const int ln = cc + 1 < c1 ? min(geo.Q, a.L - t0 - geo.Q) : 0;
-        if (ln > 0) load_x_rows<N>(a, b, h, t0 + geo.Q, ln, cr);
-        if (I0 >= 0 && I0 * 16 < len) {
-            if (npb == 4) chunk_rows<N, 4, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, pb0, cop0, Dh);
-            else if (npb == 2) chunk_rows<N, 2, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, pb0, cop0, Dh);
-            else chunk_rows<N, 1, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I0, pb0, cop0, Dh);
+        __syncthreads();  // rows, prefix and state copy of this chunk visible
+        if (ln > 0) load_x_rows<N>(v, geo.Q, t0 + geo.Q, cr, PW);
+        if (N0 > 0 && 32 * I0 < len) run_item<N, HAS_Z, HAS_D>(v, lds, sm, geo.Q, sb, t0, len, I0, P0, N0, cop, Dh);
+        if (N1 > 0 && 32 * I1 < len) {
+            load_c<N>(v, t0, I1, cop);
+            run_item<N, HAS_Z, HAS_D>(v, lds, sm, geo.Q, sb, t0, len, I1, P1, N1, cop, Dh);
         }
-        if (I1 >= 0 && I1 * 16 < len) chunk_rows<N, 4, HAS_Z, HAS_D>(a, lds, sm, b, h, t0, len, I1, 0, cop1, Dh);
-        if (ln > 0) load_b_rows<N>(a, b, t0 + geo.Q, ln, cr);
+        if (ln > 0) load_b_rows<N>(v, geo.Q, t0 + geo.Q, cr);
         // state after the chunk (not needed after the last chunk of a super-chunk,
         // except at the very end of the sequence for h_final)
         const bool need_state = (cc < c1 - 1) || (last_super && a.h_final != nullptr);
         if (need_state) {
             StateTiles<N> st;
-            chunk_state<N>(lds, sm, len, st);
-            state_update<N>(lds, sm, hs, st);
-            __syncthreads();  // every wave has finished reading the state copy for Y_off
-            if (cc < c1 - 1) state_to_lds<N>(lds, sm, hs);
+            chunk_state<N>(lds, sm, geo.Q, sb, len, st);
+            state_update<N>(lds, sm, sb, hs, st);
+        }
+        if (ln > 0) {
+            if (wave == PW) chunk_prefix(lds, sm, geo.Q, sb ^ 1, ln, A2, cr.dv);
+            if (N0 > 0) load_c<N>(v, t0 + geo.Q, I0, cop);
+        }
+        __syncthreads();  // every read of this chunk's rows and state copy done
+        if (ln > 0) {
+            state_to_lds<N>(lds, sm, hs);
+            store_xb<N>(lds, sm, geo.Q, cr);
         }
     }
     if (last_super && a.h_final != nullptr) {
@@ -598,17 +807,22 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
     }
     const SsdGeom geo = ssd_geom(a.B, a.L, a.H, a.Q);
     const Smem sm = smem_layout<N>(geo.Q);
+    const OutPlan plan = out_plan(geo.Q / 32, N);
     if (geo.K > 1) {
         profile_mark(st);
-        hipLaunchKernelGGL((ssd_super_state<N>), dim3(geo.K - 1, a.H, a.B), dim3(kThreads), sm.total, st, a, geo);
+        hipLaunchKernelGGL((ssd_super_state<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kThreads), sm.total,
+                           st, a, geo);
+        profile_mark(st);
+        hipLaunchKernelGGL((ssd_carry<N>), dim3((kP * N + 255) / 256, a.H, a.B), dim3(256), 0, st,
+                           a.h0, static_cast<float*>(a.ws), a.B, a.H, geo.K);
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
-    const dim3 grid(geo.K, a.H, a.B);
+    const dim3 grid((unsigned)(geo.K * a.H * a.B));
     profile_mark(st);
-    if (hz && hd) hipLaunchKernelGGL((ssd_chunk_scan<N, true, true>), grid, dim3(kThreads), sm.total, st, a, geo);
-    else if (hz) hipLaunchKernelGGL((ssd_chunk_scan<N, true, false>), grid, dim3(kThreads), sm.total, st, a, geo);
-    else if (hd) hipLaunchKernelGGL((ssd_chunk_scan<N, false, true>), grid, dim3(kThreads), sm.total, st, a, geo);
-    else hipLaunchKernelGGL((ssd_chunk_scan<N, false, false>), grid, dim3(kThreads), sm.total, st, a, geo);
+    if (hz && hd) hipLaunchKernelGGL((ssd_chunk_scan<N, true, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hz) hipLaunchKernelGGL((ssd_chunk_scan<N, true, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hd) hipLaunchKernelGGL((ssd_chunk_scan<N, false, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else hipLaunchKernelGGL((ssd_chunk_scan<N, false, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
     profile_mark(st);
     return hipGetLastError();
 }
@@ -619,9 +833,10 @@ const char* ssd_unsupported_reason(int L, int H, int P, int N, int Q, bool bf16)
     if (!bf16) return "SSD supports bf16 I/O only";
     if (P != kP) return "SSD supports head dim P = 64 only";
     if (N != 64 && N != 128) return "SSD supports N = 64 or 128";
-    if (Q < 32 || Q > 256 || Q % 32 != 0) return "SSD chunk must be a multiple of 32 in [32, 256]";
+    if (Q < 32 || Q > kMaxQ || Q % 32 != 0) return "SSD chunk must be a multiple of 32 in [32, 256]";
     if (H > 65535) return "H must be <= 65535";
     if (L < 0) return "L must be >= 0";
+    if ((long long)L * H * P * 2 > 0x7fffffffLL) return "L * H * P * 2 must be < 2^31 (bytes of one batch row of x)";
     return "";
 }
 
