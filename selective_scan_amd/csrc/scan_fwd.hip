@@ -132,14 +132,17 @@ struct Segment {
     static constexpr uint32_t es = BF16 ? 2 : 4;
     static constexpr bool kZ = FINAL && HAS_Z;
     __amdgpu_buffer_rsrc_t rx, rd, rz, ry;
-    uint32_t voff, rstride;
+    uint32_t voff, yoff, rstride;
     const void* Bbase;
     const void* Cbase;
     int len;
     uint32_t dq[kPrefetch], xq[kPrefetch], zq[kPrefetch];
     Row<N, BF16> Bn, Cn;
 
-    __device__ __forceinline__ Segment(const ScanArgs& a, int b, int dc, int t0, int len_) : len(len_) {
+    // store: this lane's channel exists (d < D); other lanes aim their y stores
+    // past the end of the y view, where the buffer unit drops them (no branch)
+    __device__ __forceinline__ Segment(const ScanArgs& a, int b, int dc, int t0, int len_, bool store = true)
+        : len(len_) {
         const size_t row0 = (size_t)b * a.L + t0;
         const uint32_t bytes = (uint32_t)len * (uint32_t)a.D * es;
         const char* xb = static_cast<const char*>(a.x) + row0 * a.D * es;
@@ -148,6 +151,7 @@ struct Segment {
         rz = make_rsrc(kZ ? static_cast<const char*>(a.z) + row0 * a.D * es : xb, bytes);
         ry = make_rsrc(FINAL ? static_cast<const char*>(a.y) + row0 * a.D * es : xb, bytes);
         voff = (uint32_t)dc * es;
+        yoff = store ? voff : 0x80000000u;
         rstride = (uint32_t)a.D * es;
         Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
         Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
@@ -165,7 +169,7 @@ struct Segment {
     // one time step t from ring slot k; RELOAD: refill the slot with step t + kPrefetch
     template <bool RELOAD>
     __device__ __forceinline__ void step(int t, int k, const float (&A2)[N], float (&h)[N], float Dv,
-                                         bool store, float& sumd) {
+                                         float& sumd) {
         const float dv = widen<BF16>(dq[k]), xv = widen<BF16>(xq[k]);
         const float zv = kZ ? widen<BF16>(zq[k]) : 0.0f;
         if constexpr (RELOAD) {
@@ -193,7 +197,7 @@ struct Segment {
             float v = y0 + y1;
             if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
             if constexpr (HAS_Z) v *= silu(zv);
-            if (store) store_io<BF16>(ry, voff, (uint32_t)t * rstride, v);
+            store_io<BF16>(ry, yoff, (uint32_t)t * rstride, v);
         } else {
             sumd += dv;
 #pragma unroll
@@ -206,16 +210,15 @@ struct Segment {
 
     // the whole segment from state h: full blocks of kPrefetch steps with a
     // static ring slot per step, then the tail straight from the ring.
-    __device__ __forceinline__ void run(const float (&A2)[N], float (&h)[N], float Dv, bool store,
-                                        float& sumd) {
+    __device__ __forceinline__ void run(const float (&A2)[N], float (&h)[N], float Dv, float& sumd) {
         int t = 0;
         for (; t + kPrefetch <= len; t += kPrefetch) {
 #pragma unroll
-            for (int k = 0; k < kPrefetch; ++k) step<true>(t + k, k, A2, h, Dv, store, sumd);
+            for (int k = 0; k < kPrefetch; ++k) step<true>(t + k, k, A2, h, Dv, sumd);
         }
 #pragma unroll
         for (int k = 0; k < kPrefetch - 1; ++k)
-            if (t + k < len) step<false>(t + k, k, A2, h, Dv, store, sumd);
+            if (t + k < len) step<false>(t + k, k, A2, h, Dv, sumd);
     }
 };
 
@@ -244,7 +247,7 @@ segment_aggregate(ScanArgs a, Geom g) {
     float sumd = 0.0f;
     if (len > 0) {
         Segment<N, BF16, false, false, false> seg(a, b, dc, t0, len);
-        seg.run(A2, h, 0.0f, false, sumd);
+        seg.run(A2, h, 0.0f, sumd);
     }
     // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]; a segment past L is the identity (1, 0).
     float* sP = lds;
@@ -341,7 +344,7 @@ segment_final(ScanArgs a, Geom g) {
 
     // every load that does not depend on the recurrence first: the segment's
     // first inputs, A, the state entering the group and the in-group prefix
-    Segment<N, BF16, HAS_Z, HAS_D, true> seg(a, b, dc, t0, len);
+    Segment<N, BF16, HAS_Z, HAS_D, true> seg(a, b, dc, t0, len, d < D);
     float A2[N], hg[N], E[N];
     float cs = 0.0f;
 #pragma unroll
@@ -372,7 +375,7 @@ segment_final(ScanArgs a, Geom g) {
     for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hg[n], E[n]);
     const float Dv = HAS_D ? a.Dskip[dc] : 0.0f;
     float unused = 0.0f;
-    seg.run(A2, h, Dv, d < D, unused);
+    seg.run(A2, h, Dv, unused);
     if (d < D && s == g.S - 1 && a.h_final != nullptr) {
         float* hp = a.h_final + ((size_t)b * D + d) * N;
 #pragma unroll
