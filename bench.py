@@ -47,7 +47,8 @@ def hip():
 
 
 class KernelTimer:
-    """HIP events recorded by the library around every kernel launch it makes."""
+    """HIP events the library hands to the runtime with every kernel launch it
+    makes: a (start, stop) pair per kernel, stamped at the kernel's own start and end."""
 
     def __init__(self, n):
         self.h = hip()
@@ -118,7 +119,7 @@ def scan_alg_bytes(wl):
 
 
 def count_kernels(call):
-    """Kernels one call launches: the library records one event per launch plus one."""
+    """Kernels one call launches: the library uses two events per launch."""
     import selective_scan_amd as ssa
     lib = ssa.ops.lib()
     kt = KernelTimer(64)
@@ -127,7 +128,7 @@ def count_kernels(call):
     used = kt.stop(lib)
     sync()
     kt.close()
-    return used - 1
+    return used // 2
 
 
 def time_calls(call, sets, steps, warmup, n_kernels):
@@ -149,27 +150,27 @@ def time_calls(call, sets, steps, warmup, n_kernels):
     t1.record()
     sync()
     total_ms = t0.elapsed_time(t1)
-    kt = KernelTimer(steps * (n_kernels + 1))
+    kt = KernelTimer(steps * 2 * n_kernels)
     kt.start(lib)
     for i in range(steps):
         call(sets[(warmup + steps + i) % len(sets)])
     used = kt.stop(lib)
     sync()
-    per_k = n_kernels + 1
+    per_k = 2 * n_kernels
     assert used == steps * per_k, f"recorded {used} events, expected {steps * per_k}"
-    ker = np.array([[kt.elapsed_ms(s * per_k + k, s * per_k + k + 1) for k in range(n_kernels)]
+    ker = np.array([[kt.elapsed_ms(s * per_k + 2 * k, s * per_k + 2 * k + 1) for k in range(n_kernels)]
                     for s in range(steps)])
     kt.close()
     return total_ms, ker
 
 
-def committed_traffic(kernel_source, workload):
-    """HBM bytes per launch of the dominant kernel, from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary for this workload -- only while the kernel's
-    source is byte-identical to the one the counters were taken on."""
+def committed_traffic(kernel_source, summary):
+    """HBM bytes per launch (or per call), from a committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary under profiles/ -- only while the kernel source
+    is byte-identical to the one the counters were taken on."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    path = os.path.join(ROOT, "profiles", summary)
     src = os.path.join(ROOT, "selective_scan_amd", "csrc", kernel_source)
     if not (os.path.exists(path) and os.path.exists(src)):
         return None
@@ -202,8 +203,8 @@ def scan_bench(name, wl, steps, warmup, dev):
     achieved = SLOTS_PER_UPDATE * upd / tdom / 1e12
     peak = LANE_SLOTS_PER_S / 1e12
     res["roofline"] = dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s",
-                           frac=achieved / peak, traffic=committed_traffic("scan_fwd.hip", name),
-                           kernel="segment_kernel (final pass)" if nk > 1 else "segment_kernel")
+                           frac=achieved / peak, traffic=committed_traffic("scan_fwd.hip", f"traffic_{name}.md"),
+                           kernel="segment_final" if nk > 1 else "segment")
     res["hbm_roofline_dominant"] = dict(achieved=alg / tdom / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
                                         frac=alg / tdom / 1e9 / HBM_PEAK_GBS)
     return res, w0
@@ -288,8 +289,9 @@ def ssd_bench(name, wl, steps, warmup, dev, max_sets=3):
                 mfma_tflops=fl / (ms * 1e-3) / 1e12,
                 mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 roofline=dict(bound="hbm", achieved=byt / (ms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, traffic=None,
-                              kernel="whole call (two kernels)"),
+                              frac=byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              traffic=committed_traffic("ssd_fwd.hip", f"ssd_kernels_{name[4:]}.md"),
+                              kernel="whole call (three kernels)"),
                 dominant_kernel_ms=tdom * 1e3, alg_bytes=byt, alg_flops=fl)
 
 

@@ -73,13 +73,15 @@ const char* ssm_status_string(int status);
 const char* ssm_last_error(void);
 
 /* Kernel-level timing without a profiler (diagnostic; for benchmarks).
- * After ssm_profile_events(events, n) with n > 0, every entry point called from
- * this thread records, on its stream, one event right before each kernel it
- * launches and one after its last launch, taking events[0], events[1], ... in
- * order (each a hipEvent_t created by the caller); recording stops when the n
- * events are used up. ssm_profile_events(NULL, 0) switches recording off.
- * Returns the number of events recorded since the previous call. Per thread;
- * the library never creates, synchronises or destroys the events. */
+ * After ssm_profile_events(events, n) with n > 0, every kernel launched by an
+ * entry point called from this thread takes the next two events (events[0] and
+ * events[1] for the first kernel, and so on; each a hipEvent_t created by the
+ * caller), which the HIP runtime stamps at that kernel's own start and end
+ * (hipExtLaunchKernel), so hipEventElapsedTime of a pair is the kernel's
+ * duration. Recording stops when fewer than two events remain.
+ * ssm_profile_events(NULL, 0) switches recording off. Returns the number of
+ * events used since the previous call (twice the number of kernels timed).
+ * Per thread; the library never creates, synchronises or destroys the events. */
 int ssm_profile_events(void* const* events, int n);
 
 /* ---------------------------------------------------------------------------

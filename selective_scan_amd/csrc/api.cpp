@@ -55,10 +55,12 @@ int hip_status(hipError_t e, const char* fn) {
 }  // namespace
 
 namespace ssm {
-void profile_mark(hipStream_t stream) {
-    if (g_prof.ev == nullptr || g_prof.used >= g_prof.n) return;
-    (void)hipEventRecord(static_cast<hipEvent_t>(g_prof.ev[g_prof.used]), stream);
-    ++g_prof.used;
+void profile_events(hipEvent_t* start, hipEvent_t* stop) {
+    *start = *stop = nullptr;
+    if (g_prof.ev == nullptr || g_prof.used + 2 > g_prof.n) return;
+    *start = static_cast<hipEvent_t>(g_prof.ev[g_prof.used]);
+    *stop = static_cast<hipEvent_t>(g_prof.ev[g_prof.used + 1]);
+    g_prof.used += 2;
 }
 }  // namespace ssm
 

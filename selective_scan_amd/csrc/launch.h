@@ -3,13 +3,26 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <stdint.h>
 #include <stddef.h>
 
 namespace ssm {
 
-// Records the next caller-provided timing event on `stream` if the calling
-// thread enabled ssm_profile_events(); otherwise does nothing.
-void profile_mark(hipStream_t stream);
+// The next two caller-provided timing events if the calling thread enabled
+// ssm_profile_events() and two remain; otherwise both null.
+void profile_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Launches `kernel` on `stream`. When timing is on, the runtime stamps the two
+// events at the kernel's own start and end (not at the surrounding queue
+// positions), so the pair times the kernel alone.
+template <typename... Params, typename... Args>
+inline void launch(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                   Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    profile_events(&e0, &e1);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, e0, e1, 0u, static_cast<Params>(args)...);
+}
 
 // ------------------------------------------------------------ Mamba-1 scan
 struct ScanArgs {

@@ -395,10 +395,8 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     if (a.L == 0) {
         if (a.h_final) {
             const size_t n = (size_t)a.B * a.D * a.N;
-            profile_mark(st);
-            hipLaunchKernelGGL(copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+            launch(copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                                a.h0, a.h_final, n);
-            profile_mark(st);
         }
         return hipGetLastError();
     }
@@ -407,26 +405,22 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     const size_t lds_fin = 0;
     if (g.S > 1) {
-        profile_mark(st);
-        hipLaunchKernelGGL((segment_aggregate<N, BF16>), grid, block, lds_agg, st, a, g);
+        launch((segment_aggregate<N, BF16>), grid, block, lds_agg, st, a, g);
     }
     if (g.G > 1) {
         const size_t tot = (size_t)a.B * N * a.D;
-        profile_mark(st);
-        hipLaunchKernelGGL((group_carry<N>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
+        launch((group_carry<N>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
                            a.h0, static_cast<float*>(a.ws), a.B, a.D, g);
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
-    profile_mark(st);
     if (hz && hd)
-        hipLaunchKernelGGL((segment_final<N, BF16, true, true>), grid, block, lds_fin, st, a, g);
+        launch((segment_final<N, BF16, true, true>), grid, block, lds_fin, st, a, g);
     else if (hz)
-        hipLaunchKernelGGL((segment_final<N, BF16, true, false>), grid, block, lds_fin, st, a, g);
+        launch((segment_final<N, BF16, true, false>), grid, block, lds_fin, st, a, g);
     else if (hd)
-        hipLaunchKernelGGL((segment_final<N, BF16, false, true>), grid, block, lds_fin, st, a, g);
+        launch((segment_final<N, BF16, false, true>), grid, block, lds_fin, st, a, g);
     else
-        hipLaunchKernelGGL((segment_final<N, BF16, false, false>), grid, block, lds_fin, st, a, g);
-    profile_mark(st);
+        launch((segment_final<N, BF16, false, false>), grid, block, lds_fin, st, a, g);
     return hipGetLastError();
 }
 

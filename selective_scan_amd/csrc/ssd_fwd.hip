@@ -798,10 +798,8 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
     if (a.L == 0) {
         if (a.h_final) {
             const size_t n = (size_t)a.B * a.H * N * a.P;
-            profile_mark(st);
-            hipLaunchKernelGGL(copy_state_ssd, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+            launch(copy_state_ssd, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                                a.h0, a.h_final, n);
-            profile_mark(st);
         }
         return hipGetLastError();
     }
@@ -809,21 +807,17 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
     const Smem sm = smem_layout<N>(geo.Q);
     const OutPlan plan = out_plan(geo.Q / 32, N);
     if (geo.K > 1) {
-        profile_mark(st);
-        hipLaunchKernelGGL((ssd_super_state<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kThreads), sm.total,
+        launch((ssd_super_state<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kThreads), sm.total,
                            st, a, geo);
-        profile_mark(st);
-        hipLaunchKernelGGL((ssd_carry<N>), dim3((kP * N + 255) / 256, a.H, a.B), dim3(256), 0, st,
+        launch((ssd_carry<N>), dim3((kP * N + 255) / 256, a.H, a.B), dim3(256), 0, st,
                            a.h0, static_cast<float*>(a.ws), a.B, a.H, geo.K);
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     const dim3 grid((unsigned)(geo.K * a.H * a.B));
-    profile_mark(st);
-    if (hz && hd) hipLaunchKernelGGL((ssd_chunk_scan<N, true, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else if (hz) hipLaunchKernelGGL((ssd_chunk_scan<N, true, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else if (hd) hipLaunchKernelGGL((ssd_chunk_scan<N, false, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else hipLaunchKernelGGL((ssd_chunk_scan<N, false, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    profile_mark(st);
+    if (hz && hd) launch((ssd_chunk_scan<N, true, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hz) launch((ssd_chunk_scan<N, true, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hd) launch((ssd_chunk_scan<N, false, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else launch((ssd_chunk_scan<N, false, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
     return hipGetLastError();
 }
 

@@ -103,12 +103,10 @@ hipError_t launch_n(const StepArgs& a, hipStream_t st) {
     const long F = (long)a.D * (N / 4);
     const dim3 grid((unsigned)((F + kStepThreads * kReps - 1) / (kStepThreads * kReps)), (unsigned)a.B);
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
-    profile_mark(st);
-    if (hz && hd) hipLaunchKernelGGL((step_kernel<N, BF16, true, true>), grid, dim3(kStepThreads), 0, st, a);
-    else if (hz) hipLaunchKernelGGL((step_kernel<N, BF16, true, false>), grid, dim3(kStepThreads), 0, st, a);
-    else if (hd) hipLaunchKernelGGL((step_kernel<N, BF16, false, true>), grid, dim3(kStepThreads), 0, st, a);
-    else hipLaunchKernelGGL((step_kernel<N, BF16, false, false>), grid, dim3(kStepThreads), 0, st, a);
-    profile_mark(st);
+    if (hz && hd) launch((step_kernel<N, BF16, true, true>), grid, dim3(kStepThreads), 0, st, a);
+    else if (hz) launch((step_kernel<N, BF16, true, false>), grid, dim3(kStepThreads), 0, st, a);
+    else if (hd) launch((step_kernel<N, BF16, false, true>), grid, dim3(kStepThreads), 0, st, a);
+    else launch((step_kernel<N, BF16, false, false>), grid, dim3(kStepThreads), 0, st, a);
     return hipGetLastError();
 }
 
