@@ -178,7 +178,7 @@ OutPlan out_plan(int R, int N) {
 
 // LDS layout (bytes), per workgroup
 struct Smem {
-    int xs, bs, hh, hl, sv, red, total;
+    int xs, bs, hh, hl, sv, red, tot, total;
 };
 
 template <int N>
@@ -190,7 +190,8 @@ __host__ __device__ inline Smem smem_layout(int Q) {
     s.hl = s.hh + kP * (N + kHPad) * 2;    // bf16 [P][N+kHPad]   state H^T, remainder
     s.sv = s.hl + kP * (N + kHPad) * 2;    // f32  [2][kArrays][Q] two prefix buffers
     s.red = s.sv + 2 * kArrays * Q * 4;    // f32  [2]  s_last of each prefix buffer
-    s.total = s.red + 16;
+    s.tot = s.red + 16;                    // f64  [kWaves]  per-wave partial sums
+    s.total = s.tot + 8 * kWaves;
     return s;
 }
 
@@ -369,7 +370,7 @@ struct StateTiles {
 
 template <int N>
 __device__ __forceinline__ void chunk_state(const lds_t* lds, const Smem& sm, int Q, int sb, int len,
-                                            StateTiles<N>& st) {
+                                            StateTiles<N>& st, bool accumulate = false) {
     constexpr int NBW = StateTiles<N>::NBW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4;
@@ -378,7 +379,8 @@ __device__ __forceinline__ void chunk_state(const lds_t* lds, const Smem& sm, in
     const lds_u16* bs = reinterpret_cast<const lds_u16*>(lds + sm.bs);
     const lds_f32* w = sv_arr(lds, sm, Q, sb, 2);
 #pragma unroll
-    for (int k = 0; k < NBW; ++k) st.acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NBW; ++k)
+        if (!accumulate) st.acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     // operands of one 32-step block: x (4 + 4 steps of column p), the weights,
     // and the B operands of this wave's n-blocks
     struct Ops {
@@ -486,59 +488,108 @@ __device__ __forceinline__ void block_coords(int H, int Kp, int& h, int& k, int&
     b = r / Kp;
 }
 
+// Weights of one staged block of a super-chunk's aggregate, computed by wave 0:
+// w_t = exp2(lam - s_t) Delta_t, with s_t the inclusive log2-decay prefix from the
+// super-chunk's start (fp64), lam its total, and zero for steps t >= len. `off` is
+// the prefix before the block and is advanced past it. Lane l owns steps 4l..4l+3.
+__device__ __forceinline__ void agg_weights(lds_t* lds, const Smem& sm, int sb, int len, float A2,
+                                            const float (&dv)[4], double lam, double& off) {
+    const int lane = threadIdx.x & 63;
+    lds_f32* w = sv_arr(lds, sm, kMaxQ, sb, 2);
+    float d[4];
+    double loc[4], run = 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        d[k] = (4 * lane + k < len) ? dv[k] : 0.0f;
+        run += (double)(d[k] * A2);
+        loc[k] = run;
+    }
+    double incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    const double base = off + (incl - run);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[4 * lane + k] = exp2_fast((float)(lam - (base + loc[k]))) * d[k];
+    off += __shfl(incl, 63, 64);
+}
+
+// Aggregate of one super-chunk (all but the last of each (batch, head)), from a
+// zero state: S = sum over its steps of exp2(Lam - s_t) Delta_t B_t (x) x_t, one
+// long contraction over time, staged in LDS 256 steps at a time whatever the
+// chunk length, with Lam = sum of Delta_t A log2 e over the super-chunk (its
+// total log2 decay, also written out). This is the end state of the chunk
+// recurrence started from zero: each chunk's decays multiply into exp2(Lam - s_t).
 template <int N>
 __global__ void __launch_bounds__(kThreads)
 ssd_super_state(SsdArgs a, SsdGeom geo) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     lds_t* lds = (lds_t*)lds_raw;
-    const Smem sm = smem_layout<N>(geo.Q);
+    const Smem sm = smem_layout<N>(kMaxQ);
     int h, k, b;
     block_coords(a.H, geo.K - 1, h, k, b);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const float A2 = a.A[h] * kLog2e;
-    State<N> hs;
-#pragma unroll
-    for (int kk = 0; kk < StateTiles<N>::NBW; ++kk) hs.h[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-    double lam = 0.0;
-    const int c0 = k * geo.cps, c1 = min(geo.C, c0 + geo.cps);
+    const int T0 = k * geo.cps * geo.Q, T1 = min(a.L, (k + 1) * geo.cps * geo.Q);
+    const int nblk = (T1 - T0 + kMaxQ - 1) / kMaxQ;
     const Views v = make_views<N>(a, b, h);
-    // Rows arrive two chunks ahead of their use: while chunk cc is contracted,
-    // `nxt` holds the loads of chunk cc + 1 in flight and `nxt2` receives those
-    // of chunk cc + 2. The two register sets swap roles every chunk (the loop
-    // body is written out twice so that no in-flight register is copied).
-    ChunkRows<N> ra, rb;
+
+    // total log2 decay of the super-chunk (fp64; fixed-order block reduction)
+    double lam;
     {
-        const int len0 = min(geo.Q, a.L - c0 * geo.Q);
-        load_x_rows<N>(v, geo.Q, c0 * geo.Q, rb, 0);
-        load_b_rows<N>(v, geo.Q, c0 * geo.Q, rb);
-        if (c0 + 1 < c1) {
-            load_x_rows<N>(v, geo.Q, (c0 + 1) * geo.Q, ra, 0);
-            load_b_rows<N>(v, geo.Q, (c0 + 1) * geo.Q, ra);
-        }
-        if (wave == 0) chunk_prefix(lds, sm, geo.Q, 0, len0, A2, rb.dv);
-        store_xb<N>(lds, sm, geo.Q, rb);
+        double part = 0.0;
+        for (int t = T0 + tid; t < T1; t += kThreads)
+            part += (double)(bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+                                 v.dl, (int)((uint32_t)t * v.drow + v.xh / kP), 0, 0)) * A2);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+        __attribute__((address_space(3))) double* red =
+            reinterpret_cast<__attribute__((address_space(3))) double*>(lds + sm.tot);
+        if (lane == 0) red[wave] = part;
+        __syncthreads();
+        lam = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) lam += red[w];
     }
-    auto step = [&](int cc, ChunkRows<N>& nxt, ChunkRows<N>& nxt2) {
-        const int sb = (cc - c0) & 1;
-        const int t0 = cc * geo.Q;
-        const int len = min(geo.Q, a.L - t0);
-        const int ln = cc + 1 < c1 ? min(geo.Q, a.L - t0 - geo.Q) : 0;
-        __syncthreads();  // rows and prefix of this chunk visible
-        if (cc + 2 < c1) {
-            load_x_rows<N>(v, geo.Q, t0 + 2 * geo.Q, nxt2, 0);
-            load_b_rows<N>(v, geo.Q, t0 + 2 * geo.Q, nxt2);
+
+    StateTiles<N> st;
+#pragma unroll
+    for (int kk = 0; kk < StateTiles<N>::NBW; ++kk) st.acc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    double off = 0.0;
+    // Rows arrive two blocks ahead of their use: while block j is contracted,
+    // `nxt` holds the loads of block j + 1 in flight and `nxt2` receives those of
+    // block j + 2. The two register sets swap roles every block (the loop body is
+    // written out twice so that no in-flight register is copied).
+    ChunkRows<N> ra, rb;
+    load_x_rows<N>(v, kMaxQ, T0, rb, 0);
+    load_b_rows<N>(v, kMaxQ, T0, rb);
+    if (nblk > 1) {
+        load_x_rows<N>(v, kMaxQ, T0 + kMaxQ, ra, 0);
+        load_b_rows<N>(v, kMaxQ, T0 + kMaxQ, ra);
+    }
+    if (wave == 0) agg_weights(lds, sm, 0, min(kMaxQ, T1 - T0), A2, rb.dv, lam, off);
+    store_xb<N>(lds, sm, kMaxQ, rb);
+    auto step = [&](int j, ChunkRows<N>& nxt, ChunkRows<N>& nxt2) {
+        const int sb = j & 1;
+        const int t0 = T0 + j * kMaxQ;
+        const int len = min(kMaxQ, T1 - t0);
+        const int ln = j + 1 < nblk ? min(kMaxQ, T1 - t0 - kMaxQ) : 0;
+        __syncthreads();  // rows and weights of this block visible
+        if (j + 2 < nblk) {
+            load_x_rows<N>(v, kMaxQ, t0 + 2 * kMaxQ, nxt2, 0);
+            load_b_rows<N>(v, kMaxQ, t0 + 2 * kMaxQ, nxt2);
         }
-        StateTiles<N> st;
-        chunk_state<N>(lds, sm, geo.Q, sb, len, st);
-        state_update<N>(lds, sm, sb, hs, st);
-        lam += (double)s_last(lds, sm, sb);
-        if (ln > 0 && wave == 0) chunk_prefix(lds, sm, geo.Q, sb ^ 1, ln, A2, nxt.dv);
-        __syncthreads();  // every read of this chunk's rows done
-        if (ln > 0) store_xb<N>(lds, sm, geo.Q, nxt);
+        chunk_state<N>(lds, sm, kMaxQ, sb, len, st, true);
+        if (ln > 0 && wave == 0) agg_weights(lds, sm, sb ^ 1, ln, A2, nxt.dv, lam, off);
+        __syncthreads();  // every read of this block's rows done
+        if (ln > 0) store_xb<N>(lds, sm, kMaxQ, nxt);
     };
-    for (int cc = c0; cc < c1; cc += 2) {
-        step(cc, ra, rb);
-        if (cc + 1 < c1) step(cc + 1, rb, ra);
+    for (int j = 0; j < nblk; j += 2) {
+        step(j, ra, rb);
+        if (j + 1 < nblk) step(j + 1, rb, ra);
     }
     float* out = static_cast<float*>(a.ws) + (((size_t)b * a.H + h) * (geo.K - 1) + k) * kP * N;
 #pragma unroll
@@ -547,9 +598,9 @@ ssd_super_state(SsdArgs a, SsdGeom geo) {
         for (int r = 0; r < 4; ++r) {
             int p, n;
             tile_pn<N>(kk, r, p, n);
-            out[p * N + n] = hs.h[kk][r];
+            out[p * N + n] = st.acc[kk][r];
         }
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         float* lamp = static_cast<float*>(a.ws) + ws_hagg(a.B, a.H, geo.K, N);
         lamp[((size_t)b * a.H + h) * (geo.K - 1) + k] = (float)lam;
     }
@@ -807,8 +858,8 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
     const Smem sm = smem_layout<N>(geo.Q);
     const OutPlan plan = out_plan(geo.Q / 32, N);
     if (geo.K > 1) {
-        launch((ssd_super_state<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kThreads), sm.total,
-                           st, a, geo);
+        launch((ssd_super_state<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kThreads),
+               (uint32_t)smem_layout<N>(kMaxQ).total, st, a, geo);
         launch((ssd_carry<N>), dim3((kP * N + 255) / 256, a.H, a.B), dim3(256), 0, st,
                            a.h0, static_cast<float*>(a.ws), a.B, a.H, geo.K);
     }
