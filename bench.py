@@ -356,6 +356,60 @@ def step_bench(wl, dev, reps=3):
                 note="state (12.6 MB) stays resident in the 256 MB MALL across in-place steps")
 
 
+def ssd_step_bench(wl, dev, reps=3):
+    """Mamba-2 decode: `steps` in-place steps launched on a stream, then the same
+    steps replayed from a HIP graph; per-step time and algorithmic bytes/s."""
+    import torch
+    import selective_scan_amd as ssa
+    import ssm_inputs as si
+    B, H, P, N, steps = wl["B"], wl["H"], wl["P"], wl["N"], wl["steps"]
+    w = si.ssd_step_inputs(B, H, P, N, steps=steps, dtype=wl["dtype"], seed=0)
+    tok = {k: si.to_torch(w[k], dev) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A = torch.from_numpy(w["A"]).to(dev)
+    Dk = torch.from_numpy(w["D"]).to(dev)
+    st0 = torch.from_numpy(w["state0"]).to(dev)
+    st = st0.clone()
+    y = torch.empty((steps, B, H, P), dtype=tok["x"].dtype, device=dev)
+
+    def run():
+        for s in range(steps):
+            ssa.ssm_ssd_step(st, tok["x"][s], tok["delta"][s], A, tok["Bm"][s], tok["Cm"][s], D=Dk,
+                             z=tok["z"][s], y=y[s])
+
+    def timed(fn):
+        out = []
+        for _ in range(reps):
+            st.copy_(st0)
+            sync()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            sync()
+            out.append(e0.elapsed_time(e1) / steps)
+        return float(np.median(out))
+
+    run()
+    sync()
+    ms_stream = timed(run)
+    g = torch.cuda.CUDAGraph()
+    st.copy_(st0)
+    sync()
+    s_ = torch.cuda.Stream()
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            run()
+    sync()
+    ms_graph = timed(g.replay)
+    es = 2 if wl["dtype"] == "bf16" else 4
+    alg = 2 * B * H * N * P * 4 + 3 * B * H * P * es + B * H * es + 2 * B * N * es + 2 * H * 4
+    return dict(workload="ssd_step_bf16_B64_H24_P64_N128_x200", ms_per_step_stream=ms_stream,
+                ms_per_step_graph=ms_graph, updates_per_s_graph=B * H * P * N / (ms_graph * 1e-3),
+                tokens_per_s_graph=B / (ms_graph * 1e-3), alg_bytes_per_step=alg,
+                hbm_gbs_graph=alg / (ms_graph * 1e-3) / 1e9,
+                note="state (50.3 MB) stays resident in the 256 MB MALL across in-place steps")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,6 +474,7 @@ def main():
                    "ssd_bf16_B4_L8000_H24_P64_N128_Q256"):
             other[nm] = ssd_bench(nm, si.WORKLOADS[nm], steps=10, warmup=3, dev=dev)
         other["decode"] = step_bench(si.WORKLOADS["step_bf16_B64_D3072_N16_x1000"], dev)
+        other["ssd_decode"] = ssd_step_bench(si.WORKLOADS["ssd_step_bf16_B64_H24_P64_N128_x200"], dev)
         out["other_paths"] = other
     print(json.dumps(out))
 

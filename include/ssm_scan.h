@@ -1,10 +1,11 @@
 /*
  * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
  *
- * Three entry points, each a hand-written HIP kernel pipeline for CDNA4:
+ * Four entry points, each a hand-written HIP kernel pipeline for CDNA4:
  *   ssm_scan_fwd   Mamba-1 selective scan over a whole sequence (prefill)
  *   ssm_ssd_fwd    Mamba-2 SSD: scalar decay per head, chunked decayed-attention form
  *   ssm_step       one-token recurrent decode step, state updated in place
+ *   ssm_ssd_step   the same for the Mamba-2 form (scalar decay per head, (N, P) state)
  *
  * The operation (selective SSM of Gu & Dao, "Mamba: Linear-Time Sequence
  * Modeling with Selective State Spaces", 2023, and the SSD form of Dao & Gu,
@@ -147,6 +148,28 @@ int ssm_step(int B, int D, int N, int io,
              float* state, const void* x, const void* delta, const float* A,
              const void* Bm, const void* Cm, const float* Dskip, const void* z,
              void* y, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_ssd_step -- one-token decode step of the Mamba-2 form, state in place
+ * (the incremental step of "Efficient Sequence Modeling: From S4 to Mamba-3",
+ * section 03, applied to mamba2_minimal.py's per-head scalar decay and (N, P)
+ * state). Per batch b and head h, with a = exp(delta[b,h] * A[h]):
+ *   S[n, p] = a * S[n, p] + delta[b,h] * Bm[b,n] * x[b,h,p]
+ *   y[b,h,p] = (sum_n Cm[b,n] * S[n, p] + Dskip[h] * x[b,h,p]) * silu(z[b,h,p])
+ *
+ *   state  : [B, H, N, P]  fp32, updated in place
+ *   x, z, y : [B, H, P]    io dtype   (z may be NULL)
+ *   delta  : [B, H]        io dtype
+ *   A      : [H]           fp32
+ *   Bm, Cm : [B, N]        io dtype, shared by all heads
+ *   Dskip  : [H]           fp32 or NULL
+ * Supported: P = 64; N in {16, 32, 64, 128, 256}; B * H <= 2^31 - 1.
+ * Errors as for ssm_step; every pointer must be 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+int ssm_ssd_step(int B, int H, int P, int N, int io,
+                 float* state, const void* x, const void* delta, const float* A,
+                 const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                 void* y, void* stream);
 
 #ifdef __cplusplus
 }

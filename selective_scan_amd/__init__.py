@@ -15,5 +15,6 @@ from .ops import (  # noqa: F401
     ssm_scan_workspace_size,
     ssm_ssd_fwd,
     ssm_ssd_workspace_size,
+    ssm_ssd_step,
     ssm_step,
 )

@@ -185,4 +185,25 @@ int ssm_step(int B, int D, int N, int io,
     return hip_status(ssm::launch_step(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+// ------------------------------------------------------------------ SSD step
+int ssm_ssd_step(int B, int H, int P, int N, int io,
+                 float* state, const void* x, const void* delta, const float* A,
+                 const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                 void* y, void* stream) {
+    const char* fn = "ssm_ssd_step";
+    if (B < 1 || H < 1 || P < 1 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, H, P, N must be >= 1");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (!ssm::ssd_step_supported(P, N))
+        return fail(SSM_ERR_UNSUPPORTED, fn, "P must be 64 and N one of 16, 32, 64, 128, 256");
+    if ((long long)B * H > 0x7fffffffLL) return fail(SSM_ERR_UNSUPPORTED, fn, "B * H must be < 2^31");
+    if (!product_ok({B, H, N, P}, 1LL << 40)) return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if (!state || !x || !delta || !A || !Bm || !Cm || !y)
+        return fail(SSM_ERR_INVALID_ARG, fn, "state, x, delta, A, Bm, Cm and y are required");
+    const void* ptrs[] = {state, x, delta, A, Bm, Cm, Dskip, z, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    ssm::SsdStepArgs a{B, H, P, N, io == SSM_BF16, state, x, delta, A, Bm, Cm, Dskip, z, y};
+    return hip_status(ssm::launch_ssd_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -71,6 +71,24 @@ struct StepArgs {
 bool step_supported_n(int N);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------ SSD decode step
+struct SsdStepArgs {
+    int B, H, P, N;
+    bool bf16;
+    float* state;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    void* y;
+};
+
+bool ssd_step_supported(int P, int N);
+hipError_t launch_ssd_step(const SsdStepArgs& a, hipStream_t stream);
+
 // ------------------------------------------------------------ SSD
 struct SsdArgs {
     int B, L, H, P, N, Q;

@@ -46,6 +46,8 @@ def lib():
     L.ssm_ssd_fwd.restype = i
     L.ssm_step.argtypes = [i, i, i, i] + [fp] + [vp] * 8 + [vp]
     L.ssm_step.restype = i
+    L.ssm_ssd_step.argtypes = [i, i, i, i, i] + [fp] + [vp] * 8 + [vp]
+    L.ssm_ssd_step.restype = i
     _lib = L
     return _lib
 
@@ -188,4 +190,27 @@ def ssm_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=None)
                         _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream(dev, stream))
     if st != SSM_OK:
         _raise("ssm_step", st)
+    return y
+
+
+def ssm_ssd_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=None):
+    """One Mamba-2 decode step. state: [B, H, N, P] fp32 (updated in place); x, z: [B, H, P];
+    delta: [B, H]; Bm, Cm: [B, N]; A: [H]; D: [H]. Returns y [B, H, P]."""
+    Bb, H, N, P = state.shape
+    dev, io = x.device, x.dtype
+    _check(state, "state", (Bb, H, N, P), torch.float32, dev)
+    _check(x, "x", (Bb, H, P), io, dev)
+    _check(delta, "delta", (Bb, H), io, dev)
+    _check(A, "A", (H,), torch.float32, dev)
+    _check(Bm, "Bm", (Bb, N), io, dev)
+    _check(Cm, "Cm", (Bb, N), io, dev)
+    _check(D, "D", (H,), torch.float32, dev, required=False)
+    _check(z, "z", (Bb, H, P), io, dev, required=False)
+    if y is None:
+        y = torch.empty((Bb, H, P), dtype=io, device=dev)
+    _check(y, "y", (Bb, H, P), io, dev)
+    st = lib().ssm_ssd_step(Bb, H, P, N, _io_code(x), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
+                            _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_ssd_step", st)
     return y

@@ -155,6 +155,24 @@ def step_inputs(B, D, N, steps, dtype=BF16, seed=0, with_D=True, with_z=True):
     return out
 
 
+def ssd_step_inputs(B, H, P, N, steps, dtype=BF16, seed=0, with_D=True, with_z=True):
+    """Mamba-2 decode inputs: state0 [B,H,N,P] fp32 ~ 0.1 N(0,1); per-token x, z
+    [steps,B,H,P], delta [steps,B,H] and Bm, Cm [steps,B,N] in ``dtype``; A [H],
+    D [H] fp32 (distributions as ``ssd_inputs``)."""
+    out = {}
+    out["state0"] = (0.1 * _normal(seed, TID_STATE0, (B, H, N, P))).astype(np.float32)
+    out["x"] = store(_normal(seed, TID_X, (steps, B, H, P)), dtype)
+    out["delta"] = store(_delta(seed, (steps, B, H), _dt_per_channel(seed, H)), dtype)
+    out["z"] = store(_normal(seed, TID_Z, (steps, B, H, P)), dtype) if with_z else None
+    s = 1.0 / math.sqrt(N)
+    out["Bm"] = store(_normal(seed, TID_B, (steps, B, N)) * s, dtype)
+    out["Cm"] = store(_normal(seed, TID_C, (steps, B, N)) * s, dtype)
+    out["A"] = (-np.exp(_rng(seed, TID_A).uniform(0.0, math.log(16.0), size=H))).astype(np.float32)
+    out["D"] = _normal(seed, TID_D, (H,)).astype(np.float32) if with_D else None
+    out["dtype"] = dtype
+    return out
+
+
 # Workloads of the benchmark configurations (sizes of the pages' workloads).
 WORKLOADS = {
     "scan_f32_B1_L256_D64_N16": dict(kind="scan", B=1, L=256, D=64, N=16, dtype=F32),
@@ -167,4 +185,7 @@ WORKLOADS = {
     "ssd_bf16_B4_L8000_H24_P64_N128_Q256": dict(kind="ssd", B=4, L=8000, H=24, P=64, N=128,
                                                 chunk=256, dtype=BF16),
     "step_bf16_B64_D3072_N16_x1000": dict(kind="step", B=64, D=3072, N=16, steps=1000, dtype=BF16),
+    # Mamba-2 decode (a Mamba2-130m-sized layer: 24 heads of 64, N = 128), 200 steps in place
+    "ssd_step_bf16_B64_H24_P64_N128_x200": dict(kind="ssd_step", B=64, H=24, P=64, N=128, steps=200,
+                                                dtype=BF16),
 }

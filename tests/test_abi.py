@@ -22,9 +22,9 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("ssm_scan_fwd", "ssm_ssd_fwd", "ssm_step"):
+    for n in ("ssm_scan_fwd", "ssm_ssd_fwd", "ssm_step", "ssm_ssd_step"):
         assert n in names
 
 
@@ -80,6 +80,25 @@ def test_step_rejects_bad_arguments():
     assert call(state=None) == 1
     assert call(y=ctypes.c_void_p(0x10008)) == 1
     assert call(io=3) == 1
+
+
+def test_ssd_step_rejects_bad_arguments():
+    L = ops.lib()
+    ok = dict(B=2, H=3, Pp=64, N=128, io=1)
+    def call(**kw):
+        a = dict(ok, state=P, x=P, delta=P, A=P, Bm=P, Cm=P, Dk=None, z=None, y=P)
+        a.update(kw)
+        return L.ssm_ssd_step(a["B"], a["H"], a["Pp"], a["N"], a["io"], a["state"], a["x"], a["delta"],
+                              a["A"], a["Bm"], a["Cm"], a["Dk"], a["z"], a["y"], None)
+    assert call(B=0) == 1
+    assert call(H=0) == 1
+    assert call(io=3) == 1
+    assert call(Pp=32) == 2
+    assert call(N=48) == 2
+    assert call(N=512) == 2
+    assert call(state=None) == 1
+    assert call(x=ctypes.c_void_p(0x10004)) == 1
+    assert ops.lib().ssm_last_error().startswith(b"ssm_ssd_step: ")
 
 
 def test_ssd_rejects_bad_arguments():
