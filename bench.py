@@ -470,6 +470,11 @@ def main():
                            steps=5, warmup=2, dev=dev)
         other["scan_long"] = {k: r2[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
                                                    "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
+        for nm in ("scan_bf16_B1_L4096_D1536_N64", "scan_bf16_B1_L4096_D1536_N128",
+                   "scan_bf16_B1_L4096_D1536_N256"):
+            r3, _ = scan_bench(nm, si.WORKLOADS[nm], steps=10, warmup=2, dev=dev)
+            other[nm] = {k: r3[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
+                                            "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
         for nm in ("ssd_bf16_B4_L8192_H24_P64_N128_Q256", "ssd_bf16_B4_L8192_H24_P64_N128_Q64",
                    "ssd_bf16_B4_L8000_H24_P64_N128_Q256"):
             other[nm] = ssd_bench(nm, si.WORKLOADS[nm], steps=10, warmup=3, dev=dev)

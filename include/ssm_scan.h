@@ -97,7 +97,8 @@ int ssm_profile_events(void* const* events, int n);
  *   workspace      : device scratch of at least ssm_scan_workspace_size(B, L, D, N)
  *                    bytes (NULL allowed when that size is 0); contents on entry
  *                    are ignored and on return are undefined.
- * Supported: N in {4, 8, 16, 32, 64}; B, D >= 1; L >= 0 (L = 0 writes h_final = h0).
+ * Supported: N in {4, 8, 16, 32, 64, 128, 256}; B, D >= 1; L >= 0 (L = 0 writes
+ * h_final = h0). N > 64 needs a workspace even for short sequences.
  * Every pointer must be 16-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t ssm_scan_workspace_size(int B, int L, int D, int N);

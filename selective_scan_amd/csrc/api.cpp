@@ -105,7 +105,7 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
     const char* fn = "ssm_scan_fwd";
     if (B < 1 || D < 1 || L < 0 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1 and L >= 0");
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
-    if (!ssm::scan_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64");
+    if (!ssm::scan_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128, 256");
     if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
     if (!product_ok({B, L, D, N}) || !product_ok({B, L, D}, 1LL << 40))
         return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");

@@ -178,6 +178,10 @@ WORKLOADS = {
     "scan_f32_B1_L256_D64_N16": dict(kind="scan", B=1, L=256, D=64, N=16, dtype=F32),
     "scan_bf16_B1_L4096_D1536_N16": dict(kind="scan", B=1, L=4096, D=1536, N=16, dtype=BF16),
     "scan_bf16_B8_L32768_D512_N16": dict(kind="scan", B=8, L=32768, D=512, N=16, dtype=BF16),
+    # ssm-bench's state-dimension sweep at the headline layer's size
+    "scan_bf16_B1_L4096_D1536_N64": dict(kind="scan", B=1, L=4096, D=1536, N=64, dtype=BF16),
+    "scan_bf16_B1_L4096_D1536_N128": dict(kind="scan", B=1, L=4096, D=1536, N=128, dtype=BF16),
+    "scan_bf16_B1_L4096_D1536_N256": dict(kind="scan", B=1, L=4096, D=1536, N=256, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q256": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,
                                                 chunk=256, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q64": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,

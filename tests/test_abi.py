@@ -49,7 +49,7 @@ def _scan(B=1, L=8, D=64, N=16, io=1, x=P, delta=P, A=P, Bm=P, Cm=P, Dk=None, z=
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(D=0), 1), (dict(L=-1), 1), (dict(N=0), 1), (dict(io=7), 1),
-    (dict(N=12), 2), (dict(N=128), 2), (dict(B=70000), 2),
+    (dict(N=12), 2), (dict(N=512), 2), (dict(B=70000), 2),
     (dict(x=None), 1), (dict(A=None), 1), (dict(y=None), 1), (dict(Cm=None), 1),
     (dict(x=ctypes.c_void_p(0x10004)), 1),
 ])

@@ -31,6 +31,11 @@ SMALL = [
     (2, 513, 200, 64, si.BF16, True, True, True),
     (1, 4097, 96, 16, si.BF16, False, True, False),
     (5, 77, 1, 16, si.F32, True, True, True),
+    # N above 64: the state index runs in chunks of 64 (partial C . h, then a combine)
+    (2, 700, 90, 128, si.BF16, True, True, True),
+    (1, 1500, 64, 256, si.F32, True, False, True),
+    (1, 40, 33, 128, si.F32, False, True, False),
+    (3, 257, 128, 256, si.BF16, True, True, False),
 ]
 
 
@@ -66,6 +71,16 @@ def test_scan_config_bf16_B8_L32768_D512_N16_sampled():
     w = si.scan_inputs(8, 32768, 512, 16, dtype=si.BF16, seed=0)
     sel = np.array([0, 1, 63, 64, 100, 255, 256, 300, 383, 384, 450, 510, 511])
     _check(w, sel=sel, what="c2")
+
+
+@pytest.mark.parametrize("N", [64, 128, 256])
+def test_scan_state_dim_sweep_bf16_B1_L4096_D1536_sampled(N):
+    """The state-dimension sweep (N = 64, 128, 256) at the headline layer's size;
+    oracle on 48 sampled channels (including the first and last)."""
+    print(f"[scan] bf16 B1 L4096 D1536 N{N} (48 sampled channels)", flush=True)
+    w = si.scan_inputs(1, 4096, 1536, N, dtype=si.BF16, seed=0)
+    sel = np.unique(np.concatenate([[0, 1535], np.random.default_rng(N).choice(1536, 46, replace=False)]))
+    _check(w, sel=sel, what=f"N{N} sweep")
 
 
 def test_scan_split_carry_on_gpu():
