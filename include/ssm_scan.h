@@ -143,7 +143,7 @@ int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
  *   A      : [D, N]  fp32
  *   Bm, Cm : [B, N]  io dtype
  *   Dskip  : [D]     fp32 or NULL
- * Supported: N in {4, 8, 16, 32, 64}; B <= 65535; D * N <= 2^32.
+ * Supported: N in {4, 8, 16, 32, 64, 128, 256}; B <= 65535; D * N <= 2^32.
  * ------------------------------------------------------------------------- */
 int ssm_step(int B, int D, int N, int io,
              float* state, const void* x, const void* delta, const float* A,

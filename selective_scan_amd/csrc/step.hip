@@ -118,13 +118,17 @@ hipError_t launch_dtype(const StepArgs& a, hipStream_t st) {
         case 16: return launch_n<16, BF16>(a, st);
         case 32: return launch_n<32, BF16>(a, st);
         case 64: return launch_n<64, BF16>(a, st);
+        case 128: return launch_n<128, BF16>(a, st);
+        case 256: return launch_n<256, BF16>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-bool step_supported_n(int N) { return N == 4 || N == 8 || N == 16 || N == 32 || N == 64; }
+bool step_supported_n(int N) {
+    return N == 4 || N == 8 || N == 16 || N == 32 || N == 64 || N == 128 || N == 256;
+}
 
 hipError_t launch_step(const StepArgs& a, hipStream_t st) {
     return a.bf16 ? launch_dtype<true>(a, st) : launch_dtype<false>(a, st);

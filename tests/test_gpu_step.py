@@ -35,6 +35,7 @@ def _run_steps(w, steps):
     (1, 64, 16, si.BF16, True, True), (3, 100, 4, si.F32, False, False),
     (2, 1000, 8, si.BF16, True, False), (4, 300, 32, si.F32, False, True),
     (2, 130, 64, si.BF16, True, True), (1, 1, 16, si.F32, True, True),
+    (2, 70, 128, si.BF16, True, True), (3, 33, 256, si.F32, False, True),
 ], ids=lambda c: "B{}_D{}_N{}_{}_D{}z{}".format(*c))
 def test_step_small(case):
     B, D, N, dt, wd, wz = case
@@ -61,9 +62,10 @@ def test_step_equals_prefill_of_one_on_gpu():
     compare(st.cpu().numpy(), out_f64(hf), "f32", what="step vs L=1 state")
 
 
-def test_prefill_then_step_equals_longer_prefill_on_gpu():
+@pytest.mark.parametrize("N", [16, 256])
+def test_prefill_then_step_equals_longer_prefill_on_gpu(N):
     L = 777
-    w = si.scan_inputs(2, L + 1, 256, 16, dtype=si.BF16, seed=9, with_h0=True)
+    w = si.scan_inputs(2, L + 1, 256, N, dtype=si.BF16, seed=9, with_h0=True)
     yfull, hfull = gpu_scan(w)
     cut = {k: np.ascontiguousarray(w[k][:, :L]) for k in ("x", "delta", "z", "Bm", "Cm")}
     _, h = gpu_scan(dict(w, **cut))
