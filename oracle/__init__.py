@@ -14,6 +14,8 @@ storage) and returns float64 arrays. Shapes and meaning follow the C header:
 * ``ssd_unroll``  SSD by brute-force unrolling           -> (y, h_final)
 * ``step``        one decode step                        -> (y [B,D], new state [B,D,N])
 * ``ssd_step``    one SSD decode step                    -> (y [B,H,P], new state [B,H,N,P])
+* ``scan_bwd``    gradient of ``scan`` for the loss sum(dy*y) + sum(dh_final*h_final)
+                  -> dict of dx, ddelta, dA, dBm, dCm, dD, dz, dh0
 """
 import ctypes
 import os
@@ -52,7 +54,8 @@ class Oracle:
                            ("oracle_ssd_seq", sig_ssd), ("oracle_ssd_unroll", sig_ssd),
                            ("oracle_ssd_chunked", [i] * 6 + [d] * 10),
                            ("oracle_step", [i, i, i] + [d] * 9),
-                           ("oracle_ssd_step", [i, i, i, i] + [d] * 9)]:
+                           ("oracle_ssd_step", [i, i, i, i] + [d] * 9),
+                           ("oracle_scan_bwd", [i, i, i, i] + [d] * 18)]:
             fn = getattr(self.lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -92,6 +95,36 @@ class Oracle:
 
     def scan_unroll(self, *a, **k):
         return self._scan_like(self.lib.oracle_scan_unroll, *a, **k)
+
+    def scan_bwd(self, x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_final=None,
+                 want_dh0=True):
+        """Gradients of ``scan`` for l = sum(dy * y) + sum(dh_final * h_final).
+
+        Returns a dict with dx, ddelta [B,L,D], dA [D,N], dBm, dCm [B,L,N],
+        dD [D] (None without D), dz [B,L,D] (None without z), dh0 [B,D,N]
+        (None unless want_dh0)."""
+        x, delta, A, Bm, Cm, dy = map(_f64, (x, delta, A, Bm, Cm, dy))
+        D, z, h0, dhf = _f64(D), _f64(z), _f64(h0), _f64(dh_final)
+        Bb, L, Dd = x.shape
+        N = A.shape[1]
+        assert delta.shape == x.shape and dy.shape == x.shape and A.shape == (Dd, N)
+        assert Bm.shape == (Bb, L, N) and Cm.shape == (Bb, L, N)
+        assert D is None or D.shape == (Dd,)
+        assert z is None or z.shape == x.shape
+        assert h0 is None or h0.shape == (Bb, Dd, N)
+        assert dhf is None or dhf.shape == (Bb, Dd, N)
+        out = dict(dx=np.empty_like(x), ddelta=np.empty_like(x), dA=np.empty((Dd, N)),
+                   dBm=np.empty((Bb, L, N)), dCm=np.empty((Bb, L, N)),
+                   dD=None if D is None else np.empty(Dd),
+                   dz=None if z is None else np.empty_like(x),
+                   dh0=np.empty((Bb, Dd, N)) if want_dh0 else None)
+        rc = self.lib.oracle_scan_bwd(Bb, L, Dd, N, _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                      _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dhf),
+                                      *(_ptr(out[k]) for k in ("dx", "ddelta", "dA", "dBm", "dCm",
+                                                               "dD", "dz", "dh0")))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
 
     # -- SSD ---------------------------------------------------------------
     def _ssd_args(self, x, delta, A, Bm, Cm, D, z, h0):
@@ -175,6 +208,10 @@ def scan(*a, **k):
 
 def scan_unroll(*a, **k):
     return get().scan_unroll(*a, **k)
+
+
+def scan_bwd(*a, **k):
+    return get().scan_bwd(*a, **k)
 
 
 def ssd_seq(*a, **k):

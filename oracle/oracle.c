@@ -335,3 +335,125 @@ int oracle_ssd_unroll(int B, int L, int H, int P, int N,
         for (long k = 0; k < (long)B * H * NP; ++k) h_final[k] = h0 ? h0[k] : 0.0;
     return 0;
 }
+
+/* ------------------------------------------------------------- O6 -------
+ * Gradient of O1 for training (the training workloads of "Characterizing the
+ * Behavior of Training Mamba-based State Space Models on GPUs", abstract, and
+ * the training-step sweep of "Efficient Sequence Modeling: From S4 to
+ * Mamba-3", section 05 Evaluation). The pages do not write the backward pass
+ * out; it is the chain rule applied to O1, taken here in reverse mode.
+ *
+ * For the scalar loss l = sum(dy * y) + sum(dh_final * h_final), every output
+ * is the partial derivative of l with respect to the matching input. Per
+ * (b, d), with a_t[n] = exp(delta_t A[d,n]) and v_t = C_t . h_t + D x_t:
+ *   y_t = v_t silu(z_t)                => dv_t = dy_t silu(z_t),
+ *                                        dz_t = dy_t v_t silu'(z_t),
+ *                                        silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+ *   adjoint of the state, backwards:     g_t = dv_t C_t + a_{t+1} g_{t+1},
+ *                                        with a_L g_L taken as dh_final
+ *   h_t = a_t h_{t-1} + delta_t B_t x_t => dA[d,n]    += g_t[n] a_t[n] h_{t-1}[n] delta_t
+ *                                        ddelta_t    += g_t[n] (A[d,n] a_t[n] h_{t-1}[n] + B_t[n] x_t)
+ *                                        dx_t        += g_t[n] delta_t B_t[n]  (+ dv_t D)
+ *                                        dB_t[n]     += g_t[n] delta_t x_t     (summed over d)
+ *                                        dC_t[n]     += dv_t h_t[n]           (summed over d)
+ *                                        dD[d]       += dv_t x_t
+ *                                        dh0         =  a_0 g_0
+ * dDskip is written only when Dskip is given, dz only when z is given; dh0 may be
+ * NULL. dh_final NULL means zero. The states of each (b, d) are kept for the
+ * whole sequence (L + 1 rows of N), so this is for test sizes. */
+int oracle_scan_bwd(int B, int L, int D, int N,
+                    const double* x, const double* delta, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip,
+                    const double* z, const double* h0,
+                    const double* dy, const double* dh_final,
+                    double* dx, double* ddelta, double* dA, double* dBm, double* dCm,
+                    double* dDskip, double* dz, double* dh0) {
+    if (bad_dims(B, L, D, N)) return -1;
+    if ((long)B * L * D > 0 && (!x || !delta || !dy || !dx || !ddelta)) return -1;
+    if ((long)D * N > 0 && (!A || !dA)) return -1;
+    if ((long)B * L * N > 0 && (!Bm || !Cm || !dBm || !dCm)) return -1;
+    if ((Dskip && !dDskip) || (z && !dz)) return -1;
+    const long bln = (long)B * L * N;
+    const int nthr = oracle_get_threads();
+    /* per-thread sums of dB and dC: B and C are shared by every channel */
+    double* part = (double*)calloc((size_t)nthr * 2 * (bln > 0 ? bln : 1), sizeof(double));
+    if (!part) return -1;
+    for (long k = 0; k < (long)D * N; ++k) dA[k] = 0.0;
+    if (Dskip)
+        for (long d = 0; d < D; ++d) dDskip[d] = 0.0;
+#pragma omp parallel num_threads(nthr)
+    {
+#ifdef _OPENMP
+        const int tid = omp_get_thread_num();
+#else
+        const int tid = 0;
+#endif
+        double* pB = part + (size_t)tid * 2 * bln;
+        double* pC = pB + bln;
+        double* hs = (double*)malloc(sizeof(double) * ((size_t)(L + 1) * N + 1)); /* hs[t + 1] = h_t */
+        double* c = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));         /* a_{t+1} g_{t+1} */
+#pragma omp for schedule(static)
+        for (long d = 0; d < D; ++d) {
+            for (long b = 0; b < B; ++b) {
+                for (int n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+                for (long t = 0; t < L; ++t) {
+                    long i = (b * L + t) * D + d;
+                    const double* Bt = Bm + (b * L + t) * N;
+                    for (int n = 0; n < N; ++n)
+                        hs[(t + 1) * N + n] =
+                            exp(delta[i] * A[d * N + n]) * hs[t * N + n] + delta[i] * Bt[n] * x[i];
+                }
+                for (int n = 0; n < N; ++n) c[n] = dh_final ? dh_final[(b * D + d) * N + n] : 0.0;
+                for (long t = L - 1; t >= 0; --t) {
+                    long i = (b * L + t) * D + d;
+                    const double* Bt = Bm + (b * L + t) * N;
+                    const double* Ct = Cm + (b * L + t) * N;
+                    const double* hprev = hs + t * N;
+                    const double* hcur = hs + (t + 1) * N;
+                    double dt = delta[i], xv = x[i];
+                    double v = 0.0;
+                    for (int n = 0; n < N; ++n) v += Ct[n] * hcur[n];
+                    if (Dskip) v += Dskip[d] * xv;
+                    double dv = dy[i];
+                    if (z) {
+                        double s = 1.0 / (1.0 + exp(-z[i]));
+                        dz[i] = dy[i] * v * s * (1.0 + z[i] * (1.0 - s));
+                        dv = dy[i] * z[i] * s;
+                    }
+                    double gx = 0.0, gdt = 0.0;
+                    if (Dskip) {
+                        gx = dv * Dskip[d];
+                        dDskip[d] += dv * xv;
+                    }
+                    for (int n = 0; n < N; ++n) {
+                        double g = c[n] + dv * Ct[n];
+                        double abar = exp(dt * A[d * N + n]);
+                        pC[(b * L + t) * N + n] += dv * hcur[n];
+                        pB[(b * L + t) * N + n] += g * dt * xv;
+                        gx += g * dt * Bt[n];
+                        gdt += g * (A[d * N + n] * abar * hprev[n] + Bt[n] * xv);
+                        dA[d * N + n] += g * abar * hprev[n] * dt;
+                        c[n] = abar * g;
+                    }
+                    dx[i] = gx;
+                    ddelta[i] = gdt;
+                }
+                if (dh0)
+                    for (int n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = c[n];
+            }
+        }
+        free(hs);
+        free(c);
+    }
+    for (long k = 0; k < bln; ++k) {
+        double sb = 0.0, sc = 0.0;
+        for (int r = 0; r < nthr; ++r) {
+            sb += part[(size_t)r * 2 * bln + k];
+            sc += part[(size_t)r * 2 * bln + bln + k];
+        }
+        dBm[k] = sb;
+        dCm[k] = sc;
+    }
+    free(part);
+    return 0;
+}

@@ -72,6 +72,19 @@ int oracle_ssd_unroll(int B, int L, int H, int P, int N,
                       const double* Bm, const double* Cm, const double* Dskip,
                       const double* z, const double* h0, double* y, double* h_final);
 
+/* O6: gradient of O1 (training backward pass). For the loss
+ * l = sum(dy * y) + sum(dh_final * h_final) it writes dl/d(input) for every
+ * input: dx, ddelta, dz [B,L,D]; dA [D,N]; dBm, dCm [B,L,N]; dDskip [D];
+ * dh0 [B,D,N]. dy [B,L,D] is required; dh_final [B,D,N] may be NULL (zero).
+ * dDskip is written when Dskip is given, dz when z is given; dh0 may be NULL. */
+int oracle_scan_bwd(int B, int L, int D, int N,
+                    const double* x, const double* delta, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip,
+                    const double* z, const double* h0,
+                    const double* dy, const double* dh_final,
+                    double* dx, double* ddelta, double* dA, double* dBm, double* dCm,
+                    double* dDskip, double* dz, double* dh0);
+
 #ifdef __cplusplus
 }
 #endif

@@ -338,6 +338,106 @@ def pin_linearity(orc):
     assert np.array_equal(y2, 2 * y) and np.array_equal(h2, 2 * hf)
 
 
+# ------------------------------------------------------------- backward (O6)
+GRAD_OF = {"x": "dx", "delta": "ddelta", "A": "dA", "Bm": "dBm", "Cm": "dCm", "D": "dD", "z": "dz",
+           "h0": "dh0"}
+
+
+def _loss(orc, p, dy, dhf):
+    """l = sum(dy * y) + sum(dh_final * h_final), through the forward oracle O1."""
+    y, hf = orc.scan(**p)
+    return float(np.sum(dy * y) + np.sum(dhf * hf))
+
+
+def _cotangents(p, seed):
+    r = np.random.default_rng(seed)
+    return r.standard_normal(p["x"].shape), r.standard_normal(p["h0"].shape if p["h0"] is not None
+                                                              else (p["x"].shape[0], p["A"].shape[0],
+                                                                    p["A"].shape[1]))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient element equals the central difference of the loss computed by
+    the forward oracle (O(eps^2) truncation, ~1e-10 round-off at eps = 1e-6)."""
+    for (B, L, D, N), opts, seed in [((2, 6, 3, 4), {}, 81),
+                                     ((1, 5, 2, 3), dict(h0=False, Dskip=False, z=False), 82)]:
+        p = mamba1_problem(B, L, D, N, seed=seed, **opts)
+        dy, dhf = _cotangents(p, seed + 100)
+        g = orc.scan_bwd(dy=dy, dh_final=dhf, **p)
+        for name, gname in GRAD_OF.items():
+            if p.get(name) is None:
+                if gname in ("dD", "dz"):
+                    assert g[gname] is None
+                    continue
+                # no h0 means a zero initial state, whose gradient still exists
+                p = dict(p, h0=np.zeros((B, D, N)))
+            base = p[name]
+            fd = np.zeros_like(base)
+            for idx in np.ndindex(base.shape):
+                eps = 1e-6 * max(1.0, abs(base[idx]))
+                q = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in p.items()}
+                q[name][idx] = base[idx] + eps
+                lp = _loss(orc, q, dy, dhf)
+                q[name][idx] = base[idx] - eps
+                lm = _loss(orc, q, dy, dhf)
+                fd[idx] = (lp - lm) / (2 * eps)
+            close(g[gname], fd, tol=1e-6, what=f"finite differences {gname} {B, L, D, N} {opts}")
+
+
+def pin_bwd_directional_derivative(orc):
+    """<grad, v> equals the derivative of the loss along a random direction v over
+    all inputs at once, on a longer sequence with every optional part present."""
+    p = mamba1_problem(2, 37, 4, 5, seed=91)
+    dy, dhf = _cotangents(p, 191)
+    g = orc.scan_bwd(dy=dy, dh_final=dhf, **p)
+    r = np.random.default_rng(291)
+    v = {k: r.standard_normal(p[k].shape) for k in GRAD_OF}
+    v["delta"] *= 0.05  # keeps Delta positive along the path
+    lin = sum(float(np.sum(g[GRAD_OF[k]] * v[k])) for k in GRAD_OF)
+    eps = 1e-5
+    lp = _loss(orc, {k: (p[k] + eps * v[k] if k in v else p[k]) for k in p}, dy, dhf)
+    lm = _loss(orc, {k: (p[k] - eps * v[k] if k in v else p[k]) for k in p}, dy, dhf)
+    fd = (lp - lm) / (2 * eps)
+    assert abs(lin - fd) <= 1e-7 * max(1.0, abs(fd)), f"directional derivative {lin} vs {fd}"
+
+
+def pin_bwd_zero_decay_cumsum(orc):
+    """A = 0 and no gate: the state is h0 plus a running sum, so the adjoint is a
+    reverse running sum of dy C (+ dh_final); every gradient then has a closed form
+    in cumsums."""
+    p = mamba1_problem(2, 13, 3, 4, seed=101, z=False)
+    p["A"] = np.zeros_like(p["A"])
+    dy, dhf = _cotangents(p, 201)
+    g = orc.scan_bwd(dy=dy, dh_final=dhf, **p)
+    x, dl, Bm, Cm, h0, Dv = p["x"], p["delta"], p["Bm"], p["Cm"], p["h0"], p["D"]
+    u = dl * x                                                     # [B,L,D]
+    h = h0[:, None] + np.cumsum(u[..., None] * Bm[:, :, None, :], axis=1)   # h_t [B,L,D,N]
+    hprev = np.concatenate([h0[:, None], h[:, :-1]], axis=1)
+    adj = dy[..., None] * Cm[:, :, None, :]                       # dy_t C_t [B,L,D,N]
+    gt = np.flip(np.cumsum(np.flip(adj, 1), axis=1), 1) + dhf[:, None]      # g_t
+    close(g["dx"], dy * Dv + dl * np.einsum("bldn,bln->bld", gt, Bm), what="A=0 dx")
+    close(g["ddelta"], x * np.einsum("bldn,bln->bld", gt, Bm), what="A=0 ddelta")
+    close(g["dA"], np.einsum("bldn,bldn,bld->dn", gt, hprev, dl), what="A=0 dA")
+    close(g["dBm"], np.einsum("bldn,bld->bln", gt, u), what="A=0 dB")
+    close(g["dCm"], np.einsum("bld,bldn->bln", dy, h), what="A=0 dC")
+    close(g["dD"], np.einsum("bld,bld->d", dy, x), what="A=0 dD")
+    close(g["dh0"], gt[:, 0], what="A=0 dh0")
+
+
+def pin_bwd_linear_in_cotangents(orc):
+    """The gradients are linear in (dy, dh_final); dy = 0, dh_final = 0 gives zeros."""
+    p = mamba1_problem(1, 11, 3, 4, seed=111)
+    d1, h1 = _cotangents(p, 1)
+    d2, h2 = _cotangents(p, 2)
+    g1 = orc.scan_bwd(dy=d1, dh_final=h1, **p)
+    g2 = orc.scan_bwd(dy=d2, dh_final=h2, **p)
+    g3 = orc.scan_bwd(dy=2 * d1 - 3 * d2, dh_final=2 * h1 - 3 * h2, **p)
+    for k in g1:
+        close(g3[k], 2 * g1[k] - 3 * g2[k], what=f"linearity {k}")
+    g0 = orc.scan_bwd(dy=np.zeros_like(d1), dh_final=None, **p)
+    assert all(not np.any(v) for v in g0.values()), "zero cotangents give a nonzero gradient"
+
+
 ALL_PINS = [
     pin_chunked_equals_sequential,
     pin_constant_input_closed_form,
@@ -349,4 +449,8 @@ ALL_PINS = [
     pin_split_carry,
     pin_causality,
     pin_linearity,
+    pin_bwd_finite_differences,
+    pin_bwd_directional_derivative,
+    pin_bwd_zero_decay_cumsum,
+    pin_bwd_linear_in_cotangents,
 ]

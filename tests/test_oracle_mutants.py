@@ -35,6 +35,16 @@ MUTANTS = {
     "step_no_decay": ("h[n] = exp(dt * A[d * N + n]) * h[n] + dt * Bm[b * N + n] * xv;", "h[n] = h[n] + dt * Bm[b * N + n] * xv;"),
     "ssd_step_no_delta": ("S[n * P + p] = abar * S[n * P + p] + dt * Bm[b * N + n] * xt[p];", "S[n * P + p] = abar * S[n * P + p] + Bm[b * N + n] * xt[p];"),
     "hfinal_not_written": ("h_final[(b * D + d) * N + n] = h[n];", "h_final[(b * D + d) * N + n] = 0.0;"),
+    "bwd_adjoint_no_decay": ("c[n] = abar * g;", "c[n] = g;"),
+    "bwd_dA_uses_current_state": ("dA[d * N + n] += g * abar * hprev[n] * dt;", "dA[d * N + n] += g * abar * hcur[n] * dt;"),
+    "bwd_ddelta_drops_input_term": ("gdt += g * (A[d * N + n] * abar * hprev[n] + Bt[n] * xv);",
+                                    "gdt += g * (A[d * N + n] * abar * hprev[n]);"),
+    "bwd_dz_drops_sigmoid_slope": ("dz[i] = dy[i] * v * s * (1.0 + z[i] * (1.0 - s));", "dz[i] = dy[i] * v * s;"),
+    "bwd_dB_drops_delta": ("pB[(b * L + t) * N + n] += g * dt * xv;", "pB[(b * L + t) * N + n] += g * xv;"),
+    "bwd_dC_uses_adjoint": ("pC[(b * L + t) * N + n] += dv * hcur[n];", "pC[(b * L + t) * N + n] += g * hcur[n];"),
+    "bwd_skip_gradient_ungated": ("gx = dv * Dskip[d];", "gx = dy[i] * Dskip[d];"),
+    "bwd_adjoint_ignores_dh_final": ("c[n] = dh_final ? dh_final[(b * D + d) * N + n] : 0.0;", "c[n] = 0.0;"),
+    "bwd_dx_uses_C": ("gx += g * dt * Bt[n];", "gx += g * dt * Ct[n];"),
 }
 
 
