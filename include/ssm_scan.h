@@ -1,8 +1,9 @@
 /*
  * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
  *
- * Four entry points, each a hand-written HIP kernel pipeline for CDNA4:
+ * Five entry points, each a hand-written HIP kernel pipeline for CDNA4:
  *   ssm_scan_fwd   Mamba-1 selective scan over a whole sequence (prefill)
+ *   ssm_scan_bwd   its gradient (training backward pass)
  *   ssm_ssd_fwd    Mamba-2 SSD: scalar decay per head, chunked decayed-attention form
  *   ssm_step       one-token recurrent decode step, state updated in place
  *   ssm_ssd_step   the same for the Mamba-2 form (scalar decay per head, (N, P) state)
@@ -108,6 +109,47 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
                  const void* Bm, const void* Cm, const float* Dskip,
                  const void* z, const float* h0,
                  void* y, float* h_final,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_scan_bwd -- gradient of ssm_scan_fwd (training backward pass).
+ *
+ * Training Mamba models on GPUs is the workload of "Characterizing the Behavior
+ * of Training Mamba-based State Space Models on GPUs" (abstract) and of the
+ * training-step sweep in "Efficient Sequence Modeling: From S4 to Mamba-3",
+ * section 05 Evaluation. The pages do not write the backward pass out: this is
+ * the exact gradient of the forward recurrence above, by the chain rule. For
+ * the loss  l = sum(dy * y) + sum(dh_final * h_final)  every output is dl/d(the
+ * input of the same name):
+ *
+ *   inputs  : x, delta, A, Bm, Cm, Dskip, z, h0 exactly as given to ssm_scan_fwd
+ *   dy      : [B, L, D]  io dtype, gradient of y (required)
+ *   dh_final: [B, D, N]  fp32 gradient of h_final, or NULL (zero)
+ *   dx, ddelta : [B, L, D] io dtype out
+ *   dA      : [D, N]     fp32 out (summed over batch and time)
+ *   dBm, dCm: [B, L, N]  io dtype out (summed over channels in fp32, then rounded)
+ *   dDskip  : [D]        fp32 out; given exactly when Dskip is given
+ *   dz      : [B, L, D]  io dtype out; given exactly when z is given
+ *   dh0     : [B, D, N]  fp32 out, or NULL (not written); the gradient of the
+ *                        initial state, also when h0 is NULL (zero state)
+ *   workspace: device scratch of at least ssm_scan_bwd_workspace_size(B, L, D, N)
+ *              bytes (0 only when L = 0); contents on entry are ignored.
+ * The forward states are recomputed, not read from a forward call. Outputs must
+ * not alias inputs or each other. Arithmetic is fp32 with fp32 accumulation;
+ * reductions run in a fixed order (no atomics), so results are deterministic.
+ * Supported: N in {4, 8, 16}; B <= 65535; L >= 0 (L = 0 writes dh0 = dh_final,
+ * dA = 0, dDskip = 0). Every pointer must be 16-byte aligned. Errors as for
+ * ssm_scan_fwd.
+ * ------------------------------------------------------------------------- */
+size_t ssm_scan_bwd_workspace_size(int B, int L, int D, int N);
+
+int ssm_scan_bwd(int B, int L, int D, int N, int io,
+                 const void* x, const void* delta, const float* A,
+                 const void* Bm, const void* Cm, const float* Dskip,
+                 const void* z, const float* h0,
+                 const void* dy, const float* dh_final,
+                 void* dx, void* ddelta, float* dA, void* dBm, void* dCm,
+                 float* dDskip, void* dz, float* dh0,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

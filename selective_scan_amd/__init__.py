@@ -11,6 +11,8 @@ module raises.
 from .ops import (  # noqa: F401
     SsmError,
     lib,
+    ssm_scan_bwd,
+    ssm_scan_bwd_workspace_size,
     ssm_scan_fwd,
     ssm_scan_workspace_size,
     ssm_ssd_fwd,

@@ -126,6 +126,51 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
     return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+// ------------------------------------------------------------------ scan backward
+size_t ssm_scan_bwd_workspace_size(int B, int L, int D, int N) {
+    if (B < 1 || L < 0 || D < 1 || !ssm::scan_bwd_supported_n(N)) return 0;
+    if (!product_ok({B, L, D, N})) return 0;
+    return ssm::scan_bwd_workspace_bytes(B, L, D, N);
+}
+
+int ssm_scan_bwd(int B, int L, int D, int N, int io,
+                 const void* x, const void* delta, const float* A,
+                 const void* Bm, const void* Cm, const float* Dskip,
+                 const void* z, const float* h0,
+                 const void* dy, const float* dh_final,
+                 void* dx, void* ddelta, float* dA, void* dBm, void* dCm,
+                 float* dDskip, void* dz, float* dh0,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssm_scan_bwd";
+    if (B < 1 || D < 1 || L < 0 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1 and L >= 0");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (!ssm::scan_bwd_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16");
+    if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
+    if (!product_ok({B, L, D, N}, 1LL << 40) || !product_ok({B, L, D}, 1LL << 40))
+        return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if (!A || !dA) return fail(SSM_ERR_INVALID_ARG, fn, "A and dA are required");
+    if (L > 0 && (!x || !delta || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm))
+        return fail(SSM_ERR_INVALID_ARG, fn, "x, delta, Bm, Cm, dy, dx, ddelta, dBm and dCm are required");
+    if ((Dskip == nullptr) != (dDskip == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, fn, "dDskip must be given exactly when Dskip is");
+    if ((z == nullptr) != (dz == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, fn, "dz must be given exactly when z is");
+    const void* ptrs[] = {x, delta, A, Bm, Cm, Dskip, z, h0, dy, dh_final, dx, ddelta,
+                          dA, dBm, dCm, dDskip, dz, dh0, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    const int es = io == SSM_BF16 ? 2 : 4;
+    const long long Ls = ssm::scan_bwd_segment_len(B, L, D, N);
+    if (Ls * D * es >= (1LL << 31) || Ls * N * 4 >= (1LL << 31))
+        return fail(SSM_ERR_UNSUPPORTED, fn, "one segment of [L, D] exceeds 2 GiB");
+    const size_t need = ssm::scan_bwd_workspace_bytes(B, L, D, N);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, fn, "workspace missing or smaller than ssm_scan_bwd_workspace_size()");
+    ssm::BwdArgs a{B, L, D, N, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, dy, dh_final,
+                   dx, ddelta, dA, dBm, dCm, dDskip, dz, dh0, workspace};
+    return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 // ------------------------------------------------------------------ SSD
 size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk) {
     const int Q = chunk == 0 ? 256 : chunk;

@@ -76,4 +76,35 @@ __device__ __forceinline__ void load_uniform_row(const void* __restrict__ base, 
     }
 }
 
+// Uniform rows of B or C for one time step, kept packed until use.
+template <int N, bool BF16>
+struct Row {
+    static constexpr int K = BF16 ? N / 2 : N;
+    uint32_t v[K];
+    // row `row` of a matrix whose rows are `rw` 32-bit words apart
+    __device__ __forceinline__ void load(const void* base, long row, int rw) {
+        cu32* p = (cu32*)(base) + row * rw;
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = p[k];
+    }
+    __device__ __forceinline__ float at(int n) const {
+        if constexpr (BF16) return (n & 1) ? bf16_hi(v[n >> 1]) : bf16_lo(v[n >> 1]);
+        else return __uint_as_float(v[n]);
+    }
+};
+
+// Raw element of an io tensor (bf16 bits or fp32 bits); widened only at use, so a
+// prefetched load is not waited for until the step that consumes it.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_raw(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (BF16) return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float widen(uint32_t v) {
+    if constexpr (BF16) return __uint_as_float(v << 16);
+    else return __uint_as_float(v);
+}
+
 }  // namespace ssm

@@ -53,6 +53,36 @@ ScanPlan scan_plan(int B, int L, int D, int N);
 size_t scan_workspace_bytes(int B, int L, int D, int N);
 hipError_t launch_scan_fwd(const ScanArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------ Mamba-1 scan, backward
+struct BwdArgs {
+    int B, L, D, N;
+    bool bf16;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    const float* h0;
+    const void* dy;
+    const float* dh_final;
+    void* dx;
+    void* ddelta;
+    float* dA;
+    void* dBm;
+    void* dCm;
+    float* dDskip;
+    void* dz;
+    float* dh0;
+    void* ws;
+};
+
+bool scan_bwd_supported_n(int N);
+int scan_bwd_segment_len(int B, int L, int D, int N);
+size_t scan_bwd_workspace_bytes(int B, int L, int D, int N);
+hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t stream);
+
 // ------------------------------------------------------------ decode step
 struct StepArgs {
     int B, D, N;

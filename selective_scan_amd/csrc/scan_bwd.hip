@@ -1,0 +1,850 @@
+// Backward (training) pass of the Mamba-1 selective scan on gfx950: the exact
+// gradient of y_t = (C_t . h_t + D x_t) silu(z_t), h_t = exp(Delta_t A) h_{t-1} +
+// Delta_t B_t x_t (Gu & Dao 2023) for the loss sum(dy y) + sum(dh_final h_final).
+// Training these models on GPUs is the workload of "Characterizing the Behavior
+// of Training Mamba-based State Space Models on GPUs" (abstract) and the
+// training-step sweep of "Efficient Sequence Modeling: From S4 to Mamba-3"
+// (section 05 Evaluation); the pages do not write the backward pass out, so it
+// is the chain rule applied to the forward recurrence, in reverse mode:
+//   adjoint  g_t = dv_t C_t + a_{t+1} g_{t+1}   (a_t = exp(Delta_t A), a_L g_L = dh_final)
+//   dv_t = dy_t silu(z_t);  dz_t = dy_t v_t silu'(z_t)
+//   dA      += g_t a_t h_{t-1} Delta_t          ddelta_t = sum_n g_t (A a_t h_{t-1} + B_t x_t)
+//   dx_t     = Delta_t sum_n g_t B_t + dv_t D   dB_t = sum_d g_t Delta_t x_t
+//   dC_t     = sum_d dv_t h_t                   dD = sum dv_t x_t;  dh0 = a_0 g_0
+//
+// Work mapping (as in the forward pass): one lane owns one (batch, channel) and
+// its N states; B_t and C_t are wave-uniform rows in SGPRs. The sequence is cut
+// into segments (one wave each, W waves per workgroup), and both recurrences are
+// affine maps of their state, so segments compose:
+//   1. bwd_state_aggregate: each segment from a zero state; in-group prefixes in
+//      LDS (forward carries, as in the forward pass), plus the zero-start state
+//      and the partial sum of Delta at every sub-block boundary (checkpoints).
+//   2. carry_forward: the state entering each group.
+//   3. bwd_adjoint_aggregate: each segment's adjoint from a zero start at its
+//      right end, in-group suffixes in LDS, group aggregates.
+//   4. carry_backward: the adjoint entering each group from the right.
+//   5. bwd_final: per segment, sub-blocks of K steps from the last to the first.
+//      A sub-block's entering state is rebuilt from its checkpoint and the
+//      segment's carried-in state, the K states are recomputed forwards and kept
+//      in VGPRs (K*N of them), then the adjoint walks the K steps backwards. The
+//      per-step sums over channels (dB, dC) are reduced across the 64 lanes by a
+//      transpose-reduce (permlane swaps and DPP, no LDS) and stored as fp32
+//      partials per 64-channel block; dA and dD are summed per workgroup.
+//   6. bwd_reduce_params / bwd_reduce_rows: add the partials, round dB and dC to
+//      the io type.
+#include "common.h"
+#include "launch.h"
+
+#include <algorithm>
+
+namespace ssm {
+namespace {
+
+#ifndef SSM_BWD_TARGET_WAVES
+#define SSM_BWD_TARGET_WAVES 4096
+#endif
+constexpr int kBwdTargetWaves = SSM_BWD_TARGET_WAVES;  // waves the final pass aims for
+constexpr int kBwdMinSegment = 32;
+constexpr int kBwdMaxGroup = 4;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Steps per sub-block: the final pass keeps K x N recomputed states per lane, and
+// the four per-step input streams of a sub-block, so K stays small.
+__host__ __device__ constexpr int sub_len(int N) { return N > 0 ? 4 : 4; }
+
+struct BGeom {
+    int Ls;    // steps per segment (a multiple of K)
+    int S;     // segments per chain
+    int W;     // segments (waves) per workgroup
+    int G;     // groups per chain
+    int K;     // steps per sub-block
+    int nsub;  // sub-blocks per full segment
+};
+
+BGeom bgeom(int B, int L, int D, int N) {
+    BGeom g{0, 0, 1, 0, sub_len(N), 0};
+    if (L <= 0) return g;
+    const long chains = (long)B * ((D + 63) / 64);
+    const long s_target = (kBwdTargetWaves + chains - 1) / chains;
+    long Ls = std::max<long>(kBwdMinSegment, (L + s_target - 1) / s_target);
+    Ls = (Ls + g.K - 1) / g.K * g.K;
+    Ls = std::min<long>(Ls, ((long)L + g.K - 1) / g.K * g.K);
+    g.Ls = (int)Ls;
+    g.S = (int)((L + Ls - 1) / Ls);
+    g.W = std::min(kBwdMaxGroup, g.S);
+    g.G = (g.S + g.W - 1) / g.W;
+    g.nsub = g.Ls / g.K;
+    return g;
+}
+
+// workspace layout (floats), channel index fastest:
+//   E   [B][S][N][D]   forward: exclusive in-group prefix state of each segment
+//   CS  [B][S][D]      forward: in-group prefix of sum(Delta) before each segment
+//   GH  [B][G-1][N][D] forward: aggregate of groups 0..G-2, then the state entering groups 1..G-1
+//   GP  [B][G-1][N][D] forward: decay of groups 0..G-2
+//   EB  [B][S][N][D]   adjoint: exclusive in-group suffix of each segment
+//   CSB [B][S][D]      in-group suffix of sum(Delta) after each segment
+//   GHB [B][G-1][N][D] adjoint: aggregate of groups 1..G-1, then the adjoint entering groups 0..G-2
+//   GPB [B][G-1][N][D] decay of groups 1..G-1
+//   HZ  [B][S][nsub-1][N][D] zero-start state at sub-block boundaries 1..nsub-1 of each segment
+//   CZ  [B][S][nsub-1][D]    sum(Delta) from the segment start to those boundaries
+//   PA  [B][G][N][D]   dA summed over one group's segments
+//   PD  [B][G][D]      dD summed over one group's segments
+//   PB  [ceil(D/64)][B][L][N]  dB summed over one 64-channel block
+//   PC  [ceil(D/64)][B][L][N]  dC summed over one 64-channel block
+struct BwsLayout {
+    size_t E, CS, GH, GP, EB, CSB, GHB, GPB, HZ, CZ, PA, PD, PB, PC, total;
+};
+
+__host__ __device__ inline BwsLayout bws_layout(int B, int L, int D, int N, const BGeom& g) {
+    const size_t g1 = g.G > 1 ? (size_t)(g.G - 1) : 0;
+    const size_t c1 = g.nsub > 1 ? (size_t)(g.nsub - 1) : 0;
+    const size_t nd = (size_t)(D + 63) / 64;
+    const size_t st = (size_t)N * D;
+    BwsLayout w;
+    size_t o = 0;
+    w.E = o;   o += (size_t)B * g.S * st;
+    w.CS = o;  o += (size_t)B * g.S * D;
+    w.GH = o;  o += (size_t)B * g1 * st;
+    w.GP = o;  o += (size_t)B * g1 * st;
+    w.EB = o;  o += (size_t)B * g.S * st;
+    w.CSB = o; o += (size_t)B * g.S * D;
+    w.GHB = o; o += (size_t)B * g1 * st;
+    w.GPB = o; o += (size_t)B * g1 * st;
+    w.HZ = o;  o += (size_t)B * g.S * c1 * st;
+    w.CZ = o;  o += (size_t)B * g.S * c1 * D;
+    w.PA = o;  o += (size_t)B * g.G * st;
+    w.PD = o;  o += (size_t)B * g.G * D;
+    w.PB = o;  o += nd * B * L * N;
+    w.PC = o;  o += nd * B * L * N;
+    w.total = o;
+    return w;
+}
+
+// ----------------------------------------------------------- lane reduction
+// DPP row patterns used as partner maps within a 16-lane row.
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15 - i   (i ^ 15)
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7 - i within 8 (i ^ 7)
+constexpr int kDppXor2 = 0x4e;            // quad_perm [2,3,0,1]   (i ^ 2)
+constexpr int kDppXor1 = 0xb1;            // quad_perm [1,0,3,2]   (i ^ 1)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// One halving level of the transpose-reduce with partner lane = lane ^ mask:
+// lanes whose test bit is 0 keep values [0, M/2), the others [M/2, M), each
+// adding the partner's copy of the values it keeps.
+template <int M, int LEVEL>
+__device__ __forceinline__ void halve(float (&w)[16], int lane) {
+    constexpr int H = M / 2;
+    if constexpr (LEVEL == 0 || LEVEL == 1) {
+        // bits 5 and 4: the permlane swaps exchange the two halves in place
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const uint32_t lo = __float_as_uint(w[k]), hi = __float_as_uint(w[k + H]);
+            if constexpr (LEVEL == 0) {
+                const auto r = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+                w[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            } else {
+                const auto r = __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+                w[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            }
+        }
+    } else {
+        constexpr int bit = LEVEL == 2 ? 3 : (LEVEL == 3 ? 2 : (LEVEL == 4 ? 1 : 0));
+        constexpr int ctrl = LEVEL == 2 ? kDppRowMirror : (LEVEL == 3 ? kDppRowHalfMirror
+                                                                       : (LEVEL == 4 ? kDppXor2 : kDppXor1));
+        const bool hi = (lane >> bit) & 1;
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const float keep = hi ? w[k + H] : w[k];
+            const float send = hi ? w[k] : w[k + H];
+            w[k] = keep + dpp<ctrl>(send);
+        }
+    }
+}
+
+template <int LEVEL>
+__device__ __forceinline__ float fold(float v) {
+    constexpr int ctrl = LEVEL == 2 ? kDppRowMirror : (LEVEL == 3 ? kDppRowHalfMirror
+                                                                   : (LEVEL == 4 ? kDppXor2 : kDppXor1));
+    return v + dpp<ctrl>(v);
+}
+
+// Sums w[0..N) over the 64 lanes of the wave. Afterwards lane l holds the total
+// of value index reduced_index<N>(l); the partner masks 32, 16, 15, 7, 2, 1 span
+// all six lane bits, so every total covers every lane.
+template <int N>
+__device__ __forceinline__ float lane_reduce(float (&w)[16], int lane) {
+    static_assert(N == 4 || N == 8 || N == 16, "lane_reduce handles N = 4, 8, 16");
+    halve<N, 0>(w, lane);
+    halve<N / 2, 1>(w, lane);
+    float v;
+    if constexpr (N == 16) {
+        halve<4, 2>(w, lane);
+        halve<2, 3>(w, lane);
+        v = fold<5>(fold<4>(w[0]));
+    } else if constexpr (N == 8) {
+        halve<2, 2>(w, lane);
+        v = fold<5>(fold<4>(fold<3>(w[0])));
+    } else {
+        v = fold<5>(fold<4>(fold<3>(fold<2>(w[0]))));
+    }
+    return v;
+}
+
+// Value index held by lane l after lane_reduce<N>: the test bits 5, 4, 3, 2 (as
+// many as halving levels), most significant first.
+template <int N>
+__device__ __forceinline__ int reduced_index(int lane) {
+    const int b5 = (lane >> 5) & 1, b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+    if constexpr (N == 16) return 8 * b5 + 4 * b4 + 2 * b3 + b2;
+    else if constexpr (N == 8) return 4 * b5 + 2 * b4 + b3;
+    else return 2 * b5 + b4;
+}
+
+// Lanes that store a reduced total: one per value index.
+template <int N>
+__device__ __forceinline__ bool reduced_owner(int lane) {
+    constexpr int free_bits = N == 16 ? 3 : (N == 8 ? 7 : 15);
+    return (lane & free_bits) == 0;
+}
+
+// ----------------------------------------------------------- per-segment view
+// Buffer views of one segment's rows [t0, t0 + len) of a [B][L][D] io tensor:
+// reads past len return 0 and writes past it are dropped.
+template <bool BF16>
+struct SegIO {
+    static constexpr uint32_t es = BF16 ? 2 : 4;
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ void init(const void* base, size_t row0, int len, int D) {
+        r = make_rsrc(static_cast<const char*>(base) + row0 * D * es, (uint32_t)len * (uint32_t)D * es);
+    }
+};
+
+struct SegCtx {
+    int b, s, t0, len, d, dc;
+    size_t row0;
+    uint32_t voff, rstride;
+};
+
+// ------------------------------------------------ 1. forward aggregate + checkpoints
+template <int N, bool BF16>
+__global__ void __launch_bounds__(64 * kBwdMaxGroup)
+bwd_state_aggregate(BwdArgs a, BGeom g) {
+    extern __shared__ float lds[];
+    constexpr int K = sub_len(N);
+    constexpr uint32_t es = BF16 ? 2 : 4;
+    const int W = g.W;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
+    const int d = blockIdx.y * 64 + lane, dc = d < D ? d : D - 1;
+    const int s = grp * W + wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
+    const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
+    float* ws = static_cast<float*>(a.ws);
+    const size_t c1 = g.nsub > 1 ? (size_t)(g.nsub - 1) : 0;
+
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+        h[n] = 0.0f;
+    }
+    float sumd = 0.0f;
+    if (len > 0) {
+        const size_t row0 = (size_t)b * a.L + t0;
+        SegIO<BF16> X, Dl;
+        X.init(a.x, row0, len, D);
+        Dl.init(a.delta, row0, len, D);
+        const uint32_t voff = (uint32_t)dc * es, rstride = (uint32_t)D * es;
+        const void* Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
+        constexpr int rw = BF16 ? N / 2 : N;
+        const int nsub = (len + K - 1) / K;
+        uint32_t dq[K], xq[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            dq[k] = load_raw<BF16>(Dl.r, voff, (uint32_t)k * rstride);
+            xq[k] = load_raw<BF16>(X.r, voff, (uint32_t)k * rstride);
+        }
+        Row<N, BF16> Bn;
+        Bn.load(Bbase, 0, rw);
+        for (int j = 0; j < nsub; ++j) {
+            float dv[K], xv[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                dv[k] = widen<BF16>(dq[k]);
+                xv[k] = widen<BF16>(xq[k]);
+            }
+            if (j + 1 < nsub) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const uint32_t so = (uint32_t)((j + 1) * K + k) * rstride;
+                    dq[k] = load_raw<BF16>(Dl.r, voff, so);
+                    xq[k] = load_raw<BF16>(X.r, voff, so);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const Row<N, BF16> Bt = Bn;
+                Bn.load(Bbase, min(j * K + k + 1, len - 1), rw);
+                const float u = dv[k] * xv[k];
+                sumd += dv[k];
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    h[n] = __builtin_fmaf(exp2_fast(dv[k] * A2[n]), h[n], u * Bt.at(n));
+            }
+            if (j + 1 < nsub && d < D) {
+                float* hz = ws + wl.HZ + (((size_t)b * g.S + s) * c1 + j) * N * D + d;
+#pragma unroll
+                for (int n = 0; n < N; ++n) hz[(size_t)n * D] = h[n];
+                ws[wl.CZ + (((size_t)b * g.S + s) * c1 + j) * D + d] = sumd;
+            }
+        }
+    }
+    if (g.S == 1) return;  // one segment: no carries
+    // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]; a segment past L is the identity (1, 0)
+    float* sP = lds;
+    float* sH = sP + W * N * 64;
+    float* sS = sH + W * N * 64;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        sP[(wave * N + n) * 64 + lane] = exp2_fast(A2[n] * sumd);
+        sH[(wave * N + n) * 64 + lane] = h[n];
+    }
+    sS[wave * 64 + lane] = sumd;
+    __syncthreads();
+    float E[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) E[n] = 0.0f;
+    float cs = 0.0f;
+    for (int j = 0; j < wave; ++j) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            E[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], E[n], sH[(j * N + n) * 64 + lane]);
+        cs += sS[j * 64 + lane];
+    }
+    if (d >= D || s >= g.S) return;
+    float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + d;
+#pragma unroll
+    for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
+    ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+    const bool last_in_group = (wave == W - 1) || (s == g.S - 1);
+    if (last_in_group && grp < g.G - 1) {
+        float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + grp) * N * D + d;
+        float* GP = ws + wl.GP + ((size_t)b * (g.G - 1) + grp) * N * D + d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            GH[(size_t)n * D] = __builtin_fmaf(sP[(wave * N + n) * 64 + lane], E[n], h[n]);
+            GP[(size_t)n * D] = exp2_fast(A2[n] * (cs + sumd));
+        }
+    }
+}
+
+// ------------------------------------------------------------ 3. adjoint aggregate
+template <int N, bool BF16, bool HAS_Z>
+__global__ void __launch_bounds__(64 * kBwdMaxGroup)
+bwd_adjoint_aggregate(BwdArgs a, BGeom g) {
+    extern __shared__ float lds[];
+    constexpr int K = sub_len(N);
+    constexpr uint32_t es = BF16 ? 2 : 4;
+    const int W = g.W;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
+    const int d = blockIdx.y * 64 + lane, dc = d < D ? d : D - 1;
+    const int s = grp * W + wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
+    const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
+    float* ws = static_cast<float*>(a.ws);
+
+    float A2[N], c[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+        c[n] = 0.0f;
+    }
+    float sumd = 0.0f;
+    if (len > 0) {
+        const size_t row0 = (size_t)b * a.L + t0;
+        SegIO<BF16> Dl, DY, Z;
+        Dl.init(a.delta, row0, len, D);
+        DY.init(a.dy, row0, len, D);
+        Z.init(HAS_Z ? a.z : a.dy, row0, len, D);
+        const uint32_t voff = (uint32_t)dc * es, rstride = (uint32_t)D * es;
+        const void* Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
+        constexpr int rw = BF16 ? N / 2 : N;
+        const int nsub = (len + K - 1) / K;
+        uint32_t dq[K], gq[K], zq[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t so = (uint32_t)((nsub - 1) * K + k) * rstride;
+            dq[k] = load_raw<BF16>(Dl.r, voff, so);
+            gq[k] = load_raw<BF16>(DY.r, voff, so);
+            zq[k] = HAS_Z ? load_raw<BF16>(Z.r, voff, so) : 0u;
+        }
+        Row<N, BF16> Cn;
+        Cn.load(Cbase, min(nsub * K - 1, len - 1), rw);
+        for (int j = nsub - 1; j >= 0; --j) {
+            float dl[K], dv[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                dl[k] = widen<BF16>(dq[k]);
+                dv[k] = widen<BF16>(gq[k]);
+                if constexpr (HAS_Z) dv[k] *= silu(widen<BF16>(zq[k]));
+            }
+            if (j > 0) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const uint32_t so = (uint32_t)((j - 1) * K + k) * rstride;
+                    dq[k] = load_raw<BF16>(Dl.r, voff, so);
+                    gq[k] = load_raw<BF16>(DY.r, voff, so);
+                    if constexpr (HAS_Z) zq[k] = load_raw<BF16>(Z.r, voff, so);
+                }
+            }
+#pragma unroll
+            for (int k = K - 1; k >= 0; --k) {
+                const int t = j * K + k;
+                const Row<N, BF16> Ct = Cn;
+                Cn.load(Cbase, max(min(t - 1, len - 1), 0), rw);
+                sumd += dl[k];
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float gg = __builtin_fmaf(dv[k], Ct.at(n), c[n]);
+                    c[n] = exp2_fast(dl[k] * A2[n]) * gg;
+                }
+            }
+        }
+    }
+    // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]
+    float* sP = lds;
+    float* sH = sP + W * N * 64;
+    float* sS = sH + W * N * 64;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        sP[(wave * N + n) * 64 + lane] = exp2_fast(A2[n] * sumd);
+        sH[(wave * N + n) * 64 + lane] = c[n];
+    }
+    sS[wave * 64 + lane] = sumd;
+    __syncthreads();
+    // adjoint entering this segment from the segments to its right in the group
+    float Eb[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) Eb[n] = 0.0f;
+    float csb = 0.0f;
+    for (int j = W - 1; j > wave; --j) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            Eb[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], Eb[n], sH[(j * N + n) * 64 + lane]);
+        csb += sS[j * 64 + lane];
+    }
+    if (d >= D || s >= g.S) return;
+    float* Ep = ws + wl.EB + ((size_t)b * g.S + s) * N * D + d;
+#pragma unroll
+    for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = Eb[n];
+    ws[wl.CSB + ((size_t)b * g.S + s) * D + d] = csb;
+    if (wave == 0 && grp > 0) {  // the group's own aggregate, passed to the groups on its left
+        float* GH = ws + wl.GHB + ((size_t)b * (g.G - 1) + grp - 1) * N * D + d;
+        float* GP = ws + wl.GPB + ((size_t)b * (g.G - 1) + grp - 1) * N * D + d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            GH[(size_t)n * D] = __builtin_fmaf(sP[n * 64 + lane], Eb[n], c[n]);
+            GP[(size_t)n * D] = exp2_fast(A2[n] * (csb + sumd));
+        }
+    }
+}
+
+// ------------------------------------------------------------ 2. and 4. carries
+// Forward: carry(0) = h0, carry(g+1) = GP_g carry(g) + GH_g, written over GH_g.
+// Backward: carry(G-1) = dh_final, carry(g-1) = GPB_{g-1} carry(g) + GHB_{g-1},
+// written over GHB_{g-1}. One thread per (batch, state index, channel).
+template <bool REV>
+__global__ void __launch_bounds__(256)
+bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ dec, int B, int D, int N,
+          int G) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)B * N * D) return;
+    const int d = (int)(idx % D);
+    const int n = (int)((idx / D) % N);
+    const int b = (int)(idx / ((size_t)D * N));
+    const size_t st = (size_t)N * D;
+    float* H = agg + (size_t)b * (G - 1) * st + (size_t)n * D + d;
+    const float* P = dec + (size_t)b * (G - 1) * st + (size_t)n * D + d;
+    float h = init ? init[((size_t)b * D + d) * N + n] : 0.0f;
+    for (int k = 0; k < G - 1; ++k) {
+        const int kk = REV ? G - 2 - k : k;
+        h = __builtin_fmaf(P[kk * st], h, H[kk * st]);
+        H[kk * st] = h;
+    }
+}
+
+// ------------------------------------------------------------ 5. final pass
+template <int N, bool BF16, bool HAS_Z, bool HAS_D>
+__global__ void __launch_bounds__(64 * kBwdMaxGroup)
+bwd_final(BwdArgs a, BGeom g) {
+    extern __shared__ float lds[];
+    constexpr int K = sub_len(N);
+    constexpr uint32_t es = BF16 ? 2 : 4;
+    constexpr int rw = BF16 ? N / 2 : N;
+    const int W = g.W;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
+    const int dblk = blockIdx.y;
+    const int d = dblk * 64 + lane, dc = d < D ? d : D - 1;
+    const int s = grp * W + wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
+    const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
+    const float* ws = static_cast<const float*>(a.ws);
+    const size_t c1 = g.nsub > 1 ? (size_t)(g.nsub - 1) : 0;
+
+    float A2[N], dA[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+        dA[n] = 0.0f;
+    }
+    float dD = 0.0f;
+    if (len > 0) {
+        const size_t row0 = (size_t)b * a.L + t0;
+        // state entering the segment: group carry, then the in-group prefix
+        float hin[N], c[N];
+        {
+            float hg[N], E[N];
+            float cs = 0.0f;
+            if (grp > 0) {
+                const float* p = ws + wl.GH + ((size_t)b * (g.G - 1) + grp - 1) * N * D + dc;
+#pragma unroll
+                for (int n = 0; n < N; ++n) hg[n] = p[(size_t)n * D];
+            } else if (a.h0 != nullptr) {
+                const float* p = a.h0 + ((size_t)b * D + dc) * N;
+#pragma unroll
+                for (int n = 0; n < N; ++n) hg[n] = p[n];
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) hg[n] = 0.0f;
+            }
+            if (g.S > 1) {
+                cs = ws[wl.CS + ((size_t)b * g.S + s) * D + dc];
+                const float* p = ws + wl.E + ((size_t)b * g.S + s) * N * D + dc;
+#pragma unroll
+                for (int n = 0; n < N; ++n) E[n] = p[(size_t)n * D];
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) E[n] = 0.0f;
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) hin[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hg[n], E[n]);
+        }
+        // adjoint entering the segment from the right: group carry, then the in-group suffix
+        {
+            float rg[N], Eb[N];
+            float csb = 0.0f;
+            if (grp < g.G - 1) {
+                const float* p = ws + wl.GHB + ((size_t)b * (g.G - 1) + grp) * N * D + dc;
+#pragma unroll
+                for (int n = 0; n < N; ++n) rg[n] = p[(size_t)n * D];
+            } else if (a.dh_final != nullptr) {
+                const float* p = a.dh_final + ((size_t)b * D + dc) * N;
+#pragma unroll
+                for (int n = 0; n < N; ++n) rg[n] = p[n];
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) rg[n] = 0.0f;
+            }
+            if (g.S > 1) {
+                csb = ws[wl.CSB + ((size_t)b * g.S + s) * D + dc];
+                const float* p = ws + wl.EB + ((size_t)b * g.S + s) * N * D + dc;
+#pragma unroll
+                for (int n = 0; n < N; ++n) Eb[n] = p[(size_t)n * D];
+            } else {
+#pragma unroll
+                for (int n = 0; n < N; ++n) Eb[n] = 0.0f;
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) c[n] = __builtin_fmaf(exp2_fast(A2[n] * csb), rg[n], Eb[n]);
+        }
+        const float Dv = HAS_D ? a.Dskip[dc] : 0.0f;
+
+        SegIO<BF16> X, Dl, Z, DY, DX, DDL, DZ;
+        X.init(a.x, row0, len, D);
+        Dl.init(a.delta, row0, len, D);
+        DY.init(a.dy, row0, len, D);
+        Z.init(HAS_Z ? a.z : a.dy, row0, len, D);
+        DX.init(a.dx, row0, len, D);
+        DDL.init(a.ddelta, row0, len, D);
+        DZ.init(HAS_Z ? a.dz : a.dx, row0, len, D);
+        const uint32_t voff = (uint32_t)dc * es, rstride = (uint32_t)D * es;
+        const uint32_t soff_st = d < D ? voff : 0x80000000u;  // lanes past D store nowhere
+        // per-block partial rows of dB and dC: [t0, t0 + len) x N floats
+        const size_t prow = ((size_t)dblk * a.B + b) * a.L + t0;
+        const __amdgpu_buffer_rsrc_t rPB = make_rsrc(static_cast<float*>(a.ws) + wl.PB + prow * N,
+                                                      (uint32_t)len * N * 4u);
+        const __amdgpu_buffer_rsrc_t rPC = make_rsrc(static_cast<float*>(a.ws) + wl.PC + prow * N,
+                                                      (uint32_t)len * N * 4u);
+        const uint32_t poff = reduced_owner<N>(lane) ? (uint32_t)reduced_index<N>(lane) * 4u : 0x80000000u;
+        const void* Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
+        const void* Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
+        const int nsub = (len + K - 1) / K;
+
+        uint32_t dq[K], xq[K], zq[K], gq[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const uint32_t so = (uint32_t)((nsub - 1) * K + k) * rstride;
+            dq[k] = load_raw<BF16>(Dl.r, voff, so);
+            xq[k] = load_raw<BF16>(X.r, voff, so);
+            gq[k] = load_raw<BF16>(DY.r, voff, so);
+            zq[k] = HAS_Z ? load_raw<BF16>(Z.r, voff, so) : 0u;
+        }
+        Row<N, BF16> Bn, Cn;
+        Bn.load(Bbase, min((nsub - 1) * K, len - 1), rw);
+        Cn.load(Cbase, min((nsub - 1) * K, len - 1), rw);
+        for (int j = nsub - 1; j >= 0; --j) {
+            float dl[K], xv[K], dyv[K], zv[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                dl[k] = widen<BF16>(dq[k]);
+                xv[k] = widen<BF16>(xq[k]);
+                dyv[k] = widen<BF16>(gq[k]);
+                zv[k] = HAS_Z ? widen<BF16>(zq[k]) : 0.0f;
+            }
+            if (j > 0) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const uint32_t so = (uint32_t)((j - 1) * K + k) * rstride;
+                    dq[k] = load_raw<BF16>(Dl.r, voff, so);
+                    xq[k] = load_raw<BF16>(X.r, voff, so);
+                    gq[k] = load_raw<BF16>(DY.r, voff, so);
+                    if constexpr (HAS_Z) zq[k] = load_raw<BF16>(Z.r, voff, so);
+                }
+            }
+            // the sub-block's entering state
+            float h[N];
+            if (j == 0) {
+#pragma unroll
+                for (int n = 0; n < N; ++n) h[n] = hin[n];
+            } else {
+                const size_t ck = ((size_t)b * g.S + s) * c1 + (j - 1);
+                const float* hz = ws + wl.HZ + ck * N * D + dc;
+                const float cz = ws[wl.CZ + ck * D + dc];
+#pragma unroll
+                for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cz), hin[n], hz[(size_t)n * D]);
+            }
+            // forward over the sub-block: keep the states; dz, dD and dC
+            float hs[K][N], dv[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int t = j * K + k;
+                const Row<N, BF16> Bt = Bn, Ct = Cn;
+                const int tn = min(k + 1 < K ? t + 1 : j * K + K - 1, len - 1);
+                Bn.load(Bbase, tn, rw);
+                Cn.load(Cbase, tn, rw);
+                const float u = dl[k] * xv[k];
+                float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    h[n] = __builtin_fmaf(exp2_fast(dl[k] * A2[n]), h[n], u * Bt.at(n));
+                    hs[k][n] = h[n];
+                    if (n & 1) v1 = __builtin_fmaf(Ct.at(n), h[n], v1);
+                    else v0 = __builtin_fmaf(Ct.at(n), h[n], v0);
+                }
+                float v = v0 + v1;
+                if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv[k], v);
+                if constexpr (HAS_Z) {
+                    const float sg = rcp_fast(1.0f + exp2_fast(-zv[k] * kLog2e));
+                    dv[k] = dyv[k] * zv[k] * sg;
+                    const float dzv = dyv[k] * v * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
+                    store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, dzv);
+                } else {
+                    dv[k] = dyv[k];
+                }
+                if constexpr (HAS_D) dD = __builtin_fmaf(dv[k], xv[k], dD);
+                float w[16];
+#pragma unroll
+                for (int n = 0; n < N; ++n) w[n] = d < D ? dv[k] * h[n] : 0.0f;
+                const float tot = lane_reduce<N>(w, lane);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPC, (int)poff, (int)(t * N * 4), 0);
+            }
+            // backward over the sub-block
+#pragma unroll
+            for (int k = K - 1; k >= 0; --k) {
+                const int t = j * K + k;
+                const Row<N, BF16> Bt = Bn, Ct = Cn;
+                const int tn = k > 0 ? min(t - 1, len - 1) : min(max(j - 1, 0) * K, len - 1);
+                Bn.load(Bbase, tn, rw);
+                Cn.load(Cbase, tn, rw);
+                const float u = dl[k] * xv[k];
+                float sA = 0.0f, sB = 0.0f;
+                float w[16];
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float gg = __builtin_fmaf(dv[k], Ct.at(n), c[n]);  // dl/dh_t
+                    const float ah = __builtin_fmaf(-u, Bt.at(n), hs[k][n]);  // a_t h_{t-1}
+                    const float q = gg * ah;
+                    sA = __builtin_fmaf(q, A2[n], sA);
+                    dA[n] = __builtin_fmaf(q, dl[k], dA[n]);
+                    sB = __builtin_fmaf(gg, Bt.at(n), sB);
+                    w[n] = d < D ? gg * u : 0.0f;
+                    c[n] = exp2_fast(dl[k] * A2[n]) * gg;
+                }
+                const float dxv = __builtin_fmaf(dl[k], sB, HAS_D ? dv[k] * Dv : 0.0f);
+                const float ddv = __builtin_fmaf(sA, kLn2, xv[k] * sB);
+                store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, dxv);
+                store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, ddv);
+                const float tot = lane_reduce<N>(w, lane);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPB, (int)poff, (int)(t * N * 4), 0);
+            }
+        }
+        if (s == 0 && a.dh0 != nullptr && d < D) {
+            float* p = a.dh0 + ((size_t)b * D + d) * N;
+#pragma unroll
+            for (int n = 0; n < N; ++n) p[n] = c[n];
+        }
+    }
+    // dA and dD summed over the group's segments (waves past the sequence add zeros)
+    float* lA = lds;
+    float* lD = lA + W * N * 64;
+#pragma unroll
+    for (int n = 0; n < N; ++n) lA[(wave * N + n) * 64 + lane] = dA[n];
+    lD[wave * 64 + lane] = dD;
+    __syncthreads();
+    if (wave != 0 || d >= D) return;
+    float* PA = static_cast<float*>(a.ws) + wl.PA + ((size_t)b * g.G + grp) * N * D + d;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        float acc = 0.0f;
+        for (int j = 0; j < W; ++j) acc += lA[(j * N + n) * 64 + lane];
+        PA[(size_t)n * D] = acc;
+    }
+    if constexpr (HAS_D) {
+        float acc = 0.0f;
+        for (int j = 0; j < W; ++j) acc += lD[j * 64 + lane];
+        static_cast<float*>(a.ws)[wl.PD + ((size_t)b * g.G + grp) * D + d] = acc;
+    }
+}
+
+// ------------------------------------------------------------ 6. reductions
+// dA[d][n] = sum over (batch, group) of PA; dD[d] likewise. One thread per (n, d).
+__global__ void __launch_bounds__(256)
+bwd_reduce_params(BwdArgs a, BGeom g) {
+    const int N = a.N, D = a.D;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)N * D) return;
+    const int d = (int)(idx % D), n = (int)(idx / D);
+    const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
+    const float* ws = static_cast<const float*>(a.ws);
+    const int units = a.B * g.G;
+    float acc = 0.0f;
+    for (int k = 0; k < units; ++k) acc += ws[wl.PA + ((size_t)k * N + n) * D + d];
+    a.dA[(size_t)d * N + n] = acc;
+    if (n == 0 && a.dDskip != nullptr) {
+        float accd = 0.0f;
+        for (int k = 0; k < units; ++k) accd += ws[wl.PD + (size_t)k * D + d];
+        a.dDskip[d] = accd;
+    }
+}
+
+// dB[b][t][n] = sum over 64-channel blocks of PB (dC from PC), rounded to the io type.
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+bwd_reduce_rows(BwdArgs a, BGeom g) {
+    const size_t tot = (size_t)a.B * a.L * a.N;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= tot) return;
+    const BwsLayout wl = bws_layout(a.B, a.L, a.D, a.N, g);
+    const float* ws = static_cast<const float*>(a.ws);
+    const int nd = (a.D + 63) / 64;
+    float sb = 0.0f, sc = 0.0f;
+    for (int k = 0; k < nd; ++k) {
+        sb += ws[wl.PB + (size_t)k * tot + i];
+        sc += ws[wl.PC + (size_t)k * tot + i];
+    }
+    if constexpr (BF16) {
+        static_cast<uint16_t*>(a.dBm)[i] = f32_to_bf16(sb);
+        static_cast<uint16_t*>(a.dCm)[i] = f32_to_bf16(sc);
+    } else {
+        static_cast<float*>(a.dBm)[i] = sb;
+        static_cast<float*>(a.dCm)[i] = sc;
+    }
+}
+
+// L == 0: dh0 = dh_final, dA = 0, dD = 0.
+__global__ void __launch_bounds__(256)
+bwd_empty(BwdArgs a) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t ns = (size_t)a.B * a.D * a.N;
+    if (a.dh0 != nullptr && i < ns) a.dh0[i] = a.dh_final ? a.dh_final[i] : 0.0f;
+    if (i < (size_t)a.D * a.N) a.dA[i] = 0.0f;
+    if (a.dDskip != nullptr && i < (size_t)a.D) a.dDskip[i] = 0.0f;
+}
+
+template <int N, bool BF16, bool HAS_Z, bool HAS_D>
+void launch_final(const BwdArgs& a, const BGeom& g, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+    launch((bwd_final<N, BF16, HAS_Z, HAS_D>), grid, block, (uint32_t)lds, st, a, g);
+}
+
+template <int N, bool BF16>
+hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
+    const BGeom g = bgeom(a.B, a.L, a.D, a.N);
+    if (a.L == 0) {
+        const size_t n = std::max((size_t)a.B * a.D * a.N, (size_t)a.D * a.N);
+        launch(bwd_empty, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    const dim3 grid(g.G, (a.D + 63) / 64, a.B);
+    const dim3 block(64 * g.W);
+    const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
+    const size_t lds_fin = (size_t)g.W * (N + 1) * 64 * sizeof(float);
+    float* ws = static_cast<float*>(a.ws);
+    const BwsLayout wl = bws_layout(a.B, a.L, a.D, N, g);
+    if (g.S > 1 || g.nsub > 1) launch((bwd_state_aggregate<N, BF16>), grid, block, (uint32_t)lds_agg, st, a, g);
+    const size_t tot = (size_t)a.B * N * a.D;
+    const dim3 cg((unsigned)((tot + 255) / 256));
+    if (g.G > 1) launch(bwd_carry<false>, cg, dim3(256), 0, st, a.h0, ws + wl.GH, ws + wl.GP, a.B, a.D, N, g.G);
+    if (g.S > 1) {
+        if (a.z) launch((bwd_adjoint_aggregate<N, BF16, true>), grid, block, (uint32_t)lds_agg, st, a, g);
+        else launch((bwd_adjoint_aggregate<N, BF16, false>), grid, block, (uint32_t)lds_agg, st, a, g);
+    }
+    if (g.G > 1)
+        launch(bwd_carry<true>, cg, dim3(256), 0, st, a.dh_final, ws + wl.GHB, ws + wl.GPB, a.B, a.D, N, g.G);
+    const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
+    if (hz && hd) launch_final<N, BF16, true, true>(a, g, grid, block, lds_fin, st);
+    else if (hz) launch_final<N, BF16, true, false>(a, g, grid, block, lds_fin, st);
+    else if (hd) launch_final<N, BF16, false, true>(a, g, grid, block, lds_fin, st);
+    else launch_final<N, BF16, false, false>(a, g, grid, block, lds_fin, st);
+    launch(bwd_reduce_params, dim3((unsigned)(((size_t)N * a.D + 255) / 256)), dim3(256), 0, st, a, g);
+    const size_t rows = (size_t)a.B * a.L * N;
+    launch((bwd_reduce_rows<BF16>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a, g);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_dtype(const BwdArgs& a, hipStream_t st) {
+    switch (a.N) {
+        case 4: return launch_n<4, BF16>(a, st);
+        case 8: return launch_n<8, BF16>(a, st);
+        case 16: return launch_n<16, BF16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool scan_bwd_supported_n(int N) { return N == 4 || N == 8 || N == 16; }
+
+int scan_bwd_segment_len(int B, int L, int D, int N) { return bgeom(B, L, D, N).Ls; }
+
+size_t scan_bwd_workspace_bytes(int B, int L, int D, int N) {
+    if (L <= 0) return 0;
+    const BGeom g = bgeom(B, L, D, N);
+    return bws_layout(B, L, D, N, g).total * sizeof(float);
+}
+
+hipError_t launch_scan_bwd(const BwdArgs& a, hipStream_t st) {
+    return a.bf16 ? launch_dtype<true>(a, st) : launch_dtype<false>(a, st);
+}
+
+}  // namespace ssm

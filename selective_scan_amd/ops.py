@@ -41,6 +41,9 @@ def lib():
     L.ssm_scan_workspace_size.argtypes, L.ssm_scan_workspace_size.restype = [i, i, i, i], sz
     L.ssm_scan_fwd.argtypes = [i, i, i, i, i] + [vp] * 10 + [vp, sz, vp]
     L.ssm_scan_fwd.restype = i
+    L.ssm_scan_bwd_workspace_size.argtypes, L.ssm_scan_bwd_workspace_size.restype = [i, i, i, i], sz
+    L.ssm_scan_bwd.argtypes = [i, i, i, i, i] + [vp] * 18 + [vp, sz, vp]
+    L.ssm_scan_bwd.restype = i
     L.ssm_ssd_workspace_size.argtypes, L.ssm_ssd_workspace_size.restype = [i] * 6, sz
     L.ssm_ssd_fwd.argtypes = [i] * 7 + [vp] * 10 + [vp, sz, vp]
     L.ssm_ssd_fwd.restype = i
@@ -129,6 +132,56 @@ def ssm_scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, y=None, h_fina
     if st != SSM_OK:
         _raise("ssm_scan_fwd", st)
     return y, h_final
+
+
+def ssm_scan_bwd_workspace_size(B, L, D, N):
+    return int(lib().ssm_scan_bwd_workspace_size(B, L, D, N))
+
+
+def ssm_scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_final=None, *,
+                 want_dh0=True, out=None, workspace=None, stream=None):
+    """Gradient of ``ssm_scan_fwd`` for l = sum(dy * y) + sum(dh_final * h_final).
+
+    Inputs as for ``ssm_scan_fwd``; dy: [B, L, D] io dtype; dh_final: [B, D, N] fp32
+    or None. Returns a dict with dx, ddelta [B, L, D]; dA [D, N] fp32; dBm, dCm
+    [B, L, N]; dD [D] fp32 (None without D); dz [B, L, D] (None without z); dh0
+    [B, D, N] fp32 (None unless want_dh0). ``out`` may supply any of these tensors."""
+    Bb, L, Dd = x.shape
+    N = A.shape[1]
+    dev, io = x.device, x.dtype
+    _check(x, "x", (Bb, L, Dd), io, dev)
+    _check(delta, "delta", (Bb, L, Dd), io, dev)
+    _check(A, "A", (Dd, N), torch.float32, dev)
+    _check(Bm, "Bm", (Bb, L, N), io, dev)
+    _check(Cm, "Cm", (Bb, L, N), io, dev)
+    _check(dy, "dy", (Bb, L, Dd), io, dev)
+    _check(D, "D", (Dd,), torch.float32, dev, required=False)
+    _check(z, "z", (Bb, L, Dd), io, dev, required=False)
+    _check(h0, "h0", (Bb, Dd, N), torch.float32, dev, required=False)
+    _check(dh_final, "dh_final", (Bb, Dd, N), torch.float32, dev, required=False)
+    shapes = dict(dx=((Bb, L, Dd), io), ddelta=((Bb, L, Dd), io), dA=((Dd, N), torch.float32),
+                  dBm=((Bb, L, N), io), dCm=((Bb, L, N), io), dD=((Dd,), torch.float32),
+                  dz=((Bb, L, Dd), io), dh0=((Bb, Dd, N), torch.float32))
+    wanted = dict(dD=D is not None, dz=z is not None, dh0=want_dh0)
+    g = dict(out or {})
+    for k, (shp, dt) in shapes.items():
+        if not wanted.get(k, True):
+            g[k] = None
+            continue
+        if g.get(k) is None:
+            g[k] = torch.empty(shp, dtype=dt, device=dev)
+        _check(g[k], k, shp, dt, dev)
+    need = ssm_scan_bwd_workspace_size(Bb, L, Dd, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_scan_bwd(Bb, L, Dd, N, _io_code(x), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
+                            _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                            *(_ptr(g[k]) for k in ("dx", "ddelta", "dA", "dBm", "dCm", "dD", "dz", "dh0")),
+                            _ptr(workspace), wbytes, _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_scan_bwd", st)
+    return g
 
 
 # ------------------------------------------------------------------ SSD

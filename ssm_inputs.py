@@ -14,6 +14,8 @@ Distributions (the same for every workload unless stated):
   A (SSD)       A_h = -exp(U[ln 1, ln 16])                 (fp32)
   D             ~ N(0, 1)                                  (fp32)
   state0        ~ 0.1 * N(0, 1)                            (fp32, decode only)
+  dy            ~ N(0, 1)            (gradient of y, backward pass)
+  dh_final      ~ 0.1 * N(0, 1)      (fp32, gradient of the final state, backward pass)
 Random streams: ``numpy.random.default_rng([seed, tensor_id])`` (PCG64) with a
 fixed id per tensor, so every tensor is reproducible on its own.
 """
@@ -22,7 +24,7 @@ import math
 import numpy as np
 
 # fixed stream ids, one per tensor
-TID_DT, TID_X, TID_Z, TID_EPS, TID_B, TID_C, TID_D, TID_A, TID_STATE0 = range(9)
+TID_DT, TID_X, TID_Z, TID_EPS, TID_B, TID_C, TID_D, TID_A, TID_STATE0, TID_DY, TID_DHF = range(11)
 
 BF16, F32 = "bf16", "f32"
 
@@ -121,6 +123,13 @@ def scan_inputs(B, L, D, N, dtype=BF16, seed=0, with_D=True, with_z=True, with_h
     return out
 
 
+def scan_grad_inputs(B, L, D, N, dtype=BF16, seed=0, with_dh_final=True):
+    """Cotangents for the backward pass of the Mamba-1 scan: dy [B,L,D] in
+    ``dtype`` and dh_final [B,D,N] in float32 (None when not wanted)."""
+    return dict(dy=store(_normal(seed, TID_DY, (B, L, D)), dtype),
+                dh_final=(0.1 * _normal(seed, TID_DHF, (B, D, N))).astype(np.float32) if with_dh_final else None)
+
+
 def ssd_inputs(B, L, H, P, N, dtype=BF16, seed=0, with_D=False, with_z=False, with_h0=False):
     """SSD inputs. x, z [B,L,H,P]; delta [B,L,H]; Bm, Cm [B,L,N] in ``dtype``;
     A [H], D [H], h0 [B,H,N,P] in float32."""
@@ -182,6 +191,10 @@ WORKLOADS = {
     "scan_bf16_B1_L4096_D1536_N64": dict(kind="scan", B=1, L=4096, D=1536, N=64, dtype=BF16),
     "scan_bf16_B1_L4096_D1536_N128": dict(kind="scan", B=1, L=4096, D=1536, N=128, dtype=BF16),
     "scan_bf16_B1_L4096_D1536_N256": dict(kind="scan", B=1, L=4096, D=1536, N=256, dtype=BF16),
+    # backward (training) pass of the scan at the headline layer and at the training-step
+    # sweep's shape (batch 8, d_model 256 -> 512 channels, 32K tokens)
+    "scan_bwd_bf16_B1_L4096_D1536_N16": dict(kind="scan_bwd", B=1, L=4096, D=1536, N=16, dtype=BF16),
+    "scan_bwd_bf16_B8_L32768_D512_N16": dict(kind="scan_bwd", B=8, L=32768, D=512, N=16, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q256": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,
                                                 chunk=256, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q64": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,

@@ -47,3 +47,36 @@ def gpu_scan(w, **kw):
                              h0=t["h0"], **kw)
     torch.cuda.synchronize()
     return y, hf
+
+
+def oracle_scan_bwd(w, gw, sel=None):
+    """fp64 oracle gradients on the stored inputs and cotangents. With ``sel`` the
+    per-channel outputs are computed for those channels only (dBm, dCm are then
+    partial sums and must not be compared)."""
+    f = {k: si.to_f64(w[k]) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0")}
+    dy, dhf = si.to_f64(gw["dy"]), si.to_f64(gw["dh_final"])
+    if sel is not None:
+        for k in ("x", "delta", "z"):
+            if f[k] is not None:
+                f[k] = np.ascontiguousarray(f[k][:, :, sel])
+        dy = np.ascontiguousarray(dy[:, :, sel])
+        f["A"] = np.ascontiguousarray(f["A"][sel])
+        if f["D"] is not None:
+            f["D"] = np.ascontiguousarray(f["D"][sel])
+        for k in ("h0",):
+            if f[k] is not None:
+                f[k] = np.ascontiguousarray(f[k][:, sel])
+        if dhf is not None:
+            dhf = np.ascontiguousarray(dhf[:, sel])
+    return oracle.scan_bwd(f["x"], f["delta"], f["A"], f["Bm"], f["Cm"], dy, D=f["D"], z=f["z"],
+                           h0=f["h0"], dh_final=dhf)
+
+
+def gpu_scan_bwd(w, gw, **kw):
+    import selective_scan_amd as ssa
+    t = to_dev(w, ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0"))
+    g = to_dev(gw, ("dy", "dh_final"))
+    out = ssa.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], g["dy"], D=t["D"], z=t["z"],
+                           h0=t["h0"], dh_final=g["dh_final"], **kw)
+    torch.cuda.synchronize()
+    return out

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("ssm_scan_fwd", "ssm_ssd_fwd", "ssm_step", "ssm_ssd_step"):
+    for n in ("ssm_scan_fwd", "ssm_scan_bwd", "ssm_ssd_fwd", "ssm_step", "ssm_ssd_step"):
         assert n in names
 
 
@@ -123,3 +123,32 @@ def test_python_binding_checks_tensors_before_calling():
     with pytest.raises(TypeError):
         ssa.ssm_scan_fwd(x.to(torch.float64), x, torch.zeros(8, 16), torch.zeros(1, 4, 16),
                          torch.zeros(1, 4, 16))
+
+
+def _bwd(B=1, L=64, D=64, N=16, io=1, Dk=None, z=None, dD=None, dz=None, ws=P, wsb=1 << 30, **kw):
+    a = dict(x=P, delta=P, A=P, Bm=P, Cm=P, h0=None, dy=P, dhf=None, dx=P, ddelta=P, dA=P, dBm=P,
+             dCm=P, dh0=None)
+    a.update(kw)
+    return ops.lib().ssm_scan_bwd(B, L, D, N, io, a["x"], a["delta"], a["A"], a["Bm"], a["Cm"], Dk, z,
+                                  a["h0"], a["dy"], a["dhf"], a["dx"], a["ddelta"], a["dA"], a["dBm"],
+                                  a["dCm"], dD, dz, a["dh0"], ws, wsb, None)
+
+
+# every case has exactly one defect, so no call reaches a launch
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(L=-1), 1), (dict(io=5), 1),
+    (dict(N=32), 2), (dict(N=12), 2), (dict(N=256), 2), (dict(B=70000), 2),
+    (dict(dy=None), 1), (dict(dA=None), 1), (dict(A=None), 1), (dict(dCm=None), 1), (dict(ddelta=None), 1),
+    (dict(Dk=P), 1), (dict(dD=P), 1), (dict(z=P), 1), (dict(dz=P), 1),
+    (dict(dh0=ctypes.c_void_p(0x10004)), 1), (dict(dy=ctypes.c_void_p(0x10002)), 1),
+    (dict(ws=None, wsb=0), 3), (dict(wsb=64), 3),
+])
+def test_scan_bwd_rejects_bad_arguments(kw, status):
+    assert _bwd(**kw) == status
+    assert ops.lib().ssm_last_error().startswith(b"ssm_scan_bwd: ")
+
+
+def test_scan_bwd_workspace_size():
+    assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 16) > 0
+    assert ssa.ssm_scan_bwd_workspace_size(1, 0, 1536, 16) == 0
+    assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 32) == 0  # unsupported N

@@ -1,0 +1,94 @@
+"""GPU parity of ssm_scan_bwd (gradient of the Mamba-1 scan) against the fp64
+oracle's reverse-mode gradient, on the same stored inputs and cotangents."""
+import numpy as np
+import pytest
+import torch
+
+import ssm_inputs as si
+from gpu_util import gpu_scan_bwd, oracle_scan_bwd, out_f64, storage
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+PER_CHANNEL = ("dx", "ddelta", "dz")   # [B, L, D], io dtype
+SHARED = ("dBm", "dCm")                # [B, L, N], io dtype, summed over channels
+PARAMS = ("dA", "dD", "dh0")           # fp32
+
+
+def _check(w, gw, what="", sel=None, keys=None):
+    g = gpu_scan_bwd(w, gw)
+    r = oracle_scan_bwd(w, gw, sel)
+    st = storage(w)
+    for k in keys or (PER_CHANNEL + SHARED + PARAMS):
+        if r.get(k) is None:
+            assert g.get(k) is None, f"{what}: {k} returned without its input"
+            continue
+        v = out_f64(g[k])
+        if sel is not None:
+            if k in PER_CHANNEL:
+                v = v[:, :, sel]
+            elif k in ("dA", "dD"):
+                v = v[sel]
+            elif k == "dh0":
+                v = v[:, sel]
+        compare(v, r[k], st if k in PER_CHANNEL + SHARED else "f32", what=f"{what} {k}")
+
+
+SMALL = [
+    # B, L, D, N, dtype, with_D, with_z, with_h0, with_dh_final
+    (1, 1, 64, 16, si.F32, True, True, True, True),
+    (2, 37, 70, 16, si.BF16, True, True, True, True),
+    (1, 300, 64, 4, si.F32, False, False, False, False),
+    (3, 1000, 130, 8, si.BF16, True, False, True, True),
+    (1, 2001, 32, 16, si.F32, True, True, False, True),
+    (2, 513, 200, 16, si.BF16, True, True, True, False),
+    (1, 4097, 96, 16, si.BF16, False, True, False, True),
+    (5, 77, 1, 16, si.F32, True, True, True, True),
+    (1, 6, 64, 8, si.BF16, True, True, True, True),
+    (2, 999, 64, 4, si.BF16, True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}_L{}_D{}_N{}_{}_D{}z{}h{}g{}".format(*c))
+def test_scan_bwd_small_shapes(case):
+    B, L, D, N, dt, wd, wz, wh, wg = case
+    print(f"[scan_bwd small] {case}", flush=True)
+    w = si.scan_inputs(B, L, D, N, dtype=dt, seed=7, with_D=wd, with_z=wz, with_h0=wh)
+    gw = si.scan_grad_inputs(B, L, D, N, dtype=dt, seed=8, with_dh_final=wg)
+    _check(w, gw, what=str(case))
+
+
+def test_scan_bwd_empty_sequence():
+    w = si.scan_inputs(2, 0, 64, 16, dtype=si.BF16, seed=1, with_h0=True)
+    gw = si.scan_grad_inputs(2, 0, 64, 16, dtype=si.BF16, seed=2)
+    g = gpu_scan_bwd(w, gw)
+    np.testing.assert_array_equal(out_f64(g["dh0"]), gw["dh_final"].astype(np.float64))
+    assert not torch.any(g["dA"]) and not torch.any(g["dD"])
+    assert g["dx"].shape == (2, 0, 64) and g["dBm"].shape == (2, 0, 16)
+
+
+def test_scan_bwd_headline_layer_all_outputs():
+    """The headline layer (B=1, L=4096, D=1536, N=16, bf16): every output in full."""
+    print("[scan_bwd] bf16 B1 L4096 D1536 N16", flush=True)
+    w = si.scan_inputs(1, 4096, 1536, 16, dtype=si.BF16, seed=0)
+    gw = si.scan_grad_inputs(1, 4096, 1536, 16, dtype=si.BF16, seed=0)
+    _check(w, gw, what="B1 L4096 D1536")
+
+
+def test_scan_bwd_training_shape_all_outputs():
+    """The training-step sweep's largest shape (B=8, L=32768, D=512, N=16, bf16),
+    in the launch configuration the benchmark times: every output in full."""
+    print("[scan_bwd] bf16 B8 L32768 D512 N16", flush=True)
+    w = si.scan_inputs(8, 32768, 512, 16, dtype=si.BF16, seed=0)
+    gw = si.scan_grad_inputs(8, 32768, 512, 16, dtype=si.BF16, seed=0)
+    _check(w, gw, what="B8 L32768 D512")
+
+
+def test_scan_bwd_deterministic():
+    w = si.scan_inputs(2, 1500, 100, 16, dtype=si.BF16, seed=3, with_h0=True)
+    gw = si.scan_grad_inputs(2, 1500, 100, 16, dtype=si.BF16, seed=4)
+    g1 = gpu_scan_bwd(w, gw)
+    g2 = gpu_scan_bwd(w, gw)
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g2[k]), k
