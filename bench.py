@@ -11,7 +11,8 @@ Prints ONE JSON line: throughput in state updates/s (B*L*D*N per step), the
 roofline of the dominant kernel (timed live with HIP events recorded around
 each kernel launch on the launch stream), and the fp64 oracle timed on the
 host cores on a bounded sample of the same workload. ``other_paths`` holds the
-same measurements for the long-sequence scan, the SSD and the decode step.
+same measurements for the long-sequence scan, the state-dimension sweep, the
+backward (training) scan, the SSD and the two decode steps.
 """
 import argparse
 import ctypes
@@ -242,6 +243,62 @@ def scan_cpu_baseline(wl, w0, budget_s=15.0):
                        f"N={N}: {upd / 1e6:.1f} M updates, median of {reps} run(s), {el:.3f} s each")
 
 
+# ------------------------------------------------------------------ scan backward
+# Per state update, the final backward pass must issue (non-packed VALU lane-slots):
+# forward recompute v_mul (Delta*A), v_exp_f32 (2), v_mul (u*B), v_fma (state),
+# v_fma (C.h), v_mul (dv*h for dC); backward v_fma (adjoint), v_mul + v_exp_f32 (2)
+# (decay again), v_fma (a_t h_{t-1}), v_mul (q), v_fma x 3 (ddelta, dA, dx sums),
+# v_mul (g*u for dB), v_mul (carry) -> 18; plus the sums over the 64 channels of a
+# wave for dB and dC, at least 2 x 63/64 adds -> 20 lane-slots per update.
+BWD_SLOTS_PER_UPDATE = 20.0
+
+
+def scan_bwd_bench(name, wl, steps, warmup, dev, max_sets=8):
+    import torch
+    import ssm_inputs as si
+    import selective_scan_amd as ssa
+    B, L, D, N = wl["B"], wl["L"], wl["D"], wl["N"]
+    es = 2 if wl["dtype"] == si.BF16 else 4
+    set_bytes = 4 * B * L * D * es + 2 * B * L * N * es
+    R = max(1, min(max_sets, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for r in range(R):
+        w = si.scan_inputs(B, L, D, N, dtype=wl["dtype"], seed=r)
+        gw = si.scan_grad_inputs(B, L, D, N, dtype=wl["dtype"], seed=r)
+        t = {k: si.to_torch(w[k], dev) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D")}
+        t["dy"] = si.to_torch(gw["dy"], dev)
+        t["dhf"] = si.to_torch(gw["dh_final"], dev)
+        t["out"] = dict(dx=torch.empty_like(t["x"]), ddelta=torch.empty_like(t["x"]), dz=torch.empty_like(t["x"]),
+                        dA=torch.empty_like(t["A"]), dBm=torch.empty_like(t["Bm"]), dCm=torch.empty_like(t["Cm"]),
+                        dD=torch.empty_like(t["D"]), dh0=torch.empty((B, D, N), dtype=torch.float32, device=dev))
+        sets.append(t)
+    ws = torch.empty(max(ssa.ssm_scan_bwd_workspace_size(B, L, D, N), 1), dtype=torch.uint8, device=dev)
+
+    def call(t):
+        ssa.ssm_scan_bwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], D=t["D"], z=t["z"],
+                         dh_final=t["dhf"], out=t["out"], workspace=ws)
+
+    nk = count_kernels(lambda: call(sets[0]))
+    total_ms, ker = time_calls(call, sets, steps, warmup, nk)
+    ms = total_ms / steps
+    kmean = ker.mean(axis=0)
+    dom = int(np.argmax(kmean))
+    upd = B * L * D * N
+    # algorithmic bytes: read x, Delta, z, dy, B, C, A, D, dh_final; write dx, ddelta, dz,
+    # dB, dC, dA, dD, dh0
+    alg = 7 * B * L * D * es + 4 * B * L * N * es + 2 * (D * N + D) * 4 + 2 * B * D * N * 4
+    tdom = kmean[dom] * 1e-3
+    achieved = BWD_SLOTS_PER_UPDATE * upd / tdom / 1e12
+    peak = LANE_SLOTS_PER_S / 1e12
+    return dict(workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3),
+                tokens_per_s=B * L / (ms * 1e-3), kernel_ms=[float(v) for v in kmean],
+                hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                sets=len(sets), alg_bytes=alg,
+                roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
+                              traffic=committed_traffic("scan_bwd.hip", f"traffic_{name}.md"),
+                              kernel="bwd_final"))
+
+
 # ------------------------------------------------------------------ SSD
 def ssd_alg(wl):
     """Algorithmic HBM bytes and dense matrix flops per call.
@@ -418,6 +475,8 @@ def main():
     ap.add_argument("--workload", default="scan_bf16_B1_L4096_D1536_N16")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-other", action="store_true")
+    ap.add_argument("--other", default=None,
+                    help="only run this one other-paths workload (a scan_bwd_* or ssd_* name) and print it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -436,6 +495,16 @@ def main():
         sync()
         print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "calibrate_copy_bytes_written": dst.numel() * 4,
                           "launches": 5}))
+        return
+    if args.other:
+        wl = si.WORKLOADS[args.other]
+        if wl["kind"] == "scan_bwd":
+            r = scan_bwd_bench(args.other, wl, args.steps, args.warmup, dev)
+        elif wl["kind"] == "ssd":
+            r = ssd_bench(args.other, wl, args.steps, args.warmup, dev)
+        else:
+            raise SystemExit(f"--other takes a scan_bwd_* or ssd_* workload, not {args.other}")
+        print(json.dumps(r))
         return
     wl = si.WORKLOADS[args.workload]
     assert wl["kind"] == "scan", "the headline bench line is a scan workload"
@@ -475,6 +544,9 @@ def main():
             r3, _ = scan_bench(nm, si.WORKLOADS[nm], steps=10, warmup=2, dev=dev)
             other[nm] = {k: r3[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
                                             "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
+        for nm in ("scan_bwd_bf16_B1_L4096_D1536_N16", "scan_bwd_bf16_B8_L32768_D512_N16"):
+            other[nm] = scan_bwd_bench(nm, si.WORKLOADS[nm], steps=10 if si.WORKLOADS[nm]["L"] <= 4096 else 3,
+                                       warmup=2, dev=dev)
         for nm in ("ssd_bf16_B4_L8192_H24_P64_N128_Q256", "ssd_bf16_B4_L8192_H24_P64_N128_Q64",
                    "ssd_bf16_B4_L8000_H24_P64_N128_Q256"):
             other[nm] = ssd_bench(nm, si.WORKLOADS[nm], steps=10, warmup=3, dev=dev)

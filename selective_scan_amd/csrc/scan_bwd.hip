@@ -41,10 +41,13 @@ namespace ssm {
 namespace {
 
 #ifndef SSM_BWD_TARGET_WAVES
-#define SSM_BWD_TARGET_WAVES 4096
+#define SSM_BWD_TARGET_WAVES 6144
 #endif
 constexpr int kBwdTargetWaves = SSM_BWD_TARGET_WAVES;  // waves the final pass aims for
-constexpr int kBwdMinSegment = 32;
+#ifndef SSM_BWD_MIN_SEGMENT
+#define SSM_BWD_MIN_SEGMENT 16
+#endif
+constexpr int kBwdMinSegment = SSM_BWD_MIN_SEGMENT;
 constexpr int kBwdMaxGroup = 4;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -460,24 +463,64 @@ bwd_adjoint_aggregate(BwdArgs a, BGeom g) {
 // ------------------------------------------------------------ 2. and 4. carries
 // Forward: carry(0) = h0, carry(g+1) = GP_g carry(g) + GH_g, written over GH_g.
 // Backward: carry(G-1) = dh_final, carry(g-1) = GPB_{g-1} carry(g) + GHB_{g-1},
-// written over GHB_{g-1}. One thread per (batch, state index, channel).
+// written over GHB_{g-1}. Both walk G-1 slots in order p = 0 .. G-2 (slot p, or
+// slot G-2-p backwards). Workgroup of 64 channels x 4 quarters of that walk: each
+// thread composes its quarter's affine maps, the quarters' composites are chained
+// in LDS, then each thread walks its quarter again from its entering value.
 template <bool REV>
 __global__ void __launch_bounds__(256)
 bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ dec, int B, int D, int N,
           int G) {
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (size_t)B * N * D) return;
-    const int d = (int)(idx % D);
-    const int n = (int)((idx / D) % N);
-    const int b = (int)(idx / ((size_t)D * N));
+    __shared__ float sP[4][64], sH[4][64];
+    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int d = blockIdx.x * 64 + lane, n = blockIdx.y, b = blockIdx.z;
+    const int dc = d < D ? d : D - 1;
     const size_t st = (size_t)N * D;
-    float* H = agg + (size_t)b * (G - 1) * st + (size_t)n * D + d;
-    const float* P = dec + (size_t)b * (G - 1) * st + (size_t)n * D + d;
-    float h = init ? init[((size_t)b * D + d) * N + n] : 0.0f;
-    for (int k = 0; k < G - 1; ++k) {
-        const int kk = REV ? G - 2 - k : k;
-        h = __builtin_fmaf(P[kk * st], h, H[kk * st]);
-        H[kk * st] = h;
+    float* H = agg + (size_t)b * (G - 1) * st + (size_t)n * D + dc;
+    const float* P = dec + (size_t)b * (G - 1) * st + (size_t)n * D + dc;
+    const int steps = G - 1, per = (steps + 3) / 4;
+    const int p0 = min(q * per, steps), p1 = min(p0 + per, steps);
+    constexpr int U = 8;  // loads in flight
+    float cp = 1.0f, ch = 0.0f;  // composite of this quarter
+    for (int k0 = p0; k0 < p1; k0 += U) {
+        float pv[U], hv[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int pc = min(k0 + k, p1 - 1);
+            const size_t slot = (size_t)(REV ? steps - 1 - pc : pc) * st;
+            pv[k] = P[slot];
+            hv[k] = H[slot];
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (k0 + k < p1) {
+                ch = __builtin_fmaf(pv[k], ch, hv[k]);
+                cp *= pv[k];
+            }
+        }
+    }
+    sP[q][lane] = cp;
+    sH[q][lane] = ch;
+    __syncthreads();
+    float x = init ? init[((size_t)b * D + dc) * N + n] : 0.0f;
+    for (int j = 0; j < q; ++j) x = __builtin_fmaf(sP[j][lane], x, sH[j][lane]);
+    if (d >= D) return;
+    for (int k0 = p0; k0 < p1; k0 += U) {
+        float pv[U], hv[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int pc = min(k0 + k, p1 - 1);
+            const size_t slot = (size_t)(REV ? steps - 1 - pc : pc) * st;
+            pv[k] = P[slot];
+            hv[k] = H[slot];
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (k0 + k < p1) {
+                x = __builtin_fmaf(pv[k], x, hv[k]);
+                H[(size_t)(REV ? steps - 1 - (k0 + k) : k0 + k) * st] = x;
+            }
+        }
     }
 }
 
@@ -662,9 +705,10 @@ bwd_final(BwdArgs a, BGeom g) {
                     dv[k] = dyv[k];
                 }
                 if constexpr (HAS_D) dD = __builtin_fmaf(dv[k], xv[k], dD);
+                const float dvm = d < D ? dv[k] : 0.0f;
                 float w[16];
 #pragma unroll
-                for (int n = 0; n < N; ++n) w[n] = d < D ? dv[k] * h[n] : 0.0f;
+                for (int n = 0; n < N; ++n) w[n] = dvm * h[n];
                 const float tot = lane_reduce<N>(w, lane);
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPC, (int)poff, (int)(t * N * 4), 0);
             }
@@ -677,6 +721,7 @@ bwd_final(BwdArgs a, BGeom g) {
                 Bn.load(Bbase, tn, rw);
                 Cn.load(Cbase, tn, rw);
                 const float u = dl[k] * xv[k];
+                const float um = d < D ? u : 0.0f;
                 float sA = 0.0f, sB = 0.0f;
                 float w[16];
 #pragma unroll
@@ -687,7 +732,7 @@ bwd_final(BwdArgs a, BGeom g) {
                     sA = __builtin_fmaf(q, A2[n], sA);
                     dA[n] = __builtin_fmaf(q, dl[k], dA[n]);
                     sB = __builtin_fmaf(gg, Bt.at(n), sB);
-                    w[n] = d < D ? gg * u : 0.0f;
+                    w[n] = gg * um;
                     c[n] = exp2_fast(dl[k] * A2[n]) * gg;
                 }
                 const float dxv = __builtin_fmaf(dl[k], sB, HAS_D ? dv[k] * Dv : 0.0f);
@@ -727,24 +772,37 @@ bwd_final(BwdArgs a, BGeom g) {
 }
 
 // ------------------------------------------------------------ 6. reductions
-// dA[d][n] = sum over (batch, group) of PA; dD[d] likewise. One thread per (n, d).
+// dA[d][n] = sum over (batch, group) of PA; dD[d] likewise (blockIdx.y == N). One
+// workgroup per (64 channels, n): its 4 waves take every 4th unit, 4 loads in
+// flight each, then add their sums in LDS in a fixed order.
 __global__ void __launch_bounds__(256)
 bwd_reduce_params(BwdArgs a, BGeom g) {
+    __shared__ float part[4][64];
     const int N = a.N, D = a.D;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)N * D) return;
-    const int d = (int)(idx % D), n = (int)(idx / D);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int d = blockIdx.x * 64 + lane, n = blockIdx.y;
+    const bool is_d = n == N;
+    if (is_d && a.dDskip == nullptr) return;  // uniform over the block
     const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
     const float* ws = static_cast<const float*>(a.ws);
     const int units = a.B * g.G;
-    float acc = 0.0f;
-    for (int k = 0; k < units; ++k) acc += ws[wl.PA + ((size_t)k * N + n) * D + d];
-    a.dA[(size_t)d * N + n] = acc;
-    if (n == 0 && a.dDskip != nullptr) {
-        float accd = 0.0f;
-        for (int k = 0; k < units; ++k) accd += ws[wl.PD + (size_t)k * D + d];
-        a.dDskip[d] = accd;
+    const int dc = d < D ? d : D - 1;
+    const float* base = is_d ? ws + wl.PD + dc : ws + wl.PA + (size_t)n * D + dc;
+    const size_t ustride = is_d ? (size_t)D : (size_t)N * D;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = wave; k0 < units; k0 += 16) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int k = k0 + 4 * r;
+            if (k < units) acc[r] += base[(size_t)k * ustride];
+        }
     }
+    part[wave][lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    __syncthreads();
+    if (wave != 0 || d >= D) return;
+    const float v = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    if (is_d) a.dDskip[d] = v;
+    else a.dA[(size_t)d * N + n] = v;
 }
 
 // dB[b][t][n] = sum over 64-channel blocks of PB (dC from PC), rounded to the io type.
@@ -757,17 +815,23 @@ bwd_reduce_rows(BwdArgs a, BGeom g) {
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, a.N, g);
     const float* ws = static_cast<const float*>(a.ws);
     const int nd = (a.D + 63) / 64;
-    float sb = 0.0f, sc = 0.0f;
-    for (int k = 0; k < nd; ++k) {
-        sb += ws[wl.PB + (size_t)k * tot + i];
-        sc += ws[wl.PC + (size_t)k * tot + i];
+    float sb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < nd; k0 += 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (k0 + r < nd) {
+                sb[r] += ws[wl.PB + (size_t)(k0 + r) * tot + i];
+                sc[r] += ws[wl.PC + (size_t)(k0 + r) * tot + i];
+            }
+        }
     }
+    const float sbt = (sb[0] + sb[1]) + (sb[2] + sb[3]), sct = (sc[0] + sc[1]) + (sc[2] + sc[3]);
     if constexpr (BF16) {
-        static_cast<uint16_t*>(a.dBm)[i] = f32_to_bf16(sb);
-        static_cast<uint16_t*>(a.dCm)[i] = f32_to_bf16(sc);
+        static_cast<uint16_t*>(a.dBm)[i] = f32_to_bf16(sbt);
+        static_cast<uint16_t*>(a.dCm)[i] = f32_to_bf16(sct);
     } else {
-        static_cast<float*>(a.dBm)[i] = sb;
-        static_cast<float*>(a.dCm)[i] = sc;
+        static_cast<float*>(a.dBm)[i] = sbt;
+        static_cast<float*>(a.dCm)[i] = sct;
     }
 }
 
@@ -801,8 +865,7 @@ hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
     float* ws = static_cast<float*>(a.ws);
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, N, g);
     if (g.S > 1 || g.nsub > 1) launch((bwd_state_aggregate<N, BF16>), grid, block, (uint32_t)lds_agg, st, a, g);
-    const size_t tot = (size_t)a.B * N * a.D;
-    const dim3 cg((unsigned)((tot + 255) / 256));
+    const dim3 cg((unsigned)((a.D + 63) / 64), N, a.B);
     if (g.G > 1) launch(bwd_carry<false>, cg, dim3(256), 0, st, a.h0, ws + wl.GH, ws + wl.GP, a.B, a.D, N, g.G);
     if (g.S > 1) {
         if (a.z) launch((bwd_adjoint_aggregate<N, BF16, true>), grid, block, (uint32_t)lds_agg, st, a, g);
@@ -815,7 +878,7 @@ hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
     else if (hz) launch_final<N, BF16, true, false>(a, g, grid, block, lds_fin, st);
     else if (hd) launch_final<N, BF16, false, true>(a, g, grid, block, lds_fin, st);
     else launch_final<N, BF16, false, false>(a, g, grid, block, lds_fin, st);
-    launch(bwd_reduce_params, dim3((unsigned)(((size_t)N * a.D + 255) / 256)), dim3(256), 0, st, a, g);
+    launch(bwd_reduce_params, dim3((unsigned)((a.D + 63) / 64), N + 1), dim3(256), 0, st, a, g);
     const size_t rows = (size_t)a.B * a.L * N;
     launch((bwd_reduce_rows<BF16>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a, g);
     return hipGetLastError();
