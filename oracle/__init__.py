@@ -16,6 +16,8 @@ storage) and returns float64 arrays. Shapes and meaning follow the C header:
 * ``ssd_step``    one SSD decode step                    -> (y [B,H,P], new state [B,H,N,P])
 * ``scan_bwd``    gradient of ``scan`` for the loss sum(dy*y) + sum(dh_final*h_final)
                   -> dict of dx, ddelta, dA, dBm, dCm, dD, dz, dh0
+* ``scan_disc``, ``step_disc``  ``scan`` / ``step`` with disc = "euler" | "zoh" and
+                  Delta = softplus(delta + delta_bias) preprocessing
 """
 import ctypes
 import os
@@ -55,7 +57,9 @@ class Oracle:
                            ("oracle_ssd_chunked", [i] * 6 + [d] * 10),
                            ("oracle_step", [i, i, i] + [d] * 9),
                            ("oracle_ssd_step", [i, i, i, i] + [d] * 9),
-                           ("oracle_scan_bwd", [i, i, i, i] + [d] * 18)]:
+                           ("oracle_scan_bwd", [i, i, i, i] + [d] * 18),
+                           ("oracle_scan_disc", [i, i, i, i, i, d, i] + [d] * 10),
+                           ("oracle_step_disc", [i, i, i, i, d, i] + [d] * 9)]:
             fn = getattr(self.lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -125,6 +129,43 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return out
+
+    _DISC = {"euler": 0, "zoh": 1}
+
+    def scan_disc(self, x, delta, A, Bm, Cm, D=None, z=None, h0=None, disc="euler", delta_bias=None,
+                  delta_softplus=False):
+        """``scan`` with discretisation ``disc`` and Delta = [softplus](delta + delta_bias)."""
+        x, delta, A, Bm, Cm = map(_f64, (x, delta, A, Bm, Cm))
+        D, z, h0, bias = _f64(D), _f64(z), _f64(h0), _f64(delta_bias)
+        Bb, L, Dd = x.shape
+        N = A.shape[1]
+        assert delta.shape == x.shape and A.shape == (Dd, N)
+        assert Bm.shape == (Bb, L, N) and Cm.shape == (Bb, L, N)
+        assert bias is None or bias.shape == (Dd,)
+        y = np.empty_like(x)
+        hf = np.empty((Bb, Dd, N))
+        rc = self.lib.oracle_scan_disc(Bb, L, Dd, N, self._DISC[disc], _ptr(bias), int(bool(delta_softplus)),
+                                       _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
+                                       _ptr(h0), _ptr(y), _ptr(hf))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return y, hf
+
+    def step_disc(self, state, x, delta, A, Bm, Cm, D=None, z=None, disc="euler", delta_bias=None,
+                  delta_softplus=False):
+        """``step`` with discretisation ``disc`` and Delta = [softplus](delta + delta_bias)."""
+        st = _f64(state).copy()
+        x, delta, A, Bm, Cm = map(_f64, (x, delta, A, Bm, Cm))
+        D, z, bias = _f64(D), _f64(z), _f64(delta_bias)
+        Bb, Dd, N = st.shape
+        assert x.shape == (Bb, Dd) and delta.shape == (Bb, Dd) and A.shape == (Dd, N)
+        y = np.empty((Bb, Dd))
+        rc = self.lib.oracle_step_disc(Bb, Dd, N, self._DISC[disc], _ptr(bias), int(bool(delta_softplus)),
+                                       _ptr(st), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D),
+                                       _ptr(z), _ptr(y))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return y, st
 
     # -- SSD ---------------------------------------------------------------
     def _ssd_args(self, x, delta, A, Bm, Cm, D, z, h0):
@@ -212,6 +253,14 @@ def scan_unroll(*a, **k):
 
 def scan_bwd(*a, **k):
     return get().scan_bwd(*a, **k)
+
+
+def scan_disc(*a, **k):
+    return get().scan_disc(*a, **k)
+
+
+def step_disc(*a, **k):
+    return get().step_disc(*a, **k)
 
 
 def ssd_seq(*a, **k):

@@ -457,3 +457,93 @@ int oracle_scan_bwd(int B, int L, int D, int N,
     free(part);
     return 0;
 }
+
+/* ------------------------------------------------------------- O7 -------
+ * Discretisation variants of O1 and O4.
+ *  - Delta preprocessing: Delta = Delta_raw + delta_bias[d] (when given), then
+ *    softplus(Delta) = log(1 + e^Delta) when delta_softplus is set (reading: the
+ *    usual Mamba input to the scan; the pages draw Delta through a softplus).
+ *  - Exact zero-order hold ("Efficient Sequence Modeling: From S4 to Mamba-3",
+ *    section 03 (s4_minimal.py), section 04 "Math-verified discretization" and
+ *    question Q01): for diagonal A, Abar = exp(z) and Bbar = Delta B (e^z - 1)/z
+ *    with z = Delta A, switching to the Taylor series 1 + z/2 + z^2/6 for
+ *    |z| < 1e-4 to avoid 0/0, as the page describes. Exponential-Euler keeps
+ *    Bbar = Delta B. */
+static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+
+/* (e^z - 1)/z, the page's way */
+static double zoh_phi(double z) {
+    if (fabs(z) < 1e-4) return 1.0 + z / 2.0 + z * z / 6.0;
+    return (exp(z) - 1.0) / z;
+}
+
+/* one step's discretisation of channel d, state index n */
+static void discretise(int disc, double dt, double a, double* abar, double* bcoef) {
+    *abar = exp(dt * a);
+    *bcoef = disc == 1 ? dt * zoh_phi(dt * a) : dt;
+}
+
+static double pre_delta(double raw, const double* delta_bias, long d, int delta_softplus) {
+    double dt = raw;
+    if (delta_bias) dt += delta_bias[d];
+    if (delta_softplus) dt = softplus(dt);
+    return dt;
+}
+
+int oracle_scan_disc(int B, int L, int D, int N, int disc, const double* delta_bias, int delta_softplus,
+                     const double* x, const double* delta, const double* A,
+                     const double* Bm, const double* Cm, const double* Dskip,
+                     const double* z, const double* h0, double* y, double* h_final) {
+    if (bad_dims(B, L, D, N) || (disc != 0 && disc != 1)) return -1;
+    if ((long)B * L * D > 0 && (!x || !delta || !y)) return -1;
+    if ((long)D * N > 0 && !A) return -1;
+    if ((long)B * L * N > 0 && (!Bm || !Cm)) return -1;
+    long units = (long)B * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u) {
+        long b = u / D, d = u % D;
+        double* st = (double*)malloc(sizeof(double) * (N > 0 ? N : 1));
+        for (int n = 0; n < N; ++n) st[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+        for (long t = 0; t < L; ++t) {
+            long i = (b * L + t) * D + d;
+            const double* Brow = Bm + (b * L + t) * N;
+            const double* Crow = Cm + (b * L + t) * N;
+            double dt = pre_delta(delta[i], delta_bias, d, delta_softplus), xv = x[i];
+            double ch = 0.0;
+            for (int n = 0; n < N; ++n) {
+                double abar, bcoef;
+                discretise(disc, dt, A[d * N + n], &abar, &bcoef);
+                st[n] = abar * st[n] + bcoef * Brow[n] * xv;
+                ch += Crow[n] * st[n];
+            }
+            y[i] = finish_output(ch, Dskip, d, xv, z, i);
+        }
+        if (h_final)
+            for (int n = 0; n < N; ++n) h_final[(b * D + d) * N + n] = st[n];
+        free(st);
+    }
+    return 0;
+}
+
+int oracle_step_disc(int B, int D, int N, int disc, const double* delta_bias, int delta_softplus,
+                     double* state, const double* x, const double* delta, const double* A,
+                     const double* Bm, const double* Cm, const double* Dskip,
+                     const double* z, double* y) {
+    if (bad_dims(B, D, N, 0) || (disc != 0 && disc != 1)) return -1;
+    long units = (long)B * D;
+#pragma omp parallel for schedule(static)
+    for (long u = 0; u < units; ++u) {
+        long b = u / D, d = u % D;
+        double dt = pre_delta(delta[u], delta_bias, d, delta_softplus), xv = x[u];
+        double* h = state + u * N;
+        double ch = 0.0;
+        for (int n = 0; n < N; ++n) {
+            double abar, bcoef;
+            discretise(disc, dt, A[d * N + n], &abar, &bcoef);
+            h[n] = abar * h[n] + bcoef * Bm[b * N + n] * xv;
+            ch += Cm[b * N + n] * h[n];
+        }
+        y[u] = finish_output(ch, Dskip, d, xv, z, u);
+    }
+    return 0;
+}

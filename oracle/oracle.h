@@ -85,6 +85,21 @@ int oracle_scan_bwd(int B, int L, int D, int N,
                     double* dx, double* ddelta, double* dA, double* dBm, double* dCm,
                     double* dDskip, double* dz, double* dh0);
 
+/* O7: O1 and O4 with a choice of discretisation and Delta preprocessing:
+ * disc 0 = exponential-Euler (Bbar = Delta B), 1 = exact zero-order hold
+ * (Bbar = Delta B (e^z - 1)/z, z = Delta A; Taylor 1 + z/2 + z^2/6 for |z| < 1e-4);
+ * Delta = softplus(delta + delta_bias[d]) when delta_softplus is set (the bias
+ * is added first whenever delta_bias is not NULL). */
+int oracle_scan_disc(int B, int L, int D, int N, int disc, const double* delta_bias, int delta_softplus,
+                     const double* x, const double* delta, const double* A,
+                     const double* Bm, const double* Cm, const double* Dskip,
+                     const double* z, const double* h0, double* y, double* h_final);
+
+int oracle_step_disc(int B, int D, int N, int disc, const double* delta_bias, int delta_softplus,
+                     double* state, const double* x, const double* delta, const double* A,
+                     const double* Bm, const double* Cm, const double* Dskip,
+                     const double* z, double* y);
+
 #ifdef __cplusplus
 }
 #endif

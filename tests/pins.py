@@ -438,6 +438,114 @@ def pin_bwd_linear_in_cotangents(orc):
     assert all(not np.any(v) for v in g0.values()), "zero cotangents give a nonzero gradient"
 
 
+# --------------------------------------------------- discretisation variants (O7)
+def pin_disc_euler_is_scan(orc):
+    """Exponential-Euler with no Delta preprocessing is O1 / O4 exactly."""
+    p = mamba1_problem(2, 23, 3, 4, seed=121)
+    y, hf = orc.scan(**p)
+    y2, h2 = orc.scan_disc(**p, disc="euler")
+    assert np.array_equal(y, y2) and np.array_equal(hf, h2)
+    t = {k: (v[:, 0] if k in ("x", "delta", "z", "Bm", "Cm") else v) for k, v in p.items() if k != "h0"}
+    ys, ss = orc.step(p["h0"], **t)
+    ys2, ss2 = orc.step_disc(p["h0"], **t, disc="euler")
+    assert np.array_equal(ys, ys2) and np.array_equal(ss, ss2)
+
+
+def pin_softplus_bias_preprocessing(orc):
+    """Delta = softplus(raw + bias) inside equals O1 on Delta precomputed with numpy's
+    logaddexp(0, .); a bias without softplus is a plain shift."""
+    p = mamba1_problem(2, 19, 3, 4, seed=122)
+    r = np.random.default_rng(222)
+    raw = r.normal(-2.5, 1.5, p["delta"].shape)
+    bias = r.normal(0.0, 0.8, 3)
+    for disc in ("euler", "zoh"):
+        y, hf = orc.scan_disc(**dict(p, delta=raw), disc=disc, delta_bias=bias, delta_softplus=True)
+        y2, h2 = orc.scan_disc(**dict(p, delta=np.logaddexp(0.0, raw + bias)), disc=disc)
+        close(y, y2, tol=1e-13, what=f"softplus+bias {disc} y")
+        close(hf, h2, tol=1e-13, what=f"softplus+bias {disc} h")
+    y3, _ = orc.scan_disc(**dict(p, delta=np.abs(raw)), delta_bias=np.abs(bias))
+    y4, _ = orc.scan(**dict(p, delta=np.abs(raw) + np.abs(bias)))
+    close(y3, y4, tol=1e-13, what="bias shift")
+    t = {k: (v[:, 0] if k in ("x", "z", "Bm", "Cm") else v) for k, v in p.items() if k not in ("h0", "delta")}
+    ys, ss = orc.step_disc(p["h0"], delta=raw[:, 0], **t, delta_bias=bias, delta_softplus=True)
+    ys2, ss2 = orc.step(p["h0"], delta=np.logaddexp(0.0, raw[:, 0] + bias), **t)
+    close(ys, ys2, tol=1e-13, what="step softplus y")
+    close(ss, ss2, tol=1e-13, what="step softplus state")
+
+
+def pin_zoh_step_is_exact_ode_solution(orc):
+    """One zero-order-hold step is the exact solution of dh/dt = A h + B x over Delta
+    with B x held: e^{A Delta} h0 + (integral of e^{A (Delta - s)} ds over [0, Delta]) B x,
+    the integral taken by adaptive quadrature; includes |z| < 1e-4 (Taylor branch),
+    A = 0 and A > 0."""
+    from scipy.integrate import quad
+    cases = [(0.1, -3.0), (0.5, -0.2), (1e-3, -2.0), (2e-5, -1.5), (0.3, 0.0), (0.01, 1.5), (1.7, -6.0)]
+    D, N = 1, len(cases)
+    A = np.array([[a for _, a in cases]])
+    h0 = np.linspace(-0.5, 0.7, N).reshape(1, 1, N)
+    Bm = np.linspace(0.3, 1.9, N).reshape(1, 1, N)
+    for j, (dt, a) in enumerate(cases):
+        # one channel per case: Delta is per channel, so run them one at a time
+        y, hf = orc.scan_disc(x=np.array([[[0.7]]]), delta=np.array([[[dt]]]), A=A[:, j:j + 1],
+                              Bm=Bm[:, :, j:j + 1], Cm=np.ones((1, 1, 1)), h0=h0[:, :, j:j + 1], disc="zoh")
+        integral = quad(lambda s_: math.exp(a * (dt - s_)), 0.0, dt, epsabs=0.0, epsrel=1e-13)[0]
+        exact = math.exp(a * dt) * h0[0, 0, j] + integral * Bm[0, 0, j] * 0.7
+        assert abs(hf[0, 0, 0] - exact) <= 1e-12 * max(1.0, abs(exact)), (dt, a, hf[0, 0, 0], exact)
+        assert abs(y[0, 0, 0] - exact) <= 1e-12 * max(1.0, abs(exact))
+
+
+def pin_zoh_constant_input_closed_form(orc):
+    """Constant inputs: h_t = a^t h0 + c (1 - a^t)/(1 - a), a = e^{Delta A},
+    c = expm1(Delta A)/A B x (the ZOH input), written with expm1."""
+    B, L, D, N = 1, 40, 2, 3
+    r = np.random.default_rng(131)
+    A = -np.exp(r.uniform(-1.0, 1.5, (D, N)))
+    x0, d0, b0, c0 = 0.8, 0.07, r.standard_normal(N), r.standard_normal(N)
+    h0 = r.standard_normal((B, D, N))
+    p = dict(x=np.full((B, L, D), x0), delta=np.full((B, L, D), d0), A=A,
+             Bm=np.tile(b0, (B, L, 1)), Cm=np.tile(c0, (B, L, 1)), h0=h0)
+    y, hf = orc.scan_disc(**p, disc="zoh")
+    t = np.arange(1, L + 1)[:, None, None]                       # [L,1,1]
+    z = d0 * A[None]                                             # [1,D,N]
+    c = np.expm1(z) / A[None] * b0 * x0
+    h = np.exp(t * z) * h0 + c * np.expm1(t * z) / np.expm1(z)  # [L,D,N]
+    close(y[0], np.einsum("ldn,n->ld", h, c0), tol=1e-11, what="zoh constant y")
+    close(hf[0], h[-1], tol=1e-11, what="zoh constant h")
+
+
+def pin_zoh_phi_both_branches(orc):
+    """Bbar / (Delta B) = (e^z - 1)/z on both sides of the page's 1e-4 switch,
+    against numpy's expm1(z)/z."""
+    zs = np.array([1e-6, -5e-5, 9.9e-5, -1e-4, 1.01e-4, -1e-3, 0.1, -2.0])
+    for z_ in zs:
+        y, _ = orc.scan_disc(x=np.ones((1, 1, 1)), delta=np.ones((1, 1, 1)), A=np.array([[z_]]),
+                             Bm=np.ones((1, 1, 1)), Cm=np.ones((1, 1, 1)), disc="zoh")
+        ref = np.expm1(z_) / z_
+        assert abs(y[0, 0, 0] - ref) <= 1e-10 * abs(ref), (z_, y[0, 0, 0], ref)
+
+
+def pin_disc_step_matches_scan(orc):
+    """Under ZOH with softplus(Delta + bias): prefill(1) equals one step, and
+    prefill(L) then a step equals prefill(L + 1)."""
+    p = mamba1_problem(2, 14, 3, 4, seed=141)
+    r = np.random.default_rng(241)
+    p["delta"] = r.normal(-2.0, 1.0, p["delta"].shape)
+    kw = dict(disc="zoh", delta_bias=r.normal(0.0, 0.5, 3), delta_softplus=True)
+    y, hf = orc.scan_disc(**p, **kw)
+    q = {k: (v[:, :13] if k in ("x", "delta", "z", "Bm", "Cm") else v) for k, v in p.items()}
+    y13, h13 = orc.scan_disc(**q, **kw)
+    t = {k: p[k][:, 13] for k in ("x", "delta", "z", "Bm", "Cm")}
+    ys, ss = orc.step_disc(h13, A=p["A"], D=p["D"], **t, **kw)
+    close(ys, y[:, 13], what="zoh prefill+step y")
+    close(ss, hf, what="zoh prefill+step state")
+    q1 = {k: (v[:, :1] if k in ("x", "delta", "z", "Bm", "Cm") else v) for k, v in p.items()}
+    y1, h1 = orc.scan_disc(**q1, **kw)
+    t0 = {k: p[k][:, 0] for k in ("x", "delta", "z", "Bm", "Cm")}
+    ys0, ss0 = orc.step_disc(p["h0"], A=p["A"], D=p["D"], **t0, **kw)
+    close(ys0, y1[:, 0], what="zoh L=1 y")
+    close(ss0, h1, what="zoh L=1 state")
+
+
 ALL_PINS = [
     pin_chunked_equals_sequential,
     pin_constant_input_closed_form,
@@ -453,4 +561,10 @@ ALL_PINS = [
     pin_bwd_directional_derivative,
     pin_bwd_zero_decay_cumsum,
     pin_bwd_linear_in_cotangents,
+    pin_disc_euler_is_scan,
+    pin_softplus_bias_preprocessing,
+    pin_zoh_step_is_exact_ode_solution,
+    pin_zoh_constant_input_closed_form,
+    pin_zoh_phi_both_branches,
+    pin_disc_step_matches_scan,
 ]

@@ -45,6 +45,13 @@ MUTANTS = {
     "bwd_skip_gradient_ungated": ("gx = dv * Dskip[d];", "gx = dy[i] * Dskip[d];"),
     "bwd_adjoint_ignores_dh_final": ("c[n] = dh_final ? dh_final[(b * D + d) * N + n] : 0.0;", "c[n] = 0.0;"),
     "bwd_dx_uses_C": ("gx += g * dt * Bt[n];", "gx += g * dt * Ct[n];"),
+    "zoh_taylor_sign": ("return 1.0 + z / 2.0 + z * z / 6.0;", "return 1.0 - z / 2.0 + z * z / 6.0;"),
+    "zoh_exact_branch_not_divided": ("return (exp(z) - 1.0) / z;", "return (exp(z) - 1.0);"),
+    "zoh_coefficient_without_delta": ("*bcoef = disc == 1 ? dt * zoh_phi(dt * a) : dt;",
+                                      "*bcoef = disc == 1 ? zoh_phi(dt * a) : dt;"),
+    "delta_bias_ignored": ("if (delta_bias) dt += delta_bias[d];", ""),
+    "softplus_large_branch_truncated": ("return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
+                                        "return v > 0.0 ? v : log1p(exp(v));"),
 }
 
 
