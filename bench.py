@@ -243,6 +243,54 @@ def scan_cpu_baseline(wl, w0, budget_s=15.0):
                        f"N={N}: {upd / 1e6:.1f} M updates, median of {reps} run(s), {el:.3f} s each")
 
 
+# ------------------------------------------------------------------ scan variants
+# Exact zero-order hold per state update (steps whose |z| are all >= 1/32): v_mul
+# (Delta*A), v_exp_f32 (2), v_mul (x/A), v_mul (*B), v_add (h + w), v_fma (state),
+# v_fma (C.h) -> 8 lane-slots; softplus(delta + bias) is per (step, channel), not
+# per update.
+ZOH_SLOTS_PER_UPDATE = 8.0
+
+
+def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16):
+    import torch
+    import ssm_inputs as si
+    import selective_scan_amd as ssa
+    B, L, D, N = wl["B"], wl["L"], wl["D"], wl["N"]
+    es = 2 if wl["dtype"] == si.BF16 else 4
+    set_bytes = 4 * B * L * D * es + 2 * B * L * N * es
+    R = max(1, min(max_sets, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for r in range(R):
+        w = si.scan_inputs(B, L, D, N, dtype=wl["dtype"], seed=r)
+        raw = si.scan_raw_delta(B, L, D, dtype=wl["dtype"], seed=r)
+        t = {k: si.to_torch(w[k], dev) for k in ("x", "z", "Bm", "Cm", "A", "D")}
+        t["delta"] = si.to_torch(raw["delta"], dev)
+        t["bias"] = torch.from_numpy(raw["delta_bias"]).to(dev)
+        t["y"] = torch.empty_like(t["x"])
+        t["hf"] = torch.empty((B, D, N), dtype=torch.float32, device=dev)
+        sets.append(t)
+    ws = torch.empty(max(ssa.ssm_scan_workspace_size(B, L, D, N), 1), dtype=torch.uint8, device=dev)
+
+    def call(t):
+        ssa.ssm_scan_fwd_ex(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], D=t["D"], z=t["z"], disc="zoh",
+                            delta_bias=t["bias"], delta_softplus=True, y=t["y"], h_final=t["hf"], workspace=ws)
+
+    nk = count_kernels(lambda: call(sets[0]))
+    total_ms, ker = time_calls(call, sets, steps, warmup, nk)
+    ms = total_ms / steps
+    kmean = ker.mean(axis=0)
+    dom = int(np.argmax(kmean))
+    upd = B * L * D * N
+    alg = scan_alg_bytes(wl) + D * 4
+    achieved = ZOH_SLOTS_PER_UPDATE * upd / (kmean[dom] * 1e-3) / 1e12
+    peak = LANE_SLOTS_PER_S / 1e12
+    return dict(workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3), tokens_per_s=B * L / (ms * 1e-3),
+                kernel_ms=[float(v) for v in kmean], hbm_gbs=alg / (ms * 1e-3) / 1e9,
+                hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, sets=len(sets),
+                roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
+                              traffic=None, kernel="segment_final (zero-order hold, softplus(delta + bias))"))
+
+
 # ------------------------------------------------------------------ scan backward
 # Per state update, the final backward pass must issue (non-packed VALU lane-slots):
 # forward recompute v_mul (Delta*A), v_exp_f32 (2), v_mul (u*B), v_fma (state),
@@ -476,7 +524,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-other", action="store_true")
     ap.add_argument("--other", default=None,
-                    help="only run this one other-paths workload (a scan_bwd_* or ssd_* name) and print it")
+                    help="only run this one other-paths workload (a scan_bwd_*, scan_zoh_* or ssd_* name) and print it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -500,6 +548,8 @@ def main():
         wl = si.WORKLOADS[args.other]
         if wl["kind"] == "scan_bwd":
             r = scan_bwd_bench(args.other, wl, args.steps, args.warmup, dev)
+        elif wl["kind"] == "scan_var":
+            r = scan_var_bench(args.other, wl, args.steps, args.warmup, dev)
         elif wl["kind"] == "ssd":
             r = ssd_bench(args.other, wl, args.steps, args.warmup, dev)
         else:
@@ -544,6 +594,9 @@ def main():
             r3, _ = scan_bench(nm, si.WORKLOADS[nm], steps=10, warmup=2, dev=dev)
             other[nm] = {k: r3[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
                                             "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
+        other["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"] = scan_var_bench(
+            "scan_zoh_softplus_bf16_B1_L4096_D1536_N16", si.WORKLOADS["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"],
+            steps=20, warmup=3, dev=dev)
         for nm in ("scan_bwd_bf16_B1_L4096_D1536_N16", "scan_bwd_bf16_B8_L32768_D512_N16"):
             other[nm] = scan_bwd_bench(nm, si.WORKLOADS[nm], steps=10 if si.WORKLOADS[nm]["L"] <= 4096 else 3,
                                        warmup=2, dev=dev)

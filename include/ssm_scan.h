@@ -1,12 +1,14 @@
 /*
  * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
  *
- * Five entry points, each a hand-written HIP kernel pipeline for CDNA4:
- *   ssm_scan_fwd   Mamba-1 selective scan over a whole sequence (prefill)
- *   ssm_scan_bwd   its gradient (training backward pass)
- *   ssm_ssd_fwd    Mamba-2 SSD: scalar decay per head, chunked decayed-attention form
- *   ssm_step       one-token recurrent decode step, state updated in place
- *   ssm_ssd_step   the same for the Mamba-2 form (scalar decay per head, (N, P) state)
+ * Seven entry points, each a hand-written HIP kernel pipeline for CDNA4:
+ *   ssm_scan_fwd     Mamba-1 selective scan over a whole sequence (prefill)
+ *   ssm_scan_fwd_ex  the same with exact zero-order hold and/or Delta = softplus(delta + bias)
+ *   ssm_scan_bwd     the scan's gradient (training backward pass)
+ *   ssm_ssd_fwd      Mamba-2 SSD: scalar decay per head, chunked decayed-attention form
+ *   ssm_step         one-token recurrent decode step, state updated in place
+ *   ssm_step_ex      the decode step with the options of ssm_scan_fwd_ex
+ *   ssm_ssd_step     the same for the Mamba-2 form (scalar decay per head, (N, P) state)
  *
  * The operation (selective SSM of Gu & Dao, "Mamba: Linear-Time Sequence
  * Modeling with Selective State Spaces", 2023, and the SSD form of Dao & Gu,
@@ -56,6 +58,13 @@ extern "C" {
 #define SSM_ABI_VERSION 1
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+/* Discretisation of the continuous system dh/dt = A h + B x over one step Delta
+ * (diagonal A). Exponential-Euler is what every entry point uses by default. */
+typedef enum {
+    SSM_DISC_EULER = 0, /* Abar = exp(Delta A), Bbar = Delta B */
+    SSM_DISC_ZOH = 1    /* Abar = exp(z), Bbar = Delta B (e^z - 1)/z, z = Delta A (exact zero-order hold) */
+} ssm_disc_t;
 
 typedef enum {
     SSM_OK = 0,
@@ -110,6 +119,30 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
                  const void* z, const float* h0,
                  void* y, float* h_final,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_scan_fwd_ex -- ssm_scan_fwd with a choice of discretisation and the
+ * Delta preprocessing done inside the kernels.
+ *
+ *   disc           SSM_DISC_EULER or SSM_DISC_ZOH. Exact zero-order hold is the
+ *                  discretisation of "Efficient Sequence Modeling: From S4 to
+ *                  Mamba-3" (section 03, s4_minimal.py; section 04 "Math-verified
+ *                  discretization"; Q01): Bbar = Delta B (e^z - 1)/z, z = Delta A,
+ *                  evaluated without the 0/0 at z = 0 (a series where |z| < 1/32).
+ *   delta_bias     [D] fp32 or NULL: added to delta before everything else.
+ *   delta_softplus nonzero: Delta = softplus(delta + delta_bias) = log(1 + e^(.)).
+ * Every other argument, the workspace (ssm_scan_workspace_size) and the errors
+ * are those of ssm_scan_fwd; with SSM_DISC_EULER, no bias and no softplus it is
+ * ssm_scan_fwd. The options need N in {4, 8, 16, 32} (SSM_ERR_UNSUPPORTED
+ * otherwise). delta_bias must be 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+int ssm_scan_fwd_ex(int B, int L, int D, int N, int io, int disc,
+                    const float* delta_bias, int delta_softplus,
+                    const void* x, const void* delta, const float* A,
+                    const void* Bm, const void* Cm, const float* Dskip,
+                    const void* z, const float* h0,
+                    void* y, float* h_final,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * ssm_scan_bwd -- gradient of ssm_scan_fwd (training backward pass).
@@ -191,6 +224,15 @@ int ssm_step(int B, int D, int N, int io,
              float* state, const void* x, const void* delta, const float* A,
              const void* Bm, const void* Cm, const float* Dskip, const void* z,
              void* y, void* stream);
+
+/* ssm_step_ex -- ssm_step with disc, delta_bias and delta_softplus as in
+ * ssm_scan_fwd_ex (all N of ssm_step), so a sequence prefilled with
+ * ssm_scan_fwd_ex continues token by token with the same options. */
+int ssm_step_ex(int B, int D, int N, int io, int disc,
+                const float* delta_bias, int delta_softplus,
+                float* state, const void* x, const void* delta, const float* A,
+                const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                void* y, void* stream);
 
 /* ---------------------------------------------------------------------------
  * ssm_ssd_step -- one-token decode step of the Mamba-2 form, state in place

@@ -96,23 +96,30 @@ size_t ssm_scan_workspace_size(int B, int L, int D, int N) {
     return ssm::scan_workspace_bytes(B, L, D, N);
 }
 
-int ssm_scan_fwd(int B, int L, int D, int N, int io,
-                 const void* x, const void* delta, const float* A,
-                 const void* Bm, const void* Cm, const float* Dskip,
-                 const void* z, const float* h0,
-                 void* y, float* h_final,
-                 void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "ssm_scan_fwd";
+}  // extern "C"
+
+namespace {
+
+// ssm_scan_fwd and ssm_scan_fwd_ex: validation, then the plain or the variant path.
+int scan_fwd_impl(const char* fn, int B, int L, int D, int N, int io, int disc, const float* delta_bias,
+                  int delta_softplus, const void* x, const void* delta, const float* A, const void* Bm,
+                  const void* Cm, const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
+                  void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 1 || D < 1 || L < 0 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1 and L >= 0");
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (disc != SSM_DISC_EULER && disc != SSM_DISC_ZOH)
+        return fail(SSM_ERR_INVALID_ARG, fn, "disc must be SSM_DISC_EULER or SSM_DISC_ZOH");
+    const bool variant = disc != SSM_DISC_EULER || delta_bias != nullptr || delta_softplus != 0;
     if (!ssm::scan_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128, 256");
+    if (variant && !ssm::scan_var_supported_n(N))
+        return fail(SSM_ERR_UNSUPPORTED, fn, "zero-order hold and Delta preprocessing need N in {4, 8, 16, 32}");
     if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
     if (!product_ok({B, L, D, N}) || !product_ok({B, L, D}, 1LL << 40))
         return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
     if (!A) return fail(SSM_ERR_INVALID_ARG, fn, "A is NULL");
     if (L > 0 && (!x || !delta || !Bm || !Cm || !y))
         return fail(SSM_ERR_INVALID_ARG, fn, "x, delta, Bm, Cm and y are required");
-    const void* ptrs[] = {x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace};
+    const void* ptrs[] = {x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace, delta_bias};
     for (const void* p : ptrs)
         if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
     const int es = io == SSM_BF16 ? 2 : 4;
@@ -122,8 +129,59 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
     const size_t need = ssm::scan_workspace_bytes(B, L, D, N);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(SSM_ERR_WORKSPACE, fn, "workspace missing or smaller than ssm_scan_workspace_size()");
-    ssm::ScanArgs a{B, L, D, N, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace};
-    return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)), fn);
+    ssm::ScanArgs a{B, L, D, N, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace,
+                    delta_bias, delta_softplus, disc};
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(variant ? ssm::launch_scan_fwd_var(a, st) : ssm::launch_scan_fwd(a, st), fn);
+}
+
+// ssm_step and ssm_step_ex
+int step_impl(const char* fn, int B, int D, int N, int io, int disc, const float* delta_bias, int delta_softplus,
+              float* state, const void* x, const void* delta, const float* A, const void* Bm, const void* Cm,
+              const float* Dskip, const void* z, void* y, void* stream) {
+    if (B < 1 || D < 1 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (disc != SSM_DISC_EULER && disc != SSM_DISC_ZOH)
+        return fail(SSM_ERR_INVALID_ARG, fn, "disc must be SSM_DISC_EULER or SSM_DISC_ZOH");
+    if (!ssm::step_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128, 256");
+    if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
+    if (!product_ok({B, D, N}, 1LL << 40)) return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if ((long long)D * N > (1LL << 32)) return fail(SSM_ERR_UNSUPPORTED, fn, "D * N must be <= 2^32");
+    if (!state || !x || !delta || !A || !Bm || !Cm || !y)
+        return fail(SSM_ERR_INVALID_ARG, fn, "state, x, delta, A, Bm, Cm and y are required");
+    const void* ptrs[] = {state, x, delta, A, Bm, Cm, Dskip, z, y, delta_bias};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    ssm::StepArgs a{B, D, N, io == SSM_BF16, state, x, delta, A, Bm, Cm, Dskip, z, y,
+                    delta_bias, delta_softplus, disc};
+    const bool variant = disc != SSM_DISC_EULER || delta_bias != nullptr || delta_softplus != 0;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(variant ? ssm::launch_step_var(a, st) : ssm::launch_step(a, st), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(int B, int L, int D, int N, int io,
+                 const void* x, const void* delta, const float* A,
+                 const void* Bm, const void* Cm, const float* Dskip,
+                 const void* z, const float* h0,
+                 void* y, float* h_final,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    return scan_fwd_impl("ssm_scan_fwd", B, L, D, N, io, SSM_DISC_EULER, nullptr, 0, x, delta, A, Bm, Cm, Dskip,
+                         z, h0, y, h_final, workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_ex(int B, int L, int D, int N, int io, int disc,
+                    const float* delta_bias, int delta_softplus,
+                    const void* x, const void* delta, const float* A,
+                    const void* Bm, const void* Cm, const float* Dskip,
+                    const void* z, const float* h0,
+                    void* y, float* h_final,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    return scan_fwd_impl("ssm_scan_fwd_ex", B, L, D, N, io, disc, delta_bias, delta_softplus, x, delta, A, Bm,
+                         Cm, Dskip, z, h0, y, h_final, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------------------------ scan backward
@@ -214,20 +272,17 @@ int ssm_step(int B, int D, int N, int io,
              float* state, const void* x, const void* delta, const float* A,
              const void* Bm, const void* Cm, const float* Dskip, const void* z,
              void* y, void* stream) {
-    const char* fn = "ssm_step";
-    if (B < 1 || D < 1 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1");
-    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
-    if (!ssm::step_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128, 256");
-    if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
-    if (!product_ok({B, D, N}, 1LL << 40)) return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
-    if ((long long)D * N > (1LL << 32)) return fail(SSM_ERR_UNSUPPORTED, fn, "D * N must be <= 2^32");
-    if (!state || !x || !delta || !A || !Bm || !Cm || !y)
-        return fail(SSM_ERR_INVALID_ARG, fn, "state, x, delta, A, Bm, Cm and y are required");
-    const void* ptrs[] = {state, x, delta, A, Bm, Cm, Dskip, z, y};
-    for (const void* p : ptrs)
-        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
-    ssm::StepArgs a{B, D, N, io == SSM_BF16, state, x, delta, A, Bm, Cm, Dskip, z, y};
-    return hip_status(ssm::launch_step(a, static_cast<hipStream_t>(stream)), fn);
+    return step_impl("ssm_step", B, D, N, io, SSM_DISC_EULER, nullptr, 0, state, x, delta, A, Bm, Cm, Dskip, z,
+                     y, stream);
+}
+
+int ssm_step_ex(int B, int D, int N, int io, int disc,
+                const float* delta_bias, int delta_softplus,
+                float* state, const void* x, const void* delta, const float* A,
+                const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                void* y, void* stream) {
+    return step_impl("ssm_step_ex", B, D, N, io, disc, delta_bias, delta_softplus, state, x, delta, A, Bm, Cm,
+                     Dskip, z, y, stream);
 }
 
 // ------------------------------------------------------------------ SSD step

@@ -39,6 +39,11 @@ struct ScanArgs {
     void* y;
     float* h_final;
     void* ws;
+    // discretisation variant (ssm_scan_fwd_ex): 0 exponential-Euler, 1 zero-order
+    // hold; Delta = [softplus](delta + delta_bias) when either is set
+    const float* delta_bias;
+    int delta_softplus;
+    int disc;
 };
 
 // How the sequence is cut for the L-parallel scan: S segments of Ls steps
@@ -52,6 +57,9 @@ bool scan_supported_n(int N);
 ScanPlan scan_plan(int B, int L, int D, int N);
 size_t scan_workspace_bytes(int B, int L, int D, int N);
 hipError_t launch_scan_fwd(const ScanArgs& a, hipStream_t stream);
+// zero-order hold and/or Delta preprocessing; N in {4, 8, 16, 32}
+bool scan_var_supported_n(int N);
+hipError_t launch_scan_fwd_var(const ScanArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------ Mamba-1 scan, backward
 struct BwdArgs {
@@ -96,10 +104,15 @@ struct StepArgs {
     const float* Dskip;
     const void* z;
     void* y;
+    // discretisation variant (ssm_step_ex), as in ScanArgs
+    const float* delta_bias;
+    int delta_softplus;
+    int disc;
 };
 
 bool step_supported_n(int N);
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+hipError_t launch_step_var(const StepArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------ SSD decode step
 struct SsdStepArgs {

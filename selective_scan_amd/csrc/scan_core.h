@@ -1,0 +1,641 @@
+// Mamba-1 selective scan kernels on gfx950, shared by the plain forward entry point
+// (scan_fwd.hip) and its discretisation variants (scan_var.hip).
+// The scan: h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x_t,
+// y_t = (C_t . h_t + D x_t) silu(z_t)  (Gu & Dao 2023; exponential-Euler
+// discretisation as named by "Efficient Sequence Modeling: From S4 to Mamba-3",
+// sections 03 and 04).
+//
+// Work mapping. One lane owns one (batch, channel) and keeps its N state values
+// and its row A[d, :] (pre-scaled by log2 e) in VGPRs. All lanes of a wave share
+// the time step, so B_t and C_t are wave-uniform: they are read with scalar loads
+// into SGPRs and feed the VALU directly. x, Delta, z, y are streamed with buffer
+// loads/stores whose per-step offset lives in an SGPR (no VALU address math).
+// Per state update the hot loop issues v_mul (Delta*A), v_exp_f32, v_mul (u*B),
+// v_fma (state) and v_fma (C.h).
+//
+// L-parallelism. B*D channels alone cannot fill 256 CUs, so each chain of 64
+// channels is cut into S segments of Ls steps; W consecutive segments form a
+// group, handled by one workgroup of W waves (one wave per segment). Three launches:
+//   1. segment_aggregate: every wave runs its segment from a zero state (end
+//      state H_s, decay P_s = exp(A sum Delta)); the group's waves then form, in
+//      LDS, each segment's exclusive in-group prefix E_s (and the in-group prefix
+//      of sum Delta), and the last wave the group's own aggregate (GP_g, GH_g).
+//   2. group_carry: per (batch, channel, state index) a short sequential pass
+//      over the groups gives the state entering each group (linear in groups).
+//   3. segment_final: each wave forms its segment's carried-in state
+//      h_in = exp(A * prefix sum Delta) h_group + E_s and runs the recurrence
+//      again from it, writing y (and h_final at the end of the sequence).
+// (P1, H1) then (P2, H2) compose to (P2 P1, P2 H1 + H2): the recurrence is an
+// affine map of the state, so segments compose like affine maps.
+//
+// N >= 64 (64, 128, 256): a lane's 64 states and 64 entries of A would fill its
+// registers, so the state index is cut into chunks of 16 that run as independent
+// chains (aggregate, carry and recurrence are independent across state indices);
+// the final pass writes each chunk's fp32 partial C . h to the workspace and a
+// fourth launch (combine_partials) adds the chunks, the skip and the gate.
+#pragma once
+#include "common.h"
+#include "launch.h"
+
+#include <algorithm>
+
+namespace ssm {
+namespace {
+
+// Geometry defaults; each can be overridden at build time (-DSSM_SCAN_...).
+#ifndef SSM_SCAN_PREFETCH
+#define SSM_SCAN_PREFETCH 8
+#endif
+#ifndef SSM_SCAN_TARGET_WAVES
+#define SSM_SCAN_TARGET_WAVES 4096
+#endif
+#ifndef SSM_SCAN_MIN_SEGMENT
+#define SSM_SCAN_MIN_SEGMENT 32
+#endif
+#ifndef SSM_SCAN_MAX_GROUP
+#define SSM_SCAN_MAX_GROUP 4
+#endif
+constexpr int kPrefetch = SSM_SCAN_PREFETCH;       // steps of x/Delta/z in flight per lane
+constexpr int kTargetWaves = SSM_SCAN_TARGET_WAVES;  // waves the final pass aims for
+constexpr int kMinSegment = SSM_SCAN_MIN_SEGMENT;    // shortest segment (steps)
+
+struct Geom {
+    int Ls;  // steps per segment
+    int S;   // segments per chain
+    int W;   // segments (waves) per workgroup
+    int G;   // groups per chain
+};
+
+#ifndef SSM_SCAN_CHUNK_N
+#define SSM_SCAN_CHUNK_N 16
+#endif
+#ifndef SSM_SCAN_CHUNK_WAVES
+#define SSM_SCAN_CHUNK_WAVES 16384
+#endif
+// N >= 64 runs as N / kChunkN independent chains of kChunkN states per lane (a sweep
+// of 16/32/64 states per lane and 2048-16384 target waves on the N = 64, 128, 256
+// sweep shapes put 16 and 16384 first: the short chains keep ~80 VGPRs and several
+// waves per SIMD, which outweighs the extra partial sums they write).
+constexpr int kChunkN = SSM_SCAN_CHUNK_N;
+constexpr int kChunkWaves = SSM_SCAN_CHUNK_WAVES;  // waves the chunked passes aim for
+inline int n_chunks(int N) { return N >= 64 ? N / kChunkN : 1; }
+inline int lane_states(int N) { return n_chunks(N) > 1 ? kChunkN : N; }
+inline int max_group(int N) { return std::max(1, std::min(SSM_SCAN_MAX_GROUP, 128 / lane_states(N))); }
+
+Geom geom(int B, int L, int D, int N) {
+    Geom g{1, 0, 1, 0};
+    if (L <= 0) return g;
+    const long chains = (long)B * ((D + 63) / 64) * n_chunks(N);
+    const long s_target = n_chunks(N) > 1 ? std::max<long>(1, kChunkWaves / chains)
+                                          : (kTargetWaves + chains - 1) / chains;
+    long Ls = std::max<long>(kMinSegment, (L + s_target - 1) / s_target);
+    Ls = std::min<long>(Ls, L);
+    g.Ls = (int)Ls;
+    g.S = (int)((L + Ls - 1) / Ls);
+    g.W = std::min(max_group(N), g.S);
+    g.G = (g.S + g.W - 1) / g.W;
+    return g;
+}
+
+// workspace layout (floats), all with the channel index fastest:
+//   E  [B][S][N][D]   exclusive in-group prefix state of each segment
+//   CS [B][S][D]      in-group prefix of sum(Delta) before each segment
+//   GH [B][G-1][N][D] aggregate end state of each group (from zero); group_carry
+//                     overwrites slot g with the state entering group g+1
+//   GP [B][G-1][N][D] aggregate decay of each group
+//   YP [N/16][B][L][D] fp32 partial C . h of each state chunk (N >= 64 only)
+struct WsLayout {
+    size_t E, CS, GH, GP, YP, total;
+};
+
+__host__ __device__ inline WsLayout ws_layout(int B, int D, int N, int S, int G) {
+    WsLayout w;
+    const size_t g1 = G > 1 ? (size_t)(G - 1) : 0;
+    w.E = 0;
+    w.CS = w.E + (size_t)B * S * N * D;
+    w.GH = w.CS + (size_t)B * S * D;
+    w.GP = w.GH + (size_t)B * g1 * N * D;
+    w.YP = w.GP + (size_t)B * g1 * N * D;
+    w.total = w.YP;
+    return w;
+}
+
+// Discretisation variants (template parameter V of the segment kernels):
+//   V = 0  exponential-Euler, Delta as given (the plain path);
+//   V = 1  exponential-Euler, Delta = [softplus](delta + bias);
+//   V = 2  exact zero-order hold, Delta = [softplus](delta + bias).
+// Zero-order hold ("Efficient Sequence Modeling: From S4 to Mamba-3", section 04
+// and Q01): Bbar x = Delta B x (e^z - 1)/z = (e^z - 1)/A B x with z = Delta A. A step
+// whose |z| >= kZohSmall for every lane and state takes h' = e^z (h + w) - w with
+// w = x B / A (no rounding worse than 2 ulp / kZohSmall); otherwise the wave takes
+// the blended form, (e^z - 1)/A where |z| >= kZohSmall and Delta (1 + z/2 + z^2/6 +
+// z^3/24) below it (truncation < 1e-8 relative), which also covers A = 0.
+constexpr float kZohSmall = 0.03125f;
+constexpr float kZohSmall2 = kZohSmall * kLog2e;  // the same bound on |Delta A log2 e|
+constexpr float kLn2f = 0.69314718055994531f;
+
+template <int N, int V>
+struct VarLane {};  // V = 0: nothing per lane
+template <int N>
+struct VarLane<N, 1> {
+    float bias;
+    bool softplus;
+};
+template <int N>
+struct VarLane<N, 2> {
+    float bias;
+    bool softplus;
+    float rA[N];  // 1 / A (inf for A = 0: only read where |z| >= kZohSmall)
+    float amin2;  // min over the lane's states of |A log2 e|
+};
+
+template <int N, int V>
+__device__ __forceinline__ void var_lane_init(VarLane<N, V>& vl, const ScanArgs& a, int dc, int n0) {
+    if constexpr (V >= 1) {
+        vl.bias = a.delta_bias != nullptr ? a.delta_bias[dc] : 0.0f;
+        vl.softplus = a.delta_softplus != 0;
+    }
+    if constexpr (V == 2) {
+        vl.amin2 = __builtin_inff();
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float A = a.A[(size_t)dc * a.N + n0 + n];
+            vl.rA[n] = 1.0f / A;
+            vl.amin2 = fminf(vl.amin2, fabsf(A) * kLog2e);
+        }
+    }
+}
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|), with log1p by its series
+// below 1/64 (error < 2e-8 relative) and by v_log_f32 above.
+__device__ __forceinline__ float softplus_f(float v) {
+    const float e = exp2_fast(-fabsf(v) * kLog2e);
+    const float series = e * __builtin_fmaf(e, __builtin_fmaf(e, 1.0f / 3.0f, -0.5f), 1.0f);
+    const float lg = __builtin_amdgcn_logf(1.0f + e) * kLn2f;
+    return fmaxf(v, 0.0f) + (e < 0.015625f ? series : lg);
+}
+
+template <int N, int V>
+__device__ __forceinline__ float var_delta(float dv, const VarLane<N, V>& vl) {
+    if constexpr (V == 0) {
+        return dv;
+    } else {
+        const float v = dv + vl.bias;
+        return vl.softplus ? softplus_f(v) : v;
+    }
+}
+
+// One wave's segment of the recurrence. Construction issues the first loads
+// (kPrefetch steps of x, Delta[, z] and the first B[, C] rows), so a caller can
+// start them before other prologue work; run() then walks the segment.
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL, bool PARTIAL = false, int V = 0>
+struct Segment {
+    static constexpr uint32_t es = BF16 ? 2 : 4;
+    static constexpr bool kZ = FINAL && HAS_Z;
+    __amdgpu_buffer_rsrc_t rx, rd, rz, ry;
+    uint32_t voff, yoff, rstride, ystride;
+    const void* Bbase;
+    const void* Cbase;
+    int rw;  // row stride of B and C in 32-bit words
+    int len;
+    uint32_t dq[kPrefetch], xq[kPrefetch], zq[kPrefetch];
+    Row<N, BF16> Bn, Cn;
+
+    // store: this lane's channel exists (d < D); other lanes aim their y stores
+    // past the end of the y view, where the buffer unit drops them (no branch).
+    // The lane's states are n0 .. n0 + N - 1 of a.N. PARTIAL: y is the fp32
+    // C . h of these states only, written to `yp` ([B][L][D] of this chunk).
+    __device__ __forceinline__ Segment(const ScanArgs& a, int b, int dc, int t0, int len_, int n0,
+                                       bool store = true, float* yp = nullptr)
+        : len(len_) {
+        const size_t row0 = (size_t)b * a.L + t0;
+        const uint32_t bytes = (uint32_t)len * (uint32_t)a.D * es;
+        const char* xb = static_cast<const char*>(a.x) + row0 * a.D * es;
+        rx = make_rsrc(xb, bytes);
+        rd = make_rsrc(static_cast<const char*>(a.delta) + row0 * a.D * es, bytes);
+        rz = make_rsrc(kZ ? static_cast<const char*>(a.z) + row0 * a.D * es : xb, bytes);
+        if constexpr (PARTIAL) {
+            ry = make_rsrc(yp + row0 * a.D, (uint32_t)len * (uint32_t)a.D * 4u);
+            yoff = store ? (uint32_t)dc * 4u : 0x80000000u;
+            ystride = (uint32_t)a.D * 4u;
+        } else {
+            ry = make_rsrc(FINAL ? static_cast<const char*>(a.y) + row0 * a.D * es : xb, bytes);
+            yoff = store ? (uint32_t)dc * es : 0x80000000u;
+            ystride = (uint32_t)a.D * es;
+        }
+        voff = (uint32_t)dc * es;
+        rstride = (uint32_t)a.D * es;
+        Bbase = static_cast<const char*>(a.Bm) + (row0 * a.N + n0) * es;
+        Cbase = static_cast<const char*>(a.Cm) + (row0 * a.N + n0) * es;
+        rw = BF16 ? a.N / 2 : a.N;
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) {
+            const uint32_t so = (uint32_t)min(k, len - 1) * rstride;
+            dq[k] = load_raw<BF16>(rd, voff, so);
+            xq[k] = load_raw<BF16>(rx, voff, so);
+            zq[k] = kZ ? load_raw<BF16>(rz, voff, so) : 0u;
+        }
+        Bn.load(Bbase, 0, rw);
+        if constexpr (FINAL) Cn.load(Cbase, 0, rw);
+    }
+
+    // the input term of state n for one step: h' = a h + Bbar x
+    template <int MODE>
+    __device__ __forceinline__ float update(float hv, float ab, float dv, float xv, float u, float b, float a2,
+                                            const VarLane<N, V>& vl, int n) const {
+        if constexpr (V < 2) {
+            return __builtin_fmaf(ab, hv, u * b);
+        } else if constexpr (MODE == 0) {  // every |z| >= kZohSmall in the wave
+            const float w = xv * vl.rA[n] * b;
+            return __builtin_fmaf(ab, hv + w, -w);
+        } else {
+            const float z2 = dv * a2, z = z2 * kLn2f;
+            const float taylor =
+                dv * __builtin_fmaf(z, __builtin_fmaf(z, __builtin_fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
+            const float coef = fabsf(z2) < kZohSmall2 ? taylor : (ab - 1.0f) * vl.rA[n];
+            return __builtin_fmaf(ab, hv, coef * (xv * b));
+        }
+    }
+
+    template <int MODE>
+    __device__ __forceinline__ void states(const float (&A2)[N], float (&h)[N], float dv, float xv,
+                                           const Row<N, BF16>& Bt, const Row<N, BF16>& Ct, const VarLane<N, V>& vl,
+                                           float& y0, float& y1) const {
+        const float u = dv * xv;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float ab = exp2_fast(dv * A2[n]);
+            h[n] = update<MODE>(h[n], ab, dv, xv, u, Bt.at(n), A2[n], vl, n);
+            if constexpr (FINAL) {
+                if (n & 1) y1 = __builtin_fmaf(Ct.at(n), h[n], y1);
+                else y0 = __builtin_fmaf(Ct.at(n), h[n], y0);
+            }
+        }
+    }
+
+    // one time step t from ring slot k; RELOAD: refill the slot with step t + kPrefetch
+    template <bool RELOAD>
+    __device__ __forceinline__ void step(int t, int k, const float (&A2)[N], float (&h)[N], float Dv,
+                                         float& sumd, const VarLane<N, V>& vl) {
+        const float dv = var_delta<N, V>(widen<BF16>(dq[k]), vl), xv = widen<BF16>(xq[k]);
+        const float zv = kZ ? widen<BF16>(zq[k]) : 0.0f;
+        if constexpr (RELOAD) {
+            const uint32_t so = (uint32_t)min(t + kPrefetch, len - 1) * rstride;
+            dq[k] = load_raw<BF16>(rd, voff, so);
+            xq[k] = load_raw<BF16>(rx, voff, so);
+            if constexpr (kZ) zq[k] = load_raw<BF16>(rz, voff, so);
+        }
+        const Row<N, BF16> Bt = Bn;
+        Row<N, BF16> Ct;
+        if constexpr (FINAL) Ct = Cn;
+        const int tn = min(t + 1, len - 1);
+        Bn.load(Bbase, tn, rw);
+        if constexpr (FINAL) Cn.load(Cbase, tn, rw);
+        if constexpr (V == 0) {
+            // the plain path, exponential-Euler with Delta as given
+            const float u = dv * xv;
+            if constexpr (FINAL) {
+                float y0 = 0.0f, y1 = 0.0f;
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float ab = exp2_fast(dv * A2[n]);
+                    h[n] = __builtin_fmaf(ab, h[n], u * Bt.at(n));
+                    if (n & 1) y1 = __builtin_fmaf(Ct.at(n), h[n], y1);
+                    else y0 = __builtin_fmaf(Ct.at(n), h[n], y0);
+                }
+                float v = y0 + y1;
+                if constexpr (PARTIAL) {
+                    store_io<false>(ry, yoff, (uint32_t)t * ystride, v);
+                } else {
+                    if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
+                    if constexpr (HAS_Z) v *= silu(zv);
+                    store_io<BF16>(ry, yoff, (uint32_t)t * ystride, v);
+                }
+            } else {
+                sumd += dv;
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float ab = exp2_fast(dv * A2[n]);
+                    h[n] = __builtin_fmaf(ab, h[n], u * Bt.at(n));
+                }
+            }
+            return;
+        }
+        float y0 = 0.0f, y1 = 0.0f;
+        if constexpr (V == 2) {
+            // the blended form only when some lane of the wave has a small |z| this step
+            if (__builtin_amdgcn_ballot_w64(fabsf(dv) * vl.amin2 < kZohSmall2) != 0)
+                states<1>(A2, h, dv, xv, Bt, Ct, vl, y0, y1);
+            else
+                states<0>(A2, h, dv, xv, Bt, Ct, vl, y0, y1);
+        } else {
+            states<0>(A2, h, dv, xv, Bt, Ct, vl, y0, y1);  // V = 1: exponential-Euler
+        }
+        if constexpr (FINAL) {
+            float v = y0 + y1;
+            if constexpr (PARTIAL) {
+                store_io<false>(ry, yoff, (uint32_t)t * ystride, v);
+            } else {
+                if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
+                if constexpr (HAS_Z) v *= silu(zv);
+                store_io<BF16>(ry, yoff, (uint32_t)t * ystride, v);
+            }
+        } else {
+            sumd += dv;
+        }
+    }
+
+    // the whole segment from state h: full blocks of kPrefetch steps with a
+    // static ring slot per step, then the tail straight from the ring.
+    __device__ __forceinline__ void run(const float (&A2)[N], float (&h)[N], float Dv, float& sumd,
+                                        const VarLane<N, V>& vl) {
+        int t = 0;
+        for (; t + kPrefetch <= len; t += kPrefetch) {
+#pragma unroll
+            for (int k = 0; k < kPrefetch; ++k) step<true>(t + k, k, A2, h, Dv, sumd, vl);
+        }
+#pragma unroll
+        for (int k = 0; k < kPrefetch - 1; ++k)
+            if (t + k < len) step<false>(t + k, k, A2, h, Dv, sumd, vl);
+    }
+};
+
+template <int N, bool BF16, int V = 0>
+__global__ void __launch_bounds__(64 * SSM_SCAN_MAX_GROUP)
+segment_aggregate(ScanArgs a, Geom g) {
+    extern __shared__ float lds[];
+    const int W = g.W;
+    // the wave index is uniform across the wave: say so, so that everything derived
+    // from it (segment, descriptors, offsets) lives in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.x, b = blockIdx.z;
+    const int D = a.D, NT = a.N;
+    const int nch = NT / N, nc = blockIdx.y % nch, n0 = nc * N;  // state chunk of this block
+    const int d = (blockIdx.y / nch) * 64 + lane;
+    const int dc = d < D ? d : D - 1;
+    const int s = grp * W + wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
+
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[(size_t)dc * NT + n0 + n] * kLog2e;
+        h[n] = 0.0f;
+    }
+    float sumd = 0.0f;
+    VarLane<N, V> vl;
+    var_lane_init<N, V>(vl, a, dc, n0);
+    if (len > 0) {
+        Segment<N, BF16, false, false, false, false, V> seg(a, b, dc, t0, len, n0);
+        seg.run(A2, h, 0.0f, sumd, vl);
+    }
+    // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]; a segment past L is the identity (1, 0).
+    float* sP = lds;
+    float* sH = sP + W * N * 64;
+    float* sS = sH + W * N * 64;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        sP[(wave * N + n) * 64 + lane] = exp2_fast(A2[n] * sumd);
+        sH[(wave * N + n) * 64 + lane] = h[n];
+    }
+    sS[wave * 64 + lane] = sumd;
+    __syncthreads();
+
+    float E[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) E[n] = 0.0f;
+    float cs = 0.0f;
+    for (int j = 0; j < wave; ++j) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            E[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], E[n], sH[(j * N + n) * 64 + lane]);
+        cs += sS[j * 64 + lane];
+    }
+    if (d >= D || s >= g.S) return;
+    const WsLayout wl = ws_layout(a.B, D, NT, g.S, g.G);
+    float* ws = static_cast<float*>(a.ws);
+    if (wave > 0) {  // the first segment of a group starts from the group's own entering state
+        float* Ep = ws + wl.E + (((size_t)b * g.S + s) * NT + n0) * D + d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
+        if (nc == 0) ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+    }
+    // the group's own aggregate, needed by later groups
+    const bool last_in_group = (wave == W - 1) || (s == g.S - 1);
+    if (last_in_group && grp < g.G - 1) {
+        float* GH = ws + wl.GH + (((size_t)b * (g.G - 1) + grp) * NT + n0) * D + d;
+        float* GP = ws + wl.GP + (((size_t)b * (g.G - 1) + grp) * NT + n0) * D + d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            GH[(size_t)n * D] = __builtin_fmaf(sP[(wave * N + n) * 64 + lane], E[n], h[n]);
+            GP[(size_t)n * D] = exp2_fast(A2[n] * (cs + sumd));
+        }
+    }
+}
+
+// state entering each group: carry(0) = h0, carry(g+1) = GP_g carry(g) + GH_g,
+// written over GH_g; one thread per (batch, state index, channel)
+__global__ void __launch_bounds__(256)
+group_carry(const float* __restrict__ h0, float* ws, int B, int D, int N, Geom g) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)B * N * D) return;
+    const int d = (int)(idx % D);
+    const int n = (int)((idx / D) % N);
+    const int b = (int)(idx / ((size_t)D * N));
+    const WsLayout wl = ws_layout(B, D, N, g.S, g.G);
+    float* GH = ws + wl.GH + (size_t)b * (g.G - 1) * N * D + (size_t)n * D + d;
+    const float* GP = ws + wl.GP + (size_t)b * (g.G - 1) * N * D + (size_t)n * D + d;
+    const size_t st = (size_t)N * D;
+    float h = h0 ? h0[((size_t)b * D + d) * N + n] : 0.0f;
+    constexpr int U = 16;
+    for (int k0 = 0; k0 < g.G - 1; k0 += U) {
+        float p[U], q[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int kk = min(k0 + k, g.G - 2);
+            p[k] = GP[kk * st];
+            q[k] = GH[kk * st];
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (k0 + k >= g.G - 1) break;
+            h = __builtin_fmaf(p[k], h, q[k]);
+            GH[(k0 + k) * st] = h;
+        }
+    }
+}
+
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool PARTIAL, int V = 0>
+__global__ void __launch_bounds__(64 * SSM_SCAN_MAX_GROUP)
+segment_final(ScanArgs a, Geom g) {
+    const int W = g.W;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.x, b = blockIdx.z;
+    const int D = a.D, NT = a.N;
+    const int nch = NT / N, nc = blockIdx.y % nch, n0 = nc * N;  // state chunk of this block
+    const int d = (blockIdx.y / nch) * 64 + lane;
+    const int dc = d < D ? d : D - 1;
+    const int s = grp * W + wave;
+    const int t0 = s * g.Ls;
+    if (s >= g.S) return;
+    const int len = min(g.Ls, a.L - t0);
+    const WsLayout wl = ws_layout(a.B, D, NT, g.S, g.G);
+    const float* ws = static_cast<const float*>(a.ws);
+    // this chunk's [B][L][D] partial sums; the segment adds its own (b, t0) row offset
+    float* yp = PARTIAL ? static_cast<float*>(a.ws) + wl.YP + (size_t)nc * a.B * a.L * D : nullptr;
+
+    // every load that does not depend on the recurrence first: the segment's
+    // first inputs, A, the state entering the group and the in-group prefix
+    Segment<N, BF16, HAS_Z, HAS_D, true, PARTIAL, V> seg(a, b, dc, t0, len, n0, d < D, yp);
+    float A2[N], hg[N], E[N];
+    float cs = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] = a.A[(size_t)dc * NT + n0 + n] * kLog2e;
+    if (grp > 0) {
+        const float* cp = ws + wl.GH + (((size_t)b * (g.G - 1) + grp - 1) * NT + n0) * D + dc;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = cp[(size_t)n * D];
+    } else if (a.h0 != nullptr) {
+        const float* hp = a.h0 + ((size_t)b * D + dc) * NT + n0;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = hp[n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = 0.0f;
+    }
+    if (wave > 0) {
+        cs = ws[wl.CS + ((size_t)b * g.S + s) * D + dc];
+        const float* Ep = ws + wl.E + (((size_t)b * g.S + s) * NT + n0) * D + dc;
+#pragma unroll
+        for (int n = 0; n < N; ++n) E[n] = Ep[(size_t)n * D];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) E[n] = 0.0f;
+    }
+    float h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hg[n], E[n]);
+    // the variants run with HAS_D and D = 0 when the skip is absent
+    const float Dv = (HAS_D && (V == 0 || a.Dskip != nullptr)) ? a.Dskip[dc] : 0.0f;
+    float unused = 0.0f;
+    VarLane<N, V> vl;
+    var_lane_init<N, V>(vl, a, dc, n0);
+    seg.run(A2, h, Dv, unused, vl);
+    if (d < D && s == g.S - 1 && a.h_final != nullptr) {
+        float* hp = a.h_final + ((size_t)b * D + d) * NT + n0;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hp[n] = h[n];
+    }
+}
+
+// L == 0: the final state is the initial state.
+__global__ void copy_state(const float* __restrict__ h0, float* __restrict__ out, size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = h0 ? h0[i] : 0.0f;
+}
+
+// N > 64: y = (sum over the state chunks of their partial C . h + D x) silu(z),
+// one thread per (b, t, d).
+template <bool BF16, bool HAS_Z, bool HAS_D>
+__global__ void __launch_bounds__(256)
+combine_partials(ScanArgs a, const float* __restrict__ yp, int nch) {
+    const size_t tot = (size_t)a.B * a.L * a.D;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= tot) return;
+    float v = 0.0f;
+    for (int c = 0; c < nch; ++c) v += yp[(size_t)c * tot + i];
+    if constexpr (HAS_D) {
+        const float xv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[i]) : static_cast<const float*>(a.x)[i];
+        v = __builtin_fmaf(a.Dskip[i % a.D], xv, v);
+    }
+    if constexpr (HAS_Z) {
+        const float zv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.z)[i]) : static_cast<const float*>(a.z)[i];
+        v *= silu(zv);
+    }
+    if constexpr (BF16) static_cast<uint16_t*>(a.y)[i] = f32_to_bf16(v);
+    else static_cast<float*>(a.y)[i] = v;
+}
+
+// N: states per lane (a.N itself when a.N <= 64, else the chunk of 64).
+template <int N, bool BF16>
+hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
+    const Geom g = geom(a.B, a.L, a.D, a.N);
+    if (a.L == 0) {
+        if (a.h_final) {
+            const size_t n = (size_t)a.B * a.D * a.N;
+            launch(copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.h0, a.h_final, n);
+        }
+        return hipGetLastError();
+    }
+    const int nch = a.N / N;
+    const dim3 grid(g.G, ((a.D + 63) / 64) * nch, a.B);
+    const dim3 block(64 * g.W);
+    const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
+    if (g.S > 1) launch((segment_aggregate<N, BF16>), grid, block, lds_agg, st, a, g);
+    if (g.G > 1) {
+        const size_t tot = (size_t)a.B * a.N * a.D;
+        launch(group_carry, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a.h0,
+               static_cast<float*>(a.ws), a.B, a.D, a.N, g);
+    }
+    const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
+    if (nch > 1) {
+        launch((segment_final<N, BF16, false, false, true>), grid, block, 0, st, a, g);
+        const float* yp = static_cast<const float*>(a.ws) + ws_layout(a.B, a.D, a.N, g.S, g.G).YP;
+        const size_t tot = (size_t)a.B * a.L * a.D;
+        const dim3 cg((unsigned)((tot + 255) / 256));
+        if (hz && hd) launch((combine_partials<BF16, true, true>), cg, dim3(256), 0, st, a, yp, nch);
+        else if (hz) launch((combine_partials<BF16, true, false>), cg, dim3(256), 0, st, a, yp, nch);
+        else if (hd) launch((combine_partials<BF16, false, true>), cg, dim3(256), 0, st, a, yp, nch);
+        else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, nch);
+        return hipGetLastError();
+    }
+    if (hz && hd) launch((segment_final<N, BF16, true, true, false>), grid, block, 0, st, a, g);
+    else if (hz) launch((segment_final<N, BF16, true, false, false>), grid, block, 0, st, a, g);
+    else if (hd) launch((segment_final<N, BF16, false, true, false>), grid, block, 0, st, a, g);
+    else launch((segment_final<N, BF16, false, false, false>), grid, block, 0, st, a, g);
+    return hipGetLastError();
+}
+
+// Discretisation variants (V = 1, 2) for N <= 32; the skip term goes through the
+// HAS_D path with D = 0 when absent (exact: y + 0 x = y).
+template <int N, bool BF16, int V>
+hipError_t launch_var(const ScanArgs& a, hipStream_t st) {
+    const Geom g = geom(a.B, a.L, a.D, a.N);
+    if (a.L == 0) {
+        if (a.h_final) {
+            const size_t n = (size_t)a.B * a.D * a.N;
+            launch(copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.h0, a.h_final, n);
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid(g.G, (a.D + 63) / 64, a.B);
+    const dim3 block(64 * g.W);
+    const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
+    if (g.S > 1) launch((segment_aggregate<N, BF16, V>), grid, block, lds_agg, st, a, g);
+    if (g.G > 1) {
+        const size_t tot = (size_t)a.B * a.N * a.D;
+        launch(group_carry, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a.h0,
+               static_cast<float*>(a.ws), a.B, a.D, a.N, g);
+    }
+    if (a.z != nullptr) launch((segment_final<N, BF16, true, true, false, V>), grid, block, 0, st, a, g);
+    else launch((segment_final<N, BF16, false, true, false, V>), grid, block, 0, st, a, g);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_dtype(const ScanArgs& a, hipStream_t st) {
+    switch (a.N) {
+        case 4: return launch_n<4, BF16>(a, st);
+        case 8: return launch_n<8, BF16>(a, st);
+        case 16: return launch_n<16, BF16>(a, st);
+        case 32: return launch_n<32, BF16>(a, st);
+        case 64:
+        case 128:
+        case 256: return launch_n<kChunkN, BF16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+}  // namespace ssm

@@ -98,6 +98,69 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(StepArgs a) {
     }
 }
 
+// Discretisation variants of the step (bandwidth-bound, so the options are
+// runtime flags): Delta = [softplus](delta + bias); exponential-Euler or the exact
+// zero-order hold Bbar x = (e^z - 1)/A B x, z = Delta A, with the series
+// Delta (1 + z/2 + z^2/6 + z^3/24) where |z| < 1/32 (truncation < 1e-8 relative).
+__device__ __forceinline__ float step_softplus(float v) {
+    const float e = exp2_fast(-fabsf(v) * kLog2e);
+    const float series = e * __builtin_fmaf(e, __builtin_fmaf(e, 1.0f / 3.0f, -0.5f), 1.0f);
+    const float lg = __builtin_amdgcn_logf(1.0f + e) * 0.69314718055994531f;
+    return fmaxf(v, 0.0f) + (e < 0.015625f ? series : lg);
+}
+
+__device__ __forceinline__ float step_input(float ab, float hv, float dt, float A, float xb, bool zoh) {
+    if (!zoh) return __builtin_fmaf(ab, hv, dt * xb);
+    const float z = dt * A;
+    const float taylor =
+        dt * __builtin_fmaf(z, __builtin_fmaf(z, __builtin_fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
+    const float coef = fabsf(z) < 0.03125f ? taylor : (ab - 1.0f) / A;
+    return __builtin_fmaf(ab, hv, coef * xb);
+}
+
+template <int N, bool BF16>
+__global__ void __launch_bounds__(kStepThreads) step_kernel_var(StepArgs a) {
+    constexpr int QPC = N / 4;
+    const int b = blockIdx.y;
+    const int t = threadIdx.x;
+    const int q = t & (QPC - 1);
+    const int D = a.D;
+    const int F = D * QPC;
+    const int f0 = blockIdx.x * (kStepThreads * kReps) + t;
+    const bool zoh = a.disc == 1, sp = a.delta_softplus != 0;
+    const float4 Bq = load_quarter<N, BF16>(a.Bm, b, q);
+    const float4 Cq = load_quarter<N, BF16>(a.Cm, b, q);
+    float4* st = reinterpret_cast<float4*>(a.state + (size_t)b * D * N);
+    const float4* Af = reinterpret_cast<const float4*>(a.A);
+#pragma unroll
+    for (int r = 0; r < kReps; ++r) {
+        const int f = f0 + r * kStepThreads;
+        const int d = (f < F ? f : F - 1) / QPC;
+        float dt = load_io_at<BF16>(a.delta, (size_t)b * D + d);
+        if (a.delta_bias != nullptr) dt += a.delta_bias[d];
+        if (sp) dt = step_softplus(dt);
+        const float xv = load_io_at<BF16>(a.x, (size_t)b * D + d);
+        const float4 A4 = Af[f < F ? f : F - 1];
+        const float4 h = f < F ? st[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 hn;
+        hn.x = step_input(exp2_fast(dt * kLog2e * A4.x), h.x, dt, A4.x, xv * Bq.x, zoh);
+        hn.y = step_input(exp2_fast(dt * kLog2e * A4.y), h.y, dt, A4.y, xv * Bq.y, zoh);
+        hn.z = step_input(exp2_fast(dt * kLog2e * A4.z), h.z, dt, A4.z, xv * Bq.z, zoh);
+        hn.w = step_input(exp2_fast(dt * kLog2e * A4.w), h.w, dt, A4.w, xv * Bq.w, zoh);
+        if (f < F) st[f] = hn;
+        float p = __builtin_fmaf(Cq.x, hn.x, Cq.y * hn.y) + __builtin_fmaf(Cq.z, hn.z, Cq.w * hn.w);
+#pragma unroll
+        for (int o = QPC / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o);
+        if (q == 0 && f < F) {
+            float v = p;
+            if (a.Dskip != nullptr) v = __builtin_fmaf(a.Dskip[d], xv, v);
+            if (a.z != nullptr) v *= silu(load_io_at<BF16>(a.z, (size_t)b * D + d));
+            if constexpr (BF16) static_cast<uint16_t*>(a.y)[(size_t)b * D + d] = f32_to_bf16(v);
+            else static_cast<float*>(a.y)[(size_t)b * D + d] = v;
+        }
+    }
+}
+
 template <int N, bool BF16>
 hipError_t launch_n(const StepArgs& a, hipStream_t st) {
     const long F = (long)a.D * (N / 4);
@@ -108,6 +171,28 @@ hipError_t launch_n(const StepArgs& a, hipStream_t st) {
     else if (hd) launch((step_kernel<N, BF16, false, true>), grid, dim3(kStepThreads), 0, st, a);
     else launch((step_kernel<N, BF16, false, false>), grid, dim3(kStepThreads), 0, st, a);
     return hipGetLastError();
+}
+
+template <int N, bool BF16>
+hipError_t launch_var_n(const StepArgs& a, hipStream_t st) {
+    const long F = (long)a.D * (N / 4);
+    const dim3 grid((unsigned)((F + kStepThreads * kReps - 1) / (kStepThreads * kReps)), (unsigned)a.B);
+    launch((step_kernel_var<N, BF16>), grid, dim3(kStepThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_var_dtype(const StepArgs& a, hipStream_t st) {
+    switch (a.N) {
+        case 4: return launch_var_n<4, BF16>(a, st);
+        case 8: return launch_var_n<8, BF16>(a, st);
+        case 16: return launch_var_n<16, BF16>(a, st);
+        case 32: return launch_var_n<32, BF16>(a, st);
+        case 64: return launch_var_n<64, BF16>(a, st);
+        case 128: return launch_var_n<128, BF16>(a, st);
+        case 256: return launch_var_n<256, BF16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <bool BF16>
@@ -132,6 +217,10 @@ bool step_supported_n(int N) {
 
 hipError_t launch_step(const StepArgs& a, hipStream_t st) {
     return a.bf16 ? launch_dtype<true>(a, st) : launch_dtype<false>(a, st);
+}
+
+hipError_t launch_step_var(const StepArgs& a, hipStream_t st) {
+    return a.bf16 ? launch_var_dtype<true>(a, st) : launch_var_dtype<false>(a, st);
 }
 
 }  // namespace ssm

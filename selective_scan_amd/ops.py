@@ -41,6 +41,10 @@ def lib():
     L.ssm_scan_workspace_size.argtypes, L.ssm_scan_workspace_size.restype = [i, i, i, i], sz
     L.ssm_scan_fwd.argtypes = [i, i, i, i, i] + [vp] * 10 + [vp, sz, vp]
     L.ssm_scan_fwd.restype = i
+    L.ssm_scan_fwd_ex.argtypes = [i, i, i, i, i, i, vp, i] + [vp] * 10 + [vp, sz, vp]
+    L.ssm_scan_fwd_ex.restype = i
+    L.ssm_step_ex.argtypes = [i, i, i, i, i, vp, i] + [fp] + [vp] * 8 + [vp]
+    L.ssm_step_ex.restype = i
     L.ssm_scan_bwd_workspace_size.argtypes, L.ssm_scan_bwd_workspace_size.restype = [i, i, i, i], sz
     L.ssm_scan_bwd.argtypes = [i, i, i, i, i] + [vp] * 18 + [vp, sz, vp]
     L.ssm_scan_bwd.restype = i
@@ -101,10 +105,27 @@ def ssm_scan_workspace_size(B, L, D, N):
     return int(lib().ssm_scan_workspace_size(B, L, D, N))
 
 
+SSM_DISC = {"euler": 0, "zoh": 1}
+
+
 def ssm_scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, y=None, h_final=None,
                  workspace=None, stream=None, want_final_state=True):
     """Mamba-1 selective scan. x, delta, z: [B, L, D]; Bm, Cm: [B, L, N] (bf16 or fp32);
     A: [D, N], D: [D], h0: [B, D, N] fp32. Returns (y, h_final) (h_final None if not wanted)."""
+    return _scan_fwd("ssm_scan_fwd", x, delta, A, Bm, Cm, D, z, h0, y, h_final, workspace, stream,
+                     want_final_state, None)
+
+
+def ssm_scan_fwd_ex(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, disc="euler", delta_bias=None,
+                    delta_softplus=False, y=None, h_final=None, workspace=None, stream=None,
+                    want_final_state=True):
+    """``ssm_scan_fwd`` with disc = "euler" | "zoh" (exact zero-order hold) and
+    Delta = [softplus](delta + delta_bias) inside the kernels (delta_bias: [D] fp32)."""
+    return _scan_fwd("ssm_scan_fwd_ex", x, delta, A, Bm, Cm, D, z, h0, y, h_final, workspace, stream,
+                     want_final_state, (SSM_DISC[disc], delta_bias, bool(delta_softplus)))
+
+
+def _scan_fwd(fn, x, delta, A, Bm, Cm, D, z, h0, y, h_final, workspace, stream, want_final_state, ex):
     Bb, L, Dd = x.shape
     N = A.shape[1]
     dev, io = x.device, x.dtype
@@ -126,11 +147,16 @@ def ssm_scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, y=None, h_fina
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().ssm_scan_fwd(Bb, L, Dd, N, _io_code(x), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
-                            _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final),
-                            _ptr(workspace), wbytes, _stream(dev, stream))
+    args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+            _ptr(h_final), _ptr(workspace), wbytes, _stream(dev, stream))
+    if ex is None:
+        st = lib().ssm_scan_fwd(Bb, L, Dd, N, _io_code(x), *args)
+    else:
+        disc, bias, sp = ex
+        _check(bias, "delta_bias", (Dd,), torch.float32, dev, required=False)
+        st = lib().ssm_scan_fwd_ex(Bb, L, Dd, N, _io_code(x), disc, _ptr(bias), int(sp), *args)
     if st != SSM_OK:
-        _raise("ssm_scan_fwd", st)
+        _raise(fn, st)
     return y, h_final
 
 
@@ -226,6 +252,17 @@ def ssm_ssd_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, chunk=0, y=None
 def ssm_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=None):
     """One decode step. state: [B, D, N] fp32 (updated in place); x, delta, z: [B, D];
     Bm, Cm: [B, N]; A: [D, N]; D: [D]. Returns y [B, D]."""
+    return _step("ssm_step", state, x, delta, A, Bm, Cm, D, z, y, stream, None)
+
+
+def ssm_step_ex(state, x, delta, A, Bm, Cm, D=None, z=None, *, disc="euler", delta_bias=None,
+                delta_softplus=False, y=None, stream=None):
+    """``ssm_step`` with the options of ``ssm_scan_fwd_ex``."""
+    return _step("ssm_step_ex", state, x, delta, A, Bm, Cm, D, z, y, stream,
+                 (SSM_DISC[disc], delta_bias, bool(delta_softplus)))
+
+
+def _step(fn, state, x, delta, A, Bm, Cm, D, z, y, stream, ex):
     Bb, Dd, N = state.shape
     dev, io = x.device, x.dtype
     _check(state, "state", (Bb, Dd, N), torch.float32, dev)
@@ -239,10 +276,16 @@ def ssm_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=None)
     if y is None:
         y = torch.empty((Bb, Dd), dtype=io, device=dev)
     _check(y, "y", (Bb, Dd), io, dev)
-    st = lib().ssm_step(Bb, Dd, N, _io_code(x), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
-                        _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream(dev, stream))
+    args = (_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y),
+            _stream(dev, stream))
+    if ex is None:
+        st = lib().ssm_step(Bb, Dd, N, _io_code(x), *args)
+    else:
+        disc, bias, sp = ex
+        _check(bias, "delta_bias", (Dd,), torch.float32, dev, required=False)
+        st = lib().ssm_step_ex(Bb, Dd, N, _io_code(x), disc, _ptr(bias), int(sp), *args)
     if st != SSM_OK:
-        _raise("ssm_step", st)
+        _raise(fn, st)
     return y
 
 

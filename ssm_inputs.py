@@ -123,6 +123,16 @@ def scan_inputs(B, L, D, N, dtype=BF16, seed=0, with_D=True, with_z=True, with_h
     return out
 
 
+def scan_raw_delta(B, L, D, dtype=BF16, seed=0):
+    """Delta before its softplus, for the kernels that apply softplus(delta + bias)
+    themselves: delta = 0.5 eps [B,L,D] in ``dtype`` and delta_bias = ln(expm1(dt_c))
+    [D] float32, so softplus(delta + delta_bias) has the distribution of ``scan_inputs``'
+    Delta (the same eps and dt_c streams)."""
+    eps = _normal(seed, TID_EPS, (B, L, D))
+    return dict(delta=store(0.5 * eps, dtype),
+                delta_bias=np.log(np.expm1(_dt_per_channel(seed, D))).astype(np.float32))
+
+
 def scan_grad_inputs(B, L, D, N, dtype=BF16, seed=0, with_dh_final=True):
     """Cotangents for the backward pass of the Mamba-1 scan: dy [B,L,D] in
     ``dtype`` and dh_final [B,D,N] in float32 (None when not wanted)."""
@@ -195,6 +205,8 @@ WORKLOADS = {
     # sweep's shape (batch 8, d_model 256 -> 512 channels, 32K tokens)
     "scan_bwd_bf16_B1_L4096_D1536_N16": dict(kind="scan_bwd", B=1, L=4096, D=1536, N=16, dtype=BF16),
     "scan_bwd_bf16_B8_L32768_D512_N16": dict(kind="scan_bwd", B=8, L=32768, D=512, N=16, dtype=BF16),
+    # the headline layer with exact zero-order hold and softplus(delta + bias) in the kernel
+    "scan_zoh_softplus_bf16_B1_L4096_D1536_N16": dict(kind="scan_var", B=1, L=4096, D=1536, N=16, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q256": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,
                                                 chunk=256, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q64": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,

@@ -152,3 +152,31 @@ def test_scan_bwd_workspace_size():
     assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 16) > 0
     assert ssa.ssm_scan_bwd_workspace_size(1, 0, 1536, 16) == 0
     assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 32) == 0  # unsupported N
+
+
+def _scan_ex(disc=1, bias=None, sp=1, N=16, **kw):
+    a = dict(B=1, L=64, D=64, io=1, x=P, delta=P, A=P, Bm=P, Cm=P, y=P)
+    a.update(kw)
+    return ops.lib().ssm_scan_fwd_ex(a["B"], a["L"], a["D"], N, a["io"], disc, bias, sp, a["x"], a["delta"],
+                                     a["A"], a["Bm"], a["Cm"], None, None, None, a["y"], None, None, 0, None)
+
+
+# one defect per case, so no call reaches a launch
+@pytest.mark.parametrize("kw,status", [
+    (dict(disc=2), 1), (dict(disc=-1), 1), (dict(N=64), 2), (dict(N=256, disc=0, sp=1), 2),
+    (dict(bias=ctypes.c_void_p(0x10004)), 1), (dict(x=None), 1), (dict(B=0), 1),
+])
+def test_scan_fwd_ex_rejects_bad_arguments(kw, status):
+    assert _scan_ex(**kw) == status
+    assert ops.lib().ssm_last_error().startswith(b"ssm_scan_fwd_ex: ")
+
+
+def test_step_ex_rejects_bad_arguments():
+    L = ops.lib()
+    def call(disc=1, bias=None, N=16, state=P):
+        return L.ssm_step_ex(2, 64, N, 1, disc, bias, 1, state, P, P, P, P, P, None, None, P, None)
+    assert call(disc=3) == 1
+    assert call(N=12) == 2
+    assert call(state=None) == 1
+    assert call(bias=ctypes.c_void_p(0x10008)) == 1
+    assert ops.lib().ssm_last_error().startswith(b"ssm_step_ex: ")
