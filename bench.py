@@ -165,23 +165,38 @@ def time_calls(call, sets, steps, warmup, n_kernels):
     return total_ms, ker
 
 
-def committed_traffic(kernel_source, summary):
-    """HBM bytes per launch (or per call), from a committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary under profiles/ -- only while the kernel source
-    is byte-identical to the one the counters were taken on."""
+# Sources each kernel is compiled from, in the order their bytes are hashed.
+KERNEL_SOURCES = {
+    "scan": ("scan_core.h", "scan_fwd.hip", "common.h", "launch.h"),
+    "scan_bwd": ("scan_bwd.hip", "common.h", "launch.h"),
+    "ssd": ("ssd_fwd.hip", "common.h", "launch.h"),
+}
+
+
+def sources_sha256(kind):
+    """SHA-256 of the concatenated bytes of a kernel's sources (KERNEL_SOURCES)."""
     import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "selective_scan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(kind, summary):
+    """HBM bytes per launch (or per call), from a committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary under profiles/ -- only while the kernel's
+    sources are byte-identical to the ones the counters were taken on."""
     import re
     path = os.path.join(ROOT, "profiles", summary)
-    src = os.path.join(ROOT, "selective_scan_amd", "csrc", kernel_source)
-    if not (os.path.exists(path) and os.path.exists(src)):
+    if not os.path.exists(path):
         return None
     text = open(path).read()
     m_b = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
-    m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_h = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
     if not (m_b and m_h):
         return None
-    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return int(m_b.group(1)) if cur == m_h.group(1) else None
+    return int(m_b.group(1)) if sources_sha256(kind) == m_h.group(1) else None
 
 
 def scan_bench(name, wl, steps, warmup, dev):
@@ -204,7 +219,7 @@ def scan_bench(name, wl, steps, warmup, dev):
     achieved = SLOTS_PER_UPDATE * upd / tdom / 1e12
     peak = LANE_SLOTS_PER_S / 1e12
     res["roofline"] = dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s",
-                           frac=achieved / peak, traffic=committed_traffic("scan_fwd.hip", f"traffic_{name}.md"),
+                           frac=achieved / peak, traffic=committed_traffic("scan", f"traffic_{name}.md"),
                            kernel="segment_final" if nk > 1 else "segment")
     res["hbm_roofline_dominant"] = dict(achieved=alg / tdom / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
                                         frac=alg / tdom / 1e9 / HBM_PEAK_GBS)
@@ -343,7 +358,7 @@ def scan_bwd_bench(name, wl, steps, warmup, dev, max_sets=8):
                 hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 sets=len(sets), alg_bytes=alg,
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
-                              traffic=committed_traffic("scan_bwd.hip", f"traffic_{name}.md"),
+                              traffic=committed_traffic("scan_bwd", f"traffic_{name}.md"),
                               kernel="bwd_final"))
 
 
@@ -395,7 +410,7 @@ def ssd_bench(name, wl, steps, warmup, dev, max_sets=3):
                 mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                 roofline=dict(bound="hbm", achieved=byt / (ms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              traffic=committed_traffic("ssd_fwd.hip", f"ssd_kernels_{name[4:]}.md"),
+                              traffic=committed_traffic("ssd", f"ssd_kernels_{name[4:]}.md"),
                               kernel="whole call (three kernels)"),
                 dominant_kernel_ms=tdom * 1e3, alg_bytes=byt, alg_flops=fl)
 
