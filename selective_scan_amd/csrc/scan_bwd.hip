@@ -51,9 +51,12 @@ constexpr int kBwdMinSegment = SSM_BWD_MIN_SEGMENT;
 constexpr int kBwdMaxGroup = 4;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Steps per sub-block: the final pass keeps K x N recomputed states per lane, and
-// the four per-step input streams of a sub-block, so K stays small.
+// Steps between checkpoints (K), and steps whose states the final pass keeps in
+// VGPRs at a time (KR): a K-step block runs as K/KR halves, the later half first,
+// each recomputed from the block's checkpoint (the later half re-runs the steps
+// before it: half a block of extra recurrence, instead of twice the checkpoints).
 __host__ __device__ constexpr int sub_len(int N) { return N > 0 ? 4 : 4; }
+constexpr int KR = 2;
 
 struct BGeom {
     int Ls;    // steps per segment (a multiple of K)
@@ -611,6 +614,13 @@ bwd_final(BwdArgs a, BGeom g) {
             for (int n = 0; n < N; ++n) c[n] = __builtin_fmaf(exp2_fast(A2[n] * csb), rg[n], Eb[n]);
         }
         const float Dv = HAS_D ? a.Dskip[dc] : 0.0f;
+        // parking slot for a block's entering state: this wave's dA slot, which the
+        // wave itself writes only after its last block; the segment's entering
+        // state lives in LDS too (read once per block)
+        float* lhe = lds + wave * N * 64;
+        float* lhin = lds + W * (N + 1) * 64 + wave * N * 64;
+#pragma unroll
+        for (int n = 0; n < N; ++n) lhin[n * 64 + lane] = hin[n];
 
         SegIO<BF16> X, Dl, Z, DY, DX, DDL, DZ;
         X.init(a.x, row0, len, D);
@@ -654,93 +664,129 @@ bwd_final(BwdArgs a, BGeom g) {
                 dyv[k] = widen<BF16>(gq[k]);
                 zv[k] = HAS_Z ? widen<BF16>(zq[k]) : 0.0f;
             }
-            if (j > 0) {
+            // the block's entering state, from its checkpoint; parked in this wave's LDS
+            // slot while the block's later half runs
+            {
+                float he[N];
+                if (j == 0) {
 #pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const uint32_t so = (uint32_t)((j - 1) * K + k) * rstride;
-                    dq[k] = load_raw<BF16>(Dl.r, voff, so);
-                    xq[k] = load_raw<BF16>(X.r, voff, so);
-                    gq[k] = load_raw<BF16>(DY.r, voff, so);
-                    if constexpr (HAS_Z) zq[k] = load_raw<BF16>(Z.r, voff, so);
-                }
-            }
-            // the sub-block's entering state
-            float h[N];
-            if (j == 0) {
-#pragma unroll
-                for (int n = 0; n < N; ++n) h[n] = hin[n];
-            } else {
-                const size_t ck = ((size_t)b * g.S + s) * c1 + (j - 1);
-                const float* hz = ws + wl.HZ + ck * N * D + dc;
-                const float cz = ws[wl.CZ + ck * D + dc];
-#pragma unroll
-                for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cz), hin[n], hz[(size_t)n * D]);
-            }
-            // forward over the sub-block: keep the states; dz, dD and dC
-            float hs[K][N], dv[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int t = j * K + k;
-                const Row<N, BF16> Bt = Bn, Ct = Cn;
-                const int tn = min(k + 1 < K ? t + 1 : j * K + K - 1, len - 1);
-                Bn.load(Bbase, tn, rw);
-                Cn.load(Cbase, tn, rw);
-                const float u = dl[k] * xv[k];
-                float v0 = 0.0f, v1 = 0.0f;
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    h[n] = __builtin_fmaf(exp2_fast(dl[k] * A2[n]), h[n], u * Bt.at(n));
-                    hs[k][n] = h[n];
-                    if (n & 1) v1 = __builtin_fmaf(Ct.at(n), h[n], v1);
-                    else v0 = __builtin_fmaf(Ct.at(n), h[n], v0);
-                }
-                float v = v0 + v1;
-                if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv[k], v);
-                if constexpr (HAS_Z) {
-                    const float sg = rcp_fast(1.0f + exp2_fast(-zv[k] * kLog2e));
-                    dv[k] = dyv[k] * zv[k] * sg;
-                    const float dzv = dyv[k] * v * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
-                    store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, dzv);
+                    for (int n = 0; n < N; ++n) he[n] = lhin[n * 64 + lane];
                 } else {
-                    dv[k] = dyv[k];
-                }
-                if constexpr (HAS_D) dD = __builtin_fmaf(dv[k], xv[k], dD);
-                const float dvm = d < D ? dv[k] : 0.0f;
-                float w[16];
+                    const size_t ck = ((size_t)b * g.S + s) * c1 + (j - 1);
+                    const float* hz = ws + wl.HZ + ck * N * D + dc;
+                    const float cz = ws[wl.CZ + ck * D + dc];
 #pragma unroll
-                for (int n = 0; n < N; ++n) w[n] = dvm * h[n];
-                const float tot = lane_reduce<N>(w, lane);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPC, (int)poff, (int)(t * N * 4), 0);
+                    for (int n = 0; n < N; ++n)
+                        he[n] = __builtin_fmaf(exp2_fast(A2[n] * cz), lhin[n * 64 + lane], hz[(size_t)n * D]);
+                }
+#pragma unroll
+                for (int n = 0; n < N; ++n) lhe[n * 64 + lane] = he[n];
             }
-            // backward over the sub-block
+            // the block in halves of KR steps, the later half first
 #pragma unroll
-            for (int k = K - 1; k >= 0; --k) {
-                const int t = j * K + k;
-                const Row<N, BF16> Bt = Bn, Ct = Cn;
-                const int tn = k > 0 ? min(t - 1, len - 1) : min(max(j - 1, 0) * K, len - 1);
-                Bn.load(Bbase, tn, rw);
-                Cn.load(Cbase, tn, rw);
-                const float u = dl[k] * xv[k];
-                const float um = d < D ? u : 0.0f;
-                float sA = 0.0f, sB = 0.0f;
-                float w[16];
+            for (int half = K / KR - 1; half >= 0; --half) {
+                const int k0 = half * KR;
+                // the halves do not share registers: keep the scheduler from hoisting the
+                // earlier half's work into the later one
+                __builtin_amdgcn_sched_barrier(0);
+                if (half == 0 && j > 0) {
+                    // the next block's inputs, loaded while the earlier half runs
 #pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float gg = __builtin_fmaf(dv[k], Ct.at(n), c[n]);  // dl/dh_t
-                    const float ah = __builtin_fmaf(-u, Bt.at(n), hs[k][n]);  // a_t h_{t-1}
-                    const float q = gg * ah;
-                    sA = __builtin_fmaf(q, A2[n], sA);
-                    dA[n] = __builtin_fmaf(q, dl[k], dA[n]);
-                    sB = __builtin_fmaf(gg, Bt.at(n), sB);
-                    w[n] = gg * um;
-                    c[n] = exp2_fast(dl[k] * A2[n]) * gg;
+                    for (int k = 0; k < K; ++k) {
+                        const uint32_t so = (uint32_t)((j - 1) * K + k) * rstride;
+                        dq[k] = load_raw<BF16>(Dl.r, voff, so);
+                        xq[k] = load_raw<BF16>(X.r, voff, so);
+                        gq[k] = load_raw<BF16>(DY.r, voff, so);
+                        if constexpr (HAS_Z) zq[k] = load_raw<BF16>(Z.r, voff, so);
+                    }
                 }
-                const float dxv = __builtin_fmaf(dl[k], sB, HAS_D ? dv[k] * Dv : 0.0f);
-                const float ddv = __builtin_fmaf(sA, kLn2, xv[k] * sB);
-                store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, dxv);
-                store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, ddv);
-                const float tot = lane_reduce<N>(w, lane);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPB, (int)poff, (int)(t * N * 4), 0);
+                float h[N];
+#pragma unroll
+                for (int n = 0; n < N; ++n) h[n] = lhe[n * 64 + lane];
+                // the block's steps before this half: the recurrence only
+#pragma unroll
+                for (int k = 0; k < k0; ++k) {
+                    const int t = j * K + k;
+                    const Row<N, BF16> Bt = Bn;
+                    Bn.load(Bbase, min(t + 1, len - 1), rw);
+                    Cn.load(Cbase, min(t + 1, len - 1), rw);
+                    // opaque copies: this replay's exponentials are recomputed, not kept in
+                    // registers for the earlier half that uses the same steps
+                    float dlk = dl[k], xvk = xv[k];
+                    asm volatile("" : "+v"(dlk), "+v"(xvk));
+                    const float u = dlk * xvk;
+#pragma unroll
+                    for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(dlk * A2[n]), h[n], u * Bt.at(n));
+                }
+                // forward over the half: keep its states; dz, dD and dC
+                float hs[KR][N], dv[KR];
+#pragma unroll
+                for (int kk = 0; kk < KR; ++kk) {
+                    const int k = k0 + kk, t = j * K + k;
+                    const Row<N, BF16> Bt = Bn, Ct = Cn;
+                    const int tn = min(kk + 1 < KR ? t + 1 : j * K + k0 + KR - 1, len - 1);
+                    Bn.load(Bbase, tn, rw);
+                    Cn.load(Cbase, tn, rw);
+                    const float u = dl[k] * xv[k];
+                    float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        h[n] = __builtin_fmaf(exp2_fast(dl[k] * A2[n]), h[n], u * Bt.at(n));
+                        hs[kk][n] = h[n];
+                        if (n & 1) v1 = __builtin_fmaf(Ct.at(n), h[n], v1);
+                        else v0 = __builtin_fmaf(Ct.at(n), h[n], v0);
+                    }
+                    float v = v0 + v1;
+                    if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv[k], v);
+                    if constexpr (HAS_Z) {
+                        const float sg = rcp_fast(1.0f + exp2_fast(-zv[k] * kLog2e));
+                        dv[kk] = dyv[k] * zv[k] * sg;
+                        const float dzv = dyv[k] * v * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
+                        store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, dzv);
+                    } else {
+                        dv[kk] = dyv[k];
+                    }
+                    if constexpr (HAS_D) dD = __builtin_fmaf(dv[kk], xv[k], dD);
+                    const float dvm = d < D ? dv[kk] : 0.0f;  // lanes past D add nothing
+                    float w[16];
+#pragma unroll
+                    for (int n = 0; n < N; ++n) w[n] = dvm * h[n];
+                    const float tot = lane_reduce<N>(w, lane);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPC, (int)poff, (int)(t * N * 4), 0);
+                }
+                // backward over the half
+#pragma unroll
+                for (int kk = KR - 1; kk >= 0; --kk) {
+                    const int k = k0 + kk, t = j * K + k;
+                    const Row<N, BF16> Bt = Bn, Ct = Cn;
+                    // next: the step before, else the block's first step (earlier half to
+                    // come) or the previous block's first step
+                    const int tn = kk > 0 ? min(t - 1, len - 1)
+                                          : min(half > 0 ? j * K : max(j - 1, 0) * K, len - 1);
+                    Bn.load(Bbase, tn, rw);
+                    Cn.load(Cbase, tn, rw);
+                    const float u = dl[k] * xv[k];
+                    const float um = d < D ? u : 0.0f;  // lanes past D add nothing
+                    float sA = 0.0f, sB = 0.0f;
+                    float w[16];
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        const float gg = __builtin_fmaf(dv[kk], Ct.at(n), c[n]);  // dl/dh_t
+                        const float ah = __builtin_fmaf(-u, Bt.at(n), hs[kk][n]);  // a_t h_{t-1}
+                        const float q = gg * ah;
+                        sA = __builtin_fmaf(q, A2[n], sA);
+                        dA[n] = __builtin_fmaf(q, dl[k], dA[n]);
+                        sB = __builtin_fmaf(gg, Bt.at(n), sB);
+                        w[n] = gg * um;
+                        c[n] = exp2_fast(dl[k] * A2[n]) * gg;
+                    }
+                    const float dxv = __builtin_fmaf(dl[k], sB, HAS_D ? dv[kk] * Dv : 0.0f);
+                    const float ddv = __builtin_fmaf(sA, kLn2, xv[k] * sB);
+                    store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, dxv);
+                    store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, ddv);
+                    const float tot = lane_reduce<N>(w, lane);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPB, (int)poff, (int)(t * N * 4), 0);
+                }
             }
         }
         if (s == 0 && a.dh0 != nullptr && d < D) {
@@ -861,7 +907,7 @@ hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
     const dim3 grid(g.G, (a.D + 63) / 64, a.B);
     const dim3 block(64 * g.W);
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
-    const size_t lds_fin = (size_t)g.W * (N + 1) * 64 * sizeof(float);
+    const size_t lds_fin = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     float* ws = static_cast<float*>(a.ws);
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, N, g);
     if (g.S > 1 || g.nsub > 1) launch((bwd_state_aggregate<N, BF16>), grid, block, (uint32_t)lds_agg, st, a, g);

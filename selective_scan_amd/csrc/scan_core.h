@@ -47,7 +47,7 @@ namespace {
 #define SSM_SCAN_PREFETCH 8
 #endif
 #ifndef SSM_SCAN_TARGET_WAVES
-#define SSM_SCAN_TARGET_WAVES 4096
+#define SSM_SCAN_TARGET_WAVES 5120
 #endif
 #ifndef SSM_SCAN_MIN_SEGMENT
 #define SSM_SCAN_MIN_SEGMENT 32
