@@ -483,10 +483,11 @@ bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ 
     const float* P = dec + (size_t)b * (G - 1) * st + (size_t)n * D + dc;
     const int steps = G - 1, per = (steps + 3) / 4;
     const int p0 = min(q * per, steps), p1 = min(p0 + per, steps);
-    constexpr int U = 8;  // loads in flight
+    constexpr int U = 16;  // a quarter of at most U slots stays in registers
+    float pv[U], hv[U];
     float cp = 1.0f, ch = 0.0f;  // composite of this quarter
+    const bool in_regs = per <= U;  // uniform
     for (int k0 = p0; k0 < p1; k0 += U) {
-        float pv[U], hv[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int pc = min(k0 + k, p1 - 1);
@@ -509,13 +510,14 @@ bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ 
     for (int j = 0; j < q; ++j) x = __builtin_fmaf(sP[j][lane], x, sH[j][lane]);
     if (d >= D) return;
     for (int k0 = p0; k0 < p1; k0 += U) {
-        float pv[U], hv[U];
+        if (!in_regs) {
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int pc = min(k0 + k, p1 - 1);
-            const size_t slot = (size_t)(REV ? steps - 1 - pc : pc) * st;
-            pv[k] = P[slot];
-            hv[k] = H[slot];
+            for (int k = 0; k < U; ++k) {
+                const int pc = min(k0 + k, p1 - 1);
+                const size_t slot = (size_t)(REV ? steps - 1 - pc : pc) * st;
+                pv[k] = P[slot];
+                hv[k] = H[slot];
+            }
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {

@@ -20,8 +20,8 @@
 //      state H_s, decay P_s = exp(A sum Delta)); the group's waves then form, in
 //      LDS, each segment's exclusive in-group prefix E_s (and the in-group prefix
 //      of sum Delta), and the last wave the group's own aggregate (GP_g, GH_g).
-//   2. group_carry: per (batch, channel, state index) a short sequential pass
-//      over the groups gives the state entering each group (linear in groups).
+//   2. group_carry: per (batch, channel, state index) the state entering each
+//      group, from the groups' aggregates (a two-level walk over the groups).
 //   3. segment_final: each wave forms its segment's carried-in state
 //      h_in = exp(A * prefix sum Delta) h_group + E_s and runs the recurrence
 //      again from it, writing y (and h_final at the end of the sequence).
@@ -435,33 +435,61 @@ segment_aggregate(ScanArgs a, Geom g) {
 }
 
 // state entering each group: carry(0) = h0, carry(g+1) = GP_g carry(g) + GH_g,
-// written over GH_g; one thread per (batch, state index, channel)
+// written over GH_g. Workgroup of 64 channels x 4 quarters of the G-1 groups:
+// each thread composes its quarter's affine maps, the quarters' composites are
+// chained in LDS, then each thread walks its quarter again from its entering state.
 __global__ void __launch_bounds__(256)
 group_carry(const float* __restrict__ h0, float* ws, int B, int D, int N, Geom g) {
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (size_t)B * N * D) return;
-    const int d = (int)(idx % D);
-    const int n = (int)((idx / D) % N);
-    const int b = (int)(idx / ((size_t)D * N));
+    __shared__ float sP[4][64], sH[4][64];
+    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int d = blockIdx.x * 64 + lane, n = blockIdx.y, b = blockIdx.z;
+    const int dc = d < D ? d : D - 1;
     const WsLayout wl = ws_layout(B, D, N, g.S, g.G);
-    float* GH = ws + wl.GH + (size_t)b * (g.G - 1) * N * D + (size_t)n * D + d;
-    const float* GP = ws + wl.GP + (size_t)b * (g.G - 1) * N * D + (size_t)n * D + d;
     const size_t st = (size_t)N * D;
-    float h = h0 ? h0[((size_t)b * D + d) * N + n] : 0.0f;
-    constexpr int U = 16;
-    for (int k0 = 0; k0 < g.G - 1; k0 += U) {
-        float p[U], q[U];
+    float* GH = ws + wl.GH + (size_t)b * (g.G - 1) * st + (size_t)n * D + dc;
+    const float* GP = ws + wl.GP + (size_t)b * (g.G - 1) * st + (size_t)n * D + dc;
+    const int steps = g.G - 1, per = (steps + 3) / 4;
+    const int k0 = min(q * per, steps), k1 = min(k0 + per, steps);
+    constexpr int U = 16;  // a quarter of at most U groups stays in registers
+    float p[U], v[U];
+    float cp = 1.0f, ch = 0.0f;
+    const bool in_regs = per <= U;  // uniform
+    for (int k = k0; k < k1; k += U) {
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int kk = min(k0 + k, g.G - 2);
-            p[k] = GP[kk * st];
-            q[k] = GH[kk * st];
+        for (int u = 0; u < U; ++u) {
+            const int kk = min(k + u, k1 - 1);
+            p[u] = GP[kk * st];
+            v[u] = GH[kk * st];
         }
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (k0 + k >= g.G - 1) break;
-            h = __builtin_fmaf(p[k], h, q[k]);
-            GH[(k0 + k) * st] = h;
+        for (int u = 0; u < U; ++u) {
+            if (k + u < k1) {
+                ch = __builtin_fmaf(p[u], ch, v[u]);
+                cp *= p[u];
+            }
+        }
+    }
+    sP[q][lane] = cp;
+    sH[q][lane] = ch;
+    __syncthreads();
+    float h = h0 ? h0[((size_t)b * D + dc) * N + n] : 0.0f;
+    for (int j = 0; j < q; ++j) h = __builtin_fmaf(sP[j][lane], h, sH[j][lane]);
+    if (d >= D) return;
+    for (int k = k0; k < k1; k += U) {
+        if (!in_regs) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int kk = min(k + u, k1 - 1);
+                p[u] = GP[kk * st];
+                v[u] = GH[kk * st];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (k + u < k1) {
+                h = __builtin_fmaf(p[u], h, v[u]);
+                GH[(k + u) * st] = h;
+            }
         }
     }
 }
@@ -574,9 +602,8 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     if (g.S > 1) launch((segment_aggregate<N, BF16>), grid, block, lds_agg, st, a, g);
     if (g.G > 1) {
-        const size_t tot = (size_t)a.B * a.N * a.D;
-        launch(group_carry, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a.h0,
-               static_cast<float*>(a.ws), a.B, a.D, a.N, g);
+        launch(group_carry, dim3((unsigned)((a.D + 63) / 64), (unsigned)a.N, (unsigned)a.B), dim3(256), 0, st,
+               a.h0, static_cast<float*>(a.ws), a.B, a.D, a.N, g);
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     if (nch > 1) {
@@ -614,9 +641,8 @@ hipError_t launch_var(const ScanArgs& a, hipStream_t st) {
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     if (g.S > 1) launch((segment_aggregate<N, BF16, V>), grid, block, lds_agg, st, a, g);
     if (g.G > 1) {
-        const size_t tot = (size_t)a.B * a.N * a.D;
-        launch(group_carry, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a.h0,
-               static_cast<float*>(a.ws), a.B, a.D, a.N, g);
+        launch(group_carry, dim3((unsigned)((a.D + 63) / 64), (unsigned)a.N, (unsigned)a.B), dim3(256), 0, st,
+               a.h0, static_cast<float*>(a.ws), a.B, a.D, a.N, g);
     }
     if (a.z != nullptr) launch((segment_final<N, BF16, true, true, false, V>), grid, block, 0, st, a, g);
     else launch((segment_final<N, BF16, false, true, false, V>), grid, block, 0, st, a, g);

@@ -67,7 +67,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTargetBlocks = 768;  // workgroups of the scan kernel
+#ifndef SSM_SSD_TARGET_BLOCKS
+#define SSM_SSD_TARGET_BLOCKS 768
+#endif
+constexpr int kTargetBlocks = SSM_SSD_TARGET_BLOCKS;  // workgroups of the scan kernel
 constexpr int kP = 64;              // head dim handled
 constexpr int kMaxQ = 256;          // longest chunk
 constexpr int kXS = kP + 16;        // LDS row stride (elements) of x rows
