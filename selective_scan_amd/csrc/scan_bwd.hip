@@ -16,21 +16,21 @@
 // its N states; B_t and C_t are wave-uniform rows in SGPRs. The sequence is cut
 // into segments (one wave each, W waves per workgroup), and both recurrences are
 // affine maps of their state, so segments compose:
-//   1. bwd_state_aggregate: each segment from a zero state; in-group prefixes in
-//      LDS (forward carries, as in the forward pass), plus the zero-start state
-//      and the partial sum of Delta at every sub-block boundary (checkpoints).
-//   2. carry_forward: the state entering each group.
-//   3. bwd_adjoint_aggregate: each segment's adjoint from a zero start at its
-//      right end, in-group suffixes in LDS, group aggregates.
-//   4. carry_backward: the adjoint entering each group from the right.
-//   5. bwd_final: per segment, sub-blocks of K steps from the last to the first.
+//   1. bwd_aggregate: one forward sweep per segment gives the state from a zero
+//      start (with the zero-start state and partial sum of Delta at every
+//      checkpoint boundary) and the adjoint the segment passes left from a zero
+//      start at its right end (a forward-order sum over a running product of the
+//      same decays); in-group prefixes (state) and suffixes (adjoint) in LDS.
+//   2. bwd_carry<false>: the state entering each group.
+//   3. bwd_carry<true>: the adjoint entering each group from the right.
+//   4. bwd_final: per segment, blocks of K steps from the last to the first.
 //      A sub-block's entering state is rebuilt from its checkpoint and the
 //      segment's carried-in state, the K states are recomputed forwards and kept
 //      in VGPRs (K*N of them), then the adjoint walks the K steps backwards. The
 //      per-step sums over channels (dB, dC) are reduced across the 64 lanes by a
 //      transpose-reduce (permlane swaps and DPP, no LDS) and stored as fp32
 //      partials per 64-channel block; dA and dD are summed per workgroup.
-//   6. bwd_reduce_params / bwd_reduce_rows: add the partials, round dB and dC to
+//   5. bwd_reduce_params / bwd_reduce_rows: add the partials, round dB and dC to
 //      the io type.
 #include "common.h"
 #include "launch.h"
@@ -236,13 +236,22 @@ struct SegCtx {
     uint32_t voff, rstride;
 };
 
-// ------------------------------------------------ 1. forward aggregate + checkpoints
-template <int N, bool BF16>
+// ------------------------------------------------ 1. segment aggregates + checkpoints
+// One forward sweep per segment gives both aggregates the carries need:
+//  - the state from a zero start, with the zero-start state and partial sum(Delta)
+//    at every checkpoint boundary;
+//  - the adjoint the segment passes to its left from a zero start at its right end,
+//    sum_s (prod_{k=t0..s} a_k) dv_s C_s: a forward-order sum over a running
+//    product of the same decays, so no second pass over the segment is needed.
+// Then the group's waves form, in LDS, each segment's exclusive in-group prefix
+// (state) and suffix (adjoint), and the groups' own aggregates.
+template <int N, bool BF16, bool HAS_Z>
 __global__ void __launch_bounds__(64 * kBwdMaxGroup)
-bwd_state_aggregate(BwdArgs a, BGeom g) {
+bwd_aggregate(BwdArgs a, BGeom g) {
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
     constexpr uint32_t es = BF16 ? 2 : 4;
+    constexpr int rw = BF16 ? N / 2 : N;
     const int W = g.W;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
@@ -254,36 +263,46 @@ bwd_state_aggregate(BwdArgs a, BGeom g) {
     float* ws = static_cast<float*>(a.ws);
     const size_t c1 = g.nsub > 1 ? (size_t)(g.nsub - 1) : 0;
 
-    float A2[N], h[N];
+    float A2[N], h[N], pr[N], ga[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
         h[n] = 0.0f;
+        pr[n] = 1.0f;
+        ga[n] = 0.0f;
     }
     float sumd = 0.0f;
     if (len > 0) {
         const size_t row0 = (size_t)b * a.L + t0;
-        SegIO<BF16> X, Dl;
+        SegIO<BF16> X, Dl, DY, Z;
         X.init(a.x, row0, len, D);
         Dl.init(a.delta, row0, len, D);
+        DY.init(a.dy, row0, len, D);
+        Z.init(HAS_Z ? a.z : a.dy, row0, len, D);
         const uint32_t voff = (uint32_t)dc * es, rstride = (uint32_t)D * es;
         const void* Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
-        constexpr int rw = BF16 ? N / 2 : N;
+        const void* Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
         const int nsub = (len + K - 1) / K;
-        uint32_t dq[K], xq[K];
+        uint32_t dq[K], xq[K], gq[K], zq[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            dq[k] = load_raw<BF16>(Dl.r, voff, (uint32_t)k * rstride);
-            xq[k] = load_raw<BF16>(X.r, voff, (uint32_t)k * rstride);
+            const uint32_t so = (uint32_t)k * rstride;
+            dq[k] = load_raw<BF16>(Dl.r, voff, so);
+            xq[k] = load_raw<BF16>(X.r, voff, so);
+            gq[k] = load_raw<BF16>(DY.r, voff, so);
+            zq[k] = HAS_Z ? load_raw<BF16>(Z.r, voff, so) : 0u;
         }
-        Row<N, BF16> Bn;
+        Row<N, BF16> Bn, Cn;
         Bn.load(Bbase, 0, rw);
+        Cn.load(Cbase, 0, rw);
         for (int j = 0; j < nsub; ++j) {
-            float dv[K], xv[K];
+            float dv[K], xv[K], gv[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
                 dv[k] = widen<BF16>(dq[k]);
                 xv[k] = widen<BF16>(xq[k]);
+                gv[k] = widen<BF16>(gq[k]);  // dl/dv_t = dy_t silu(z_t)
+                if constexpr (HAS_Z) gv[k] *= silu(widen<BF16>(zq[k]));
             }
             if (j + 1 < nsub) {
 #pragma unroll
@@ -291,17 +310,25 @@ bwd_state_aggregate(BwdArgs a, BGeom g) {
                     const uint32_t so = (uint32_t)((j + 1) * K + k) * rstride;
                     dq[k] = load_raw<BF16>(Dl.r, voff, so);
                     xq[k] = load_raw<BF16>(X.r, voff, so);
+                    gq[k] = load_raw<BF16>(DY.r, voff, so);
+                    if constexpr (HAS_Z) zq[k] = load_raw<BF16>(Z.r, voff, so);
                 }
             }
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                const Row<N, BF16> Bt = Bn;
-                Bn.load(Bbase, min(j * K + k + 1, len - 1), rw);
+                const Row<N, BF16> Bt = Bn, Ct = Cn;
+                const int tn = min(j * K + k + 1, len - 1);
+                Bn.load(Bbase, tn, rw);
+                Cn.load(Cbase, tn, rw);
                 const float u = dv[k] * xv[k];
                 sumd += dv[k];
 #pragma unroll
-                for (int n = 0; n < N; ++n)
-                    h[n] = __builtin_fmaf(exp2_fast(dv[k] * A2[n]), h[n], u * Bt.at(n));
+                for (int n = 0; n < N; ++n) {
+                    const float ab = exp2_fast(dv[k] * A2[n]);
+                    h[n] = __builtin_fmaf(ab, h[n], u * Bt.at(n));
+                    pr[n] *= ab;
+                    ga[n] = __builtin_fmaf(pr[n], gv[k] * Ct.at(n), ga[n]);
+                }
             }
             if (j + 1 < nsub && d < D) {
                 float* hz = ws + wl.HZ + (((size_t)b * g.S + s) * c1 + j) * N * D + d;
@@ -311,7 +338,7 @@ bwd_state_aggregate(BwdArgs a, BGeom g) {
             }
         }
     }
-    if (g.S == 1) return;  // one segment: no carries
+    if (g.S == 1) return;  // one segment: no carries (uniform over the grid)
     // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]; a segment past L is the identity (1, 0)
     float* sP = lds;
     float* sH = sP + W * N * 64;
@@ -323,147 +350,66 @@ bwd_state_aggregate(BwdArgs a, BGeom g) {
     }
     sS[wave * 64 + lane] = sumd;
     __syncthreads();
+    // state: exclusive in-group prefix, and the group's aggregate (last wave)
     float E[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) E[n] = 0.0f;
     float cs = 0.0f;
-    for (int j = 0; j < wave; ++j) {
+    for (int jw = 0; jw < wave; ++jw) {
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            E[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], E[n], sH[(j * N + n) * 64 + lane]);
-        cs += sS[j * 64 + lane];
+            E[n] = __builtin_fmaf(sP[(jw * N + n) * 64 + lane], E[n], sH[(jw * N + n) * 64 + lane]);
+        cs += sS[jw * 64 + lane];
     }
-    if (d >= D || s >= g.S) return;
-    float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + d;
-#pragma unroll
-    for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
-    ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+    const bool live = d < D && s < g.S;
     const bool last_in_group = (wave == W - 1) || (s == g.S - 1);
-    if (last_in_group && grp < g.G - 1) {
-        float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + grp) * N * D + d;
-        float* GP = ws + wl.GP + ((size_t)b * (g.G - 1) + grp) * N * D + d;
+    if (live) {
+        float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + d;
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            GH[(size_t)n * D] = __builtin_fmaf(sP[(wave * N + n) * 64 + lane], E[n], h[n]);
-            GP[(size_t)n * D] = exp2_fast(A2[n] * (cs + sumd));
-        }
-    }
-}
-
-// ------------------------------------------------------------ 3. adjoint aggregate
-template <int N, bool BF16, bool HAS_Z>
-__global__ void __launch_bounds__(64 * kBwdMaxGroup)
-bwd_adjoint_aggregate(BwdArgs a, BGeom g) {
-    extern __shared__ float lds[];
-    constexpr int K = sub_len(N);
-    constexpr uint32_t es = BF16 ? 2 : 4;
-    const int W = g.W;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
-    const int d = blockIdx.y * 64 + lane, dc = d < D ? d : D - 1;
-    const int s = grp * W + wave;
-    const int t0 = s * g.Ls;
-    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
-    const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
-    float* ws = static_cast<float*>(a.ws);
-
-    float A2[N], c[N];
+        for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
+        ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+        if (last_in_group && grp < g.G - 1) {
+            float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + grp) * N * D + d;
+            float* GP = ws + wl.GP + ((size_t)b * (g.G - 1) + grp) * N * D + d;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
-        c[n] = 0.0f;
-    }
-    float sumd = 0.0f;
-    if (len > 0) {
-        const size_t row0 = (size_t)b * a.L + t0;
-        SegIO<BF16> Dl, DY, Z;
-        Dl.init(a.delta, row0, len, D);
-        DY.init(a.dy, row0, len, D);
-        Z.init(HAS_Z ? a.z : a.dy, row0, len, D);
-        const uint32_t voff = (uint32_t)dc * es, rstride = (uint32_t)D * es;
-        const void* Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
-        constexpr int rw = BF16 ? N / 2 : N;
-        const int nsub = (len + K - 1) / K;
-        uint32_t dq[K], gq[K], zq[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const uint32_t so = (uint32_t)((nsub - 1) * K + k) * rstride;
-            dq[k] = load_raw<BF16>(Dl.r, voff, so);
-            gq[k] = load_raw<BF16>(DY.r, voff, so);
-            zq[k] = HAS_Z ? load_raw<BF16>(Z.r, voff, so) : 0u;
-        }
-        Row<N, BF16> Cn;
-        Cn.load(Cbase, min(nsub * K - 1, len - 1), rw);
-        for (int j = nsub - 1; j >= 0; --j) {
-            float dl[K], dv[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                dl[k] = widen<BF16>(dq[k]);
-                dv[k] = widen<BF16>(gq[k]);
-                if constexpr (HAS_Z) dv[k] *= silu(widen<BF16>(zq[k]));
-            }
-            if (j > 0) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const uint32_t so = (uint32_t)((j - 1) * K + k) * rstride;
-                    dq[k] = load_raw<BF16>(Dl.r, voff, so);
-                    gq[k] = load_raw<BF16>(DY.r, voff, so);
-                    if constexpr (HAS_Z) zq[k] = load_raw<BF16>(Z.r, voff, so);
-                }
-            }
-#pragma unroll
-            for (int k = K - 1; k >= 0; --k) {
-                const int t = j * K + k;
-                const Row<N, BF16> Ct = Cn;
-                Cn.load(Cbase, max(min(t - 1, len - 1), 0), rw);
-                sumd += dl[k];
-#pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float gg = __builtin_fmaf(dv[k], Ct.at(n), c[n]);
-                    c[n] = exp2_fast(dl[k] * A2[n]) * gg;
-                }
+            for (int n = 0; n < N; ++n) {
+                GH[(size_t)n * D] = __builtin_fmaf(sP[(wave * N + n) * 64 + lane], E[n], h[n]);
+                GP[(size_t)n * D] = exp2_fast(A2[n] * (cs + sumd));
             }
         }
     }
-    // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]
-    float* sP = lds;
-    float* sH = sP + W * N * 64;
-    float* sS = sH + W * N * 64;
+    __syncthreads();  // every read of the state aggregates done
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        sP[(wave * N + n) * 64 + lane] = exp2_fast(A2[n] * sumd);
-        sH[(wave * N + n) * 64 + lane] = c[n];
-    }
-    sS[wave * 64 + lane] = sumd;
+    for (int n = 0; n < N; ++n) sH[(wave * N + n) * 64 + lane] = ga[n];
     __syncthreads();
-    // adjoint entering this segment from the segments to its right in the group
+    // adjoint: exclusive in-group suffix, and the group's aggregate (first wave)
     float Eb[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) Eb[n] = 0.0f;
     float csb = 0.0f;
-    for (int j = W - 1; j > wave; --j) {
+    for (int jw = W - 1; jw > wave; --jw) {
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            Eb[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], Eb[n], sH[(j * N + n) * 64 + lane]);
-        csb += sS[j * 64 + lane];
+            Eb[n] = __builtin_fmaf(sP[(jw * N + n) * 64 + lane], Eb[n], sH[(jw * N + n) * 64 + lane]);
+        csb += sS[jw * 64 + lane];
     }
-    if (d >= D || s >= g.S) return;
-    float* Ep = ws + wl.EB + ((size_t)b * g.S + s) * N * D + d;
+    if (!live) return;
+    float* Ebp = ws + wl.EB + ((size_t)b * g.S + s) * N * D + d;
 #pragma unroll
-    for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = Eb[n];
+    for (int n = 0; n < N; ++n) Ebp[(size_t)n * D] = Eb[n];
     ws[wl.CSB + ((size_t)b * g.S + s) * D + d] = csb;
     if (wave == 0 && grp > 0) {  // the group's own aggregate, passed to the groups on its left
         float* GH = ws + wl.GHB + ((size_t)b * (g.G - 1) + grp - 1) * N * D + d;
         float* GP = ws + wl.GPB + ((size_t)b * (g.G - 1) + grp - 1) * N * D + d;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            GH[(size_t)n * D] = __builtin_fmaf(sP[n * 64 + lane], Eb[n], c[n]);
+            GH[(size_t)n * D] = __builtin_fmaf(sP[n * 64 + lane], Eb[n], ga[n]);
             GP[(size_t)n * D] = exp2_fast(A2[n] * (csb + sumd));
         }
     }
 }
 
-// ------------------------------------------------------------ 2. and 4. carries
+// ------------------------------------------------------------ 2. and 3. carries
 // Forward: carry(0) = h0, carry(g+1) = GP_g carry(g) + GH_g, written over GH_g.
 // Backward: carry(G-1) = dh_final, carry(g-1) = GPB_{g-1} carry(g) + GHB_{g-1},
 // written over GHB_{g-1}. Both walk G-1 slots in order p = 0 .. G-2 (slot p, or
@@ -529,7 +475,7 @@ bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ 
     }
 }
 
-// ------------------------------------------------------------ 5. final pass
+// ------------------------------------------------------------ 4. final pass
 template <int N, bool BF16, bool HAS_Z, bool HAS_D>
 __global__ void __launch_bounds__(64 * kBwdMaxGroup)
 bwd_final(BwdArgs a, BGeom g) {
@@ -819,7 +765,7 @@ bwd_final(BwdArgs a, BGeom g) {
     }
 }
 
-// ------------------------------------------------------------ 6. reductions
+// ------------------------------------------------------------ 5. reductions
 // dA[d][n] = sum over (batch, group) of PA; dD[d] likewise (blockIdx.y == N). One
 // workgroup per (64 channels, n): its 4 waves take every 4th unit, 4 loads in
 // flight each, then add their sums in LDS in a fixed order.
@@ -912,13 +858,12 @@ hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
     const size_t lds_fin = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     float* ws = static_cast<float*>(a.ws);
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, N, g);
-    if (g.S > 1 || g.nsub > 1) launch((bwd_state_aggregate<N, BF16>), grid, block, (uint32_t)lds_agg, st, a, g);
+    if (g.S > 1 || g.nsub > 1) {
+        if (a.z) launch((bwd_aggregate<N, BF16, true>), grid, block, (uint32_t)lds_agg, st, a, g);
+        else launch((bwd_aggregate<N, BF16, false>), grid, block, (uint32_t)lds_agg, st, a, g);
+    }
     const dim3 cg((unsigned)((a.D + 63) / 64), N, a.B);
     if (g.G > 1) launch(bwd_carry<false>, cg, dim3(256), 0, st, a.h0, ws + wl.GH, ws + wl.GP, a.B, a.D, N, g.G);
-    if (g.S > 1) {
-        if (a.z) launch((bwd_adjoint_aggregate<N, BF16, true>), grid, block, (uint32_t)lds_agg, st, a, g);
-        else launch((bwd_adjoint_aggregate<N, BF16, false>), grid, block, (uint32_t)lds_agg, st, a, g);
-    }
     if (g.G > 1)
         launch(bwd_carry<true>, cg, dim3(256), 0, st, a.dh_final, ws + wl.GHB, ws + wl.GPB, a.B, a.D, N, g.G);
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
