@@ -327,7 +327,7 @@ bwd_aggregate(BwdArgs a, BGeom g) {
                     const float ab = exp2_fast(dv[k] * A2[n]);
                     h[n] = __builtin_fmaf(ab, h[n], u * Bt.at(n));
                     pr[n] *= ab;
-                    ga[n] = __builtin_fmaf(pr[n], gv[k] * Ct.at(n), ga[n]);
+                    ga[n] = __builtin_fmaf(pr[n] * gv[k], Ct.at(n), ga[n]);
                 }
             }
             if (j + 1 < nsub && d < D) {
