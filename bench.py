@@ -173,13 +173,23 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """C++ source without comments and with runs of whitespace collapsed: what the
+    compiler sees (string literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def sources_sha256(kind):
-    """SHA-256 of the concatenated bytes of a kernel's sources (KERNEL_SOURCES)."""
+    """SHA-256 of a kernel's sources (KERNEL_SOURCES, in order), comments and
+    whitespace excluded: a comment edit does not void a measurement."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "selective_scan_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "selective_scan_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

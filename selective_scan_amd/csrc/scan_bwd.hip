@@ -23,10 +23,12 @@
 //      same decays); in-group prefixes (state) and suffixes (adjoint) in LDS.
 //   2. bwd_carry<false>: the state entering each group.
 //   3. bwd_carry<true>: the adjoint entering each group from the right.
-//   4. bwd_final: per segment, blocks of K steps from the last to the first.
-//      A sub-block's entering state is rebuilt from its checkpoint and the
-//      segment's carried-in state, the K states are recomputed forwards and kept
-//      in VGPRs (K*N of them), then the adjoint walks the K steps backwards. The
+//   4. bwd_final: per segment, blocks of K steps (checkpoint to checkpoint) from
+//      the last to the first. A block's entering state is rebuilt from its
+//      checkpoint and the segment's carried-in state; the block then runs as
+//      halves of KR steps, the later half first: the half's states are recomputed
+//      forwards (the later half replays the steps before it) and kept in VGPRs
+//      (KR*N of them), then the adjoint walks the half's steps backwards. The
 //      per-step sums over channels (dB, dC) are reduced across the 64 lanes by a
 //      transpose-reduce (permlane swaps and DPP, no LDS) and stored as fp32
 //      partials per 64-channel block; dA and dD are summed per workgroup.
@@ -63,8 +65,8 @@ struct BGeom {
     int S;     // segments per chain
     int W;     // segments (waves) per workgroup
     int G;     // groups per chain
-    int K;     // steps per sub-block
-    int nsub;  // sub-blocks per full segment
+    int K;     // steps between checkpoints (a block)
+    int nsub;  // blocks per full segment
 };
 
 BGeom bgeom(int B, int L, int D, int N) {
@@ -92,7 +94,7 @@ BGeom bgeom(int B, int L, int D, int N) {
 //   CSB [B][S][D]      in-group suffix of sum(Delta) after each segment
 //   GHB [B][G-1][N][D] adjoint: aggregate of groups 1..G-1, then the adjoint entering groups 0..G-2
 //   GPB [B][G-1][N][D] decay of groups 1..G-1
-//   HZ  [B][S][nsub-1][N][D] zero-start state at sub-block boundaries 1..nsub-1 of each segment
+//   HZ  [B][S][nsub-1][N][D] zero-start state at block boundaries 1..nsub-1 of each segment
 //   CZ  [B][S][nsub-1][D]    sum(Delta) from the segment start to those boundaries
 //   PA  [B][G][N][D]   dA summed over one group's segments
 //   PD  [B][G][D]      dD summed over one group's segments
