@@ -122,3 +122,11 @@ def test_scan_deterministic_and_ignores_workspace_contents():
     ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
     y2, h2 = gpu_scan(w, workspace=ws)
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_scan_long_sequence_few_channels():
+    """B=1, L=20000, D=64: hundreds of segment groups, so the group carry walks
+    quarters longer than it keeps in registers (the re-read path)."""
+    print("[scan] B1 L20000 D64 N16 (long group walk)", flush=True)
+    w = si.scan_inputs(1, 20000, 64, 16, dtype=si.BF16, seed=9, with_h0=True)
+    _check(w, what="long walk")

@@ -92,3 +92,12 @@ def test_scan_bwd_deterministic():
     for k, v in g1.items():
         if v is not None:
             assert torch.equal(v, g2[k]), k
+
+
+def test_scan_bwd_long_sequence_few_channels():
+    """B=1, L=20000, D=64, N=16: 1250 segments in 313 groups, so both carries walk
+    quarters longer than they keep in registers (the re-read path)."""
+    print("[scan_bwd] B1 L20000 D64 N16 (long group walk)", flush=True)
+    w = si.scan_inputs(1, 20000, 64, 16, dtype=si.BF16, seed=10, with_h0=True)
+    gw = si.scan_grad_inputs(1, 20000, 64, 16, dtype=si.BF16, seed=11)
+    _check(w, gw, what="long walk")
