@@ -101,3 +101,15 @@ def test_scan_bwd_long_sequence_few_channels():
     w = si.scan_inputs(1, 20000, 64, 16, dtype=si.BF16, seed=10, with_h0=True)
     gw = si.scan_grad_inputs(1, 20000, 64, 16, dtype=si.BF16, seed=11)
     _check(w, gw, what="long walk")
+
+
+def test_scan_bwd_without_dh0_changes_nothing_else():
+    """dh0 not requested (NULL): every other gradient is bit-identical."""
+    w = si.scan_inputs(2, 700, 96, 16, dtype=si.BF16, seed=12, with_h0=True)
+    gw = si.scan_grad_inputs(2, 700, 96, 16, dtype=si.BF16, seed=13)
+    g1 = gpu_scan_bwd(w, gw)
+    g2 = gpu_scan_bwd(w, gw, want_dh0=False)
+    assert g2["dh0"] is None
+    for k, v in g1.items():
+        if k != "dh0":
+            assert torch.equal(v, g2[k]), k
