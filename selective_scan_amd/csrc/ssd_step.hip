@@ -59,29 +59,39 @@ __global__ void __launch_bounds__(kSThreads) ssd_step_kernel(SsdStepArgs a) {
     const int tid = threadIdx.x, pq = tid & 15, ng = tid >> 4;
     float4* S = reinterpret_cast<float4*>(a.state + (size_t)bh * N * kSP) + pq;
 
+    // Every load is issued before the first state store: stores count against the
+    // same outstanding-memory counter as loads, so a load issued after a store would
+    // also wait for that store.
     float4 s[R];
+    float bn[R], cn[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) s[k] = S[(ng + 16 * k) * (kSP / 4)];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        bn[k] = ld1<BF16>(a.Bm, (size_t)b * N + ng + 16 * k);
+        cn[k] = ld1<BF16>(a.Cm, (size_t)b * N + ng + 16 * k);
+    }
     const float dt = ld1<BF16>(a.delta, bh);
-    const float decay = exp2_fast(dt * a.A[h] * kLog2e);
+    const float Ah = a.A[h];
     const float4 xv = ld4<BF16>(a.x, (size_t)bh * kSP + 4 * pq);
+    const float dh = HAS_D ? a.Dskip[h] : 0.0f;
+    const float4 zv = HAS_Z ? ld4<BF16>(a.z, (size_t)bh * kSP + 4 * pq) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float decay = exp2_fast(dt * Ah * kLog2e);
     const float4 u = make_float4(dt * xv.x, dt * xv.y, dt * xv.z, dt * xv.w);
     float4 yp = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
         const int n = ng + 16 * k;
-        const float bn = ld1<BF16>(a.Bm, (size_t)b * N + n);
-        const float cn = ld1<BF16>(a.Cm, (size_t)b * N + n);
         float4 v;
-        v.x = __builtin_fmaf(decay, s[k].x, bn * u.x);
-        v.y = __builtin_fmaf(decay, s[k].y, bn * u.y);
-        v.z = __builtin_fmaf(decay, s[k].z, bn * u.z);
-        v.w = __builtin_fmaf(decay, s[k].w, bn * u.w);
+        v.x = __builtin_fmaf(decay, s[k].x, bn[k] * u.x);
+        v.y = __builtin_fmaf(decay, s[k].y, bn[k] * u.y);
+        v.z = __builtin_fmaf(decay, s[k].z, bn[k] * u.z);
+        v.w = __builtin_fmaf(decay, s[k].w, bn[k] * u.w);
         S[n * (kSP / 4)] = v;
-        yp.x = __builtin_fmaf(cn, v.x, yp.x);
-        yp.y = __builtin_fmaf(cn, v.y, yp.y);
-        yp.z = __builtin_fmaf(cn, v.z, yp.z);
-        yp.w = __builtin_fmaf(cn, v.w, yp.w);
+        yp.x = __builtin_fmaf(cn[k], v.x, yp.x);
+        yp.y = __builtin_fmaf(cn[k], v.y, yp.y);
+        yp.z = __builtin_fmaf(cn[k], v.z, yp.z);
+        yp.w = __builtin_fmaf(cn[k], v.w, yp.w);
     }
     // sum over the 4 row groups of this wave (lanes 16 and 32 apart) ...
 #pragma unroll
@@ -104,14 +114,12 @@ __global__ void __launch_bounds__(kSThreads) ssd_step_kernel(SsdStepArgs a) {
             v.w += red[w][pq].w;
         }
         if constexpr (HAS_D) {
-            const float dh = a.Dskip[h];
             v.x = __builtin_fmaf(dh, xv.x, v.x);
             v.y = __builtin_fmaf(dh, xv.y, v.y);
             v.z = __builtin_fmaf(dh, xv.z, v.z);
             v.w = __builtin_fmaf(dh, xv.w, v.w);
         }
         if constexpr (HAS_Z) {
-            const float4 zv = ld4<BF16>(a.z, (size_t)bh * kSP + 4 * pq);
             v.x *= silu(zv.x);
             v.y *= silu(zv.y);
             v.z *= silu(zv.z);

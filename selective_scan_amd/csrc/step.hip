@@ -17,11 +17,14 @@
 #ifndef SSM_STEP_REPS
 #define SSM_STEP_REPS 2
 #endif
+#ifndef SSM_STEP_THREADS
+#define SSM_STEP_THREADS 256
+#endif
 
 namespace ssm {
 namespace {
 
-constexpr int kStepThreads = 256;
+constexpr int kStepThreads = SSM_STEP_THREADS;
 constexpr int kReps = SSM_STEP_REPS;
 
 template <bool BF16>
@@ -132,16 +135,32 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel_var(StepArgs a) {
     const float4 Cq = load_quarter<N, BF16>(a.Cm, b, q);
     float4* st = reinterpret_cast<float4*>(a.state + (size_t)b * D * N);
     const float4* Af = reinterpret_cast<const float4*>(a.A);
+    // every load of the lane is issued before its first state store (a load issued
+    // after a store would also wait for the store)
+    float dl[kReps], bias[kReps], xs[kReps], zs[kReps], sk[kReps];
+    float4 A4s[kReps], hs[kReps];
 #pragma unroll
     for (int r = 0; r < kReps; ++r) {
         const int f = f0 + r * kStepThreads;
         const int d = (f < F ? f : F - 1) / QPC;
-        float dt = load_io_at<BF16>(a.delta, (size_t)b * D + d);
-        if (a.delta_bias != nullptr) dt += a.delta_bias[d];
+        dl[r] = load_io_at<BF16>(a.delta, (size_t)b * D + d);
+        bias[r] = a.delta_bias != nullptr ? a.delta_bias[d] : 0.0f;
+        xs[r] = load_io_at<BF16>(a.x, (size_t)b * D + d);
+        zs[r] = a.z != nullptr ? load_io_at<BF16>(a.z, (size_t)b * D + d) : 0.0f;
+        sk[r] = a.Dskip != nullptr ? a.Dskip[d] : 0.0f;
+        A4s[r] = Af[f < F ? f : F - 1];
+        hs[r] = f < F ? st[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < kReps; ++r) {
+        const int f = f0 + r * kStepThreads;
+        const int d = (f < F ? f : F - 1) / QPC;
+        float dt = dl[r];
+        if (a.delta_bias != nullptr) dt += bias[r];
         if (sp) dt = step_softplus(dt);
-        const float xv = load_io_at<BF16>(a.x, (size_t)b * D + d);
-        const float4 A4 = Af[f < F ? f : F - 1];
-        const float4 h = f < F ? st[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float xv = xs[r];
+        const float4 A4 = A4s[r];
+        const float4 h = hs[r];
         float4 hn;
         hn.x = step_input(exp2_fast(dt * kLog2e * A4.x), h.x, dt, A4.x, xv * Bq.x, zoh);
         hn.y = step_input(exp2_fast(dt * kLog2e * A4.y), h.y, dt, A4.y, xv * Bq.y, zoh);
@@ -153,8 +172,8 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel_var(StepArgs a) {
         for (int o = QPC / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o);
         if (q == 0 && f < F) {
             float v = p;
-            if (a.Dskip != nullptr) v = __builtin_fmaf(a.Dskip[d], xv, v);
-            if (a.z != nullptr) v *= silu(load_io_at<BF16>(a.z, (size_t)b * D + d));
+            if (a.Dskip != nullptr) v = __builtin_fmaf(sk[r], xv, v);
+            if (a.z != nullptr) v *= silu(zs[r]);
             if constexpr (BF16) static_cast<uint16_t*>(a.y)[(size_t)b * D + d] = f32_to_bf16(v);
             else static_cast<float*>(a.y)[(size_t)b * D + d] = v;
         }
