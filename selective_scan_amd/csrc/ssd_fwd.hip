@@ -9,14 +9,14 @@
 //   y_i = exp(s_i) C_i . H_in  +  sum_{j<=i} (C_i . B_j) exp(s_i - s_j) Delta_j x_j
 // and the state after it is H_out = exp(s_last) H_in + sum_j exp(s_last - s_j) Delta_j B_j (x) x_j.
 //
-// Kernels (one workgroup of 8 waves per (batch, head, super-chunk); a
-// super-chunk is a run of consecutive chunks walked in order):
-//   ssd_super_state  every super-chunk but the last: its aggregate state from a
-//                    zero start and its total log2 decay;
+// Kernels (one workgroup per (batch, head, super-chunk); a super-chunk is a run
+// of consecutive chunks walked in order):
+//   ssd_state_agg    (4 waves) every super-chunk but the last: its aggregate
+//                    state from a zero start and its total log2 decay;
 //   ssd_carry        per (batch, head, state element), a linear walk over the
 //                    super-chunks that turns the aggregates into the state
 //                    entering each super-chunk (h0 folded in), in place;
-//   ssd_chunk_scan   starting from its entering state, for every chunk:
+//   ssd_chunk_scan   (8 waves) starting from its entering state, for every chunk:
 //                    Y_off = diag(e^s) C H, G^T = B C^T, M = G o decay o Delta
 //                    (causal), Y_diag = M X, y = (Y_off + Y_diag + D x) silu(z),
 //                    then the chunk state S = (w o X)^T B and H <- e^{s_last} H + S.
@@ -36,8 +36,7 @@
 // last step of j's 32-step block: one exp per row and a per-column factor staged
 // once per chunk (both factors <= 1, so neither can overflow).
 // Pipeline per chunk: the next chunk's x rows and Delta load into registers
-// during the output phase, its B rows during the state phase (super_state: both
-// two chunks ahead); one wave (in the scan kernel the one with the least output
+// during the output phase, its B rows during the state phase; one wave (in the scan kernel the one with the least output
 // work) writes its decay prefix into the second of two prefix buffers, and the C
 // rows of a wave's first output block load across the barrier; two barriers per
 // chunk.
@@ -491,104 +490,188 @@ __device__ __forceinline__ void block_coords(int H, int Kp, int& h, int& k, int&
     b = r / Kp;
 }
 
-// Weights of one staged block of a super-chunk's aggregate, computed by wave 0:
-// w_t = exp2(lam - s_t) Delta_t, with s_t the inclusive log2-decay prefix from the
-// super-chunk's start (fp64), lam its total, and zero for steps t >= len. `off` is
-// the prefix before the block and is advanced past it. Lane l owns steps 4l..4l+3.
-__device__ __forceinline__ void agg_weights(lds_t* lds, const Smem& sm, int sb, int len, float A2,
-                                            const float (&dv)[4], double lam, double& off) {
-    const int lane = threadIdx.x & 63;
-    lds_f32* w = sv_arr(lds, sm, kMaxQ, sb, 2);
-    float d[4];
-    double loc[4], run = 0.0;
+// Aggregate of one super-chunk (all but the last of each (batch, head)), from a
+// zero state: S = sum over its steps t of exp2(Lam - s_t) Delta_t B_t (x) x_t,
+// with s_t the inclusive log2-decay prefix from the super-chunk's start and Lam
+// its total (also written out). The super-chunk is walked in blocks of kAggT
+// steps; per block j with total log2 decay S_j the aggregate is rescaled and
+// extended, S <- exp2(S_j) S + sum_{t in j} exp2(S_j - s_t) Delta_t B_t (x) x_t,
+// with s_t now the prefix inside the block (fp64, rounded once), which is the
+// same sum regrouped.
+//
+// One workgroup of 4 waves per (batch, head, super-chunk). Wave w owns the n
+// columns [w N/4, (w+1) N/4) of S^T (P x N) for all 64 p, as 16x16 tiles. Its
+// operands per 32-step sub-block: x^T read with the LDS transpose read (exact
+// bf16), and (w o B) formed in registers from the transposed B rows and split
+// into a bf16 high part and remainder (two MFMAs). Every wave computes the
+// block's decay prefix itself (one Delta per lane, an fp64 scan across the
+// wave) and keeps its weights in a private LDS slot. Rows of x and B (and the
+// Delta of each lane) arrive two blocks ahead of their use in registers.
+constexpr int kAggWaves = 4;
+constexpr int kAggThreads = 64 * kAggWaves;
+constexpr int kAggT = 64;  // steps per staged block
+
+template <int N>
+struct AggLds {
+    static constexpr int BS = N + kPad;                      // B row stride (elements)
+    static constexpr int XS_OFF = 0;                         // bf16 [kAggT][kXS]
+    static constexpr int BS_OFF = XS_OFF + kAggT * kXS * 2;  // bf16 [kAggT][BS]
+    static constexpr int W_OFF = BS_OFF + kAggT * BS * 2;    // f32 [kAggWaves][kAggT]
+    static constexpr int TOTAL = W_OFF + kAggWaves * kAggT * 4;
+};
+
+template <int N>
+struct AggRows {
+    static constexpr int XQ = kAggT * (kP / 8) / kAggThreads;  // 16-byte pieces per thread
+    static constexpr int BQ = kAggT * (N / 8) / kAggThreads;
+    u32x4 xv[XQ];
+    u32x4 bv[BQ];
+    uint32_t dl;  // Delta of step `lane` of the block (bf16 bits)
+};
+
+template <int N>
+__device__ __forceinline__ void agg_load(const Views& v, int t0, AggRows<N>& r) {
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        d[k] = (4 * lane + k < len) ? dv[k] : 0.0f;
-        run += (double)(d[k] * A2);
-        loc[k] = run;
+    for (int k = 0; k < AggRows<N>::XQ; ++k) {
+        const int q = tid + k * kAggThreads;
+        const int row = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
+        r.xv[k] = ld_buf16(v.x, (uint32_t)(t0 + row) * v.xrow + v.xh + 2 * c8);
     }
-    double incl = run;
+#pragma unroll
+    for (int k = 0; k < AggRows<N>::BQ; ++k) {
+        const int q = tid + k * kAggThreads;
+        const int row = q / (N / 8), c8 = (q % (N / 8)) * 8;
+        r.bv[k] = ld_buf16(v.bm, (uint32_t)((t0 + row) * N + c8) * 2);
+    }
+    r.dl = __builtin_amdgcn_raw_buffer_load_b16(v.dl, (int)((uint32_t)(t0 + (tid & 63)) * v.drow + v.xh / kP), 0,
+                                                0);
+}
+
+// Rows of a block into LDS (rows at or past len as zeros), and this wave's
+// weights exp2(S_j - s_t) Delta_t into its slot; returns the block's total log2
+// decay S_j (fp64, the same value in every lane).
+template <int N>
+__device__ __forceinline__ double agg_stage(lds_t* lds, const AggRows<N>& r, int len, float A2) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    lds_u16* xs = reinterpret_cast<lds_u16*>(lds + AggLds<N>::XS_OFF);
+    lds_u16* bs = reinterpret_cast<lds_u16*>(lds + AggLds<N>::BS_OFF);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < AggRows<N>::XQ; ++k) {
+        const int q = tid + k * kAggThreads;
+        const int row = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
+        *reinterpret_cast<lds_u32x4*>(xs + row * kXS + c8) = row < len ? r.xv[k] : zero;
+    }
+#pragma unroll
+    for (int k = 0; k < AggRows<N>::BQ; ++k) {
+        const int q = tid + k * kAggThreads;
+        const int row = q / (N / 8), c8 = (q % (N / 8)) * 8;
+        *reinterpret_cast<lds_u32x4*>(bs + row * AggLds<N>::BS + c8) = row < len ? r.bv[k] : zero;
+    }
+    const float d = lane < len ? bf16_to_f32((uint16_t)r.dl) : 0.0f;
+    double incl = (double)(d * A2);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const double u = __shfl_up(incl, o, 64);
         if (lane >= o) incl += u;
     }
-    const double base = off + (incl - run);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[4 * lane + k] = exp2_fast((float)(lam - (base + loc[k]))) * d[k];
-    off += __shfl(incl, 63, 64);
+    const double tot = __shfl(incl, 63, 64);
+    lds_f32* w = reinterpret_cast<lds_f32*>(lds + AggLds<N>::W_OFF) + wave * kAggT;
+    w[lane] = exp2_fast((float)(tot - incl)) * d;
+    return tot;
 }
 
-// Aggregate of one super-chunk (all but the last of each (batch, head)), from a
-// zero state: S = sum over its steps of exp2(Lam - s_t) Delta_t B_t (x) x_t, one
-// long contraction over time, staged in LDS 256 steps at a time whatever the
-// chunk length, with Lam = sum of Delta_t A log2 e over the super-chunk (its
-// total log2 decay, also written out). This is the end state of the chunk
-// recurrence started from zero: each chunk's decays multiply into exp2(Lam - s_t).
+// Three waves per SIMD (at most 168 registers a lane; the compiler would
+// otherwise take ~220 with the accumulators in AGPRs and fit two): every
+// aggregate of a 768-block launch is resident at once.
 template <int N>
-__global__ void __launch_bounds__(kThreads)
-ssd_super_state(SsdArgs a, SsdGeom geo) {
-    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+__global__ void __launch_bounds__(kAggThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+ssd_state_agg(SsdArgs a, SsdGeom geo) {
+    constexpr int NBW = N / 64;  // 16-column n-blocks per wave
+    constexpr int BS = AggLds<N>::BS;
+    __shared__ __attribute__((aligned(16))) char lds_raw[AggLds<N>::TOTAL];
     lds_t* lds = (lds_t*)lds_raw;
-    const Smem sm = smem_layout<N>(kMaxQ);
     int h, k, b;
     block_coords(a.H, geo.K - 1, h, k, b);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, i = lane & 15;
     const float A2 = a.A[h] * kLog2e;
     const int T0 = k * geo.cps * geo.Q, T1 = min(a.L, (k + 1) * geo.cps * geo.Q);
-    const int nblk = (T1 - T0 + kMaxQ - 1) / kMaxQ;
+    const int nblk = (T1 - T0 + kAggT - 1) / kAggT;
     const Views v = make_views<N>(a, b, h);
+    const lds_u16* xs = reinterpret_cast<const lds_u16*>(lds + AggLds<N>::XS_OFF);
+    const lds_u16* bs = reinterpret_cast<const lds_u16*>(lds + AggLds<N>::BS_OFF);
+    const lds_f32* wv = reinterpret_cast<const lds_f32*>(lds + AggLds<N>::W_OFF) + wave * kAggT;
+    const int n0w = wave * (N / 4);
 
-    // total log2 decay of the super-chunk (fp64; fixed-order block reduction)
-    double lam;
-    {
-        double part = 0.0;
-        for (int t = T0 + tid; t < T1; t += kThreads)
-            part += (double)(bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-                                 v.dl, (int)((uint32_t)t * v.drow + v.xh / kP), 0, 0)) * A2);
+    f32x4 acc[4][NBW];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-        __attribute__((address_space(3))) double* red =
-            reinterpret_cast<__attribute__((address_space(3))) double*>(lds + sm.tot);
-        if (lane == 0) red[wave] = part;
-        __syncthreads();
-        lam = 0.0;
+    for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) lam += red[w];
-    }
+        for (int nb = 0; nb < NBW; ++nb) acc[pb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    StateTiles<N> st;
+    // one block's contraction from LDS, after scaling the aggregate by its decay
+    auto contract = [&](float dec) {
 #pragma unroll
-    for (int kk = 0; kk < StateTiles<N>::NBW; ++kk) st.acc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
-    double off = 0.0;
-    // Rows arrive two blocks ahead of their use: while block j is contracted,
-    // `nxt` holds the loads of block j + 1 in flight and `nxt2` receives those of
-    // block j + 2. The two register sets swap roles every block (the loop body is
-    // written out twice so that no in-flight register is copied).
-    ChunkRows<N> ra, rb;
-    load_x_rows<N>(v, kMaxQ, T0, rb, 0);
-    load_b_rows<N>(v, kMaxQ, T0, rb);
-    if (nblk > 1) {
-        load_x_rows<N>(v, kMaxQ, T0 + kMaxQ, ra, 0);
-        load_b_rows<N>(v, kMaxQ, T0 + kMaxQ, ra);
-    }
-    if (wave == 0) agg_weights(lds, sm, 0, min(kMaxQ, T1 - T0), A2, rb.dv, lam, off);
-    store_xb<N>(lds, sm, kMaxQ, rb);
-    auto step = [&](int j, ChunkRows<N>& nxt, ChunkRows<N>& nxt2) {
-        const int sb = j & 1;
-        const int t0 = T0 + j * kMaxQ;
-        const int len = min(kMaxQ, T1 - t0);
-        const int ln = j + 1 < nblk ? min(kMaxQ, T1 - t0 - kMaxQ) : 0;
-        __syncthreads();  // rows and weights of this block visible
-        if (j + 2 < nblk) {
-            load_x_rows<N>(v, kMaxQ, t0 + 2 * kMaxQ, nxt2, 0);
-            load_b_rows<N>(v, kMaxQ, t0 + 2 * kMaxQ, nxt2);
+        for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pb][nb][r] *= dec;
+#pragma unroll
+        for (int kb = 0; kb < kAggT / 32; ++kb) {
+            const int t = kb * 32 + 8 * g;
+            const f32x4 w0 = ld_f32x4(wv + t), w1 = ld_f32x4(wv + t + 4);
+            bf16x8 bhi[NBW], blo[NBW];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const int n0 = n0w + nb * 16;
+                const bf16x8 bb = cat(ld_tr4(bs, BS, t, n0), ld_tr4(bs, BS, t + 4, n0));
+                float vv[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vv[e] = (float)bb[e] * w0[e];
+                    vv[e + 4] = (float)bb[e + 4] * w1[e];
+                }
+                split8(vv, bhi[nb], blo[nb]);
+            }
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const bf16x8 xo = cat(ld_tr4(xs, kXS, t, pb * 16), ld_tr4(xs, kXS, t + 4, pb * 16));
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) acc[pb][nb] = mfma16(xo, bhi[nb], acc[pb][nb]);
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) acc[pb][nb] = mfma16(xo, blo[nb], acc[pb][nb]);
+            }
         }
-        chunk_state<N>(lds, sm, kMaxQ, sb, len, st, true);
-        if (ln > 0 && wave == 0) agg_weights(lds, sm, sb ^ 1, ln, A2, nxt.dv, lam, off);
-        __syncthreads();  // every read of this block's rows done
-        if (ln > 0) store_xb<N>(lds, sm, kMaxQ, nxt);
+    };
+
+    double lam = 0.0;
+    float dec = 1.0f;
+    // Two register sets swap roles every block (the body is written out twice so
+    // that no in-flight register is copied): while block j is contracted, `nxt`
+    // holds the loads of block j + 1 and `nxt2` receives those of block j + 2.
+    AggRows<N> ra, rb;
+    agg_load<N>(v, T0, rb);
+    if (nblk > 1) agg_load<N>(v, T0 + kAggT, ra);
+    {
+        const double s = agg_stage<N>(lds, rb, min(kAggT, T1 - T0), A2);
+        lam += s;
+        dec = exp2_fast((float)s);
+    }
+    auto step = [&](int j, AggRows<N>& nxt, AggRows<N>& nxt2) {
+        const int t0 = T0 + j * kAggT;
+        __syncthreads();  // rows of block j visible
+        if (j + 2 < nblk) agg_load<N>(v, t0 + 2 * kAggT, nxt2);
+        contract(dec);
+        __syncthreads();  // every read of block j's rows done
+        if (j + 1 < nblk) {
+            const double s = agg_stage<N>(lds, nxt, min(kAggT, T1 - t0 - kAggT), A2);
+            lam += s;
+            dec = exp2_fast((float)s);
+        }
     };
     for (int j = 0; j < nblk; j += 2) {
         step(j, ra, rb);
@@ -596,13 +679,11 @@ ssd_super_state(SsdArgs a, SsdGeom geo) {
     }
     float* out = static_cast<float*>(a.ws) + (((size_t)b * a.H + h) * (geo.K - 1) + k) * kP * N;
 #pragma unroll
-    for (int kk = 0; kk < StateTiles<N>::NBW; ++kk)
+    for (int pb = 0; pb < 4; ++pb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int p, n;
-            tile_pn<N>(kk, r, p, n);
-            out[p * N + n] = st.acc[kk][r];
-        }
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[(pb * 16 + 4 * g + r) * N + n0w + nb * 16 + i] = acc[pb][nb][r];
     if (tid == 0) {
         float* lamp = static_cast<float*>(a.ws) + ws_hagg(a.B, a.H, geo.K, N);
         lamp[((size_t)b * a.H + h) * (geo.K - 1) + k] = (float)lam;
@@ -861,8 +942,8 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
     const Smem sm = smem_layout<N>(geo.Q);
     const OutPlan plan = out_plan(geo.Q / 32, N);
     if (geo.K > 1) {
-        launch((ssd_super_state<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kThreads),
-               (uint32_t)smem_layout<N>(kMaxQ).total, st, a, geo);
+        launch((ssd_state_agg<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kAggThreads), 0, st, a,
+               geo);
         launch((ssd_carry<N>), dim3((kP * N + 255) / 256, a.H, a.B), dim3(256), 0, st,
                            a.h0, static_cast<float*>(a.ws), a.B, a.H, geo.K);
     }
