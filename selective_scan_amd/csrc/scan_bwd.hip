@@ -478,8 +478,11 @@ bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ 
 }
 
 // ------------------------------------------------------------ 4. final pass
+// At least three waves per SIMD: with every option on (z, D) the compiler's own
+// allocation at N = 16 takes 183 VGPRs (two waves); capped at 168 it spills
+// three, and the third wave hides more latency than the spills cost.
 template <int N, bool BF16, bool HAS_Z, bool HAS_D>
-__global__ void __launch_bounds__(64 * kBwdMaxGroup)
+__global__ void __launch_bounds__(64 * kBwdMaxGroup) __attribute__((amdgpu_waves_per_eu(3)))
 bwd_final(BwdArgs a, BGeom g) {
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
