@@ -133,6 +133,11 @@ __host__ __device__ inline WsLayout ws_layout(int B, int D, int N, int S, int G)
 constexpr float kZohSmall = 0.03125f;
 constexpr float kZohSmall2 = kZohSmall * kLog2e;  // the same bound on |Delta A log2 e|
 constexpr float kLn2f = 0.69314718055994531f;
+// (ln 2)^k / (k+1)!, k = 1, 2, 3: the series 1 + z/2 + z^2/6 + z^3/24 in z2 = z log2 e
+constexpr double kLn2d = 0.69314718055994531;
+constexpr float kZohT1 = (float)(kLn2d / 2.0);
+constexpr float kZohT2 = (float)(kLn2d * kLn2d / 6.0);
+constexpr float kZohT3 = (float)(kLn2d * kLn2d * kLn2d / 24.0);
 
 template <int N, int V>
 struct VarLane {};  // V = 0: nothing per lane
@@ -249,10 +254,13 @@ struct Segment {
             const float w = xv * vl.rA[n] * b;
             return __builtin_fmaf(ab, hv + w, -w);
         } else {
-            const float z2 = dv * a2, z = z2 * kLn2f;
-            const float taylor =
-                dv * __builtin_fmaf(z, __builtin_fmaf(z, __builtin_fmaf(z, 1.0f / 24.0f, 1.0f / 6.0f), 0.5f), 1.0f);
-            const float coef = fabsf(z2) < kZohSmall2 ? taylor : (ab - 1.0f) * vl.rA[n];
+            // coef = Delta (e^z - 1)/z: the series in z2 = z log2 e (coefficients
+            // (ln 2)^k / (k+1)! folded in) below the switch, (e^z - 1)/A as
+            // ab/A - 1/A in one fma above it
+            const float z2 = dv * a2;
+            const float taylor = dv * __builtin_fmaf(z2, __builtin_fmaf(z2, __builtin_fmaf(z2, kZohT3, kZohT2), kZohT1),
+                                                     1.0f);
+            const float coef = fabsf(z2) < kZohSmall2 ? taylor : __builtin_fmaf(ab, vl.rA[n], -vl.rA[n]);
             return __builtin_fmaf(ab, hv, coef * (xv * b));
         }
     }
