@@ -35,11 +35,11 @@
 // Below the diagonal, exp2(s_i - s_j) = exp2(s_i - s_r) exp2(s_r - s_j) with r the
 // last step of j's 32-step block: one exp per row and a per-column factor staged
 // once per chunk (both factors <= 1, so neither can overflow).
-// Pipeline per chunk: the next chunk's x rows and Delta load into registers
-// during the output phase, its B rows during the state phase; one wave (in the scan kernel the one with the least output
-// work) writes its decay prefix into the second of two prefix buffers, and the C
-// rows of a wave's first output block load across the barrier; two barriers per
-// chunk.
+// Pipeline per chunk (ssd_chunk_scan): the next chunk's x rows and Delta load
+// into registers during the output phase, its B rows during the state phase; the
+// wave with the least output work writes the next decay prefix into the second
+// of two prefix buffers, and the C rows of a wave's first output block load
+// across the barrier; two barriers per chunk.
 #include "common.h"
 #include "launch.h"
 
