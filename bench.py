@@ -236,9 +236,10 @@ def scan_bench(name, wl, steps, warmup, dev):
     return res, w0
 
 
-def scan_cpu_baseline(wl, w0, budget_s=15.0):
+def scan_cpu_baseline(wl, w0, budget_s=15.0, total_s=10.0):
     """The fp64 oracle (as it stands) on the host cores: whole sequences of as many
-    channels as fit in about `budget_s` seconds (all of them when they fit)."""
+    channels as fit in about `budget_s` seconds (all of them when they fit), run
+    again until about `total_s` seconds of work have been timed; the median run."""
     import oracle
     import ssm_inputs as si
     o = oracle.get()
@@ -258,7 +259,7 @@ def scan_cpu_baseline(wl, w0, budget_s=15.0):
     probe = run(min(D, T))                       # one channel per thread
     dsel = int(min(D, max(T, budget_s / max(probe, 1e-6) * T * 0.7)))
     reps, els = 0, []
-    while reps < 5 and (reps == 0 or sum(els) < 2.0):
+    while reps < 1000 and (reps < 3 or sum(els) < total_s):
         els.append(run(dsel))
         reps += 1
     el = float(np.median(els))
