@@ -493,7 +493,38 @@ def step_bench(wl, dev, reps=3):
                           hbm_frac=alg / (cold["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           note="step s updates the state of layer s mod layers: the states "
                                "(%d x %.1f MB) exceed the MALL, so each step streams its state from HBM"
-                               % (cold["layers"], st0.numel() * 4 / 1e6)))
+                               % (cold["layers"], st0.numel() * 4 / 1e6)),
+                streaming_floor=streaming_floor(st0, steps))
+
+
+def streaming_floor(st0, steps, reps=3):
+    """Context for a decode step: a plain in-place scale of a tensor of the state's
+    size (torch's mul_, one launch per step), graph-replayed `steps` times on one
+    tensor (MALL-resident) and rotating over tensors adding up to more than the MALL.
+    What one launch per step reaches by pure streaming at this size."""
+    import torch
+    st = st0.clone()
+    g = torch.cuda.CUDAGraph()
+    sync()
+    s_ = torch.cuda.Stream()
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            for _ in range(steps):
+                st.mul_(0.999)
+    sync()
+    hot = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        sync()
+        hot.append(e0.elapsed_time(e1) / steps)
+    cold = cold_decode(lambda stv, s_: stv.mul_(0.999), st0, steps, reps=reps)
+    return dict(ms_per_step_hot=float(np.median(hot)), ms_per_step_cold=cold["ms"],
+                bytes_per_step=2 * st0.numel() * 4,
+                note="plain in-place scale of a tensor of the state's size (torch mul_), graph-replayed "
+                     "like the steps: reads and writes the state only")
 
 
 def cold_decode(step, st0, steps, reps=3, min_bytes=2 * MALL_BYTES):
@@ -585,7 +616,8 @@ def ssd_step_bench(wl, dev, reps=3):
                           hbm_frac=alg / (cold["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           note="step s updates the state of layer s mod layers: the states "
                                "(%d x %.1f MB) exceed the MALL, so each step streams its state from HBM"
-                               % (cold["layers"], st0.numel() * 4 / 1e6)))
+                               % (cold["layers"], st0.numel() * 4 / 1e6)),
+                streaming_floor=streaming_floor(st0, steps))
 
 
 def main():
