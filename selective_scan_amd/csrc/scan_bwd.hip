@@ -818,13 +818,22 @@ bwd_reduce_rows(BwdArgs a, BGeom g) {
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, a.N, g);
     const float* ws = static_cast<const float*>(a.ws);
     const int nd = (a.D + 63) / 64;
+    // 16 blocks' partials loaded before any is added (one memory latency per 16
+    // blocks, not per 4); accumulator r still sums blocks r, r + 4, ... in order
     float sb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 0; k0 < nd; k0 += 4) {
+    for (int k0 = 0; k0 < nd; k0 += 16) {
+        float vb[16], vc[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (k0 + r < nd) {
-                sb[r] += ws[wl.PB + (size_t)(k0 + r) * tot + i];
-                sc[r] += ws[wl.PC + (size_t)(k0 + r) * tot + i];
+        for (int j = 0; j < 16; ++j) {
+            const int k = min(k0 + j, nd - 1);
+            vb[j] = ws[wl.PB + (size_t)k * tot + i];
+            vc[j] = ws[wl.PC + (size_t)k * tot + i];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (k0 + j < nd) {
+                sb[j & 3] += vb[j];
+                sc[j & 3] += vc[j];
             }
         }
     }
