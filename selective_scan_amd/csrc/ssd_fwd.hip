@@ -704,9 +704,23 @@ ssd_carry(const float* __restrict__ h0, float* __restrict__ ws, int B, int H, in
     float v = h0 ? h0[(bh * N + n) * kP + p] : 0.0f;
     const float* lam = ws + ws_hagg(B, H, K, N) + bh * (K - 1);
     float* slot = ws + bh * (K - 1) * kP * N + e;
-    for (int k = 0; k < K - 1; ++k) {
-        v = __builtin_fmaf(exp2_fast(lam[k]), v, slot[(size_t)k * kP * N]);
-        slot[(size_t)k * kP * N] = v;
+    // eight slots loaded before any is written (a load issued after a store would
+    // also wait for the store: one memory round trip per 8 super-chunks, not per one)
+    for (int k0 = 0; k0 < K - 1; k0 += 8) {
+        float sl[8], lm[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = min(k0 + j, K - 2);
+            sl[j] = slot[(size_t)k * kP * N];
+            lm[j] = lam[k];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (k0 + j < K - 1) {
+                v = __builtin_fmaf(exp2_fast(lm[j]), v, sl[j]);
+                slot[(size_t)(k0 + j) * kP * N] = v;
+            }
+        }
     }
 }
 
