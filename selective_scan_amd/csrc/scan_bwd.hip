@@ -792,13 +792,16 @@ bwd_reduce_params(BwdArgs a, BGeom g) {
     const int dc = d < D ? d : D - 1;
     const float* base = is_d ? ws + wl.PD + dc : ws + wl.PA + (size_t)n * D + dc;
     const size_t ustride = is_d ? (size_t)D : (size_t)N * D;
+    // eight units loaded before any is added; accumulator r still takes units
+    // wave + 4 r, wave + 4 r + 16, ... in order
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = wave; k0 < units; k0 += 16) {
+    for (int k0 = wave; k0 < units; k0 += 32) {
+        float v[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int k = k0 + 4 * r;
-            if (k < units) acc[r] += base[(size_t)k * ustride];
-        }
+        for (int j = 0; j < 8; ++j) v[j] = base[(size_t)min(k0 + 4 * j, units - 1) * ustride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (k0 + 4 * j < units) acc[j & 3] += v[j];
     }
     part[wave][lane] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
