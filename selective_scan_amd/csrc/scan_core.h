@@ -579,8 +579,16 @@ combine_partials(ScanArgs a, const float* __restrict__ yp, int nch) {
     const size_t tot = (size_t)a.B * a.L * a.D;
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= tot) return;
+    // eight chunks' partials loaded before any is added (added in chunk order)
     float v = 0.0f;
-    for (int c = 0; c < nch; ++c) v += yp[(size_t)c * tot + i];
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = yp[(size_t)min(c0 + j, nch - 1) * tot + i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (c0 + j < nch) v += t[j];
+    }
     if constexpr (HAS_D) {
         const float xv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[i]) : static_cast<const float*>(a.x)[i];
         v = __builtin_fmaf(a.Dskip[i % a.D], xv, v);
