@@ -824,6 +824,17 @@ __device__ __forceinline__ void out_item(const Views& v, const lds_t* lds, const
     // epilogue: rows 32 I + 8 (r/4) + 4 hf + r % 4, columns p = 32 (pb0 + q) + c;
     // rows past the sequence end fall outside the y view and are dropped
     const uint32_t off0 = (uint32_t)(t0 + 32 * I + 4 * hf) * v.xrow + v.xh + 2 * (32 * pb0 + c);
+    // the gate's z values are all loaded before the first y store (a load issued
+    // after a store would also wait for that store)
+    uint16_t zr[NPB][16];
+    if constexpr (HAS_Z) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int q = 0; q < NPB; ++q)
+                zr[q][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                    v.z, (int)(off0 + (uint32_t)(8 * (r >> 2) + (r & 3)) * v.xrow + 64 * q), 0, 0);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 32 * I + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -832,8 +843,7 @@ __device__ __forceinline__ void out_item(const Views& v, const lds_t* lds, const
         for (int q = 0; q < NPB; ++q) {
             float val = acc[q][r];
             if constexpr (HAS_D) val = __builtin_fmaf(Dh, bf16_to_f32(xs[row * kXS + 32 * (pb0 + q) + c]), val);
-            if constexpr (HAS_Z)
-                val *= silu(bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(v.z, (int)(off + 64 * q), 0, 0)));
+            if constexpr (HAS_Z) val *= silu(bf16_to_f32(zr[q][r]));
             __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), v.y, (int)(off + 64 * q), 0, 0);
         }
     }
