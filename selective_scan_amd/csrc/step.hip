@@ -60,22 +60,21 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(StepArgs a) {
     float4* st = reinterpret_cast<float4*>(a.state + (size_t)b * D * N);
     const float4* Af = reinterpret_cast<const float4*>(a.A);
 
+    // every load of both reps before any store (a load issued after a store would
+    // also wait for that store) and without a branch (so none is waited for before
+    // the next is issued): lanes past the row read its last quarter and store nothing
     float4 h[kReps], A4[kReps];
-    float dv[kReps], xv[kReps], zv[kReps];
+    float dv[kReps], xv[kReps], zv[kReps], dk[kReps];
 #pragma unroll
     for (int r = 0; r < kReps; ++r) {
-        const int f = f0 + r * kStepThreads;
-        const int d = f / QPC;
-        if (f < F) {
-            h[r] = st[f];
-            A4[r] = Af[f];
-            dv[r] = load_io_at<BF16>(a.delta, (size_t)b * D + d);
-            xv[r] = load_io_at<BF16>(a.x, (size_t)b * D + d);
-            zv[r] = HAS_Z ? load_io_at<BF16>(a.z, (size_t)b * D + d) : 0.0f;
-        } else {
-            h[r] = A4[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-            dv[r] = xv[r] = zv[r] = 0.0f;
-        }
+        const int fc = min(f0 + r * kStepThreads, F - 1);
+        const int d = fc / QPC;
+        h[r] = st[fc];
+        A4[r] = Af[fc];
+        dv[r] = load_io_at<BF16>(a.delta, (size_t)b * D + d);
+        xv[r] = load_io_at<BF16>(a.x, (size_t)b * D + d);
+        zv[r] = HAS_Z ? load_io_at<BF16>(a.z, (size_t)b * D + d) : 0.0f;
+        dk[r] = HAS_D ? a.Dskip[d] : 0.0f;
     }
 #pragma unroll
     for (int r = 0; r < kReps; ++r) {
@@ -93,7 +92,7 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel(StepArgs a) {
         if (q == 0 && f < F) {
             const int d = f / QPC;
             float v = p;
-            if constexpr (HAS_D) v = __builtin_fmaf(a.Dskip[d], xv[r], v);
+            if constexpr (HAS_D) v = __builtin_fmaf(dk[r], xv[r], v);
             if constexpr (HAS_Z) v *= silu(zv[r]);
             if constexpr (BF16) static_cast<uint16_t*>(a.y)[(size_t)b * D + d] = f32_to_bf16(v);
             else static_cast<float*>(a.y)[(size_t)b * D + d] = v;
@@ -136,20 +135,26 @@ __global__ void __launch_bounds__(kStepThreads) step_kernel_var(StepArgs a) {
     float4* st = reinterpret_cast<float4*>(a.state + (size_t)b * D * N);
     const float4* Af = reinterpret_cast<const float4*>(a.A);
     // every load of the lane is issued before its first state store (a load issued
-    // after a store would also wait for the store)
+    // after a store would also wait for the store) and without a branch (so none is
+    // waited for before the next is issued): an absent bias, skip or gate reads a
+    // tensor of the same shape instead and is not used; lanes past the row read its
+    // last quarter and store nothing
+    const float* biasp = a.delta_bias != nullptr ? a.delta_bias : a.A;
+    const float* skp = a.Dskip != nullptr ? a.Dskip : a.A;
+    const void* zp = a.z != nullptr ? a.z : a.x;
     float dl[kReps], bias[kReps], xs[kReps], zs[kReps], sk[kReps];
     float4 A4s[kReps], hs[kReps];
 #pragma unroll
     for (int r = 0; r < kReps; ++r) {
-        const int f = f0 + r * kStepThreads;
-        const int d = (f < F ? f : F - 1) / QPC;
+        const int fc = min(f0 + r * kStepThreads, F - 1);
+        const int d = fc / QPC;
         dl[r] = load_io_at<BF16>(a.delta, (size_t)b * D + d);
-        bias[r] = a.delta_bias != nullptr ? a.delta_bias[d] : 0.0f;
+        bias[r] = biasp[d];
         xs[r] = load_io_at<BF16>(a.x, (size_t)b * D + d);
-        zs[r] = a.z != nullptr ? load_io_at<BF16>(a.z, (size_t)b * D + d) : 0.0f;
-        sk[r] = a.Dskip != nullptr ? a.Dskip[d] : 0.0f;
-        A4s[r] = Af[f < F ? f : F - 1];
-        hs[r] = f < F ? st[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+        zs[r] = load_io_at<BF16>(zp, (size_t)b * D + d);
+        sk[r] = skp[d];
+        A4s[r] = Af[fc];
+        hs[r] = st[fc];
     }
 #pragma unroll
     for (int r = 0; r < kReps; ++r) {
