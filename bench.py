@@ -168,6 +168,7 @@ def time_calls(call, sets, steps, warmup, n_kernels):
 # Sources each kernel is compiled from, in the order their bytes are hashed.
 KERNEL_SOURCES = {
     "scan": ("scan_core.h", "scan_fwd.hip", "common.h", "launch.h"),
+    "scan_var": ("scan_core.h", "scan_var.hip", "common.h", "launch.h"),
     "scan_bwd": ("scan_bwd.hip", "common.h", "launch.h"),
     "ssd": ("ssd_fwd.hip", "common.h", "launch.h"),
 }
@@ -314,7 +315,8 @@ def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16):
                 kernel_ms=[float(v) for v in kmean], hbm_gbs=alg / (ms * 1e-3) / 1e9,
                 hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, sets=len(sets),
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
-                              traffic=None, kernel="segment_final (zero-order hold, softplus(delta + bias))"))
+                              traffic=committed_traffic("scan_var", f"traffic_{name}.md"),
+                              kernel="segment_final (zero-order hold, softplus(delta + bias))"))
 
 
 # ------------------------------------------------------------------ scan backward
