@@ -31,8 +31,10 @@
 // N >= 64 (64, 128, 256): a lane's 64 states and 64 entries of A would fill its
 // registers, so the state index is cut into chunks of 16 that run as independent
 // chains (aggregate, carry and recurrence are independent across state indices);
-// the final pass writes each chunk's fp32 partial C . h to the workspace and a
-// fourth launch (combine_partials) adds the chunks, the skip and the gate.
+// the final pass (segment_final_sink: one workgroup holds the chunk waves of a
+// segment and 64 channels) adds the chunks' partial C . h in LDS and writes one
+// fp32 sum per (t, channel); a fourth launch (combine_partials) adds the skip and
+// applies the gate.
 #pragma once
 #include "common.h"
 #include "launch.h"
@@ -103,7 +105,7 @@ Geom geom(int B, int L, int D, int N) {
 //   GH [B][G-1][N][D] aggregate end state of each group (from zero); group_carry
 //                     overwrites slot g with the state entering group g+1
 //   GP [B][G-1][N][D] aggregate decay of each group
-//   YP [N/16][B][L][D] fp32 partial C . h of each state chunk (N >= 64 only)
+//   YP [B][L][D]      fp32 C . h summed over the state chunks (N >= 64 only)
 struct WsLayout {
     size_t E, CS, GH, GP, YP, total;
 };
@@ -193,8 +195,9 @@ __device__ __forceinline__ float var_delta(float dv, const VarLane<N, V>& vl) {
 // One wave's segment of the recurrence. Construction issues the first loads
 // (kPrefetch steps of x, Delta[, z] and the first B[, C] rows), so a caller can
 // start them before other prologue work; run() then walks the segment.
-template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL, bool PARTIAL = false, int V = 0>
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL, bool PARTIAL = false, int V = 0, bool SINK = false>
 struct Segment {
+    static_assert(!SINK || (PARTIAL && V == 0), "the LDS sink holds plain partial sums");
     static constexpr uint32_t es = BF16 ? 2 : 4;
     static constexpr bool kZ = FINAL && HAS_Z;
     __amdgpu_buffer_rsrc_t rx, rd, rz, ry;
@@ -203,6 +206,7 @@ struct Segment {
     const void* Cbase;
     int rw;  // row stride of B and C in 32-bit words
     int len;
+    float* lsink = nullptr;  // SINK: ring slot k's partial sums go to lsink[64 k + lane]
     uint32_t dq[kPrefetch], xq[kPrefetch], zq[kPrefetch];
     Row<N, BF16> Bn, Cn;
 
@@ -312,7 +316,9 @@ struct Segment {
                     else y0 = __builtin_fmaf(Ct.at(n), h[n], y0);
                 }
                 float v = y0 + y1;
-                if constexpr (PARTIAL) {
+                if constexpr (SINK) {
+                    lsink[k * 64 + (threadIdx.x & 63)] = v;
+                } else if constexpr (PARTIAL) {
                     store_io<false>(ry, yoff, (uint32_t)t * ystride, v);
                 } else {
                     if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
@@ -565,14 +571,103 @@ segment_final(ScanArgs a, Geom g) {
     }
 }
 
+// N >= 64: one workgroup per (segment, 64 channels, batch) holds the N / 16 state
+// chunks of the segment, one wave each. Every kPrefetch steps the waves leave their
+// partial C . h sums in LDS (two slots, alternating), meet at a barrier, and the
+// workgroup adds them in chunk order into one fp32 sum per (t, channel), written to
+// YP; combine_partials then adds D x and applies the gate.
+template <bool BF16>
+__global__ void __launch_bounds__(1024)
+segment_final_sink(ScanArgs a, Geom g) {
+    extern __shared__ float lds[];
+    constexpr int N = kChunkN;
+    const int nch = a.N / N;
+    const int nc = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n0 = nc * N;
+    const int s = blockIdx.x, b = blockIdx.z;
+    const int D = a.D, NT = a.N;
+    const int d = blockIdx.y * 64 + lane;
+    const int dc = d < D ? d : D - 1;
+    const int grp = s / g.W, win = s % g.W;
+    const int t0 = s * g.Ls;
+    const int len = min(g.Ls, a.L - t0);
+    const WsLayout wl = ws_layout(a.B, D, NT, g.S, g.G);
+    const float* ws = static_cast<const float*>(a.ws);
+    float* yp = static_cast<float*>(a.ws) + wl.YP;
+
+    Segment<N, BF16, false, false, true, true, 0, true> seg(a, b, dc, t0, len, n0, d < D, yp);
+    float A2[N], hg[N], E[N];
+    float cs = 0.0f;
+#pragma unroll
+    for (int n = 0; n < N; ++n) A2[n] = a.A[(size_t)dc * NT + n0 + n] * kLog2e;
+    if (grp > 0) {
+        const float* cp = ws + wl.GH + (((size_t)b * (g.G - 1) + grp - 1) * NT + n0) * D + dc;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = cp[(size_t)n * D];
+    } else if (a.h0 != nullptr) {
+        const float* hp = a.h0 + ((size_t)b * D + dc) * NT + n0;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = hp[n];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) hg[n] = 0.0f;
+    }
+    if (win > 0) {
+        cs = ws[wl.CS + ((size_t)b * g.S + s) * D + dc];
+        const float* Ep = ws + wl.E + (((size_t)b * g.S + s) * NT + n0) * D + dc;
+#pragma unroll
+        for (int n = 0; n < N; ++n) E[n] = Ep[(size_t)n * D];
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) E[n] = 0.0f;
+    }
+    float h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hg[n], E[n]);
+    float unused = 0.0f;
+    VarLane<N, 0> vl;
+    var_lane_init<N, 0>(vl, a, dc, n0);
+    // the sums of the steps [tb, tb + cnt) from LDS slot `slot`, in chunk order
+    auto reduce = [&](int slot, int tb, int cnt) {
+        const float* base = lds + (size_t)slot * nch * kPrefetch * 64;
+        for (int o = threadIdx.x; o < cnt * 64; o += nch * 64) {
+            const int k = o >> 6, l = o & 63, dd = blockIdx.y * 64 + l;
+            float v = 0.0f;
+            for (int c = 0; c < nch; ++c) v += base[(c * kPrefetch + k) * 64 + l];
+            if (dd < D) yp[((size_t)b * a.L + t0 + tb + k) * D + dd] = v;
+        }
+    };
+    int t = 0, j = 0;
+    for (; t + kPrefetch <= len; t += kPrefetch, ++j) {
+        seg.lsink = lds + ((size_t)(j & 1) * nch + nc) * kPrefetch * 64;
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) seg.template step<true>(t + k, k, A2, h, 0.0f, unused, vl);
+        __syncthreads();
+        reduce(j & 1, t, kPrefetch);
+    }
+    if (t < len) {
+        seg.lsink = lds + ((size_t)(j & 1) * nch + nc) * kPrefetch * 64;
+#pragma unroll
+        for (int k = 0; k < kPrefetch - 1; ++k)
+            if (t + k < len) seg.template step<false>(t + k, k, A2, h, 0.0f, unused, vl);
+        __syncthreads();
+        reduce(j & 1, t, len - t);
+    }
+    if (d < D && s == g.S - 1 && a.h_final != nullptr) {
+        float* hp = a.h_final + ((size_t)b * D + d) * NT + n0;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hp[n] = h[n];
+    }
+}
+
 // L == 0: the final state is the initial state.
 __global__ void copy_state(const float* __restrict__ h0, float* __restrict__ out, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) out[i] = h0 ? h0[i] : 0.0f;
 }
 
-// N > 64: y = (sum over the state chunks of their partial C . h + D x) silu(z),
-// one thread per (b, t, d).
+// N >= 64: y = (C . h summed over the state chunks + D x) silu(z), one thread per
+// (b, t, d); nch planes of sums are added in plane order (one plane as launched).
 template <bool BF16, bool HAS_Z, bool HAS_D>
 __global__ void __launch_bounds__(256)
 combine_partials(ScanArgs a, const float* __restrict__ yp, int nch) {
@@ -623,14 +718,16 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     if (nch > 1) {
-        launch((segment_final<N, BF16, false, false, true>), grid, block, 0, st, a, g);
+        const dim3 sgrid((unsigned)g.S, (unsigned)((a.D + 63) / 64), (unsigned)a.B);
+        const size_t lds_sink = (size_t)2 * nch * kPrefetch * 64 * sizeof(float);
+        launch((segment_final_sink<BF16>), sgrid, dim3(64 * nch), (uint32_t)lds_sink, st, a, g);
         const float* yp = static_cast<const float*>(a.ws) + ws_layout(a.B, a.D, a.N, g.S, g.G).YP;
         const size_t tot = (size_t)a.B * a.L * a.D;
         const dim3 cg((unsigned)((tot + 255) / 256));
-        if (hz && hd) launch((combine_partials<BF16, true, true>), cg, dim3(256), 0, st, a, yp, nch);
-        else if (hz) launch((combine_partials<BF16, true, false>), cg, dim3(256), 0, st, a, yp, nch);
-        else if (hd) launch((combine_partials<BF16, false, true>), cg, dim3(256), 0, st, a, yp, nch);
-        else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, nch);
+        if (hz && hd) launch((combine_partials<BF16, true, true>), cg, dim3(256), 0, st, a, yp, 1);
+        else if (hz) launch((combine_partials<BF16, true, false>), cg, dim3(256), 0, st, a, yp, 1);
+        else if (hd) launch((combine_partials<BF16, false, true>), cg, dim3(256), 0, st, a, yp, 1);
+        else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, 1);
         return hipGetLastError();
     }
     if (hz && hd) launch((segment_final<N, BF16, true, true, false>), grid, block, 0, st, a, g);
