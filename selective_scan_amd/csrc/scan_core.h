@@ -31,10 +31,10 @@
 // N >= 64 (64, 128, 256): a lane's 64 states and 64 entries of A would fill its
 // registers, so the state index is cut into chunks of 16 that run as independent
 // chains (aggregate, carry and recurrence are independent across state indices);
-// the final pass (segment_final_sink: one workgroup holds the chunk waves of a
+// the final pass (segment_final_sink: one workgroup holds up to 8 chunk waves of a
 // segment and 64 channels) adds the chunks' partial C . h in LDS and writes one
-// fp32 sum per (t, channel); a fourth launch (combine_partials) adds the skip and
-// applies the gate.
+// fp32 sum per (t, channel) and chunk group; a fourth launch (combine_partials)
+// adds the groups' sums, the skip and the gate.
 #pragma once
 #include "common.h"
 #include "launch.h"
@@ -105,7 +105,8 @@ Geom geom(int B, int L, int D, int N) {
 //   GH [B][G-1][N][D] aggregate end state of each group (from zero); group_carry
 //                     overwrites slot g with the state entering group g+1
 //   GP [B][G-1][N][D] aggregate decay of each group
-//   YP [B][L][D]      fp32 C . h summed over the state chunks (N >= 64 only)
+//   YP [P][B][L][D]   fp32 C . h summed over each group of up to 8 state chunks
+//                     (P = sink_planes(N) groups; N >= 64 only)
 struct WsLayout {
     size_t E, CS, GH, GP, YP, total;
 };
@@ -571,29 +572,36 @@ segment_final(ScanArgs a, Geom g) {
     }
 }
 
-// N >= 64: one workgroup per (segment, 64 channels, batch) holds the N / 16 state
-// chunks of the segment, one wave each. Every kPrefetch steps the waves leave their
-// partial C . h sums in LDS (two slots, alternating), meet at a barrier, and the
-// workgroup adds them in chunk order into one fp32 sum per (t, channel), written to
-// YP; combine_partials then adds D x and applies the gate.
+// N >= 64: one workgroup per (segment, 64 channels, batch, group of up to
+// kSinkChunks state chunks) holds those chunks of the segment, one wave each. Every
+// kPrefetch steps the waves leave their partial C . h sums in LDS (two slots,
+// alternating), meet at a barrier, and the workgroup adds them in chunk order into
+// one fp32 sum per (t, channel), written to its chunk group's plane of YP;
+// combine_partials then adds the planes, D x and the gate.
+constexpr int kSinkChunks = 8;
+inline int sink_planes(int N) { return std::max(1, n_chunks(N) / kSinkChunks); }
+
 template <bool BF16>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(64 * kSinkChunks)
 segment_final_sink(ScanArgs a, Geom g) {
     extern __shared__ float lds[];
     constexpr int N = kChunkN;
-    const int nch = a.N / N;
-    const int nc = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int nch = blockDim.x >> 6;             // chunks in this workgroup
+    const int ngrp = (a.N / N) / nch;            // chunk groups (planes of YP)
+    const int cg = blockIdx.y % ngrp, dblk = blockIdx.y / ngrp;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int nc = cg * nch + wave;
     const int n0 = nc * N;
     const int s = blockIdx.x, b = blockIdx.z;
     const int D = a.D, NT = a.N;
-    const int d = blockIdx.y * 64 + lane;
+    const int d = dblk * 64 + lane;
     const int dc = d < D ? d : D - 1;
     const int grp = s / g.W, win = s % g.W;
     const int t0 = s * g.Ls;
     const int len = min(g.Ls, a.L - t0);
     const WsLayout wl = ws_layout(a.B, D, NT, g.S, g.G);
     const float* ws = static_cast<const float*>(a.ws);
-    float* yp = static_cast<float*>(a.ws) + wl.YP;
+    float* yp = static_cast<float*>(a.ws) + wl.YP + (size_t)cg * a.B * a.L * D;
 
     Segment<N, BF16, false, false, true, true, 0, true> seg(a, b, dc, t0, len, n0, d < D, yp);
     float A2[N], hg[N], E[N];
@@ -631,7 +639,7 @@ segment_final_sink(ScanArgs a, Geom g) {
     auto reduce = [&](int slot, int tb, int cnt) {
         const float* base = lds + (size_t)slot * nch * kPrefetch * 64;
         for (int o = threadIdx.x; o < cnt * 64; o += nch * 64) {
-            const int k = o >> 6, l = o & 63, dd = blockIdx.y * 64 + l;
+            const int k = o >> 6, l = o & 63, dd = dblk * 64 + l;
             float v = 0.0f;
             for (int c = 0; c < nch; ++c) v += base[(c * kPrefetch + k) * 64 + l];
             if (dd < D) yp[((size_t)b * a.L + t0 + tb + k) * D + dd] = v;
@@ -639,14 +647,14 @@ segment_final_sink(ScanArgs a, Geom g) {
     };
     int t = 0, j = 0;
     for (; t + kPrefetch <= len; t += kPrefetch, ++j) {
-        seg.lsink = lds + ((size_t)(j & 1) * nch + nc) * kPrefetch * 64;
+        seg.lsink = lds + ((size_t)(j & 1) * nch + wave) * kPrefetch * 64;
 #pragma unroll
         for (int k = 0; k < kPrefetch; ++k) seg.template step<true>(t + k, k, A2, h, 0.0f, unused, vl);
         __syncthreads();
         reduce(j & 1, t, kPrefetch);
     }
     if (t < len) {
-        seg.lsink = lds + ((size_t)(j & 1) * nch + nc) * kPrefetch * 64;
+        seg.lsink = lds + ((size_t)(j & 1) * nch + wave) * kPrefetch * 64;
 #pragma unroll
         for (int k = 0; k < kPrefetch - 1; ++k)
             if (t + k < len) seg.template step<false>(t + k, k, A2, h, 0.0f, unused, vl);
@@ -667,7 +675,7 @@ __global__ void copy_state(const float* __restrict__ h0, float* __restrict__ out
 }
 
 // N >= 64: y = (C . h summed over the state chunks + D x) silu(z), one thread per
-// (b, t, d); nch planes of sums are added in plane order (one plane as launched).
+// (b, t, d); the nch planes of sums are added in plane order.
 template <bool BF16, bool HAS_Z, bool HAS_D>
 __global__ void __launch_bounds__(256)
 combine_partials(ScanArgs a, const float* __restrict__ yp, int nch) {
@@ -718,16 +726,17 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     if (nch > 1) {
-        const dim3 sgrid((unsigned)g.S, (unsigned)((a.D + 63) / 64), (unsigned)a.B);
-        const size_t lds_sink = (size_t)2 * nch * kPrefetch * 64 * sizeof(float);
-        launch((segment_final_sink<BF16>), sgrid, dim3(64 * nch), (uint32_t)lds_sink, st, a, g);
+        const int planes = sink_planes(a.N), cpw = nch / planes;
+        const dim3 sgrid((unsigned)g.S, (unsigned)(((a.D + 63) / 64) * planes), (unsigned)a.B);
+        const size_t lds_sink = (size_t)2 * cpw * kPrefetch * 64 * sizeof(float);
+        launch((segment_final_sink<BF16>), sgrid, dim3(64 * cpw), (uint32_t)lds_sink, st, a, g);
         const float* yp = static_cast<const float*>(a.ws) + ws_layout(a.B, a.D, a.N, g.S, g.G).YP;
         const size_t tot = (size_t)a.B * a.L * a.D;
         const dim3 cg((unsigned)((tot + 255) / 256));
-        if (hz && hd) launch((combine_partials<BF16, true, true>), cg, dim3(256), 0, st, a, yp, 1);
-        else if (hz) launch((combine_partials<BF16, true, false>), cg, dim3(256), 0, st, a, yp, 1);
-        else if (hd) launch((combine_partials<BF16, false, true>), cg, dim3(256), 0, st, a, yp, 1);
-        else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, 1);
+        if (hz && hd) launch((combine_partials<BF16, true, true>), cg, dim3(256), 0, st, a, yp, planes);
+        else if (hz) launch((combine_partials<BF16, true, false>), cg, dim3(256), 0, st, a, yp, planes);
+        else if (hd) launch((combine_partials<BF16, false, true>), cg, dim3(256), 0, st, a, yp, planes);
+        else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, planes);
         return hipGetLastError();
     }
     if (hz && hd) launch((segment_final<N, BF16, true, true, false>), grid, block, 0, st, a, g);
