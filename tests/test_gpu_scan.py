@@ -31,7 +31,8 @@ SMALL = [
     (2, 513, 200, 64, si.BF16, True, True, True),
     (1, 4097, 96, 16, si.BF16, False, True, False),
     (5, 77, 1, 16, si.F32, True, True, True),
-    # N above 64: the state index runs in chunks of 64 (partial C . h, then a combine)
+    # N >= 64: the state index runs in chunks of 16 states whose C . h sums a workgroup
+    # adds in LDS (two groups of eight chunks at N = 256), then a combine
     (2, 700, 90, 128, si.BF16, True, True, True),
     (1, 1500, 64, 256, si.F32, True, False, True),
     (1, 40, 33, 128, si.F32, False, True, False),
