@@ -196,9 +196,9 @@ __device__ __forceinline__ float var_delta(float dv, const VarLane<N, V>& vl) {
 // One wave's segment of the recurrence. Construction issues the first loads
 // (kPrefetch steps of x, Delta[, z] and the first B[, C] rows), so a caller can
 // start them before other prologue work; run() then walks the segment.
-template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL, bool PARTIAL = false, int V = 0, bool SINK = false>
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL, int V = 0, bool SINK = false>
 struct Segment {
-    static_assert(!SINK || (PARTIAL && V == 0), "the LDS sink holds plain partial sums");
+    static_assert(!SINK || (FINAL && V == 0), "the LDS sink holds plain partial sums");
     static constexpr uint32_t es = BF16 ? 2 : 4;
     static constexpr bool kZ = FINAL && HAS_Z;
     __amdgpu_buffer_rsrc_t rx, rd, rz, ry;
@@ -213,10 +213,10 @@ struct Segment {
 
     // store: this lane's channel exists (d < D); other lanes aim their y stores
     // past the end of the y view, where the buffer unit drops them (no branch).
-    // The lane's states are n0 .. n0 + N - 1 of a.N. PARTIAL: y is the fp32
-    // C . h of these states only, written to `yp` ([B][L][D] of this chunk).
+    // The lane's states are n0 .. n0 + N - 1 of a.N. SINK: the fp32 C . h of these
+    // states only goes to LDS (lsink) instead of y.
     __device__ __forceinline__ Segment(const ScanArgs& a, int b, int dc, int t0, int len_, int n0,
-                                       bool store = true, float* yp = nullptr)
+                                       bool store = true)
         : len(len_) {
         const size_t row0 = (size_t)b * a.L + t0;
         const uint32_t bytes = (uint32_t)len * (uint32_t)a.D * es;
@@ -224,15 +224,9 @@ struct Segment {
         rx = make_rsrc(xb, bytes);
         rd = make_rsrc(static_cast<const char*>(a.delta) + row0 * a.D * es, bytes);
         rz = make_rsrc(kZ ? static_cast<const char*>(a.z) + row0 * a.D * es : xb, bytes);
-        if constexpr (PARTIAL) {
-            ry = make_rsrc(yp + row0 * a.D, (uint32_t)len * (uint32_t)a.D * 4u);
-            yoff = store ? (uint32_t)dc * 4u : 0x80000000u;
-            ystride = (uint32_t)a.D * 4u;
-        } else {
-            ry = make_rsrc(FINAL ? static_cast<const char*>(a.y) + row0 * a.D * es : xb, bytes);
-            yoff = store ? (uint32_t)dc * es : 0x80000000u;
-            ystride = (uint32_t)a.D * es;
-        }
+        ry = make_rsrc(FINAL ? static_cast<const char*>(a.y) + row0 * a.D * es : xb, bytes);
+        yoff = store ? (uint32_t)dc * es : 0x80000000u;
+        ystride = (uint32_t)a.D * es;
         voff = (uint32_t)dc * es;
         rstride = (uint32_t)a.D * es;
         Bbase = static_cast<const char*>(a.Bm) + (row0 * a.N + n0) * es;
@@ -319,8 +313,6 @@ struct Segment {
                 float v = y0 + y1;
                 if constexpr (SINK) {
                     lsink[k * 64 + (threadIdx.x & 63)] = v;
-                } else if constexpr (PARTIAL) {
-                    store_io<false>(ry, yoff, (uint32_t)t * ystride, v);
                 } else {
                     if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
                     if constexpr (HAS_Z) v *= silu(zv);
@@ -348,13 +340,9 @@ struct Segment {
         }
         if constexpr (FINAL) {
             float v = y0 + y1;
-            if constexpr (PARTIAL) {
-                store_io<false>(ry, yoff, (uint32_t)t * ystride, v);
-            } else {
-                if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
-                if constexpr (HAS_Z) v *= silu(zv);
-                store_io<BF16>(ry, yoff, (uint32_t)t * ystride, v);
-            }
+            if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
+            if constexpr (HAS_Z) v *= silu(zv);
+            store_io<BF16>(ry, yoff, (uint32_t)t * ystride, v);
         } else {
             sumd += dv;
         }
@@ -402,7 +390,7 @@ segment_aggregate(ScanArgs a, Geom g) {
     VarLane<N, V> vl;
     var_lane_init<N, V>(vl, a, dc, n0);
     if (len > 0) {
-        Segment<N, BF16, false, false, false, false, V> seg(a, b, dc, t0, len, n0);
+        Segment<N, BF16, false, false, false, V> seg(a, b, dc, t0, len, n0);
         seg.run(A2, h, 0.0f, sumd, vl);
     }
     // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]; a segment past L is the identity (1, 0).
@@ -509,7 +497,7 @@ group_carry(const float* __restrict__ h0, float* ws, int B, int D, int N, Geom g
     }
 }
 
-template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool PARTIAL, int V = 0>
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, int V = 0>
 __global__ void __launch_bounds__(64 * SSM_SCAN_MAX_GROUP)
 segment_final(ScanArgs a, Geom g) {
     const int W = g.W;
@@ -525,12 +513,10 @@ segment_final(ScanArgs a, Geom g) {
     const int len = min(g.Ls, a.L - t0);
     const WsLayout wl = ws_layout(a.B, D, NT, g.S, g.G);
     const float* ws = static_cast<const float*>(a.ws);
-    // this chunk's [B][L][D] partial sums; the segment adds its own (b, t0) row offset
-    float* yp = PARTIAL ? static_cast<float*>(a.ws) + wl.YP + (size_t)nc * a.B * a.L * D : nullptr;
 
     // every load that does not depend on the recurrence first: the segment's
     // first inputs, A, the state entering the group and the in-group prefix
-    Segment<N, BF16, HAS_Z, HAS_D, true, PARTIAL, V> seg(a, b, dc, t0, len, n0, d < D, yp);
+    Segment<N, BF16, HAS_Z, HAS_D, true, V> seg(a, b, dc, t0, len, n0, d < D);
     float A2[N], hg[N], E[N];
     float cs = 0.0f;
 #pragma unroll
@@ -603,7 +589,7 @@ segment_final_sink(ScanArgs a, Geom g) {
     const float* ws = static_cast<const float*>(a.ws);
     float* yp = static_cast<float*>(a.ws) + wl.YP + (size_t)cg * a.B * a.L * D;
 
-    Segment<N, BF16, false, false, true, true, 0, true> seg(a, b, dc, t0, len, n0, d < D, yp);
+    Segment<N, BF16, false, false, true, 0, true> seg(a, b, dc, t0, len, n0, d < D);
     float A2[N], hg[N], E[N];
     float cs = 0.0f;
 #pragma unroll
@@ -739,10 +725,10 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
         else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, planes);
         return hipGetLastError();
     }
-    if (hz && hd) launch((segment_final<N, BF16, true, true, false>), grid, block, 0, st, a, g);
-    else if (hz) launch((segment_final<N, BF16, true, false, false>), grid, block, 0, st, a, g);
-    else if (hd) launch((segment_final<N, BF16, false, true, false>), grid, block, 0, st, a, g);
-    else launch((segment_final<N, BF16, false, false, false>), grid, block, 0, st, a, g);
+    if (hz && hd) launch((segment_final<N, BF16, true, true>), grid, block, 0, st, a, g);
+    else if (hz) launch((segment_final<N, BF16, true, false>), grid, block, 0, st, a, g);
+    else if (hd) launch((segment_final<N, BF16, false, true>), grid, block, 0, st, a, g);
+    else launch((segment_final<N, BF16, false, false>), grid, block, 0, st, a, g);
     return hipGetLastError();
 }
 
@@ -766,8 +752,8 @@ hipError_t launch_var(const ScanArgs& a, hipStream_t st) {
         launch(group_carry, dim3((unsigned)((a.D + 63) / 64), (unsigned)a.N, (unsigned)a.B), dim3(256), 0, st,
                a.h0, static_cast<float*>(a.ws), a.B, a.D, a.N, g);
     }
-    if (a.z != nullptr) launch((segment_final<N, BF16, true, true, false, V>), grid, block, 0, st, a, g);
-    else launch((segment_final<N, BF16, false, true, false, V>), grid, block, 0, st, a, g);
+    if (a.z != nullptr) launch((segment_final<N, BF16, true, true, V>), grid, block, 0, st, a, g);
+    else launch((segment_final<N, BF16, false, true, V>), grid, block, 0, st, a, g);
     return hipGetLastError();
 }
 
