@@ -57,13 +57,17 @@ extern "C" {
 
 #define SSM_ABI_VERSION 1
 
-typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+/* Storage type of the io tensors. The last enumerator only widens the type to a
+ * full int, so any int a caller passes is a valid value (out-of-range values are
+ * rejected with SSM_ERR_INVALID_ARG). */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1, SSM_DTYPE_INT_RANGE_ = 0x7fffffff } ssm_dtype_t;
 
 /* Discretisation of the continuous system dh/dt = A h + B x over one step Delta
  * (diagonal A). Exponential-Euler is what every entry point uses by default. */
 typedef enum {
     SSM_DISC_EULER = 0, /* Abar = exp(Delta A), Bbar = Delta B */
-    SSM_DISC_ZOH = 1    /* Abar = exp(z), Bbar = Delta B (e^z - 1)/z, z = Delta A (exact zero-order hold) */
+    SSM_DISC_ZOH = 1,   /* Abar = exp(z), Bbar = Delta B (e^z - 1)/z, z = Delta A (exact zero-order hold) */
+    SSM_DISC_INT_RANGE_ = 0x7fffffff
 } ssm_disc_t;
 
 typedef enum {
@@ -98,6 +102,18 @@ int ssm_profile_events(void* const* events, int n);
 /* ---------------------------------------------------------------------------
  * ssm_scan_fwd -- Mamba-1 selective scan (prefill).
  *
+ * Defined by "Efficient Sequence Modeling: From S4 to Mamba-3", section 03
+ * System (mamba_minimal.py: input-dependent Delta, B, C and an explicit
+ * time-loop selective scan), with the exponential-Euler discretisation the
+ * same page names as the lambda = 1, theta = 0 limit (section 04, "Complex
+ * transitions for state tracking"; section 09 Validation). Per (b, d), over
+ * t = 0 .. L-1, from h = h0[b, d, :] (or zeros):
+ *   h[n]      = exp(delta[b,t,d] * A[d,n]) * h[n] + delta[b,t,d] * Bm[b,t,n] * x[b,t,d]
+ *   y[b,t,d]  = (sum_n Cm[b,t,n] * h[n] + Dskip[d] * x[b,t,d]) * silu(z[b,t,d])
+ *   h_final[b, d, :] = h after the last step.
+ * The work is cut along L into segments whose carried states compose as affine
+ * maps; the result equals the sequential recurrence up to rounding.
+ *
  *   x, delta, z, y : [B, L, D]  io dtype     (z may be NULL)
  *   A              : [D, N]     fp32, A < 0 as used in exp(delta * A)
  *   Bm, Cm         : [B, L, N]  io dtype, shared by all D channels
@@ -113,7 +129,7 @@ int ssm_profile_events(void* const* events, int n);
  * ------------------------------------------------------------------------- */
 size_t ssm_scan_workspace_size(int B, int L, int D, int N);
 
-int ssm_scan_fwd(int B, int L, int D, int N, int io,
+int ssm_scan_fwd(int B, int L, int D, int N, ssm_dtype_t io,
                  const void* x, const void* delta, const float* A,
                  const void* Bm, const void* Cm, const float* Dskip,
                  const void* z, const float* h0,
@@ -136,7 +152,7 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
  * ssm_scan_fwd. The options need N in {4, 8, 16, 32} (SSM_ERR_UNSUPPORTED
  * otherwise). delta_bias must be 16-byte aligned.
  * ------------------------------------------------------------------------- */
-int ssm_scan_fwd_ex(int B, int L, int D, int N, int io, int disc,
+int ssm_scan_fwd_ex(int B, int L, int D, int N, ssm_dtype_t io, ssm_disc_t disc,
                     const float* delta_bias, int delta_softplus,
                     const void* x, const void* delta, const float* A,
                     const void* Bm, const void* Cm, const float* Dskip,
@@ -176,7 +192,7 @@ int ssm_scan_fwd_ex(int B, int L, int D, int N, int io, int disc,
  * ------------------------------------------------------------------------- */
 size_t ssm_scan_bwd_workspace_size(int B, int L, int D, int N);
 
-int ssm_scan_bwd(int B, int L, int D, int N, int io,
+int ssm_scan_bwd(int B, int L, int D, int N, ssm_dtype_t io,
                  const void* x, const void* delta, const float* A,
                  const void* Bm, const void* Cm, const float* Dskip,
                  const void* z, const float* h0,
@@ -187,6 +203,18 @@ int ssm_scan_bwd(int B, int L, int D, int N, int io,
 
 /* ---------------------------------------------------------------------------
  * ssm_ssd_fwd -- Mamba-2 SSD chunked scan (prefill), scalar decay per head.
+ *
+ * Defined by "Efficient Sequence Modeling: From S4 to Mamba-3", section 03
+ * System (mamba2_minimal.py: a scalar A per head reduces the recurrence to SSD,
+ * computed as chunked decayed-attention matmuls with a carried (N, P) state)
+ * and section 04 "Chunked SSD with a sequential reference" (the chunked form
+ * equals the sequential recurrence). Per (b, h), from S = h0[b, h] (or zeros):
+ *   S[n, p]    = exp(delta[b,t,h] * A[h]) * S[n, p] + delta[b,t,h] * Bm[b,t,n] * x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n Cm[b,t,n] * S[n, p] + Dskip[h] * x[b,t,h,p]) * silu(z[b,t,h,p])
+ *   h_final[b, h] = S after the last step.
+ * Inside a chunk, with s_i the inclusive prefix of delta * A_h:
+ *   y_i = sum_{j <= i} (C_i . B_j) exp(s_i - s_j) delta_j x_j + exp(s_i) C_i S_in (+ skip, gate);
+ *   S_out = exp(s_last) S_in + sum_j exp(s_last - s_j) delta_j B_j^T x_j.
  *
  *   x, z, y : [B, L, H, P]  io dtype     (z may be NULL)
  *   delta   : [B, L, H]     io dtype
@@ -203,7 +231,7 @@ int ssm_scan_bwd(int B, int L, int D, int N, int io,
  * ------------------------------------------------------------------------- */
 size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk);
 
-int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
+int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, ssm_dtype_t io,
                 const void* x, const void* delta, const float* A,
                 const void* Bm, const void* Cm, const float* Dskip,
                 const void* z, const float* h0,
@@ -213,6 +241,11 @@ int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
 /* ---------------------------------------------------------------------------
  * ssm_step -- one-token recurrent decode step, state read and written in place.
  *
+ * Defined by "Efficient Sequence Modeling: From S4 to Mamba-3", section 03
+ * System (mamba_minimal.py's incremental step() for decoding) and section 09
+ * Validation (step() equals a full forward): one iteration of the ssm_scan_fwd
+ * recurrence above, per (b, d), on the state [b, d, :] held in place.
+ *
  *   state  : [B, D, N]  fp32, updated in place
  *   x, delta, z, y : [B, D]  io dtype   (z may be NULL)
  *   A      : [D, N]  fp32
@@ -220,7 +253,7 @@ int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
  *   Dskip  : [D]     fp32 or NULL
  * Supported: N in {4, 8, 16, 32, 64, 128, 256}; B <= 65535; D * N <= 2^32.
  * ------------------------------------------------------------------------- */
-int ssm_step(int B, int D, int N, int io,
+int ssm_step(int B, int D, int N, ssm_dtype_t io,
              float* state, const void* x, const void* delta, const float* A,
              const void* Bm, const void* Cm, const float* Dskip, const void* z,
              void* y, void* stream);
@@ -228,7 +261,7 @@ int ssm_step(int B, int D, int N, int io,
 /* ssm_step_ex -- ssm_step with disc, delta_bias and delta_softplus as in
  * ssm_scan_fwd_ex (all N of ssm_step), so a sequence prefilled with
  * ssm_scan_fwd_ex continues token by token with the same options. */
-int ssm_step_ex(int B, int D, int N, int io, int disc,
+int ssm_step_ex(int B, int D, int N, ssm_dtype_t io, ssm_disc_t disc,
                 const float* delta_bias, int delta_softplus,
                 float* state, const void* x, const void* delta, const float* A,
                 const void* Bm, const void* Cm, const float* Dskip, const void* z,
@@ -251,7 +284,7 @@ int ssm_step_ex(int B, int D, int N, int io, int disc,
  * Supported: P = 64; N in {16, 32, 64, 128, 256}; B * H <= 2^31 - 1.
  * Errors as for ssm_step; every pointer must be 16-byte aligned.
  * ------------------------------------------------------------------------- */
-int ssm_ssd_step(int B, int H, int P, int N, int io,
+int ssm_ssd_step(int B, int H, int P, int N, ssm_dtype_t io,
                  float* state, const void* x, const void* delta, const float* A,
                  const void* Bm, const void* Cm, const float* Dskip, const void* z,
                  void* y, void* stream);

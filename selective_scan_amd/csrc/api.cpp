@@ -163,7 +163,7 @@ int step_impl(const char* fn, int B, int D, int N, int io, int disc, const float
 
 extern "C" {
 
-int ssm_scan_fwd(int B, int L, int D, int N, int io,
+int ssm_scan_fwd(int B, int L, int D, int N, ssm_dtype_t io,
                  const void* x, const void* delta, const float* A,
                  const void* Bm, const void* Cm, const float* Dskip,
                  const void* z, const float* h0,
@@ -173,7 +173,7 @@ int ssm_scan_fwd(int B, int L, int D, int N, int io,
                          z, h0, y, h_final, workspace, workspace_bytes, stream);
 }
 
-int ssm_scan_fwd_ex(int B, int L, int D, int N, int io, int disc,
+int ssm_scan_fwd_ex(int B, int L, int D, int N, ssm_dtype_t io, ssm_disc_t disc,
                     const float* delta_bias, int delta_softplus,
                     const void* x, const void* delta, const float* A,
                     const void* Bm, const void* Cm, const float* Dskip,
@@ -191,7 +191,7 @@ size_t ssm_scan_bwd_workspace_size(int B, int L, int D, int N) {
     return ssm::scan_bwd_workspace_bytes(B, L, D, N);
 }
 
-int ssm_scan_bwd(int B, int L, int D, int N, int io,
+int ssm_scan_bwd(int B, int L, int D, int N, ssm_dtype_t io,
                  const void* x, const void* delta, const float* A,
                  const void* Bm, const void* Cm, const float* Dskip,
                  const void* z, const float* h0,
@@ -237,7 +237,7 @@ size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk) {
     return ssm::ssd_workspace_bytes(B, L, H, P, N, Q);
 }
 
-int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
+int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, ssm_dtype_t io,
                 const void* x, const void* delta, const float* A,
                 const void* Bm, const void* Cm, const float* Dskip,
                 const void* z, const float* h0,
@@ -268,7 +268,7 @@ int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, int io,
 }
 
 // ------------------------------------------------------------------ step
-int ssm_step(int B, int D, int N, int io,
+int ssm_step(int B, int D, int N, ssm_dtype_t io,
              float* state, const void* x, const void* delta, const float* A,
              const void* Bm, const void* Cm, const float* Dskip, const void* z,
              void* y, void* stream) {
@@ -276,7 +276,7 @@ int ssm_step(int B, int D, int N, int io,
                      y, stream);
 }
 
-int ssm_step_ex(int B, int D, int N, int io, int disc,
+int ssm_step_ex(int B, int D, int N, ssm_dtype_t io, ssm_disc_t disc,
                 const float* delta_bias, int delta_softplus,
                 float* state, const void* x, const void* delta, const float* A,
                 const void* Bm, const void* Cm, const float* Dskip, const void* z,
@@ -286,7 +286,7 @@ int ssm_step_ex(int B, int D, int N, int io, int disc,
 }
 
 // ------------------------------------------------------------------ SSD step
-int ssm_ssd_step(int B, int H, int P, int N, int io,
+int ssm_ssd_step(int B, int H, int P, int N, ssm_dtype_t io,
                  float* state, const void* x, const void* delta, const float* A,
                  const void* Bm, const void* Cm, const float* Dskip, const void* z,
                  void* y, void* stream) {

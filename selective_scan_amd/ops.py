@@ -4,6 +4,7 @@ Argument checks here only concern the Python side (tensor device, dtype,
 contiguity, shapes); the library validates again before any HIP call and every
 non-OK status becomes an ``SsmError``.
 """
+import contextlib
 import ctypes
 import os
 
@@ -95,6 +96,14 @@ def _stream(device, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context for a call launched on ``stream``: tensors this binding
+    allocates (outputs, workspace) are taken from the caching allocator on the
+    launch stream itself, so a block freed on return (the workspace) is only handed
+    out again to work queued after these kernels on that stream."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _raise(fn, status):
     L = lib()
     raise SsmError(fn, status, L.ssm_last_error().decode())
@@ -137,15 +146,16 @@ def _scan_fwd(fn, x, delta, A, Bm, Cm, D, z, h0, y, h_final, workspace, stream, 
     _check(z, "z", (Bb, L, Dd), io, dev, required=False)
     _check(h0, "h0", (Bb, Dd, N), torch.float32, dev, required=False)
     _check(x, "x", (Bb, L, Dd), io, dev)
-    if y is None:
-        y = torch.empty((Bb, L, Dd), dtype=io, device=dev)
-    _check(y, "y", (Bb, L, Dd), io, dev)
-    if want_final_state and h_final is None:
-        h_final = torch.empty((Bb, Dd, N), dtype=torch.float32, device=dev)
-    _check(h_final, "h_final", (Bb, Dd, N), torch.float32, dev, required=False)
     need = ssm_scan_workspace_size(Bb, L, Dd, N)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((Bb, L, Dd), dtype=io, device=dev)
+        if want_final_state and h_final is None:
+            h_final = torch.empty((Bb, Dd, N), dtype=torch.float32, device=dev)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(y, "y", (Bb, L, Dd), io, dev)
+    _check(h_final, "h_final", (Bb, Dd, N), torch.float32, dev, required=False)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
             _ptr(h_final), _ptr(workspace), wbytes, _stream(dev, stream))
@@ -190,16 +200,17 @@ def ssm_scan_bwd(x, delta, A, Bm, Cm, dy, D=None, z=None, h0=None, dh_final=None
                   dz=((Bb, L, Dd), io), dh0=((Bb, Dd, N), torch.float32))
     wanted = dict(dD=D is not None, dz=z is not None, dh0=want_dh0)
     g = dict(out or {})
-    for k, (shp, dt) in shapes.items():
-        if not wanted.get(k, True):
-            g[k] = None
-            continue
-        if g.get(k) is None:
-            g[k] = torch.empty(shp, dtype=dt, device=dev)
-        _check(g[k], k, shp, dt, dev)
     need = ssm_scan_bwd_workspace_size(Bb, L, Dd, N)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        for k, (shp, dt) in shapes.items():
+            if not wanted.get(k, True):
+                g[k] = None
+                continue
+            if g.get(k) is None:
+                g[k] = torch.empty(shp, dtype=dt, device=dev)
+            _check(g[k], k, shp, dt, dev)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ssm_scan_bwd(Bb, L, Dd, N, _io_code(x), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm),
                             _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_final),
@@ -230,15 +241,16 @@ def ssm_ssd_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, chunk=0, y=None
     _check(D, "D", (H,), torch.float32, dev, required=False)
     _check(z, "z", (Bb, L, H, P), io, dev, required=False)
     _check(h0, "h0", (Bb, H, N, P), torch.float32, dev, required=False)
-    if y is None:
-        y = torch.empty((Bb, L, H, P), dtype=io, device=dev)
-    _check(y, "y", (Bb, L, H, P), io, dev)
-    if want_final_state and h_final is None:
-        h_final = torch.empty((Bb, H, N, P), dtype=torch.float32, device=dev)
-    _check(h_final, "h_final", (Bb, H, N, P), torch.float32, dev, required=False)
     need = ssm_ssd_workspace_size(Bb, L, H, P, N, chunk)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((Bb, L, H, P), dtype=io, device=dev)
+        if want_final_state and h_final is None:
+            h_final = torch.empty((Bb, H, N, P), dtype=torch.float32, device=dev)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(y, "y", (Bb, L, H, P), io, dev)
+    _check(h_final, "h_final", (Bb, H, N, P), torch.float32, dev, required=False)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().ssm_ssd_fwd(Bb, L, H, P, N, int(chunk), _io_code(x), _ptr(x), _ptr(delta), _ptr(A),
                            _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final),
@@ -274,7 +286,8 @@ def _step(fn, state, x, delta, A, Bm, Cm, D, z, y, stream, ex):
     _check(D, "D", (Dd,), torch.float32, dev, required=False)
     _check(z, "z", (Bb, Dd), io, dev, required=False)
     if y is None:
-        y = torch.empty((Bb, Dd), dtype=io, device=dev)
+        with _on(stream):
+            y = torch.empty((Bb, Dd), dtype=io, device=dev)
     _check(y, "y", (Bb, Dd), io, dev)
     args = (_ptr(state), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y),
             _stream(dev, stream))
@@ -303,7 +316,8 @@ def ssm_ssd_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=N
     _check(D, "D", (H,), torch.float32, dev, required=False)
     _check(z, "z", (Bb, H, P), io, dev, required=False)
     if y is None:
-        y = torch.empty((Bb, H, P), dtype=io, device=dev)
+        with _on(stream):
+            y = torch.empty((Bb, H, P), dtype=io, device=dev)
     _check(y, "y", (Bb, H, P), io, dev)
     st = lib().ssm_ssd_step(Bb, H, P, N, _io_code(x), _ptr(state), _ptr(x), _ptr(delta), _ptr(A),
                             _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream(dev, stream))

@@ -67,21 +67,20 @@ def test_scan_config_bf16_B1_L4096_D1536_N16():
     _check(w, what="c1")
 
 
-def test_scan_config_bf16_B8_L32768_D512_N16_sampled():
-    print("[scan] bf16 B8 L32768 D512 N16 (sampled channels)", flush=True)
+def test_scan_config_bf16_B8_L32768_D512_N16():
+    """The long-sequence workload in full: every y element (134 M) and the final state."""
+    print("[scan] bf16 B8 L32768 D512 N16 (every element)", flush=True)
     w = si.scan_inputs(8, 32768, 512, 16, dtype=si.BF16, seed=0)
-    sel = np.array([0, 1, 63, 64, 100, 255, 256, 300, 383, 384, 450, 510, 511])
-    _check(w, sel=sel, what="c2")
+    _check(w, what="c2")
 
 
 @pytest.mark.parametrize("N", [64, 128, 256])
-def test_scan_state_dim_sweep_bf16_B1_L4096_D1536_sampled(N):
-    """The state-dimension sweep (N = 64, 128, 256) at the headline layer's size;
-    oracle on 48 sampled channels (including the first and last)."""
-    print(f"[scan] bf16 B1 L4096 D1536 N{N} (48 sampled channels)", flush=True)
+def test_scan_state_dim_sweep_bf16_B1_L4096_D1536(N):
+    """The state-dimension sweep (N = 64, 128, 256) at the headline layer's size,
+    every channel against the oracle."""
+    print(f"[scan] bf16 B1 L4096 D1536 N{N} (every channel)", flush=True)
     w = si.scan_inputs(1, 4096, 1536, N, dtype=si.BF16, seed=0)
-    sel = np.unique(np.concatenate([[0, 1535], np.random.default_rng(N).choice(1536, 46, replace=False)]))
-    _check(w, sel=sel, what=f"N{N} sweep")
+    _check(w, what=f"N{N} sweep")
 
 
 def test_scan_split_carry_on_gpu():

@@ -44,10 +44,36 @@ def test_step_small(case):
     _run_steps(w, 12)
 
 
-def test_step_config_bf16_B64_D3072_N16():
-    print("[step] bf16 B64 D3072 N16, 25 chained steps", flush=True)
-    w = si.step_inputs(64, 3072, 16, steps=25, dtype=si.BF16, seed=0)
-    _run_steps(w, 25)
+def test_step_config_bf16_B64_D3072_N16_1000_steps():
+    """The decode workload as stated: 1000 consecutive in-place steps on the GPU
+    (queued back to back, no synchronisation between them), then the same chain on
+    the oracle; y compared at every step, the state after every 100th step."""
+    steps, every = 1000, 100
+    print(f"[step] bf16 B64 D3072 N16, {steps} chained in-place steps", flush=True)
+    w = si.step_inputs(64, 3072, 16, steps=steps, dtype=si.BF16, seed=0)
+    tok = {k: si.to_torch(w[k], DEV) for k in ("x", "delta", "z", "Bm", "Cm")}
+    A = torch.from_numpy(w["A"]).to(DEV)
+    Dk = torch.from_numpy(w["D"]).to(DEV)
+    st = torch.from_numpy(w["state0"]).to(DEV)
+    y = torch.empty((steps, 64, 3072), dtype=torch.bfloat16, device=DEV)
+    snaps = []
+    for s in range(steps):
+        ssa.ssm_step(st, tok["x"][s], tok["delta"][s], A, tok["Bm"][s], tok["Cm"][s], D=Dk, z=tok["z"][s],
+                     y=y[s])
+        if (s + 1) % every == 0:
+            snaps.append(st.clone())
+    torch.cuda.synchronize()
+    yg = out_f64(y)
+    sg = [t.cpu().numpy().astype(np.float64) for t in snaps]
+    st_o = w["state0"].astype(np.float64)
+    Af, Df = w["A"].astype(np.float64), w["D"].astype(np.float64)
+    for s in range(steps):
+        yo, st_o = oracle.step(st_o, si.to_f64(w["x"][s]), si.to_f64(w["delta"][s]), Af, si.to_f64(w["Bm"][s]),
+                               si.to_f64(w["Cm"][s]), D=Df, z=si.to_f64(w["z"][s]))
+        compare(yg[s], yo, "bf16", what=f"step {s} y")
+        if (s + 1) % every == 0:
+            info = compare(sg[(s + 1) // every - 1], st_o, "f32", what=f"state after step {s + 1}")
+            print(f"  state after {s + 1} steps: normwise {info['normwise']:.2e}", flush=True)
 
 
 def test_step_equals_prefill_of_one_on_gpu():
