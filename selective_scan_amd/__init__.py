@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     ssm_scan_bwd_workspace_size,
     ssm_scan_fwd,
     ssm_scan_fwd_ex,
+    ssm_scan_fwd_noalloc,
     ssm_scan_workspace_size,
     ssm_ssd_fwd,
     ssm_ssd_workspace_size,

@@ -104,7 +104,7 @@ namespace {
 int scan_fwd_impl(const char* fn, int B, int L, int D, int N, int io, int disc, const float* delta_bias,
                   int delta_softplus, const void* x, const void* delta, const float* A, const void* Bm,
                   const void* Cm, const float* Dskip, const void* z, const float* h0, void* y, float* h_final,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool launch = true) {
     if (B < 1 || D < 1 || L < 0 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1 and L >= 0");
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
     if (disc != SSM_DISC_EULER && disc != SSM_DISC_ZOH)
@@ -129,6 +129,7 @@ int scan_fwd_impl(const char* fn, int B, int L, int D, int N, int io, int disc, 
     const size_t need = ssm::scan_workspace_bytes(B, L, D, N);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(SSM_ERR_WORKSPACE, fn, "workspace missing or smaller than ssm_scan_workspace_size()");
+    if (!launch) return ok();
     ssm::ScanArgs a{B, L, D, N, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, workspace,
                     delta_bias, delta_softplus, disc};
     const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -182,6 +183,40 @@ int ssm_scan_fwd_ex(int B, int L, int D, int N, ssm_dtype_t io, ssm_disc_t disc,
                     void* workspace, size_t workspace_bytes, void* stream) {
     return scan_fwd_impl("ssm_scan_fwd_ex", B, L, D, N, io, disc, delta_bias, delta_softplus, x, delta, A, Bm,
                          Cm, Dskip, z, h0, y, h_final, workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_noalloc(int B, int L, int D, int N, ssm_dtype_t io,
+                         const void* x, const void* delta, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip,
+                         const void* z, const float* h0,
+                         void* y, float* h_final, void* stream) {
+    const char* fn = "ssm_scan_fwd_noalloc";
+    // the checks of ssm_scan_fwd, then the size limit of the fixed scratch, all
+    // before any HIP call
+    const size_t need = (B >= 1 && D >= 1 && L >= 0 && ssm::scan_supported_n(N) && product_ok({B, L, D, N}))
+                            ? ssm::scan_workspace_bytes(B, L, D, N)
+                            : 0;
+    // a stand-in workspace address of exactly the needed size (never dereferenced:
+    // scan_fwd_impl only validates here)
+    void* stand_in = need > 0 ? reinterpret_cast<void*>(uintptr_t{256}) : nullptr;
+    const int st = scan_fwd_impl(fn, B, L, D, N, io, SSM_DISC_EULER, nullptr, 0, x, delta, A, Bm, Cm, Dskip, z, h0,
+                                 y, h_final, stand_in, need, nullptr, /*launch=*/false);
+    if (st != SSM_OK) return st;
+    if (need > ssm::kNoallocScratchBytes) {
+        char buf[160];
+        std::snprintf(buf, sizeof buf, "the shape needs %zu bytes of scratch; the fixed scratch holds %zu", need,
+                      ssm::kNoallocScratchBytes);
+        return fail(SSM_ERR_UNSUPPORTED, fn, buf);
+    }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    hipError_t e = hs ? hipStreamGetDevice(hs, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    void* ws = nullptr;
+    if ((e = ssm::noalloc_scratch(dev, &ws)) != hipSuccess) return hip_status(e, fn);
+    ssm::ScanArgs a{B, L, D, N, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, ws,
+                    nullptr, 0, SSM_DISC_EULER};
+    return hip_status(ssm::launch_scan_fwd(a, hs), fn);
 }
 
 // ------------------------------------------------------------------ scan backward

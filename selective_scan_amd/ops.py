@@ -42,6 +42,8 @@ def lib():
     L.ssm_scan_workspace_size.argtypes, L.ssm_scan_workspace_size.restype = [i, i, i, i], sz
     L.ssm_scan_fwd.argtypes = [i, i, i, i, i] + [vp] * 10 + [vp, sz, vp]
     L.ssm_scan_fwd.restype = i
+    L.ssm_scan_fwd_noalloc.argtypes = [i, i, i, i, i] + [vp] * 10 + [vp]
+    L.ssm_scan_fwd_noalloc.restype = i
     L.ssm_scan_fwd_ex.argtypes = [i, i, i, i, i, i, vp, i] + [vp] * 10 + [vp, sz, vp]
     L.ssm_scan_fwd_ex.restype = i
     L.ssm_step_ex.argtypes = [i, i, i, i, i, vp, i] + [fp] + [vp] * 8 + [vp]
@@ -123,6 +125,27 @@ def ssm_scan_fwd(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, y=None, h_fina
     A: [D, N], D: [D], h0: [B, D, N] fp32. Returns (y, h_final) (h_final None if not wanted)."""
     return _scan_fwd("ssm_scan_fwd", x, delta, A, Bm, Cm, D, z, h0, y, h_final, workspace, stream,
                      want_final_state, None)
+
+
+def ssm_scan_fwd_noalloc(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, y, h_final=None, stream=None):
+    """``ssm_scan_fwd`` on the library's fixed per-GPU scratch (no workspace, no
+    allocation here or in the library): the caller passes every output tensor.
+    Calls that may overlap on one GPU race on the shared scratch."""
+    Bb, L, Dd = x.shape
+    N = A.shape[1]
+    dev, io = x.device, x.dtype
+    for t, nm, shp, dt, req in ((x, "x", (Bb, L, Dd), io, True), (delta, "delta", (Bb, L, Dd), io, True),
+                                (A, "A", (Dd, N), torch.float32, True), (Bm, "Bm", (Bb, L, N), io, True),
+                                (Cm, "Cm", (Bb, L, N), io, True), (D, "D", (Dd,), torch.float32, False),
+                                (z, "z", (Bb, L, Dd), io, False), (h0, "h0", (Bb, Dd, N), torch.float32, False),
+                                (y, "y", (Bb, L, Dd), io, True),
+                                (h_final, "h_final", (Bb, Dd, N), torch.float32, False)):
+        _check(t, nm, shp, dt, dev, required=req)
+    st = lib().ssm_scan_fwd_noalloc(Bb, L, Dd, N, _io_code(x), _ptr(x), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                    _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_final), _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_scan_fwd_noalloc", st)
+    return y, h_final
 
 
 def ssm_scan_fwd_ex(x, delta, A, Bm, Cm, D=None, z=None, h0=None, *, disc="euler", delta_bias=None,

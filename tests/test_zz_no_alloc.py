@@ -1,0 +1,52 @@
+"""ssm_scan_fwd_noalloc (the scan on the library's fixed per-GPU scratch, for
+callers that cannot allocate) against ssm_scan_fwd with a caller workspace, on
+two calls in a row, the second on a smaller input: outputs equal bit for bit
+(the same kernels), and both within the parity bar of the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import selective_scan_amd as ssa
+import ssm_inputs as si
+from gpu_util import DEV, oracle_scan, out_f64, to_dev
+from parity import compare
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # the headline-sized layer first (18.6 MiB of scratch), then a smaller ragged one
+    # (1.2 MiB) with an initial state: the second call runs on what the first left
+    (1, 4096, 1536, 16, si.BF16, False),
+    (2, 1000, 200, 16, si.BF16, True),
+]
+
+
+def test_noalloc_two_calls_match_workspace_entry_and_oracle():
+    outs = []
+    for (B, L, D, N, dt, wh) in CASES:
+        print(f"[noalloc] B{B} L{L} D{D} N{N} h0={wh}", flush=True)
+        w = si.scan_inputs(B, L, D, N, dtype=dt, seed=41, with_h0=wh)
+        t = to_dev(w, ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0"))
+        y = torch.empty_like(t["x"])
+        hf = torch.empty((B, D, N), dtype=torch.float32, device=DEV)
+        ssa.ssm_scan_fwd_noalloc(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], D=t["D"], z=t["z"], h0=t["h0"],
+                                 y=y, h_final=hf)
+        outs.append((w, t, y, hf))
+    torch.cuda.synchronize()
+    for (w, t, y, hf) in outs:
+        y_ref, h_ref = ssa.ssm_scan_fwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], D=t["D"], z=t["z"],
+                                        h0=t["h0"])
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(hf, h_ref)
+        yr, hr = oracle_scan(w)
+        compare(out_f64(y), yr, "bf16", what="noalloc y")
+        compare(out_f64(hf), hr, "f32", what="noalloc h_final")
+
+
+def test_noalloc_rejects_a_shape_beyond_the_scratch():
+    x = torch.empty((1, 4096, 1536), dtype=torch.bfloat16, device=DEV)
+    A = torch.empty((1536, 64), dtype=torch.float32, device=DEV)
+    Bm = torch.empty((1, 4096, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ssa.SsmError) as e:
+        ssa.ssm_scan_fwd_noalloc(x, x, A, Bm, Bm, y=torch.empty_like(x))
+    assert e.value.status == 2
