@@ -1,18 +1,23 @@
 """Benchmark of the selective-scan hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME] [--no-cpu] [--no-other]
+    python bench.py --valu-rates | --calibrate-copy | --other NAME
 
 A step is one ssm_scan_fwd call over one batch of synthetic input already
-resident in HBM (bf16 I/O, B=1, L=4096, D=1536, N=16 by default). Inputs rotate
-over several independent batches whose total size exceeds the 256 MB
-last-level (MALL) cache, so every step streams its batch from HBM.
+resident in HBM. The default workload is the long-sequence scan (bf16 I/O,
+B=8, L=32768, D=512, N=16: 1.09 GB per call, more than four times the 256 MB
+last-level (MALL) cache, so every step streams from HBM).
 
-Prints ONE JSON line: throughput in state updates/s (B*L*D*N per step), the
-roofline of the dominant kernel (timed live with HIP events recorded around
-each kernel launch on the launch stream), and the fp64 oracle timed on the
-host cores on a bounded sample of the same workload. ``other_paths`` holds the
-same measurements for the long-sequence scan, the state-dimension sweep, the
-backward (training) scan, the SSD and the two decode steps.
+Prints ONE JSON line: throughput in state updates/s (B*L*D*N per step) over K
+back-to-back steps, the median and P95 of at least 100 individually timed calls,
+the HBM roofline of the dominant kernel and of the whole call (algorithmic bytes
+over time; every kernel timed live with HIP events the runtime stamps at the
+kernel's own start and end), the VALU issue figures from committed rocprofv3
+instruction counters, the fp64 oracle timed on the host cores on a bounded
+sample of the same workload, and the pages' own published figures as context.
+``other_paths`` holds the small fp32 case, the Mamba-130m-sized layer, the
+state-dimension sweep, the zero-order-hold variant, the backward scan, the SSD,
+the two decode steps, and the VALU issue-rate probes.
 """
 import argparse
 import ctypes
@@ -30,12 +35,39 @@ sys.path.insert(0, ROOT)
 # MI355X published peaks and unit counts
 HBM_PEAK_GBS = 8000.0
 CUS, LANES, CLOCK_GHZ = 256, 64, 2.4
-LANE_SLOTS_PER_S = CUS * LANES * CLOCK_GHZ * 1e9      # one fp32 VALU op per lane per clock
+# fp32 vector peak 157.3 TFLOP/s = 256 CU x 128 FMA lanes per clock x 2 flops x 2.4 GHz: a
+# wave64 v_fma_f32 (non-packed) issues in two cycles per SIMD, as the VALU-rate probe
+# confirms. One lane-slot = one fp32 FMA-class op of one lane.
+FMA_LANES_PER_CU_CLK = 128
+LANE_SLOTS_PER_S = CUS * FMA_LANES_PER_CU_CLK * CLOCK_GHZ * 1e9   # 78.6e12
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
-# per state update the minimal instruction mix: v_mul (Delta*A), v_exp_f32 (half
-# rate: 2 lane-slots), v_mul (u*B), v_fma (state), v_fma (C.h) -> 6 lane-slots
-SLOTS_PER_UPDATE = 6.0
+# Non-transcendental VALU ops per state update that one pass of the recurrence needs:
+# v_mul (Delta*A), v_mul (u*B), v_fma (state), v_fma (C.h); plus one v_exp_f32, priced at the
+# transcendental issue cost the VALU-rate probes measure (about 3.8 slots on the MI355X).
+FMA_OPS_PER_UPDATE = 4.0
+DEFAULT_TRANS_COST = 3.8
+DEFAULT_WORKLOAD = "scan_bf16_B8_L32768_D512_N16"
+LATENCY_CALLS = 100
+
+# The pages' own figures (other hardware, other implementations): context, never the target.
+PAGE_CONTEXT = {
+    "note": "published by the pages for naive per-timestep implementations on NVIDIA parts; "
+            "context only, not comparable kernels and not the target",
+    "ssm_bench_bandwidth_utilisation": {
+        "value": "0.01-0.08 % of peak (A100-SXM4-40GB), 0.02-0.15 % of peak (Tesla T4)",
+        "what": "Python-loop selective-scan SSM, one kernel launch per time step, bf16, batch 1, "
+                "L 512-4096, state dims 64/128/256",
+        "source": "ssm-bench README, status table"},
+    "s4d_train_step_32k": {
+        "value": "13.5 s per training step at 32K tokens", "hardware": "RTX 4050 Laptop (6 GB)",
+        "what": "S4D (FFT convolution; not the selective scan), batch 8, d_model 256, 2 layers",
+        "source": "Efficient Sequence Modeling: From S4 to Mamba-3, section 06 Results"},
+    "mamba1_python_loop_train_step": {
+        "value": "2632 ms per training step at 1K tokens; 248 s at 4K", "hardware": "RTX 4050 Laptop (6 GB)",
+        "what": "Python-loop Mamba-1 selective scan, batch 8, d_model 256, 2 layers",
+        "source": "Efficient Sequence Modeling: From S4 to Mamba-3, section 06 Results"},
+}
 
 
 def hip():
@@ -165,6 +197,22 @@ def time_calls(call, sets, steps, warmup, n_kernels):
     return total_ms, ker
 
 
+def latency(call, sets, n=LATENCY_CALLS):
+    """`n` calls, each between its own pair of events on the launch stream (rotating
+    over `sets`): median and P95 of the per-call time, in ms."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    sync()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        call(sets[i % len(sets)])
+        b.record()
+    sync()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return dict(median_ms=float(np.median(t)), p95_ms=float(np.percentile(t, 95)), min_ms=float(t.min()),
+                calls=n)
+
+
 # Sources each kernel is compiled from, in the order their bytes are hashed.
 KERNEL_SOURCES = {
     "scan": ("scan_core.h", "scan_fwd.hip", "common.h", "launch.h"),
@@ -210,30 +258,94 @@ def committed_traffic(kind, summary):
     return int(m_b.group(1)) if sources_sha256(kind) == m_h.group(1) else None
 
 
-def scan_bench(name, wl, steps, warmup, dev):
+def committed_valu(kind, summary):
+    """Per-kernel VALU and transcendental instruction counts per launch (wave
+    instructions, from rocprofv3 SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32) from a
+    committed summary under profiles/, only while the kernel's sources are unchanged.
+    Returns {kernel: (valu, trans)} or None."""
+    import re
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
+    if not m_h or sources_sha256(kind) != m_h.group(1):
+        return None
+    out = {}
+    for m in re.finditer(r"valu_insts_per_launch\s+(\S+):\s*(\d+)\s+trans_insts_per_launch:\s*(\d+)", text):
+        out[m.group(1)] = (int(m.group(2)), int(m.group(3)))
+    return out or None
+
+
+def one_pass_slots(trans_cost):
+    return FMA_OPS_PER_UPDATE + trans_cost
+
+
+def alu_figures(counts, names, kmean_ms, t_call_ms, updates, trans_cost):
+    """VALU issue per kernel and for the call from committed instruction counts: a
+    wave instruction is 64 lane-slots, a transcendental one `trans_cost` times that
+    (its issue rate relative to an FMA, measured by the VALU-rate probes)."""
+    if counts is None:
+        return None
+    per, tot = {}, 0.0
+    for nm, t in zip(names, kmean_ms):
+        if nm not in counts:
+            continue
+        valu, trans = counts[nm]
+        slots = LANES * (valu + (trans_cost - 1.0) * trans)
+        tot += slots
+        per[nm] = dict(valu_insts=valu, trans_insts=trans, slots_per_update=slots / updates,
+                       issue_tslot_s=slots / (t * 1e-3) / 1e12,
+                       issue_frac=slots / (t * 1e-3) / LANE_SLOTS_PER_S)
+    return dict(peak_tslot_s=LANE_SLOTS_PER_S / 1e12, trans_cost_slots=trans_cost, kernels=per,
+                call_slots_per_update=tot / updates,
+                call_issue_frac=tot / (t_call_ms * 1e-3) / LANE_SLOTS_PER_S,
+                model_slots_per_update_one_pass=one_pass_slots(trans_cost),
+                call_frac_of_one_pass_ceiling=one_pass_slots(trans_cost) * updates / (t_call_ms * 1e-3)
+                / LANE_SLOTS_PER_S,
+                note="lane-slots = 64 x (VALU instructions + (trans_cost - 1) x transcendental ones), from "
+                     "rocprofv3 SQ_INSTS_VALU / SQ_INSTS_VALU_TRANS_F32 per launch; issue_frac = slots over "
+                     "kernel time x 256 CU x 128 FMA lanes x 2.4 GHz; call_frac_of_one_pass_ceiling = the "
+                     "minimal single-pass mix (4 FMA-class ops + one exp per update) over the call's time")
+
+
+def scan_kernel_names(nk, wl):
+    if nk == 3:
+        return ["segment_aggregate", "group_carry", "segment_final"]
+    if nk == 2:
+        return ["segment_aggregate", "segment_final"]
+    if nk == 4:  # N >= 64: the final pass sums C . h in LDS, then a combine pass
+        return ["segment_aggregate", "group_carry", "segment_final_sink", "combine_partials"]
+    return ["segment_final"] if nk == 1 else [f"kernel{i}" for i in range(nk)]
+
+
+def scan_bench(name, wl, steps, warmup, dev, trans_cost=DEFAULT_TRANS_COST, lat_calls=LATENCY_CALLS):
     sets, ws, w0, set_bytes = scan_setup(wl, dev)
     nk = count_kernels(lambda: scan_call(sets[0], ws))
     total_ms, ker = time_calls(lambda t: scan_call(t, ws), sets, steps, warmup, nk)
+    lat = latency(lambda t: scan_call(t, ws), sets, max(lat_calls, steps))
     upd = wl["B"] * wl["L"] * wl["D"] * wl["N"]
     ms = total_ms / steps
     kmean = ker.mean(axis=0)
+    names = scan_kernel_names(nk, wl)
     dom = int(np.argmax(kmean))
     alg = scan_alg_bytes(wl)
     res = dict(
         workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3),
         tokens_per_s=wl["B"] * wl["L"] / (ms * 1e-3),
         hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        kernel_ms=[float(v) for v in kmean], dominant_kernel=dom, sets=len(sets),
-        set_mb=set_bytes / 1e6,
+        call_latency=lat, kernel_ms=dict(zip(names, (float(v) for v in kmean))), dominant_kernel=names[dom],
+        sets=len(sets), set_mb=set_bytes / 1e6, alg_bytes=alg,
     )
     tdom = kmean[dom] * 1e-3
-    achieved = SLOTS_PER_UPDATE * upd / tdom / 1e12
-    peak = LANE_SLOTS_PER_S / 1e12
-    res["roofline"] = dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s",
-                           frac=achieved / peak, traffic=committed_traffic("scan", f"traffic_{name}.md"),
-                           kernel="segment_final" if nk > 1 else "segment")
-    res["hbm_roofline_dominant"] = dict(achieved=alg / tdom / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
-                                        frac=alg / tdom / 1e9 / HBM_PEAK_GBS)
+    traffic = committed_traffic("scan", f"traffic_{name}.md")
+    res["roofline"] = dict(bound="hbm", achieved=alg / tdom / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                           frac=alg / tdom / 1e9 / HBM_PEAK_GBS, traffic=traffic, kernel=names[dom],
+                           call=dict(achieved=alg / (ms * 1e-3) / 1e9, frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS),
+                           note="achieved = the call's algorithmic bytes (x, Delta, z, B, C, A, D read; y, "
+                                "h_final written) over the dominant kernel's mean time; 'call' over the whole "
+                                "call. The scan at N = 16 is bound by VALU issue, not HBM: see 'alu'")
+    res["alu"] = alu_figures(committed_valu("scan", f"valu_{name}.md"), names, kmean, ms, upd, trans_cost)
     return res, w0
 
 
@@ -272,13 +384,13 @@ def scan_cpu_baseline(wl, w0, budget_s=15.0, total_s=10.0):
 
 # ------------------------------------------------------------------ scan variants
 # Exact zero-order hold per state update (steps whose |z| are all >= 1/32): v_mul
-# (Delta*A), v_exp_f32 (2), v_mul (x/A), v_mul (*B), v_add (h + w), v_fma (state),
-# v_fma (C.h) -> 8 lane-slots; softplus(delta + bias) is per (step, channel), not
+# (Delta*A), v_mul (x/A), v_mul (*B), v_add (h + w), v_fma (state), v_fma (C.h) -> 6
+# FMA-class ops and one v_exp_f32; softplus(delta + bias) is per (step, channel), not
 # per update.
-ZOH_SLOTS_PER_UPDATE = 8.0
+ZOH_FMA_OPS_PER_UPDATE = 6.0
 
 
-def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16):
+def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16, trans_cost=DEFAULT_TRANS_COST):
     import torch
     import ssm_inputs as si
     import selective_scan_amd as ssa
@@ -304,15 +416,16 @@ def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16):
 
     nk = count_kernels(lambda: call(sets[0]))
     total_ms, ker = time_calls(call, sets, steps, warmup, nk)
+    lat = latency(call, sets)
     ms = total_ms / steps
     kmean = ker.mean(axis=0)
     dom = int(np.argmax(kmean))
     upd = B * L * D * N
     alg = scan_alg_bytes(wl) + D * 4
-    achieved = ZOH_SLOTS_PER_UPDATE * upd / (kmean[dom] * 1e-3) / 1e12
+    achieved = (ZOH_FMA_OPS_PER_UPDATE + trans_cost) * upd / (kmean[dom] * 1e-3) / 1e12
     peak = LANE_SLOTS_PER_S / 1e12
     return dict(workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3), tokens_per_s=B * L / (ms * 1e-3),
-                kernel_ms=[float(v) for v in kmean], hbm_gbs=alg / (ms * 1e-3) / 1e9,
+                call_latency=lat, kernel_ms=[float(v) for v in kmean], hbm_gbs=alg / (ms * 1e-3) / 1e9,
                 hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, sets=len(sets),
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
                               traffic=committed_traffic("scan_var", f"traffic_{name}.md"),
@@ -320,16 +433,17 @@ def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16):
 
 
 # ------------------------------------------------------------------ scan backward
-# Per state update, the final backward pass must issue (non-packed VALU lane-slots):
-# forward recompute v_mul (Delta*A), v_exp_f32 (2), v_mul (u*B), v_fma (state),
-# v_fma (C.h), v_mul (dv*h for dC); backward v_fma (adjoint), v_mul + v_exp_f32 (2)
-# (decay again), v_fma (a_t h_{t-1}), v_mul (q), v_fma x 3 (ddelta, dA, dx sums),
-# v_mul (g*u for dB), v_mul (carry) -> 18; plus the sums over the 64 channels of a
-# wave for dB and dC, at least 2 x 63/64 adds -> 20 lane-slots per update.
-BWD_SLOTS_PER_UPDATE = 20.0
+# Per state update, the final backward pass must issue: forward recompute v_mul
+# (Delta*A), v_exp_f32, v_mul (u*B), v_fma (state), v_fma (C.h), v_mul (dv*h for dC);
+# backward v_fma (adjoint), v_mul + v_exp_f32 (decay again), v_fma (a_t h_{t-1}), v_mul
+# (q), v_fma x 3 (ddelta, dA, dx sums), v_mul (g*u for dB), v_mul (carry) -> 14 FMA-class
+# ops and two v_exp_f32; plus the sums over the 64 channels of a wave for dB and dC, at
+# least 2 x 63/64 adds -> 16 FMA-class ops and two exps per update.
+BWD_FMA_OPS_PER_UPDATE = 16.0
+BWD_EXPS_PER_UPDATE = 2.0
 
 
-def scan_bwd_bench(name, wl, steps, warmup, dev, max_sets=8):
+def scan_bwd_bench(name, wl, steps, warmup, dev, max_sets=8, trans_cost=DEFAULT_TRANS_COST):
     import torch
     import ssm_inputs as si
     import selective_scan_amd as ssa
@@ -356,6 +470,7 @@ def scan_bwd_bench(name, wl, steps, warmup, dev, max_sets=8):
 
     nk = count_kernels(lambda: call(sets[0]))
     total_ms, ker = time_calls(call, sets, steps, warmup, nk)
+    lat = latency(call, sets)
     ms = total_ms / steps
     kmean = ker.mean(axis=0)
     dom = int(np.argmax(kmean))
@@ -364,10 +479,10 @@ def scan_bwd_bench(name, wl, steps, warmup, dev, max_sets=8):
     # dB, dC, dA, dD, dh0
     alg = 7 * B * L * D * es + 4 * B * L * N * es + 2 * (D * N + D) * 4 + 2 * B * D * N * 4
     tdom = kmean[dom] * 1e-3
-    achieved = BWD_SLOTS_PER_UPDATE * upd / tdom / 1e12
+    achieved = (BWD_FMA_OPS_PER_UPDATE + BWD_EXPS_PER_UPDATE * trans_cost) * upd / tdom / 1e12
     peak = LANE_SLOTS_PER_S / 1e12
     return dict(workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3),
-                tokens_per_s=B * L / (ms * 1e-3), kernel_ms=[float(v) for v in kmean],
+                tokens_per_s=B * L / (ms * 1e-3), call_latency=lat, kernel_ms=[float(v) for v in kmean],
                 hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 sets=len(sets), alg_bytes=alg,
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
@@ -411,13 +526,14 @@ def ssd_bench(name, wl, steps, warmup, dev, max_sets=3):
 
     nk = count_kernels(lambda: call(sets[0]))
     total_ms, ker = time_calls(call, sets, steps, warmup, nk)
+    lat = latency(call, sets)
     ms = total_ms / steps
     kmean = ker.mean(axis=0)
     byt, fl = ssd_alg(wl)
     upd = B * L * H * P * N
     tdom = kmean[int(np.argmax(kmean))] * 1e-3
     return dict(workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3),
-                tokens_per_s=B * L / (ms * 1e-3), kernel_ms=[float(v) for v in kmean],
+                tokens_per_s=B * L / (ms * 1e-3), call_latency=lat, kernel_ms=[float(v) for v in kmean],
                 hbm_gbs=byt / (ms * 1e-3) / 1e9, hbm_frac=byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 mfma_tflops=fl / (ms * 1e-3) / 1e12,
                 mfma_frac=fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
@@ -429,7 +545,11 @@ def ssd_bench(name, wl, steps, warmup, dev, max_sets=3):
 
 
 # ------------------------------------------------------------------ decode
-def step_bench(wl, dev, reps=3):
+def step_bench(wl, dev, reps=3, only=None):
+    """The decode workload: `steps` in-place steps, stream-launched and HIP-graph
+    replayed (state MALL-resident), then the cold multi-layer variant and the
+    streaming floor. only="hot" / "cold": just that graph-replayed variant (for
+    counter runs that must not mix the two)."""
     import torch
     import selective_scan_amd as ssa
     import ssm_inputs as si
@@ -447,19 +567,26 @@ def step_bench(wl, dev, reps=3):
             ssa.ssm_step(st, tok["x"][s], tok["delta"][s], A, tok["Bm"][s], tok["Cm"][s], D=Dk,
                          z=tok["z"][s], y=y[s])
 
-    run()
-    sync()
+    step1 = (lambda stv, s_: ssa.ssm_step(stv, tok["x"][s_], tok["delta"][s_], A, tok["Bm"][s_], tok["Cm"][s_],
+                                          D=Dk, z=tok["z"][s_], y=y[s_]))
+    if only == "cold":
+        cold = cold_decode(step1, st0, steps)
+        return dict(workload="step_bf16_B64_D3072_N16_x1000", only="cold", cold_ms_per_step=cold["ms"],
+                    layers=cold["layers"])
     times = []
-    for _ in range(reps):
-        st.copy_(st0)
-        sync()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+    if only is None:
         run()
-        e1.record()
         sync()
-        times.append(e0.elapsed_time(e1))
-    # HIP-graph replay of the same 1000 launches
+        for _ in range(reps):
+            st.copy_(st0)
+            sync()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            sync()
+            times.append(e0.elapsed_time(e1))
+    # HIP-graph replay of the same launches
     g = torch.cuda.CUDAGraph()
     st.copy_(st0)
     sync()
@@ -478,13 +605,14 @@ def step_bench(wl, dev, reps=3):
         e1.record()
         sync()
         gtimes.append(e0.elapsed_time(e1))
+    if only == "hot":
+        return dict(workload="step_bf16_B64_D3072_N16_x1000", only="hot",
+                    hot_ms_per_step=float(np.median(gtimes)) / steps)
     es = 2 if wl["dtype"] == "bf16" else 4
     alg = 2 * B * D * N * 4 + 4 * B * D * es + 2 * B * N * es + (D * N + D) * 4
     med = float(np.median(times)) / steps
     gmed = float(np.median(gtimes)) / steps
-    cold = cold_decode(lambda stv, s_: ssa.ssm_step(stv, tok["x"][s_], tok["delta"][s_], A, tok["Bm"][s_],
-                                                    tok["Cm"][s_], D=Dk, z=tok["z"][s_], y=y[s_]),
-                       st0, steps)
+    cold = cold_decode(step1, st0, steps)
     return dict(workload="step_bf16_B64_D3072_N16_x1000", ms_per_step_stream=med,
                 ms_per_step_graph=gmed, updates_per_s_graph=B * D * N / (gmed * 1e-3),
                 tokens_per_s_graph=B / (gmed * 1e-3),
@@ -500,11 +628,13 @@ def step_bench(wl, dev, reps=3):
 
 
 def streaming_floor(st0, steps, reps=3):
-    """Context for a decode step: a plain in-place scale of a tensor of the state's
-    size (torch's mul_, one launch per step), graph-replayed `steps` times on one
-    tensor (MALL-resident) and rotating over tensors adding up to more than the MALL.
-    What one launch per step reaches by pure streaming at this size."""
+    """Context for a decode step: this library's in-place streaming kernel
+    (ssm_diag_stream_scale: every 16-byte load of a lane issued before its first
+    store, one launch per step) on a tensor of the state's size, graph-replayed
+    `steps` times on one tensor (MALL-resident) and rotating over tensors adding up
+    to more than the MALL. What one launch per step reaches by pure streaming."""
     import torch
+    import selective_scan_amd as ssa
     st = st0.clone()
     g = torch.cuda.CUDAGraph()
     sync()
@@ -512,7 +642,7 @@ def streaming_floor(st0, steps, reps=3):
     with torch.cuda.stream(s_):
         with torch.cuda.graph(g, stream=s_):
             for _ in range(steps):
-                st.mul_(0.999)
+                ssa.ssm_diag_stream_scale(st, 0.999)
     sync()
     hot = []
     for _ in range(reps):
@@ -522,11 +652,41 @@ def streaming_floor(st0, steps, reps=3):
         e1.record()
         sync()
         hot.append(e0.elapsed_time(e1) / steps)
-    cold = cold_decode(lambda stv, s_: stv.mul_(0.999), st0, steps, reps=reps)
-    return dict(ms_per_step_hot=float(np.median(hot)), ms_per_step_cold=cold["ms"],
-                bytes_per_step=2 * st0.numel() * 4,
-                note="plain in-place scale of a tensor of the state's size (torch mul_), graph-replayed "
-                     "like the steps: reads and writes the state only")
+    cold = cold_decode(lambda stv, s_: ssa.ssm_diag_stream_scale(stv, 0.999), st0, steps, reps=reps)
+    nb = 2 * st0.numel() * 4
+    return dict(ms_per_step_hot=float(np.median(hot)), ms_per_step_cold=cold["ms"], bytes_per_step=nb,
+                hbm_frac_cold=nb / (cold["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                note="ssm_diag_stream_scale (this library's in-place streaming kernel) on a tensor of the "
+                     "state's size, graph-replayed like the steps: reads and writes the state only")
+
+
+def valu_rates(dev, blocks=8192, iters=2048):
+    """The VALU issue-rate probes: exp-only, fma-only and 1:3 chains, full occupancy."""
+    import torch
+    import selective_scan_amd as ssa
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    res = {}
+    for mode, nm in ((0, "exp"), (1, "fma"), (2, "exp1_fma3")):
+        ssa.ssm_diag_valu_rate(mode, out, 16)
+        sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops = ssa.ssm_diag_valu_rate(mode, out, iters)
+        e1.record()
+        sync()
+        ms = e0.elapsed_time(e1)
+        res[nm] = dict(ops_per_s=ops / (ms * 1e-3), ms=ms, ops=ops)
+    fma, ex = res["fma"]["ops_per_s"], res["exp"]["ops_per_s"]
+    mix = res["exp1_fma3"]["ops_per_s"]
+    res["exp_cost_in_fma_slots"] = fma / ex
+    # if exp and fma shared one issue port with costs c_e and 1, a 1:3 mix would run at
+    # 4 / (c_e + 3) of the fma rate; co-issue would show as a faster mix
+    res["mix_predicted_no_coissue_ops_per_s"] = 4.0 * fma / (fma / ex + 3.0)
+    res["mix_measured_over_predicted"] = mix / res["mix_predicted_no_coissue_ops_per_s"]
+    res["fma_frac_of_lane_peak"] = fma / LANE_SLOTS_PER_S
+    res["note"] = ("lane ops/s of ssm_diag_valu_rate: 8 independent chains per lane, %d lanes; the lane-slot "
+                   "peak is 256 CU x 64 lanes x 2.4 GHz = %.1f T/s" % (blocks * 256, LANE_SLOTS_PER_S / 1e12))
+    return res
 
 
 def cold_decode(step, st0, steps, reps=3, min_bytes=2 * MALL_BYTES):
@@ -558,9 +718,10 @@ def cold_decode(step, st0, steps, reps=3, min_bytes=2 * MALL_BYTES):
     return dict(layers=R, ms=float(np.median(out)))
 
 
-def ssd_step_bench(wl, dev, reps=3):
+def ssd_step_bench(wl, dev, reps=3, only=None):
     """Mamba-2 decode: `steps` in-place steps launched on a stream, then the same
-    steps replayed from a HIP graph; per-step time and algorithmic bytes/s."""
+    steps replayed from a HIP graph; per-step time and algorithmic bytes/s.
+    only="hot" / "cold": just that graph-replayed variant (for counter runs)."""
     import torch
     import selective_scan_amd as ssa
     import ssm_inputs as si
@@ -591,9 +752,17 @@ def ssd_step_bench(wl, dev, reps=3):
             out.append(e0.elapsed_time(e1) / steps)
         return float(np.median(out))
 
-    run()
-    sync()
-    ms_stream = timed(run)
+    step1 = (lambda stv, s_: ssa.ssm_ssd_step(stv, tok["x"][s_], tok["delta"][s_], A, tok["Bm"][s_],
+                                              tok["Cm"][s_], D=Dk, z=tok["z"][s_], y=y[s_]))
+    if only == "cold":
+        cold = cold_decode(step1, st0, steps)
+        return dict(workload="ssd_step_bf16_B64_H24_P64_N128_x200", only="cold", cold_ms_per_step=cold["ms"],
+                    layers=cold["layers"])
+    ms_stream = None
+    if only is None:
+        run()
+        sync()
+        ms_stream = timed(run)
     g = torch.cuda.CUDAGraph()
     st.copy_(st0)
     sync()
@@ -603,11 +772,11 @@ def ssd_step_bench(wl, dev, reps=3):
             run()
     sync()
     ms_graph = timed(g.replay)
+    if only == "hot":
+        return dict(workload="ssd_step_bf16_B64_H24_P64_N128_x200", only="hot", hot_ms_per_step=ms_graph)
     es = 2 if wl["dtype"] == "bf16" else 4
     alg = 2 * B * H * N * P * 4 + 3 * B * H * P * es + B * H * es + 2 * B * N * es + 2 * H * 4
-    cold = cold_decode(lambda stv, s_: ssa.ssm_ssd_step(stv, tok["x"][s_], tok["delta"][s_], A, tok["Bm"][s_],
-                                                        tok["Cm"][s_], D=Dk, z=tok["z"][s_], y=y[s_]),
-                       st0, steps)
+    cold = cold_decode(step1, st0, steps)
     return dict(workload="ssd_step_bf16_B64_H24_P64_N128_x200", ms_per_step_stream=ms_stream,
                 ms_per_step_graph=ms_graph, updates_per_s_graph=B * H * P * N / (ms_graph * 1e-3),
                 tokens_per_s_graph=B / (ms_graph * 1e-3), alg_bytes_per_step=alg,
@@ -622,18 +791,29 @@ def ssd_step_bench(wl, dev, reps=3):
                 streaming_floor=streaming_floor(st0, steps))
 
 
+def scan_summary(r):
+    keys = ("workload", "ms_per_step", "updates_per_s", "tokens_per_s", "call_latency", "hbm_gbs", "hbm_frac",
+            "kernel_ms", "roofline", "alu")
+    return {k: r[k] for k in keys if k in r}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="scan_bf16_B1_L4096_D1536_N16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-other", action="store_true")
     ap.add_argument("--other", default=None,
-                    help="only run this one other-paths workload (a scan_bwd_*, scan_zoh_* or ssd_* name) and print it")
+                    help="only run this one workload of the other paths (a scan_*, scan_bwd_*, scan_zoh_*, ssd_*, "
+                         "step_* or ssd_step_* name) and print it")
+    ap.add_argument("--decode-pass", choices=("hot", "cold"), default=None,
+                    help="with --other step_*/ssd_step_*: run only the graph-replayed hot or cold variant")
+    ap.add_argument("--valu-rates", action="store_true",
+                    help="only run the VALU issue-rate probes (exp, fma, 1:3 mix) and print them")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
+                    help="only run a plain 1 GiB device copy (ssm_diag_copy) 5 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the selective scan here has no multi-GPU path "
@@ -641,15 +821,19 @@ def main():
         sys.exit(2)
     import torch
     import ssm_inputs as si
+    import selective_scan_amd as ssa
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            ssa.ssm_diag_copy(src, dst)
         sync()
         print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "calibrate_copy_bytes_written": dst.numel() * 4,
-                          "launches": 5}))
+                          "launches": 5, "kernel": "copy16 (ssm_diag_copy)"}))
+        return
+    if args.valu_rates:
+        print(json.dumps(valu_rates(dev)))
         return
     if args.other:
         wl = si.WORKLOADS[args.other]
@@ -659,13 +843,21 @@ def main():
             r = scan_var_bench(args.other, wl, args.steps, args.warmup, dev)
         elif wl["kind"] == "ssd":
             r = ssd_bench(args.other, wl, args.steps, args.warmup, dev)
+        elif wl["kind"] == "scan":
+            r = scan_summary(scan_bench(args.other, wl, args.steps, args.warmup, dev)[0])
+        elif wl["kind"] == "step":
+            r = step_bench(wl, dev, only=args.decode_pass)
+        elif wl["kind"] == "ssd_step":
+            r = ssd_step_bench(wl, dev, only=args.decode_pass)
         else:
-            raise SystemExit(f"--other takes a scan_bwd_* or ssd_* workload, not {args.other}")
+            raise SystemExit(f"--other takes a scan_*, scan_bwd_*, scan_zoh_* or ssd_* workload, not {args.other}")
         print(json.dumps(r))
         return
     wl = si.WORKLOADS[args.workload]
     assert wl["kind"] == "scan", "the headline bench line is a scan workload"
-    res, w0 = scan_bench(args.workload, wl, args.steps, args.warmup, dev)
+    rates = valu_rates(dev)
+    trans_cost = rates["exp_cost_in_fma_slots"]
+    res, w0 = scan_bench(args.workload, wl, args.steps, args.warmup, dev, trans_cost=trans_cost)
     out = {
         "metric": "selective-scan state updates/s (B*L*D*N) + % of MI355X HBM roofline",
         "value": res["updates_per_s"],
@@ -684,29 +876,33 @@ def main():
         "tokens_per_s": res["tokens_per_s"],
         "hbm_gbs": res["hbm_gbs"],
         "hbm_frac": res["hbm_frac"],
+        "call_latency": res["call_latency"],
         "kernel_ms": res["kernel_ms"],
         "roofline": res["roofline"],
-        "hbm_roofline_dominant": res["hbm_roofline_dominant"],
+        "alu": res["alu"],
+        "context": dict(PAGE_CONTEXT, this_run=dict(
+            hbm_frac_call=res["hbm_frac"], updates_per_s=res["updates_per_s"],
+            note="this line's own HBM fraction, beside the pages' 0.01-0.15 % for per-timestep Python loops")),
     }
     if not args.no_cpu:
         out["cpu_baseline"] = scan_cpu_baseline(wl, w0)
+    del w0
     if not args.no_other:
-        other = {}
-        r2, _ = scan_bench("scan_bf16_B8_L32768_D512_N16", si.WORKLOADS["scan_bf16_B8_L32768_D512_N16"],
-                           steps=5, warmup=2, dev=dev)
-        other["scan_long"] = {k: r2[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
-                                                   "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
-        for nm in ("scan_bf16_B1_L4096_D1536_N64", "scan_bf16_B1_L4096_D1536_N128",
-                   "scan_bf16_B1_L4096_D1536_N256"):
-            r3, _ = scan_bench(nm, si.WORKLOADS[nm], steps=10, warmup=2, dev=dev)
-            other[nm] = {k: r3[k] for k in ("workload", "ms_per_step", "updates_per_s", "tokens_per_s",
-                                            "hbm_gbs", "hbm_frac", "kernel_ms", "roofline")}
+        other = {"valu_rates": rates}
+        for nm in ("scan_f32_B1_L256_D64_N16", "scan_bf16_B1_L4096_D1536_N16", "scan_bf16_B1_L4096_D1536_N64",
+                   "scan_bf16_B1_L4096_D1536_N128", "scan_bf16_B1_L4096_D1536_N256"):
+            if nm == args.workload:
+                continue
+            r3, _ = scan_bench(nm, si.WORKLOADS[nm], steps=20, warmup=3, dev=dev, trans_cost=trans_cost)
+            other[nm] = scan_summary(r3)
+        other["scan_f32_B1_L256_D64_N16"]["latency_us"] = {
+            k: v * 1e3 for k, v in other["scan_f32_B1_L256_D64_N16"]["call_latency"].items() if k.endswith("_ms")}
         other["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"] = scan_var_bench(
             "scan_zoh_softplus_bf16_B1_L4096_D1536_N16", si.WORKLOADS["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"],
-            steps=20, warmup=3, dev=dev)
+            steps=20, warmup=3, dev=dev, trans_cost=trans_cost)
         for nm in ("scan_bwd_bf16_B1_L4096_D1536_N16", "scan_bwd_bf16_B8_L32768_D512_N16"):
             other[nm] = scan_bwd_bench(nm, si.WORKLOADS[nm], steps=10 if si.WORKLOADS[nm]["L"] <= 4096 else 3,
-                                       warmup=2, dev=dev)
+                                       warmup=2, dev=dev, trans_cost=trans_cost)
         for nm in ("ssd_bf16_B4_L8192_H24_P64_N128_Q256", "ssd_bf16_B4_L8192_H24_P64_N128_Q64",
                    "ssd_bf16_B4_L8000_H24_P64_N128_Q256"):
             other[nm] = ssd_bench(nm, si.WORKLOADS[nm], steps=10, warmup=3, dev=dev)

@@ -11,6 +11,9 @@ module raises.
 from .ops import (  # noqa: F401
     SsmError,
     lib,
+    ssm_diag_copy,
+    ssm_diag_stream_scale,
+    ssm_diag_valu_rate,
     ssm_scan_bwd,
     ssm_scan_bwd_workspace_size,
     ssm_scan_fwd,

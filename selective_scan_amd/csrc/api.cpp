@@ -9,6 +9,7 @@
 #include <limits>
 #include <string>
 
+#include "extras.h"
 #include "launch.h"
 
 namespace {
@@ -339,6 +340,29 @@ int ssm_ssd_step(int B, int H, int P, int N, ssm_dtype_t io,
         if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
     ssm::SsdStepArgs a{B, H, P, N, io == SSM_BF16, state, x, delta, A, Bm, Cm, Dskip, z, y};
     return hip_status(ssm::launch_ssd_step(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ------------------------------------------------------------------ diagnostics
+int ssm_diag_valu_rate(int mode, int blocks, int iters, float* out, void* stream) {
+    const char* fn = "ssm_diag_valu_rate";
+    if (mode < 0 || mode > 2) return fail(SSM_ERR_INVALID_ARG, fn, "mode must be 0, 1 or 2");
+    if (blocks < 1 || blocks > (1 << 20) || iters < 0) return fail(SSM_ERR_INVALID_ARG, fn, "bad blocks or iters");
+    if (!out || !aligned16(out)) return fail(SSM_ERR_INVALID_ARG, fn, "out is NULL or not 16-byte aligned");
+    return hip_status(ssm::launch_valu_rate(mode, blocks, iters, out, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ssm_diag_stream_scale(float* p, size_t n, float s, void* stream) {
+    const char* fn = "ssm_diag_stream_scale";
+    if (!p || !aligned16(p) || n % 4 != 0 || n == 0)
+        return fail(SSM_ERR_INVALID_ARG, fn, "p must be 16-byte aligned and n a positive multiple of 4");
+    return hip_status(ssm::launch_stream_scale(p, n, s, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ssm_diag_copy(const float* src, float* dst, size_t n, void* stream) {
+    const char* fn = "ssm_diag_copy";
+    if (!src || !dst || !aligned16(src) || !aligned16(dst) || n % 4 != 0 || n == 0)
+        return fail(SSM_ERR_INVALID_ARG, fn, "pointers must be 16-byte aligned and n a positive multiple of 4");
+    return hip_status(ssm::launch_copy(src, dst, n, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

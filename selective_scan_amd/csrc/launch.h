@@ -7,8 +7,6 @@
 #include <stdint.h>
 #include <stddef.h>
 
-#include "ssm_scan.h"
-
 namespace ssm {
 
 // The next two caller-provided timing events if the calling thread enabled
@@ -57,11 +55,6 @@ struct ScanPlan {
 
 bool scan_supported_n(int N);
 ScanPlan scan_plan(int B, int L, int D, int N);
-
-// ssm_scan_fwd_noalloc: the workspace lives in a fixed device array of this many
-// bytes per GPU (scan_noalloc.hip); *out = its device address on `device`.
-constexpr size_t kNoallocScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
-hipError_t noalloc_scratch(int device, void** out);
 size_t scan_workspace_bytes(int B, int L, int D, int N);
 hipError_t launch_scan_fwd(const ScanArgs& a, hipStream_t stream);
 // zero-order hold and/or Delta preprocessing; N in {4, 8, 16, 32}

@@ -10,7 +10,7 @@
 
 #include <mutex>
 
-#include "launch.h"
+#include "extras.h"
 
 namespace ssm {
 

@@ -58,6 +58,9 @@ def lib():
     L.ssm_step.restype = i
     L.ssm_ssd_step.argtypes = [i, i, i, i, i] + [fp] + [vp] * 8 + [vp]
     L.ssm_ssd_step.restype = i
+    L.ssm_diag_valu_rate.argtypes, L.ssm_diag_valu_rate.restype = [i, i, i, vp, vp], i
+    L.ssm_diag_stream_scale.argtypes, L.ssm_diag_stream_scale.restype = [vp, sz, ctypes.c_float, vp], i
+    L.ssm_diag_copy.argtypes, L.ssm_diag_copy.restype = [vp, vp, sz, vp], i
     _lib = L
     return _lib
 
@@ -347,3 +350,27 @@ def ssm_ssd_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=N
     if st != SSM_OK:
         _raise("ssm_ssd_step", st)
     return y
+
+
+# ------------------------------------------------------------------ diagnostics
+def ssm_diag_valu_rate(mode, out, iters, stream=None):
+    """VALU issue-rate probe (mode 0 exp, 1 fma, 2 exp:fma 1:3); ``out`` is an fp32
+    tensor of blocks * 256 elements. Returns the number of ops it issues."""
+    blocks = out.numel() // 256
+    st = lib().ssm_diag_valu_rate(int(mode), blocks, int(iters), _ptr(out), _stream(out.device, stream))
+    if st != SSM_OK:
+        _raise("ssm_diag_valu_rate", st)
+    return blocks * 256 * 32 * int(iters)
+
+
+def ssm_diag_stream_scale(t, s, stream=None):
+    """t *= s in place on a contiguous fp32 tensor (the pure-streaming floor)."""
+    st = lib().ssm_diag_stream_scale(_ptr(t), t.numel(), float(s), _stream(t.device, stream))
+    if st != SSM_OK:
+        _raise("ssm_diag_stream_scale", st)
+
+
+def ssm_diag_copy(src, dst, stream=None):
+    st = lib().ssm_diag_copy(_ptr(src), _ptr(dst), src.numel(), _stream(src.device, stream))
+    if st != SSM_OK:
+        _raise("ssm_diag_copy", st)

@@ -203,3 +203,12 @@ def test_noalloc_scratch_limit_is_the_declared_one():
     limit = 32 << 20
     assert ssa.ssm_scan_workspace_size(8, 32768, 512, 16) <= limit      # the long-sequence workload fits
     assert ssa.ssm_scan_workspace_size(1, 4096, 1536, 64) > limit
+
+
+def test_python_binding_has_every_entry_point_by_name():
+    """The binding keeps the C names: every declared function except the library
+    utilities (version, status strings, last error, timing hook) has a same-name
+    Python function in the package."""
+    utilities = {"ssm_abi_version", "ssm_last_error", "ssm_profile_events", "ssm_status_string"}
+    missing = [n for n in declared_functions() if n not in utilities and not hasattr(ssa, n)]
+    assert not missing, missing
