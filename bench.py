@@ -219,6 +219,8 @@ KERNEL_SOURCES = {
     "scan_var": ("scan_core.h", "scan_var.hip", "common.h", "launch.h"),
     "scan_bwd": ("scan_bwd.hip", "common.h", "launch.h"),
     "ssd": ("ssd_fwd.hip", "common.h", "launch.h"),
+    "step": ("step.hip", "common.h", "launch.h"),
+    "ssd_step": ("ssd_step.hip", "common.h", "launch.h"),
 }
 
 
@@ -614,6 +616,7 @@ def step_bench(wl, dev, reps=3, only=None):
     gmed = float(np.median(gtimes)) / steps
     cold = cold_decode(step1, st0, steps)
     return dict(workload="step_bf16_B64_D3072_N16_x1000", ms_per_step_stream=med,
+                traffic=committed_traffic("step", "traffic_step_bf16_B64_D3072_N16.md"), alg_bytes_per_step=alg,
                 ms_per_step_graph=gmed, updates_per_s_graph=B * D * N / (gmed * 1e-3),
                 tokens_per_s_graph=B / (gmed * 1e-3),
                 hbm_gbs_graph=alg / (gmed * 1e-3) / 1e9,
@@ -778,6 +781,7 @@ def ssd_step_bench(wl, dev, reps=3, only=None):
     alg = 2 * B * H * N * P * 4 + 3 * B * H * P * es + B * H * es + 2 * B * N * es + 2 * H * 4
     cold = cold_decode(step1, st0, steps)
     return dict(workload="ssd_step_bf16_B64_H24_P64_N128_x200", ms_per_step_stream=ms_stream,
+                traffic=committed_traffic("ssd_step", "traffic_ssd_step_bf16_B64_H24_P64_N128.md"),
                 ms_per_step_graph=ms_graph, updates_per_s_graph=B * H * P * N / (ms_graph * 1e-3),
                 tokens_per_s_graph=B / (ms_graph * 1e-3), alg_bytes_per_step=alg,
                 hbm_gbs_graph=alg / (ms_graph * 1e-3) / 1e9,
