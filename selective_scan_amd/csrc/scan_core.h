@@ -298,6 +298,12 @@ struct Segment {
         const int tn = min(t + 1, len - 1);
         Bn.load(Bbase, tn, rw);
         if constexpr (FINAL) Cn.load(Cbase, tn, rw);
+        // The aggregate pass pins the next step's B row load here, a whole step ahead
+        // of its use: left alone, the scheduler sinks each scalar load to just before
+        // its first use and every step waits out its latency (B8 L32768 D512 N16:
+        // 340 -> 287 us per launch, bitwise the same). The final pass holds the C rows
+        // as well; there the barrier leaves too few SGPRs and was slower (428 -> 440 us).
+        if constexpr (!FINAL) __builtin_amdgcn_sched_barrier(0);
         if constexpr (V == 0) {
             // the plain path, exponential-Euler with Delta as given
             const float u = dv * xv;
