@@ -18,6 +18,8 @@ storage) and returns float64 arrays. Shapes and meaning follow the C header:
                   -> dict of dx, ddelta, dA, dBm, dCm, dD, dz, dh0
 * ``scan_disc``, ``step_disc``  ``scan`` / ``step`` with disc = "euler" | "zoh" and
                   Delta = softplus(delta + delta_bias) preprocessing
+* ``scan3``       Mamba-3: complex transitions Are + i theta, exponential-trapezoidal
+                  rule weighted by lam -> (y [B,L,D], h_final complex [B,D,N])
 """
 import ctypes
 import os
@@ -59,7 +61,8 @@ class Oracle:
                            ("oracle_ssd_step", [i, i, i, i] + [d] * 9),
                            ("oracle_scan_bwd", [i, i, i, i] + [d] * 18),
                            ("oracle_scan_disc", [i, i, i, i, i, d, i] + [d] * 10),
-                           ("oracle_step_disc", [i, i, i, i, d, i] + [d] * 9)]:
+                           ("oracle_step_disc", [i, i, i, i, d, i] + [d] * 9),
+                           ("oracle_scan3", [i, i, i, i] + [d] * 14)]:
             fn = getattr(self.lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -150,6 +153,30 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return y, hf
+
+    def scan3(self, x, delta, lam, Are, theta, Bm, Cm, D=None, z=None, h0=None, x_prev=None, B_prev=None):
+        """Mamba-3 scan (O8). h0: complex [B,D,N] or None; x_prev [B,D] and B_prev [B,N]:
+        the token before the sequence (both None: zero). Returns (y, h_final complex)."""
+        x, delta, lam, Are, theta, Bm, Cm = map(_f64, (x, delta, lam, Are, theta, Bm, Cm))
+        D, z, xp, bp = _f64(D), _f64(z), _f64(x_prev), _f64(B_prev)
+        Bb, L, Dd = x.shape
+        N = Are.shape[1]
+        assert delta.shape == x.shape and lam.shape == x.shape
+        assert Are.shape == (Dd, N) and theta.shape == (Dd, N)
+        assert Bm.shape == (Bb, L, N) and Cm.shape == (Bb, L, N)
+        h0r = None
+        if h0 is not None:
+            h0 = np.asarray(h0, dtype=np.complex128)
+            assert h0.shape == (Bb, Dd, N)
+            h0r = np.ascontiguousarray(np.stack([h0.real, h0.imag], axis=-1))
+        y = np.empty_like(x)
+        hf = np.empty((Bb, Dd, N, 2))
+        rc = self.lib.oracle_scan3(Bb, L, Dd, N, _ptr(x), _ptr(delta), _ptr(lam), _ptr(Are), _ptr(theta),
+                                   _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0r), _ptr(xp), _ptr(bp),
+                                   _ptr(y), _ptr(hf))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return y, hf[..., 0] + 1j * hf[..., 1]
 
     def step_disc(self, state, x, delta, A, Bm, Cm, D=None, z=None, disc="euler", delta_bias=None,
                   delta_softplus=False):
@@ -261,6 +288,10 @@ def scan_disc(*a, **k):
 
 def step_disc(*a, **k):
     return get().step_disc(*a, **k)
+
+
+def scan3(*a, **k):
+    return get().scan3(*a, **k)
 
 
 def ssd_seq(*a, **k):

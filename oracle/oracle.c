@@ -29,6 +29,7 @@
  */
 #include "oracle.h"
 
+#include <complex.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -544,6 +545,68 @@ int oracle_step_disc(int B, int D, int N, int disc, const double* delta_bias, in
             ch += Cm[b * N + n] * h[n];
         }
         y[u] = finish_output(ch, Dskip, d, xv, z, u);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------- O8 -------
+ * Mamba-3 ("Efficient Sequence Modeling: From S4 to Mamba-3", section 03
+ * System, mamba3_minimal.py, and section 04 "Complex transitions for state
+ * tracking"): complex diagonal transitions A = Are + i theta (the page writes
+ * A = -exp(a) + i theta; Are is passed as the value -exp(a)) with a
+ * data-dependent exponential-trapezoidal rule weighted by lam. The pages name
+ * the rule and pin its reduction to exponential-Euler at lam = 1, theta = 0
+ * but do not write it out; the reading taken is the trapezoidal rule applied to
+ * the exact solution over one step,
+ *   h(t) = e^{Delta A} h(t-1) + integral_0^Delta e^{A (Delta - s)} B x ds,
+ * with the integrand's two endpoint values e^{Delta A} B_{t-1} x_{t-1} and
+ * B_t x_t weighted (1 - lam) and lam (lam = 1/2: the trapezoidal rule; lam = 1:
+ * exponential-Euler). The output reads the real part of the state. */
+int oracle_scan3(int B, int L, int D, int N,
+                 const double* x, const double* delta, const double* lam,
+                 const double* Are, const double* theta,
+                 const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                 const double* h0, const double* x_prev, const double* B_prev,
+                 double* y, double* h_final) {
+    if (bad_dims(B, L, D, N)) return -1;
+    if ((long)B * L * D > 0 && (!x || !delta || !lam || !y)) return -1;
+    if ((long)D * N > 0 && (!Are || !theta)) return -1;
+    if ((long)B * L * N > 0 && (!Bm || !Cm)) return -1;
+    if ((x_prev == NULL) != (B_prev == NULL)) return -1;
+    long units = (long)B * D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < units; ++u) {
+        long b = u / D, d = u % D;
+        double complex* h = (double complex*)malloc(sizeof(double complex) * (N > 0 ? N : 1));
+        for (int n = 0; n < N; ++n) {
+            long k = ((b * D + d) * N + n) * 2;
+            h[n] = h0 ? h0[k] + I * h0[k + 1] : 0.0;
+        }
+        double xp = x_prev ? x_prev[b * D + d] : 0.0;   /* x_{t-1} */
+        const double* Bp = B_prev ? B_prev + b * N : NULL;  /* B_{t-1} */
+        for (long t = 0; t < L; ++t) {
+            long i = (b * L + t) * D + d;
+            const double* Bt = Bm + (b * L + t) * N;
+            const double* Ct = Cm + (b * L + t) * N;
+            double dt = delta[i], xv = x[i], lm = lam[i];
+            double ch = 0.0;
+            for (int n = 0; n < N; ++n) {
+                double complex alpha = cexp(dt * (Are[d * N + n] + I * theta[d * N + n]));
+                double prev = Bp ? Bp[n] * xp : 0.0;
+                h[n] = alpha * h[n] + (1.0 - lm) * dt * alpha * prev + lm * dt * Bt[n] * xv;
+                ch += Ct[n] * creal(h[n]);
+            }
+            y[i] = finish_output(ch, Dskip, d, xv, z, i);
+            xp = xv;
+            Bp = Bt;
+        }
+        if (h_final)
+            for (int n = 0; n < N; ++n) {
+                long k = ((b * D + d) * N + n) * 2;
+                h_final[k] = creal(h[n]);
+                h_final[k + 1] = cimag(h[n]);
+            }
+        free(h);
     }
     return 0;
 }

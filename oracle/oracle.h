@@ -100,6 +100,21 @@ int oracle_step_disc(int B, int D, int N, int disc, const double* delta_bias, in
                      const double* Bm, const double* Cm, const double* Dskip,
                      const double* z, double* y);
 
+/* O8: Mamba-3 selective scan with complex diagonal transitions and the
+ * exponential-trapezoidal rule. Per (b, d), complex state h[n], for t = 0..L-1:
+ *   alpha = exp(delta_t * (Are[d,n] + i theta[d,n]))
+ *   h[n]  = alpha h[n] + (1 - lam_t) delta_t alpha B_{t-1}[n] x_{t-1} + lam_t delta_t B_t[n] x_t
+ *   y_t   = (sum_n C_t[n] Re(h[n]) + D x_t) silu(z_t)
+ * with B_{-1} x_{-1} taken from x_prev [B,D] and B_prev [B,N] (both NULL: zero).
+ * h0 and h_final are complex, [B,D,N,2] (real, imaginary); h0 NULL = zero.
+ * lam = 1, theta = 0 is exactly O1's exponential-Euler recurrence. */
+int oracle_scan3(int B, int L, int D, int N,
+                 const double* x, const double* delta, const double* lam,
+                 const double* Are, const double* theta,
+                 const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                 const double* h0, const double* x_prev, const double* B_prev,
+                 double* y, double* h_final);
+
 #ifdef __cplusplus
 }
 #endif

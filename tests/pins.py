@@ -18,8 +18,9 @@ TIGHT = 1e-10  # fp64 vs fp64: differences are rounding-order only
 
 
 def relerr(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
+    a, b = np.asarray(a), np.asarray(b)
+    dt = np.complex128 if (np.iscomplexobj(a) or np.iscomplexobj(b)) else np.float64
+    a, b = a.astype(dt), b.astype(dt)
     nb = np.linalg.norm(b.ravel())
     d = np.linalg.norm((a - b).ravel())
     return d / nb if nb > 0 else d
@@ -546,6 +547,126 @@ def pin_disc_step_matches_scan(orc):
     close(ss0, h1, what="zoh L=1 state")
 
 
+# --------------------------------------------------- Mamba-3 (O8)
+def mamba3_problem(B, L, D, N, seed, lam=None, theta=True, h0=True, Dskip=True, z=True):
+    """fp64 Mamba-3 problem: Are < 0, rotation rates theta, lam in [0, 1] per (b, t, d)."""
+    r = np.random.default_rng(seed)
+    p = mamba1_problem(B, L, D, N, seed, h0=False, Dskip=Dskip, z=z)
+    A = p.pop("A")
+    p["Are"] = A
+    p["theta"] = r.uniform(-3.0, 3.0, (D, N)) if theta else np.zeros((D, N))
+    p["lam"] = r.uniform(0.0, 1.0, (B, L, D)) if lam is None else np.full((B, L, D), float(lam))
+    if h0:
+        p["h0"] = 0.5 * (r.standard_normal((B, D, N)) + 1j * r.standard_normal((B, D, N)))
+    return p
+
+
+def pin_m3_reduces_to_euler(orc):
+    """lam = 1, theta = 0 is exponential-Euler, i.e. O1 (the reduction the case study's
+    test pins: section 04 "Complex transitions for state tracking", section 09)."""
+    p = mamba3_problem(2, 37, 3, 5, seed=301, lam=1.0, theta=False, h0=False)
+    y, hf = orc.scan3(**p)
+    q = {k: p[k] for k in ("x", "delta", "Bm", "Cm", "D", "z")}
+    y1, h1 = orc.scan(**q, A=p["Are"])
+    close(y, y1, tol=1e-13, what="m3 reduction y")
+    close(hf.real, h1, tol=1e-13, what="m3 reduction h")
+    assert np.max(np.abs(hf.imag)) == 0.0
+
+
+def pin_m3_rotation_block_form(orc):
+    """lam = 1: the complex recurrence equals the real 2-dimensional system whose
+    transition over one step is the matrix exponential of Delta [[Are, -theta],
+    [theta, Are]] acting on (Re h, Im h) (scipy's expm), with the input entering the
+    real component; the output reads the real component."""
+    from scipy.linalg import expm
+    B, L, D, N = 1, 9, 2, 3
+    p = mamba3_problem(B, L, D, N, seed=302, lam=1.0, Dskip=False, z=False)
+    y, hf = orc.scan3(**p)
+    yr = np.zeros((B, L, D))
+    for d in range(D):
+        for n in range(N):
+            v = np.array([p["h0"][0, d, n].real, p["h0"][0, d, n].imag])
+            M = np.array([[p["Are"][d, n], -p["theta"][d, n]], [p["theta"][d, n], p["Are"][d, n]]])
+            for t in range(L):
+                dt = p["delta"][0, t, d]
+                v = expm(dt * M) @ v + np.array([dt * p["Bm"][0, t, n] * p["x"][0, t, d], 0.0])
+                yr[0, t, d] += p["Cm"][0, t, n] * v[0]
+            assert abs(hf[0, d, n] - (v[0] + 1j * v[1])) <= 1e-12 * max(1.0, abs(v[0]) + abs(v[1]))
+    close(y, yr, tol=1e-12, what="m3 rotation-block y")
+
+
+def _m3_exact(a, th, b, xf, T):
+    """h(T) of dh/dt = (a + i th) h + b x(t), h(0) = 0, by adaptive quadrature."""
+    from scipy.integrate import quad
+    re = quad(lambda s_: math.exp(a * (T - s_)) * math.cos(th * (T - s_)) * b * xf(s_), 0.0, T,
+              epsabs=1e-15, epsrel=1e-13, limit=400)[0]
+    im = quad(lambda s_: math.exp(a * (T - s_)) * math.sin(th * (T - s_)) * b * xf(s_), 0.0, T,
+              epsabs=1e-15, epsrel=1e-13, limit=400)[0]
+    return re + 1j * im
+
+
+def pin_m3_trapezoid_order(orc):
+    """Against the exact solution of dh/dt = A h + B x(t) for a smooth input sampled at
+    the step ends: lam = 1/2 (the trapezoidal rule on the one-step integral) is second
+    order -- halving Delta cuts the error about 4x -- and lam = 1 (exponential-Euler)
+    first order, about 2x; for real and complex A."""
+    T, b = 2.0, 0.9
+    xf = lambda t: math.sin(1.3 * t) + 0.5 * math.cos(0.4 * t)  # noqa: E731
+    for a, th in ((-0.7, 0.0), (-0.4, 1.7)):
+        exact = _m3_exact(a, th, b, xf, T)
+        for lam, lo, hi in ((0.5, 3.6, 4.4), (1.0, 1.7, 2.3)):
+            errs = []
+            for L in (64, 128, 256):
+                dt = T / L
+                xs = np.array([xf((t + 1) * dt) for t in range(L)])
+                p = dict(x=xs.reshape(1, L, 1), delta=np.full((1, L, 1), dt), lam=np.full((1, L, 1), lam),
+                         Are=np.array([[a]]), theta=np.array([[th]]), Bm=np.full((1, L, 1), b),
+                         Cm=np.ones((1, L, 1)), x_prev=np.array([[xf(0.0)]]), B_prev=np.array([[b]]))
+                _, hf = orc.scan3(**p)
+                errs.append(abs(hf[0, 0, 0] - exact))
+            for e1, e2 in zip(errs, errs[1:]):
+                assert lo <= e1 / e2 <= hi, (a, th, lam, errs)
+
+
+def pin_m3_constant_input_closed_form(orc):
+    """Constant inputs (and the same token before the sequence): h_t = alpha^t h0 +
+    c (1 - alpha^t)/(1 - alpha) with alpha = e^{Delta (Are + i theta)} and
+    c = ((1 - lam) alpha + lam) Delta B x, in numpy complex arithmetic."""
+    B, L, D, N = 1, 33, 2, 3
+    r = np.random.default_rng(303)
+    Are = -np.exp(r.uniform(-1.0, 1.0, (D, N)))
+    th = r.uniform(-2.0, 2.0, (D, N))
+    x0, d0, l0 = 0.8, 0.11, 0.3
+    b0, c0 = r.standard_normal(N), r.standard_normal(N)
+    h0 = r.standard_normal((B, D, N)) + 1j * r.standard_normal((B, D, N))
+    p = dict(x=np.full((B, L, D), x0), delta=np.full((B, L, D), d0), lam=np.full((B, L, D), l0), Are=Are,
+             theta=th, Bm=np.tile(b0, (B, L, 1)), Cm=np.tile(c0, (B, L, 1)), h0=h0,
+             x_prev=np.full((B, D), x0), B_prev=np.tile(b0, (B, 1)))
+    y, hf = orc.scan3(**p)
+    alpha = np.exp(d0 * (Are + 1j * th))                          # [D,N]
+    c = ((1 - l0) * alpha + l0) * d0 * b0 * x0                     # [D,N]
+    t = np.arange(1, L + 1)[:, None, None]
+    h = alpha[None] ** t * h0[0] + c * (1 - alpha[None] ** t) / (1 - alpha)   # [L,D,N]
+    close(y[0], np.einsum("ldn,n->ld", h.real, c0), tol=1e-11, what="m3 constant y")
+    close(hf[0], h[-1], tol=1e-11, what="m3 constant h")
+
+
+def pin_m3_split_carry(orc):
+    """scan3(x[:m]) then scan3(x[m:]) from its final state and its last token equals
+    scan3(x)."""
+    p = mamba3_problem(2, 40, 3, 4, seed=304)
+    y, hf = orc.scan3(**p)
+    m = 17
+    cut = lambda k, s_: p[k][:, s_]  # noqa: E731
+    seq = ("x", "delta", "lam", "Bm", "Cm", "z")
+    y1, h1 = orc.scan3(**{k: (cut(k, slice(0, m)) if k in seq else v) for k, v in p.items()})
+    q = {k: (cut(k, slice(m, None)) if k in seq else v) for k, v in p.items()}
+    q.update(h0=h1, x_prev=p["x"][:, m - 1], B_prev=p["Bm"][:, m - 1])
+    y2, h2 = orc.scan3(**q)
+    close(np.concatenate([y1, y2], axis=1), y, what="m3 split y")
+    close(h2, hf, what="m3 split h")
+
+
 ALL_PINS = [
     pin_chunked_equals_sequential,
     pin_constant_input_closed_form,
@@ -567,4 +688,9 @@ ALL_PINS = [
     pin_zoh_constant_input_closed_form,
     pin_zoh_phi_both_branches,
     pin_disc_step_matches_scan,
+    pin_m3_reduces_to_euler,
+    pin_m3_rotation_block_form,
+    pin_m3_trapezoid_order,
+    pin_m3_constant_input_closed_form,
+    pin_m3_split_carry,
 ]

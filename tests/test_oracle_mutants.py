@@ -52,6 +52,14 @@ MUTANTS = {
     "delta_bias_ignored": ("if (delta_bias) dt += delta_bias[d];", ""),
     "softplus_large_branch_truncated": ("return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
                                         "return v > 0.0 ? v : log1p(exp(v));"),
+    "m3_prev_term_without_decay": ("(1.0 - lm) * dt * alpha * prev", "(1.0 - lm) * dt * prev"),
+    "m3_lambda_weights_swapped": ("(1.0 - lm) * dt * alpha * prev + lm * dt * Bt[n] * xv",
+                                  "lm * dt * alpha * prev + (1.0 - lm) * dt * Bt[n] * xv"),
+    "m3_rotation_sign": ("cexp(dt * (Are[d * N + n] + I * theta[d * N + n]))",
+                         "cexp(dt * (Are[d * N + n] - I * theta[d * N + n]))"),
+    "m3_output_reads_imaginary_part": ("ch += Ct[n] * creal(h[n]);", "ch += Ct[n] * cimag(h[n]);"),
+    "m3_previous_token_not_advanced": ("xp = xv;\n            Bp = Bt;", "Bp = Bt;"),
+    "m3_h0_imaginary_dropped": ("h[n] = h0 ? h0[k] + I * h0[k + 1] : 0.0;", "h[n] = h0 ? h0[k] : 0.0;"),
 }
 
 
