@@ -1,9 +1,11 @@
 /*
  * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan library.
  *
- * Seven entry points, each a hand-written HIP kernel pipeline for CDNA4:
+ * Entry points, each a hand-written HIP kernel pipeline for CDNA4:
  *   ssm_scan_fwd     Mamba-1 selective scan over a whole sequence (prefill)
+ *   ssm_scan_fwd_noalloc  the same on a fixed per-GPU scratch (no workspace argument)
  *   ssm_scan_fwd_ex  the same with exact zero-order hold and/or Delta = softplus(delta + bias)
+ *   ssm_scan3_fwd    Mamba-3: complex transitions, exponential-trapezoidal rule
  *   ssm_scan_bwd     the scan's gradient (training backward pass)
  *   ssm_ssd_fwd      Mamba-2 SSD: scalar decay per head, chunked decayed-attention form
  *   ssm_step         one-token recurrent decode step, state updated in place
@@ -188,6 +190,47 @@ int ssm_scan_fwd_ex(int B, int L, int D, int N, ssm_dtype_t io, ssm_disc_t disc,
                     const void* z, const float* h0,
                     void* y, float* h_final,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_scan3_fwd -- Mamba-3 selective scan: complex diagonal transitions and the
+ * exponential-trapezoidal rule.
+ *
+ * "Efficient Sequence Modeling: From S4 to Mamba-3", section 03 System
+ * (mamba3_minimal.py: complex diagonal transitions A = -exp(a) + i theta with a
+ * data-dependent exponential-trapezoidal rule, reducing to Mamba-1/2 at lam = 1)
+ * and section 04 "Complex transitions for state tracking" (the rotation phase
+ * lets the state track parity; lam = 1, theta = 0 is exponential-Euler). The
+ * pages do not write the rule out; the reading implemented is the trapezoidal
+ * rule, weighted by lam, on the exact one-step integral of e^{A (Delta - s)} B x.
+ * Per (b, d), complex state h[n], for t = 0 .. L-1:
+ *   alpha   = exp(delta[b,t,d] * (Are[d,n] + i theta[d,n]))
+ *   h[n]    = alpha h[n] + (1 - lam[b,t,d]) delta[b,t,d] alpha Bm[b,t-1,n] x[b,t-1,d]
+ *                        + lam[b,t,d] delta[b,t,d] Bm[b,t,n] x[b,t,d]
+ *   y[b,t,d] = (sum_n Cm[b,t,n] Re(h[n]) + Dskip[d] x[b,t,d]) * silu(z[b,t,d])
+ * where the step before t = 0 is (x_prev[b,d], B_prev[b,:]) -- the last token of
+ * a previous call, so that a sequence can be continued -- or zero when both are
+ * NULL.
+ *
+ *   x, delta, lam, z, y : [B, L, D]  io dtype (z may be NULL); lam in [0, 1]
+ *   Are, theta     : [D, N]     fp32 (Are < 0: the real part of A; theta in radians
+ *                               per unit of delta)
+ *   Bm, Cm         : [B, L, N]  io dtype
+ *   Dskip          : [D]        fp32 or NULL
+ *   h0, h_final    : [B, D, N, 2] fp32 complex (real, imaginary), or NULL
+ *   x_prev, B_prev : [B, D], [B, N] io dtype, both given or both NULL
+ *   workspace      : at least ssm_scan3_workspace_size(B, L, D, N) bytes
+ * Supported: N in {4, 8, 16}; B <= 65535. Every pointer must be 16-byte aligned.
+ * Errors as for ssm_scan_fwd.
+ * ------------------------------------------------------------------------- */
+size_t ssm_scan3_workspace_size(int B, int L, int D, int N);
+
+int ssm_scan3_fwd(int B, int L, int D, int N, ssm_dtype_t io,
+                  const void* x, const void* delta, const void* lam,
+                  const float* Are, const float* theta,
+                  const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                  const float* h0, const void* x_prev, const void* B_prev,
+                  void* y, float* h_final,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * ssm_scan_bwd -- gradient of ssm_scan_fwd (training backward pass).

@@ -11,6 +11,7 @@
 
 #include "extras.h"
 #include "launch.h"
+#include "scan3.h"
 
 namespace {
 
@@ -218,6 +219,43 @@ int ssm_scan_fwd_noalloc(int B, int L, int D, int N, ssm_dtype_t io,
     ssm::ScanArgs a{B, L, D, N, io == SSM_BF16, x, delta, A, Bm, Cm, Dskip, z, h0, y, h_final, ws,
                     nullptr, 0, SSM_DISC_EULER};
     return hip_status(ssm::launch_scan_fwd(a, hs), fn);
+}
+
+// ------------------------------------------------------------------ Mamba-3 scan
+size_t ssm_scan3_workspace_size(int B, int L, int D, int N) {
+    if (B < 1 || L < 0 || D < 1 || !ssm::scan3_supported_n(N)) return 0;
+    if (!product_ok({B, L, D, N})) return 0;
+    return ssm::scan3_workspace_bytes(B, L, D, N);
+}
+
+int ssm_scan3_fwd(int B, int L, int D, int N, ssm_dtype_t io,
+                  const void* x, const void* delta, const void* lam,
+                  const float* Are, const float* theta,
+                  const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                  const float* h0, const void* x_prev, const void* B_prev,
+                  void* y, float* h_final,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "ssm_scan3_fwd";
+    if (B < 1 || D < 1 || L < 0 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1 and L >= 0");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (!ssm::scan3_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16");
+    if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
+    if (!product_ok({B, L, D, N}, 1LL << 40) || !product_ok({B, L, D}, 1LL << 40))
+        return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if (!Are || !theta) return fail(SSM_ERR_INVALID_ARG, fn, "Are and theta are required");
+    if (L > 0 && (!x || !delta || !lam || !Bm || !Cm || !y))
+        return fail(SSM_ERR_INVALID_ARG, fn, "x, delta, lam, Bm, Cm and y are required");
+    if ((x_prev == nullptr) != (B_prev == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, fn, "x_prev and B_prev must be given together");
+    const void* ptrs[] = {x, delta, lam, Are, theta, Bm, Cm, Dskip, z, h0, x_prev, B_prev, y, h_final, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    const size_t need = ssm::scan3_workspace_bytes(B, L, D, N);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(SSM_ERR_WORKSPACE, fn, "workspace missing or smaller than ssm_scan3_workspace_size()");
+    ssm::Scan3Args a{B, L, D, N, io == SSM_BF16, x, delta, lam, Are, theta, Bm, Cm, Dskip, z, h0, x_prev, B_prev,
+                     y, h_final, workspace};
+    return hip_status(ssm::launch_scan3_fwd(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 // ------------------------------------------------------------------ scan backward

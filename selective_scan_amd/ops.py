@@ -44,6 +44,9 @@ def lib():
     L.ssm_scan_fwd.restype = i
     L.ssm_scan_fwd_noalloc.argtypes = [i, i, i, i, i] + [vp] * 10 + [vp]
     L.ssm_scan_fwd_noalloc.restype = i
+    L.ssm_scan3_workspace_size.argtypes, L.ssm_scan3_workspace_size.restype = [i, i, i, i], sz
+    L.ssm_scan3_fwd.argtypes = [i, i, i, i, i] + [vp] * 14 + [vp, sz, vp]
+    L.ssm_scan3_fwd.restype = i
     L.ssm_scan_fwd_ex.argtypes = [i, i, i, i, i, i, vp, i] + [vp] * 10 + [vp, sz, vp]
     L.ssm_scan_fwd_ex.restype = i
     L.ssm_step_ex.argtypes = [i, i, i, i, i, vp, i] + [fp] + [vp] * 8 + [vp]
@@ -193,6 +196,44 @@ def _scan_fwd(fn, x, delta, A, Bm, Cm, D, z, h0, y, h_final, workspace, stream, 
         st = lib().ssm_scan_fwd_ex(Bb, L, Dd, N, _io_code(x), disc, _ptr(bias), int(sp), *args)
     if st != SSM_OK:
         _raise(fn, st)
+    return y, h_final
+
+
+def ssm_scan3_workspace_size(B, L, D, N):
+    return int(lib().ssm_scan3_workspace_size(B, L, D, N))
+
+
+def ssm_scan3_fwd(x, delta, lam, Are, theta, Bm, Cm, D=None, z=None, h0=None, x_prev=None, B_prev=None, *,
+                  y=None, h_final=None, workspace=None, stream=None, want_final_state=True):
+    """Mamba-3 scan. x, delta, lam, z: [B, L, D]; Bm, Cm: [B, L, N] (bf16 or fp32); Are,
+    theta: [D, N] fp32; D: [D]; h0: [B, D, N, 2] fp32 (real, imaginary); x_prev [B, D] and
+    B_prev [B, N]: the token before the sequence. Returns (y, h_final [B, D, N, 2])."""
+    Bb, L, Dd = x.shape
+    N = Are.shape[1]
+    dev, io = x.device, x.dtype
+    for t, nm, shp, dt, req in ((x, "x", (Bb, L, Dd), io, True), (delta, "delta", (Bb, L, Dd), io, True),
+                                (lam, "lam", (Bb, L, Dd), io, True), (Are, "Are", (Dd, N), torch.float32, True),
+                                (theta, "theta", (Dd, N), torch.float32, True), (Bm, "Bm", (Bb, L, N), io, True),
+                                (Cm, "Cm", (Bb, L, N), io, True), (D, "D", (Dd,), torch.float32, False),
+                                (z, "z", (Bb, L, Dd), io, False), (h0, "h0", (Bb, Dd, N, 2), torch.float32, False),
+                                (x_prev, "x_prev", (Bb, Dd), io, False), (B_prev, "B_prev", (Bb, N), io, False)):
+        _check(t, nm, shp, dt, dev, required=req)
+    need = ssm_scan3_workspace_size(Bb, L, Dd, N)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((Bb, L, Dd), dtype=io, device=dev)
+        if want_final_state and h_final is None:
+            h_final = torch.empty((Bb, Dd, N, 2), dtype=torch.float32, device=dev)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(y, "y", (Bb, L, Dd), io, dev)
+    _check(h_final, "h_final", (Bb, Dd, N, 2), torch.float32, dev, required=False)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ssm_scan3_fwd(Bb, L, Dd, N, _io_code(x), _ptr(x), _ptr(delta), _ptr(lam), _ptr(Are), _ptr(theta),
+                             _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(h0), _ptr(x_prev), _ptr(B_prev), _ptr(y),
+                             _ptr(h_final), _ptr(workspace), wbytes, _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_scan3_fwd", st)
     return y, h_final
 
 

@@ -25,6 +25,7 @@ import numpy as np
 
 # fixed stream ids, one per tensor
 TID_DT, TID_X, TID_Z, TID_EPS, TID_B, TID_C, TID_D, TID_A, TID_STATE0, TID_DY, TID_DHF = range(11)
+TID_LAM, TID_THETA, TID_PREV = 11, 12, 13
 
 BF16, F32 = "bf16", "f32"
 
@@ -123,6 +124,25 @@ def scan_inputs(B, L, D, N, dtype=BF16, seed=0, with_D=True, with_z=True, with_h
     return out
 
 
+def scan3_inputs(B, L, D, N, dtype=BF16, seed=0, with_D=True, with_z=True, with_h0=False, with_prev=False):
+    """Mamba-3 scan inputs: those of ``scan_inputs`` (A as the real part Are) plus
+    lam = sigmoid(N(0,1)) [B,L,D] in ``dtype``, rotation rates theta ~ U(-pi, pi) [D,N]
+    float32, complex h0 [B,D,N,2] (real, imaginary) float32 and the token before the
+    sequence, x_prev [B,D] and B_prev [B,N] in ``dtype``."""
+    out = scan_inputs(B, L, D, N, dtype=dtype, seed=seed, with_D=with_D, with_z=with_z, with_h0=False)
+    out["Are"] = out.pop("A")
+    out["lam"] = store(1.0 / (1.0 + np.exp(-_normal(seed, TID_LAM, (B, L, D)))), dtype)
+    out["theta"] = _rng(seed, TID_THETA).uniform(-math.pi, math.pi, (D, N)).astype(np.float32)
+    out["h0"] = (0.1 * _normal(seed, TID_STATE0, (B, D, N, 2))).astype(np.float32) if with_h0 else None
+    if with_prev:
+        r = _rng(seed, TID_PREV)
+        out["x_prev"] = store(r.standard_normal((B, D)), dtype)
+        out["B_prev"] = store(r.standard_normal((B, N)) / math.sqrt(N), dtype)
+    else:
+        out["x_prev"] = out["B_prev"] = None
+    return out
+
+
 def scan_raw_delta(B, L, D, dtype=BF16, seed=0):
     """Delta before its softplus, for the kernels that apply softplus(delta + bias)
     themselves: delta = 0.5 eps [B,L,D] in ``dtype`` and delta_bias = ln(expm1(dt_c))
@@ -207,6 +227,8 @@ WORKLOADS = {
     "scan_bwd_bf16_B8_L32768_D512_N16": dict(kind="scan_bwd", B=8, L=32768, D=512, N=16, dtype=BF16),
     # the headline layer with exact zero-order hold and softplus(delta + bias) in the kernel
     "scan_zoh_softplus_bf16_B1_L4096_D1536_N16": dict(kind="scan_var", B=1, L=4096, D=1536, N=16, dtype=BF16),
+    # the headline layer as a Mamba-3 scan (complex transitions, exponential-trapezoidal rule)
+    "scan3_bf16_B1_L4096_D1536_N16": dict(kind="scan3", B=1, L=4096, D=1536, N=16, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q256": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,
                                                 chunk=256, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q64": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,

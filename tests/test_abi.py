@@ -212,3 +212,26 @@ def test_python_binding_has_every_entry_point_by_name():
     utilities = {"ssm_abi_version", "ssm_last_error", "ssm_profile_events", "ssm_status_string"}
     missing = [n for n in declared_functions() if n not in utilities and not hasattr(ssa, n)]
     assert not missing, missing
+
+
+def _scan3(B=1, L=8, D=64, N=16, io=1, x=P, delta=P, lam=P, Are=P, theta=P, Bm=P, Cm=P, Dk=None, z=None, h0=None,
+           xp=None, bp=None, y=P, hf=None, ws=None, wsb=0):
+    return ops.lib().ssm_scan3_fwd(B, L, D, N, io, x, delta, lam, Are, theta, Bm, Cm, Dk, z, h0, xp, bp, y, hf, ws,
+                                   wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(L=-1), 1), (dict(io=3), 1), (dict(N=32), 2), (dict(N=12), 2), (dict(B=70000), 2),
+    (dict(lam=None), 1), (dict(theta=None), 1), (dict(Are=None), 1), (dict(y=None), 1),
+    (dict(xp=P), 1), (dict(bp=P), 1), (dict(h0=ctypes.c_void_p(0x10004)), 1),
+    (dict(L=4096, D=1536), 3),
+])
+def test_scan3_rejects_bad_arguments(kw, status):
+    assert _scan3(**kw) == status
+    assert ops.lib().ssm_last_error().startswith(b"ssm_scan3_fwd: ")
+
+
+def test_scan3_workspace_size():
+    assert ssa.ssm_scan3_workspace_size(1, 4096, 1536, 16) > 0
+    assert ssa.ssm_scan3_workspace_size(1, 32, 64, 16) == 0      # a single segment needs none
+    assert ssa.ssm_scan3_workspace_size(1, 4096, 1536, 32) == 0  # unsupported N
