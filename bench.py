@@ -434,6 +434,55 @@ def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16, trans_cost=DEFAULT
                               kernel="segment_final (zero-order hold, softplus(delta + bias))"))
 
 
+# ------------------------------------------------------------------ Mamba-3 scan
+# One pass of the Mamba-3 recurrence per state update: v_mul (Delta*Are), v_mul
+# (Delta*theta), v_mul x 2 (|alpha| cos, |alpha| sin), v_fma (h + q B_{t-1}), v_mul (r B_t),
+# v_fma x 2 (real part), v_mul + v_fma (imaginary part), v_fma (C.Re h) -> 11 FMA-class
+# ops, and three transcendentals (v_exp_f32, v_sin_f32, v_cos_f32).
+SCAN3_FMA_OPS_PER_UPDATE = 11.0
+SCAN3_TRANS_PER_UPDATE = 3.0
+
+
+def scan3_bench(name, wl, steps, warmup, dev, max_sets=16, trans_cost=DEFAULT_TRANS_COST):
+    import torch
+    import ssm_inputs as si
+    import selective_scan_amd as ssa
+    B, L, D, N = wl["B"], wl["L"], wl["D"], wl["N"]
+    es = 2 if wl["dtype"] == si.BF16 else 4
+    set_bytes = 5 * B * L * D * es + 2 * B * L * N * es
+    R = max(1, min(max_sets, math.ceil(2 * MALL_BYTES / set_bytes)))
+    keys = ("x", "delta", "lam", "Are", "theta", "Bm", "Cm", "D", "z")
+    sets = []
+    for r in range(R):
+        w = si.scan3_inputs(B, L, D, N, dtype=wl["dtype"], seed=r)
+        t = {k: si.to_torch(w[k], dev) for k in keys}
+        t["y"] = torch.empty_like(t["x"])
+        t["hf"] = torch.empty((B, D, N, 2), dtype=torch.float32, device=dev)
+        sets.append(t)
+    ws = torch.empty(max(ssa.ssm_scan3_workspace_size(B, L, D, N), 1), dtype=torch.uint8, device=dev)
+
+    def call(t):
+        ssa.ssm_scan3_fwd(t["x"], t["delta"], t["lam"], t["Are"], t["theta"], t["Bm"], t["Cm"], D=t["D"], z=t["z"],
+                          y=t["y"], h_final=t["hf"], workspace=ws)
+
+    nk = count_kernels(lambda: call(sets[0]))
+    total_ms, ker = time_calls(call, sets, steps, warmup, nk)
+    lat = latency(call, sets)
+    ms = total_ms / steps
+    kmean = ker.mean(axis=0)
+    dom = int(np.argmax(kmean))
+    upd = B * L * D * N
+    alg = 5 * B * L * D * es + 2 * B * L * N * es + 2 * D * N * 4 + D * 4 + 2 * B * D * N * 4
+    slots = SCAN3_FMA_OPS_PER_UPDATE + SCAN3_TRANS_PER_UPDATE * trans_cost
+    achieved = slots * upd / (kmean[dom] * 1e-3) / 1e12
+    peak = LANE_SLOTS_PER_S / 1e12
+    return dict(workload=name, ms_per_step=ms, updates_per_s=upd / (ms * 1e-3), tokens_per_s=B * L / (ms * 1e-3),
+                call_latency=lat, kernel_ms=[float(v) for v in kmean], hbm_gbs=alg / (ms * 1e-3) / 1e9,
+                hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, sets=len(sets), alg_bytes=alg,
+                roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
+                              slots_per_update=slots, kernel="seg_final3 (dominant)"))
+
+
 # ------------------------------------------------------------------ scan backward
 # Per state update, the final backward pass must issue: forward recompute v_mul
 # (Delta*A), v_exp_f32, v_mul (u*B), v_fma (state), v_fma (C.h), v_mul (dv*h for dC);
@@ -845,6 +894,8 @@ def main():
             r = scan_bwd_bench(args.other, wl, args.steps, args.warmup, dev)
         elif wl["kind"] == "scan_var":
             r = scan_var_bench(args.other, wl, args.steps, args.warmup, dev)
+        elif wl["kind"] == "scan3":
+            r = scan3_bench(args.other, wl, args.steps, args.warmup, dev)
         elif wl["kind"] == "ssd":
             r = ssd_bench(args.other, wl, args.steps, args.warmup, dev)
         elif wl["kind"] == "scan":
@@ -904,6 +955,9 @@ def main():
         other["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"] = scan_var_bench(
             "scan_zoh_softplus_bf16_B1_L4096_D1536_N16", si.WORKLOADS["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"],
             steps=20, warmup=3, dev=dev, trans_cost=trans_cost)
+        other["scan3_bf16_B1_L4096_D1536_N16"] = scan3_bench(
+            "scan3_bf16_B1_L4096_D1536_N16", si.WORKLOADS["scan3_bf16_B1_L4096_D1536_N16"], steps=20, warmup=3,
+            dev=dev, trans_cost=trans_cost)
         for nm in ("scan_bwd_bf16_B1_L4096_D1536_N16", "scan_bwd_bf16_B8_L32768_D512_N16"):
             other[nm] = scan_bwd_bench(nm, si.WORKLOADS[nm], steps=10 if si.WORKLOADS[nm]["L"] <= 4096 else 3,
                                        warmup=2, dev=dev, trans_cost=trans_cost)

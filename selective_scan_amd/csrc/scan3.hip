@@ -79,12 +79,21 @@ __device__ __forceinline__ float ld_io(const void* p, size_t i) {
     else return static_cast<const float*>(p)[i];
 }
 
-// Complex decay over a total sum(Delta) s: exp(s (Are + i theta)) with A2 = Are log2 e
-// and th = theta / (2 pi) (revolutions).
+// One step's complex decay exp(dv (Are + i theta)) with A2 = Are log2 e and th =
+// theta / (2 pi) (revolutions; one step turns far less than a revolution).
+__device__ __forceinline__ void cstep(float dv, float A2, float th, float& pr, float& pi) {
+    const float m = exp2_fast(dv * A2);
+    const float ph = dv * th;
+    pr = m * __builtin_amdgcn_cosf(ph);
+    pi = m * __builtin_amdgcn_sinf(ph);
+}
+
+// The same over a sum of many steps s, with the phase first reduced to
+// [-1/2, 1/2] revolution, where v_sin / v_cos are most accurate.
 __device__ __forceinline__ void cdecay(float s, float A2, float th, float& pr, float& pi) {
     const float m = exp2_fast(s * A2);
     float ph = s * th;
-    ph -= __builtin_rintf(ph);  // v_sin / v_cos are most accurate near zero revolutions
+    ph -= __builtin_rintf(ph);
     pr = m * __builtin_amdgcn_cosf(ph);
     pi = m * __builtin_amdgcn_sinf(ph);
 }
@@ -116,10 +125,21 @@ __device__ __forceinline__ void walk3(const Scan3Args& a, int b, int d, int dc, 
 #pragma unroll
         for (int k = 0; k < Row<N, BF16>::K; ++k) Bp.v[k] = 0u;
     }
+    // this step's x, Delta, lam (and z) were loaded one step earlier
+    auto at = [&](int t) { return ((size_t)b * a.L + t0 + t) * D + dc; };
+    float dn = ld_io<BF16>(a.delta, at(0)), xn = ld_io<BF16>(a.x, at(0)), ln = ld_io<BF16>(a.lam, at(0));
+    float zn = (FINAL && a.z != nullptr) ? ld_io<BF16>(a.z, at(0)) : 0.0f;
     for (int t = 0; t < len; ++t) {
         const size_t row = (size_t)b * a.L + t0 + t;
         const size_t i = row * D + dc;
-        const float dv = ld_io<BF16>(a.delta, i), xv = ld_io<BF16>(a.x, i), lv = ld_io<BF16>(a.lam, i);
+        const float dv = dn, xv = xn, lv = ln, zv = zn;
+        {
+            const size_t j = at(min(t + 1, len - 1));
+            dn = ld_io<BF16>(a.delta, j);
+            xn = ld_io<BF16>(a.x, j);
+            ln = ld_io<BF16>(a.lam, j);
+            if (FINAL && a.z != nullptr) zn = ld_io<BF16>(a.z, j);
+        }
         Bt.load(a.Bm, (long)row, rw);
         if constexpr (FINAL) Ct.load(a.Cm, (long)row, rw);
         const float q = (1.0f - lv) * dv * xp;  // weight of B_{t-1}[n] (times alpha)
@@ -128,7 +148,7 @@ __device__ __forceinline__ void walk3(const Scan3Args& a, int b, int d, int dc, 
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             float ar, ai;
-            cdecay(dv, A2[n], th[n], ar, ai);
+            cstep(dv, A2[n], th[n], ar, ai);
             const float g = __builtin_fmaf(q, Bp.at(n), hr[n]);  // h + q B_{t-1}: both multiplied by alpha
             const float nr = __builtin_fmaf(ar, g, __builtin_fmaf(-ai, hi[n], r * Bt.at(n)));
             const float ni = __builtin_fmaf(ai, g, ar * hi[n]);
@@ -141,7 +161,7 @@ __device__ __forceinline__ void walk3(const Scan3Args& a, int b, int d, int dc, 
         }
         if constexpr (FINAL) {
             float v = __builtin_fmaf(Dv, xv, y0 + y1);
-            if (a.z != nullptr) v *= silu(ld_io<BF16>(a.z, i));
+            if (a.z != nullptr) v *= silu(zv);
             if (d < D) {
                 if constexpr (BF16) static_cast<uint16_t*>(a.y)[i] = f32_to_bf16(v);
                 else static_cast<float*>(a.y)[i] = v;
