@@ -144,14 +144,14 @@ int ssm_scan_fwd(int B, int L, int D, int N, ssm_dtype_t io,
  * forbid hipMalloc): no workspace argument, and nothing is allocated or freed.
  *
  * The scan's carry workspace is a fixed device array inside the library,
- * SSM_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the library's load until
+ * SSM_NOALLOC_SCRATCH_BYTES (128 MiB) per GPU, held from the library's load until
  * the process ends. Its device address is looked up on the first call made for
  * a device (with that device made current for the lookup). Every other argument,
  * the result and the errors are those of ssm_scan_fwd; a shape whose
  * ssm_scan_workspace_size() exceeds SSM_NOALLOC_SCRATCH_BYTES returns
- * SSM_ERR_UNSUPPORTED (for instance B=8, L=32768, D=512, N=16 needs 30.75 MiB and
- * fits; N = 64 at B=1, L=4096, D=1536 needs 96 MiB and does not). The kernels run on the device
- * of `stream` (the current device when stream is NULL).
+ * SSM_ERR_UNSUPPORTED (for instance B=8, L=32768, D=512, N=16 needs 99.5 MiB
+ * and fits; N = 256 at B=1, L=4096, D=1536 needs 141.2 MiB and does not). The
+ * kernels run on the device of `stream` (the current device when stream is NULL).
  *
  * Concurrency: all calls on one GPU share its scratch array and nothing clears
  * it between calls (the scan ignores its previous contents). Calls that can
@@ -159,7 +159,7 @@ int ssm_scan_fwd(int B, int L, int D, int N, ssm_dtype_t io,
  * ordering -- race on it and give undefined results; serialise them (one stream,
  * or events between streams).
  * ------------------------------------------------------------------------- */
-#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 int ssm_scan_fwd_noalloc(int B, int L, int D, int N, ssm_dtype_t io,
                          const void* x, const void* delta, const float* A,

@@ -46,10 +46,13 @@ namespace {
 
 // Geometry defaults; each can be overridden at build time (-DSSM_SCAN_...).
 #ifndef SSM_SCAN_PREFETCH
-#define SSM_SCAN_PREFETCH 8
+#define SSM_SCAN_PREFETCH 4
+#endif
+#ifndef SSM_SCAN_PREFETCH_FINAL
+#define SSM_SCAN_PREFETCH_FINAL 2
 #endif
 #ifndef SSM_SCAN_TARGET_WAVES
-#define SSM_SCAN_TARGET_WAVES 5120
+#define SSM_SCAN_TARGET_WAVES 16384
 #endif
 #ifndef SSM_SCAN_MIN_SEGMENT
 #define SSM_SCAN_MIN_SEGMENT 32
@@ -57,7 +60,15 @@ namespace {
 #ifndef SSM_SCAN_MAX_GROUP
 #define SSM_SCAN_MAX_GROUP 4
 #endif
-constexpr int kPrefetch = SSM_SCAN_PREFETCH;       // steps of x/Delta/z in flight per lane
+// Steps of x/Delta/z in flight per lane: kPrefetch in the aggregate pass and the
+// chunked (N >= 64) final pass, kPrefetchFinal in the plain final pass. Fewer
+// registers in the ring buy waves, and with 16384 target waves (three or more
+// waves per SIMD over the launch) the waves hide the load latency better than a
+// deep ring: B8 L32768 D512 N16 went from 0.72 ms per call (5120 waves, ring of 8)
+// to 0.64 ms (aggregate 287 -> 269 us, final 427 -> 356 us); at B1 L4096 D1536
+// N16 0.051 -> 0.049 ms; N = 64 unchanged.
+constexpr int kPrefetch = SSM_SCAN_PREFETCH;
+constexpr int kPrefetchFinal = SSM_SCAN_PREFETCH_FINAL;
 constexpr int kTargetWaves = SSM_SCAN_TARGET_WAVES;  // waves the final pass aims for
 constexpr int kMinSegment = SSM_SCAN_MIN_SEGMENT;    // shortest segment (steps)
 
@@ -194,12 +205,14 @@ __device__ __forceinline__ float var_delta(float dv, const VarLane<N, V>& vl) {
 }
 
 // One wave's segment of the recurrence. Construction issues the first loads
-// (kPrefetch steps of x, Delta[, z] and the first B[, C] rows), so a caller can
+// (kP steps of x, Delta[, z] and the first B[, C] rows), so a caller can
 // start them before other prologue work; run() then walks the segment.
 template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL, int V = 0, bool SINK = false>
 struct Segment {
     static_assert(!SINK || (FINAL && V == 0), "the LDS sink holds plain partial sums");
     static constexpr uint32_t es = BF16 ? 2 : 4;
+    // ring depth; the LDS sink's slot layout is sized with kPrefetch
+    static constexpr int kP = FINAL && !SINK ? kPrefetchFinal : kPrefetch;
     static constexpr bool kZ = FINAL && HAS_Z;
     __amdgpu_buffer_rsrc_t rx, rd, rz, ry;
     uint32_t voff, yoff, rstride, ystride;
@@ -208,7 +221,7 @@ struct Segment {
     int rw;  // row stride of B and C in 32-bit words
     int len;
     float* lsink = nullptr;  // SINK: ring slot k's partial sums go to lsink[64 k + lane]
-    uint32_t dq[kPrefetch], xq[kPrefetch], zq[kPrefetch];
+    uint32_t dq[kP], xq[kP], zq[kP];
     Row<N, BF16> Bn, Cn;
 
     // store: this lane's channel exists (d < D); other lanes aim their y stores
@@ -233,7 +246,7 @@ struct Segment {
         Cbase = static_cast<const char*>(a.Cm) + (row0 * a.N + n0) * es;
         rw = BF16 ? a.N / 2 : a.N;
 #pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) {
+        for (int k = 0; k < kP; ++k) {
             const uint32_t so = (uint32_t)min(k, len - 1) * rstride;
             dq[k] = load_raw<BF16>(rd, voff, so);
             xq[k] = load_raw<BF16>(rx, voff, so);
@@ -280,14 +293,14 @@ struct Segment {
         }
     }
 
-    // one time step t from ring slot k; RELOAD: refill the slot with step t + kPrefetch
+    // one time step t from ring slot k; RELOAD: refill the slot with step t + kP
     template <bool RELOAD>
     __device__ __forceinline__ void step(int t, int k, const float (&A2)[N], float (&h)[N], float Dv,
                                          float& sumd, const VarLane<N, V>& vl) {
         const float dv = var_delta<N, V>(widen<BF16>(dq[k]), vl), xv = widen<BF16>(xq[k]);
         const float zv = kZ ? widen<BF16>(zq[k]) : 0.0f;
         if constexpr (RELOAD) {
-            const uint32_t so = (uint32_t)min(t + kPrefetch, len - 1) * rstride;
+            const uint32_t so = (uint32_t)min(t + kP, len - 1) * rstride;
             dq[k] = load_raw<BF16>(rd, voff, so);
             xq[k] = load_raw<BF16>(rx, voff, so);
             if constexpr (kZ) zq[k] = load_raw<BF16>(rz, voff, so);
@@ -354,17 +367,17 @@ struct Segment {
         }
     }
 
-    // the whole segment from state h: full blocks of kPrefetch steps with a
+    // the whole segment from state h: full blocks of kP steps with a
     // static ring slot per step, then the tail straight from the ring.
     __device__ __forceinline__ void run(const float (&A2)[N], float (&h)[N], float Dv, float& sumd,
                                         const VarLane<N, V>& vl) {
         int t = 0;
-        for (; t + kPrefetch <= len; t += kPrefetch) {
+        for (; t + kP <= len; t += kP) {
 #pragma unroll
-            for (int k = 0; k < kPrefetch; ++k) step<true>(t + k, k, A2, h, Dv, sumd, vl);
+            for (int k = 0; k < kP; ++k) step<true>(t + k, k, A2, h, Dv, sumd, vl);
         }
 #pragma unroll
-        for (int k = 0; k < kPrefetch - 1; ++k)
+        for (int k = 0; k < kP - 1; ++k)
             if (t + k < len) step<false>(t + k, k, A2, h, Dv, sumd, vl);
     }
 };

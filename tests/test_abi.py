@@ -190,7 +190,7 @@ def _noalloc(B=1, L=8, D=64, N=16, io=1, x=P, delta=P, A=P, Bm=P, Cm=P, Dk=None,
     (dict(B=0), 1), (dict(L=-1), 1), (dict(io=5), 1), (dict(N=12), 2), (dict(x=None), 1),
     (dict(y=ctypes.c_void_p(0x10008)), 1),
     # fits ssm_scan_fwd with a workspace, but not the fixed scratch
-    (dict(L=4096, D=1536, N=64), 2), (dict(B=2, L=8192, D=4096, N=32), 2),
+    (dict(L=4096, D=1536, N=256), 2), (dict(B=2, L=8192, D=4096, N=32), 2),
 ])
 def test_scan_fwd_noalloc_rejects_before_any_hip_call(kw, status):
     assert _noalloc(**kw) == status
@@ -199,10 +199,10 @@ def test_scan_fwd_noalloc_rejects_before_any_hip_call(kw, status):
 
 def test_noalloc_scratch_limit_is_the_declared_one():
     src = open(HEADER).read()
-    assert "#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in src
-    limit = 32 << 20
+    assert "#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in src
+    limit = 128 << 20
     assert ssa.ssm_scan_workspace_size(8, 32768, 512, 16) <= limit      # the long-sequence workload fits
-    assert ssa.ssm_scan_workspace_size(1, 4096, 1536, 64) > limit
+    assert ssa.ssm_scan_workspace_size(1, 4096, 1536, 256) > limit
 
 
 def test_python_binding_has_every_entry_point_by_name():

@@ -45,8 +45,8 @@ def test_noalloc_two_calls_match_workspace_entry_and_oracle():
 
 def test_noalloc_rejects_a_shape_beyond_the_scratch():
     x = torch.empty((1, 4096, 1536), dtype=torch.bfloat16, device=DEV)
-    A = torch.empty((1536, 64), dtype=torch.float32, device=DEV)
-    Bm = torch.empty((1, 4096, 64), dtype=torch.bfloat16, device=DEV)
+    A = torch.empty((1536, 256), dtype=torch.float32, device=DEV)
+    Bm = torch.empty((1, 4096, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ssa.SsmError) as e:
         ssa.ssm_scan_fwd_noalloc(x, x, A, Bm, Bm, y=torch.empty_like(x))
     assert e.value.status == 2
