@@ -180,8 +180,8 @@ int ssm_scan_fwd_noalloc(int B, int L, int D, int N, ssm_dtype_t io,
  *   delta_softplus nonzero: Delta = softplus(delta + delta_bias) = log(1 + e^(.)).
  * Every other argument, the workspace (ssm_scan_workspace_size) and the errors
  * are those of ssm_scan_fwd; with SSM_DISC_EULER, no bias and no softplus it is
- * ssm_scan_fwd. The options need N in {4, 8, 16, 32} (SSM_ERR_UNSUPPORTED
- * otherwise). delta_bias must be 16-byte aligned.
+ * ssm_scan_fwd. Every N of ssm_scan_fwd is supported (N >= 64 runs as chunks of
+ * 16 states, as there). delta_bias must be 16-byte aligned.
  * ------------------------------------------------------------------------- */
 int ssm_scan_fwd_ex(int B, int L, int D, int N, ssm_dtype_t io, ssm_disc_t disc,
                     const float* delta_bias, int delta_softplus,

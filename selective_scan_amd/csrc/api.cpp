@@ -114,7 +114,7 @@ int scan_fwd_impl(const char* fn, int B, int L, int D, int N, int io, int disc, 
     const bool variant = disc != SSM_DISC_EULER || delta_bias != nullptr || delta_softplus != 0;
     if (!ssm::scan_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128, 256");
     if (variant && !ssm::scan_var_supported_n(N))
-        return fail(SSM_ERR_UNSUPPORTED, fn, "zero-order hold and Delta preprocessing need N in {4, 8, 16, 32}");
+        return fail(SSM_ERR_UNSUPPORTED, fn, "zero-order hold and Delta preprocessing: unsupported N");
     if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
     if (!product_ok({B, L, D, N}) || !product_ok({B, L, D}, 1LL << 40))
         return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");

@@ -209,7 +209,7 @@ __device__ __forceinline__ float var_delta(float dv, const VarLane<N, V>& vl) {
 // start them before other prologue work; run() then walks the segment.
 template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool FINAL, int V = 0, bool SINK = false>
 struct Segment {
-    static_assert(!SINK || (FINAL && V == 0), "the LDS sink holds plain partial sums");
+    static_assert(!SINK || FINAL, "the LDS sink holds the final pass's partial sums");
     static constexpr uint32_t es = BF16 ? 2 : 4;
     // ring depth; the LDS sink's slot layout is sized with kPrefetch
     static constexpr int kP = FINAL && !SINK ? kPrefetchFinal : kPrefetch;
@@ -359,9 +359,13 @@ struct Segment {
         }
         if constexpr (FINAL) {
             float v = y0 + y1;
-            if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
-            if constexpr (HAS_Z) v *= silu(zv);
-            store_io<BF16>(ry, yoff, (uint32_t)t * ystride, v);
+            if constexpr (SINK) {
+                lsink[k * 64 + (threadIdx.x & 63)] = v;
+            } else {
+                if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv, v);
+                if constexpr (HAS_Z) v *= silu(zv);
+                store_io<BF16>(ry, yoff, (uint32_t)t * ystride, v);
+            }
         } else {
             sumd += dv;
         }
@@ -586,7 +590,7 @@ segment_final(ScanArgs a, Geom g) {
 constexpr int kSinkChunks = 8;
 inline int sink_planes(int N) { return std::max(1, n_chunks(N) / kSinkChunks); }
 
-template <bool BF16>
+template <bool BF16, int V = 0>
 __global__ void __launch_bounds__(64 * kSinkChunks)
 segment_final_sink(ScanArgs a, Geom g) {
     extern __shared__ float lds[];
@@ -608,7 +612,7 @@ segment_final_sink(ScanArgs a, Geom g) {
     const float* ws = static_cast<const float*>(a.ws);
     float* yp = static_cast<float*>(a.ws) + wl.YP + (size_t)cg * a.B * a.L * D;
 
-    Segment<N, BF16, false, false, true, 0, true> seg(a, b, dc, t0, len, n0, d < D);
+    Segment<N, BF16, false, false, true, V, true> seg(a, b, dc, t0, len, n0, d < D);
     float A2[N], hg[N], E[N];
     float cs = 0.0f;
 #pragma unroll
@@ -638,8 +642,8 @@ segment_final_sink(ScanArgs a, Geom g) {
 #pragma unroll
     for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hg[n], E[n]);
     float unused = 0.0f;
-    VarLane<N, 0> vl;
-    var_lane_init<N, 0>(vl, a, dc, n0);
+    VarLane<N, V> vl;
+    var_lane_init<N, V>(vl, a, dc, n0);
     // the sums of the steps [tb, tb + cnt) from LDS slot `slot`, in chunk order
     auto reduce = [&](int slot, int tb, int cnt) {
         const float* base = lds + (size_t)slot * nch * kPrefetch * 64;
@@ -709,8 +713,29 @@ combine_partials(ScanArgs a, const float* __restrict__ yp, int nch) {
     else static_cast<float*>(a.y)[i] = v;
 }
 
-// N: states per lane (a.N itself when a.N <= 64, else the chunk of 64).
-template <int N, bool BF16>
+// N >= 64, after the aggregate and carry passes: the state chunks' final pass
+// into the planes of partial sums, then their sum with D x and the gate.
+template <bool BF16, int V>
+void launch_sink(const ScanArgs& a, const Geom& g, hipStream_t st) {
+    const int nch = a.N / kChunkN;
+    const int planes = sink_planes(a.N), cpw = nch / planes;
+    const dim3 sgrid((unsigned)g.S, (unsigned)(((a.D + 63) / 64) * planes), (unsigned)a.B);
+    const size_t lds_sink = (size_t)2 * cpw * kPrefetch * 64 * sizeof(float);
+    launch((segment_final_sink<BF16, V>), sgrid, dim3(64 * cpw), (uint32_t)lds_sink, st, a, g);
+    const float* yp = static_cast<const float*>(a.ws) + ws_layout(a.B, a.D, a.N, g.S, g.G).YP;
+    const size_t tot = (size_t)a.B * a.L * a.D;
+    const dim3 cg((unsigned)((tot + 255) / 256));
+    const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
+    if (hz && hd) launch((combine_partials<BF16, true, true>), cg, dim3(256), 0, st, a, yp, planes);
+    else if (hz) launch((combine_partials<BF16, true, false>), cg, dim3(256), 0, st, a, yp, planes);
+    else if (hd) launch((combine_partials<BF16, false, true>), cg, dim3(256), 0, st, a, yp, planes);
+    else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, planes);
+}
+
+// N: states per lane (a.N itself when a.N <= 32, else the chunk of kChunkN).
+// V: the discretisation (0 plain; 1, 2 the variants, which run the final pass
+// with HAS_D and D = 0 when the skip is absent: exact, y + 0 x = y).
+template <int N, bool BF16, int V = 0>
 hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     const Geom g = geom(a.B, a.L, a.D, a.N);
     if (a.L == 0) {
@@ -724,55 +749,25 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     const dim3 grid(g.G, ((a.D + 63) / 64) * nch, a.B);
     const dim3 block(64 * g.W);
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
-    if (g.S > 1) launch((segment_aggregate<N, BF16>), grid, block, lds_agg, st, a, g);
-    if (g.G > 1) {
-        launch(group_carry, dim3((unsigned)((a.D + 63) / 64), (unsigned)a.N, (unsigned)a.B), dim3(256), 0, st,
-               a.h0, static_cast<float*>(a.ws), a.B, a.D, a.N, g);
-    }
-    const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
-    if (nch > 1) {
-        const int planes = sink_planes(a.N), cpw = nch / planes;
-        const dim3 sgrid((unsigned)g.S, (unsigned)(((a.D + 63) / 64) * planes), (unsigned)a.B);
-        const size_t lds_sink = (size_t)2 * cpw * kPrefetch * 64 * sizeof(float);
-        launch((segment_final_sink<BF16>), sgrid, dim3(64 * cpw), (uint32_t)lds_sink, st, a, g);
-        const float* yp = static_cast<const float*>(a.ws) + ws_layout(a.B, a.D, a.N, g.S, g.G).YP;
-        const size_t tot = (size_t)a.B * a.L * a.D;
-        const dim3 cg((unsigned)((tot + 255) / 256));
-        if (hz && hd) launch((combine_partials<BF16, true, true>), cg, dim3(256), 0, st, a, yp, planes);
-        else if (hz) launch((combine_partials<BF16, true, false>), cg, dim3(256), 0, st, a, yp, planes);
-        else if (hd) launch((combine_partials<BF16, false, true>), cg, dim3(256), 0, st, a, yp, planes);
-        else launch((combine_partials<BF16, false, false>), cg, dim3(256), 0, st, a, yp, planes);
-        return hipGetLastError();
-    }
-    if (hz && hd) launch((segment_final<N, BF16, true, true>), grid, block, 0, st, a, g);
-    else if (hz) launch((segment_final<N, BF16, true, false>), grid, block, 0, st, a, g);
-    else if (hd) launch((segment_final<N, BF16, false, true>), grid, block, 0, st, a, g);
-    else launch((segment_final<N, BF16, false, false>), grid, block, 0, st, a, g);
-    return hipGetLastError();
-}
-
-// Discretisation variants (V = 1, 2) for N <= 32; the skip term goes through the
-// HAS_D path with D = 0 when absent (exact: y + 0 x = y).
-template <int N, bool BF16, int V>
-hipError_t launch_var(const ScanArgs& a, hipStream_t st) {
-    const Geom g = geom(a.B, a.L, a.D, a.N);
-    if (a.L == 0) {
-        if (a.h_final) {
-            const size_t n = (size_t)a.B * a.D * a.N;
-            launch(copy_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.h0, a.h_final, n);
-        }
-        return hipGetLastError();
-    }
-    const dim3 grid(g.G, (a.D + 63) / 64, a.B);
-    const dim3 block(64 * g.W);
-    const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     if (g.S > 1) launch((segment_aggregate<N, BF16, V>), grid, block, lds_agg, st, a, g);
     if (g.G > 1) {
         launch(group_carry, dim3((unsigned)((a.D + 63) / 64), (unsigned)a.N, (unsigned)a.B), dim3(256), 0, st,
                a.h0, static_cast<float*>(a.ws), a.B, a.D, a.N, g);
     }
-    if (a.z != nullptr) launch((segment_final<N, BF16, true, true, V>), grid, block, 0, st, a, g);
-    else launch((segment_final<N, BF16, false, true, V>), grid, block, 0, st, a, g);
+    if (nch > 1) {
+        launch_sink<BF16, V>(a, g, st);
+        return hipGetLastError();
+    }
+    const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
+    if constexpr (V != 0) {
+        if (hz) launch((segment_final<N, BF16, true, true, V>), grid, block, 0, st, a, g);
+        else launch((segment_final<N, BF16, false, true, V>), grid, block, 0, st, a, g);
+    } else {
+        if (hz && hd) launch((segment_final<N, BF16, true, true>), grid, block, 0, st, a, g);
+        else if (hz) launch((segment_final<N, BF16, true, false>), grid, block, 0, st, a, g);
+        else if (hd) launch((segment_final<N, BF16, false, true>), grid, block, 0, st, a, g);
+        else launch((segment_final<N, BF16, false, false>), grid, block, 0, st, a, g);
+    }
     return hipGetLastError();
 }
 

@@ -7,16 +7,21 @@
 
 namespace ssm {
 
-bool scan_var_supported_n(int N) { return N == 4 || N == 8 || N == 16 || N == 32; }
+bool scan_var_supported_n(int N) {
+    return N == 4 || N == 8 || N == 16 || N == 32 || N == 64 || N == 128 || N == 256;
+}
 
 namespace {
 template <bool BF16, int V>
 hipError_t var_n(const ScanArgs& a, hipStream_t st) {
     switch (a.N) {
-        case 4: return launch_var<4, BF16, V>(a, st);
-        case 8: return launch_var<8, BF16, V>(a, st);
-        case 16: return launch_var<16, BF16, V>(a, st);
-        case 32: return launch_var<32, BF16, V>(a, st);
+        case 4: return launch_n<4, BF16, V>(a, st);
+        case 8: return launch_n<8, BF16, V>(a, st);
+        case 16: return launch_n<16, BF16, V>(a, st);
+        case 32: return launch_n<32, BF16, V>(a, st);
+        case 64:
+        case 128:
+        case 256: return launch_n<kChunkN, BF16, V>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -163,7 +163,9 @@ def _scan_ex(disc=1, bias=None, sp=1, N=16, **kw):
 
 # one defect per case, so no call reaches a launch
 @pytest.mark.parametrize("kw,status", [
-    (dict(disc=2), 1), (dict(disc=-1), 1), (dict(N=64), 2), (dict(N=256, disc=0, sp=1), 2),
+    (dict(disc=2), 1), (dict(disc=-1), 1), (dict(N=12), 2),
+    # N >= 64 is supported and needs a workspace, which these calls lack
+    (dict(N=64), 3), (dict(N=256, disc=0, sp=1), 3),
     (dict(bias=ctypes.c_void_p(0x10004)), 1), (dict(x=None), 1), (dict(B=0), 1),
 ])
 def test_scan_fwd_ex_rejects_bad_arguments(kw, status):

@@ -56,6 +56,11 @@ CASES = [
     (2, 513, 200, 16, si.BF16, "euler", True, False, True, True, True),
     (1, 4097, 96, 16, si.BF16, "zoh", True, True, False, True, False),
     (5, 77, 1, 16, si.F32, "zoh", True, True, True, True, True),
+    # N >= 64: chunks of 16 states, partial sums added across the chunks
+    (2, 300, 70, 64, si.BF16, "zoh", True, True, True, True, True),
+    (1, 1000, 96, 128, si.F32, "euler", True, True, False, True, False),
+    (1, 257, 64, 256, si.BF16, "zoh", True, True, True, False, True),
+    (3, 129, 130, 64, si.F32, "euler", True, False, False, False, True),
 ]
 
 
@@ -69,18 +74,20 @@ def test_scan_variant_small_shapes(case):
     compare(out_f64(hf), hr, "f32", what=f"{case} h_final")
 
 
+@pytest.mark.parametrize("N", [16, 64])
 @pytest.mark.parametrize("scale", [1e-3, 0.05])
-def test_scan_zoh_small_z_and_zero_A(scale):
+def test_scan_zoh_small_z_and_zero_A(scale, N):
     """Tiny Delta (every |z| below the switch: the blended series path) and mixed
     scales, with A holding exact zeros and a positive entry."""
-    B, L, D, N = 2, 700, 96, 16
+    B, L, D = 2, 700, 96
     A = -np.tile(np.arange(1, N + 1, dtype=np.float64), (D, 1))
     A[:, 0] = 0.0
     A[::7, 5] = 0.25
+    A[::5, N - 3] = 0.0
     w, _ = _inputs(B, L, D, N, si.F32, 12, False, True, True, True, A=A, delta_scale=scale)
     (y, hf), (yr, hr) = _run(w, None, "zoh", False)
-    compare(out_f64(y), yr, "f32", what=f"zoh scale {scale} y")
-    compare(out_f64(hf), hr, "f32", what=f"zoh scale {scale} h_final")
+    compare(out_f64(y), yr, "f32", what=f"zoh scale {scale} N{N} y")
+    compare(out_f64(hf), hr, "f32", what=f"zoh scale {scale} N{N} h_final")
 
 
 def test_scan_zoh_softplus_headline_layer():
@@ -91,6 +98,18 @@ def test_scan_zoh_softplus_headline_layer():
     (y, hf), (yr, hr) = _run(w, bias, "zoh", True)
     compare(out_f64(y), yr, "bf16", what="headline zoh y")
     compare(out_f64(hf), hr, "f32", what="headline zoh h_final")
+
+
+@pytest.mark.parametrize("N", [64, 128, 256])
+def test_scan_zoh_softplus_state_dim_sweep(N):
+    """The state-dimension sweep shape B=1, L=4096, D=1536, N = 64 / 128 / 256, bf16,
+    with Delta through the fused softplus(delta + bias) and exact zero-order hold;
+    every output."""
+    print(f"[scan_var] zoh softplus B1 L4096 D1536 N{N}", flush=True)
+    w, bias = _inputs(1, 4096, 1536, N, si.BF16, 1, True, True, True, False)
+    (y, hf), (yr, hr) = _run(w, bias, "zoh", True)
+    compare(out_f64(y), yr, "bf16", what=f"sweep N{N} zoh y")
+    compare(out_f64(hf), hr, "f32", what=f"sweep N{N} zoh h_final")
 
 
 @pytest.mark.parametrize("disc", ["euler", "zoh"])
