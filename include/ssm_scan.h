@@ -258,9 +258,10 @@ int ssm_scan3_fwd(int B, int L, int D, int N, ssm_dtype_t io,
  * The forward states are recomputed, not read from a forward call. Outputs must
  * not alias inputs or each other. Arithmetic is fp32 with fp32 accumulation;
  * reductions run in a fixed order (no atomics), so results are deterministic.
- * Supported: N in {4, 8, 16}; B <= 65535; L >= 0 (L = 0 writes dh0 = dh_final,
- * dA = 0, dDskip = 0). Every pointer must be 16-byte aligned. Errors as for
- * ssm_scan_fwd.
+ * Supported: N in {4, 8, 16, 32, 64, 128, 256} (N >= 32 runs as chunks of 16
+ * states whose partial sums over n are added in chunk order); B <= 65535; L >= 0
+ * (L = 0 writes dh0 = dh_final, dA = 0, dDskip = 0). Every pointer must be
+ * 16-byte aligned. Errors as for ssm_scan_fwd.
  * ------------------------------------------------------------------------- */
 size_t ssm_scan_bwd_workspace_size(int B, int L, int D, int N);
 

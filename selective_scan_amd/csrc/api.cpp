@@ -276,7 +276,7 @@ int ssm_scan_bwd(int B, int L, int D, int N, ssm_dtype_t io,
     const char* fn = "ssm_scan_bwd";
     if (B < 1 || D < 1 || L < 0 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1 and L >= 0");
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
-    if (!ssm::scan_bwd_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16");
+    if (!ssm::scan_bwd_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128, 256");
     if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
     if (!product_ok({B, L, D, N}, 1LL << 40) || !product_ok({B, L, D}, 1LL << 40))
         return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");

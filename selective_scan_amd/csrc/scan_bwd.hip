@@ -56,6 +56,12 @@ constexpr int kBwdTargetWaves = SSM_BWD_TARGET_WAVES;  // waves the final pass a
 constexpr int kBwdMinSegment = SSM_BWD_MIN_SEGMENT;
 constexpr int kBwdMaxGroup = 4;
 constexpr float kLn2 = 0.69314718055994531f;
+// N > 16 runs as N / 16 independent chunks of 16 states per lane (both
+// recurrences are diagonal in n). The per-(t, channel) sums over n that dx,
+// ddelta and dz need are then split: each chunk writes its partial sums to a
+// plane of its own and bwd_combine adds the planes in chunk order.
+constexpr int kBwdChunkN = 16;
+__host__ __device__ inline int bwd_chunks(int N) { return N > kBwdChunkN ? N / kBwdChunkN : 1; }
 
 // Steps between checkpoints (K), and steps whose states the final pass keeps in
 // VGPRs at a time (KR): a K-step block runs as K/KR halves, the later half first,
@@ -76,7 +82,7 @@ struct BGeom {
 BGeom bgeom(int B, int L, int D, int N) {
     BGeom g{0, 0, 1, 0, sub_len(N), 0};
     if (L <= 0) return g;
-    const long chains = (long)B * ((D + 63) / 64);
+    const long chains = (long)B * ((D + 63) / 64) * bwd_chunks(N);
     const long s_target = (kBwdTargetWaves + chains - 1) / chains;
     long Ls = std::max<long>(kBwdMinSegment, (L + s_target - 1) / s_target);
     Ls = (Ls + g.K - 1) / g.K * g.K;
@@ -104,8 +110,12 @@ BGeom bgeom(int B, int L, int D, int N) {
 //   PD  [B][G][D]      dD summed over one group's segments
 //   PB  [ceil(D/64)][B][L][N]  dB summed over one 64-channel block
 //   PC  [ceil(D/64)][B][L][N]  dC summed over one 64-channel block
+//   QS  [N/16][B][L][D] (N > 16) sum over the chunk's states of g_t B_t
+//   QD  [N/16][B][L][D] (N > 16) the chunk's part of ddelta
+//   QV  [N/16][B][L][D] (N > 16) the chunk's part of C_t . h_t
+// (state index n is global: a chunk's states are n0 .. n0 + 15 of N)
 struct BwsLayout {
-    size_t E, CS, GH, GP, EB, CSB, GHB, GPB, HZ, CZ, PA, PD, PB, PC, total;
+    size_t E, CS, GH, GP, EB, CSB, GHB, GPB, HZ, CZ, PA, PD, PB, PC, QS, QD, QV, total;
 };
 
 __host__ __device__ inline BwsLayout bws_layout(int B, int L, int D, int N, const BGeom& g) {
@@ -129,6 +139,10 @@ __host__ __device__ inline BwsLayout bws_layout(int B, int L, int D, int N, cons
     w.PD = o;  o += (size_t)B * g.G * D;
     w.PB = o;  o += nd * B * L * N;
     w.PC = o;  o += nd * B * L * N;
+    const size_t nq = bwd_chunks(N) > 1 ? (size_t)bwd_chunks(N) * B * L * D : 0;
+    w.QS = o;  o += nq;
+    w.QD = o;  o += nq;
+    w.QV = o;  o += nq;
     w.total = o;
     return w;
 }
@@ -257,22 +271,25 @@ bwd_aggregate(BwdArgs a, BGeom g) {
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
     constexpr uint32_t es = BF16 ? 2 : 4;
-    constexpr int rw = BF16 ? N / 2 : N;
+    // N states per lane: n0 .. n0 + N - 1 of the NT in a row
+    const int NT = a.N, nch = NT / N;
+    const int rw = BF16 ? NT / 2 : NT;
     const int W = g.W;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
-    const int d = blockIdx.y * 64 + lane, dc = d < D ? d : D - 1;
+    const int cidx = blockIdx.y % nch, n0 = cidx * N;
+    const int d = (blockIdx.y / nch) * 64 + lane, dc = d < D ? d : D - 1;
     const int s = grp * W + wave;
     const int t0 = s * g.Ls;
     const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
-    const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
+    const BwsLayout wl = bws_layout(a.B, a.L, D, NT, g);
     float* ws = static_cast<float*>(a.ws);
     const size_t c1 = g.nsub > 1 ? (size_t)(g.nsub - 1) : 0;
 
     float A2[N], h[N], pr[N], ga[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+        A2[n] = a.A[(size_t)dc * NT + n0 + n] * kLog2e;
         h[n] = 0.0f;
         pr[n] = 1.0f;
         ga[n] = 0.0f;
@@ -286,8 +303,8 @@ bwd_aggregate(BwdArgs a, BGeom g) {
         DY.init(a.dy, row0, len, D);
         Z.init(HAS_Z ? a.z : a.dy, row0, len, D);
         const uint32_t voff = (uint32_t)dc * es, rstride = (uint32_t)D * es;
-        const void* Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
-        const void* Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
+        const void* Bbase = static_cast<const char*>(a.Bm) + (row0 * NT + n0) * es;
+        const void* Cbase = static_cast<const char*>(a.Cm) + (row0 * NT + n0) * es;
         const int nsub = (len + K - 1) / K;
         uint32_t dq[K], xq[K], gq[K], zq[K];
 #pragma unroll
@@ -337,10 +354,10 @@ bwd_aggregate(BwdArgs a, BGeom g) {
                 }
             }
             if (j + 1 < nsub && d < D) {
-                float* hz = ws + wl.HZ + (((size_t)b * g.S + s) * c1 + j) * N * D + d;
+                float* hz = ws + wl.HZ + ((((size_t)b * g.S + s) * c1 + j) * NT + n0) * D + d;
 #pragma unroll
                 for (int n = 0; n < N; ++n) hz[(size_t)n * D] = h[n];
-                ws[wl.CZ + (((size_t)b * g.S + s) * c1 + j) * D + d] = sumd;
+                if (cidx == 0) ws[wl.CZ + (((size_t)b * g.S + s) * c1 + j) * D + d] = sumd;
             }
         }
     }
@@ -370,13 +387,13 @@ bwd_aggregate(BwdArgs a, BGeom g) {
     const bool live = d < D && s < g.S;
     const bool last_in_group = (wave == W - 1) || (s == g.S - 1);
     if (live) {
-        float* Ep = ws + wl.E + ((size_t)b * g.S + s) * N * D + d;
+        float* Ep = ws + wl.E + (((size_t)b * g.S + s) * NT + n0) * D + d;
 #pragma unroll
         for (int n = 0; n < N; ++n) Ep[(size_t)n * D] = E[n];
-        ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
+        if (cidx == 0) ws[wl.CS + ((size_t)b * g.S + s) * D + d] = cs;
         if (last_in_group && grp < g.G - 1) {
-            float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + grp) * N * D + d;
-            float* GP = ws + wl.GP + ((size_t)b * (g.G - 1) + grp) * N * D + d;
+            float* GH = ws + wl.GH + (((size_t)b * (g.G - 1) + grp) * NT + n0) * D + d;
+            float* GP = ws + wl.GP + (((size_t)b * (g.G - 1) + grp) * NT + n0) * D + d;
 #pragma unroll
             for (int n = 0; n < N; ++n) {
                 GH[(size_t)n * D] = __builtin_fmaf(sP[(wave * N + n) * 64 + lane], E[n], h[n]);
@@ -400,13 +417,13 @@ bwd_aggregate(BwdArgs a, BGeom g) {
         csb += sS[jw * 64 + lane];
     }
     if (!live) return;
-    float* Ebp = ws + wl.EB + ((size_t)b * g.S + s) * N * D + d;
+    float* Ebp = ws + wl.EB + (((size_t)b * g.S + s) * NT + n0) * D + d;
 #pragma unroll
     for (int n = 0; n < N; ++n) Ebp[(size_t)n * D] = Eb[n];
-    ws[wl.CSB + ((size_t)b * g.S + s) * D + d] = csb;
+    if (cidx == 0) ws[wl.CSB + ((size_t)b * g.S + s) * D + d] = csb;
     if (wave == 0 && grp > 0) {  // the group's own aggregate, passed to the groups on its left
-        float* GH = ws + wl.GHB + ((size_t)b * (g.G - 1) + grp - 1) * N * D + d;
-        float* GP = ws + wl.GPB + ((size_t)b * (g.G - 1) + grp - 1) * N * D + d;
+        float* GH = ws + wl.GHB + (((size_t)b * (g.G - 1) + grp - 1) * NT + n0) * D + d;
+        float* GP = ws + wl.GPB + (((size_t)b * (g.G - 1) + grp - 1) * NT + n0) * D + d;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             GH[(size_t)n * D] = __builtin_fmaf(sP[n * 64 + lane], Eb[n], ga[n]);
@@ -485,29 +502,33 @@ bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ 
 // At least three waves per SIMD: with every option on (z, D) the compiler's own
 // allocation at N = 16 takes 183 VGPRs (two waves); capped at 168 it spills
 // three, and the third wave hides more latency than the spills cost.
-template <int N, bool BF16, bool HAS_Z, bool HAS_D>
+// CH: one chunk of N states out of a.N > N; dx, ddelta and dz then go out as
+// this chunk's partial sums (QS, QD, QV) for bwd_combine.
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH>
 __global__ void __launch_bounds__(64 * kBwdMaxGroup) __attribute__((amdgpu_waves_per_eu(3)))
 bwd_final(BwdArgs a, BGeom g) {
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
     constexpr uint32_t es = BF16 ? 2 : 4;
-    constexpr int rw = BF16 ? N / 2 : N;
+    const int NT = a.N, nch = CH ? NT / N : 1;
+    const int rw = BF16 ? NT / 2 : NT;
     const int W = g.W;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
-    const int dblk = blockIdx.y;
+    const int cidx = blockIdx.y % nch, n0 = cidx * N;
+    const int dblk = blockIdx.y / nch;
     const int d = dblk * 64 + lane, dc = d < D ? d : D - 1;
     const int s = grp * W + wave;
     const int t0 = s * g.Ls;
     const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
-    const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
+    const BwsLayout wl = bws_layout(a.B, a.L, D, NT, g);
     const float* ws = static_cast<const float*>(a.ws);
     const size_t c1 = g.nsub > 1 ? (size_t)(g.nsub - 1) : 0;
 
     float A2[N], dA[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+        A2[n] = a.A[(size_t)dc * NT + n0 + n] * kLog2e;
         dA[n] = 0.0f;
     }
     float dD = 0.0f;
@@ -519,11 +540,11 @@ bwd_final(BwdArgs a, BGeom g) {
             float hg[N], E[N];
             float cs = 0.0f;
             if (grp > 0) {
-                const float* p = ws + wl.GH + ((size_t)b * (g.G - 1) + grp - 1) * N * D + dc;
+                const float* p = ws + wl.GH + (((size_t)b * (g.G - 1) + grp - 1) * NT + n0) * D + dc;
 #pragma unroll
                 for (int n = 0; n < N; ++n) hg[n] = p[(size_t)n * D];
             } else if (a.h0 != nullptr) {
-                const float* p = a.h0 + ((size_t)b * D + dc) * N;
+                const float* p = a.h0 + ((size_t)b * D + dc) * NT + n0;
 #pragma unroll
                 for (int n = 0; n < N; ++n) hg[n] = p[n];
             } else {
@@ -532,7 +553,7 @@ bwd_final(BwdArgs a, BGeom g) {
             }
             if (g.S > 1) {
                 cs = ws[wl.CS + ((size_t)b * g.S + s) * D + dc];
-                const float* p = ws + wl.E + ((size_t)b * g.S + s) * N * D + dc;
+                const float* p = ws + wl.E + (((size_t)b * g.S + s) * NT + n0) * D + dc;
 #pragma unroll
                 for (int n = 0; n < N; ++n) E[n] = p[(size_t)n * D];
             } else {
@@ -547,11 +568,11 @@ bwd_final(BwdArgs a, BGeom g) {
             float rg[N], Eb[N];
             float csb = 0.0f;
             if (grp < g.G - 1) {
-                const float* p = ws + wl.GHB + ((size_t)b * (g.G - 1) + grp) * N * D + dc;
+                const float* p = ws + wl.GHB + (((size_t)b * (g.G - 1) + grp) * NT + n0) * D + dc;
 #pragma unroll
                 for (int n = 0; n < N; ++n) rg[n] = p[(size_t)n * D];
             } else if (a.dh_final != nullptr) {
-                const float* p = a.dh_final + ((size_t)b * D + dc) * N;
+                const float* p = a.dh_final + ((size_t)b * D + dc) * NT + n0;
 #pragma unroll
                 for (int n = 0; n < N; ++n) rg[n] = p[n];
             } else {
@@ -560,7 +581,7 @@ bwd_final(BwdArgs a, BGeom g) {
             }
             if (g.S > 1) {
                 csb = ws[wl.CSB + ((size_t)b * g.S + s) * D + dc];
-                const float* p = ws + wl.EB + ((size_t)b * g.S + s) * N * D + dc;
+                const float* p = ws + wl.EB + (((size_t)b * g.S + s) * NT + n0) * D + dc;
 #pragma unroll
                 for (int n = 0; n < N; ++n) Eb[n] = p[(size_t)n * D];
             } else {
@@ -589,15 +610,23 @@ bwd_final(BwdArgs a, BGeom g) {
         DZ.init(HAS_Z ? a.dz : a.dx, row0, len, D);
         const uint32_t voff = (uint32_t)dc * es, rstride = (uint32_t)D * es;
         const uint32_t soff_st = d < D ? voff : 0x80000000u;  // lanes past D store nowhere
-        // per-block partial rows of dB and dC: [t0, t0 + len) x N floats
+        // per-block partial rows of dB and dC: [t0, t0 + len) x NT floats
         const size_t prow = ((size_t)dblk * a.B + b) * a.L + t0;
-        const __amdgpu_buffer_rsrc_t rPB = make_rsrc(static_cast<float*>(a.ws) + wl.PB + prow * N,
-                                                      (uint32_t)len * N * 4u);
-        const __amdgpu_buffer_rsrc_t rPC = make_rsrc(static_cast<float*>(a.ws) + wl.PC + prow * N,
-                                                      (uint32_t)len * N * 4u);
-        const uint32_t poff = reduced_owner<N>(lane) ? (uint32_t)reduced_index<N>(lane) * 4u : 0x80000000u;
-        const void* Bbase = static_cast<const char*>(a.Bm) + row0 * N * es;
-        const void* Cbase = static_cast<const char*>(a.Cm) + row0 * N * es;
+        const __amdgpu_buffer_rsrc_t rPB = make_rsrc(static_cast<float*>(a.ws) + wl.PB + prow * NT,
+                                                      (uint32_t)len * NT * 4u);
+        const __amdgpu_buffer_rsrc_t rPC = make_rsrc(static_cast<float*>(a.ws) + wl.PC + prow * NT,
+                                                      (uint32_t)len * NT * 4u);
+        const uint32_t poff =
+            reduced_owner<N>(lane) ? (uint32_t)(n0 + reduced_index<N>(lane)) * 4u : 0x80000000u;
+        // CH: this chunk's planes of partial sums over [t0, t0 + len) x D floats
+        const size_t qrow = ((size_t)cidx * a.B + b) * a.L + t0;
+        const uint32_t qbytes = CH ? (uint32_t)len * (uint32_t)D * 4u : 0u;
+        const __amdgpu_buffer_rsrc_t rQS = make_rsrc(static_cast<float*>(a.ws) + wl.QS + qrow * D, qbytes);
+        const __amdgpu_buffer_rsrc_t rQD = make_rsrc(static_cast<float*>(a.ws) + wl.QD + qrow * D, qbytes);
+        const __amdgpu_buffer_rsrc_t rQV = make_rsrc(static_cast<float*>(a.ws) + wl.QV + qrow * D, qbytes);
+        const uint32_t qoff = d < D ? (uint32_t)dc * 4u : 0x80000000u, qstride = (uint32_t)D * 4u;
+        const void* Bbase = static_cast<const char*>(a.Bm) + (row0 * NT + n0) * es;
+        const void* Cbase = static_cast<const char*>(a.Cm) + (row0 * NT + n0) * es;
         const int nsub = (len + K - 1) / K;
 
         uint32_t dq[K], xq[K], zq[K], gq[K];
@@ -630,7 +659,7 @@ bwd_final(BwdArgs a, BGeom g) {
                     for (int n = 0; n < N; ++n) he[n] = lhin[n * 64 + lane];
                 } else {
                     const size_t ck = ((size_t)b * g.S + s) * c1 + (j - 1);
-                    const float* hz = ws + wl.HZ + ck * N * D + dc;
+                    const float* hz = ws + wl.HZ + (ck * NT + n0) * D + dc;
                     const float cz = ws[wl.CZ + ck * D + dc];
 #pragma unroll
                     for (int n = 0; n < N; ++n)
@@ -694,22 +723,29 @@ bwd_final(BwdArgs a, BGeom g) {
                         else v0 = __builtin_fmaf(Ct.at(n), h[n], v0);
                     }
                     float v = v0 + v1;
-                    if constexpr (HAS_D) v = __builtin_fmaf(Dv, xv[k], v);
+                    if constexpr (HAS_D && !CH) v = __builtin_fmaf(Dv, xv[k], v);
                     if constexpr (HAS_Z) {
                         const float sg = rcp_fast(1.0f + exp2_fast(-zv[k] * kLog2e));
                         dv[kk] = dyv[k] * zv[k] * sg;
-                        const float dzv = dyv[k] * v * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
-                        store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, dzv);
+                        if constexpr (CH) {
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rQV, (int)qoff,
+                                                                  (int)((uint32_t)t * qstride), 0);
+                        } else {
+                            const float dzv = dyv[k] * v * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
+                            store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, dzv);
+                        }
                     } else {
                         dv[kk] = dyv[k];
                     }
-                    if constexpr (HAS_D) dD = __builtin_fmaf(dv[kk], xv[k], dD);
+                    if constexpr (HAS_D) {
+                        if (!CH || cidx == 0) dD = __builtin_fmaf(dv[kk], xv[k], dD);
+                    }
                     const float dvm = d < D ? dv[kk] : 0.0f;  // lanes past D add nothing
                     float w[16];
 #pragma unroll
                     for (int n = 0; n < N; ++n) w[n] = dvm * h[n];
                     const float tot = lane_reduce<N>(w, lane);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPC, (int)poff, (int)(t * N * 4), 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPC, (int)poff, (int)(t * NT * 4), 0);
                 }
                 // backward over the half
 #pragma unroll
@@ -737,17 +773,24 @@ bwd_final(BwdArgs a, BGeom g) {
                         w[n] = gg * um;
                         c[n] = exp2_fast(dl[k] * A2[n]) * gg;
                     }
-                    const float dxv = __builtin_fmaf(dl[k], sB, HAS_D ? dv[kk] * Dv : 0.0f);
                     const float ddv = __builtin_fmaf(sA, kLn2, xv[k] * sB);
-                    store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, dxv);
-                    store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, ddv);
+                    if constexpr (CH) {
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rQS, (int)qoff,
+                                                              (int)((uint32_t)t * qstride), 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ddv), rQD, (int)qoff,
+                                                              (int)((uint32_t)t * qstride), 0);
+                    } else {
+                        const float dxv = __builtin_fmaf(dl[k], sB, HAS_D ? dv[kk] * Dv : 0.0f);
+                        store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, dxv);
+                        store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, ddv);
+                    }
                     const float tot = lane_reduce<N>(w, lane);
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPB, (int)poff, (int)(t * N * 4), 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPB, (int)poff, (int)(t * NT * 4), 0);
                 }
             }
         }
         if (s == 0 && a.dh0 != nullptr && d < D) {
-            float* p = a.dh0 + ((size_t)b * D + d) * N;
+            float* p = a.dh0 + ((size_t)b * D + d) * NT + n0;
 #pragma unroll
             for (int n = 0; n < N; ++n) p[n] = c[n];
         }
@@ -760,14 +803,14 @@ bwd_final(BwdArgs a, BGeom g) {
     lD[wave * 64 + lane] = dD;
     __syncthreads();
     if (wave != 0 || d >= D) return;
-    float* PA = static_cast<float*>(a.ws) + wl.PA + ((size_t)b * g.G + grp) * N * D + d;
+    float* PA = static_cast<float*>(a.ws) + wl.PA + (((size_t)b * g.G + grp) * NT + n0) * D + d;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         float acc = 0.0f;
         for (int j = 0; j < W; ++j) acc += lA[(j * N + n) * 64 + lane];
         PA[(size_t)n * D] = acc;
     }
-    if constexpr (HAS_D) {
+    if (HAS_D && cidx == 0) {
         float acc = 0.0f;
         for (int j = 0; j < W; ++j) acc += lD[j * 64 + lane];
         static_cast<float*>(a.ws)[wl.PD + ((size_t)b * g.G + grp) * D + d] = acc;
@@ -850,6 +893,59 @@ bwd_reduce_rows(BwdArgs a, BGeom g) {
     }
 }
 
+// N > 16: dx, ddelta and dz from the chunks' partial sums, added in chunk order
+// (eight chunks' partials loaded before any is added). With v = sum_c QV + D x
+// the forward output before the gate and dv = dy silu(z):
+//   dx = Delta sum_c QS + dv D,  ddelta = sum_c QD,  dz = dy v silu'(z).
+template <bool BF16, bool HAS_Z, bool HAS_D>
+__global__ void __launch_bounds__(256)
+bwd_combine(BwdArgs a, BGeom g) {
+    const size_t tot = (size_t)a.B * a.L * a.D;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= tot) return;
+    const BwsLayout wl = bws_layout(a.B, a.L, a.D, a.N, g);
+    const float* ws = static_cast<const float*>(a.ws);
+    const int nch = bwd_chunks(a.N);
+    float sB = 0.0f, sD = 0.0f, sV = 0.0f;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+        float qb[8], qd[8], qv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const size_t o = (size_t)min(c0 + j, nch - 1) * tot + i;
+            qb[j] = ws[wl.QS + o];
+            qd[j] = ws[wl.QD + o];
+            qv[j] = HAS_Z ? ws[wl.QV + o] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (c0 + j < nch) {
+                sB += qb[j];
+                sD += qd[j];
+                if constexpr (HAS_Z) sV += qv[j];
+            }
+        }
+    }
+    auto rd = [&](const void* p) {
+        return BF16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+    };
+    auto wr = [&](void* p, float v) {
+        if constexpr (BF16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+        else static_cast<float*>(p)[i] = v;
+    };
+    const float dl = rd(a.delta), xv = rd(a.x), dy = rd(a.dy);
+    const float Dv = HAS_D ? a.Dskip[i % a.D] : 0.0f;
+    float dv = dy;
+    if constexpr (HAS_Z) {
+        const float zv = rd(a.z);
+        const float sg = rcp_fast(1.0f + exp2_fast(-zv * kLog2e));
+        dv = dy * zv * sg;
+        const float v = HAS_D ? __builtin_fmaf(Dv, xv, sV) : sV;
+        wr(a.dz, dy * v * sg * __builtin_fmaf(zv, 1.0f - sg, 1.0f));
+    }
+    wr(a.dx, __builtin_fmaf(dl, sB, HAS_D ? dv * Dv : 0.0f));
+    wr(a.ddelta, sD);
+}
+
 // L == 0: dh0 = dh_final, dA = 0, dD = 0.
 __global__ void __launch_bounds__(256)
 bwd_empty(BwdArgs a) {
@@ -860,12 +956,17 @@ bwd_empty(BwdArgs a) {
     if (a.dDskip != nullptr && i < (size_t)a.D) a.dDskip[i] = 0.0f;
 }
 
-template <int N, bool BF16, bool HAS_Z, bool HAS_D>
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH>
 void launch_final(const BwdArgs& a, const BGeom& g, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
-    launch((bwd_final<N, BF16, HAS_Z, HAS_D>), grid, block, (uint32_t)lds, st, a, g);
+    launch((bwd_final<N, BF16, HAS_Z, HAS_D, CH>), grid, block, (uint32_t)lds, st, a, g);
+    if constexpr (CH) {
+        const size_t tot = (size_t)a.B * a.L * a.D;
+        launch((bwd_combine<BF16, HAS_Z, HAS_D>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a, g);
+    }
 }
 
-template <int N, bool BF16>
+// N: states per lane (a.N itself, or the chunk of kBwdChunkN when CH).
+template <int N, bool BF16, bool CH = false>
 hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
     const BGeom g = bgeom(a.B, a.L, a.D, a.N);
     if (a.L == 0) {
@@ -873,27 +974,28 @@ hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
         launch(bwd_empty, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
         return hipGetLastError();
     }
-    const dim3 grid(g.G, (a.D + 63) / 64, a.B);
+    const int NT = a.N;
+    const dim3 grid(g.G, ((a.D + 63) / 64) * (NT / N), a.B);
     const dim3 block(64 * g.W);
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     const size_t lds_fin = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
     float* ws = static_cast<float*>(a.ws);
-    const BwsLayout wl = bws_layout(a.B, a.L, a.D, N, g);
+    const BwsLayout wl = bws_layout(a.B, a.L, a.D, NT, g);
     if (g.S > 1 || g.nsub > 1) {
         if (a.z) launch((bwd_aggregate<N, BF16, true>), grid, block, (uint32_t)lds_agg, st, a, g);
         else launch((bwd_aggregate<N, BF16, false>), grid, block, (uint32_t)lds_agg, st, a, g);
     }
-    const dim3 cg((unsigned)((a.D + 63) / 64), N, a.B);
-    if (g.G > 1) launch(bwd_carry<false>, cg, dim3(256), 0, st, a.h0, ws + wl.GH, ws + wl.GP, a.B, a.D, N, g.G);
+    const dim3 cg((unsigned)((a.D + 63) / 64), NT, a.B);
+    if (g.G > 1) launch(bwd_carry<false>, cg, dim3(256), 0, st, a.h0, ws + wl.GH, ws + wl.GP, a.B, a.D, NT, g.G);
     if (g.G > 1)
-        launch(bwd_carry<true>, cg, dim3(256), 0, st, a.dh_final, ws + wl.GHB, ws + wl.GPB, a.B, a.D, N, g.G);
+        launch(bwd_carry<true>, cg, dim3(256), 0, st, a.dh_final, ws + wl.GHB, ws + wl.GPB, a.B, a.D, NT, g.G);
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
-    if (hz && hd) launch_final<N, BF16, true, true>(a, g, grid, block, lds_fin, st);
-    else if (hz) launch_final<N, BF16, true, false>(a, g, grid, block, lds_fin, st);
-    else if (hd) launch_final<N, BF16, false, true>(a, g, grid, block, lds_fin, st);
-    else launch_final<N, BF16, false, false>(a, g, grid, block, lds_fin, st);
-    launch(bwd_reduce_params, dim3((unsigned)((a.D + 63) / 64), N + 1), dim3(256), 0, st, a, g);
-    const size_t rows = (size_t)a.B * a.L * N;
+    if (hz && hd) launch_final<N, BF16, true, true, CH>(a, g, grid, block, lds_fin, st);
+    else if (hz) launch_final<N, BF16, true, false, CH>(a, g, grid, block, lds_fin, st);
+    else if (hd) launch_final<N, BF16, false, true, CH>(a, g, grid, block, lds_fin, st);
+    else launch_final<N, BF16, false, false, CH>(a, g, grid, block, lds_fin, st);
+    launch(bwd_reduce_params, dim3((unsigned)((a.D + 63) / 64), NT + 1), dim3(256), 0, st, a, g);
+    const size_t rows = (size_t)a.B * a.L * NT;
     launch((bwd_reduce_rows<BF16>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a, g);
     return hipGetLastError();
 }
@@ -904,13 +1006,17 @@ hipError_t launch_dtype(const BwdArgs& a, hipStream_t st) {
         case 4: return launch_n<4, BF16>(a, st);
         case 8: return launch_n<8, BF16>(a, st);
         case 16: return launch_n<16, BF16>(a, st);
+        case 32:
+        case 64:
+        case 128:
+        case 256: return launch_n<kBwdChunkN, BF16, true>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-bool scan_bwd_supported_n(int N) { return N == 4 || N == 8 || N == 16; }
+bool scan_bwd_supported_n(int N) { return N == 4 || N == 8 || N == 16 || N == 32 || N == 64 || N == 128 || N == 256; }
 
 int scan_bwd_segment_len(int B, int L, int D, int N) { return bgeom(B, L, D, N).Ls; }
 

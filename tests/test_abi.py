@@ -137,7 +137,7 @@ def _bwd(B=1, L=64, D=64, N=16, io=1, Dk=None, z=None, dD=None, dz=None, ws=P, w
 # every case has exactly one defect, so no call reaches a launch
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 1), (dict(L=-1), 1), (dict(io=5), 1),
-    (dict(N=32), 2), (dict(N=12), 2), (dict(N=256), 2), (dict(B=70000), 2),
+    (dict(N=24), 2), (dict(N=12), 2), (dict(N=512), 2), (dict(B=70000), 2),
     (dict(dy=None), 1), (dict(dA=None), 1), (dict(A=None), 1), (dict(dCm=None), 1), (dict(ddelta=None), 1),
     (dict(Dk=P), 1), (dict(dD=P), 1), (dict(z=P), 1), (dict(dz=P), 1),
     (dict(dh0=ctypes.c_void_p(0x10004)), 1), (dict(dy=ctypes.c_void_p(0x10002)), 1),
@@ -151,7 +151,8 @@ def test_scan_bwd_rejects_bad_arguments(kw, status):
 def test_scan_bwd_workspace_size():
     assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 16) > 0
     assert ssa.ssm_scan_bwd_workspace_size(1, 0, 1536, 16) == 0
-    assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 32) == 0  # unsupported N
+    assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 32) > 0
+    assert ssa.ssm_scan_bwd_workspace_size(1, 4096, 1536, 12) == 0  # unsupported N
 
 
 def _scan_ex(disc=1, bias=None, sp=1, N=16, **kw):

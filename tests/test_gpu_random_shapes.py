@@ -25,7 +25,8 @@ SSD_CASES = _draw(12, 2024, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 
                                        int(r.choice([64, 128])), int(r.choice([32, 64, 96, 128, 160, 192, 224, 256])))
                   + _flags(r, 3))
 BWD_CASES = _draw(10, 2025, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 3000)), int(r.integers(1, 300)),
-                                       int(r.choice([4, 8, 16])), bool(r.integers(0, 2))) + _flags(r, 4))
+                                       int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)))
+                  + _flags(r, 4))
 VAR_CASES = _draw(8, 2026, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 2000)), int(r.integers(1, 200)),
                                       int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)),
                                       str(r.choice(["euler", "zoh"])), bool(r.integers(0, 2))))

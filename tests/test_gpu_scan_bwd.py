@@ -46,6 +46,12 @@ SMALL = [
     (5, 77, 1, 16, si.F32, True, True, True, True),
     (1, 6, 64, 8, si.BF16, True, True, True, True),
     (2, 999, 64, 4, si.BF16, True, True, True, True),
+    # N >= 32: chunks of 16 states, partial sums over n added across the chunks
+    (2, 300, 70, 32, si.BF16, True, True, True, True),
+    (1, 1000, 96, 64, si.F32, False, True, False, True),
+    (3, 257, 130, 128, si.BF16, True, False, True, False),
+    (1, 129, 64, 256, si.F32, True, True, True, True),
+    (2, 5, 33, 64, si.BF16, False, False, False, False),
 ]
 
 
@@ -73,6 +79,16 @@ def test_scan_bwd_headline_layer_all_outputs():
     w = si.scan_inputs(1, 4096, 1536, 16, dtype=si.BF16, seed=0)
     gw = si.scan_grad_inputs(1, 4096, 1536, 16, dtype=si.BF16, seed=0)
     _check(w, gw, what="B1 L4096 D1536")
+
+
+@pytest.mark.parametrize("N", [32, 64, 128, 256])
+def test_scan_bwd_state_dim_sweep_all_outputs(N):
+    """The state-dimension sweep shape (B=1, L=4096, D=1536, bf16) at N = 32, 64,
+    128, 256: every output in full."""
+    print(f"[scan_bwd] bf16 B1 L4096 D1536 N{N}", flush=True)
+    w = si.scan_inputs(1, 4096, 1536, N, dtype=si.BF16, seed=0)
+    gw = si.scan_grad_inputs(1, 4096, 1536, N, dtype=si.BF16, seed=0)
+    _check(w, gw, what=f"B1 L4096 D1536 N{N}")
 
 
 def test_scan_bwd_training_shape_all_outputs():
