@@ -265,14 +265,14 @@ struct SegCtx {
 //    product of the same decays, so no second pass over the segment is needed.
 // Then the group's waves form, in LDS, each segment's exclusive in-group prefix
 // (state) and suffix (adjoint), and the groups' own aggregates.
-template <int N, bool BF16, bool HAS_Z>
+// CH: one chunk of N states (n0 .. n0 + N - 1) out of a.N > N.
+template <int N, bool BF16, bool HAS_Z, bool CH>
 __global__ void __launch_bounds__(64 * kBwdMaxGroup)
 bwd_aggregate(BwdArgs a, BGeom g) {
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
     constexpr uint32_t es = BF16 ? 2 : 4;
-    // N states per lane: n0 .. n0 + N - 1 of the NT in a row
-    const int NT = a.N, nch = NT / N;
+    const int NT = CH ? a.N : N, nch = CH ? NT / N : 1;
     const int rw = BF16 ? NT / 2 : NT;
     const int W = g.W;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -510,7 +510,7 @@ bwd_final(BwdArgs a, BGeom g) {
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
     constexpr uint32_t es = BF16 ? 2 : 4;
-    const int NT = a.N, nch = CH ? NT / N : 1;
+    const int NT = CH ? a.N : N, nch = CH ? NT / N : 1;
     const int rw = BF16 ? NT / 2 : NT;
     const int W = g.W;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -982,8 +982,8 @@ hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
     float* ws = static_cast<float*>(a.ws);
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, NT, g);
     if (g.S > 1 || g.nsub > 1) {
-        if (a.z) launch((bwd_aggregate<N, BF16, true>), grid, block, (uint32_t)lds_agg, st, a, g);
-        else launch((bwd_aggregate<N, BF16, false>), grid, block, (uint32_t)lds_agg, st, a, g);
+        if (a.z) launch((bwd_aggregate<N, BF16, true, CH>), grid, block, (uint32_t)lds_agg, st, a, g);
+        else launch((bwd_aggregate<N, BF16, false, CH>), grid, block, (uint32_t)lds_agg, st, a, g);
     }
     const dim3 cg((unsigned)((a.D + 63) / 64), NT, a.B);
     if (g.G > 1) launch(bwd_carry<false>, cg, dim3(256), 0, st, a.h0, ws + wl.GH, ws + wl.GP, a.B, a.D, NT, g.G);
