@@ -431,7 +431,8 @@ def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16, trans_cost=DEFAULT
                 hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, sets=len(sets),
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
                               traffic=committed_traffic("scan_var", f"traffic_{name}.md"),
-                              kernel="segment_final (zero-order hold, softplus(delta + bias))"))
+                              kernel=("segment_final_sink" if N >= 64 else "segment_final")
+                              + " (zero-order hold, softplus(delta + bias))"))
 
 
 # ------------------------------------------------------------------ Mamba-3 scan
@@ -952,13 +953,13 @@ def main():
             other[nm] = scan_summary(r3)
         other["scan_f32_B1_L256_D64_N16"]["latency_us"] = {
             k: v * 1e3 for k, v in other["scan_f32_B1_L256_D64_N16"]["call_latency"].items() if k.endswith("_ms")}
-        other["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"] = scan_var_bench(
-            "scan_zoh_softplus_bf16_B1_L4096_D1536_N16", si.WORKLOADS["scan_zoh_softplus_bf16_B1_L4096_D1536_N16"],
-            steps=20, warmup=3, dev=dev, trans_cost=trans_cost)
+        for nm in ("scan_zoh_softplus_bf16_B1_L4096_D1536_N16", "scan_zoh_softplus_bf16_B1_L4096_D1536_N64"):
+            other[nm] = scan_var_bench(nm, si.WORKLOADS[nm], steps=20, warmup=3, dev=dev, trans_cost=trans_cost)
         other["scan3_bf16_B1_L4096_D1536_N16"] = scan3_bench(
             "scan3_bf16_B1_L4096_D1536_N16", si.WORKLOADS["scan3_bf16_B1_L4096_D1536_N16"], steps=20, warmup=3,
             dev=dev, trans_cost=trans_cost)
-        for nm in ("scan_bwd_bf16_B1_L4096_D1536_N16", "scan_bwd_bf16_B8_L32768_D512_N16"):
+        for nm in ("scan_bwd_bf16_B1_L4096_D1536_N16", "scan_bwd_bf16_B8_L32768_D512_N16",
+                   "scan_bwd_bf16_B1_L4096_D1536_N64"):
             other[nm] = scan_bwd_bench(nm, si.WORKLOADS[nm], steps=10 if si.WORKLOADS[nm]["L"] <= 4096 else 3,
                                        warmup=2, dev=dev, trans_cost=trans_cost)
         for nm in ("ssd_bf16_B4_L8192_H24_P64_N128_Q256", "ssd_bf16_B4_L8192_H24_P64_N128_Q64",

@@ -225,8 +225,11 @@ WORKLOADS = {
     # sweep's shape (batch 8, d_model 256 -> 512 channels, 32K tokens)
     "scan_bwd_bf16_B1_L4096_D1536_N16": dict(kind="scan_bwd", B=1, L=4096, D=1536, N=16, dtype=BF16),
     "scan_bwd_bf16_B8_L32768_D512_N16": dict(kind="scan_bwd", B=8, L=32768, D=512, N=16, dtype=BF16),
+    # ... and at N = 64 of the state-dimension sweep (chunks of 16 states)
+    "scan_bwd_bf16_B1_L4096_D1536_N64": dict(kind="scan_bwd", B=1, L=4096, D=1536, N=64, dtype=BF16),
     # the headline layer with exact zero-order hold and softplus(delta + bias) in the kernel
     "scan_zoh_softplus_bf16_B1_L4096_D1536_N16": dict(kind="scan_var", B=1, L=4096, D=1536, N=16, dtype=BF16),
+    "scan_zoh_softplus_bf16_B1_L4096_D1536_N64": dict(kind="scan_var", B=1, L=4096, D=1536, N=64, dtype=BF16),
     # the headline layer as a Mamba-3 scan (complex transitions, exponential-trapezoidal rule)
     "scan3_bf16_B1_L4096_D1536_N16": dict(kind="scan3", B=1, L=4096, D=1536, N=16, dtype=BF16),
     "ssd_bf16_B4_L8192_H24_P64_N128_Q256": dict(kind="ssd", B=4, L=8192, H=24, P=64, N=128,
