@@ -218,6 +218,7 @@ KERNEL_SOURCES = {
     "scan": ("scan_core.h", "scan_fwd.hip", "common.h", "launch.h"),
     "scan_var": ("scan_core.h", "scan_var.hip", "common.h", "launch.h"),
     "scan_bwd": ("scan_bwd.hip", "common.h", "launch.h"),
+    "scan3": ("scan3.hip", "scan3.h", "common.h", "launch.h"),
     "ssd": ("ssd_fwd.hip", "common.h", "launch.h"),
     "step": ("step.hip", "common.h", "launch.h"),
     "ssd_step": ("ssd_step.hip", "common.h", "launch.h"),
@@ -481,7 +482,8 @@ def scan3_bench(name, wl, steps, warmup, dev, max_sets=16, trans_cost=DEFAULT_TR
                 call_latency=lat, kernel_ms=[float(v) for v in kmean], hbm_gbs=alg / (ms * 1e-3) / 1e9,
                 hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, sets=len(sets), alg_bytes=alg,
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
-                              slots_per_update=slots, kernel="seg_final3 (dominant)"))
+                              slots_per_update=slots, traffic=committed_traffic("scan3", f"traffic_{name}.md"),
+                              kernel="seg_final3 (dominant)"))
 
 
 # ------------------------------------------------------------------ scan backward
