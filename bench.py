@@ -740,7 +740,8 @@ def valu_rates(dev, blocks=8192, iters=2048):
     res["mix_measured_over_predicted"] = mix / res["mix_predicted_no_coissue_ops_per_s"]
     res["fma_frac_of_lane_peak"] = fma / LANE_SLOTS_PER_S
     res["note"] = ("lane ops/s of ssm_diag_valu_rate: 8 independent chains per lane, %d lanes; the lane-slot "
-                   "peak is 256 CU x 64 lanes x 2.4 GHz = %.1f T/s" % (blocks * 256, LANE_SLOTS_PER_S / 1e12))
+                   "peak is 256 CU x 128 lane-ops per clock (4 SIMDs, a wave64 instruction every 2 clocks) "
+                   "x 2.4 GHz = %.1f T/s" % (blocks * 256, LANE_SLOTS_PER_S / 1e12))
     return res
 
 
