@@ -6,6 +6,7 @@
  *   ssm_scan_fwd_noalloc  the same on a fixed per-GPU scratch (no workspace argument)
  *   ssm_scan_fwd_ex  the same with exact zero-order hold and/or Delta = softplus(delta + bias)
  *   ssm_scan3_fwd    Mamba-3: complex transitions, exponential-trapezoidal rule
+ *   ssm_step3        the Mamba-3 one-token decode step, complex state updated in place
  *   ssm_scan_bwd     the scan's gradient (training backward pass)
  *   ssm_ssd_fwd      Mamba-2 SSD: scalar decay per head, chunked decayed-attention form
  *   ssm_step         one-token recurrent decode step, state updated in place
@@ -231,6 +232,38 @@ int ssm_scan3_fwd(int B, int L, int D, int N, ssm_dtype_t io,
                   const float* h0, const void* x_prev, const void* B_prev,
                   void* y, float* h_final,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ssm_step3 -- Mamba-3 one-token decode step: the recurrence of ssm_scan3_fwd for
+ * one time step, the complex state updated in place.
+ *
+ * "Efficient Sequence Modeling: From S4 to Mamba-3", section 03 System
+ * (mamba3_minimal.py: the incremental form of the complex, exponential-trapezoidal
+ * recurrence). Per (batch b, channel d) and state n:
+ *   alpha = exp(delta (Are[d,n] + i theta[d,n]))
+ *   h[n]  = alpha (h[n] + (1 - lam) delta B_prev[n] x_prev) + lam delta B[n] x
+ *   y     = (sum_n C[n] Re h[n] + Dskip[d] x) * silu(z)
+ * ssm_step3 on a state equals ssm_scan3_fwd over one token from that state with
+ * the same (x_prev, B_prev); a decode loop passes the previous token's x and B
+ * row as the next call's x_prev and B_prev.
+ *
+ *   state  : [B, D, N, 2] fp32 (real, imaginary), read and written in place
+ *   x, delta, lam, z : [B, D] io dtype (z may be NULL: no gate)
+ *   Are, theta       : [D, N] fp32, as for ssm_scan3_fwd
+ *   Bm, Cm           : [B, N] io dtype
+ *   Dskip            : [D] fp32 or NULL
+ *   x_prev, B_prev   : [B, D] and [B, N] io dtype, both or neither (neither: the
+ *                      previous token's term is zero, as at a sequence start)
+ *   y                : [B, D] io dtype out
+ * Supported: N in {4, 8, 16, 32, 64, 128}. Every pointer must be 16-byte aligned.
+ * Errors: SSM_ERR_INVALID_ARG (a required pointer NULL, x_prev without B_prev or the
+ * reverse, bad dims, misalignment), SSM_ERR_UNSUPPORTED (N), SSM_ERR_HIP.
+ * ------------------------------------------------------------------------- */
+int ssm_step3(int B, int D, int N, ssm_dtype_t io,
+              float* state, const void* x, const void* delta, const void* lam,
+              const float* Are, const float* theta, const void* Bm, const void* Cm,
+              const float* Dskip, const void* z, const void* x_prev, const void* B_prev,
+              void* y, void* stream);
 
 /* ---------------------------------------------------------------------------
  * ssm_scan_bwd -- gradient of ssm_scan_fwd (training backward pass).

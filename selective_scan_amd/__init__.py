@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     ssm_diag_valu_rate,
     ssm_scan3_fwd,
     ssm_scan3_workspace_size,
+    ssm_step3,
     ssm_scan_bwd,
     ssm_scan_bwd_workspace_size,
     ssm_scan_fwd,

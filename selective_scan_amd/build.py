@@ -14,8 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm_scan.so")
 
-SOURCES = ["api.cpp", "scan_fwd.hip", "scan_var.hip", "scan3.hip", "scan_noalloc.hip", "scan_bwd.hip", "step.hip",
-           "ssd_fwd.hip", "ssd_step.hip", "diag.hip"]
+SOURCES = ["api.cpp", "scan_fwd.hip", "scan_var.hip", "scan3.hip", "step3.hip", "scan_noalloc.hip", "scan_bwd.hip",
+           "step.hip", "ssd_fwd.hip", "ssd_step.hip", "diag.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

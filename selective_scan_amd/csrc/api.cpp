@@ -12,6 +12,7 @@
 #include "extras.h"
 #include "launch.h"
 #include "scan3.h"
+#include "step3.h"
 
 namespace {
 
@@ -256,6 +257,27 @@ int ssm_scan3_fwd(int B, int L, int D, int N, ssm_dtype_t io,
     ssm::Scan3Args a{B, L, D, N, io == SSM_BF16, x, delta, lam, Are, theta, Bm, Cm, Dskip, z, h0, x_prev, B_prev,
                      y, h_final, workspace};
     return hip_status(ssm::launch_scan3_fwd(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ssm_step3(int B, int D, int N, ssm_dtype_t io,
+              float* state, const void* x, const void* delta, const void* lam,
+              const float* Are, const float* theta, const void* Bm, const void* Cm,
+              const float* Dskip, const void* z, const void* x_prev, const void* B_prev,
+              void* y, void* stream) {
+    const char* fn = "ssm_step3";
+    if (B < 1 || D < 1 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1");
+    if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
+    if (!ssm::step3_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128");
+    if (!product_ok({B, D, N}, 1LL << 40)) return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
+    if (!state || !x || !delta || !lam || !Are || !theta || !Bm || !Cm || !y)
+        return fail(SSM_ERR_INVALID_ARG, fn, "state, x, delta, lam, Are, theta, Bm, Cm and y are required");
+    if ((x_prev == nullptr) != (B_prev == nullptr))
+        return fail(SSM_ERR_INVALID_ARG, fn, "x_prev and B_prev must be given together");
+    const void* ptrs[] = {state, x, delta, lam, Are, theta, Bm, Cm, Dskip, z, x_prev, B_prev, y};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SSM_ERR_INVALID_ARG, fn, "every pointer must be 16-byte aligned");
+    ssm::Step3Args a{B, D, N, io == SSM_BF16, state, x, delta, lam, Are, theta, Bm, Cm, Dskip, z, x_prev, B_prev, y};
+    return hip_status(ssm::launch_step3(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 // ------------------------------------------------------------------ scan backward

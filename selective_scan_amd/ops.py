@@ -61,6 +61,8 @@ def lib():
     L.ssm_step.restype = i
     L.ssm_ssd_step.argtypes = [i, i, i, i, i] + [fp] + [vp] * 8 + [vp]
     L.ssm_ssd_step.restype = i
+    L.ssm_step3.argtypes = [i, i, i, i] + [fp] + [vp] * 12 + [vp]
+    L.ssm_step3.restype = i
     L.ssm_diag_valu_rate.argtypes, L.ssm_diag_valu_rate.restype = [i, i, i, vp, vp], i
     L.ssm_diag_stream_scale.argtypes, L.ssm_diag_stream_scale.restype = [vp, sz, ctypes.c_float, vp], i
     L.ssm_diag_copy.argtypes, L.ssm_diag_copy.restype = [vp, vp, sz, vp], i
@@ -390,6 +392,33 @@ def ssm_ssd_step(state, x, delta, A, Bm, Cm, D=None, z=None, *, y=None, stream=N
                             _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(y), _stream(dev, stream))
     if st != SSM_OK:
         _raise("ssm_ssd_step", st)
+    return y
+
+
+def ssm_step3(state, x, delta, lam, Are, theta, Bm, Cm, D=None, z=None, x_prev=None, B_prev=None, *, y=None,
+              stream=None):
+    """One Mamba-3 decode step. state: [B, D, N, 2] fp32 (real, imaginary; updated in
+    place); x, delta, lam, z: [B, D]; Bm, Cm: [B, N]; Are, theta: [D, N] fp32; D: [D];
+    x_prev [B, D] and B_prev [B, N]: the previous token. Returns y [B, D]."""
+    Bb, Dd, N, two = state.shape
+    dev, io = x.device, x.dtype
+    _check(state, "state", (Bb, Dd, N, 2), torch.float32, dev)
+    for t, nm, shp, dt, req in ((x, "x", (Bb, Dd), io, True), (delta, "delta", (Bb, Dd), io, True),
+                                (lam, "lam", (Bb, Dd), io, True), (Are, "Are", (Dd, N), torch.float32, True),
+                                (theta, "theta", (Dd, N), torch.float32, True), (Bm, "Bm", (Bb, N), io, True),
+                                (Cm, "Cm", (Bb, N), io, True), (D, "D", (Dd,), torch.float32, False),
+                                (z, "z", (Bb, Dd), io, False), (x_prev, "x_prev", (Bb, Dd), io, False),
+                                (B_prev, "B_prev", (Bb, N), io, False)):
+        _check(t, nm, shp, dt, dev, required=req)
+    if y is None:
+        with _on(stream):
+            y = torch.empty((Bb, Dd), dtype=io, device=dev)
+    _check(y, "y", (Bb, Dd), io, dev)
+    st = lib().ssm_step3(Bb, Dd, N, _io_code(x), _ptr(state), _ptr(x), _ptr(delta), _ptr(lam), _ptr(Are),
+                         _ptr(theta), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z), _ptr(x_prev), _ptr(B_prev), _ptr(y),
+                         _stream(dev, stream))
+    if st != SSM_OK:
+        _raise("ssm_step3", st)
     return y
 
 

@@ -238,3 +238,19 @@ def test_scan3_workspace_size():
     assert ssa.ssm_scan3_workspace_size(1, 4096, 1536, 16) > 0
     assert ssa.ssm_scan3_workspace_size(1, 32, 64, 16) == 0      # a single segment needs none
     assert ssa.ssm_scan3_workspace_size(1, 4096, 1536, 32) == 0  # unsupported N
+
+
+def _step3(B=2, D=64, N=16, io=1, state=P, x=P, delta=P, lam=P, Are=P, theta=P, Bm=P, Cm=P, Dk=None, z=None,
+           xp=None, bp=None, y=P):
+    return ops.lib().ssm_step3(B, D, N, io, state, x, delta, lam, Are, theta, Bm, Cm, Dk, z, xp, bp, y, None)
+
+
+# one defect per case, so no call reaches a launch
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(D=0), 1), (dict(io=7), 1), (dict(N=12), 2), (dict(N=256), 2), (dict(state=None), 1),
+    (dict(lam=None), 1), (dict(theta=None), 1), (dict(y=None), 1), (dict(xp=P), 1), (dict(bp=P), 1),
+    (dict(z=ctypes.c_void_p(0x10008)), 1),
+])
+def test_step3_rejects_bad_arguments(kw, status):
+    assert _step3(**kw) == status
+    assert ops.lib().ssm_last_error().startswith(b"ssm_step3: ")
