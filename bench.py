@@ -219,6 +219,7 @@ KERNEL_SOURCES = {
     "scan_var": ("scan_core.h", "scan_var.hip", "common.h", "launch.h"),
     "scan_bwd": ("scan_bwd.hip", "common.h", "launch.h"),
     "scan3": ("scan3.hip", "scan3.h", "common.h", "launch.h"),
+    "step3": ("step3.hip", "step3.h", "common.h", "launch.h"),
     "ssd": ("ssd_fwd.hip", "common.h", "launch.h"),
     "step": ("step.hip", "common.h", "launch.h"),
     "ssd_step": ("ssd_step.hip", "common.h", "launch.h"),
@@ -682,6 +683,94 @@ def step_bench(wl, dev, reps=3, only=None):
                 streaming_floor=streaming_floor(st0, steps))
 
 
+def step3_bench(wl, dev, reps=3, only=None):
+    """The Mamba-3 decode workload: `steps` in-place steps of ssm_step3, each given the
+    previous token, stream-launched and HIP-graph replayed (state MALL-resident), then
+    the cold multi-layer variant and the streaming floor. only="hot" / "cold" as for
+    step_bench."""
+    import torch
+    import selective_scan_amd as ssa
+    import ssm_inputs as si
+    name = "step3_bf16_B64_D3072_N16_x200"
+    B, D, N, steps = wl["B"], wl["D"], wl["N"], wl["steps"]
+    w = si.scan3_inputs(B, steps, D, N, dtype=wl["dtype"], seed=0, with_h0=True, with_prev=True)
+    # token-major copies, so that token s is a contiguous, aligned [B, ...] slice
+    tok = {k: si.to_torch(np.ascontiguousarray(np.swapaxes(w[k], 0, 1)), dev)
+           for k in ("x", "delta", "lam", "z", "Bm", "Cm")}
+    Are, th = torch.from_numpy(w["Are"]).to(dev), torch.from_numpy(w["theta"]).to(dev)
+    Dk = torch.from_numpy(w["D"]).to(dev)
+    xp0, bp0 = si.to_torch(w["x_prev"], dev), si.to_torch(w["B_prev"], dev)
+    st0 = torch.from_numpy(w["h0"]).to(dev)
+    st = st0.clone()
+    y = torch.empty((steps, B, D), dtype=tok["x"].dtype, device=dev)
+
+    def step1(stv, s_):
+        xp, bp = (xp0, bp0) if s_ == 0 else (tok["x"][s_ - 1], tok["Bm"][s_ - 1])
+        ssa.ssm_step3(stv, tok["x"][s_], tok["delta"][s_], tok["lam"][s_], Are, th, tok["Bm"][s_], tok["Cm"][s_],
+                      D=Dk, z=tok["z"][s_], x_prev=xp, B_prev=bp, y=y[s_])
+
+    def run():
+        for s_ in range(steps):
+            step1(st, s_)
+
+    if only == "cold":
+        cold = cold_decode(step1, st0, steps)
+        return dict(workload=name, only="cold", cold_ms_per_step=cold["ms"], layers=cold["layers"])
+    times = []
+    if only is None:
+        run()
+        sync()
+        for _ in range(reps):
+            st.copy_(st0)
+            sync()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            sync()
+            times.append(e0.elapsed_time(e1))
+    g = torch.cuda.CUDAGraph()
+    st.copy_(st0)
+    sync()
+    s_ = torch.cuda.Stream()
+    with torch.cuda.stream(s_):
+        with torch.cuda.graph(g, stream=s_):
+            run()
+    sync()
+    gtimes = []
+    for _ in range(reps):
+        st.copy_(st0)
+        sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        sync()
+        gtimes.append(e0.elapsed_time(e1))
+    if only == "hot":
+        return dict(workload=name, only="hot", hot_ms_per_step=float(np.median(gtimes)) / steps)
+    es = 2 if wl["dtype"] == "bf16" else 4
+    # complex state read and written; x, Delta, lam, z, x_prev read and y written; B, C,
+    # B_prev rows; Are, theta and D
+    alg = 2 * B * D * N * 8 + 6 * B * D * es + 3 * B * N * es + (2 * D * N + D) * 4
+    med = float(np.median(times)) / steps
+    gmed = float(np.median(gtimes)) / steps
+    cold = cold_decode(step1, st0, steps)
+    return dict(workload=name, ms_per_step_stream=med,
+                traffic=committed_traffic("step3", "traffic_step3_bf16_B64_D3072_N16.md"), alg_bytes_per_step=alg,
+                ms_per_step_graph=gmed, updates_per_s_graph=B * D * N / (gmed * 1e-3),
+                tokens_per_s_graph=B / (gmed * 1e-3), hbm_gbs_graph=alg / (gmed * 1e-3) / 1e9,
+                note="complex state (%.1f MB) stays resident in the 256 MB MALL across in-place steps"
+                     % (st0.numel() * 4 / 1e6),
+                cold=dict(layers=cold["layers"], ms_per_step_graph=cold["ms"],
+                          hbm_gbs_graph=alg / (cold["ms"] * 1e-3) / 1e9,
+                          hbm_frac=alg / (cold["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          note="step s updates the state of layer s mod layers: the states "
+                               "(%d x %.1f MB) exceed the MALL, so each step streams its state from HBM"
+                               % (cold["layers"], st0.numel() * 4 / 1e6)),
+                streaming_floor=streaming_floor(st0, steps))
+
+
 def streaming_floor(st0, steps, reps=3):
     """Context for a decode step: this library's in-place streaming kernel
     (ssm_diag_stream_scale: every 16-byte load of a lane issued before its first
@@ -864,9 +953,9 @@ def main():
     ap.add_argument("--no-other", action="store_true")
     ap.add_argument("--other", default=None,
                     help="only run this one workload of the other paths (a scan_*, scan_bwd_*, scan_zoh_*, ssd_*, "
-                         "step_* or ssd_step_* name) and print it")
+                         "step_*, ssd_step_* or step3_* name) and print it")
     ap.add_argument("--decode-pass", choices=("hot", "cold"), default=None,
-                    help="with --other step_*/ssd_step_*: run only the graph-replayed hot or cold variant")
+                    help="with --other step_*/ssd_step_*/step3_*: run only the graph-replayed hot or cold variant")
     ap.add_argument("--valu-rates", action="store_true",
                     help="only run the VALU issue-rate probes (exp, fma, 1:3 mix) and print them")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -908,6 +997,8 @@ def main():
             r = step_bench(wl, dev, only=args.decode_pass)
         elif wl["kind"] == "ssd_step":
             r = ssd_step_bench(wl, dev, only=args.decode_pass)
+        elif wl["kind"] == "step3":
+            r = step3_bench(wl, dev, only=args.decode_pass)
         else:
             raise SystemExit(f"--other takes a scan_*, scan_bwd_*, scan_zoh_* or ssd_* workload, not {args.other}")
         print(json.dumps(r))
@@ -970,6 +1061,7 @@ def main():
             other[nm] = ssd_bench(nm, si.WORKLOADS[nm], steps=10, warmup=3, dev=dev)
         other["decode"] = step_bench(si.WORKLOADS["step_bf16_B64_D3072_N16_x1000"], dev)
         other["ssd_decode"] = ssd_step_bench(si.WORKLOADS["ssd_step_bf16_B64_H24_P64_N128_x200"], dev)
+        other["mamba3_decode"] = step3_bench(si.WORKLOADS["step3_bf16_B64_D3072_N16_x200"], dev)
         out["other_paths"] = other
     print(json.dumps(out))
 

@@ -255,9 +255,10 @@ int ssm_scan3_fwd(int B, int L, int D, int N, ssm_dtype_t io,
  *   x_prev, B_prev   : [B, D] and [B, N] io dtype, both or neither (neither: the
  *                      previous token's term is zero, as at a sequence start)
  *   y                : [B, D] io dtype out
- * Supported: N in {4, 8, 16, 32, 64, 128}. Every pointer must be 16-byte aligned.
- * Errors: SSM_ERR_INVALID_ARG (a required pointer NULL, x_prev without B_prev or the
- * reverse, bad dims, misalignment), SSM_ERR_UNSUPPORTED (N), SSM_ERR_HIP.
+ * Supported: N in {4, 8, 16, 32, 64, 128}; B <= 65535; D * N < 2^31. Every pointer
+ * must be 16-byte aligned. Errors: SSM_ERR_INVALID_ARG (a required pointer NULL,
+ * x_prev without B_prev or the reverse, bad dims, misalignment), SSM_ERR_UNSUPPORTED
+ * (N, B or D * N out of range), SSM_ERR_HIP.
  * ------------------------------------------------------------------------- */
 int ssm_step3(int B, int D, int N, ssm_dtype_t io,
               float* state, const void* x, const void* delta, const void* lam,

@@ -268,6 +268,8 @@ int ssm_step3(int B, int D, int N, ssm_dtype_t io,
     if (B < 1 || D < 1 || N < 1) return fail(SSM_ERR_INVALID_ARG, fn, "B, D, N must be >= 1");
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
     if (!ssm::step3_supported_n(N)) return fail(SSM_ERR_UNSUPPORTED, fn, "N must be one of 4, 8, 16, 32, 64, 128");
+    if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");
+    if ((long long)D * N > 0x7fffffffLL) return fail(SSM_ERR_UNSUPPORTED, fn, "D * N must be < 2^31");
     if (!product_ok({B, D, N}, 1LL << 40)) return fail(SSM_ERR_INVALID_ARG, fn, "tensor sizes overflow");
     if (!state || !x || !delta || !lam || !Are || !theta || !Bm || !Cm || !y)
         return fail(SSM_ERR_INVALID_ARG, fn, "state, x, delta, lam, Are, theta, Bm, Cm and y are required");

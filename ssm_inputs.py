@@ -242,4 +242,6 @@ WORKLOADS = {
     # Mamba-2 decode (a Mamba2-130m-sized layer: 24 heads of 64, N = 128), 200 steps in place
     "ssd_step_bf16_B64_H24_P64_N128_x200": dict(kind="ssd_step", B=64, H=24, P=64, N=128, steps=200,
                                                 dtype=BF16),
+    # Mamba-3 decode at the Mamba-1 decode layer's size (complex state: 25.2 MB), 200 steps in place
+    "step3_bf16_B64_D3072_N16_x200": dict(kind="step3", B=64, D=3072, N=16, steps=200, dtype=BF16),
 }

@@ -247,7 +247,8 @@ def _step3(B=2, D=64, N=16, io=1, state=P, x=P, delta=P, lam=P, Are=P, theta=P, 
 
 # one defect per case, so no call reaches a launch
 @pytest.mark.parametrize("kw,status", [
-    (dict(B=0), 1), (dict(D=0), 1), (dict(io=7), 1), (dict(N=12), 2), (dict(N=256), 2), (dict(state=None), 1),
+    (dict(B=0), 1), (dict(D=0), 1), (dict(io=7), 1), (dict(N=12), 2), (dict(N=256), 2), (dict(B=70000), 2),
+    (dict(D=1 << 26, N=64), 2), (dict(state=None), 1),
     (dict(lam=None), 1), (dict(theta=None), 1), (dict(y=None), 1), (dict(xp=P), 1), (dict(bp=P), 1),
     (dict(z=ctypes.c_void_p(0x10008)), 1),
 ])
