@@ -3,6 +3,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+import selective_scan_amd as ssa
 import ssm_inputs as si
 from gpu_util import DEV, gpu_scan, oracle_scan, out_f64, storage, to_dev
 from parity import compare
@@ -130,3 +132,33 @@ def test_scan_long_sequence_few_channels():
     print("[scan] B1 L20000 D64 N16 (long group walk)", flush=True)
     w = si.scan_inputs(1, 20000, 64, 16, dtype=si.BF16, seed=9, with_h0=True)
     _check(w, what="long walk")
+
+
+def test_scan_tensors_beyond_2GiB():
+    """Maximum-size edge: B=1, L=2^21 + 37 (ragged), D=1024, bf16, so x, Delta, z and y
+    each hold 4.3 GB and every byte offset past 2 GiB is formed from a segment's 64-bit
+    base. The inputs repeat a seeded block of 4096 steps along L (drawing 2^31 values
+    per tensor would take minutes on the host); the oracle runs on 16 channels, the
+    last one included, over the whole sequence."""
+    B, Lb, L, D, N = 1, 4096, (1 << 21) + 37, 1024, 16
+    print(f"[scan] bf16 B{B} L{L} D{D} N{N} (> 2 GiB per tensor)", flush=True)
+    w = si.scan_inputs(B, Lb, D, N, dtype=si.BF16, seed=23, with_h0=True)
+    reps = -(-L // Lb)
+    t = to_dev(w, ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0"))
+    big = {k: t[k].repeat(1, reps, 1)[:, :L].contiguous() for k in ("x", "delta", "z", "Bm", "Cm")}
+    assert big["x"].numel() * 2 > (1 << 31)
+    y, hf = ssa.ssm_scan_fwd(big["x"], big["delta"], t["A"], big["Bm"], big["Cm"], D=t["D"], z=big["z"],
+                             h0=t["h0"])
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 63, 64, 127, 300, 511, 512, 640, 777, 900, 959, 960, 1000, 1022, 1023])
+    yg = out_f64(y[:, :, torch.from_numpy(sel).to(DEV)].contiguous())
+    hg = out_f64(hf)[:, sel]
+    del big, y
+    torch.cuda.empty_cache()
+    tile = lambda a: np.ascontiguousarray(np.tile(a, (1, reps, 1))[:, :L])
+    f = {k: si.to_f64(w[k]) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0")}
+    yr, hr = oracle.scan(tile(f["x"][:, :, sel]), tile(f["delta"][:, :, sel]), np.ascontiguousarray(f["A"][sel]),
+                         tile(f["Bm"]), tile(f["Cm"]), D=np.ascontiguousarray(f["D"][sel]),
+                         z=tile(f["z"][:, :, sel]), h0=np.ascontiguousarray(f["h0"][:, sel]))
+    compare(yg, yr, "bf16", what="beyond 2 GiB y")
+    compare(hg, hr, "f32", what="beyond 2 GiB h_final")

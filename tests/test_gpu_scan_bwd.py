@@ -129,3 +129,44 @@ def test_scan_bwd_without_dh0_changes_nothing_else():
     for k, v in g1.items():
         if k != "dh0":
             assert torch.equal(v, g2[k]), k
+
+
+def test_scan_bwd_tensors_beyond_2GiB():
+    """Maximum-size edge: B=1, L=2^20 + 37 (ragged), D=2048, N=16, bf16, so x, Delta, z,
+    dy and the per-channel gradients each hold 4.3 GB (the checkpoints 34 GB). The
+    inputs repeat a seeded block of 4096 steps along L; the oracle runs on 16 channels
+    over the whole sequence (dx, ddelta, dz, dA, dD, dh0 of those channels; dB and dC
+    sum over every channel and are covered by the full-size tests above)."""
+    import oracle
+    import selective_scan_amd as ssa
+    from gpu_util import DEV, to_dev
+    B, Lb, L, D, N = 1, 4096, (1 << 20) + 37, 2048, 16
+    print(f"[scan_bwd] bf16 B{B} L{L} D{D} N{N} (> 2 GiB per tensor)", flush=True)
+    w = si.scan_inputs(B, Lb, D, N, dtype=si.BF16, seed=25, with_h0=True)
+    gw = si.scan_grad_inputs(B, Lb, D, N, dtype=si.BF16, seed=26)
+    reps = -(-L // Lb)
+    t = to_dev(w, ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0"))
+    g = to_dev(gw, ("dy", "dh_final"))
+    big = {k: t[k].repeat(1, reps, 1)[:, :L].contiguous() for k in ("x", "delta", "z", "Bm", "Cm")}
+    dy = g["dy"].repeat(1, reps, 1)[:, :L].contiguous()
+    assert big["x"].numel() * 2 > (1 << 31)
+    out = ssa.ssm_scan_bwd(big["x"], big["delta"], t["A"], big["Bm"], big["Cm"], dy, D=t["D"], z=big["z"],
+                           h0=t["h0"], dh_final=g["dh_final"])
+    torch.cuda.synchronize()
+    sel = np.array([0, 1, 63, 64, 500, 1023, 1024, 1500, 1919, 1920, 2000, 2040, 2045, 2046, 2047, 777])
+    sd = torch.from_numpy(sel).to(DEV)
+    got = {k: out_f64(out[k][:, :, sd].contiguous()) for k in ("dx", "ddelta", "dz")}
+    got["dA"], got["dD"], got["dh0"] = out_f64(out["dA"])[sel], out_f64(out["dD"])[sel], out_f64(out["dh0"])[:, sel]
+    del big, dy, out
+    torch.cuda.empty_cache()
+    tile = lambda a: np.ascontiguousarray(np.tile(a, (1, reps, 1))[:, :L])
+    f = {k: si.to_f64(w[k]) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0")}
+    r = oracle.scan_bwd(tile(f["x"][:, :, sel]), tile(f["delta"][:, :, sel]), np.ascontiguousarray(f["A"][sel]),
+                        tile(f["Bm"]), tile(f["Cm"]), tile(si.to_f64(gw["dy"])[:, :, sel]),
+                        D=np.ascontiguousarray(f["D"][sel]), z=tile(f["z"][:, :, sel]),
+                        h0=np.ascontiguousarray(f["h0"][:, sel]),
+                        dh_final=np.ascontiguousarray(si.to_f64(gw["dh_final"])[:, sel]))
+    for k in ("dx", "ddelta", "dz"):
+        compare(got[k], r[k], "bf16", what=f"beyond 2 GiB {k}")
+    for k in ("dA", "dD", "dh0"):
+        compare(got[k], r[k], "f32", what=f"beyond 2 GiB {k}")

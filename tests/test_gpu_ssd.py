@@ -111,3 +111,38 @@ def test_ssd_deterministic():
     y1, h1 = gpu_ssd(w, 256)
     y2, h2 = gpu_ssd(w, 256)
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_ssd_tensors_beyond_2GiB():
+    """Maximum-size edge: B=16, L=2^16 + 100 (ragged last chunk), H=24, P=64, N=128,
+    chunk 256, bf16, so x and y hold 3.2 GB each and the later batch rows start past
+    2 GiB. The inputs repeat a seeded block of 1024 steps along L; the oracle runs on
+    the first and last batch rows and two heads over the whole sequence."""
+    B, Lb, L, H, P, N = 16, 1024, (1 << 16) + 100, 24, 64, 128
+    print(f"[ssd] bf16 B{B} L{L} H{H} N{N} (> 2 GiB per tensor)", flush=True)
+    w = si.ssd_inputs(B, Lb, H, P, N, seed=24, with_D=True, with_z=True, with_h0=True)
+    reps = -(-L // Lb)
+    t = {k: si.to_torch(w[k], DEV) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0")}
+    big = {}
+    for k in ("x", "delta", "z", "Bm", "Cm"):
+        v = t[k]
+        big[k] = v.repeat(1, reps, *([1] * (v.dim() - 2)))[:, :L].contiguous()
+    assert big["x"].numel() * 2 > (1 << 31)
+    y, hf = ssa.ssm_ssd_fwd(big["x"], big["delta"], t["A"], big["Bm"], big["Cm"], D=t["D"], z=big["z"], h0=t["h0"],
+                            chunk=256)
+    torch.cuda.synchronize()
+    bsel, hsel = np.array([0, B - 1]), np.array([0, H - 1])
+    yg = out_f64(y[torch.from_numpy(bsel).to(DEV)][:, :, torch.from_numpy(hsel).to(DEV)].contiguous())
+    hg = out_f64(hf)[bsel][:, hsel]
+    del big, y
+    torch.cuda.empty_cache()
+    f = {k: si.to_f64(w[k]) for k in ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0")}
+
+    def tile(a):
+        a = a[bsel]
+        return np.ascontiguousarray(np.tile(a, (1, reps) + (1,) * (a.ndim - 2))[:, :L])
+    yr, hr = oracle.ssd_seq(tile(f["x"][:, :, hsel]), tile(f["delta"][:, :, hsel]), np.ascontiguousarray(f["A"][hsel]),
+                            tile(f["Bm"]), tile(f["Cm"]), D=np.ascontiguousarray(f["D"][hsel]),
+                            z=tile(f["z"][:, :, hsel]), h0=np.ascontiguousarray(f["h0"][bsel][:, hsel]))
+    compare(yg, yr, "bf16", what="beyond 2 GiB y")
+    compare(hg, hr, "f32", what="beyond 2 GiB h_final")
