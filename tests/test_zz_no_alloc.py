@@ -50,3 +50,41 @@ def test_noalloc_rejects_a_shape_beyond_the_scratch():
     with pytest.raises(ssa.SsmError) as e:
         ssa.ssm_scan_fwd_noalloc(x, x, A, Bm, Bm, y=torch.empty_like(x))
     assert e.value.status == 2
+
+
+def test_noalloc_under_hip_graph_capture():
+    """The callers this entry point is for: two scans captured in a HIP graph (no
+    allocation inside the capture) and replayed three times, with eager work and
+    synchronisations between replays; every replay equals the eager calls bit for bit."""
+    shapes = [(2, 3000, 256, 16), (1, 700, 130, 8)]
+    data = []
+    for i, (B, L, D, N) in enumerate(shapes):
+        w = si.scan_inputs(B, L, D, N, dtype=si.BF16, seed=43 + i, with_h0=True)
+        t = to_dev(w, ("x", "delta", "z", "Bm", "Cm", "A", "D", "h0"))
+        data.append((t, torch.empty_like(t["x"]), torch.empty((B, D, N), dtype=torch.float32, device=DEV)))
+
+    def run(outs):
+        for (t, _, _), (y, hf) in zip(data, outs):
+            ssa.ssm_scan_fwd_noalloc(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], D=t["D"], z=t["z"], h0=t["h0"],
+                                     y=y, h_final=hf)
+
+    eager = [(y.clone(), hf.clone()) for (_, y, hf) in data]
+    run(eager)
+    torch.cuda.synchronize()
+    outs = [(y, hf) for (_, y, hf) in data]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run(outs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y, hf in outs:
+            y.zero_()
+            hf.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (y, hf), (ye, he) in zip(outs, eager):
+            assert torch.equal(y, ye) and torch.equal(hf, he), f"replay {rep} differs from eager"
+        _ = (eager[0][1] * 2.0).sum().item()  # unrelated eager work between replays
