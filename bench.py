@@ -164,6 +164,22 @@ def count_kernels(call):
     return used // 2
 
 
+def warm_ms(call, s, steps=20, warmup=3):
+    """Milliseconds per call with one input set called over and over: the set stays
+    in the 256 MB MALL when it fits (the warm figure beside the cold, rotating one)."""
+    import torch
+    for _ in range(warmup):
+        call(s)
+    sync()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        call(s)
+    t1.record()
+    sync()
+    return t0.elapsed_time(t1) / steps
+
+
 def time_calls(call, sets, steps, warmup, n_kernels):
     """Time `steps` calls (rotating over `sets`) between two events on the launch
     stream; then time every kernel of another `steps` calls with the library's
@@ -340,6 +356,7 @@ def scan_bench(name, wl, steps, warmup, dev, trans_cost=DEFAULT_TRANS_COST, lat_
         hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         call_latency=lat, kernel_ms=dict(zip(names, (float(v) for v in kmean))), dominant_kernel=names[dom],
         sets=len(sets), set_mb=set_bytes / 1e6, alg_bytes=alg,
+        warm_ms_per_step=warm_ms(lambda t: scan_call(t, ws), sets[0]),
     )
     tdom = kmean[dom] * 1e-3
     traffic = committed_traffic("scan", f"traffic_{name}.md")
@@ -381,9 +398,34 @@ def scan_cpu_baseline(wl, w0, budget_s=15.0, total_s=10.0):
         reps += 1
     el = float(np.median(els))
     upd = B * L * dsel * N
+    # one thread on a slice sized to about 2 s
+    o.set_threads(1)
+    d1 = int(max(1, min(D, 2.0 / max(probe * T / min(D, T), 1e-6))))
+    e1 = run(d1)
+    o.set_threads(T)
     return dict(value=upd / el, unit="state updates/s", cores=T, kind="oracle",
                 sample=f"fp64 oracle (sequential recurrence) on B={B}, L={L}, {dsel} of {D} channels, "
-                       f"N={N}: {upd / 1e6:.1f} M updates, median of {reps} run(s), {el:.3f} s each")
+                       f"N={N}: {upd / 1e6:.1f} M updates, median of {reps} run(s), {el:.3f} s each",
+                cpu_model=cpu_model(),
+                single_thread=dict(value=B * L * d1 * N / e1, unit="state updates/s",
+                                   sample=f"{d1} of {D} channels, one run of {e1:.2f} s"))
+
+
+def device_info(dev):
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    return dict(name=p.name, arch=getattr(p, "gcnArchName", None), compute_units=p.multi_processor_count,
+                memory_gb=round(p.total_memory / 1e9, 1))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ------------------------------------------------------------------ scan variants
@@ -582,6 +624,7 @@ def ssd_bench(name, wl, steps, warmup, dev, max_sets=3):
     nk = count_kernels(lambda: call(sets[0]))
     total_ms, ker = time_calls(call, sets, steps, warmup, nk)
     lat = latency(call, sets)
+    warm = warm_ms(call, sets[0])
     ms = total_ms / steps
     kmean = ker.mean(axis=0)
     byt, fl = ssd_alg(wl)
@@ -596,7 +639,51 @@ def ssd_bench(name, wl, steps, warmup, dev, max_sets=3):
                               frac=byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                               traffic=committed_traffic("ssd", f"ssd_kernels_{name[4:]}.md"),
                               kernel="whole call (three kernels)"),
-                dominant_kernel_ms=tdom * 1e3, alg_bytes=byt, alg_flops=fl)
+                dominant_kernel_ms=tdom * 1e3, alg_bytes=byt, alg_flops=fl, warm_ms_per_step=warm)
+
+
+def ssd_cpu_oracle(wl, heads=16):
+    """The fp64 oracle's SSD in both forms, sequential (O2) and chunked at the
+    workload's chunk length (O3), on one batch row and `heads` heads over the whole
+    sequence, all host threads (one (batch, head) per thread)."""
+    import oracle
+    import ssm_inputs as si
+    o = oracle.get()
+    o.set_threads(len(os.sched_getaffinity(0)))
+    L, H, P, N, Q = wl["L"], wl["H"], wl["P"], wl["N"], wl["chunk"]
+    h = min(heads, H)
+    w = si.ssd_inputs(1, L, h, P, N, seed=0)
+    f = {k: si.to_f64(w[k]) for k in ("x", "delta", "Bm", "Cm", "A")}
+    upd = L * h * P * N
+    out = {}
+    for form, fn in (("sequential", lambda: o.ssd_seq(f["x"], f["delta"], f["A"], f["Bm"], f["Cm"])),
+                     ("chunked", lambda: o.ssd_chunked(f["x"], f["delta"], f["A"], f["Bm"], f["Cm"], chunk=Q))):
+        t0 = time.perf_counter()
+        fn()
+        el = time.perf_counter() - t0
+        out[form] = dict(value=upd / el, unit="state updates/s", seconds=el)
+    out.update(cores=o.get_threads(), kind="oracle", sample=f"B=1, L={L}, {h} of {H} heads, P={P}, N={N}, chunk {Q}")
+    return out
+
+
+def copy_gbs(dev, reps=5):
+    """This library's plain 1 GiB device copy (ssm_diag_copy), GB/s moved (read + write)."""
+    import torch
+    import selective_scan_amd as ssa
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ssa.ssm_diag_copy(src, dst)
+    sync()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        ssa.ssm_diag_copy(src, dst)
+    t1.record()
+    sync()
+    ms = t0.elapsed_time(t1) / reps
+    nb = 2 * src.numel() * 4
+    return dict(gbs=nb / (ms * 1e-3) / 1e9, frac=nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, ms=ms, bytes=nb,
+                kernel="copy16 (ssm_diag_copy), 1 GiB")
 
 
 # ------------------------------------------------------------------ decode
@@ -939,7 +1026,7 @@ def ssd_step_bench(wl, dev, reps=3, only=None):
 
 def scan_summary(r):
     keys = ("workload", "ms_per_step", "updates_per_s", "tokens_per_s", "call_latency", "hbm_gbs", "hbm_frac",
-            "kernel_ms", "roofline", "alu")
+            "kernel_ms", "roofline", "alu", "warm_ms_per_step")
     return {k: r[k] for k in keys if k in r}
 
 
@@ -1023,6 +1110,7 @@ def main():
         "data": "synthetic (seeded; distributions of the pages' workloads)",
         "config": {"workload": args.workload, "B": wl["B"], "L": wl["L"], "D": wl["D"],
                    "N": wl["N"], "io": wl["dtype"], "rotating_input_sets": res["sets"]},
+        "device": device_info(dev),
         "tokens_per_s": res["tokens_per_s"],
         "hbm_gbs": res["hbm_gbs"],
         "hbm_frac": res["hbm_frac"],
@@ -1059,6 +1147,9 @@ def main():
         for nm in ("ssd_bf16_B4_L8192_H24_P64_N128_Q256", "ssd_bf16_B4_L8192_H24_P64_N128_Q64",
                    "ssd_bf16_B4_L8000_H24_P64_N128_Q256"):
             other[nm] = ssd_bench(nm, si.WORKLOADS[nm], steps=10, warmup=3, dev=dev)
+            if not args.no_cpu and nm.endswith("Q256") and "L8192" in nm:
+                other[nm]["cpu_oracle"] = ssd_cpu_oracle(si.WORKLOADS[nm])
+        other["copy"] = copy_gbs(dev)
         other["decode"] = step_bench(si.WORKLOADS["step_bf16_B64_D3072_N16_x1000"], dev)
         other["ssd_decode"] = ssd_step_bench(si.WORKLOADS["ssd_step_bf16_B64_H24_P64_N128_x200"], dev)
         other["mamba3_decode"] = step3_bench(si.WORKLOADS["step3_bf16_B64_D3072_N16_x200"], dev)

@@ -4,7 +4,8 @@
 //    transcendental unit costs relative to an FMA on the chip it runs on;
 //  - an in-place scale of an fp32 array, the pure-streaming floor a decode step
 //    (read the state, write it back) is compared with;
-//  - a plain device copy, the reference that scales the HBM byte counters.
+//  - a plain device copy, the reference that scales the HBM byte counters and the
+//    copy bandwidth the bench reports as context.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,9 +70,23 @@ __global__ void __launch_bounds__(256) stream_scale(float4* __restrict__ p, size
     }
 }
 
+// dst = src over n4 float4; like stream_scale, each lane issues kScaleVec loads
+// before its first store
 __global__ void __launch_bounds__(256) copy16(const float4* __restrict__ src, float4* __restrict__ dst, size_t n4) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride * kScaleVec) {
+        float4 v[kScaleVec];
+#pragma unroll
+        for (int k = 0; k < kScaleVec; ++k) {
+            const size_t j = i + k * stride;
+            v[k] = src[j < n4 ? j : i];
+        }
+#pragma unroll
+        for (int k = 0; k < kScaleVec; ++k) {
+            const size_t j = i + k * stride;
+            if (j < n4) dst[j] = v[k];
+        }
+    }
 }
 
 }  // namespace
@@ -95,7 +110,10 @@ hipError_t launch_stream_scale(float* p, size_t n, float s, hipStream_t st) {
 
 hipError_t launch_copy(const float* src, float* dst, size_t n, hipStream_t st) {
     const size_t n4 = n / 4;
-    launch(copy16, dim3(8192), dim3(256), 0, st, reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst),
+    // one float4 per lane per round, kScaleVec rounds in flight per lane
+    const size_t lanes = (n4 + kScaleVec - 1) / kScaleVec;
+    const unsigned blocks = (unsigned)std::max<size_t>(1, std::min<size_t>((lanes + 255) / 256, 1u << 20));
+    launch(copy16, dim3(blocks), dim3(256), 0, st, reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst),
            n4);
     return hipGetLastError();
 }

@@ -435,12 +435,17 @@ def ssm_diag_valu_rate(mode, out, iters, stream=None):
 
 def ssm_diag_stream_scale(t, s, stream=None):
     """t *= s in place on a contiguous fp32 tensor (the pure-streaming floor)."""
+    _check(t, "t", tuple(t.shape), torch.float32, t.device)
     st = lib().ssm_diag_stream_scale(_ptr(t), t.numel(), float(s), _stream(t.device, stream))
     if st != SSM_OK:
         _raise("ssm_diag_stream_scale", st)
 
 
 def ssm_diag_copy(src, dst, stream=None):
+    """dst = src for contiguous fp32 tensors of the same shape (the copy kernel the HBM
+    byte counters are calibrated with)."""
+    _check(src, "src", tuple(src.shape), torch.float32, src.device)
+    _check(dst, "dst", tuple(src.shape), torch.float32, src.device)
     st = lib().ssm_diag_copy(_ptr(src), _ptr(dst), src.numel(), _stream(src.device, stream))
     if st != SSM_OK:
         _raise("ssm_diag_copy", st)

@@ -1,0 +1,36 @@
+"""The measurement kernels of the library (not the scan itself): the copy the HBM
+byte counters are calibrated with, the in-place streaming kernel the decode steps
+are compared with, and the VALU issue-rate probes, checked for what they compute."""
+import pytest
+import torch
+
+import selective_scan_amd as ssa
+from gpu_util import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n", [4, 4 * 1000 + 4, (1 << 22) + 12])
+def test_diag_copy_and_scale(n):
+    g = torch.Generator(device="cpu").manual_seed(n)
+    src = torch.randn(n, generator=g).to(DEV)
+    dst = torch.full_like(src, float("nan"))
+    ssa.ssm_diag_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    ssa.ssm_diag_stream_scale(dst, 0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src * 0.5)  # a power-of-two scale is exact
+
+
+def test_diag_valu_rate_probe_values():
+    """The probes' chains stay in [0.5, 1] and the three modes compute what they say:
+    the fma chain's fixed point is 0.75; the outputs are finite."""
+    out = torch.empty(2 * 256, dtype=torch.float32, device=DEV)
+    for mode in (0, 1, 2):
+        ssa.ssm_diag_valu_rate(mode, out, 64)
+        torch.cuda.synchronize()
+        v = out / 8.0  # each lane sums its 8 chains
+        assert torch.isfinite(out).all() and bool((v >= 0.5).all()) and bool((v <= 1.0).all()), mode
+        if mode == 1:
+            assert torch.allclose(v, torch.full_like(v, 0.75), atol=1e-6)
