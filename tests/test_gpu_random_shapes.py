@@ -67,3 +67,44 @@ def test_scan_variant_random_shapes(case):
     (y, hf), (yr, hr) = V._run(w, bias, disc, sp)
     compare(out_f64(y), yr, storage(w), what=f"{case} y")
     compare(out_f64(hf), hr, "f32", what=f"{case} h_final")
+
+
+SCAN_CASES = _draw(10, 2027, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 5000)), int(r.integers(1, 400)),
+                                        int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)))
+                   + _flags(r, 3))
+SCAN3_CASES = _draw(8, 2028, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 3000)), int(r.integers(1, 300)),
+                                        int(r.choice([4, 8, 16])), bool(r.integers(0, 2))) + _flags(r, 4))
+STEP3_CASES = _draw(6, 2029, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 40)), int(r.integers(1, 300)),
+                                        int(r.choice([4, 8, 16, 32, 64, 128])), bool(r.integers(0, 2))))
+
+
+@pytest.mark.parametrize("case", SCAN_CASES, ids=lambda c: "B{}_L{}_D{}_N{}_bf{}_D{}z{}h{}".format(*c))
+def test_scan_random_shapes(case):
+    import test_gpu_scan as S
+    B, L, D, N, bf, wd, wz, wh = case
+    print(f"[scan random] {case}", flush=True)
+    w = si.scan_inputs(B, L, D, N, dtype=si.BF16 if bf else si.F32, seed=L, with_D=wd, with_z=wz, with_h0=wh)
+    S._check(w, what=str(case))
+
+
+@pytest.mark.parametrize("case", SCAN3_CASES, ids=lambda c: "B{}_L{}_D{}_N{}_bf{}_D{}z{}h{}p{}".format(*c))
+def test_scan3_random_shapes(case):
+    import test_gpu_scan3 as S3
+    B, L, D, N, bf, wd, wz, wh, wp = case
+    print(f"[scan3 random] {case}", flush=True)
+    w = si.scan3_inputs(B, L, D, N, dtype=si.BF16 if bf else si.F32, seed=L, with_D=wd, with_z=wz, with_h0=wh,
+                        with_prev=wp)
+    S3._check(w, str(case))
+
+
+@pytest.mark.parametrize("case", STEP3_CASES, ids=lambda c: "B{}_T{}_D{}_N{}_bf{}".format(*c))
+def test_step3_random_chains(case):
+    import test_gpu_step3 as T3
+    B, T, D, N, bf = case
+    print(f"[step3 random] {case}", flush=True)
+    w = si.scan3_inputs(B, T, D, N, dtype=si.BF16 if bf else si.F32, seed=T, with_h0=True, with_prev=True)
+    st, prev = T3._start(w)
+    y = T3.gpu_steps(w, 0, T, st, prev)
+    yr, hr = T3.oracle_scan3(w)
+    compare(out_f64(y), yr, storage(w), what=f"{case} y")
+    compare(out_f64(st), hr, "f32", what=f"{case} state")
