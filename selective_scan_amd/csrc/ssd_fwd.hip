@@ -246,11 +246,11 @@ __device__ __forceinline__ u32x4 ld_buf16(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 // Rows of x and B of one chunk (and, in the prefix wave, its Delta) held in registers
-// between the global load and the LDS store.
-template <int N>
+// between the global load and the LDS store, for chunks of at most QM steps.
+template <int N, int QM>
 struct ChunkRows {
-    static constexpr int XQ = kMaxQ * (kP / 8) / kThreads;  // 16-byte pieces per thread
-    static constexpr int BQ = kMaxQ * (N / 8) / kThreads;
+    static constexpr int XQ = QM * (kP / 8) / kThreads;  // 16-byte pieces per thread
+    static constexpr int BQ = QM * (N / 8) / kThreads;
     u32x4 xv[XQ];
     u32x4 bv[BQ];
     float dv[4];
@@ -258,11 +258,11 @@ struct ChunkRows {
 
 // x rows (and, in wave pw, Delta) of the chunk starting at step t0; rows of
 // pieces that start at or past Q are not loaded.
-template <int N>
-__device__ __forceinline__ void load_x_rows(const Views& v, int Q, int t0, ChunkRows<N>& cr, int pw) {
+template <int N, int QM>
+__device__ __forceinline__ void load_x_rows(const Views& v, int Q, int t0, ChunkRows<N, QM>& cr, int pw) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int k = 0; k < ChunkRows<N>::XQ; ++k) {
+    for (int k = 0; k < ChunkRows<N, QM>::XQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
         if (k * kThreads / (kP / 8) < Q) cr.xv[k] = ld_buf16(v.x, (uint32_t)(t0 + r) * v.xrow + v.xh + 2 * c8);
@@ -277,11 +277,11 @@ __device__ __forceinline__ void load_x_rows(const Views& v, int Q, int t0, Chunk
     }
 }
 
-template <int N>
-__device__ __forceinline__ void load_b_rows(const Views& v, int Q, int t0, ChunkRows<N>& cr) {
+template <int N, int QM>
+__device__ __forceinline__ void load_b_rows(const Views& v, int Q, int t0, ChunkRows<N, QM>& cr) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int k = 0; k < ChunkRows<N>::BQ; ++k) {
+    for (int k = 0; k < ChunkRows<N, QM>::BQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
         if (k * kThreads / (N / 8) < Q) cr.bv[k] = ld_buf16(v.bm, (uint32_t)((t0 + r) * N + c8) * 2);
@@ -289,19 +289,19 @@ __device__ __forceinline__ void load_b_rows(const Views& v, int Q, int t0, Chunk
 }
 
 // x and B rows of a chunk from registers into LDS (rows >= len hold zeros)
-template <int N>
-__device__ __forceinline__ void store_xb(lds_t* lds, const Smem& sm, int Q, const ChunkRows<N>& cr) {
+template <int N, int QM>
+__device__ __forceinline__ void store_xb(lds_t* lds, const Smem& sm, int Q, const ChunkRows<N, QM>& cr) {
     const int tid = threadIdx.x;
     lds_u16* xs = reinterpret_cast<lds_u16*>(lds + sm.xs);
     lds_u16* bs = reinterpret_cast<lds_u16*>(lds + sm.bs);
 #pragma unroll
-    for (int k = 0; k < ChunkRows<N>::XQ; ++k) {
+    for (int k = 0; k < ChunkRows<N, QM>::XQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (kP / 8), c8 = (q % (kP / 8)) * 8;
         if (k * kThreads / (kP / 8) < Q && r < Q) *reinterpret_cast<lds_u32x4*>(xs + r * kXS + c8) = cr.xv[k];
     }
 #pragma unroll
-    for (int k = 0; k < ChunkRows<N>::BQ; ++k) {
+    for (int k = 0; k < ChunkRows<N, QM>::BQ; ++k) {
         const int q = tid + k * kThreads;
         const int r = q / (N / 8), c8 = (q % (N / 8)) * 8;
         if (k * kThreads / (N / 8) < Q && r < Q) *reinterpret_cast<lds_u32x4*>(bs + r * (N + kPad) + c8) = cr.bv[k];
@@ -857,7 +857,10 @@ __device__ __forceinline__ void run_item(const Views& v, const lds_t* lds, const
     else out_item<N, 1, HAS_Z, HAS_D>(v, lds, sm, Q, sb, t0, len, I, pb0, cop, Dh);
 }
 
-template <int N, bool HAS_Z, bool HAS_D>
+// QM: the longest chunk the launch may have (64 or kMaxQ): it sizes the registers that
+// carry the next chunk's x and B rows. With QM = 64 they are few enough to be loaded
+// before the output phase, which then hides their latency.
+template <int N, bool HAS_Z, bool HAS_D, int QM>
 __global__ void __launch_bounds__(kThreads)
 ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -892,16 +895,16 @@ ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
             }
     }
     const Views v = make_views<N>(a, b, h);
-    ChunkRows<N> cr;
+    ChunkRows<N, QM> cr;
     bf16x8 cop[N / 16];
     {
         const int len0 = min(geo.Q, a.L - c0 * geo.Q);
-        load_x_rows<N>(v, geo.Q, c0 * geo.Q, cr, PW);
-        load_b_rows<N>(v, geo.Q, c0 * geo.Q, cr);
+        load_x_rows<N, QM>(v, geo.Q, c0 * geo.Q, cr, PW);
+        load_b_rows<N, QM>(v, geo.Q, c0 * geo.Q, cr);
         if (N0 > 0) load_c<N>(v, c0 * geo.Q, I0, cop);
         state_to_lds<N>(lds, sm, hs);
         if (wave == PW) chunk_prefix(lds, sm, geo.Q, 0, len0, A2, cr.dv);
-        store_xb<N>(lds, sm, geo.Q, cr);
+        store_xb<N, QM>(lds, sm, geo.Q, cr);
     }
     const bool last_super = (k == geo.K - 1);
     for (int cc = c0; cc < c1; ++cc) {
@@ -910,13 +913,18 @@ ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
         const int len = min(geo.Q, a.L - t0);
         const int ln = cc + 1 < c1 ? min(geo.Q, a.L - t0 - geo.Q) : 0;
         __syncthreads();  // rows, prefix and state copy of this chunk visible
-        if (ln > 0) load_x_rows<N>(v, geo.Q, t0 + geo.Q, cr, PW);
+        if (ln > 0) {
+            load_x_rows<N, QM>(v, geo.Q, t0 + geo.Q, cr, PW);
+            if constexpr (QM <= 64) load_b_rows<N, QM>(v, geo.Q, t0 + geo.Q, cr);
+        }
         if (N0 > 0 && 32 * I0 < len) run_item<N, HAS_Z, HAS_D>(v, lds, sm, geo.Q, sb, t0, len, I0, P0, N0, cop, Dh);
         if (N1 > 0 && 32 * I1 < len) {
             load_c<N>(v, t0, I1, cop);
             run_item<N, HAS_Z, HAS_D>(v, lds, sm, geo.Q, sb, t0, len, I1, P1, N1, cop, Dh);
         }
-        if (ln > 0) load_b_rows<N>(v, geo.Q, t0 + geo.Q, cr);
+        if constexpr (QM > 64) {
+            if (ln > 0) load_b_rows<N, QM>(v, geo.Q, t0 + geo.Q, cr);
+        }
         // state after the chunk (not needed after the last chunk of a super-chunk,
         // except at the very end of the sequence for h_final)
         const bool need_state = (cc < c1 - 1) || (last_super && a.h_final != nullptr);
@@ -932,7 +940,7 @@ ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
         __syncthreads();  // every read of this chunk's rows and state copy done
         if (ln > 0) {
             state_to_lds<N>(lds, sm, hs);
-            store_xb<N>(lds, sm, geo.Q, cr);
+            store_xb<N, QM>(lds, sm, geo.Q, cr);
         }
     }
     if (last_super && a.h_final != nullptr) {
@@ -950,6 +958,15 @@ ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
 __global__ void copy_state_ssd(const float* __restrict__ h0, float* __restrict__ out, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) out[i] = h0 ? h0[i] : 0.0f;
+}
+
+template <int N, int QM>
+void launch_scan(const SsdArgs& a, const SsdGeom& geo, const OutPlan& plan, const Smem& sm, dim3 grid, bool hz,
+                 bool hd, hipStream_t st) {
+    if (hz && hd) launch((ssd_chunk_scan<N, true, true, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hz) launch((ssd_chunk_scan<N, true, false, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hd) launch((ssd_chunk_scan<N, false, true, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else launch((ssd_chunk_scan<N, false, false, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
 }
 
 template <int N>
@@ -973,10 +990,8 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     const dim3 grid((unsigned)(geo.K * a.H * a.B));
-    if (hz && hd) launch((ssd_chunk_scan<N, true, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else if (hz) launch((ssd_chunk_scan<N, true, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else if (hd) launch((ssd_chunk_scan<N, false, true>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else launch((ssd_chunk_scan<N, false, false>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    if (geo.Q <= 64) launch_scan<N, 64>(a, geo, plan, sm, grid, hz, hd, st);
+    else launch_scan<N, kMaxQ>(a, geo, plan, sm, grid, hz, hd, st);
     return hipGetLastError();
 }
 
