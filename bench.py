@@ -330,11 +330,11 @@ def alu_figures(counts, names, kmean_ms, t_call_ms, updates, trans_cost):
 
 
 def scan_kernel_names(nk, wl):
-    if nk == 3:
-        return ["segment_aggregate", "group_carry", "segment_final"]
+    if nk == 3:  # N = 64, 128: the chunked final pass finishes y itself
+        return ["segment_aggregate", "group_carry", "segment_final_sink" if wl["N"] >= 64 else "segment_final"]
     if nk == 2:
         return ["segment_aggregate", "segment_final"]
-    if nk == 4:  # N >= 64: the final pass sums C . h in LDS, then a combine pass
+    if nk == 4:  # N = 256: two groups of state chunks, their sums added by a combine pass
         return ["segment_aggregate", "group_carry", "segment_final_sink", "combine_partials"]
     return ["segment_final"] if nk == 1 else [f"kernel{i}" for i in range(nk)]
 

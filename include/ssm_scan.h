@@ -127,7 +127,8 @@ int ssm_profile_events(void* const* events, int n);
  *                    bytes (NULL allowed when that size is 0); contents on entry
  *                    are ignored and on return are undefined.
  * Supported: N in {4, 8, 16, 32, 64, 128, 256}; B, D >= 1; L >= 0 (L = 0 writes
- * h_final = h0). N >= 64 needs a workspace whenever L > 0 (it holds the C . h sums).
+ * h_final = h0). N = 256 needs a workspace whenever L > 0 (it holds the C . h sums
+ * of its two groups of state chunks).
  * Every pointer must be 16-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t ssm_scan_workspace_size(int B, int L, int D, int N);

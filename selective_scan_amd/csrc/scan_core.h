@@ -585,12 +585,15 @@ segment_final(ScanArgs a, Geom g) {
 // kSinkChunks state chunks) holds those chunks of the segment, one wave each. Every
 // kPrefetch steps the waves leave their partial C . h sums in LDS (two slots,
 // alternating), meet at a barrier, and the workgroup adds them in chunk order into
-// one fp32 sum per (t, channel), written to its chunk group's plane of YP;
-// combine_partials then adds the planes, D x and the gate.
+// one fp32 sum per (t, channel). FUSE (one chunk group, N <= 128): the workgroup
+// holds every state chunk, so it finishes y itself (D x, the gate, the rounding);
+// otherwise the sums go to the group's plane of YP and combine_partials adds the
+// planes, D x and the gate.
 constexpr int kSinkChunks = 8;
 inline int sink_planes(int N) { return std::max(1, n_chunks(N) / kSinkChunks); }
+static_assert(64 / kChunkN >= kPrefetch, "a fused sink needs a wave per step of the ring");
 
-template <bool BF16, int V = 0>
+template <bool BF16, int V = 0, bool FUSE = false>
 __global__ void __launch_bounds__(64 * kSinkChunks)
 segment_final_sink(ScanArgs a, Geom g) {
     extern __shared__ float lds[];
@@ -610,7 +613,7 @@ segment_final_sink(ScanArgs a, Geom g) {
     const int len = min(g.Ls, a.L - t0);
     const WsLayout wl = ws_layout(a.B, D, NT, g.S, g.G);
     const float* ws = static_cast<const float*>(a.ws);
-    float* yp = static_cast<float*>(a.ws) + wl.YP + (size_t)cg * a.B * a.L * D;
+    float* yp = FUSE ? nullptr : static_cast<float*>(a.ws) + wl.YP + (size_t)cg * a.B * a.L * D;
 
     Segment<N, BF16, false, false, true, V, true> seg(a, b, dc, t0, len, n0, d < D);
     float A2[N], hg[N], E[N];
@@ -644,19 +647,45 @@ segment_final_sink(ScanArgs a, Geom g) {
     float unused = 0.0f;
     VarLane<N, V> vl;
     var_lane_init<N, V>(vl, a, dc, n0);
+    // FUSE: wave w finishes step tb + w of its lane's channel; its x and z are
+    // loaded when the block of steps starts, so the loads overlap the block.
+    const bool has_d = FUSE && a.Dskip != nullptr, has_z = FUSE && a.z != nullptr;
+    const float Dv = has_d ? a.Dskip[dc] : 0.0f;
+    const size_t row0 = (size_t)b * a.L + t0;
+    float xr = 0.0f, zr = 0.0f;
+    auto fetch_xz = [&](int tb) {
+        const size_t i = (row0 + min(tb + wave, len - 1)) * D + dc;
+        if (has_d) xr = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.x)[i]) : static_cast<const float*>(a.x)[i];
+        if (has_z) zr = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a.z)[i]) : static_cast<const float*>(a.z)[i];
+    };
     // the sums of the steps [tb, tb + cnt) from LDS slot `slot`, in chunk order
     auto reduce = [&](int slot, int tb, int cnt) {
         const float* base = lds + (size_t)slot * nch * kPrefetch * 64;
-        for (int o = threadIdx.x; o < cnt * 64; o += nch * 64) {
-            const int k = o >> 6, l = o & 63, dd = dblk * 64 + l;
-            float v = 0.0f;
-            for (int c = 0; c < nch; ++c) v += base[(c * kPrefetch + k) * 64 + l];
-            if (dd < D) yp[((size_t)b * a.L + t0 + tb + k) * D + dd] = v;
+        if constexpr (FUSE) {
+            if (wave < cnt) {
+                float v = 0.0f;
+                for (int c = 0; c < nch; ++c) v += base[(c * kPrefetch + wave) * 64 + lane];
+                if (has_d) v = __builtin_fmaf(Dv, xr, v);
+                if (has_z) v *= silu(zr);
+                const size_t i = (row0 + tb + wave) * D + d;
+                if (d < D) {
+                    if constexpr (BF16) static_cast<uint16_t*>(a.y)[i] = f32_to_bf16(v);
+                    else static_cast<float*>(a.y)[i] = v;
+                }
+            }
+        } else {
+            for (int o = threadIdx.x; o < cnt * 64; o += nch * 64) {
+                const int k = o >> 6, l = o & 63, dd = dblk * 64 + l;
+                float v = 0.0f;
+                for (int c = 0; c < nch; ++c) v += base[(c * kPrefetch + k) * 64 + l];
+                if (dd < D) yp[(row0 + tb + k) * D + dd] = v;
+            }
         }
     };
     int t = 0, j = 0;
     for (; t + kPrefetch <= len; t += kPrefetch, ++j) {
         seg.lsink = lds + ((size_t)(j & 1) * nch + wave) * kPrefetch * 64;
+        if constexpr (FUSE) fetch_xz(t);
 #pragma unroll
         for (int k = 0; k < kPrefetch; ++k) seg.template step<true>(t + k, k, A2, h, 0.0f, unused, vl);
         __syncthreads();
@@ -664,6 +693,7 @@ segment_final_sink(ScanArgs a, Geom g) {
     }
     if (t < len) {
         seg.lsink = lds + ((size_t)(j & 1) * nch + wave) * kPrefetch * 64;
+        if constexpr (FUSE) fetch_xz(t);
 #pragma unroll
         for (int k = 0; k < kPrefetch - 1; ++k)
             if (t + k < len) seg.template step<false>(t + k, k, A2, h, 0.0f, unused, vl);
@@ -713,14 +743,19 @@ combine_partials(ScanArgs a, const float* __restrict__ yp, int nch) {
     else static_cast<float*>(a.y)[i] = v;
 }
 
-// N >= 64, after the aggregate and carry passes: the state chunks' final pass
-// into the planes of partial sums, then their sum with D x and the gate.
+// N >= 64, after the aggregate and carry passes: the state chunks' final pass,
+// finishing y itself when one workgroup holds every chunk, else into the planes
+// of partial sums, then their sum with D x and the gate.
 template <bool BF16, int V>
 void launch_sink(const ScanArgs& a, const Geom& g, hipStream_t st) {
     const int nch = a.N / kChunkN;
     const int planes = sink_planes(a.N), cpw = nch / planes;
     const dim3 sgrid((unsigned)g.S, (unsigned)(((a.D + 63) / 64) * planes), (unsigned)a.B);
     const size_t lds_sink = (size_t)2 * cpw * kPrefetch * 64 * sizeof(float);
+    if (planes == 1) {
+        launch((segment_final_sink<BF16, V, true>), sgrid, dim3(64 * cpw), (uint32_t)lds_sink, st, a, g);
+        return;
+    }
     launch((segment_final_sink<BF16, V>), sgrid, dim3(64 * cpw), (uint32_t)lds_sink, st, a, g);
     const float* yp = static_cast<const float*>(a.ws) + ws_layout(a.B, a.D, a.N, g.S, g.G).YP;
     const size_t tot = (size_t)a.B * a.L * a.D;
