@@ -597,6 +597,9 @@ bwd_final(BwdArgs a, BGeom g) {
         // state lives in LDS too (read once per block)
         float* lhe = lds + wave * N * 64;
         float* lhin = lds + W * (N + 1) * 64 + wave * N * 64;
+        // the state entering a block's later half (after its replay), read back by
+        // that half's first backward step
+        float* lhh = lds + W * (2 * N + 1) * 64 + wave * N * 64;
 #pragma unroll
         for (int n = 0; n < N; ++n) lhin[n * 64 + lane] = hin[n];
 
@@ -704,6 +707,10 @@ bwd_final(BwdArgs a, BGeom g) {
 #pragma unroll
                     for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(dlk * A2[n]), h[n], u * Bt.at(n));
                 }
+                if (half > 0) {
+#pragma unroll
+                    for (int n = 0; n < N; ++n) lhh[n * 64 + lane] = h[n];
+                }
                 // forward over the half: keep its states; dz, dD and dC
                 float hs[KR][N], dv[KR];
 #pragma unroll
@@ -765,13 +772,16 @@ bwd_final(BwdArgs a, BGeom g) {
 #pragma unroll
                     for (int n = 0; n < N; ++n) {
                         const float gg = __builtin_fmaf(dv[kk], Ct.at(n), c[n]);  // dl/dh_t
-                        const float ah = __builtin_fmaf(-u, Bt.at(n), hs[kk][n]);  // a_t h_{t-1}
-                        const float q = gg * ah;
+                        // a_t h_{t-1} from h_{t-1} itself: recovering it as h_t - Delta_t B_t x_t
+                        // would cancel where the decay is strong
+                        const float at = exp2_fast(dl[k] * A2[n]);
+                        const float hp = kk > 0 ? hs[kk - 1][n] : (half > 0 ? lhh : lhe)[n * 64 + lane];
+                        const float q = gg * (at * hp);
                         sA = __builtin_fmaf(q, A2[n], sA);
                         dA[n] = __builtin_fmaf(q, dl[k], dA[n]);
                         sB = __builtin_fmaf(gg, Bt.at(n), sB);
                         w[n] = gg * um;
-                        c[n] = exp2_fast(dl[k] * A2[n]) * gg;
+                        c[n] = at * gg;
                     }
                     const float ddv = __builtin_fmaf(sA, kLn2, xv[k] * sB);
                     if constexpr (CH) {
@@ -978,7 +988,7 @@ hipError_t launch_n(const BwdArgs& a, hipStream_t st) {
     const dim3 grid(g.G, ((a.D + 63) / 64) * (NT / N), a.B);
     const dim3 block(64 * g.W);
     const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
-    const size_t lds_fin = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
+    const size_t lds_fin = (size_t)g.W * (3 * N + 1) * 64 * sizeof(float);
     float* ws = static_cast<float*>(a.ws);
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, NT, g);
     if (g.S > 1 || g.nsub > 1) {
