@@ -179,3 +179,115 @@ def test_scan_bwd_full_decay(shape):
     for k in ("dx", "ddelta", "dz", "dBm", "dCm", "dD", "dh0"):
         compare(out_f64(g[k]), r[k], st if k in ("dx", "ddelta", "dz", "dBm", "dCm") else "f32", what=f"dt_big {k}")
     assert float(np.abs(out_f64(g["dA"]) - r["dA"]).max()) <= 1e-3 * scale
+
+
+# ---------------------------------------------------------------- the other paths
+
+@pytest.mark.parametrize("kind", ("A0", "dt0_all", "dt_big", "x0"))
+def test_ssd_step_degenerate_inputs(kind):
+    """Mamba-2 decode chained in place: no decay, identity steps (the state bit for
+    bit), full decay, zero input."""
+    B, H, N, steps = 2, 3, 128, 20
+    print(f"[degenerate ssd step] {kind}", flush=True)
+    w = si.ssd_step_inputs(B, H, 64, N, steps, dtype=si.BF16, seed=26, with_D=True, with_z=True)
+    dl = si.to_f64(w["delta"])
+    if kind == "A0":
+        w["A"] = np.zeros_like(w["A"])
+    elif kind == "dt0_all":
+        w["delta"] = si.store(np.zeros_like(dl), si.BF16)
+    elif kind == "dt_big":
+        w["delta"] = si.store(np.full_like(dl, 40.0), si.BF16)
+    else:
+        w["x"] = si.store(np.zeros_like(si.to_f64(w["x"])), si.BF16)
+    st_g = torch.from_numpy(w["state0"]).to(DEV)
+    st_o = w["state0"].astype(np.float64)
+    A, Dk = torch.from_numpy(w["A"]).to(DEV), torch.from_numpy(w["D"]).to(DEV)
+    for s in range(steps):
+        tok = {k: w[k][s] for k in ("x", "delta", "z", "Bm", "Cm")}
+        td = {k: si.to_torch(np.ascontiguousarray(v), DEV) for k, v in tok.items()}
+        y = ssa.ssm_ssd_step(st_g, td["x"], td["delta"], A, td["Bm"], td["Cm"], D=Dk, z=td["z"])
+        yo, st_o = oracle.ssd_step(st_o, si.to_f64(tok["x"]), si.to_f64(tok["delta"]), w["A"].astype(np.float64),
+                                   si.to_f64(tok["Bm"]), si.to_f64(tok["Cm"]), D=w["D"].astype(np.float64),
+                                   z=si.to_f64(tok["z"]))
+        torch.cuda.synchronize()
+        compare(out_f64(y), yo, "bf16", what=f"{kind} step {s} y")
+    compare(st_g.cpu().numpy(), st_o, "f32", what=f"{kind} state")
+    if kind == "dt0_all":
+        np.testing.assert_array_equal(st_g.cpu().numpy(), w["state0"])
+
+
+@pytest.mark.parametrize("case", [
+    # kind, disc, softplus, N
+    ("dt_big", "zoh", False, 16), ("dt_big", "zoh", False, 64), ("dt0_run", "zoh", False, 16),
+    ("A0", "zoh", False, 16), ("raw_pos", "zoh", True, 16), ("raw_neg", "zoh", True, 64),
+    ("raw_pos", "euler", True, 16), ("raw_neg", "euler", True, 16),
+], ids=lambda c: "{}_{}_sp{}_N{}".format(*c))
+def test_scan_variant_degenerate_inputs(case):
+    """The discretisation variants at the extremes: zero-order hold under full decay
+    (e^z - 1 -> -1), identity steps and A = 0 (its limit Delta), and softplus(delta +
+    bias) of raw values around +-80 (Delta ~ 75, or ~ e^-85 where only the series holds)."""
+    from test_gpu_scan_var import _run
+    kind, disc, sp, N = case
+    print(f"[degenerate variant] {case}", flush=True)
+    B, L, D = 2, 300, 70
+    w = si.scan_inputs(B, L, D, N, dtype=si.BF16, seed=27, with_h0=True)
+    bias = None
+    if kind in ("raw_pos", "raw_neg"):
+        r = si.scan_raw_delta(B, L, D, dtype=si.BF16, seed=27)
+        raw = si.to_f64(r["delta"])
+        raw[:, L // 4: L // 2] = 80.0 if kind == "raw_pos" else -80.0
+        w["delta"], bias = si.store(raw, si.BF16), r["delta_bias"]
+    else:
+        w = _degenerate(w, kind)
+    (y, hf), (yr, hr) = _run(w, bias, disc, sp)
+    compare(out_f64(y), yr, "bf16", what=f"{case} y")
+    compare(out_f64(hf), hr, "f32", what=f"{case} h_final")
+
+
+def _mamba3_degenerate(w, kind):
+    dl = si.to_f64(w["delta"])
+    L = dl.shape[1]
+    if kind == "theta_big":  # up to tens of radians per step, many turns per segment
+        w["theta"] = np.random.default_rng(28).uniform(-200.0, 200.0, w["theta"].shape).astype(np.float32)
+    elif kind == "Are0":     # |alpha| = 1: rotation only
+        w["Are"] = np.zeros_like(w["Are"])
+    elif kind in ("lam0", "lam1"):
+        w["lam"] = si.store(np.full_like(si.to_f64(w["lam"]), 0.0 if kind == "lam0" else 1.0), w["dtype"])
+    elif kind == "dt0_run":
+        dl = dl.copy()
+        dl[:, L // 5: (3 * L) // 5] = 0.0
+        w["delta"] = si.store(dl, w["dtype"])
+    elif kind == "dt_big":
+        w["delta"] = si.store(np.full_like(dl, 40.0), w["dtype"])
+    else:
+        raise ValueError(kind)
+    return w
+
+
+@pytest.mark.parametrize("kind", ("theta_big", "Are0", "lam0", "lam1", "dt0_run", "dt_big"))
+def test_scan3_degenerate_inputs(kind):
+    """Mamba-3 scan: phases of many turns, no magnitude decay, the two ends of the
+    trapezoid weight, identity steps and full decay, across segments with a ragged tail."""
+    from test_gpu_scan3 import gpu_scan3, oracle_scan3
+    print(f"[degenerate scan3] {kind}", flush=True)
+    w = _mamba3_degenerate(si.scan3_inputs(2, 700, 96, 16, dtype=si.BF16, seed=28, with_h0=True, with_prev=True),
+                           kind)
+    y, hf = gpu_scan3(w)
+    yr, hr = oracle_scan3(w)
+    compare(out_f64(y), yr, "bf16", what=f"{kind} y")
+    compare(out_f64(hf), hr, "f32", what=f"{kind} h_final")
+
+
+@pytest.mark.parametrize("kind", ("theta_big", "Are0", "lam0", "dt_big"))
+def test_step3_degenerate_inputs(kind):
+    """Mamba-3 decode chained over 30 tokens against the oracle's scan over them."""
+    from test_gpu_scan3 import oracle_scan3
+    from test_gpu_step3 import _start, gpu_steps
+    print(f"[degenerate step3] {kind}", flush=True)
+    w = _mamba3_degenerate(si.scan3_inputs(2, 30, 70, 16, dtype=si.BF16, seed=29, with_h0=True, with_prev=True),
+                           kind)
+    st, prev = _start(w)
+    y = gpu_steps(w, 0, 30, st, prev)
+    yr, hr = oracle_scan3(w)
+    compare(out_f64(y), yr, "bf16", what=f"{kind} y")
+    compare(st.cpu().numpy().astype(np.float64), hr, "f32", what=f"{kind} state")
