@@ -65,6 +65,11 @@ def test_scan_workspace_checks():
     assert _scan(L=4096, D=1536, ws=P, wsb=need - 1) == 3
     assert ssa.ssm_scan_workspace_size(1, 4096, 1536, 12) == 0
     assert ssa.ssm_scan_workspace_size(1, 32, 64, 16) == 0  # a single segment needs none
+    # N = 64, 128: one workgroup holds every state chunk and finishes y itself, so a
+    # single segment needs none either; N = 256 sums two chunk groups through the workspace
+    assert ssa.ssm_scan_workspace_size(1, 32, 64, 64) == 0
+    assert ssa.ssm_scan_workspace_size(1, 32, 64, 128) == 0
+    assert ssa.ssm_scan_workspace_size(1, 32, 64, 256) > 0
 
 
 def test_step_rejects_bad_arguments():
