@@ -113,6 +113,7 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 
 struct SsdGeom {
     int Q;    // chunk length
+    int Qp;   // chunk length rounded up to the 32-row blocks the kernels tile by
     int C;    // chunks per sequence
     int cps;  // chunks per super-chunk
     int K;    // super-chunks per sequence
@@ -121,6 +122,7 @@ struct SsdGeom {
 SsdGeom ssd_geom(int B, int L, int H, int Q) {
     SsdGeom g;
     g.Q = Q;
+    g.Qp = (Q + 31) / 32 * 32;
     g.C = L > 0 ? (L + Q - 1) / Q : 0;
     const long bh = (long)B * H;
     long K = (kTargetBlocks + bh - 1) / bh;
@@ -737,7 +739,7 @@ __device__ __forceinline__ void load_c(const Views& v, int t0, int I, bf16x8 (&c
 // Outputs of one 32-row block I of a chunk for NPB 32-column blocks of p from pb0.
 // Lane l: hf = l / 32, c = l % 32. MFMA 32x32x16 layouts: A operand A[c][8 hf + e],
 // B operand B[8 hf + e][c], accumulator element r at row 8(r/4) + 4 hf + r%4, column c.
-template <int N, int NPB, bool HAS_Z, bool HAS_D>
+template <int N, int NPB, bool HAS_Z, bool HAS_D, bool PAD>
 __device__ __forceinline__ void out_item(const Views& v, const lds_t* lds, const Smem& sm, int Q, int sb,
                                          int t0, int len, int I, int pb0, const bf16x8 (&cop)[N / 16], float Dh) {
     const int lane = threadIdx.x & 63;
@@ -822,7 +824,9 @@ __device__ __forceinline__ void out_item(const Views& v, const lds_t* lds, const
         }
     }
     // epilogue: rows 32 I + 8 (r/4) + 4 hf + r % 4, columns p = 32 (pb0 + q) + c;
-    // rows past the sequence end fall outside the y view and are dropped
+    // rows past the sequence end fall outside the y view and are dropped; PAD (a
+    // chunk that is not a whole number of blocks): rows at or past the chunk's
+    // length, the next chunk's, are not stored
     const uint32_t off0 = (uint32_t)(t0 + 32 * I + 4 * hf) * v.xrow + v.xh + 2 * (32 * pb0 + c);
     // the gate's z values are all loaded before the first y store (a load issued
     // after a store would also wait for that store)
@@ -844,28 +848,34 @@ __device__ __forceinline__ void out_item(const Views& v, const lds_t* lds, const
             float val = acc[q][r];
             if constexpr (HAS_D) val = __builtin_fmaf(Dh, bf16_to_f32(xs[row * kXS + 32 * (pb0 + q) + c]), val);
             if constexpr (HAS_Z) val *= silu(bf16_to_f32(zr[q][r]));
-            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), v.y, (int)(off + 64 * q), 0, 0);
+            if (!PAD || row < len)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), v.y, (int)(off + 64 * q), 0, 0);
         }
     }
     (void)len;
 }
 
-template <int N, bool HAS_Z, bool HAS_D>
+template <int N, bool HAS_Z, bool HAS_D, bool PAD>
 __device__ __forceinline__ void run_item(const Views& v, const lds_t* lds, const Smem& sm, int Q, int sb, int t0,
                                          int len, int I, int pb0, int npb, const bf16x8 (&cop)[N / 16], float Dh) {
-    if (npb == 2) out_item<N, 2, HAS_Z, HAS_D>(v, lds, sm, Q, sb, t0, len, I, pb0, cop, Dh);
-    else out_item<N, 1, HAS_Z, HAS_D>(v, lds, sm, Q, sb, t0, len, I, pb0, cop, Dh);
+    if (npb == 2) out_item<N, 2, HAS_Z, HAS_D, PAD>(v, lds, sm, Q, sb, t0, len, I, pb0, cop, Dh);
+    else out_item<N, 1, HAS_Z, HAS_D, PAD>(v, lds, sm, Q, sb, t0, len, I, pb0, cop, Dh);
 }
 
 // QM: the longest chunk the launch may have (64 or kMaxQ): it sizes the registers that
 // carry the next chunk's x and B rows. With QM = 64 they are few enough to be loaded
-// before the output phase, which then hides their latency.
-template <int N, bool HAS_Z, bool HAS_D, int QM>
+// before the output phase, which then hides their latency. PAD: the chunk length is
+// not a multiple of 32 (its tiles then span the next multiple).
+template <int N, bool HAS_Z, bool HAS_D, int QM, bool PAD>
 __global__ void __launch_bounds__(kThreads)
 ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
     extern __shared__ __attribute__((aligned(16))) char lds_raw[];
     lds_t* lds = (lds_t*)lds_raw;
-    const Smem sm = smem_layout<N>(geo.Q);
+    // tiles, LDS rows and prefix arrays span Qp rows; chunks start every Q steps.
+    // Rows of a chunk at or past its length (the next chunk's, or past the
+    // sequence) enter with zero weight and their outputs are not stored.
+    const int Q = geo.Q, Qp = PAD ? geo.Qp : geo.Q;
+    const Smem sm = smem_layout<N>(Qp);
     int h, k, b;
     block_coords(a.H, geo.K, h, k, b);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -898,49 +908,49 @@ ssd_chunk_scan(SsdArgs a, SsdGeom geo, OutPlan plan) {
     ChunkRows<N, QM> cr;
     bf16x8 cop[N / 16];
     {
-        const int len0 = min(geo.Q, a.L - c0 * geo.Q);
-        load_x_rows<N, QM>(v, geo.Q, c0 * geo.Q, cr, PW);
-        load_b_rows<N, QM>(v, geo.Q, c0 * geo.Q, cr);
-        if (N0 > 0) load_c<N>(v, c0 * geo.Q, I0, cop);
+        const int len0 = min(Q, a.L - c0 * Q);
+        load_x_rows<N, QM>(v, Qp, c0 * Q, cr, PW);
+        load_b_rows<N, QM>(v, Qp, c0 * Q, cr);
+        if (N0 > 0) load_c<N>(v, c0 * Q, I0, cop);
         state_to_lds<N>(lds, sm, hs);
-        if (wave == PW) chunk_prefix(lds, sm, geo.Q, 0, len0, A2, cr.dv);
-        store_xb<N, QM>(lds, sm, geo.Q, cr);
+        if (wave == PW) chunk_prefix(lds, sm, Qp, 0, len0, A2, cr.dv);
+        store_xb<N, QM>(lds, sm, Qp, cr);
     }
     const bool last_super = (k == geo.K - 1);
     for (int cc = c0; cc < c1; ++cc) {
         const int sb = (cc - c0) & 1;
-        const int t0 = cc * geo.Q;
-        const int len = min(geo.Q, a.L - t0);
-        const int ln = cc + 1 < c1 ? min(geo.Q, a.L - t0 - geo.Q) : 0;
+        const int t0 = cc * Q;
+        const int len = min(Q, a.L - t0);
+        const int ln = cc + 1 < c1 ? min(Q, a.L - t0 - Q) : 0;
         __syncthreads();  // rows, prefix and state copy of this chunk visible
         if (ln > 0) {
-            load_x_rows<N, QM>(v, geo.Q, t0 + geo.Q, cr, PW);
-            if constexpr (QM <= 64) load_b_rows<N, QM>(v, geo.Q, t0 + geo.Q, cr);
+            load_x_rows<N, QM>(v, Qp, t0 + Q, cr, PW);
+            if constexpr (QM <= 64) load_b_rows<N, QM>(v, Qp, t0 + Q, cr);
         }
-        if (N0 > 0 && 32 * I0 < len) run_item<N, HAS_Z, HAS_D>(v, lds, sm, geo.Q, sb, t0, len, I0, P0, N0, cop, Dh);
+        if (N0 > 0 && 32 * I0 < len) run_item<N, HAS_Z, HAS_D, PAD>(v, lds, sm, Qp, sb, t0, len, I0, P0, N0, cop, Dh);
         if (N1 > 0 && 32 * I1 < len) {
             load_c<N>(v, t0, I1, cop);
-            run_item<N, HAS_Z, HAS_D>(v, lds, sm, geo.Q, sb, t0, len, I1, P1, N1, cop, Dh);
+            run_item<N, HAS_Z, HAS_D, PAD>(v, lds, sm, Qp, sb, t0, len, I1, P1, N1, cop, Dh);
         }
         if constexpr (QM > 64) {
-            if (ln > 0) load_b_rows<N, QM>(v, geo.Q, t0 + geo.Q, cr);
+            if (ln > 0) load_b_rows<N, QM>(v, Qp, t0 + Q, cr);
         }
         // state after the chunk (not needed after the last chunk of a super-chunk,
         // except at the very end of the sequence for h_final)
         const bool need_state = (cc < c1 - 1) || (last_super && a.h_final != nullptr);
         if (need_state) {
             StateTiles<N> st;
-            chunk_state<N>(lds, sm, geo.Q, sb, len, st);
+            chunk_state<N>(lds, sm, Qp, sb, len, st);
             state_update<N>(lds, sm, sb, hs, st);
         }
         if (ln > 0) {
-            if (wave == PW) chunk_prefix(lds, sm, geo.Q, sb ^ 1, ln, A2, cr.dv);
-            if (N0 > 0) load_c<N>(v, t0 + geo.Q, I0, cop);
+            if (wave == PW) chunk_prefix(lds, sm, Qp, sb ^ 1, ln, A2, cr.dv);
+            if (N0 > 0) load_c<N>(v, t0 + Q, I0, cop);
         }
         __syncthreads();  // every read of this chunk's rows and state copy done
         if (ln > 0) {
             state_to_lds<N>(lds, sm, hs);
-            store_xb<N, QM>(lds, sm, geo.Q, cr);
+            store_xb<N, QM>(lds, sm, Qp, cr);
         }
     }
     if (last_super && a.h_final != nullptr) {
@@ -960,13 +970,13 @@ __global__ void copy_state_ssd(const float* __restrict__ h0, float* __restrict__
     if (i < n) out[i] = h0 ? h0[i] : 0.0f;
 }
 
-template <int N, int QM>
+template <int N, int QM, bool PAD>
 void launch_scan(const SsdArgs& a, const SsdGeom& geo, const OutPlan& plan, const Smem& sm, dim3 grid, bool hz,
                  bool hd, hipStream_t st) {
-    if (hz && hd) launch((ssd_chunk_scan<N, true, true, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else if (hz) launch((ssd_chunk_scan<N, true, false, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else if (hd) launch((ssd_chunk_scan<N, false, true, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
-    else launch((ssd_chunk_scan<N, false, false, QM>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    if (hz && hd) launch((ssd_chunk_scan<N, true, true, QM, PAD>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hz) launch((ssd_chunk_scan<N, true, false, QM, PAD>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else if (hd) launch((ssd_chunk_scan<N, false, true, QM, PAD>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
+    else launch((ssd_chunk_scan<N, false, false, QM, PAD>), grid, dim3(kThreads), sm.total, st, a, geo, plan);
 }
 
 template <int N>
@@ -980,8 +990,8 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
         return hipGetLastError();
     }
     const SsdGeom geo = ssd_geom(a.B, a.L, a.H, a.Q);
-    const Smem sm = smem_layout<N>(geo.Q);
-    const OutPlan plan = out_plan(geo.Q / 32, N);
+    const Smem sm = smem_layout<N>(geo.Qp);
+    const OutPlan plan = out_plan(geo.Qp / 32, N);
     if (geo.K > 1) {
         launch((ssd_state_agg<N>), dim3((unsigned)((geo.K - 1) * a.H * a.B)), dim3(kAggThreads), 0, st, a,
                geo);
@@ -990,8 +1000,14 @@ hipError_t launch_n(const SsdArgs& a, hipStream_t st) {
     }
     const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     const dim3 grid((unsigned)(geo.K * a.H * a.B));
-    if (geo.Q <= 64) launch_scan<N, 64>(a, geo, plan, sm, grid, hz, hd, st);
-    else launch_scan<N, kMaxQ>(a, geo, plan, sm, grid, hz, hd, st);
+    const bool pad = geo.Qp != geo.Q;
+    if (geo.Qp <= 64) {
+        if (pad) launch_scan<N, 64, true>(a, geo, plan, sm, grid, hz, hd, st);
+        else launch_scan<N, 64, false>(a, geo, plan, sm, grid, hz, hd, st);
+    } else {
+        if (pad) launch_scan<N, kMaxQ, true>(a, geo, plan, sm, grid, hz, hd, st);
+        else launch_scan<N, kMaxQ, false>(a, geo, plan, sm, grid, hz, hd, st);
+    }
     return hipGetLastError();
 }
 
@@ -1001,7 +1017,7 @@ const char* ssd_unsupported_reason(int L, int H, int P, int N, int Q, bool bf16)
     if (!bf16) return "SSD supports bf16 I/O only";
     if (P != kP) return "SSD supports head dim P = 64 only";
     if (N != 64 && N != 128) return "SSD supports N = 64 or 128";
-    if (Q < 32 || Q > kMaxQ || Q % 32 != 0) return "SSD chunk must be a multiple of 32 in [32, 256]";
+    if (Q < 1 || Q > kMaxQ) return "SSD chunk must be in [1, 256]";
     if (H > 65535) return "H must be <= 65535";
     if (L < 0) return "L must be >= 0";
     if ((long long)L * H * P * 2 > 0x7fffffffLL) return "L * H * P * 2 must be < 2^31 (bytes of one batch row of x)";

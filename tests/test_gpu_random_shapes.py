@@ -24,6 +24,9 @@ def _flags(rng, k):
 SSD_CASES = _draw(12, 2024, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 2500)), int(r.integers(1, 5)),
                                        int(r.choice([64, 128])), int(r.choice([32, 64, 96, 128, 160, 192, 224, 256])))
                   + _flags(r, 3))
+# chunk lengths anywhere in [1, 256], mostly not multiples of 32
+SSD_ANY_CHUNK = _draw(8, 2027, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 1500)), int(r.integers(1, 4)),
+                                          int(r.choice([64, 128])), int(r.integers(1, 257))) + _flags(r, 3))
 BWD_CASES = _draw(10, 2025, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 3000)), int(r.integers(1, 300)),
                                        int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)))
                   + _flags(r, 4))
@@ -38,6 +41,15 @@ def test_ssd_random_shapes(case):
     B, L, H, N, Q, wd, wz, wh = case
     print(f"[ssd random] {case}", flush=True)
     w = si.ssd_inputs(B, L, H, 64, N, dtype=si.BF16, seed=L, with_D=wd, with_z=wz, with_h0=wh)
+    T._check(w, Q, what=str(case))
+
+
+@pytest.mark.parametrize("case", SSD_ANY_CHUNK, ids=lambda c: "B{}_L{}_H{}_N{}_Q{}_D{}z{}h{}".format(*c))
+def test_ssd_random_chunk_lengths(case):
+    import test_gpu_ssd as T
+    B, L, H, N, Q, wd, wz, wh = case
+    print(f"[ssd random chunk] {case}", flush=True)
+    w = si.ssd_inputs(B, L, H, 64, N, dtype=si.BF16, seed=L + 7, with_D=wd, with_z=wz, with_h0=wh)
     T._check(w, Q, what=str(case))
 
 

@@ -59,6 +59,15 @@ SMALL = [
     (1, 800, 2, 128, 192, True, True, True),
     (2, 700, 1, 64, 224, False, True, True),
     (1, 650, 2, 128, 160, True, False, True),
+    # chunks that are not a multiple of 32: tiled as the next multiple, the rows
+    # past a chunk's end (the next chunk's) masked
+    (1, 300, 2, 128, 1, True, True, True),
+    (2, 257, 2, 64, 7, True, False, True),
+    (1, 90, 1, 64, 33, False, True, False),
+    (1, 500, 3, 128, 50, True, True, True),
+    (1, 1000, 2, 64, 100, True, True, False),
+    (2, 700, 2, 128, 200, False, True, True),
+    (1, 513, 2, 128, 255, True, True, True),
 ]
 
 
