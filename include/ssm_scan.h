@@ -333,10 +333,12 @@ int ssm_scan_bwd(int B, int L, int D, int N, ssm_dtype_t io,
  *   h_final : [B, H, N, P]  fp32 out, or NULL
  *   chunk   : chunk length Q >= 1 (0 = default 256). The last chunk is ragged
  *             when Q does not divide L. The result does not depend on Q beyond
- *             rounding.
- * Supported: io = SSM_BF16; N in {64, 128}; P = 64; chunk in [1, 256] (the
- * kernels tile a chunk by 32 rows, so a chunk that is not a multiple of 32 costs
- * the work of the next multiple); B, H <= 65535; B * H <= 2^24; L * H * P * 2 < 2^31.
+ *             rounding; chunks above 256 steps run as 256-step chunks (one
+ *             chunk's rows must fit a workgroup's LDS). The kernels tile a chunk
+ *             by 32 rows, so a chunk that is not a multiple of 32 costs the work
+ *             of the next multiple.
+ * Supported: io = SSM_BF16; N in {64, 128}; P = 64; B, H <= 65535;
+ * B * H <= 2^24; L * H * P * 2 < 2^31.
  * ------------------------------------------------------------------------- */
 size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk);
 

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <limits>
@@ -162,6 +163,12 @@ int step_impl(const char* fn, int B, int D, int N, int io, int disc, const float
     const hipStream_t st = static_cast<hipStream_t>(stream);
     return hip_status(variant ? ssm::launch_step_var(a, st) : ssm::launch_step(a, st), fn);
 }
+
+// The SSD chunk length the kernels run: 256 by default; chunks above 256 steps (one
+// chunk's rows must fit a workgroup's LDS) run as 256-step chunks. The chunked form
+// computes the same recurrence whatever its chunk length; only the rounding follows
+// the chunking.
+int ssd_chunk(int chunk) { return chunk == 0 ? 256 : std::min(chunk, 256); }
 
 }  // namespace
 
@@ -329,7 +336,7 @@ int ssm_scan_bwd(int B, int L, int D, int N, ssm_dtype_t io,
 
 // ------------------------------------------------------------------ SSD
 size_t ssm_ssd_workspace_size(int B, int L, int H, int P, int N, int chunk) {
-    const int Q = chunk == 0 ? 256 : chunk;
+    const int Q = ssd_chunk(chunk);
     if (B < 1 || L < 0 || H < 1 || P < 1 || N < 1 || Q < 1) return 0;
     if (!product_ok({B, L, H, P}) || !product_ok({B, H, N, P})) return 0;
     return ssm::ssd_workspace_bytes(B, L, H, P, N, Q);
@@ -345,7 +352,7 @@ int ssm_ssd_fwd(int B, int L, int H, int P, int N, int chunk, ssm_dtype_t io,
     if (B < 1 || H < 1 || P < 1 || N < 1 || L < 0 || chunk < 0)
         return fail(SSM_ERR_INVALID_ARG, fn, "B, H, P, N must be >= 1, L >= 0, chunk >= 0");
     if (io != SSM_F32 && io != SSM_BF16) return fail(SSM_ERR_INVALID_ARG, fn, "io must be SSM_F32 or SSM_BF16");
-    const int Q = chunk == 0 ? 256 : chunk;
+    const int Q = ssd_chunk(chunk);
     const char* why = ssm::ssd_unsupported_reason(L, H, P, N, Q, io == SSM_BF16);
     if (why[0] != '\0') return fail(SSM_ERR_UNSUPPORTED, fn, why);
     if (B > 65535) return fail(SSM_ERR_UNSUPPORTED, fn, "B must be <= 65535");

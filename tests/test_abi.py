@@ -117,8 +117,6 @@ def test_ssd_rejects_bad_arguments():
     assert call(io=0) == 2          # fp32 I/O not built for SSD
     assert call(Pp=32) == 2
     assert call(N=96) == 2
-    assert call(chunk=257) == 2     # chunks of 1 .. 256 steps
-    assert call(chunk=512) == 2
     assert call(B=70000) == 2
 
 

@@ -68,6 +68,9 @@ SMALL = [
     (1, 1000, 2, 64, 100, True, True, False),
     (2, 700, 2, 128, 200, False, True, True),
     (1, 513, 2, 128, 255, True, True, True),
+    # chunks above 256 steps run as 256-step chunks (the same recurrence)
+    (1, 700, 2, 128, 300, True, True, True),
+    (2, 1100, 1, 64, 512, False, True, True),
 ]
 
 
