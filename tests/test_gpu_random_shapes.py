@@ -1,7 +1,8 @@
-"""GPU parity on shapes drawn at random (fixed seed) beside the hand-picked ones:
-the SSD forward (chunk lengths, head counts, ragged tails, super-chunk splits),
-the scan's backward pass and the scan with its discretisation options, each
-against the fp64 oracle on the same stored inputs."""
+"""GPU parity on shapes drawn at random (fixed seeds) beside the hand-picked ones:
+the scan, the SSD forward (chunk lengths, head counts, ragged tails, super-chunk
+splits), the scan's backward pass, the scan with its discretisation options, the
+Mamba-3 scan, and chains of the three decode steps, each against the fp64 oracle
+on the same stored inputs."""
 import numpy as np
 import pytest
 
@@ -21,16 +22,16 @@ def _flags(rng, k):
     return tuple(bool(rng.integers(0, 2)) for _ in range(k))
 
 
-SSD_CASES = _draw(12, 2024, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 2500)), int(r.integers(1, 5)),
+SSD_CASES = _draw(30, 2024, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 2500)), int(r.integers(1, 5)),
                                        int(r.choice([64, 128])), int(r.choice([32, 64, 96, 128, 160, 192, 224, 256])))
                   + _flags(r, 3))
 # chunk lengths anywhere in [1, 256], mostly not multiples of 32
-SSD_ANY_CHUNK = _draw(8, 2027, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 1500)), int(r.integers(1, 4)),
+SSD_ANY_CHUNK = _draw(24, 2027, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 1500)), int(r.integers(1, 4)),
                                           int(r.choice([64, 128])), int(r.integers(1, 257))) + _flags(r, 3))
-BWD_CASES = _draw(10, 2025, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 3000)), int(r.integers(1, 300)),
+BWD_CASES = _draw(30, 2025, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 3000)), int(r.integers(1, 300)),
                                        int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)))
                   + _flags(r, 4))
-VAR_CASES = _draw(8, 2026, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 2000)), int(r.integers(1, 200)),
+VAR_CASES = _draw(24, 2026, lambda r: (int(r.integers(1, 3)), int(r.integers(1, 2000)), int(r.integers(1, 200)),
                                       int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)),
                                       str(r.choice(["euler", "zoh"])), bool(r.integers(0, 2))))
 
@@ -81,12 +82,12 @@ def test_scan_variant_random_shapes(case):
     compare(out_f64(hf), hr, "f32", what=f"{case} h_final")
 
 
-SCAN_CASES = _draw(10, 2027, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 5000)), int(r.integers(1, 400)),
+SCAN_CASES = _draw(40, 2027, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 5000)), int(r.integers(1, 400)),
                                         int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)))
                    + _flags(r, 3))
-SCAN3_CASES = _draw(8, 2028, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 3000)), int(r.integers(1, 300)),
+SCAN3_CASES = _draw(20, 2028, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 3000)), int(r.integers(1, 300)),
                                         int(r.choice([4, 8, 16])), bool(r.integers(0, 2))) + _flags(r, 4))
-STEP3_CASES = _draw(6, 2029, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 40)), int(r.integers(1, 300)),
+STEP3_CASES = _draw(12, 2029, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 40)), int(r.integers(1, 300)),
                                         int(r.choice([4, 8, 16, 32, 64, 128])), bool(r.integers(0, 2))))
 
 
@@ -120,3 +121,30 @@ def test_step3_random_chains(case):
     yr, hr = T3.oracle_scan3(w)
     compare(out_f64(y), yr, storage(w), what=f"{case} y")
     compare(out_f64(st), hr, "f32", what=f"{case} state")
+
+
+STEP_CASES = _draw(12, 2030, lambda r: (int(r.integers(1, 5)), int(r.integers(1, 400)),
+                                        int(r.choice([4, 8, 16, 32, 64, 128, 256])), bool(r.integers(0, 2)))
+                   + _flags(r, 2))
+SSD_STEP_CASES = _draw(10, 2031, lambda r: (int(r.integers(1, 4)), int(r.integers(1, 6)),
+                                            int(r.choice([16, 32, 64, 128, 256])), bool(r.integers(0, 2)))
+                       + _flags(r, 2))
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "B{}_D{}_N{}_bf{}_D{}z{}".format(*c))
+def test_step_random_chains(case):
+    """Eight chained Mamba-1 decode steps in place against the oracle's steps."""
+    import test_gpu_step as ST
+    B, D, N, bf, wd, wz = case
+    print(f"[step random] {case}", flush=True)
+    ST._run_steps(si.step_inputs(B, D, N, 8, dtype=si.BF16 if bf else si.F32, seed=D, with_D=wd, with_z=wz), 8)
+
+
+@pytest.mark.parametrize("case", SSD_STEP_CASES, ids=lambda c: "B{}_H{}_N{}_bf{}_D{}z{}".format(*c))
+def test_ssd_step_random_chains(case):
+    """Six chained Mamba-2 decode steps in place against the oracle's steps."""
+    import test_gpu_ssd_step as SST
+    B, H, N, bf, wd, wz = case
+    print(f"[ssd step random] {case}", flush=True)
+    SST._run_steps(si.ssd_step_inputs(B, H, 64, N, 6, dtype=si.BF16 if bf else si.F32, seed=H + 3, with_D=wd,
+                                      with_z=wz), 6)
