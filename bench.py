@@ -892,12 +892,13 @@ def streaming_floor(st0, steps, reps=3):
 
 
 def valu_rates(dev, blocks=8192, iters=2048):
-    """The VALU issue-rate probes: exp-only, fma-only and 1:3 chains, full occupancy."""
+    """The VALU issue-rate probes: exp-only, fma-only, 1:3, sin-only and cos-only
+    chains, full occupancy."""
     import torch
     import selective_scan_amd as ssa
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     res = {}
-    for mode, nm in ((0, "exp"), (1, "fma"), (2, "exp1_fma3")):
+    for mode, nm in ((0, "exp"), (1, "fma"), (2, "exp1_fma3"), (3, "sin"), (4, "cos")):
         ssa.ssm_diag_valu_rate(mode, out, 16)
         sync()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -910,6 +911,8 @@ def valu_rates(dev, blocks=8192, iters=2048):
     fma, ex = res["fma"]["ops_per_s"], res["exp"]["ops_per_s"]
     mix = res["exp1_fma3"]["ops_per_s"]
     res["exp_cost_in_fma_slots"] = fma / ex
+    res["sin_cost_in_fma_slots"] = fma / res["sin"]["ops_per_s"]
+    res["cos_cost_in_fma_slots"] = fma / res["cos"]["ops_per_s"]
     # if exp and fma shared one issue port with costs c_e and 1, a 1:3 mix would run at
     # 4 / (c_e + 3) of the fma rate; co-issue would show as a faster mix
     res["mix_predicted_no_coissue_ops_per_s"] = 4.0 * fma / (fma / ex + 3.0)

@@ -406,9 +406,9 @@ int ssm_ssd_step(int B, int H, int P, int N, ssm_dtype_t io,
  *
  * ssm_diag_valu_rate: `blocks` workgroups of 256 lanes, each lane running 8
  *   independent chains for `iters` rounds of 4 dependent ops: mode 0 v_exp_f32
- *   only, mode 1 v_fma_f32 only, mode 2 one v_exp_f32 per three v_fma_f32 (so
- *   blocks * 256 * 32 * iters ops in all). out: blocks * 256 floats (a sum per
- *   lane, so nothing is optimised away).
+ *   only, mode 1 v_fma_f32 only, mode 2 one v_exp_f32 per three v_fma_f32, mode 3
+ *   v_sin_f32 only, mode 4 v_cos_f32 only (so blocks * 256 * 32 * iters ops in
+ *   all). out: blocks * 256 floats (a sum per lane, so nothing is optimised away).
  * ssm_diag_stream_scale: p[i] *= s for i < n, in place (n a multiple of 4): what a
  *   kernel that only reads and writes an array of the decode state's size reaches.
  * ssm_diag_copy: dst[i] = src[i] (n a multiple of 4): the byte reference that

@@ -414,7 +414,7 @@ int ssm_ssd_step(int B, int H, int P, int N, ssm_dtype_t io,
 // ------------------------------------------------------------------ diagnostics
 int ssm_diag_valu_rate(int mode, int blocks, int iters, float* out, void* stream) {
     const char* fn = "ssm_diag_valu_rate";
-    if (mode < 0 || mode > 2) return fail(SSM_ERR_INVALID_ARG, fn, "mode must be 0, 1 or 2");
+    if (mode < 0 || mode > 4) return fail(SSM_ERR_INVALID_ARG, fn, "mode must be 0 .. 4");
     if (blocks < 1 || blocks > (1 << 20) || iters < 0) return fail(SSM_ERR_INVALID_ARG, fn, "bad blocks or iters");
     if (!out || !aligned16(out)) return fail(SSM_ERR_INVALID_ARG, fn, "out is NULL or not 16-byte aligned");
     return hip_status(ssm::launch_valu_rate(mode, blocks, iters, out, static_cast<hipStream_t>(stream)), fn);

@@ -1,7 +1,8 @@
 // Diagnostic kernels for the benchmark (not part of the scan itself):
-//  - VALU issue-rate probes: long chains of v_exp_f32 only, of v_fma_f32 only, and
-//    of one v_exp_f32 per three v_fma_f32, so the bench can measure what the
-//    transcendental unit costs relative to an FMA on the chip it runs on;
+//  - VALU issue-rate probes: long chains of v_exp_f32 only, of v_fma_f32 only, of
+//    one v_exp_f32 per three v_fma_f32, of v_sin_f32 only and of v_cos_f32 only, so
+//    the bench can measure what the transcendental unit costs relative to an FMA on
+//    the chip it runs on;
 //  - an in-place scale of an fp32 array, the pure-streaming floor a decode step
 //    (read the state, write it back) is compared with;
 //  - a plain device copy, the reference that scales the HBM byte counters and the
@@ -19,9 +20,11 @@ namespace {
 
 constexpr int kChains = 8;  // independent dependency chains per lane
 
-// MODE 0: exp only, 1: fma only, 2: one exp per three fma. Every chain stays in
-// [0.5, 1] (2^-x of x in [0.5, 1]; the fma contracts towards 0.75), so no special
-// value ever enters the pipes. `iters` rounds of kChains x 4 ops per lane.
+// MODE 0: exp only, 1: fma only, 2: one exp per three fma, 3: v_sin_f32 only,
+// 4: v_cos_f32 only. Modes 0-2 keep every chain in [0.5, 1] (2^-x of x in [0.5, 1];
+// the fma contracts towards 0.75), modes 3 and 4 in [-1, 1] (the argument is in
+// revolutions), so no special value ever enters the pipes. `iters` rounds of
+// kChains x 4 ops per lane.
 template <int MODE>
 __global__ void __launch_bounds__(256) valu_rate(float* out, int iters) {
     float v[kChains];
@@ -36,6 +39,10 @@ __global__ void __launch_bounds__(256) valu_rate(float* out, int iters) {
                     v[c] = __builtin_amdgcn_exp2f(-v[c]);
                 } else if constexpr (MODE == 1) {
                     v[c] = __builtin_fmaf(v[c], 0.5f, 0.375f);
+                } else if constexpr (MODE == 3) {
+                    v[c] = __builtin_amdgcn_sinf(v[c]);
+                } else if constexpr (MODE == 4) {
+                    v[c] = __builtin_amdgcn_cosf(v[c]);
                 } else {
                     if (r == 3) v[c] = __builtin_amdgcn_exp2f(-v[c]);
                     else v[c] = __builtin_fmaf(v[c], 0.5f, 0.375f);
@@ -95,7 +102,9 @@ hipError_t launch_valu_rate(int mode, int blocks, int iters, float* out, hipStre
     const dim3 g(blocks), b(256);
     if (mode == 0) launch(valu_rate<0>, g, b, 0, st, out, iters);
     else if (mode == 1) launch(valu_rate<1>, g, b, 0, st, out, iters);
-    else launch(valu_rate<2>, g, b, 0, st, out, iters);
+    else if (mode == 2) launch(valu_rate<2>, g, b, 0, st, out, iters);
+    else if (mode == 3) launch(valu_rate<3>, g, b, 0, st, out, iters);
+    else launch(valu_rate<4>, g, b, 0, st, out, iters);
     return hipGetLastError();
 }
 

@@ -176,7 +176,11 @@ __device__ __forceinline__ void walk3(const Scan3Args& a, int b, int d, int dc, 
 
 template <int N, bool BF16>
 __global__ void __launch_bounds__(64 * kW3) seg_agg3(Scan3Args a, Geom3 g) {
-    __shared__ float sPr[kW3][N][64], sPi[kW3][N][64], sHr[kW3][N][64], sHi[kW3][N][64], sS[kW3][64];
+    // Each wave's end state and sum of Delta go through LDS; its decay
+    // exp(sum Delta (Are + i theta)) is recomputed by the waves that need it (the same
+    // lane holds the same channel's Are and theta), which halves the LDS a workgroup
+    // takes (33 KB) and lets three workgroups share a CU instead of two.
+    __shared__ float sHr[kW3][N][64], sHi[kW3][N][64], sS[kW3][64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = blockIdx.x, b = blockIdx.z;
     const int D = a.D;
@@ -196,7 +200,6 @@ __global__ void __launch_bounds__(64 * kW3) seg_agg3(Scan3Args a, Geom3 g) {
     if (len > 0) walk3<N, BF16, false>(a, b, d, dc, t0, len, A2, th, hr, hi, 0.0f, sumd);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        cdecay(sumd, A2[n], th[n], sPr[wave][n][lane], sPi[wave][n][lane]);
         sHr[wave][n][lane] = hr[n];
         sHi[wave][n][lane] = hi[n];
     }
@@ -208,15 +211,17 @@ __global__ void __launch_bounds__(64 * kW3) seg_agg3(Scan3Args a, Geom3 g) {
     for (int n = 0; n < N; ++n) er[n] = ei[n] = 0.0f;
     float cs = 0.0f;
     for (int j = 0; j < wave; ++j) {
+        const float sj = sS[j][lane];
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const float pr = sPr[j][n][lane], pi = sPi[j][n][lane];
+            float pr, pi;
+            cdecay(sj, A2[n], th[n], pr, pi);
             const float nr = pr * er[n] - pi * ei[n] + sHr[j][n][lane];
             const float ni = pr * ei[n] + pi * er[n] + sHi[j][n][lane];
             er[n] = nr;
             ei[n] = ni;
         }
-        cs += sS[j][lane];
+        cs += sj;
     }
     if (d >= D || s >= g.S) return;
     const Ws3 wl = ws3(a.B, D, N, g.S, g.G);
@@ -235,7 +240,8 @@ __global__ void __launch_bounds__(64 * kW3) seg_agg3(Scan3Args a, Geom3 g) {
         float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + grp) * 2 * N * D + d;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            const float pr = sPr[wave][n][lane], pi = sPi[wave][n][lane];
+            float pr, pi;
+            cdecay(sumd, A2[n], th[n], pr, pi);
             GH[(size_t)n * D] = pr * er[n] - pi * ei[n] + hr[n];
             GH[(size_t)(N + n) * D] = pr * ei[n] + pi * er[n] + hi[n];
         }

@@ -424,7 +424,7 @@ def ssm_step3(state, x, delta, lam, Are, theta, Bm, Cm, D=None, z=None, x_prev=N
 
 # ------------------------------------------------------------------ diagnostics
 def ssm_diag_valu_rate(mode, out, iters, stream=None):
-    """VALU issue-rate probe (mode 0 exp, 1 fma, 2 exp:fma 1:3); ``out`` is an fp32
+    """VALU issue-rate probe (mode 0 exp, 1 fma, 2 exp:fma 1:3, 3 sin, 4 cos); ``out`` is an fp32
     tensor of blocks * 256 elements. Returns the number of ops it issues."""
     blocks = out.numel() // 256
     st = lib().ssm_diag_valu_rate(int(mode), blocks, int(iters), _ptr(out), _stream(out.device, stream))

@@ -24,13 +24,15 @@ def test_diag_copy_and_scale(n):
 
 
 def test_diag_valu_rate_probe_values():
-    """The probes' chains stay in [0.5, 1] and the three modes compute what they say:
+    """The probes' chains stay in range ([0.5, 1], the sin and cos chains in [-1, 1]) and
+    the modes compute what they say:
     the fma chain's fixed point is 0.75; the outputs are finite."""
     out = torch.empty(2 * 256, dtype=torch.float32, device=DEV)
-    for mode in (0, 1, 2):
+    for mode in (0, 1, 2, 3, 4):
         ssa.ssm_diag_valu_rate(mode, out, 64)
         torch.cuda.synchronize()
         v = out / 8.0  # each lane sums its 8 chains
-        assert torch.isfinite(out).all() and bool((v >= 0.5).all()) and bool((v <= 1.0).all()), mode
+        lo = -1.0 if mode >= 3 else 0.5  # the sin and cos chains live in [-1, 1]
+        assert torch.isfinite(out).all() and bool((v >= lo).all()) and bool((v <= 1.0).all()), mode
         if mode == 1:
             assert torch.allclose(v, torch.full_like(v, 0.75), atol=1e-6)
