@@ -416,15 +416,14 @@ segment_aggregate(ScanArgs a, Geom g) {
         Segment<N, BF16, false, false, false, V> seg(a, b, dc, t0, len, n0);
         seg.run(A2, h, 0.0f, sumd, vl);
     }
-    // LDS: P[w][n][lane], H[w][n][lane], SD[w][lane]; a segment past L is the identity (1, 0).
-    float* sP = lds;
-    float* sH = sP + W * N * 64;
+    // LDS: H[w][n][lane], SD[w][lane]; a segment past L is the identity (sum 0, H 0).
+    // A segment's decay exp2(A2 sum Delta) is recomputed by the waves that need it
+    // (the same lane holds the same channel's A), so only H and the sum go through
+    // LDS: less LDS per workgroup, more workgroups per CU.
+    float* sH = lds;
     float* sS = sH + W * N * 64;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        sP[(wave * N + n) * 64 + lane] = exp2_fast(A2[n] * sumd);
-        sH[(wave * N + n) * 64 + lane] = h[n];
-    }
+    for (int n = 0; n < N; ++n) sH[(wave * N + n) * 64 + lane] = h[n];
     sS[wave * 64 + lane] = sumd;
     __syncthreads();
 
@@ -433,10 +432,11 @@ segment_aggregate(ScanArgs a, Geom g) {
     for (int n = 0; n < N; ++n) E[n] = 0.0f;
     float cs = 0.0f;
     for (int j = 0; j < wave; ++j) {
+        const float sj = sS[j * 64 + lane];
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            E[n] = __builtin_fmaf(sP[(j * N + n) * 64 + lane], E[n], sH[(j * N + n) * 64 + lane]);
-        cs += sS[j * 64 + lane];
+            E[n] = __builtin_fmaf(exp2_fast(A2[n] * sj), E[n], sH[(j * N + n) * 64 + lane]);
+        cs += sj;
     }
     if (d >= D || s >= g.S) return;
     const WsLayout wl = ws_layout(a.B, D, NT, g.S, g.G);
@@ -454,7 +454,7 @@ segment_aggregate(ScanArgs a, Geom g) {
         float* GP = ws + wl.GP + (((size_t)b * (g.G - 1) + grp) * NT + n0) * D + d;
 #pragma unroll
         for (int n = 0; n < N; ++n) {
-            GH[(size_t)n * D] = __builtin_fmaf(sP[(wave * N + n) * 64 + lane], E[n], h[n]);
+            GH[(size_t)n * D] = __builtin_fmaf(exp2_fast(A2[n] * sumd), E[n], h[n]);
             GP[(size_t)n * D] = exp2_fast(A2[n] * (cs + sumd));
         }
     }
@@ -783,7 +783,7 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
     const int nch = a.N / N;
     const dim3 grid(g.G, ((a.D + 63) / 64) * nch, a.B);
     const dim3 block(64 * g.W);
-    const size_t lds_agg = (size_t)g.W * (2 * N + 1) * 64 * sizeof(float);
+    const size_t lds_agg = (size_t)g.W * (N + 1) * 64 * sizeof(float);
     if (g.S > 1) launch((segment_aggregate<N, BF16, V>), grid, block, lds_agg, st, a, g);
     if (g.G > 1) {
         launch(group_carry, dim3((unsigned)((a.D + 63) / 64), (unsigned)a.N, (unsigned)a.B), dim3(256), 0, st,
