@@ -301,12 +301,14 @@ def one_pass_slots(trans_cost):
     return FMA_OPS_PER_UPDATE + trans_cost
 
 
-def alu_figures(counts, names, kmean_ms, t_call_ms, updates, trans_cost):
+def alu_figures(counts, names, kmean_ms, t_call_ms, updates, trans_cost, one_pass=None, one_pass_note=None):
     """VALU issue per kernel and for the call from committed instruction counts: a
     wave instruction is 64 lane-slots, a transcendental one `trans_cost` times that
-    (its issue rate relative to an FMA, measured by the VALU-rate probes)."""
+    (its issue rate relative to an FMA, measured by the VALU-rate probes). one_pass:
+    the minimal single-pass mix in lane-slots per update (default: the Mamba-1 one)."""
     if counts is None:
         return None
+    one = one_pass if one_pass is not None else one_pass_slots(trans_cost)
     per, tot = {}, 0.0
     for nm, t in zip(names, kmean_ms):
         if nm not in counts:
@@ -320,13 +322,13 @@ def alu_figures(counts, names, kmean_ms, t_call_ms, updates, trans_cost):
     return dict(peak_tslot_s=LANE_SLOTS_PER_S / 1e12, trans_cost_slots=trans_cost, kernels=per,
                 call_slots_per_update=tot / updates,
                 call_issue_frac=tot / (t_call_ms * 1e-3) / LANE_SLOTS_PER_S,
-                model_slots_per_update_one_pass=one_pass_slots(trans_cost),
-                call_frac_of_one_pass_ceiling=one_pass_slots(trans_cost) * updates / (t_call_ms * 1e-3)
-                / LANE_SLOTS_PER_S,
+                model_slots_per_update_one_pass=one,
+                call_frac_of_one_pass_ceiling=one * updates / (t_call_ms * 1e-3) / LANE_SLOTS_PER_S,
                 note="lane-slots = 64 x (VALU instructions + (trans_cost - 1) x transcendental ones), from "
                      "rocprofv3 SQ_INSTS_VALU / SQ_INSTS_VALU_TRANS_F32 per launch; issue_frac = slots over "
                      "kernel time x 256 CU x 128 FMA lanes x 2.4 GHz; call_frac_of_one_pass_ceiling = the "
-                     "minimal single-pass mix (4 FMA-class ops + one exp per update) over the call's time")
+                     "minimal single-pass mix (%s) over the call's time"
+                     % (one_pass_note or "4 FMA-class ops + one exp per update"))
 
 
 def scan_kernel_names(nk, wl):
@@ -526,7 +528,10 @@ def scan3_bench(name, wl, steps, warmup, dev, max_sets=16, trans_cost=DEFAULT_TR
                 hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, sets=len(sets), alg_bytes=alg,
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
                               slots_per_update=slots, traffic=committed_traffic("scan3", f"traffic_{name}.md"),
-                              kernel="seg_final3 (dominant)"))
+                              kernel="seg_final3 (dominant)"),
+                alu=alu_figures(committed_valu("scan3", f"valu_{name}.md"), ["seg_agg3", "carry3", "seg_final3"],
+                                kmean, ms, upd, trans_cost, one_pass=slots,
+                                one_pass_note="11 FMA-class ops, one exp, one sin and one cos per update"))
 
 
 # ------------------------------------------------------------------ scan backward
