@@ -478,7 +478,10 @@ def scan_var_bench(name, wl, steps, warmup, dev, max_sets=16, trans_cost=DEFAULT
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
                               traffic=committed_traffic("scan_var", f"traffic_{name}.md"),
                               kernel=("segment_final_sink" if N >= 64 else "segment_final")
-                              + " (zero-order hold, softplus(delta + bias))"))
+                              + " (zero-order hold, softplus(delta + bias))"),
+                alu=alu_figures(committed_valu("scan_var", f"valu_{name}.md"), scan_kernel_names(nk, wl), kmean,
+                                ms, upd, trans_cost, one_pass=ZOH_FMA_OPS_PER_UPDATE + trans_cost,
+                                one_pass_note="the fast zero-order-hold form: 6 FMA-class ops and one exp per update"))
 
 
 # ------------------------------------------------------------------ Mamba-3 scan
@@ -589,7 +592,21 @@ def scan_bwd_bench(name, wl, steps, warmup, dev, max_sets=8, trans_cost=DEFAULT_
                 sets=len(sets), alg_bytes=alg,
                 roofline=dict(bound="alu", achieved=achieved, peak=peak, unit="Tslot/s", frac=achieved / peak,
                               traffic=committed_traffic("scan_bwd", f"traffic_{name}.md"),
-                              kernel="bwd_final"))
+                              kernel="bwd_final"),
+                alu=alu_figures(committed_valu("scan_bwd", f"valu_{name}.md"), bwd_kernel_names(nk), kmean, ms,
+                                upd, trans_cost, one_pass=BWD_FMA_OPS_PER_UPDATE + BWD_EXPS_PER_UPDATE * trans_cost,
+                                one_pass_note="the final pass's 16 FMA-class ops and two exps per update"))
+
+
+def bwd_kernel_names(nk):
+    """The backward call's launches in order (N >= 32 adds the chunk-sum combine)."""
+    base = ["bwd_aggregate", "bwd_carry_state", "bwd_carry_adjoint", "bwd_final"]
+    tail = ["bwd_reduce_params", "bwd_reduce_rows"]
+    if nk == 7:
+        return base + ["bwd_combine"] + tail
+    if nk == 6:
+        return base + tail
+    return [f"kernel{i}" for i in range(nk)]
 
 
 # ------------------------------------------------------------------ SSD
