@@ -581,6 +581,88 @@ segment_final(ScanArgs a, Geom g) {
     }
 }
 
+// A short chain (2 .. kFusedSegs segments, N <= 32): one workgroup of one wave per
+// segment runs the whole call. Each wave runs its segment from a zero state, the
+// waves meet in LDS for the exclusive prefix of the earlier segments (their end
+// states and sums of Delta; decays recomputed from the sums), and each wave runs its
+// segment again from its entering state, writing y. One launch, no workspace.
+constexpr int kFusedSegs = 8;
+
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, int V = 0>
+__global__ void __launch_bounds__(64 * kFusedSegs)
+segment_fused(ScanArgs a, Geom g) {
+    extern __shared__ float lds[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int b = blockIdx.z, D = a.D;
+    const int d = blockIdx.y * 64 + lane;
+    const int dc = d < D ? d : D - 1;
+    const int s = wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
+
+    float A2[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.A[(size_t)dc * N + n] * kLog2e;
+        h[n] = 0.0f;
+    }
+    VarLane<N, V> vl;
+    var_lane_init<N, V>(vl, a, dc, 0);
+    float sumd = 0.0f;
+    if (len > 0) {
+        Segment<N, BF16, false, false, false, V> seg(a, b, dc, t0, len, 0);
+        seg.run(A2, h, 0.0f, sumd, vl);
+    }
+    float* sH = lds;
+    float* sS = sH + kFusedSegs * N * 64;
+#pragma unroll
+    for (int n = 0; n < N; ++n) sH[(wave * N + n) * 64 + lane] = h[n];
+    sS[wave * 64 + lane] = sumd;
+    __syncthreads();
+    if (len == 0) return;
+    // entering state: exp2(A2 * prefix sum Delta) h0 + the earlier segments' composite
+    float E[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) E[n] = 0.0f;
+    float cs = 0.0f;
+    for (int j = 0; j < wave; ++j) {
+        const float sj = sS[j * 64 + lane];
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            E[n] = __builtin_fmaf(exp2_fast(A2[n] * sj), E[n], sH[(j * N + n) * 64 + lane]);
+        cs += sj;
+    }
+    if (a.h0 != nullptr) {
+        const float* hp = a.h0 + ((size_t)b * D + dc) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = __builtin_fmaf(exp2_fast(A2[n] * cs), hp[n], E[n]);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) h[n] = E[n];
+    }
+    const float Dv = (HAS_D && (V == 0 || a.Dskip != nullptr)) ? a.Dskip[dc] : 0.0f;
+    float unused = 0.0f;
+    Segment<N, BF16, HAS_Z, HAS_D, true, V> seg(a, b, dc, t0, len, 0, d < D);
+    seg.run(A2, h, Dv, unused, vl);
+    if (d < D && s == g.S - 1 && a.h_final != nullptr) {
+        float* hp = a.h_final + ((size_t)b * D + d) * N;
+#pragma unroll
+        for (int n = 0; n < N; ++n) hp[n] = h[n];
+    }
+}
+
+// A chain of 2 .. kFusedSegs segments with a single chunk of states runs as one
+// launch when its waves get a SIMD each (at most four segments) or when the call has
+// enough chains to put two or more waves on every SIMD anyway: with few chains, five to
+// eight segments in one workgroup would share SIMDs that the separate launches spread
+// over two CUs (B1 L256 D64: 24 -> 26 us), while a batch of short sequences gains
+// (B64 L256 D1536: 178 -> 131-153 us).
+inline bool fused_call(const Geom& g, int B, int D, int N) {
+    if (g.S <= 1 || g.S > kFusedSegs || n_chunks(N) != 1) return false;
+    const long waves = (long)B * ((D + 63) / 64) * g.S;
+    return g.S <= 4 || waves >= 2048;
+}
+
 // N >= 64: one workgroup per (segment, 64 channels, batch, group of up to
 // kSinkChunks state chunks) holds those chunks of the segment, one wave each. Every
 // kPrefetch steps the waves leave their partial C . h sums in LDS (two slots,
@@ -781,6 +863,21 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
         return hipGetLastError();
     }
     const int nch = a.N / N;
+    const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
+    if (fused_call(g, a.B, a.D, a.N)) {
+        const dim3 fgrid(1, (a.D + 63) / 64, a.B), fblock(64 * g.S);
+        const size_t lds_f = (size_t)kFusedSegs * (N + 1) * 64 * sizeof(float);
+        if constexpr (V != 0) {
+            if (hz) launch((segment_fused<N, BF16, true, true, V>), fgrid, fblock, lds_f, st, a, g);
+            else launch((segment_fused<N, BF16, false, true, V>), fgrid, fblock, lds_f, st, a, g);
+        } else {
+            if (hz && hd) launch((segment_fused<N, BF16, true, true>), fgrid, fblock, lds_f, st, a, g);
+            else if (hz) launch((segment_fused<N, BF16, true, false>), fgrid, fblock, lds_f, st, a, g);
+            else if (hd) launch((segment_fused<N, BF16, false, true>), fgrid, fblock, lds_f, st, a, g);
+            else launch((segment_fused<N, BF16, false, false>), fgrid, fblock, lds_f, st, a, g);
+        }
+        return hipGetLastError();
+    }
     const dim3 grid(g.G, ((a.D + 63) / 64) * nch, a.B);
     const dim3 block(64 * g.W);
     const size_t lds_agg = (size_t)g.W * (N + 1) * 64 * sizeof(float);
@@ -793,7 +890,6 @@ hipError_t launch_n(const ScanArgs& a, hipStream_t st) {
         launch_sink<BF16, V>(a, g, st);
         return hipGetLastError();
     }
-    const bool hz = a.z != nullptr, hd = a.Dskip != nullptr;
     if constexpr (V != 0) {
         if (hz) launch((segment_final<N, BF16, true, true, V>), grid, block, 0, st, a, g);
         else launch((segment_final<N, BF16, false, true, V>), grid, block, 0, st, a, g);

@@ -14,7 +14,10 @@ ScanPlan scan_plan(int B, int L, int D, int N) {
 
 size_t scan_workspace_bytes(int B, int L, int D, int N) {
     const Geom g = geom(B, L, D, N);
-    // one workgroup holds every state chunk (N <= 128) and finishes y itself
+    // a short chain run in one workgroup needs none
+    if (fused_call(g, B, D, N)) return 0;
+    // one workgroup holds every state chunk (N <= 128) and finishes y itself; a
+    // single segment needs no carries
     if (sink_planes(N) == 1) return g.S <= 1 ? 0 : ws_layout(B, D, N, g.S, g.G).total * sizeof(float);
     // else the summed C . h of each group of state chunks follows the carry arrays (YP)
     return (ws_layout(B, D, N, g.S, g.G).total + (size_t)sink_planes(N) * B * L * D) * sizeof(float);

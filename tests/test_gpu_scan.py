@@ -39,6 +39,13 @@ SMALL = [
     (1, 1500, 64, 256, si.F32, True, False, True),
     (1, 40, 33, 128, si.F32, False, True, False),
     (3, 257, 128, 256, si.BF16, True, True, False),
+    # short chains run as one launch (every segment of a chain in one workgroup, the
+    # carries in LDS): two to four segments, and a batch of short sequences at eight
+    (3, 120, 200, 8, si.F32, True, False, True),
+    (1, 100, 64, 32, si.BF16, True, True, True),
+    (2, 65, 130, 4, si.BF16, False, True, True),
+    (64, 256, 1536, 16, si.BF16, True, True, True),
+    (16, 250, 1024, 32, si.F32, True, True, False),
 ]
 
 

@@ -61,6 +61,9 @@ CASES = [
     (1, 1000, 96, 128, si.F32, "euler", True, True, False, True, False),
     (1, 257, 64, 256, si.BF16, "zoh", True, True, True, False, True),
     (3, 129, 130, 64, si.F32, "euler", True, False, False, False, True),
+    # short chains in one launch
+    (2, 100, 70, 16, si.BF16, "zoh", True, True, True, True, True),
+    (32, 256, 1024, 16, si.BF16, "zoh", True, True, True, True, True),
 ]
 
 
