@@ -334,6 +334,80 @@ __global__ void __launch_bounds__(64 * kW3) seg_final3(Scan3Args a, Geom3 g) {
     }
 }
 
+// A short sequence (2 .. kW3 segments, one group): one launch. Each wave runs its
+// segment from a zero state, the waves meet in LDS for the exclusive prefix of the
+// earlier segments (end states and sums of Delta; decays recomputed), and each wave
+// runs its segment again from its entering state (h0 folded in). No workspace.
+template <int N, bool BF16>
+__global__ void __launch_bounds__(64 * kW3) seg_fused3(Scan3Args a, Geom3 g) {
+    __shared__ float sHr[kW3][N][64], sHi[kW3][N][64], sS[kW3][64];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int b = blockIdx.z, D = a.D;
+    const int d = blockIdx.y * 64 + lane, dc = d < D ? d : D - 1;
+    const int s = wave;
+    const int t0 = s * g.Ls;
+    const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
+    float A2[N], th[N], hr[N], hi[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        A2[n] = a.Are[(size_t)dc * N + n] * kLog2e;
+        th[n] = a.theta[(size_t)dc * N + n] * kInv2Pi;
+        hr[n] = 0.0f;
+        hi[n] = 0.0f;
+    }
+    float sumd = 0.0f;
+    if (len > 0) walk3<N, BF16, false>(a, b, d, dc, t0, len, A2, th, hr, hi, 0.0f, sumd);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        sHr[wave][n][lane] = hr[n];
+        sHi[wave][n][lane] = hi[n];
+    }
+    sS[wave][lane] = sumd;
+    __syncthreads();
+    if (len == 0) return;
+    float er[N], ei[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) er[n] = ei[n] = 0.0f;
+    float cs = 0.0f;
+    for (int j = 0; j < wave; ++j) {
+        const float sj = sS[j][lane];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            float pr, pi;
+            cdecay(sj, A2[n], th[n], pr, pi);
+            const float nr = pr * er[n] - pi * ei[n] + sHr[j][n][lane];
+            const float ni = pr * ei[n] + pi * er[n] + sHi[j][n][lane];
+            er[n] = nr;
+            ei[n] = ni;
+        }
+        cs += sj;
+    }
+    // h_in = exp(A cs) h0 + E
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        if (a.h0 != nullptr) {
+            const float gr = a.h0[(((size_t)b * D + dc) * N + n) * 2], gi = a.h0[(((size_t)b * D + dc) * N + n) * 2 + 1];
+            float pr, pi;
+            cdecay(cs, A2[n], th[n], pr, pi);
+            hr[n] = pr * gr - pi * gi + er[n];
+            hi[n] = pr * gi + pi * gr + ei[n];
+        } else {
+            hr[n] = er[n];
+            hi[n] = ei[n];
+        }
+    }
+    const float Dv = a.Dskip ? a.Dskip[dc] : 0.0f;
+    float unused = 0.0f;
+    walk3<N, BF16, true>(a, b, d, dc, t0, len, A2, th, hr, hi, Dv, unused);
+    if (d < D && s == g.S - 1 && a.h_final != nullptr) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            a.h_final[(((size_t)b * D + d) * N + n) * 2] = hr[n];
+            a.h_final[(((size_t)b * D + d) * N + n) * 2 + 1] = hi[n];
+        }
+    }
+}
+
 // L == 0: the final state is the initial state.
 __global__ void copy_state3(const float* __restrict__ h0, float* __restrict__ out, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -348,6 +422,11 @@ hipError_t launch3(const Scan3Args& a, hipStream_t st) {
             const size_t n = (size_t)a.B * a.D * a.N * 2;
             launch(copy_state3, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.h0, a.h_final, n);
         }
+        return hipGetLastError();
+    }
+    if (g.S > 1 && g.G == 1) {
+        launch((seg_fused3<N, BF16>), dim3(1, (unsigned)((a.D + 63) / 64), (unsigned)a.B), dim3(64 * g.S), 0, st,
+               a, g);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)g.G, (unsigned)((a.D + 63) / 64), (unsigned)a.B);
@@ -376,7 +455,7 @@ int scan3_segment_len(int B, int L, int D) { return geom3(B, L, D).Ls; }
 
 size_t scan3_workspace_bytes(int B, int L, int D, int N) {
     const Geom3 g = geom3(B, L, D);
-    if (g.S <= 1) return 0;
+    if (g.S <= 1 || g.G == 1) return 0;  // one segment, or one group run in one launch
     return ws3(B, D, N, g.S, g.G).total * sizeof(float);
 }
 

@@ -240,6 +240,7 @@ def test_scan3_rejects_bad_arguments(kw, status):
 def test_scan3_workspace_size():
     assert ssa.ssm_scan3_workspace_size(1, 4096, 1536, 16) > 0
     assert ssa.ssm_scan3_workspace_size(1, 32, 64, 16) == 0      # a single segment needs none
+    assert ssa.ssm_scan3_workspace_size(1, 100, 64, 16) == 0     # one group of segments: one launch
     assert ssa.ssm_scan3_workspace_size(1, 4096, 1536, 32) == 0  # unsupported N
 
 

@@ -47,6 +47,9 @@ SMALL = [
     (1, 2000, 96, 16, si.F32, True, True, False, True),
     (2, 4097, 200, 16, si.BF16, True, True, True, True),
     (5, 77, 1, 8, si.F32, True, True, True, False),
+    # one group of two to four segments runs as one launch
+    (3, 100, 130, 16, si.BF16, True, True, True, True),
+    (16, 128, 1024, 16, si.BF16, True, True, False, True),
 ]
 
 
