@@ -17,24 +17,27 @@
 // channels is cut into S segments of Ls steps; W consecutive segments form a
 // group, handled by one workgroup of W waves (one wave per segment). Three launches:
 //   1. segment_aggregate: every wave runs its segment from a zero state (end
-//      state H_s, decay P_s = exp(A sum Delta)); the group's waves then form, in
-//      LDS, each segment's exclusive in-group prefix E_s (and the in-group prefix
-//      of sum Delta), and the last wave the group's own aggregate (GP_g, GH_g).
+//      state H_s, sum of Delta; its decay P_s = exp(A sum Delta) is recomputed
+//      where needed); the group's waves then form, in LDS, each segment's
+//      exclusive in-group prefix E_s (and the in-group prefix of sum Delta), and
+//      the last wave the group's own aggregate (GP_g, GH_g).
 //   2. group_carry: per (batch, channel, state index) the state entering each
 //      group, from the groups' aggregates (a two-level walk over the groups).
 //   3. segment_final: each wave forms its segment's carried-in state
 //      h_in = exp(A * prefix sum Delta) h_group + E_s and runs the recurrence
 //      again from it, writing y (and h_final at the end of the sequence).
 // (P1, H1) then (P2, H2) compose to (P2 P1, P2 H1 + H2): the recurrence is an
-// affine map of the state, so segments compose like affine maps.
+// affine map of the state, so segments compose like affine maps. A short chain
+// (segment_fused) runs all three steps in one launch, one workgroup per chain.
 //
 // N >= 64 (64, 128, 256): a lane's 64 states and 64 entries of A would fill its
 // registers, so the state index is cut into chunks of 16 that run as independent
 // chains (aggregate, carry and recurrence are independent across state indices);
 // the final pass (segment_final_sink: one workgroup holds up to 8 chunk waves of a
-// segment and 64 channels) adds the chunks' partial C . h in LDS and writes one
-// fp32 sum per (t, channel) and chunk group; a fourth launch (combine_partials)
-// adds the groups' sums, the skip and the gate.
+// segment and 64 channels) adds the chunks' partial C . h in LDS; with every chunk
+// in the workgroup (N <= 128) it finishes y there, else it writes one fp32 sum per
+// (t, channel) and chunk group and a fourth launch (combine_partials) adds the
+// groups' sums, the skip and the gate.
 #pragma once
 #include "common.h"
 #include "launch.h"
