@@ -19,6 +19,7 @@
 //      term, read from the token before the segment.
 //   2. carry3: per (batch, state, channel) the state entering each group.
 //   3. seg_final3: the recurrence again from the carried-in state, writing y.
+// One group of segments (seg_fused3) runs all three in one launch.
 // Segments compose as affine maps with complex coefficients: (P1, H1) then
 // (P2, H2) = (P2 P1, P2 H1 + H2), P = exp(A sum Delta) = 2^{Are' S} (cos, sin)(theta S).
 // alpha takes v_exp_f32, v_sin_f32 and v_cos_f32 (the last two in revolutions).
