@@ -32,6 +32,9 @@
 //      per-step sums over channels (dB, dC) are reduced across the 64 lanes by a
 //      transpose-reduce (permlane swaps and DPP, no LDS) and stored as fp32
 //      partials per 64-channel block; dA and dD are summed per workgroup.
+//      N = 32, 64: the workgroup is one segment's chunk waves, which add their
+//      per-(t, channel) sums over n in LDS and finish dx, ddelta and dz there;
+//      N = 128, 256: each chunk writes those sums to planes and bwd_combine adds them.
 //   5. bwd_reduce_params / bwd_reduce_rows: add the partials, round dB and dC to
 //      the io type.
 #include "common.h"
@@ -58,10 +61,21 @@ constexpr int kBwdMaxGroup = 4;
 constexpr float kLn2 = 0.69314718055994531f;
 // N > 16 runs as N / 16 independent chunks of 16 states per lane (both
 // recurrences are diagonal in n). The per-(t, channel) sums over n that dx,
-// ddelta and dz need are then split: each chunk writes its partial sums to a
-// plane of its own and bwd_combine adds the planes in chunk order.
+// ddelta and dz need are then split into per-chunk partial sums, added in chunk
+// order: in LDS by the final pass itself (N <= 64, below), or by bwd_combine from a
+// plane per chunk.
 constexpr int kBwdChunkN = 16;
 __host__ __device__ inline int bwd_chunks(int N) { return N > kBwdChunkN ? N / kBwdChunkN : 1; }
+// Up to four chunks (N <= 64) the final pass runs every chunk of a segment in
+// one workgroup (one wave each), and the chunks add those per-(t, channel)
+// partial sums in LDS once per checkpoint block; one wave per step of the block
+// then finishes dx, ddelta and dz. No planes, no combine launch. (Eight chunks
+// would need 96 KB of LDS per workgroup, one workgroup and two waves per SIMD
+// where the planes run three: slower at N = 128.)
+constexpr int kBwdSinkMaxChunks = 4;
+__host__ __device__ inline bool bwd_sink(int N) {
+    return bwd_chunks(N) > 1 && bwd_chunks(N) <= kBwdSinkMaxChunks;
+}
 
 // Steps between checkpoints (K), and steps whose states the final pass keeps in
 // VGPRs at a time (KR): a K-step block runs as K/KR halves, the later half first,
@@ -77,10 +91,11 @@ struct BGeom {
     int G;     // groups per chain
     int K;     // steps between checkpoints (a block)
     int nsub;  // blocks per full segment
+    int P;     // final-pass workgroups per chain along the sequence (G, or S with the sink)
 };
 
 BGeom bgeom(int B, int L, int D, int N) {
-    BGeom g{0, 0, 1, 0, sub_len(N), 0};
+    BGeom g{0, 0, 1, 0, sub_len(N), 0, 0};
     if (L <= 0) return g;
     const long chains = (long)B * ((D + 63) / 64) * bwd_chunks(N);
     const long s_target = (kBwdTargetWaves + chains - 1) / chains;
@@ -92,6 +107,7 @@ BGeom bgeom(int B, int L, int D, int N) {
     g.W = std::min(kBwdMaxGroup, g.S);
     g.G = (g.S + g.W - 1) / g.W;
     g.nsub = g.Ls / g.K;
+    g.P = bwd_sink(N) ? g.S : g.G;
     return g;
 }
 
@@ -106,14 +122,16 @@ BGeom bgeom(int B, int L, int D, int N) {
 //   GPB [B][G-1][N][D] decay of groups 1..G-1
 //   HZ  [B][S][nsub-1][N][D] zero-start state at block boundaries 1..nsub-1 of each segment
 //   CZ  [B][S][nsub-1][D]    sum(Delta) from the segment start to those boundaries
-//   PA  [B][G][N][D]   dA summed over one group's segments
-//   PD  [B][G][D]      dD summed over one group's segments
+//   PA  [B][P][N][D]   dA summed over one final-pass workgroup's segments
+//   PD  [B][P][D]      dD likewise
 //   PB  [ceil(D/64)][B][L][N]  dB summed over one 64-channel block
 //   PC  [ceil(D/64)][B][L][N]  dC summed over one 64-channel block
-//   QS  [N/16][B][L][D] (N > 16) sum over the chunk's states of g_t B_t
-//   QD  [N/16][B][L][D] (N > 16) the chunk's part of ddelta
-//   QV  [N/16][B][L][D] (N > 16) the chunk's part of C_t . h_t
-// (state index n is global: a chunk's states are n0 .. n0 + 15 of N)
+//   QS  [N/16][B][L][D] (N > 128) sum over the chunk's states of g_t B_t
+//   QD  [N/16][B][L][D] (N > 128) the chunk's part of ddelta
+//   QV  [N/16][B][L][D] (N > 128) the chunk's part of C_t . h_t
+// (state index n is global: a chunk's states are n0 .. n0 + 15 of N). With the
+// sink (16 < N <= 128) the final pass also keeps each segment's entering state in
+// its E slot, which only that segment's waves read.
 struct BwsLayout {
     size_t E, CS, GH, GP, EB, CSB, GHB, GPB, HZ, CZ, PA, PD, PB, PC, QS, QD, QV, total;
 };
@@ -135,11 +153,11 @@ __host__ __device__ inline BwsLayout bws_layout(int B, int L, int D, int N, cons
     w.GPB = o; o += (size_t)B * g1 * st;
     w.HZ = o;  o += (size_t)B * g.S * c1 * st;
     w.CZ = o;  o += (size_t)B * g.S * c1 * D;
-    w.PA = o;  o += (size_t)B * g.G * st;
-    w.PD = o;  o += (size_t)B * g.G * D;
+    w.PA = o;  o += (size_t)B * g.P * st;
+    w.PD = o;  o += (size_t)B * g.P * D;
     w.PB = o;  o += nd * B * L * N;
     w.PC = o;  o += nd * B * L * N;
-    const size_t nq = bwd_chunks(N) > 1 ? (size_t)bwd_chunks(N) * B * L * D : 0;
+    const size_t nq = bwd_chunks(N) > 1 && !bwd_sink(N) ? (size_t)bwd_chunks(N) * B * L * D : 0;
     w.QS = o;  o += nq;
     w.QD = o;  o += nq;
     w.QV = o;  o += nq;
@@ -504,21 +522,28 @@ bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ 
 // three, and the third wave hides more latency than the spills cost.
 // CH: one chunk of N states out of a.N > N; dx, ddelta and dz then go out as
 // this chunk's partial sums (QS, QD, QV) for bwd_combine.
-template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH>
-__global__ void __launch_bounds__(64 * kBwdMaxGroup) __attribute__((amdgpu_waves_per_eu(3)))
-bwd_final(BwdArgs a, BGeom g) {
+// NC > 0 (the sink, CH only): the workgroup is one segment's NC chunk waves (wave =
+// chunk), one workgroup per segment; NC = 0: W segments of one group for one chunk.
+// NC is a template argument: a loop over a run-time chunk count inside the block
+// loop raised the kernel from 165 to 200 VGPRs.
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH, int NC>
+__global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
+    __attribute__((amdgpu_waves_per_eu(3))) bwd_final(BwdArgs a, BGeom g) {
+    constexpr bool SINK = NC > 0;
+    static_assert(!SINK || CH, "the sink adds chunk partials");
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
     constexpr uint32_t es = BF16 ? 2 : 4;
-    const int NT = CH ? a.N : N, nch = CH ? NT / N : 1;
+    const int NT = CH ? a.N : N, nch = SINK ? NC : (CH ? NT / N : 1);
     const int rw = BF16 ? NT / 2 : NT;
-    const int W = g.W;
+    const int W = SINK ? nch : g.W;  // waves per workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int grp = blockIdx.x, b = blockIdx.z, D = a.D;
-    const int cidx = blockIdx.y % nch, n0 = cidx * N;
-    const int dblk = blockIdx.y / nch;
+    const int b = blockIdx.z, D = a.D;
+    const int cidx = SINK ? wave : blockIdx.y % nch, n0 = cidx * N;
+    const int dblk = SINK ? blockIdx.y : blockIdx.y / nch;
     const int d = dblk * 64 + lane, dc = d < D ? d : D - 1;
-    const int s = grp * W + wave;
+    const int s = SINK ? (int)blockIdx.x : (int)blockIdx.x * W + wave;
+    const int grp = SINK ? s / g.W : (int)blockIdx.x;  // the segment's group (carries)
     const int t0 = s * g.Ls;
     const int len = s < g.S ? min(g.Ls, a.L - t0) : 0;
     const BwsLayout wl = bws_layout(a.B, a.L, D, NT, g);
@@ -593,15 +618,29 @@ bwd_final(BwdArgs a, BGeom g) {
         }
         const float Dv = HAS_D ? a.Dskip[dc] : 0.0f;
         // parking slot for a block's entering state: this wave's dA slot, which the
-        // wave itself writes only after its last block; the segment's entering
-        // state lives in LDS too (read once per block)
+        // wave itself writes only after its last block
         float* lhe = lds + wave * N * 64;
-        float* lhin = lds + W * (N + 1) * 64 + wave * N * 64;
         // the state entering a block's later half (after its replay), read back by
         // that half's first backward step
-        float* lhh = lds + W * (2 * N + 1) * 64 + wave * N * 64;
+        float* lhh = lds + W * (SINK ? N + 1 : 2 * N + 1) * 64 + wave * N * 64;
+        // the segment's entering state (read once per block): in LDS, or with the
+        // sink in the segment's E slot (already read above; only this wave uses it)
+        float* lhin = SINK ? static_cast<float*>(a.ws) + wl.E + (((size_t)b * g.S + s) * NT + n0) * D + dc
+                           : lds + W * (N + 1) * 64 + wave * N * 64;
+        const size_t hst = SINK ? (size_t)D : 64;  // its stride over n
+        // sink: per-(step, channel) partials of the block's steps, [wave][3][K][64]
+        // (sum of g B, the ddelta part, C . h), and [K][4][64] coefficients of each
+        // step's finish: Delta, dv D, dy silu'(z) and D x. Every chunk wave computes
+        // the same coefficients from the same inputs and stores them unconditionally
+        // (the same value to the same address): a store guarded by the wave index
+        // splits the block's code and costs ~40 VGPRs
+        float* lx = lds + W * (2 * N + 1) * 64 + lane;  // this lane's column
+        float* lc = lx + W * 3 * K * 64;
+        float* mx = lx + wave * 3 * K * 64;               // this wave's partials
+        if (!SINK || d < D) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) lhin[n * 64 + lane] = hin[n];
+            for (int n = 0; n < N; ++n) lhin[n * hst + (SINK ? 0 : lane)] = hin[n];
+        }
 
         SegIO<BF16> X, Dl, Z, DY, DX, DDL, DZ;
         X.init(a.x, row0, len, D);
@@ -657,16 +696,21 @@ bwd_final(BwdArgs a, BGeom g) {
             // slot while the block's later half runs
             {
                 float he[N];
+                const int hl = SINK ? 0 : lane;
+                const float* hinp = lhin;
+                // sink: an opaque copy, so that the state's loads stay in the block (hoisted
+                // out of the loop they would hold N more VGPRs for the whole segment)
+                if constexpr (SINK) asm volatile("" : "+v"(hinp));
                 if (j == 0) {
 #pragma unroll
-                    for (int n = 0; n < N; ++n) he[n] = lhin[n * 64 + lane];
+                    for (int n = 0; n < N; ++n) he[n] = hinp[n * hst + hl];
                 } else {
                     const size_t ck = ((size_t)b * g.S + s) * c1 + (j - 1);
                     const float* hz = ws + wl.HZ + (ck * NT + n0) * D + dc;
                     const float cz = ws[wl.CZ + ck * D + dc];
 #pragma unroll
                     for (int n = 0; n < N; ++n)
-                        he[n] = __builtin_fmaf(exp2_fast(A2[n] * cz), lhin[n * 64 + lane], hz[(size_t)n * D]);
+                        he[n] = __builtin_fmaf(exp2_fast(A2[n] * cz), hinp[n * hst + hl], hz[(size_t)n * D]);
                 }
 #pragma unroll
                 for (int n = 0; n < N; ++n) lhe[n * 64 + lane] = he[n];
@@ -734,7 +778,11 @@ bwd_final(BwdArgs a, BGeom g) {
                     if constexpr (HAS_Z) {
                         const float sg = rcp_fast(1.0f + exp2_fast(-zv[k] * kLog2e));
                         dv[kk] = dyv[k] * zv[k] * sg;
-                        if constexpr (CH) {
+                        if constexpr (SINK) {
+                            mx[(2 * K + k) * 64] = v;
+                            lc[(k * 4 + 2) * 64] = dyv[k] * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
+                            lc[(k * 4 + 3) * 64] = HAS_D ? Dv * xv[k] : 0.0f;
+                        } else if constexpr (CH) {
                             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rQV, (int)qoff,
                                                                   (int)((uint32_t)t * qstride), 0);
                         } else {
@@ -743,6 +791,10 @@ bwd_final(BwdArgs a, BGeom g) {
                         }
                     } else {
                         dv[kk] = dyv[k];
+                    }
+                    if constexpr (SINK) {
+                        lc[(k * 4 + 0) * 64] = dl[k];
+                        lc[(k * 4 + 1) * 64] = HAS_D ? dv[kk] * Dv : 0.0f;
                     }
                     if constexpr (HAS_D) {
                         if (!CH || cidx == 0) dD = __builtin_fmaf(dv[kk], xv[k], dD);
@@ -784,7 +836,10 @@ bwd_final(BwdArgs a, BGeom g) {
                         c[n] = at * gg;
                     }
                     const float ddv = __builtin_fmaf(sA, kLn2, xv[k] * sB);
-                    if constexpr (CH) {
+                    if constexpr (SINK) {
+                        mx[k * 64] = sB;
+                        mx[(K + k) * 64] = ddv;
+                    } else if constexpr (CH) {
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rQS, (int)qoff,
                                                               (int)((uint32_t)t * qstride), 0);
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ddv), rQD, (int)qoff,
@@ -798,12 +853,49 @@ bwd_final(BwdArgs a, BGeom g) {
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rPB, (int)poff, (int)(t * NT * 4), 0);
                 }
             }
+            if constexpr (SINK) {
+                // every chunk's partials of the block are in LDS (the workgroup is one
+                // segment, so every wave takes the same number of blocks): step k of the
+                // block is finished by wave k mod nch, adding the chunks in order
+                __syncthreads();
+                static_assert(NC <= K || NC % K == 0, "every step of a block has one finishing wave");
+#pragma unroll
+                for (int i = 0; i < (NC < K ? K / NC : 1); ++i) {
+                    const int k = wave + i * NC;
+                    if (NC > K && k >= K) break;  // waves past the block's steps
+                    const int t = j * K + k;
+                    float qs = 0.0f, qd = 0.0f, qv = 0.0f;
+#pragma unroll
+                    for (int cc = 0; cc < NC; ++cc) {
+                        qs += lx[(cc * 3 * K + k) * 64];
+                        qd += lx[(cc * 3 * K + K + k) * 64];
+                        if constexpr (HAS_Z) qv += lx[(cc * 3 * K + 2 * K + k) * 64];
+                    }
+                    const float* cf = lc + k * 4 * 64;
+                    // dx = Delta sum g B + dv D;  dz = dy silu'(z) (sum C . h + D x)
+                    if constexpr (HAS_Z)
+                        store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, cf[2 * 64] * (qv + cf[3 * 64]));
+                    store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, __builtin_fmaf(cf[0], qs, cf[64]));
+                    store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, qd);
+                }
+                // the next block rewrites the partials
+                __syncthreads();
+            }
         }
         if (s == 0 && a.dh0 != nullptr && d < D) {
             float* p = a.dh0 + ((size_t)b * D + d) * NT + n0;
 #pragma unroll
             for (int n = 0; n < N; ++n) p[n] = c[n];
         }
+    }
+    if constexpr (SINK) {
+        // one segment per workgroup: each wave's dA (its chunk) and dD (chunk 0) as they are
+        if (d >= D) return;
+        float* PA = static_cast<float*>(a.ws) + wl.PA + (((size_t)b * g.P + s) * NT + n0) * D + d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) PA[(size_t)n * D] = dA[n];
+        if (HAS_D && cidx == 0) static_cast<float*>(a.ws)[wl.PD + ((size_t)b * g.P + s) * D + d] = dD;
+        return;
     }
     // dA and dD summed over the group's segments (waves past the sequence add zeros)
     float* lA = lds;
@@ -813,7 +905,7 @@ bwd_final(BwdArgs a, BGeom g) {
     lD[wave * 64 + lane] = dD;
     __syncthreads();
     if (wave != 0 || d >= D) return;
-    float* PA = static_cast<float*>(a.ws) + wl.PA + (((size_t)b * g.G + grp) * NT + n0) * D + d;
+    float* PA = static_cast<float*>(a.ws) + wl.PA + (((size_t)b * g.P + grp) * NT + n0) * D + d;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         float acc = 0.0f;
@@ -823,12 +915,12 @@ bwd_final(BwdArgs a, BGeom g) {
     if (HAS_D && cidx == 0) {
         float acc = 0.0f;
         for (int j = 0; j < W; ++j) acc += lD[j * 64 + lane];
-        static_cast<float*>(a.ws)[wl.PD + ((size_t)b * g.G + grp) * D + d] = acc;
+        static_cast<float*>(a.ws)[wl.PD + ((size_t)b * g.P + grp) * D + d] = acc;
     }
 }
 
 // ------------------------------------------------------------ 5. reductions
-// dA[d][n] = sum over (batch, group) of PA; dD[d] likewise (blockIdx.y == N). One
+// dA[d][n] = sum over (batch, final-pass workgroup) of PA; dD[d] likewise (blockIdx.y == N). One
 // workgroup per (64 channels, n): its 4 waves take every 4th unit, 4 loads in
 // flight each, then add their sums in LDS in a fixed order.
 __global__ void __launch_bounds__(256)
@@ -841,7 +933,7 @@ bwd_reduce_params(BwdArgs a, BGeom g) {
     if (is_d && a.dDskip == nullptr) return;  // uniform over the block
     const BwsLayout wl = bws_layout(a.B, a.L, D, N, g);
     const float* ws = static_cast<const float*>(a.ws);
-    const int units = a.B * g.G;
+    const int units = a.B * g.P;
     const int dc = d < D ? d : D - 1;
     const float* base = is_d ? ws + wl.PD + dc : ws + wl.PA + (size_t)n * D + dc;
     const size_t ustride = is_d ? (size_t)D : (size_t)N * D;
@@ -968,7 +1060,22 @@ bwd_empty(BwdArgs a) {
 
 template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH>
 void launch_final(const BwdArgs& a, const BGeom& g, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
-    launch((bwd_final<N, BF16, HAS_Z, HAS_D, CH>), grid, block, (uint32_t)lds, st, a, g);
+    if constexpr (CH) {
+        if (bwd_sink(a.N)) {
+            // one workgroup per segment and 64-channel block, one wave per chunk: the
+            // parking slots (entering state of a block and of its later half, dD) and
+            // the block's partials, [3][K][64] floats per wave
+            const int nch = bwd_chunks(a.N);
+            const dim3 sgrid(g.S, (a.D + 63) / 64, a.B);
+            const size_t slds = ((size_t)nch * ((2 * N + 1) + 3 * g.K) + 4 * g.K) * 64 * sizeof(float);
+            if (nch == 2)
+                launch((bwd_final<N, BF16, HAS_Z, HAS_D, true, 2>), sgrid, dim3(64 * nch), (uint32_t)slds, st, a, g);
+            else
+                launch((bwd_final<N, BF16, HAS_Z, HAS_D, true, 4>), sgrid, dim3(64 * nch), (uint32_t)slds, st, a, g);
+            return;
+        }
+    }
+    launch((bwd_final<N, BF16, HAS_Z, HAS_D, CH, 0>), grid, block, (uint32_t)lds, st, a, g);
     if constexpr (CH) {
         const size_t tot = (size_t)a.B * a.L * a.D;
         launch((bwd_combine<BF16, HAS_Z, HAS_D>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a, g);
