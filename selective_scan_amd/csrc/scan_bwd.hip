@@ -61,20 +61,19 @@ constexpr int kBwdMaxGroup = 4;
 constexpr float kLn2 = 0.69314718055994531f;
 // N > 16 runs as N / 16 independent chunks of 16 states per lane (both
 // recurrences are diagonal in n). The per-(t, channel) sums over n that dx,
-// ddelta and dz need are then split into per-chunk partial sums, added in chunk
-// order: in LDS by the final pass itself (N <= 64, below), or by bwd_combine from a
-// plane per chunk.
+// ddelta and dz need are then split into per-chunk partial sums. The final pass
+// runs up to four chunks of a segment as one workgroup (one wave each), whose
+// waves add their partials in LDS once per checkpoint block: with at most four
+// chunks (N <= 64) one wave per step of the block then finishes dx, ddelta and
+// dz; with more, each group of four chunks writes its sums to a plane and
+// bwd_combine adds the N / 64 planes. (Eight-wave groups would need 96 KB of LDS
+// per workgroup: one workgroup and two waves per SIMD, against three.)
 constexpr int kBwdChunkN = 16;
+constexpr int kBwdGroupMax = 4;
 __host__ __device__ inline int bwd_chunks(int N) { return N > kBwdChunkN ? N / kBwdChunkN : 1; }
-// Up to four chunks (N <= 64) the final pass runs every chunk of a segment in
-// one workgroup (one wave each), and the chunks add those per-(t, channel)
-// partial sums in LDS once per checkpoint block; one wave per step of the block
-// then finishes dx, ddelta and dz. No planes, no combine launch. (Eight chunks
-// would need 96 KB of LDS per workgroup, one workgroup and two waves per SIMD
-// where the planes run three: slower at N = 128.)
-constexpr int kBwdSinkMaxChunks = 4;
-__host__ __device__ inline bool bwd_sink(int N) {
-    return bwd_chunks(N) > 1 && bwd_chunks(N) <= kBwdSinkMaxChunks;
+__host__ __device__ inline int bwd_group(int N) { return bwd_chunks(N) < kBwdGroupMax ? bwd_chunks(N) : kBwdGroupMax; }
+__host__ __device__ inline int bwd_planes(int N) {
+    return bwd_chunks(N) > kBwdGroupMax ? bwd_chunks(N) / kBwdGroupMax : 0;
 }
 
 // Steps between checkpoints (K), and steps whose states the final pass keeps in
@@ -107,7 +106,7 @@ BGeom bgeom(int B, int L, int D, int N) {
     g.W = std::min(kBwdMaxGroup, g.S);
     g.G = (g.S + g.W - 1) / g.W;
     g.nsub = g.Ls / g.K;
-    g.P = bwd_sink(N) ? g.S : g.G;
+    g.P = bwd_chunks(N) > 1 ? g.S : g.G;
     return g;
 }
 
@@ -126,12 +125,12 @@ BGeom bgeom(int B, int L, int D, int N) {
 //   PD  [B][P][D]      dD likewise
 //   PB  [ceil(D/64)][B][L][N]  dB summed over one 64-channel block
 //   PC  [ceil(D/64)][B][L][N]  dC summed over one 64-channel block
-//   QS  [N/16][B][L][D] (N > 128) sum over the chunk's states of g_t B_t
-//   QD  [N/16][B][L][D] (N > 128) the chunk's part of ddelta
-//   QV  [N/16][B][L][D] (N > 128) the chunk's part of C_t . h_t
-// (state index n is global: a chunk's states are n0 .. n0 + 15 of N). With the
-// sink (16 < N <= 128) the final pass also keeps each segment's entering state in
-// its E slot, which only that segment's waves read.
+//   QS  [N/64][B][L][D] (N > 64) sum over a group of four chunks' states of g_t B_t
+//   QD  [N/64][B][L][D] (N > 64) the group's part of ddelta
+//   QV  [N/64][B][L][D] (N > 64) the group's part of C_t . h_t
+// (state index n is global: a chunk's states are n0 .. n0 + 15 of N). For N > 16
+// the final pass also keeps each segment's entering state in its E slot, which
+// only that segment's wave of the chunk reads.
 struct BwsLayout {
     size_t E, CS, GH, GP, EB, CSB, GHB, GPB, HZ, CZ, PA, PD, PB, PC, QS, QD, QV, total;
 };
@@ -157,7 +156,7 @@ __host__ __device__ inline BwsLayout bws_layout(int B, int L, int D, int N, cons
     w.PD = o;  o += (size_t)B * g.P * D;
     w.PB = o;  o += nd * B * L * N;
     w.PC = o;  o += nd * B * L * N;
-    const size_t nq = bwd_chunks(N) > 1 && !bwd_sink(N) ? (size_t)bwd_chunks(N) * B * L * D : 0;
+    const size_t nq = (size_t)bwd_planes(N) * B * L * D;
     w.QS = o;  o += nq;
     w.QD = o;  o += nq;
     w.QV = o;  o += nq;
@@ -522,25 +521,29 @@ bwd_carry(const float* __restrict__ init, float* agg, const float* __restrict__ 
 // three, and the third wave hides more latency than the spills cost.
 // CH: one chunk of N states out of a.N > N; dx, ddelta and dz then go out as
 // this chunk's partial sums (QS, QD, QV) for bwd_combine.
-// NC > 0 (the sink, CH only): the workgroup is one segment's NC chunk waves (wave =
-// chunk), one workgroup per segment; NC = 0: W segments of one group for one chunk.
-// NC is a template argument: a loop over a run-time chunk count inside the block
-// loop raised the kernel from 165 to 200 VGPRs.
-template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH, int NC>
-__global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
+// CH (N > 16, the sink): the workgroup is one segment's group of NC chunk waves
+// (wave w takes chunk NC * group + w), one workgroup per segment, group and 64
+// channels; GP: the groups' sums go to planes for bwd_combine (more than one group).
+// Otherwise W segments of one group of segments. NC is a template argument: a loop
+// over a run-time chunk count inside the block loop raised the kernel from 165 to
+// 200 VGPRs.
+template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH, int NC, bool GP>
+__global__ void __launch_bounds__(CH ? 64 * NC : 64 * kBwdMaxGroup)
     __attribute__((amdgpu_waves_per_eu(3))) bwd_final(BwdArgs a, BGeom g) {
-    constexpr bool SINK = NC > 0;
-    static_assert(!SINK || CH, "the sink adds chunk partials");
+    constexpr bool SINK = CH;
+    static_assert(!CH || NC > 0, "chunk waves per workgroup");
     extern __shared__ float lds[];
     constexpr int K = sub_len(N);
     constexpr uint32_t es = BF16 ? 2 : 4;
-    const int NT = CH ? a.N : N, nch = SINK ? NC : (CH ? NT / N : 1);
+    const int NT = CH ? a.N : N, nch = SINK ? NC : 1;
+    const int ngrp = CH ? NT / (N * (NC > 0 ? NC : 1)) : 1;  // chunk groups
     const int rw = BF16 ? NT / 2 : NT;
     const int W = SINK ? nch : g.W;  // waves per workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int b = blockIdx.z, D = a.D;
-    const int cidx = SINK ? wave : blockIdx.y % nch, n0 = cidx * N;
-    const int dblk = SINK ? blockIdx.y : blockIdx.y / nch;
+    const int cgrp = SINK ? (int)blockIdx.y % ngrp : 0;
+    const int cidx = SINK ? cgrp * NC + wave : 0, n0 = cidx * N;
+    const int dblk = SINK ? (int)blockIdx.y / ngrp : (int)blockIdx.y;
     const int d = dblk * 64 + lane, dc = d < D ? d : D - 1;
     const int s = SINK ? (int)blockIdx.x : (int)blockIdx.x * W + wave;
     const int grp = SINK ? s / g.W : (int)blockIdx.x;  // the segment's group (carries)
@@ -660,9 +663,9 @@ __global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
                                                       (uint32_t)len * NT * 4u);
         const uint32_t poff =
             reduced_owner<N>(lane) ? (uint32_t)(n0 + reduced_index<N>(lane)) * 4u : 0x80000000u;
-        // CH: this chunk's planes of partial sums over [t0, t0 + len) x D floats
-        const size_t qrow = ((size_t)cidx * a.B + b) * a.L + t0;
-        const uint32_t qbytes = CH ? (uint32_t)len * (uint32_t)D * 4u : 0u;
+        // GP: this chunk group's planes of partial sums over [t0, t0 + len) x D floats
+        const size_t qrow = ((size_t)cgrp * a.B + b) * a.L + t0;
+        const uint32_t qbytes = GP ? (uint32_t)len * (uint32_t)D * 4u : 0u;
         const __amdgpu_buffer_rsrc_t rQS = make_rsrc(static_cast<float*>(a.ws) + wl.QS + qrow * D, qbytes);
         const __amdgpu_buffer_rsrc_t rQD = make_rsrc(static_cast<float*>(a.ws) + wl.QD + qrow * D, qbytes);
         const __amdgpu_buffer_rsrc_t rQV = make_rsrc(static_cast<float*>(a.ws) + wl.QV + qrow * D, qbytes);
@@ -780,11 +783,10 @@ __global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
                         dv[kk] = dyv[k] * zv[k] * sg;
                         if constexpr (SINK) {
                             mx[(2 * K + k) * 64] = v;
-                            lc[(k * 4 + 2) * 64] = dyv[k] * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
-                            lc[(k * 4 + 3) * 64] = HAS_D ? Dv * xv[k] : 0.0f;
-                        } else if constexpr (CH) {
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rQV, (int)qoff,
-                                                                  (int)((uint32_t)t * qstride), 0);
+                            if constexpr (!GP) {
+                                lc[(k * 4 + 2) * 64] = dyv[k] * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
+                                lc[(k * 4 + 3) * 64] = HAS_D ? Dv * xv[k] : 0.0f;
+                            }
                         } else {
                             const float dzv = dyv[k] * v * sg * __builtin_fmaf(zv[k], 1.0f - sg, 1.0f);
                             store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, dzv);
@@ -792,7 +794,7 @@ __global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
                     } else {
                         dv[kk] = dyv[k];
                     }
-                    if constexpr (SINK) {
+                    if constexpr (SINK && !GP) {
                         lc[(k * 4 + 0) * 64] = dl[k];
                         lc[(k * 4 + 1) * 64] = HAS_D ? dv[kk] * Dv : 0.0f;
                     }
@@ -839,11 +841,6 @@ __global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
                     if constexpr (SINK) {
                         mx[k * 64] = sB;
                         mx[(K + k) * 64] = ddv;
-                    } else if constexpr (CH) {
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sB), rQS, (int)qoff,
-                                                              (int)((uint32_t)t * qstride), 0);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ddv), rQD, (int)qoff,
-                                                              (int)((uint32_t)t * qstride), 0);
                     } else {
                         const float dxv = __builtin_fmaf(dl[k], sB, HAS_D ? dv[kk] * Dv : 0.0f);
                         store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, dxv);
@@ -856,7 +853,8 @@ __global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
             if constexpr (SINK) {
                 // every chunk's partials of the block are in LDS (the workgroup is one
                 // segment, so every wave takes the same number of blocks): step k of the
-                // block is finished by wave k mod nch, adding the chunks in order
+                // block is finished by wave k mod NC, adding the group's chunks in order
+                // (GP: into the group's planes)
                 __syncthreads();
                 static_assert(NC <= K || NC % K == 0, "every step of a block has one finishing wave");
 #pragma unroll
@@ -871,12 +869,21 @@ __global__ void __launch_bounds__(NC > 0 ? 64 * NC : 64 * kBwdMaxGroup)
                         qd += lx[(cc * 3 * K + K + k) * 64];
                         if constexpr (HAS_Z) qv += lx[(cc * 3 * K + 2 * K + k) * 64];
                     }
-                    const float* cf = lc + k * 4 * 64;
-                    // dx = Delta sum g B + dv D;  dz = dy silu'(z) (sum C . h + D x)
-                    if constexpr (HAS_Z)
-                        store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, cf[2 * 64] * (qv + cf[3 * 64]));
-                    store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, __builtin_fmaf(cf[0], qs, cf[64]));
-                    store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, qd);
+                    if constexpr (GP) {
+                        // the group's sums, for bwd_combine
+                        const int to = (int)((uint32_t)t * qstride);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(qs), rQS, (int)qoff, to, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(qd), rQD, (int)qoff, to, 0);
+                        if constexpr (HAS_Z)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(qv), rQV, (int)qoff, to, 0);
+                    } else {
+                        const float* cf = lc + k * 4 * 64;
+                        // dx = Delta sum g B + dv D;  dz = dy silu'(z) (sum C . h + D x)
+                        if constexpr (HAS_Z)
+                            store_io<BF16>(DZ.r, soff_st, (uint32_t)t * rstride, cf[2 * 64] * (qv + cf[3 * 64]));
+                        store_io<BF16>(DX.r, soff_st, (uint32_t)t * rstride, __builtin_fmaf(cf[0], qs, cf[64]));
+                        store_io<BF16>(DDL.r, soff_st, (uint32_t)t * rstride, qd);
+                    }
                 }
                 // the next block rewrites the partials
                 __syncthreads();
@@ -995,9 +1002,9 @@ bwd_reduce_rows(BwdArgs a, BGeom g) {
     }
 }
 
-// N > 16: dx, ddelta and dz from the chunks' partial sums, added in chunk order
-// (eight chunks' partials loaded before any is added). With v = sum_c QV + D x
-// the forward output before the gate and dv = dy silu(z):
+// N > 64: dx, ddelta and dz from the chunk groups' partial sums (planes), added in
+// group order (all N / 64 <= 4 planes loaded before any is added). With
+// v = sum_c QV + D x the forward output before the gate and dv = dy silu(z):
 //   dx = Delta sum_c QS + dv D,  ddelta = sum_c QD,  dz = dy v silu'(z).
 template <bool BF16, bool HAS_Z, bool HAS_D>
 __global__ void __launch_bounds__(256)
@@ -1007,20 +1014,20 @@ bwd_combine(BwdArgs a, BGeom g) {
     if (i >= tot) return;
     const BwsLayout wl = bws_layout(a.B, a.L, a.D, a.N, g);
     const float* ws = static_cast<const float*>(a.ws);
-    const int nch = bwd_chunks(a.N);
+    const int np = bwd_planes(a.N);
     float sB = 0.0f, sD = 0.0f, sV = 0.0f;
-    for (int c0 = 0; c0 < nch; c0 += 8) {
-        float qb[8], qd[8], qv[8];
+    for (int c0 = 0; c0 < np; c0 += 4) {
+        float qb[4], qd[4], qv[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const size_t o = (size_t)min(c0 + j, nch - 1) * tot + i;
+        for (int j = 0; j < 4; ++j) {
+            const size_t o = (size_t)min(c0 + j, np - 1) * tot + i;
             qb[j] = ws[wl.QS + o];
             qd[j] = ws[wl.QD + o];
             qv[j] = HAS_Z ? ws[wl.QV + o] : 0.0f;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (c0 + j < nch) {
+        for (int j = 0; j < 4; ++j) {
+            if (c0 + j < np) {
                 sB += qb[j];
                 sD += qd[j];
                 if constexpr (HAS_Z) sV += qv[j];
@@ -1061,24 +1068,25 @@ bwd_empty(BwdArgs a) {
 template <int N, bool BF16, bool HAS_Z, bool HAS_D, bool CH>
 void launch_final(const BwdArgs& a, const BGeom& g, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
     if constexpr (CH) {
-        if (bwd_sink(a.N)) {
-            // one workgroup per segment and 64-channel block, one wave per chunk: the
-            // parking slots (entering state of a block and of its later half, dD) and
-            // the block's partials, [3][K][64] floats per wave
-            const int nch = bwd_chunks(a.N);
-            const dim3 sgrid(g.S, (a.D + 63) / 64, a.B);
-            const size_t slds = ((size_t)nch * ((2 * N + 1) + 3 * g.K) + 4 * g.K) * 64 * sizeof(float);
-            if (nch == 2)
-                launch((bwd_final<N, BF16, HAS_Z, HAS_D, true, 2>), sgrid, dim3(64 * nch), (uint32_t)slds, st, a, g);
-            else
-                launch((bwd_final<N, BF16, HAS_Z, HAS_D, true, 4>), sgrid, dim3(64 * nch), (uint32_t)slds, st, a, g);
-            return;
+        // one workgroup per (segment, chunk group, 64-channel block), one wave per
+        // chunk: the parking slots (entering state of a block and of its later half,
+        // dD) and the block's partials, [3][K][64] floats per wave, and the steps'
+        // finishing coefficients
+        const int nc = bwd_group(a.N), ngrp = bwd_chunks(a.N) / nc;
+        const dim3 sgrid(g.S, ((a.D + 63) / 64) * ngrp, a.B);
+        const size_t slds = ((size_t)nc * ((2 * N + 1) + 3 * g.K) + 4 * g.K) * 64 * sizeof(float);
+        if (nc == 2)
+            launch((bwd_final<N, BF16, HAS_Z, HAS_D, true, 2, false>), sgrid, dim3(64 * nc), (uint32_t)slds, st, a, g);
+        else if (ngrp == 1)
+            launch((bwd_final<N, BF16, HAS_Z, HAS_D, true, 4, false>), sgrid, dim3(64 * nc), (uint32_t)slds, st, a, g);
+        else
+            launch((bwd_final<N, BF16, HAS_Z, HAS_D, true, 4, true>), sgrid, dim3(64 * nc), (uint32_t)slds, st, a, g);
+        if (ngrp > 1) {
+            const size_t tot = (size_t)a.B * a.L * a.D;
+            launch((bwd_combine<BF16, HAS_Z, HAS_D>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a, g);
         }
-    }
-    launch((bwd_final<N, BF16, HAS_Z, HAS_D, CH, 0>), grid, block, (uint32_t)lds, st, a, g);
-    if constexpr (CH) {
-        const size_t tot = (size_t)a.B * a.L * a.D;
-        launch((bwd_combine<BF16, HAS_Z, HAS_D>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, a, g);
+    } else {
+        launch((bwd_final<N, BF16, HAS_Z, HAS_D, false, 0, false>), grid, block, (uint32_t)lds, st, a, g);
     }
 }
 
