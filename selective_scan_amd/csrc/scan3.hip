@@ -265,16 +265,33 @@ __global__ void __launch_bounds__(256) carry3(Scan3Args a, Geom3 g) {
         hr = a.h0[(((size_t)b * D + d) * N + n) * 2];
         hi = a.h0[(((size_t)b * D + d) * N + n) * 2 + 1];
     }
-    for (int k = 0; k < g.G - 1; ++k) {
-        float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + k) * 2 * N * D + d;
-        float pr, pi;
-        cdecay(ws[wl.GS + ((size_t)b * (g.G - 1) + k) * D + d], A2, th, pr, pi);
-        const float nr = pr * hr - pi * hi + GH[(size_t)n * D];
-        const float ni = pr * hi + pi * hr + GH[(size_t)(N + n) * D];
-        hr = nr;
-        hi = ni;
-        GH[(size_t)n * D] = hr;
-        GH[(size_t)(N + n) * D] = hi;
+    // U groups' aggregates loaded before any is chained (one memory round trip per U
+    // groups: a load after the previous group's store would wait for it)
+    constexpr int U = 8;
+    const int steps = g.G - 1;
+    for (int k0 = 0; k0 < steps; k0 += U) {
+        float gs[U], vr[U], vi[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = min(k0 + u, steps - 1);
+            const float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + k) * 2 * N * D + d;
+            gs[u] = ws[wl.GS + ((size_t)b * (g.G - 1) + k) * D + d];
+            vr[u] = GH[(size_t)n * D];
+            vi[u] = GH[(size_t)(N + n) * D];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (k0 + u >= steps) break;
+            float* GH = ws + wl.GH + ((size_t)b * (g.G - 1) + k0 + u) * 2 * N * D + d;
+            float pr, pi;
+            cdecay(gs[u], A2, th, pr, pi);
+            const float nr = pr * hr - pi * hi + vr[u];
+            const float ni = pr * hi + pi * hr + vi[u];
+            hr = nr;
+            hi = ni;
+            GH[(size_t)n * D] = hr;
+            GH[(size_t)(N + n) * D] = hi;
+        }
     }
 }
 
