@@ -294,7 +294,8 @@ int ssm_step3(int B, int D, int N, ssm_dtype_t io,
  * not alias inputs or each other. Arithmetic is fp32 with fp32 accumulation;
  * reductions run in a fixed order (no atomics), so results are deterministic.
  * Supported: N in {4, 8, 16, 32, 64, 128, 256} (N >= 32 runs as chunks of 16
- * states whose partial sums over n are added in chunk order); B <= 65535; L >= 0
+ * states whose partial sums over n are added in a fixed order: chunk order within
+ * groups of up to four chunks, then the groups in order); B <= 65535; L >= 0
  * (L = 0 writes dh0 = dh_final, dA = 0, dDskip = 0). Every pointer must be
  * 16-byte aligned. Errors as for ssm_scan_fwd.
  * ------------------------------------------------------------------------- */
