@@ -140,6 +140,7 @@ BWD_SHAPES = [
     # B, L, D, N, dtype
     (2, 300, 70, 16, si.BF16),
     (1, 200, 64, 64, si.F32),
+    (1, 130, 70, 128, si.BF16),
 ]
 
 
