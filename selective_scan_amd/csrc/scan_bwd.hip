@@ -45,10 +45,17 @@
 namespace ssm {
 namespace {
 
+// Waves the final pass aims for: 8192 with every state in one lane (B8 L32768 D512
+// N16: 2.46 ms per call against 2.49-2.52 at 6144), 6144 with 16-state chunks
+// (B1 L4096 D1536 N64: 0.60 ms against 0.64 at 8192).
 #ifndef SSM_BWD_TARGET_WAVES
-#define SSM_BWD_TARGET_WAVES 6144
+#define SSM_BWD_TARGET_WAVES 8192
 #endif
-constexpr int kBwdTargetWaves = SSM_BWD_TARGET_WAVES;  // waves the final pass aims for
+#ifndef SSM_BWD_TARGET_WAVES_CHUNKED
+#define SSM_BWD_TARGET_WAVES_CHUNKED 6144
+#endif
+constexpr int kBwdTargetWaves = SSM_BWD_TARGET_WAVES;
+constexpr int kBwdTargetWavesChunked = SSM_BWD_TARGET_WAVES_CHUNKED;
 // Segments of at least 32 steps: at B = 1, L = 4096, D = 1536 that gives 3072 waves
 // (one full round of the final pass at three waves per SIMD) instead of 6144 16-step
 // segments, and the per-segment work (aggregate prefixes, partial sums) halves
@@ -97,7 +104,8 @@ BGeom bgeom(int B, int L, int D, int N) {
     BGeom g{0, 0, 1, 0, sub_len(N), 0, 0};
     if (L <= 0) return g;
     const long chains = (long)B * ((D + 63) / 64) * bwd_chunks(N);
-    const long s_target = (kBwdTargetWaves + chains - 1) / chains;
+    const long target = bwd_chunks(N) > 1 ? kBwdTargetWavesChunked : kBwdTargetWaves;
+    const long s_target = (target + chains - 1) / chains;
     long Ls = std::max<long>(kBwdMinSegment, (L + s_target - 1) / s_target);
     Ls = (Ls + g.K - 1) / g.K * g.K;
     Ls = std::min<long>(Ls, ((long)L + g.K - 1) / g.K * g.K);
